@@ -1,0 +1,54 @@
+"""CPU oracle for weight-only INT4 per-group quantization and the dequantize-matmul.
+
+TEST INFRASTRUCTURE ONLY.  This package is the plain, slow, obviously correct
+reference that the HIP path is checked against.  Only ``tests/``, the smoke
+check in ``__graft_entry__`` and the CPU-baseline leg of ``bench.py`` may import
+it; the library ``weight_only_int4_group_amd`` never does, and this package
+never imports the library.  Both sides draw their inputs from ``workloads``.
+
+Sources (web pages; cited by page, section and table/equation):
+  * [discosf] discosf.com news 6284891, a tutorial on quantization, speculative
+    sampling and PD disaggregation in nano-vllm.  Section 2.1: a quantizer maps
+    a float range onto an integer range with a scale and a zero point; the
+    per-group granularity (e.g. 128 elements per group) is the usual choice for
+    4-bit GPTQ/AWQ.  Section 2.2: 70B weights are about 140 GB in FP16, 70 GB in
+    INT8, 35 GB in INT4.  Section 2.3: scale and zero point travel with the
+    weights; the loader either dequantizes or feeds low-precision operators.
+  * [aiwing] aiwing.uk, chapter 22 (advanced inference optimisation), section
+    22.3: the bytes-per-parameter table (FP32 4, FP16 2, INT8 1, INT4 0.5,
+    INT2 0.25; a 7B model is 28/14/7/3.5/1.75 GB); weight-only quantization
+    either dequantizes to FP16 then multiplies, or uses a mixed-precision
+    kernel; the AWQ equation W_hat = quant(W / s) * s with s the per-channel
+    activation magnitude; weights can be quantized offline.
+  * [mhpq] mhpq.cn news 1188791, practitioner notes.  Section 2.1: a 1024x1024
+    weight matrix in INT4 takes a quarter of its FP16 size.
+
+Readings taken where the pages are silent (each one is listed with its reason
+in the design notes of the repository):
+  R1 asymmetric unsigned 4-bit codes 0..15 with a zero point;
+  R2 groups are 128 consecutive input features of one output row;
+  R3 the range of a group is its min and max, widened to include 0;
+  R4 scale = (max - min) / 15;  R5 the scale is rounded UP to fp16;
+  R6 the zero point is the integer z = rint(-min / scale), stored as fp16,
+     and dequantization is (q - z) * scale;
+  R7 q = clamp(rint(W' / scale) + z, 0, 15), rint ties to even, applied before
+     adding z;  R8 W' = W / s is one correctly rounded fp64 division;
+  R9 an all-zero group has scale 0, zero point 0 and codes 0; non-finite W or
+     s, or s <= 0, is an error; a scale that overflows fp16 is an error.
+Pins: every function here is checked by tests against facts the pages or the
+mathematics fix (bound, grid reconstruction, byte counts, brute force in exact
+rationals, integer special case); see tests/test_oracle_*.py.
+"""
+from .quantizer import (GROUP, QMAX, NonFiniteInput, OracleError, QuantResult, ScaleOverflow,
+                       quantize, round_up_fp16)
+from .layout import (TILE_BYTES, TILE_ROWS, meta_index, nibble_address, pack_codes, pack_meta,
+                     unpack_codes, unpack_meta)
+from .matmul import dequantize, gemm
+from . import accounting, exact
+
+__all__ = [
+    "GROUP", "QMAX", "NonFiniteInput", "OracleError", "QuantResult", "ScaleOverflow",
+    "quantize", "round_up_fp16", "TILE_BYTES", "TILE_ROWS", "meta_index", "nibble_address",
+    "pack_codes", "pack_meta", "unpack_codes", "unpack_meta", "dequantize", "gemm",
+    "accounting", "exact",
+]

@@ -1,0 +1,101 @@
+"""fp64 reference quantizer: weight-only asymmetric INT4, groups of 128, AWQ pre-scale.
+
+Follows, in order:
+  * aiwing.uk ch.22 sec.22.3, AWQ equation: the weight is divided by the
+    per-input-channel activation magnitude s before quantization and the
+    dequantized value is multiplied by s again (W_hat = quant(W/s) * s);
+  * discosf.com tutorial sec.2.1: quant() finds a scale and a zero point that
+    map the float range of a group onto the integer range; one scale/zero pair
+    per group of 128 elements.
+Readings R1-R9 (package docstring) fix what the pages leave open.
+TEST INFRASTRUCTURE: see the package docstring for who may import this.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+GROUP = 128   # elements per quantization group along K (discosf sec.2.1)
+QMAX = 15     # unsigned 4-bit code range 0..15 (reading R1)
+
+
+class OracleError(ValueError):
+    pass
+
+
+class NonFiniteInput(OracleError):
+    """W or s holds NaN/Inf, or some s <= 0 (reading R9)."""
+
+
+class ScaleOverflow(OracleError):
+    """A group's scale, rounded up to fp16, exceeds the largest finite fp16 (reading R9)."""
+
+
+@dataclass
+class QuantResult:
+    q: np.ndarray       # uint8 [N][K], codes 0..15
+    scales: np.ndarray  # float16 [N][K/128]
+    zeros: np.ndarray   # float16 [N][K/128], integer-valued 0..15
+
+
+def round_up_fp16(v: np.ndarray) -> np.ndarray:
+    """Smallest fp16 value >= v, for float64 v >= 0 (reading R5); +inf past 65504.
+
+    Done as: round to nearest fp16 (NumPy's correctly rounded float64 -> float16
+    cast), then step one fp16 ulp up wherever the nearest value fell below v.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        h = v.astype(np.float16)
+    below = h.astype(np.float64) < v
+    h[below] = np.nextafter(h[below], np.float16(np.inf))
+    return h
+
+
+def quantize(W: np.ndarray, s: np.ndarray | None = None) -> QuantResult:
+    """Quantize fp16 ``W[N][K]`` (optionally divided by fp16 ``s[K]`` first) to INT4 groups."""
+    W = np.asarray(W)
+    if W.dtype != np.float16 or W.ndim != 2:
+        raise TypeError("W must be a 2-D float16 array")
+    N, K = W.shape
+    if K % GROUP:
+        raise ValueError("K must be a multiple of 128")
+    Wd = W.astype(np.float64)
+    if s is None:
+        sd = np.ones(K, dtype=np.float64)
+    else:
+        s = np.asarray(s)
+        if s.dtype != np.float16 or s.shape != (K,):
+            raise TypeError("s must be a float16 array of length K")
+        sd = s.astype(np.float64)
+    if not np.all(np.isfinite(Wd)) or not np.all(np.isfinite(sd)) or not np.all(sd > 0):
+        raise NonFiniteInput("non-finite W or s, or s <= 0")
+
+    # AWQ step (aiwing sec.22.3): W' = W / s, one correctly rounded fp64 division per element.
+    Wp = Wd / sd[None, :]
+    G = K // GROUP
+    Wg = Wp.reshape(N, G, GROUP)
+
+    # Group range, widened to contain 0 (R3); scale = range / 15 rounded up to fp16 (R4, R5).
+    mn = np.minimum(Wg.min(axis=2), 0.0)
+    mx = np.maximum(Wg.max(axis=2), 0.0)
+    rng = mx - mn
+    scale16 = round_up_fp16(rng / QMAX)
+    if not np.all(np.isfinite(scale16)):
+        raise ScaleOverflow("group scale exceeds the fp16 range")
+    scale = scale16.astype(np.float64)
+
+    live = rng > 0   # an all-zero group keeps scale 0, zero point 0, codes 0 (R9)
+    safe = np.where(live, scale, 1.0)
+    # Zero point: the integer nearest to -min/scale (R6); lies in 0..15 because scale >= range/15.
+    z = np.where(live, np.rint(-mn / safe), 0.0)
+    # Codes: rint (ties to even) of W'/scale, then shifted by z and clamped to 0..15 (R7).
+    t = np.rint(Wg / safe[:, :, None]) + z[:, :, None]
+    q = np.where(live[:, :, None], np.clip(t, 0, QMAX), 0.0)
+
+    return QuantResult(
+        q=q.reshape(N, K).astype(np.uint8),
+        scales=np.where(live, scale16, np.float16(0)).astype(np.float16),
+        zeros=z.astype(np.int64).astype(np.float16),   # integer -> fp16: never a negative zero
+    )
