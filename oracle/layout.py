@@ -17,8 +17,9 @@ Definition.  W is [N][K]; G = K / 128 groups per row; N is a multiple of 16.
   * Inside a word, the 4-bit slot i (bits 4i .. 4i+3) holds column
     j = 2 * (i % 4) + i // 4: even j in the low half-word, odd j in the high
     half-word, each in increasing order.
-  * Scales and zero points (fp16 each) are stored tile by tile: the value of
-    row 16b + r, group g is element (b * G + g) * 16 + r of its buffer.
+  * Scales and zero points (fp16 each) are plain row-major [N][G] arrays: the
+    value of row n, group g is element n * G + g of its buffer, so one output
+    row's metadata is contiguous and can be fetched with one wide load.
 TEST INFRASTRUCTURE: see the package docstring for who may import this.
 """
 from __future__ import annotations
@@ -82,7 +83,7 @@ def meta_index(n, g, N: int, K: int):
     G = _check(N, K)
     n = np.asarray(n, dtype=np.int64)
     g = np.asarray(g, dtype=np.int64)
-    return ((n // TILE_ROWS) * G + g) * TILE_ROWS + n % TILE_ROWS
+    return n * G + g
 
 
 def pack_meta(a: np.ndarray) -> np.ndarray:

@@ -52,7 +52,8 @@ def test_meta_layout():
     buf = oracle.pack_meta(a)
     assert np.array_equal(oracle.unpack_meta(buf, N, K), a)
     assert buf[oracle.meta_index(17, 2, N, K)] == a[17, 2]
-    assert int(oracle.meta_index(17, 2, N, K)) == (1 * G + 2) * 16 + 1
+    assert int(oracle.meta_index(17, 2, N, K)) == 17 * G + 2
+    assert np.array_equal(buf, a.ravel())   # row-major: the identity on [N][G]
 
 
 def test_layout_rejects_bad_shapes():
