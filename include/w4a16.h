@@ -1,0 +1,127 @@
+/*
+ * w4a16.h -- weight-only INT4 per-group quantization and the fused
+ * dequantize-matmul, for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (sources are web pages, cited by title and section):
+ *
+ *  - "Chapter 22: Advanced inference optimisation" (aiwing.uk), section 22.3,
+ *    AWQ paragraph and its equation: the weight is divided by a per-input-
+ *    channel activation magnitude s before it is quantized, and the quantized
+ *    value is multiplied by s again:  W_hat = quant(W / s) * s.
+ *  - The nano-vllm tutorial (discosf.com), section 2.1: quant() maps the
+ *    float range of a group onto the integer range with a scale and a zero
+ *    point; per-group granularity with 128 elements per group is the usual
+ *    choice for 4-bit GPTQ/AWQ.  Section 2.3: the scale and zero point travel
+ *    with the weights, and the loader either dequantizes or feeds operators
+ *    that take the low-precision weights directly.
+ *  - Same chapter 22, section 22.3, weight-only paragraph: activations stay in
+ *    FP16 and the product is the plain matmul against the dequantized
+ *    weights; a mixed-precision kernel only computes it faster.
+ *
+ * Readings where the pages leave a step open (all taken identically by the
+ * library and by the CPU reference it is tested against):
+ *  - codes are unsigned 4-bit 0..15 with an integer zero point z (0..15)
+ *    stored as fp16, and dequantization is (q - z) * scale;
+ *  - a group is 128 consecutive input features (K) of one output row (N);
+ *  - the group range is [min(0, min W'), max(0, max W')] with W' = W / s;
+ *    scale = range / 15 rounded UP to the next fp16 value; z = rint(-min /
+ *    scale); q = clamp(rint(W' / scale) + z, 0, 15); rint ties to even; all
+ *    of it in fp64 with one correctly rounded division per quotient;
+ *  - an all-zero group has scale 0, zero point 0 and codes 0.
+ *
+ * Shapes: W is [N][K] (output x input features, like a linear layer's
+ * weight), X is [M][K], Y = X . W_hat^T is [M][N].  K must be a multiple of
+ * 128 and N a multiple of 16.  fp16 means IEEE binary16.
+ *
+ * Packed layout (this library's own; the pages only fix the content):
+ *  - Wq: N*K/2 bytes.  Tile (b, g) covers rows 16b..16b+15 and the 128
+ *    columns of group g; it is 1024 bytes at byte offset (b*G + g)*1024,
+ *    G = K/128.  Inside a tile, lane L = 16c + r (row r, column octet c =
+ *    0..3) owns the 16 bytes at 16L: four little-endian 32-bit words, word t
+ *    holding the codes of columns 128g + 32t + 8c + j, j = 0..7, with column
+ *    j in the 4-bit slot i (bits 4i..4i+3) where j = 2*(i % 4) + i / 4.
+ *    One 64-lane wave therefore reads a whole tile with one 128-bit load per
+ *    lane, and word t of a lane is exactly that lane's B operand of a
+ *    16x16x32 fp16 MFMA.
+ *  - scales, zeros: fp16 row-major [N][G] (element n*G + g).
+ *
+ * Ownership and streams: the caller allocates and owns every buffer (device
+ * memory unless noted) and passes a hipStream_t as `stream` (NULL = the null
+ * stream).  All pointers must be 16-byte aligned.  The library keeps a small
+ * per-device status word (allocated on first use, never freed) for the
+ * packer's error report; it allocates nothing else.
+ *
+ * Errors: every argument is validated on the host before any HIP call, so an
+ * invalid call returns its status without touching the GPU.  Status codes are
+ * the W4A16_* values below; w4a16_strerror() names them.
+ */
+#ifndef W4A16_H
+#define W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define W4A16_GROUP 128      /* elements per quantization group along K     */
+#define W4A16_TILE_ROWS 16   /* rows of W per packed tile (N % 16 == 0)      */
+
+enum {
+  W4A16_OK = 0,
+  W4A16_EINVAL = -1,       /* NULL pointer, M/N/K out of range, K % 128, N % 16 */
+  W4A16_EALIGN = -2,       /* a pointer is not 16-byte aligned                  */
+  W4A16_EUNSUPPORTED = -3, /* unknown kernel path requested                     */
+  W4A16_ENONFINITE = -4,   /* NaN/Inf in W or s, or some s <= 0 (packer)        */
+  W4A16_ERANGE = -5,       /* a group scale rounds up past the fp16 range       */
+  W4A16_EHIP = -6          /* a HIP runtime call or kernel launch failed        */
+};
+
+/* Kernel choice for w4a16_gemm_path(); w4a16_gemm() always uses AUTO. */
+enum {
+  W4A16_PATH_AUTO = 0,     /* pick by M (decode / verify / prefill)               */
+  W4A16_PATH_SKINNY = 1,   /* streaming split-K MFMA kernel, M <= 16 per pass     */
+  W4A16_PATH_TILED = 2     /* LDS-tiled MFMA GEMM for large M                     */
+};
+
+/* Byte sizes of the three packed buffers of an [N][K] weight (host outputs).
+ * wq = N*K/2, scales = zeros = 2*N*(K/128).  EINVAL on bad shapes or NULL. */
+int w4a16_packed_sizes(int64_t N, int64_t K, size_t *wq_bytes, size_t *scales_bytes,
+                       size_t *zeros_bytes);
+
+/* Quantize and pack (offline step; chapter 22 section 22.3 notes weights are
+ * quantized offline).  W: fp16 [N][K] row-major.  s: fp16 [K] AWQ scale, or
+ * NULL for s = 1.  Writes Wq, scales, zeros in the layout above.  Blocks on
+ * `stream` before returning so that it can report ENONFINITE (non-finite W or
+ * s, or s <= 0) or ERANGE (a group's fp16 scale would overflow); on such an
+ * error the outputs hold unspecified values. */
+int w4a16_quantize_pack(const void *W, const void *s, int64_t N, int64_t K, void *Wq,
+                        void *scales, void *zeros, void *stream);
+
+/* Y[M][N] = X[M][K] . W_hat^T with W_hat[n][k] = (q - z) * scale * s[k].
+ * X: fp16 [M][K]; Wq/scales/zeros: packed as above; s: fp16 [K] or NULL;
+ * Y: fp16 [M][N] row-major, fully overwritten.  fp32 accumulation; X * s is
+ * rounded to fp16 once.  Asynchronous on `stream`.  M >= 1. */
+int w4a16_gemm(const void *X, const void *Wq, const void *scales, const void *zeros,
+               const void *s, void *Y, int64_t M, int64_t N, int64_t K, void *stream);
+
+/* Same as w4a16_gemm with an explicit kernel path (tests and benchmarks). */
+int w4a16_gemm_path(const void *X, const void *Wq, const void *scales, const void *zeros,
+                    const void *s, void *Y, int64_t M, int64_t N, int64_t K, int path,
+                    void *stream);
+
+/* Which path AUTO takes for this shape (host only; no GPU call). */
+int w4a16_select_path(int64_t M, int64_t N, int64_t K);
+
+/* Static description of a status code. */
+const char *w4a16_strerror(int status);
+
+/* Library ABI version (major * 100 + minor). */
+int w4a16_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A16_H */

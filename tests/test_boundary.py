@@ -1,0 +1,107 @@
+"""The C-ABI library: it loads without a GPU, exports what include/w4a16.h declares,
+and validates every argument on the host before any HIP call.
+
+Only calls that fail validation are made here (no compute happens without a GPU).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from tests.conftest import ROOT
+
+import weight_only_int4_group_amd as w4
+
+HEADER = os.path.join(ROOT, "include", "w4a16.h")
+V = ctypes.c_void_p
+A16 = V(1 << 20)        # a 16-byte aligned stand-in address (never dereferenced)
+ODD = V((1 << 20) + 2)  # a misaligned one
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char \*)\s*(w4a16_\w+)\s*\(", text, re.M)))
+
+
+def status_constants():
+    text = open(HEADER).read()
+    return {name: int(val) for name, val in re.findall(r"(W4A16_E?\w+)\s*=\s*(-?\d+)", text)}
+
+
+def test_library_exports_every_declared_function():
+    L = w4.lib()
+    names = declared_functions()
+    assert len(names) >= 6
+    for name in names:
+        assert hasattr(L, name), name
+    assert set(names) == set(w4.EXPORTED_SYMBOLS)
+    assert w4.w4a16_version() >= 100
+
+
+def test_status_codes_match_header():
+    consts = status_constants()
+    for code, name in w4.STATUS.items():
+        assert consts[name] == code
+    for code in w4.STATUS:
+        assert w4.w4a16_strerror(code) and w4.w4a16_strerror(code) != "unknown status"
+    assert w4.w4a16_strerror(12345) == "unknown status"
+
+
+@pytest.mark.parametrize("N,K", [(1024, 1024), (16, 128), (14336, 4096), (4096, 14336),
+                                 (18944, 3584), (28672, 8192)])
+def test_packed_sizes(N, K):
+    wq, sc, z = w4.w4a16_packed_sizes(N, K)
+    assert wq == N * K // 2 and sc == z == 2 * N * (K // 128)
+
+
+@pytest.mark.parametrize("N,K", [(0, 128), (16, 0), (8, 128), (16, 64), (17, 128), (16, 200),
+                                 (-16, 128), (1 << 25, 128)])
+def test_packed_sizes_rejects(N, K):
+    with pytest.raises(w4.W4A16Error) as e:
+        w4.w4a16_packed_sizes(N, K)
+    assert e.value.status == -1
+
+
+def test_packed_sizes_null_outputs():
+    assert w4.lib().w4a16_packed_sizes(16, 128, None, None, None) == -1
+
+
+def gemm_rc(X=A16, Wq=A16, sc=A16, z=A16, s=None, Y=A16, M=1, N=16, K=128, path=0):
+    return w4.lib().w4a16_gemm_path(X, Wq, sc, z, s, Y, M, N, K, path, None)
+
+
+def pack_rc(W=A16, s=None, N=16, K=128, Wq=A16, sc=A16, z=A16):
+    return w4.lib().w4a16_quantize_pack(W, s, N, K, Wq, sc, z, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(K=100), -1), (dict(K=0), -1), (dict(N=8), -1), (dict(N=0), -1), (dict(M=-1), -1),
+    (dict(M=1 << 23), -1), (dict(X=None), -1), (dict(Wq=None), -1), (dict(sc=None), -1),
+    (dict(z=None), -1), (dict(Y=None), -1), (dict(X=ODD), -2), (dict(Y=ODD), -2),
+    (dict(s=ODD), -2), (dict(Wq=ODD), -2), (dict(path=7), -3), (dict(path=-1), -3),
+])
+def test_gemm_validation(kw, code):
+    assert gemm_rc(**kw) == code
+
+
+def test_gemm_empty_batch_is_a_noop():
+    # M = 0: nothing to read or write, the pointers may be NULL, no HIP call is made
+    assert gemm_rc(X=None, Y=None, M=0) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(W=None), -1), (dict(Wq=None), -1), (dict(sc=None), -1), (dict(z=None), -1),
+    (dict(N=24), -1), (dict(K=192), -1), (dict(N=0), -1), (dict(W=ODD), -2), (dict(s=ODD), -2),
+    (dict(z=ODD), -2),
+])
+def test_pack_validation(kw, code):
+    assert pack_rc(**kw) == code
+
+
+def test_select_path():
+    sel = w4.w4a16_select_path
+    for M in (1, 2, 5, 9, 16):
+        assert sel(M, 4096, 4096) == w4.PATH_SKINNY
+    for M in (64, 256, 4096):
+        assert sel(M, 4096, 4096) == w4.PATH_TILED

@@ -1,0 +1,132 @@
+"""GPU dequantize-matmul vs the fp64 oracle, element by element, on both kernel paths.
+
+Shapes span several packed tiles and ragged tails: N = 272 is 17 row tiles (not a
+multiple of the tiled kernel's 128-row block), K = 640 is 5 groups, and M runs
+over every value from 1 to 17 plus ragged larger batches.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import weight_only_int4_group_amd as w4
+from tests.gpu_helpers import assert_close, note, to_dev, to_host, torch_cuda
+from workloads import activations, awq_scales, weights
+
+pytestmark = pytest.mark.gpu
+
+PATHS = {"auto": w4.PATH_AUTO, "skinny": w4.PATH_SKINNY, "tiled": w4.PATH_TILED}
+
+
+def packed_case(N, K, awq, key=2, mat=0):
+    W = weights(key, mat, N, K)
+    s = awq_scales(key, mat, K) if awq else None
+    torch_cuda()
+    pw = w4.w4a16_quantize_pack(to_dev(W), None if s is None else to_dev(s))
+    ref = oracle.quantize(W, s)
+    return pw, s, ref
+
+
+_CACHE = {}
+
+
+def cached_case(N, K, awq):
+    key = (N, K, awq)
+    if key not in _CACHE:
+        _CACHE[key] = packed_case(N, K, awq)
+    return _CACHE[key]
+
+
+def run(X, pw, s, path):
+    Xd = to_dev(X)
+    sd = None if s is None else to_dev(s)
+    return to_host(w4.w4a16_gemm_path(Xd, pw, sd, PATHS[path]))
+
+
+@pytest.mark.parametrize("path", ["skinny", "tiled"])
+@pytest.mark.parametrize("awq", [False, True])
+@pytest.mark.parametrize("M", list(range(1, 18)))
+def test_small_M_all_paths(M, awq, path):
+    N, K = 272, 640
+    pw, s, ref = cached_case(N, K, awq)
+    X = activations(2, 0, M, K)
+    note(f"gemm path={path} M={M} N={N} K={K} awq={awq}")
+    Y = run(X, pw, s, path)
+    assert_close(Y, oracle.gemm(X, ref.q, ref.scales, ref.zeros, s), f"M={M} {path}")
+
+
+@pytest.mark.parametrize("path", ["auto", "skinny", "tiled"])
+@pytest.mark.parametrize("M", [31, 64, 100, 128, 129, 257])
+def test_larger_M(M, path):
+    N, K = 272, 640
+    pw, s, ref = cached_case(N, K, True)
+    X = activations(2, 1, M, K, outliers=True)
+    note(f"gemm path={path} M={M} N={N} K={K}")
+    Y = run(X, pw, s, path)
+    assert_close(Y, oracle.gemm(X, ref.q, ref.scales, ref.zeros, s), f"M={M} {path}")
+
+
+@pytest.mark.parametrize("N,K", [(16, 128), (16, 4096), (1024, 128), (528, 1152), (64, 14336)])
+@pytest.mark.parametrize("M", [1, 5, 33])
+def test_shape_extremes(N, K, M):
+    pw, s, ref = packed_case(N, K, True, key=3, mat=N + K)
+    X = activations(3, 0, M, K)
+    note(f"gemm auto M={M} N={N} K={K}")
+    Y = run(X, pw, s, "auto")
+    assert_close(Y, oracle.gemm(X, ref.q, ref.scales, ref.zeros, s), f"{M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("path", ["skinny", "tiled"])
+def test_integer_case_bit_exact(path):
+    """Pin P5: s = 1, integer weights with codes 0 and 15 in every group -> scale 1,
+    zero point 8; X in {-1, 0, 1}: Y is an integer matmul, exact in fp16."""
+    rng = np.random.default_rng(9)
+    N, K, M = 64, 256, 24
+    W = rng.integers(-8, 8, size=(N, K))
+    W[:, 0::128] = -8
+    W[:, 1::128] = 7
+    W = W.astype(np.float16)
+    X = rng.integers(-1, 2, size=(M, K)).astype(np.float16)
+    ref = oracle.quantize(W, None)
+    assert np.all(ref.scales == 1) and np.all(ref.zeros == 8)
+    torch_cuda()
+    pw = w4.w4a16_quantize_pack(to_dev(W))
+    note(f"integer case path={path}")
+    Y = run(X, pw, None, path)
+    Yref = X.astype(np.float64) @ W.astype(np.float64).T
+    assert np.array_equal(Y.astype(np.float64), Yref)
+
+
+def test_zero_weights_give_zero():
+    N, K, M = 32, 256, 3
+    W = np.zeros((N, K), np.float16)
+    torch_cuda()
+    pw = w4.w4a16_quantize_pack(to_dev(W))
+    X = activations(4, 0, M, K)
+    for path in ("skinny", "tiled"):
+        note(f"zero weights path={path}")
+        assert np.all(run(X, pw, None, path) == 0)
+
+
+def test_deterministic_and_row_independent():
+    """Same inputs twice -> identical bits; row 0 of a batch equals the M = 1 result
+    computed by the same kernel (pin P6's batch identity, on the GPU)."""
+    N, K = 1024, 4096
+    pw, s, _ = packed_case(N, K, True, key=5)
+    for path, M in (("skinny", 9), ("tiled", 40)):
+        X = activations(5, 0, M, K)
+        note(f"determinism path={path} M={M}")
+        a = run(X, pw, s, path)
+        b = run(X, pw, s, path)
+        assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+    X = activations(5, 0, 5, K)
+    full = run(X, pw, s, "skinny")
+    one = run(X[:1], pw, s, "skinny")
+    assert np.array_equal(full[:1].view(np.uint16), one.view(np.uint16))
+
+
+def test_empty_batch():
+    torch = torch_cuda()
+    pw, s, _ = cached_case(272, 640, False)
+    X = torch.empty((0, 640), dtype=torch.float16, device="cuda")
+    Y = w4.w4a16_gemm(X, pw)
+    assert tuple(Y.shape) == (0, 272)

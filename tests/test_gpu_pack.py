@@ -1,0 +1,100 @@
+"""GPU packer vs the fp64 oracle: packed codes, scales and zero points must be bit-exact."""
+import numpy as np
+import pytest
+
+import oracle
+import weight_only_int4_group_amd as w4
+from tests.gpu_helpers import h16_bits, note, to_dev, to_host, torch_cuda
+from workloads import awq_scales, weights
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_pack(W, s):
+    torch_cuda()
+    pw = w4.w4a16_quantize_pack(to_dev(W), None if s is None else to_dev(s))
+    return to_host(pw.wq), to_host(pw.scales), to_host(pw.zeros)
+
+
+def check_exact(W, s, tag):
+    note(f"pack {tag} N={W.shape[0]} K={W.shape[1]} awq={s is not None}")
+    wq, sc, z = gpu_pack(W, s)
+    ref = oracle.quantize(W, s)
+    assert np.array_equal(h16_bits(sc), h16_bits(oracle.pack_meta(ref.scales)).reshape(sc.shape)), tag
+    assert np.array_equal(h16_bits(z), h16_bits(oracle.pack_meta(ref.zeros)).reshape(z.shape)), tag
+    assert np.array_equal(wq, oracle.pack_codes(ref.q)), tag
+
+
+def test_pack_gemv_1024():
+    check_exact(weights(0, 0, 1024, 1024), None, "1024x1024")
+
+
+@pytest.mark.parametrize("N,K", [(16, 128), (48, 384), (272, 640), (1024, 4096)])
+def test_pack_awq_shapes(N, K):
+    check_exact(weights(1, 9, N, K), awq_scales(1, 9, K), f"awq {N}x{K}")
+
+
+def test_pack_edge_groups():
+    rng = np.random.default_rng(11)
+    N, K = 64, 1024
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
+    W[0:16, 0:128] = 0                                  # all-zero group
+    W[16, 128:256] = np.float16(-0.0)                   # signed zeros only
+    W[17, 256:384] = 3.0                                # constant positive group
+    W[18, 256:384] = -3.0                               # constant negative group
+    W[19, 384:512] = np.float16(6e-8)                   # subnormal weights -> tiny scale
+    W[20, 512:640] = rng.standard_normal(128).astype(np.float16) * np.float16(1e-5)
+    W[21, 640:768] = np.float16(60000.0)                # near the top of fp16
+    W[22, 768:896] *= 500                               # outlier-heavy group
+    W[23, 896:1024] = np.linspace(-1, 1, 128).astype(np.float16)  # ties land on .5
+    check_exact(W, None, "edge groups")
+    s = np.exp(rng.uniform(-1, 1, K)).astype(np.float16)   # keeps 60000 / s in range
+    check_exact(W, s, "edge groups + awq")
+
+
+def test_pack_on_grid_exact():
+    # weights on the quantization grid are reconstructed exactly (pin P2's input family)
+    rng = np.random.default_rng(5)
+    N, K, G = 32, 256, 2
+    q = rng.integers(0, 16, size=(N, G, 128))
+    q[:, :, 0], q[:, :, 1] = 0, 15
+    z = rng.integers(0, 16, size=(N, G))
+    scale = np.ldexp(rng.integers(64, 128, size=(N, G)).astype(np.float64),
+                     rng.integers(-16, -8, size=(N, G)))
+    W = ((q - z[:, :, None]) * scale[:, :, None]).reshape(N, K).astype(np.float16)
+    wq, sc, zz = gpu_pack(W, None)
+    assert np.array_equal(sc.astype(np.float64), scale)
+    assert np.array_equal(zz.astype(np.int64), z)
+    assert np.array_equal(oracle.unpack_codes(wq, N, K), q.reshape(N, K).astype(np.uint8))
+
+
+@pytest.mark.parametrize("bad", ["nan_w", "inf_w", "zero_s", "neg_s", "inf_s"])
+def test_pack_rejects_nonfinite(bad):
+    N, K = 32, 256
+    W = weights(0, 3, N, K)
+    s = np.ones(K, np.float16)
+    if bad == "nan_w":
+        W[5, 7] = np.nan
+    elif bad == "inf_w":
+        W[31, 255] = np.inf
+    elif bad == "zero_s":
+        s[100] = 0
+    elif bad == "neg_s":
+        s[3] = -1
+    else:
+        s[200] = np.inf
+    note(f"pack rejects {bad}")
+    with pytest.raises(w4.W4A16Error) as e:
+        w4.w4a16_quantize_pack(to_dev(W), to_dev(s))
+    assert e.value.status == -4
+
+
+def test_pack_rejects_scale_overflow():
+    N, K = 16, 128
+    W = np.zeros((N, K), np.float16)
+    W[3, 0], W[3, 1] = np.float16(60000), np.float16(-60000)
+    s = np.full(K, np.float16(0.05))          # W/s spans 2.4e6: range/15 > 65504
+    note("pack rejects scale overflow")
+    with pytest.raises(w4.W4A16Error) as e:
+        w4.w4a16_quantize_pack(to_dev(W), to_dev(s))
+    assert e.value.status == -5

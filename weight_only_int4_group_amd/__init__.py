@@ -1,0 +1,166 @@
+"""Weight-only INT4 per-group quantization (W4A16) for AMD Instinct MI355X.
+
+Thin ctypes binding over ``libw4a16.so`` (C ABI in ``include/w4a16.h``).  The
+binding only marshals arguments: it checks tensor dtypes/devices, allocates
+outputs with torch (device memory and streams are torch's), and passes raw
+pointers and the current HIP stream to the library.  Every step of the
+computation runs in the library's HIP kernels; there is no fallback.
+
+    from weight_only_int4_group_amd import w4a16_quantize_pack, w4a16_gemm
+    pw = w4a16_quantize_pack(W, s)        # W: fp16 [N][K] cuda, s: fp16 [K] or None
+    Y = w4a16_gemm(X, pw, s)              # X: fp16 [M][K] cuda -> Y: fp16 [M][N]
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+from .build import LIB_PATH
+
+__all__ = [
+    "W4A16Error", "PackedWeight", "GROUP", "PATH_AUTO", "PATH_SKINNY", "PATH_TILED", "lib",
+    "w4a16_packed_sizes", "w4a16_quantize_pack", "w4a16_gemm", "w4a16_gemm_path",
+    "w4a16_select_path", "w4a16_strerror", "w4a16_version", "EXPORTED_SYMBOLS",
+]
+
+GROUP = 128
+PATH_AUTO, PATH_SKINNY, PATH_TILED = 0, 1, 2
+STATUS = {0: "W4A16_OK", -1: "W4A16_EINVAL", -2: "W4A16_EALIGN", -3: "W4A16_EUNSUPPORTED",
+          -4: "W4A16_ENONFINITE", -5: "W4A16_ERANGE", -6: "W4A16_EHIP"}
+EXPORTED_SYMBOLS = ("w4a16_packed_sizes", "w4a16_quantize_pack", "w4a16_gemm",
+                    "w4a16_gemm_path", "w4a16_select_path", "w4a16_strerror", "w4a16_version")
+
+
+class W4A16Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({w4a16_strerror(status)})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libw4a16.so (built in-tree by ``weight_only_int4_group_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m weight_only_int4_group_amd.build` (needs hipcc)")
+    L = ctypes.CDLL(LIB_PATH)
+    i64, vp, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t)
+    L.w4a16_packed_sizes.argtypes = [i64, i64, sz, sz, sz]
+    L.w4a16_quantize_pack.argtypes = [vp, vp, i64, i64, vp, vp, vp, vp]
+    L.w4a16_gemm.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, vp]
+    L.w4a16_gemm_path.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, vp]
+    L.w4a16_select_path.argtypes = [i64, i64, i64]
+    L.w4a16_strerror.argtypes = [ctypes.c_int]
+    L.w4a16_strerror.restype = ctypes.c_char_p
+    L.w4a16_version.argtypes = []
+    for name in ("w4a16_packed_sizes", "w4a16_quantize_pack", "w4a16_gemm", "w4a16_gemm_path",
+                 "w4a16_select_path", "w4a16_version"):
+        getattr(L, name).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def w4a16_strerror(status: int) -> str:
+    return lib().w4a16_strerror(status).decode()
+
+
+def w4a16_version() -> int:
+    return lib().w4a16_version()
+
+
+def w4a16_packed_sizes(N: int, K: int) -> tuple:
+    a, b, c = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    rc = lib().w4a16_packed_sizes(N, K, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c))
+    if rc:
+        raise W4A16Error(rc, "w4a16_packed_sizes")
+    return a.value, b.value, c.value
+
+
+def w4a16_select_path(M: int, N: int, K: int) -> int:
+    return lib().w4a16_select_path(M, N, K)
+
+
+@dataclass
+class PackedWeight:
+    """Packed INT4 weight: codes (uint8, N*K/2 bytes) and fp16 [N][K/128] scales/zeros."""
+    wq: "object"
+    scales: "object"
+    zeros: "object"
+    N: int
+    K: int
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_handle(dev):
+    return ctypes.c_void_p(_torch().cuda.current_stream(dev).cuda_stream)
+
+
+def _dev_ptr(t, name, dtype=None, numel=None):
+    torch = _torch()
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device (cuda) tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} must have {numel} elements, got {t.numel()}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def w4a16_quantize_pack(W, s=None, out: PackedWeight | None = None) -> PackedWeight:
+    """Quantize fp16 W[N][K] (AWQ scale s[K] or None) into a PackedWeight (blocks)."""
+    torch = _torch()
+    if W.dim() != 2:
+        raise ValueError("W must be 2-D [N][K]")
+    N, K = W.shape
+    wq_b, sc_b, z_b = w4a16_packed_sizes(N, K)
+    if out is None:
+        out = PackedWeight(torch.empty(wq_b, dtype=torch.uint8, device=W.device),
+                           torch.empty((N, K // GROUP), dtype=torch.float16, device=W.device),
+                           torch.empty((N, K // GROUP), dtype=torch.float16, device=W.device),
+                           N, K)
+    rc = lib().w4a16_quantize_pack(
+        _dev_ptr(W, "W", torch.float16), _dev_ptr(s, "s", torch.float16, K), N, K,
+        _dev_ptr(out.wq, "wq", torch.uint8, wq_b),
+        _dev_ptr(out.scales, "scales", torch.float16, sc_b // 2),
+        _dev_ptr(out.zeros, "zeros", torch.float16, z_b // 2), _stream_handle(W.device))
+    if rc:
+        raise W4A16Error(rc, "w4a16_quantize_pack")
+    return out
+
+
+def w4a16_gemm_path(X, pw: PackedWeight, s=None, path: int = PATH_AUTO, out=None):
+    """Y[M][N] = X[M][K] . dequant(pw)^T (fp16), on the current stream, asynchronously."""
+    torch = _torch()
+    if X.dim() != 2 or X.shape[1] != pw.K:
+        raise ValueError("X must be [M][K] with K matching the packed weight")
+    M = X.shape[0]
+    if out is None:
+        out = torch.empty((M, pw.N), dtype=torch.float16, device=X.device)
+    elif tuple(out.shape) != (M, pw.N):
+        raise ValueError("out must be [M][N]")
+    rc = lib().w4a16_gemm_path(
+        _dev_ptr(X, "X", torch.float16), _dev_ptr(pw.wq, "wq", torch.uint8),
+        _dev_ptr(pw.scales, "scales", torch.float16), _dev_ptr(pw.zeros, "zeros", torch.float16),
+        _dev_ptr(s, "s", torch.float16, pw.K), _dev_ptr(out, "out", torch.float16),
+        M, pw.N, pw.K, path, _stream_handle(X.device))
+    if rc:
+        raise W4A16Error(rc, "w4a16_gemm")
+    return out
+
+
+def w4a16_gemm(X, pw: PackedWeight, s=None, out=None):
+    return w4a16_gemm_path(X, pw, s, PATH_AUTO, out)

@@ -1,0 +1,136 @@
+// C-ABI front end: argument validation (host only, before any HIP call),
+// kernel choice by M, and launches on the caller's stream.
+#include <mutex>
+#include <vector>
+
+#include "../../include/w4a16.h"
+#include "w4a16_internal.h"
+
+namespace {
+
+constexpr int64_t kMaxDim = int64_t(1) << 24;  // rows / columns per operand
+constexpr int64_t kMaxM = int64_t(1) << 22;    // batch rows per call
+
+// Largest M the streaming kernel takes in one pass (its A operand is 16 rows).
+constexpr int64_t kSkinnyMaxM = 16;
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_shape(int64_t N, int64_t K) {
+  if (N <= 0 || K <= 0 || N > kMaxDim || K > kMaxDim) return W4A16_EINVAL;
+  if (N % W4A16_TILE_ROWS || K % W4A16_GROUP) return W4A16_EINVAL;
+  return W4A16_OK;
+}
+
+// Per-device status word of the packer, allocated on first use.
+std::mutex g_status_mu;
+std::vector<unsigned *> g_status;
+
+int status_word(unsigned **out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return W4A16_EHIP;
+  std::lock_guard<std::mutex> lock(g_status_mu);
+  if ((int)g_status.size() <= dev) g_status.resize(dev + 1, nullptr);
+  if (!g_status[dev]) {
+    void *p = nullptr;
+    if (hipMalloc(&p, 256) != hipSuccess) return W4A16_EHIP;
+    g_status[dev] = static_cast<unsigned *>(p);
+  }
+  *out = g_status[dev];
+  return W4A16_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int w4a16_version(void) { return 100; }
+
+const char *w4a16_strerror(int status) {
+  switch (status) {
+    case W4A16_OK: return "ok";
+    case W4A16_EINVAL: return "invalid argument (NULL pointer, or M/N/K out of range, K % 128 != 0, N % 16 != 0)";
+    case W4A16_EALIGN: return "pointer not 16-byte aligned";
+    case W4A16_EUNSUPPORTED: return "unsupported kernel path";
+    case W4A16_ENONFINITE: return "non-finite W or s, or s <= 0";
+    case W4A16_ERANGE: return "group scale exceeds the fp16 range";
+    case W4A16_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int w4a16_packed_sizes(int64_t N, int64_t K, size_t *wq_bytes, size_t *scales_bytes,
+                       size_t *zeros_bytes) {
+  if (!wq_bytes || !scales_bytes || !zeros_bytes) return W4A16_EINVAL;
+  const int rc = check_shape(N, K);
+  if (rc) return rc;
+  *wq_bytes = (size_t)N * (size_t)K / 2;
+  *scales_bytes = (size_t)N * (size_t)(K / W4A16_GROUP) * 2;
+  *zeros_bytes = *scales_bytes;
+  return W4A16_OK;
+}
+
+int w4a16_quantize_pack(const void *W, const void *s, int64_t N, int64_t K, void *Wq,
+                        void *scales, void *zeros, void *stream) {
+  if (!W || !Wq || !scales || !zeros) return W4A16_EINVAL;
+  int rc = check_shape(N, K);
+  if (rc) return rc;
+  if (!aligned16(W) || !aligned16(Wq) || !aligned16(scales) || !aligned16(zeros) ||
+      (s && !aligned16(s)))
+    return W4A16_EALIGN;
+  unsigned *status = nullptr;
+  if ((rc = status_word(&status))) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (hipMemsetAsync(status, 0, sizeof(unsigned), st) != hipSuccess) return W4A16_EHIP;
+  if (w4a16::launch_pack(W, s, (int)N, (int)K, Wq, scales, zeros, status, st) != hipSuccess)
+    return W4A16_EHIP;
+  unsigned host = 0;
+  if (hipMemcpyAsync(&host, status, sizeof(unsigned), hipMemcpyDeviceToHost, st) != hipSuccess)
+    return W4A16_EHIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return W4A16_EHIP;
+  if (host & w4a16::kPackNonFinite) return W4A16_ENONFINITE;
+  if (host & w4a16::kPackRange) return W4A16_ERANGE;
+  return W4A16_OK;
+}
+
+int w4a16_select_path(int64_t M, int64_t N, int64_t K) {
+  (void)N;
+  (void)K;
+  return M <= kSkinnyMaxM ? W4A16_PATH_SKINNY : W4A16_PATH_TILED;
+}
+
+int w4a16_gemm_path(const void *X, const void *Wq, const void *scales, const void *zeros,
+                    const void *s, void *Y, int64_t M, int64_t N, int64_t K, int path,
+                    void *stream) {
+  int rc = check_shape(N, K);
+  if (rc) return rc;
+  if (M < 0 || M > kMaxM) return W4A16_EINVAL;
+  if (path != W4A16_PATH_AUTO && path != W4A16_PATH_SKINNY && path != W4A16_PATH_TILED)
+    return W4A16_EUNSUPPORTED;
+  if (M == 0) return W4A16_OK;  // empty batch: nothing to read or write
+  if (!X || !Wq || !scales || !zeros || !Y) return W4A16_EINVAL;
+  if (!aligned16(X) || !aligned16(Wq) || !aligned16(scales) || !aligned16(zeros) ||
+      !aligned16(Y) || (s && !aligned16(s)))
+    return W4A16_EALIGN;
+  if (path == W4A16_PATH_AUTO) path = w4a16_select_path(M, N, K);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t err = hipSuccess;
+  if (path == W4A16_PATH_SKINNY) {
+    // the streaming kernel covers 16 rows of X per pass
+    for (int64_t m0 = 0; m0 < M && err == hipSuccess; m0 += kSkinnyMaxM) {
+      const int64_t mb = (M - m0) < kSkinnyMaxM ? (M - m0) : kSkinnyMaxM;
+      err = w4a16::launch_skinny(static_cast<const _Float16 *>(X) + m0 * K, Wq, scales, zeros, s,
+                                 static_cast<_Float16 *>(Y) + m0 * N, (int)mb, (int)N, (int)K, st);
+    }
+  } else {
+    err = w4a16::launch_tiled(X, Wq, scales, zeros, s, Y, (int)M, (int)N, (int)K, st);
+  }
+  return err == hipSuccess ? W4A16_OK : W4A16_EHIP;
+}
+
+int w4a16_gemm(const void *X, const void *Wq, const void *scales, const void *zeros,
+               const void *s, void *Y, int64_t M, int64_t N, int64_t K, void *stream) {
+  return w4a16_gemm_path(X, Wq, scales, zeros, s, Y, M, N, K, W4A16_PATH_AUTO, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,146 @@
+// Quantize-and-pack: fp16 W[N][K] (and optional fp16 AWQ scale s[K]) ->
+// packed 4-bit codes, fp16 per-group scales and fp16 zero points.
+//
+// The arithmetic follows "Chapter 22: Advanced inference optimisation"
+// (aiwing.uk), section 22.3, AWQ equation (divide W by s, then quantize), and
+// the nano-vllm tutorial (discosf.com), section 2.1 (a scale and a zero point
+// per group of 128 elements map the float range onto the integer range).
+// Every quotient is one correctly rounded fp64 division and nothing is fused,
+// so the result is unique: the group range [min(0, min W'), max(0, max W')],
+// scale = range / 15 rounded up to fp16, z = rint(-min / scale),
+// q = clamp(rint(W' / scale) + z, 0, 15), ties to even.
+//
+// One 64-lane wave handles one packed tile (16 rows x 128 columns = one group
+// of 16 rows).  Lane L = 16c + r reads the 32 values of row r that it will
+// own in the packed tile (columns 32t + 8c + j), so the group's min/max is a
+// reduction over the four lanes r, r+16, r+32, r+48 and the lane then writes
+// its 16 packed bytes directly.
+#include "w4a16_device.h"
+#include "w4a16_internal.h"
+
+namespace w4a16 {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Smallest fp16 value >= v for finite v > 0, built from the binary16 grid:
+// below 2^-14 the grid step is 2^-24; in [2^e, 2^(e+1)) it is 2^(e-10).
+// Returns false when that value would exceed the largest finite fp16.
+__device__ bool fp16_ceil(double v, _Float16 *out) {
+  if (!(v <= 65504.0)) return false;
+  double step;
+  if (v < 0x1p-14) {
+    step = 0x1p-24;
+  } else {
+    int e;
+    (void)frexp(v, &e);          // v = m * 2^e, m in [0.5, 1): v in [2^(e-1), 2^e)
+    step = ldexp(1.0, e - 11);   // 2^((e-1) - 10)
+  }
+  const double h = ceil(v / step) * step;   // exact: step is a power of two
+  if (h > 65504.0) return false;
+  *out = (_Float16)h;                       // exact: h lies on the fp16 grid
+  return true;
+}
+
+__device__ __forceinline__ bool finite_h(_Float16 x) {
+  const uint16_t b = __builtin_bit_cast(uint16_t, x);
+  return (b & 0x7C00u) != 0x7C00u;
+}
+
+__global__ __launch_bounds__(256) void pack_kernel(const _Float16 *__restrict__ W,
+                                                   const _Float16 *__restrict__ s, int N, int K,
+                                                   u32x4 *__restrict__ Wq,
+                                                   _Float16 *__restrict__ scales,
+                                                   _Float16 *__restrict__ zeros,
+                                                   unsigned *__restrict__ status) {
+#pragma clang fp contract(off)
+  const int G = K / kGroup;
+  const long long tiles = (long long)(N / kTileRows) * G;
+  const long long tile = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (tile >= tiles) return;  // uniform per wave
+  const int lane = threadIdx.x & 63;
+  const int c = lane >> 4, r = lane & 15;
+  const int b = (int)(tile / G), g = (int)(tile % G);
+  const int n = b * kTileRows + r;
+
+  double wp[32];
+  unsigned bad = 0;
+  double mn = 0.0, mx = 0.0;  // the range always contains 0
+  const _Float16 *wrow = W + (size_t)n * K + (size_t)g * kGroup + 8 * c;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const half8 wv = load_half8(wrow + 32 * t);
+    half8 sv;
+    if (s) {
+      sv = load_half8(s + (size_t)g * kGroup + 32 * t + 8 * c);
+    } else {
+      const half8 one = {1, 1, 1, 1, 1, 1, 1, 1};
+      sv = one;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (!finite_h(wv[j]) || !finite_h(sv[j]) || !((double)sv[j] > 0.0)) bad |= kPackNonFinite;
+      const double q = (double)wv[j] / (double)sv[j];
+      wp[8 * t + j] = q;
+      mn = q < mn ? q : mn;
+      mx = q > mx ? q : mx;
+    }
+  }
+  // The four lanes that share row r hold the four column octets of the group.
+  mn = fmin(mn, __shfl_xor(mn, 16));
+  mn = fmin(mn, __shfl_xor(mn, 32));
+  mx = fmax(mx, __shfl_xor(mx, 16));
+  mx = fmax(mx, __shfl_xor(mx, 32));
+
+  const double range = mx - mn;
+  _Float16 sc16 = 0, z16 = 0;
+  double scale = 1.0, z = 0.0;
+  const bool live = range > 0.0;
+  if (live) {
+    if (!fp16_ceil(range / 15.0, &sc16)) {
+      bad |= kPackRange;
+      sc16 = 0;
+    } else {
+      scale = (double)sc16;
+      z = rint(-mn / scale);
+      z16 = (_Float16)z;  // exact: an integer in 0..15
+    }
+  }
+
+  u32x4 out = {0, 0, 0, 0};
+  if (live) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        double v = rint(wp[8 * t + j] / scale) + z;
+        v = v < 0.0 ? 0.0 : (v > 15.0 ? 15.0 : v);
+        const uint32_t code = (uint32_t)v;
+        const int slot = (j >> 1) + 4 * (j & 1);  // column j -> 4-bit slot
+        word |= code << (4 * slot);
+      }
+      out[t] = word;
+    }
+  }
+  Wq[tile * 64 + lane] = out;
+  if (c == 0) {
+    scales[(size_t)n * G + g] = sc16;
+    zeros[(size_t)n * G + g] = z16;
+  }
+  if (bad) atomicOr(status, bad);
+}
+
+}  // namespace
+
+hipError_t launch_pack(const void *W, const void *s, int N, int K, void *Wq, void *scales,
+                       void *zeros, unsigned *status, hipStream_t stream) {
+  const long long tiles = (long long)(N / kTileRows) * (K / kGroup);
+  const long long blocks = (tiles + 3) / 4;
+  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     (const _Float16 *)W, (const _Float16 *)s, N, K, (u32x4 *)Wq,
+                     (_Float16 *)scales, (_Float16 *)zeros, status);
+  return hipGetLastError();
+}
+
+}  // namespace w4a16

@@ -1,0 +1,65 @@
+// Device-side helpers shared by the packer and the two GEMM kernels.
+//
+// Packed code tile (16 rows x 128 columns, 1024 bytes): lane L = 16c + r owns
+// 16 bytes, i.e. four 32-bit words; word t holds the eight codes of columns
+// 32t + 8c + j (j = 0..7) of row r, column j sitting in the 4-bit slot i with
+// j = 2*(i % 4) + i / 4.  So the masks 0x000F000F, after shifting the word
+// right by 4p, select exactly the pair of columns (2p, 2p+1) as the low and
+// high halves of a 32-bit register.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4a16 {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+
+constexpr int kGroup = 128;
+constexpr int kTileRows = 16;
+constexpr int kTileBytes = 1024;
+constexpr int kWave = 64;
+
+// fp16 bit pattern 0x6400 is 1024.0; OR-ing a 4-bit code q into its low
+// mantissa bits gives the fp16 value 1024 + q exactly (the ulp at 1024 is 1).
+constexpr uint32_t kMagic2 = 0x64006400u;
+
+__device__ __forceinline__ half2v as_half2(uint32_t v) { return __builtin_bit_cast(half2v, v); }
+
+// Packed pair (1024 + z, 1024 + z) for an integer-valued fp16 zero point z.
+__device__ __forceinline__ half2v zero_bias(_Float16 z) {
+  _Float16 b = (_Float16)1024.0f + z;   // exact: z is an integer in 0..15
+  half2v r = {b, b};
+  return r;
+}
+
+// Eight codes of one word -> the eight exact fp16 values (q_j - z), j = 0..7.
+// (1024 + q) - (1024 + z) is an exact fp16 subtraction of two integers.
+__device__ __forceinline__ half8 decode_word(uint32_t w, half2v bias) {
+  half2v p0 = as_half2((w & 0x000F000Fu) | kMagic2) - bias;
+  half2v p1 = as_half2(((w >> 4) & 0x000F000Fu) | kMagic2) - bias;
+  half2v p2 = as_half2(((w >> 8) & 0x000F000Fu) | kMagic2) - bias;
+  half2v p3 = as_half2(((w >> 12) & 0x000F000Fu) | kMagic2) - bias;
+  half8 r = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+  return r;
+}
+
+__device__ __forceinline__ half8 load_half8(const _Float16 *p) {
+  return *reinterpret_cast<const half8 *>(p);
+}
+
+__device__ __forceinline__ half8 zero_half8() {
+  half8 z = {0, 0, 0, 0, 0, 0, 0, 0};
+  return z;
+}
+
+// D += A . B for one 16x16x32 fp16 MFMA with fp32 accumulation.  Lane l
+// supplies A[l % 16][8(l/16) .. 8(l/16)+7] and B[8(l/16) .. +7][l % 16] and
+// receives D[4(l/16) + v][l % 16], v = 0..3.
+__device__ __forceinline__ float4v mfma16(half8 a, half8 b, float4v c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+}  // namespace w4a16
