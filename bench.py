@@ -2,19 +2,24 @@
 
 One step = the seven dequantize-matmuls of a Llama-3-8B-shaped decoder layer at
 decode batch M = 1 (q, k, v, o: 4096 -> 4096/1024; gate, up: 4096 -> 14336;
-down: 14336 -> 4096), group 128, AWQ scale s, each launched through the C ABI on
-torch's current stream.  Inputs are resident in HBM before timing starts; the
-packed weights rotate over enough layer copies (>= 1 GiB) that each step reads
-weights from HBM rather than from the 256 MB last-level cache.
+down: 14336 -> 4096), group 128, AWQ scale s, each with its own seeded input.
+The seven problems are independent here, so the step is ONE grouped launch
+through the C ABI (w4a16_gemm_grouped) on torch's current stream.  Inputs are
+resident in HBM before timing starts; the packed weights rotate over enough
+layer copies (>= 1 GiB) that each step streams its weights from HBM rather
+than from the 256 MB last-level cache.
 
-Printed JSON line (rank 0):
-  value      aggregate HBM throughput of the step: algorithmic bytes per step
-             (packed codes + fp16 scales/zeros + s + X + Y) / wall time per step;
-  roofline   the dominant kernel's achieved bandwidth: its algorithmic bytes per
-             launch / its average launch duration from HIP events recorded on the
-             launch stream around every launch of the timed region;
-  prefill    the 70B-shaped layer at M = 4096 (compute-bound): TFLOP/s against
-             the dense fp16 MFMA peak, same method;
+Printed JSON line:
+  value         algorithmic bytes per step (packed codes + fp16 scales/zeros + s
+                + X + Y) / wall time per step, in TB/s;
+  roofline      the step's kernel (one launch per step): its algorithmic bytes /
+                its average duration, from HIP events recorded on the launch
+                stream around every launch of the timed region;
+  layer_variants  the same layer as 4 launches in a real layer's dependency
+                order ([q,k,v], [o], [gate,up], [down]) and as 7 separate
+                launches, timed the same way (context for the headline);
+  prefill       the 70B-shaped layer at M = 4096 (compute-bound): TFLOP/s
+                against the dense fp16 MFMA peak;
   cpu_baseline  the fp64 CPU oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -38,8 +43,12 @@ def alg_bytes(M, N, K, awq):
     return N * K // 2 + 4 * N * K // 128 + (2 * K if awq else 0) + 2 * M * K + 2 * M * N
 
 
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def prepare_layer(cfg, M, torch, w4, workloads, copies_min_bytes=POOL_BYTES):
-    """Pack every matrix of a configuration once on the GPU; replicate the packed
+    """Pack every matrix of a configuration once on the GPU, and replicate the packed
     buffers into enough copies to cover `copies_min_bytes`."""
     mats = []
     for mi, mat in enumerate(cfg.matrices):
@@ -56,91 +65,58 @@ def prepare_layer(cfg, M, torch, w4, workloads, copies_min_bytes=POOL_BYTES):
         mats.append(dict(name=mat.name, N=mat.N, K=mat.K, pw=pw, s=sd, X=X, Y=Y,
                          bytes=alg_bytes(M, mat.N, mat.K, sd is not None),
                          flops=2 * M * mat.N * mat.K))
-    layer_w = sum(m["pw"].wq.numel() + 2 * m["pw"].scales.numel() * 2 for m in mats)
+    layer_w = sum(m["pw"].wq.numel() + 4 * m["pw"].scales.numel() for m in mats)
     copies = max(1, -(-copies_min_bytes // layer_w))
-    pool = []
-    for _ in range(copies):
-        pool.append([w4.PackedWeight(m["pw"].wq.clone(), m["pw"].scales.clone(),
-                                     m["pw"].zeros.clone(), m["N"], m["K"]) for m in mats])
+    pool = [[m["pw"]] for m in mats] if copies == 1 else None
+    if copies > 1:
+        pool = [[w4.PackedWeight(m["pw"].wq.clone(), m["pw"].scales.clone(),
+                                 m["pw"].zeros.clone(), m["N"], m["K"]) for _ in range(copies)]
+                for m in mats]
     torch.cuda.synchronize()
-    return mats, pool, layer_w
+    return mats, pool, layer_w, copies
 
 
-def timed_steps(mats, pool, steps, warmup, torch, w4, per_launch_events=True):
-    """Run warmup + steps; return (wall seconds, per-matrix list of launch ms)."""
+def make_calls(mats, pool, copies, groups, w4):
+    """For every layer copy, one prepared grouped call per group of matrix indices."""
+    return [[w4.GroupedCall([(mats[j]["X"], pool[j][c], mats[j]["s"], mats[j]["Y"])
+                             for j in grp]) for grp in groups] for c in range(copies)]
+
+
+def timed(calls, steps, warmup, torch):
+    """Warm up, then run `steps` steps (step i uses copy i % copies); every launch is
+    bracketed by HIP events on the launch stream.  Returns (wall s, launch ms [launch][step])."""
     stream = torch.cuda.current_stream()
-
-    def step(i, evs=None):
-        layer = pool[i % len(pool)]
-        for j, m in enumerate(mats):
-            if evs is not None:
-                evs[j][0].record(stream)
-            w4.w4a16_gemm(m["X"], layer[j], m["s"], out=m["Y"])
-            if evs is not None:
-                evs[j][1].record(stream)
-
+    nl = len(calls[0])
     for i in range(warmup):
-        step(i)
-    events = []
-    if per_launch_events:
-        events = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-                   for _ in mats] for _ in range(steps)]
+        for call in calls[i % len(calls)]:
+            call()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(nl)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        step(warmup + i, events[i] if per_launch_events else None)
+        for j, call in enumerate(calls[(warmup + i) % len(calls)]):
+            ev[i][j][0].record(stream)
+            call()
+            ev[i][j][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    launch_ms = [[ev[j][0].elapsed_time(ev[j][1]) for ev in events] for j in range(len(mats))]
-    return wall, launch_ms
+    return wall, [[ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(steps)] for j in range(nl)]
 
 
-def kernel_groups(mats, M, w4):
-    """Group the launches by the kernel instance they run (same kernel name in a trace)."""
-    groups = {}
-    for j, m in enumerate(mats):
-        path = w4.w4a16_select_path(M, m["N"], m["K"])
-        if path == w4.PATH_SKINNY:
-            chunks = (m["K"] // 128 + 3) // 4
-            waves = 2 if chunks <= 2 else 4 if chunks <= 4 else 8 if chunks <= 8 else 16
-            name = f"skinny_kernel<{waves},4>"
-        else:
-            name = "tiled_kernel"
-        groups.setdefault(name, []).append(j)
-    return groups
-
-
-def roofline_of(mats, launch_ms, groups, bound):
-    """The dominant kernel instance (largest share of the step's launch time)."""
-    best = None
-    for name, idx in groups.items():
-        tot_ms = sum(sum(launch_ms[j]) for j in idx)
-        n_launch = sum(len(launch_ms[j]) for j in idx)
-        if best is None or tot_ms > best[1]:
-            best = (name, tot_ms, n_launch, idx)
-    name, tot_ms, n_launch, idx = best
-    avg_ms = tot_ms / n_launch
-    per_launch = sum(mats[j]["bytes" if bound == "hbm" else "flops"] for j in idx) / len(idx)
-    if bound == "hbm":
-        achieved = per_launch / (avg_ms * 1e-3) / 1e9
-        peak, unit = HBM_PEAK_GBS, "GB/s"
+def variant(mats, groups, launch_ms, steps, wall, unit_key):
+    step_units = sum(m[unit_key] for m in mats)
+    kern = sum(float(np.mean(x)) for x in launch_ms)  # ms of kernel time per step
+    out = {"launches_per_step": len(groups), "ms_per_step": round(wall / steps * 1e3, 5),
+           "kernel_ms_per_step": round(kern, 5)}
+    if unit_key == "bytes":
+        out["TB/s"] = round(step_units / (wall / steps) / 1e12, 4)
+        out["kernel_TB/s"] = round(step_units / (kern * 1e-3) / 1e12, 4)
     else:
-        achieved = per_launch / (avg_ms * 1e-3) / 1e12
-        peak, unit = FP16_PEAK_TFLOPS, "TFLOP/s"
-    return {"bound": bound, "kernel": name, "launches_per_step": len(idx),
-            "avg_launch_us": round(avg_ms * 1e3, 3), "per_launch": per_launch,
-            "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-            "frac": round(achieved / peak, 4), "traffic": None}
-
-
-def per_matrix(mats, launch_ms, bound):
-    out = {}
-    for j, m in enumerate(mats):
-        ms = float(np.median(launch_ms[j]))
-        if bound == "hbm":
-            out[m["name"]] = {"us": round(ms * 1e3, 2), "TB/s": round(m["bytes"] / ms / 1e9, 3)}
-        else:
-            out[m["name"]] = {"us": round(ms * 1e3, 2), "TFLOP/s": round(m["flops"] / ms / 1e9, 1)}
+        out["TFLOP/s"] = round(step_units / (wall / steps) / 1e12, 2)
+    out["launches"] = [{"matrices": [mats[j]["name"] for j in grp],
+                        "us": round(float(np.median(launch_ms[i])) * 1e3, 2)}
+                       for i, grp in enumerate(groups)]
     return out
 
 
@@ -172,8 +148,8 @@ def cpu_baseline(cfg, M, workloads, rows=1024, budget_s=10.0):
         dt = time.perf_counter() - t0
         if dt >= budget_s:
             break
-    return {"value": byts / dt / 1e12, "unit": "TB/s", "cores": int(threads), "kind": "oracle",
-            "seconds": round(dt, 2),
+    return {"value": float(f"{byts / dt / 1e12:.6g}"), "unit": "TB/s", "cores": int(threads),
+            "kind": "oracle", "seconds": round(dt, 2),
             "sample": f"first {rows} rows of each of the {len(cfg.matrices)} matrices of "
                       f"{cfg.name} at M={M}, oracle.gemm (fp64 dequantize + matmul) "
                       f"repeated {reps}x"}
@@ -182,11 +158,11 @@ def cpu_baseline(cfg, M, workloads, rows=1024, budget_s=10.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="llama3_8b_decode")
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -202,58 +178,74 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     w4.lib()  # fail loudly if the HIP library is missing
-    cfg = workloads.config_by_name(args.workload)
+    cfg = workloads.config_by_name("llama3_8b_decode")
     M = cfg.Ms[0]
-    print(f"[bench] preparing {cfg.name} M={M}", file=sys.stderr, flush=True)
-    mats, pool, layer_w = prepare_layer(cfg, M, torch, w4, workloads)
+    log(f"preparing {cfg.name} M={M}")
+    mats, pool, layer_w, copies = prepare_layer(cfg, M, torch, w4, workloads)
     step_bytes = sum(m["bytes"] for m in mats)
-    print(f"[bench] {len(pool)} layer copies, {layer_w * len(pool) / 2**30:.2f} GiB of packed "
-          f"weights; timing {args.steps} steps", file=sys.stderr, flush=True)
-    wall, launch_ms = timed_steps(mats, pool, args.steps, args.warmup, torch, w4)
+    names = [m["name"] for m in mats]
+    one = [list(range(len(mats)))]
+    log(f"{copies} layer copies, {layer_w * copies / 2**30:.2f} GiB of packed weights; "
+        f"timing {args.steps} steps")
+    wall, lms = timed(make_calls(mats, pool, copies, one, w4), args.steps, args.warmup, torch)
     ms_per_step = wall / args.steps * 1e3
-    value = step_bytes / (ms_per_step * 1e-3) / 1e12
-    roof = roofline_of(mats, launch_ms, kernel_groups(mats, M, w4), "hbm")
-
+    avg_ms = float(np.mean(lms[0]))
+    achieved = step_bytes / (avg_ms * 1e-3) / 1e9
     out = {
-        "metric": METRIC, "value": round(value, 4), "unit": "TB/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp16",
-        "data": "synthetic",
-        "config": {"workload": f"{cfg.name}: Llama-3-8B-shaped decoder layer (7 matrices), "
-                               f"M={M}, group 128, AWQ s, asym uint4 + fp16 scale/zero",
-                   "M": M, "step_bytes": step_bytes, "weight_copies": len(pool),
+        "metric": METRIC, "value": round(step_bytes / (ms_per_step * 1e-3) / 1e12, 4),
+        "unit": "TB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp16", "data": "synthetic",
+        "config": {"workload": "llama3_8b_decode_layer: the 7 matrices of a Llama-3-8B-shaped "
+                               "decoder layer, M=1, group 128, AWQ s, asym uint4 + fp16 "
+                               "scale/zero, one grouped launch per step",
+                   "M": M, "step_bytes": step_bytes, "weight_copies": copies,
                    "parallelism": "single GPU"},
-        "roofline": roof,
-        "per_matrix": per_matrix(mats, launch_ms, "hbm"),
-        "layer_kernel_TBps": round(step_bytes / (sum(sum(x) for x in launch_ms) /
-                                                 args.steps * 1e-3) / 1e12, 4),
+        "roofline": {"bound": "hbm", "kernel": "skinny_kernel (grouped, 7 problems)",
+                     "avg_launch_us": round(avg_ms * 1e3, 3), "per_launch_bytes": step_bytes,
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
     }
+    if not args.no_variants:
+        idx = {n: i for i, n in enumerate(names)}
+        dep = [[idx["q"], idx["k"], idx["v"]], [idx["o"]], [idx["gate"], idx["up"]], [idx["down"]]]
+        sep = [[j] for j in range(len(mats))]
+        vs = {}
+        for label, groups in (("dependency_order_4_launches", dep), ("separate_7_launches", sep)):
+            w, l = timed(make_calls(mats, pool, copies, groups, w4), 200, 20, torch)
+            vs[label] = variant(mats, groups, l, 200, w, "bytes")
+        out["layer_variants"] = vs
     del pool, mats
     torch.cuda.empty_cache()
 
     if not args.no_prefill:
         pcfg = workloads.config_by_name("llama_70b_prefill")
         PM = pcfg.Ms[0]
-        print(f"[bench] preparing {pcfg.name} M={PM}", file=sys.stderr, flush=True)
-        pmats, ppool, _ = prepare_layer(pcfg, PM, torch, w4, workloads, copies_min_bytes=0)
-        pwall, pms = timed_steps(pmats, ppool, args.prefill_steps, 2, torch, w4)
+        log(f"preparing {pcfg.name} M={PM}")
+        pmats, ppool, _, pc = prepare_layer(pcfg, PM, torch, w4, workloads, copies_min_bytes=0)
+        groups = [[j] for j in range(len(pmats))]
+        pwall, pms = timed(make_calls(pmats, ppool, pc, groups, w4), args.prefill_steps, 2, torch)
         flops = sum(m["flops"] for m in pmats)
-        pstep = pwall / args.prefill_steps
+        tot_ms = sum(float(np.mean(x)) for x in pms)
         out["prefill"] = {
-            "workload": f"{pcfg.name}: 70B-shaped layer (7 matrices), M={PM}, AWQ s, "
-                        "1% activation channels x20",
-            "TFLOP/s": round(flops / pstep / 1e12, 2), "ms_per_step": round(pstep * 1e3, 4),
-            "frac_of_fp16_peak": round(flops / pstep / 1e12 / FP16_PEAK_TFLOPS, 4),
-            "roofline": roofline_of(pmats, pms, kernel_groups(pmats, PM, w4), "mfma"),
-            "per_matrix": per_matrix(pmats, pms, "mfma"),
+            "workload": f"{pcfg.name}: the 7 matrices of a 70B-shaped layer, M={PM}, AWQ s, "
+                        "1% activation channels x20, one launch per matrix",
+            "TFLOP/s": round(flops / (pwall / args.prefill_steps) / 1e12, 2),
+            "ms_per_step": round(pwall / args.prefill_steps * 1e3, 4),
+            "roofline": {"bound": "mfma", "kernel": "tiled_kernel",
+                         "avg_launch_us": round(tot_ms / len(pmats) * 1e3, 2),
+                         "achieved": round(flops / (tot_ms * 1e-3) / 1e12, 2),
+                         "peak": FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(flops / (tot_ms * 1e-3) / 1e12 / FP16_PEAK_TFLOPS, 4),
+                         "traffic": None},
+            "per_matrix": variant(pmats, groups, pms, args.prefill_steps, pwall, "flops")["launches"],
         }
         del ppool, pmats
         torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        log("timing the CPU oracle")
         out["cpu_baseline"] = cpu_baseline(cfg, M, workloads)
-        out["cpu_baseline"]["value"] = float(f"{out['cpu_baseline']['value']:.6g}")
     print(json.dumps(out), flush=True)
 
 

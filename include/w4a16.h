@@ -31,7 +31,8 @@
  *
  * Shapes: W is [N][K] (output x input features, like a linear layer's
  * weight), X is [M][K], Y = X . W_hat^T is [M][N].  K must be a multiple of
- * 128 and N a multiple of 16.  fp16 means IEEE binary16.
+ * 128, N a multiple of 16, N and K at most 2^24, and the packed codes of one
+ * matrix (N*K/2 bytes) under 2 GiB - 1 MiB.  fp16 means IEEE binary16.
  *
  * Packed layout (this library's own; the pages only fix the content):
  *  - Wq: N*K/2 bytes.  Tile (b, g) covers rows 16b..16b+15 and the 128
@@ -43,7 +44,11 @@
  *    One 64-lane wave therefore reads a whole tile with one 128-bit load per
  *    lane, and word t of a lane is exactly that lane's B operand of a
  *    16x16x32 fp16 MFMA.
- *  - scales, zeros: fp16 row-major [N][G] (element n*G + g).
+ *  - scales, zeros: fp16, in quads of 4 groups.  With Gq = ceil(G / 4), the
+ *    value of row n = 16b + r and group g = 4u + i is element
+ *    ((b*Gq + u)*16 + r)*4 + i; each buffer holds N*4*Gq elements, and the
+ *    slots of groups G..4*Gq-1 are zero.  The metadata of one 16-row block
+ *    and 4 consecutive groups is thus one contiguous 128-byte run.
  *
  * Ownership and streams: the caller allocates and owns every buffer (device
  * memory unless noted) and passes a hipStream_t as `stream` (NULL = the null
@@ -86,7 +91,8 @@ enum {
 };
 
 /* Byte sizes of the three packed buffers of an [N][K] weight (host outputs).
- * wq = N*K/2, scales = zeros = 2*N*(K/128).  EINVAL on bad shapes or NULL. */
+ * wq = N*K/2, scales = zeros = 2*N*4*ceil(K/512).  EINVAL on bad shapes or
+ * NULL. */
 int w4a16_packed_sizes(int64_t N, int64_t K, size_t *wq_bytes, size_t *scales_bytes,
                        size_t *zeros_bytes);
 
@@ -110,6 +116,28 @@ int w4a16_gemm(const void *X, const void *Wq, const void *scales, const void *ze
 int w4a16_gemm_path(const void *X, const void *Wq, const void *scales, const void *zeros,
                     const void *s, void *Y, int64_t M, int64_t N, int64_t K, int path,
                     void *stream);
+
+/* One independent dequantize-matmul of a grouped call; fields as in
+ * w4a16_gemm (device pointers; s may be NULL; M may be 0). */
+typedef struct w4a16_problem {
+  const void *X;
+  const void *Wq;
+  const void *scales;
+  const void *zeros;
+  const void *s;
+  void *Y;
+  int64_t M, N, K;
+} w4a16_problem;
+
+/* Several independent dequantize-matmuls, each computed exactly as
+ * w4a16_gemm computes it, in as few launches as possible: problems that the
+ * M-dispatch sends to the streaming kernel (small M) share one launch, up to
+ * 8 problems per launch, so a layer's small projections ride along with its
+ * large ones; the others get a launch each.  `problems` is a host array of
+ * `count` entries (count 0 is a no-op).  Every problem is validated first; on
+ * an error nothing is launched.  Outputs must not overlap each other or any
+ * input.  Asynchronous on `stream`. */
+int w4a16_gemm_grouped(const w4a16_problem *problems, int count, void *stream);
 
 /* Which path AUTO takes for this shape (host only; no GPU call). */
 int w4a16_select_path(int64_t M, int64_t N, int64_t K);

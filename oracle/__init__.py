@@ -41,14 +41,15 @@ rationals, integer special case); see tests/test_oracle_*.py.
 """
 from .quantizer import (GROUP, QMAX, NonFiniteInput, OracleError, QuantResult, ScaleOverflow,
                        quantize, round_up_fp16)
-from .layout import (TILE_BYTES, TILE_ROWS, meta_index, nibble_address, pack_codes, pack_meta,
-                     unpack_codes, unpack_meta)
+from .layout import (META_QUAD, TILE_BYTES, TILE_ROWS, meta_groups, meta_index, nibble_address,
+                     pack_codes, pack_meta, unpack_codes, unpack_meta)
 from .matmul import dequantize, gemm
 from . import accounting, exact
 
 __all__ = [
     "GROUP", "QMAX", "NonFiniteInput", "OracleError", "QuantResult", "ScaleOverflow",
-    "quantize", "round_up_fp16", "TILE_BYTES", "TILE_ROWS", "meta_index", "nibble_address",
+    "quantize", "round_up_fp16", "META_QUAD", "TILE_BYTES", "TILE_ROWS", "meta_groups",
+    "meta_index", "nibble_address",
     "pack_codes", "pack_meta", "unpack_codes", "unpack_meta", "dequantize", "gemm",
     "accounting", "exact",
 ]

@@ -27,8 +27,9 @@ def int4_group_bytes(params: int, group: int = 128, meta_bits: int = 32) -> Frac
 
 
 def packed_sizes(N: int, K: int) -> tuple:
-    """(code bytes, scale bytes, zero-point bytes) of one packed [N][K] matrix."""
+    """(code bytes, scale bytes, zero-point bytes) of one packed [N][K] matrix; the
+    metadata holds the groups of a row rounded up to a multiple of 4."""
     if N % 16 or K % 128:
         raise ValueError("N must be a multiple of 16 and K of 128")
-    groups = N * (K // 128)
+    groups = N * (-(-(K // 128) // 4) * 4)
     return N * K // 2, 2 * groups, 2 * groups

@@ -17,9 +17,12 @@ Definition.  W is [N][K]; G = K / 128 groups per row; N is a multiple of 16.
   * Inside a word, the 4-bit slot i (bits 4i .. 4i+3) holds column
     j = 2 * (i % 4) + i // 4: even j in the low half-word, odd j in the high
     half-word, each in increasing order.
-  * Scales and zero points (fp16 each) are plain row-major [N][G] arrays: the
-    value of row n, group g is element n * G + g of its buffer, so one output
-    row's metadata is contiguous and can be fetched with one wide load.
+  * Scales and zero points (fp16 each) are stored in quads of 4 groups:
+    with Gq = ceil(G / 4), the value of row n = 16b + r, group g = 4u + i is
+    element ((b * Gq + u) * 16 + r) * 4 + i of its buffer (N * 4 * Gq
+    elements; the slots of groups G .. 4*Gq - 1 hold zero).  So the metadata
+    of one 16-row block and 4 consecutive groups is one contiguous 128-byte
+    run: a single 8-byte load per row fetches 4 groups.
 TEST INFRASTRUCTURE: see the package docstring for who may import this.
 """
 from __future__ import annotations
@@ -28,6 +31,7 @@ import numpy as np
 
 TILE_ROWS = 16
 TILE_BYTES = 1024
+META_QUAD = 4
 _GROUP = 128
 
 
@@ -78,29 +82,40 @@ def unpack_codes(buf: np.ndarray, N: int, K: int) -> np.ndarray:
     return ((buf[byte] >> shift.astype(np.uint8)) & 0xF).astype(np.uint8).reshape(N, K)
 
 
+def meta_groups(K: int) -> int:
+    """Groups per row in the metadata buffers: G rounded up to a multiple of 4."""
+    G = K // _GROUP
+    return -(-G // META_QUAD) * META_QUAD
+
+
 def meta_index(n, g, N: int, K: int):
     """Element index of (row n, group g) in the scale / zero-point buffers."""
-    G = _check(N, K)
+    _check(N, K)
+    Gq = meta_groups(K) // META_QUAD
     n = np.asarray(n, dtype=np.int64)
     g = np.asarray(g, dtype=np.int64)
-    return n * G + g
+    b, r = n // TILE_ROWS, n % TILE_ROWS
+    u, i = g // META_QUAD, g % META_QUAD
+    return ((b * Gq + u) * TILE_ROWS + r) * META_QUAD + i
 
 
 def pack_meta(a: np.ndarray) -> np.ndarray:
-    """Per-group array a[N][G] (fp16) -> flat fp16 buffer in tile order."""
+    """Per-group array a[N][G] (fp16) -> flat buffer of N * meta_groups(K) elements."""
     a = np.asarray(a)
     N, G = a.shape
+    K = G * _GROUP
     nn, gg = np.meshgrid(np.arange(N), np.arange(G), indexing="ij")
-    out = np.empty(N * G, dtype=a.dtype)
-    out[meta_index(nn.ravel(), gg.ravel(), N, G * _GROUP)] = a.ravel()
+    out = np.zeros(N * meta_groups(K), dtype=a.dtype)
+    out[meta_index(nn.ravel(), gg.ravel(), N, K)] = a.ravel()
     return out
 
 
 def unpack_meta(buf: np.ndarray, N: int, K: int) -> np.ndarray:
-    """Flat tile-order buffer -> a[N][G]."""
-    G = _check(N, K)
+    """Flat metadata buffer -> a[N][G]."""
+    _check(N, K)
+    G = K // _GROUP
     buf = np.asarray(buf).ravel()
-    if buf.size != N * G:
+    if buf.size != N * meta_groups(K):
         raise ValueError("buffer size mismatch")
     nn, gg = np.meshgrid(np.arange(N), np.arange(G), indexing="ij")
     return buf[meta_index(nn.ravel(), gg.ravel(), N, K)].reshape(N, G)

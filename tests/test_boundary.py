@@ -12,6 +12,7 @@ import pytest
 from tests.conftest import ROOT
 
 import weight_only_int4_group_amd as w4
+from oracle.accounting import packed_sizes as oracle_sizes
 
 HEADER = os.path.join(ROOT, "include", "w4a16.h")
 V = ctypes.c_void_p
@@ -52,11 +53,12 @@ def test_status_codes_match_header():
                                  (18944, 3584), (28672, 8192)])
 def test_packed_sizes(N, K):
     wq, sc, z = w4.w4a16_packed_sizes(N, K)
-    assert wq == N * K // 2 and sc == z == 2 * N * (K // 128)
+    assert (wq, sc, z) == oracle_sizes(N, K)
+    assert wq == N * K // 2 and sc == z == 2 * N * (-(-(K // 128) // 4) * 4)
 
 
 @pytest.mark.parametrize("N,K", [(0, 128), (16, 0), (8, 128), (16, 64), (17, 128), (16, 200),
-                                 (-16, 128), (1 << 25, 128)])
+                                 (-16, 128), (1 << 25, 128), (65536, 65536)])
 def test_packed_sizes_rejects(N, K):
     with pytest.raises(w4.W4A16Error) as e:
         w4.w4a16_packed_sizes(N, K)
@@ -105,3 +107,19 @@ def test_select_path():
         assert sel(M, 4096, 4096) == w4.PATH_SKINNY
     for M in (64, 256, 4096):
         assert sel(M, 4096, 4096) == w4.PATH_TILED
+
+
+def test_grouped_validation():
+    L = w4.lib()
+    assert L.w4a16_gemm_grouped(None, 0, None) == 0          # nothing to do
+    assert L.w4a16_gemm_grouped(None, 2, None) == -1         # NULL array
+    assert L.w4a16_gemm_grouped(None, -1, None) == -1
+    good = w4.Problem(A16, A16, A16, A16, None, A16, 0, 16, 128)   # M = 0: valid no-op
+    bad_k = w4.Problem(A16, A16, A16, A16, None, A16, 1, 16, 100)
+    bad_al = w4.Problem(ODD, A16, A16, A16, None, A16, 1, 16, 128)
+    arr = (w4.Problem * 3)(good, good, good)
+    assert L.w4a16_gemm_grouped(arr, 3, None) == 0           # all empty: no HIP call
+    arr = (w4.Problem * 3)(good, bad_k, good)
+    assert L.w4a16_gemm_grouped(arr, 3, None) == -1
+    arr = (w4.Problem * 2)(bad_al, good)
+    assert L.w4a16_gemm_grouped(arr, 2, None) == -2

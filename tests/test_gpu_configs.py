@@ -63,8 +63,13 @@ def test_config_matrix(ci, mi):
         qb = ref.q[16 * j:16 * j + 16]
         assert np.array_equal(wq[b * G * 1024:(b + 1) * G * 1024], oracle.pack_codes(qb)), \
             f"packed codes differ in row block {b}"
-    assert np.array_equal(h16_bits(sc[rows]), h16_bits(ref.scales))
-    assert np.array_equal(h16_bits(zr[rows]), h16_bits(ref.zeros))
+    assert np.array_equal(h16_bits(oracle.unpack_meta(sc, N, K)[rows]), h16_bits(ref.scales))
+    assert np.array_equal(h16_bits(oracle.unpack_meta(zr, N, K)[rows]), h16_bits(ref.zeros))
+    Gm = oracle.meta_groups(K)
+    for b in blocks:   # whole metadata blocks of the sampled row blocks, padding included
+        lo, hi = b * 16 * Gm, (b + 1) * 16 * Gm
+        refb = oracle.pack_meta(ref.scales[16 * blocks.index(b):16 * blocks.index(b) + 16])
+        assert np.array_equal(h16_bits(sc[lo:hi]), h16_bits(refb))
 
     for M in cfg.Ms:
         note(f"config {cfg.name} matrix {mat.name} M={M}: gemm "

@@ -130,3 +130,29 @@ def test_empty_batch():
     X = torch.empty((0, 640), dtype=torch.float16, device="cuda")
     Y = w4.w4a16_gemm(X, pw)
     assert tuple(Y.shape) == (0, 272)
+
+
+def test_grouped_matches_single_calls_and_oracle():
+    """One grouped call over problems of mixed shapes, M (including 0 and a tiled-path M)
+    and AWQ scales: each output equals the single-call output bit for bit and the oracle
+    within tolerance.  Nine streaming problems take two launches of the kernel."""
+    torch_cuda()
+    cases = [(1, 272, 640, True), (1, 16, 128, False), (5, 528, 1152, True), (0, 64, 256, False),
+             (40, 272, 640, False), (16, 1024, 4096, True), (3, 48, 384, False),
+             (9, 128, 1280, True), (2, 64, 14336, True), (1, 32, 256, False), (7, 80, 512, True)]
+    items, refs = [], []
+    for i, (M, N, K, awq) in enumerate(cases):
+        pw, s, ref = packed_case(N, K, awq, key=8, mat=i)
+        X = activations(8, i, M, K)
+        sd = None if s is None else to_dev(s)
+        items.append((to_dev(X), pw, sd))
+        refs.append(oracle.gemm(X, ref.q, ref.scales, ref.zeros, s))
+    note(f"grouped call over {len(cases)} problems")
+    Ys = [to_host(y) for y in w4.w4a16_gemm_grouped(items)]
+    for (M, N, K, _), (Xd, pw, sd), Y, Yref in zip(cases, items, Ys, refs):
+        assert Y.shape == (M, N)
+        if M == 0:
+            continue
+        assert_close(Y, Yref, f"grouped {M}x{N}x{K}")
+        single = to_host(w4.w4a16_gemm(Xd, pw, sd))
+        assert np.array_equal(Y.view(np.uint16), single.view(np.uint16)), f"{M}x{N}x{K}"

@@ -20,8 +20,8 @@ def check_exact(W, s, tag):
     note(f"pack {tag} N={W.shape[0]} K={W.shape[1]} awq={s is not None}")
     wq, sc, z = gpu_pack(W, s)
     ref = oracle.quantize(W, s)
-    assert np.array_equal(h16_bits(sc), h16_bits(oracle.pack_meta(ref.scales)).reshape(sc.shape)), tag
-    assert np.array_equal(h16_bits(z), h16_bits(oracle.pack_meta(ref.zeros)).reshape(z.shape)), tag
+    assert np.array_equal(h16_bits(sc), h16_bits(oracle.pack_meta(ref.scales))), tag
+    assert np.array_equal(h16_bits(z), h16_bits(oracle.pack_meta(ref.zeros))), tag
     assert np.array_equal(wq, oracle.pack_codes(ref.q)), tag
 
 
@@ -63,8 +63,8 @@ def test_pack_on_grid_exact():
                      rng.integers(-16, -8, size=(N, G)))
     W = ((q - z[:, :, None]) * scale[:, :, None]).reshape(N, K).astype(np.float16)
     wq, sc, zz = gpu_pack(W, None)
-    assert np.array_equal(sc.astype(np.float64), scale)
-    assert np.array_equal(zz.astype(np.int64), z)
+    assert np.array_equal(oracle.unpack_meta(sc, N, K).astype(np.float64), scale)
+    assert np.array_equal(oracle.unpack_meta(zz, N, K).astype(np.int64), z)
     assert np.array_equal(oracle.unpack_codes(wq, N, K), q.reshape(N, K).astype(np.uint8))
 
 

@@ -46,14 +46,23 @@ def test_layout_word_semantics():
 
 
 def test_meta_layout():
-    N, K = 48, 512
+    # G = 5 groups -> 8 slots per row (quads of 4, zero padded)
+    N, K = 48, 640
     G = K // 128
-    a = np.arange(N * G, dtype=np.float16).reshape(N, G)
+    a = (np.arange(N * G, dtype=np.float16) + 1).reshape(N, G)
     buf = oracle.pack_meta(a)
+    assert buf.size == N * 8 and oracle.meta_groups(K) == 8
     assert np.array_equal(oracle.unpack_meta(buf, N, K), a)
-    assert buf[oracle.meta_index(17, 2, N, K)] == a[17, 2]
-    assert int(oracle.meta_index(17, 2, N, K)) == 17 * G + 2
-    assert np.array_equal(buf, a.ravel())   # row-major: the identity on [N][G]
+    # hand-derived: row 17 = block 1, r 1; group 4 = quad 1, slot 0; Gq = 2
+    # index ((1 * 2 + 1) * 16 + 1) * 4 + 0 = 196
+    assert int(oracle.meta_index(17, 4, N, K)) == 196 and buf[196] == a[17, 4]
+    # row 5, group 2: ((0 * 2 + 0) * 16 + 5) * 4 + 2 = 22
+    assert int(oracle.meta_index(5, 2, N, K)) == 22
+    # padding slots (groups 5..7) are zero, and every real value appears once
+    assert np.count_nonzero(buf) == N * G
+    # one 16-row block x 4 groups is one contiguous run of 64 elements (128 bytes)
+    idx = oracle.meta_index(np.repeat(np.arange(16, 32), 4), np.tile(np.arange(4, 8), 16), N, K)
+    assert sorted(idx.tolist()) == list(range(idx.min(), idx.min() + 64))
 
 
 def test_layout_rejects_bad_shapes():

@@ -22,6 +22,7 @@ __all__ = [
     "W4A16Error", "PackedWeight", "GROUP", "PATH_AUTO", "PATH_SKINNY", "PATH_TILED", "lib",
     "w4a16_packed_sizes", "w4a16_quantize_pack", "w4a16_gemm", "w4a16_gemm_path",
     "w4a16_select_path", "w4a16_strerror", "w4a16_version", "EXPORTED_SYMBOLS",
+    "w4a16_gemm_grouped", "GroupedCall",
 ]
 
 GROUP = 128
@@ -29,7 +30,15 @@ PATH_AUTO, PATH_SKINNY, PATH_TILED = 0, 1, 2
 STATUS = {0: "W4A16_OK", -1: "W4A16_EINVAL", -2: "W4A16_EALIGN", -3: "W4A16_EUNSUPPORTED",
           -4: "W4A16_ENONFINITE", -5: "W4A16_ERANGE", -6: "W4A16_EHIP"}
 EXPORTED_SYMBOLS = ("w4a16_packed_sizes", "w4a16_quantize_pack", "w4a16_gemm",
-                    "w4a16_gemm_path", "w4a16_select_path", "w4a16_strerror", "w4a16_version")
+                    "w4a16_gemm_path", "w4a16_gemm_grouped", "w4a16_select_path",
+                    "w4a16_strerror", "w4a16_version")
+
+
+class Problem(ctypes.Structure):
+    """Mirror of the C struct w4a16_problem."""
+    _fields_ = [("X", ctypes.c_void_p), ("Wq", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("zeros", ctypes.c_void_p), ("s", ctypes.c_void_p), ("Y", ctypes.c_void_p),
+                ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64)]
 
 
 class W4A16Error(RuntimeError):
@@ -55,12 +64,13 @@ def lib() -> ctypes.CDLL:
     L.w4a16_quantize_pack.argtypes = [vp, vp, i64, i64, vp, vp, vp, vp]
     L.w4a16_gemm.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, vp]
     L.w4a16_gemm_path.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, vp]
+    L.w4a16_gemm_grouped.argtypes = [ctypes.POINTER(Problem), ctypes.c_int, vp]
     L.w4a16_select_path.argtypes = [i64, i64, i64]
     L.w4a16_strerror.argtypes = [ctypes.c_int]
     L.w4a16_strerror.restype = ctypes.c_char_p
     L.w4a16_version.argtypes = []
     for name in ("w4a16_packed_sizes", "w4a16_quantize_pack", "w4a16_gemm", "w4a16_gemm_path",
-                 "w4a16_select_path", "w4a16_version"):
+                 "w4a16_gemm_grouped", "w4a16_select_path", "w4a16_version"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -88,7 +98,8 @@ def w4a16_select_path(M: int, N: int, K: int) -> int:
 
 @dataclass
 class PackedWeight:
-    """Packed INT4 weight: codes (uint8, N*K/2 bytes) and fp16 [N][K/128] scales/zeros."""
+    """Packed INT4 weight: codes (uint8, N*K/2 bytes) and the fp16 scale and zero-point
+    buffers (flat, in the 4-group-quad layout of include/w4a16.h)."""
     wq: "object"
     scales: "object"
     zeros: "object"
@@ -129,8 +140,8 @@ def w4a16_quantize_pack(W, s=None, out: PackedWeight | None = None) -> PackedWei
     wq_b, sc_b, z_b = w4a16_packed_sizes(N, K)
     if out is None:
         out = PackedWeight(torch.empty(wq_b, dtype=torch.uint8, device=W.device),
-                           torch.empty((N, K // GROUP), dtype=torch.float16, device=W.device),
-                           torch.empty((N, K // GROUP), dtype=torch.float16, device=W.device),
+                           torch.empty(sc_b // 2, dtype=torch.float16, device=W.device),
+                           torch.empty(z_b // 2, dtype=torch.float16, device=W.device),
                            N, K)
     rc = lib().w4a16_quantize_pack(
         _dev_ptr(W, "W", torch.float16), _dev_ptr(s, "s", torch.float16, K), N, K,
@@ -164,3 +175,40 @@ def w4a16_gemm_path(X, pw: PackedWeight, s=None, path: int = PATH_AUTO, out=None
 
 def w4a16_gemm(X, pw: PackedWeight, s=None, out=None):
     return w4a16_gemm_path(X, pw, s, PATH_AUTO, out)
+
+
+class GroupedCall:
+    """A prepared w4a16_gemm_grouped call: the problem array is marshalled once, so
+    each call is a single C call on the current stream (for captured or repeated
+    launches over the same buffers).  Items are (X, PackedWeight, s or None, Y)."""
+
+    def __init__(self, items):
+        torch = _torch()
+        self.items = list(items)  # keep the tensors alive
+        self.array = (Problem * len(self.items))()
+        for i, (X, pw, s, Y) in enumerate(self.items):
+            if X.dim() != 2 or X.shape[1] != pw.K or tuple(Y.shape) != (X.shape[0], pw.N):
+                raise ValueError(f"problem {i}: X must be [M][K] and Y [M][N]")
+            self.array[i] = Problem(
+                _dev_ptr(X, "X", torch.float16), _dev_ptr(pw.wq, "wq", torch.uint8),
+                _dev_ptr(pw.scales, "scales", torch.float16),
+                _dev_ptr(pw.zeros, "zeros", torch.float16), _dev_ptr(s, "s", torch.float16, pw.K),
+                _dev_ptr(Y, "Y", torch.float16), X.shape[0], pw.N, pw.K)
+        self.device = self.items[0][0].device if self.items else None
+
+    def __call__(self):
+        if not self.items:
+            return
+        rc = lib().w4a16_gemm_grouped(self.array, len(self.items), _stream_handle(self.device))
+        if rc:
+            raise W4A16Error(rc, "w4a16_gemm_grouped")
+
+
+def w4a16_gemm_grouped(items):
+    """Several independent Y = X . dequant(pw)^T in as few launches as possible.
+    items: list of (X, PackedWeight, s or None); returns the list of Y tensors."""
+    torch = _torch()
+    full = [(X, pw, s, torch.empty((X.shape[0], pw.N), dtype=torch.float16, device=X.device))
+            for (X, pw, s) in items]
+    GroupedCall(full)()
+    return [it[3] for it in full]

@@ -4,12 +4,15 @@
 #include <vector>
 
 #include "../../include/w4a16.h"
+#include "w4a16_device.h"
 #include "w4a16_internal.h"
 
 namespace {
 
 constexpr int64_t kMaxDim = int64_t(1) << 24;  // rows / columns per operand
 constexpr int64_t kMaxM = int64_t(1) << 22;    // batch rows per call
+// Packed codes of one matrix are addressed with 32-bit byte offsets.
+constexpr int64_t kMaxPackedBytes = (int64_t(1) << 31) - (int64_t(1) << 20);
 
 // Largest M the streaming kernel takes in one pass (its A operand is 16 rows).
 constexpr int64_t kSkinnyMaxM = 16;
@@ -19,6 +22,7 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 int check_shape(int64_t N, int64_t K) {
   if (N <= 0 || K <= 0 || N > kMaxDim || K > kMaxDim) return W4A16_EINVAL;
   if (N % W4A16_TILE_ROWS || K % W4A16_GROUP) return W4A16_EINVAL;
+  if (N * K / 2 > kMaxPackedBytes) return W4A16_EINVAL;
   return W4A16_OK;
 }
 
@@ -65,7 +69,7 @@ int w4a16_packed_sizes(int64_t N, int64_t K, size_t *wq_bytes, size_t *scales_by
   const int rc = check_shape(N, K);
   if (rc) return rc;
   *wq_bytes = (size_t)N * (size_t)K / 2;
-  *scales_bytes = (size_t)N * (size_t)(K / W4A16_GROUP) * 2;
+  *scales_bytes = (size_t)N * (size_t)w4a16::meta_groups((int)(K / W4A16_GROUP)) * 2;
   *zeros_bytes = *scales_bytes;
   return W4A16_OK;
 }
@@ -99,33 +103,86 @@ int w4a16_select_path(int64_t M, int64_t N, int64_t K) {
   return M <= kSkinnyMaxM ? W4A16_PATH_SKINNY : W4A16_PATH_TILED;
 }
 
-int w4a16_gemm_path(const void *X, const void *Wq, const void *scales, const void *zeros,
-                    const void *s, void *Y, int64_t M, int64_t N, int64_t K, int path,
-                    void *stream) {
+}  // extern "C"
+
+namespace {
+
+int check_gemm(const void *X, const void *Wq, const void *scales, const void *zeros, const void *s,
+               const void *Y, int64_t M, int64_t N, int64_t K) {
   int rc = check_shape(N, K);
   if (rc) return rc;
   if (M < 0 || M > kMaxM) return W4A16_EINVAL;
-  if (path != W4A16_PATH_AUTO && path != W4A16_PATH_SKINNY && path != W4A16_PATH_TILED)
-    return W4A16_EUNSUPPORTED;
   if (M == 0) return W4A16_OK;  // empty batch: nothing to read or write
   if (!X || !Wq || !scales || !zeros || !Y) return W4A16_EINVAL;
   if (!aligned16(X) || !aligned16(Wq) || !aligned16(scales) || !aligned16(zeros) ||
       !aligned16(Y) || (s && !aligned16(s)))
     return W4A16_EALIGN;
+  return W4A16_OK;
+}
+
+// Streaming-kernel pieces of one problem: 16 rows of X per piece.
+void skinny_pieces(const w4a16_problem &p, std::vector<w4a16::SkinnyDesc> &out) {
+  for (int64_t m0 = 0; m0 < p.M; m0 += kSkinnyMaxM) {
+    const int64_t mb = (p.M - m0) < kSkinnyMaxM ? (p.M - m0) : kSkinnyMaxM;
+    out.push_back({static_cast<const _Float16 *>(p.X) + m0 * p.K, p.Wq, p.scales, p.zeros, p.s,
+                   static_cast<_Float16 *>(p.Y) + m0 * p.N, (int)mb, (int)p.N, (int)p.K});
+  }
+}
+
+hipError_t launch_pieces(const std::vector<w4a16::SkinnyDesc> &pieces, hipStream_t st) {
+  const int cap = w4a16::skinny_max_problems();
+  for (size_t i = 0; i < pieces.size(); i += cap) {
+    const int n = (int)((pieces.size() - i) < (size_t)cap ? (pieces.size() - i) : (size_t)cap);
+    const hipError_t err = w4a16::launch_skinny_set(pieces.data() + i, n, st);
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+int w4a16_gemm_path(const void *X, const void *Wq, const void *scales, const void *zeros,
+                    const void *s, void *Y, int64_t M, int64_t N, int64_t K, int path,
+                    void *stream) {
+  if (path != W4A16_PATH_AUTO && path != W4A16_PATH_SKINNY && path != W4A16_PATH_TILED)
+    return W4A16_EUNSUPPORTED;
+  const int rc = check_gemm(X, Wq, scales, zeros, s, Y, M, N, K);
+  if (rc || M == 0) return rc;
   if (path == W4A16_PATH_AUTO) path = w4a16_select_path(M, N, K);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t err = hipSuccess;
+  hipError_t err;
   if (path == W4A16_PATH_SKINNY) {
-    // the streaming kernel covers 16 rows of X per pass
-    for (int64_t m0 = 0; m0 < M && err == hipSuccess; m0 += kSkinnyMaxM) {
-      const int64_t mb = (M - m0) < kSkinnyMaxM ? (M - m0) : kSkinnyMaxM;
-      err = w4a16::launch_skinny(static_cast<const _Float16 *>(X) + m0 * K, Wq, scales, zeros, s,
-                                 static_cast<_Float16 *>(Y) + m0 * N, (int)mb, (int)N, (int)K, st);
-    }
+    std::vector<w4a16::SkinnyDesc> pieces;
+    skinny_pieces({X, Wq, scales, zeros, s, Y, M, N, K}, pieces);
+    err = launch_pieces(pieces, st);
   } else {
     err = w4a16::launch_tiled(X, Wq, scales, zeros, s, Y, (int)M, (int)N, (int)K, st);
   }
   return err == hipSuccess ? W4A16_OK : W4A16_EHIP;
+}
+
+int w4a16_gemm_grouped(const w4a16_problem *problems, int count, void *stream) {
+  if (count < 0 || (count > 0 && !problems)) return W4A16_EINVAL;
+  for (int i = 0; i < count; ++i) {
+    const w4a16_problem &p = problems[i];
+    const int rc = check_gemm(p.X, p.Wq, p.scales, p.zeros, p.s, p.Y, p.M, p.N, p.K);
+    if (rc) return rc;
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  std::vector<w4a16::SkinnyDesc> pieces;
+  for (int i = 0; i < count; ++i) {
+    const w4a16_problem &p = problems[i];
+    if (p.M == 0) continue;
+    if (w4a16_select_path(p.M, p.N, p.K) == W4A16_PATH_SKINNY) {
+      skinny_pieces(p, pieces);
+    } else if (w4a16::launch_tiled(p.X, p.Wq, p.scales, p.zeros, p.s, p.Y, (int)p.M, (int)p.N,
+                                   (int)p.K, st) != hipSuccess) {
+      return W4A16_EHIP;
+    }
+  }
+  return launch_pieces(pieces, st) == hipSuccess ? W4A16_OK : W4A16_EHIP;
 }
 
 int w4a16_gemm(const void *X, const void *Wq, const void *scales, const void *zeros,

@@ -14,7 +14,8 @@
 // of 16 rows).  Lane L = 16c + r reads the 32 values of row r that it will
 // own in the packed tile (columns 32t + 8c + j), so the group's min/max is a
 // reduction over the four lanes r, r+16, r+32, r+48 and the lane then writes
-// its 16 packed bytes directly.
+// its 16 packed bytes directly.  Lane r of octet 0 writes the row's scale and
+// zero point; the wave of a row's last group also zeroes its padding slots.
 #include "w4a16_device.h"
 #include "w4a16_internal.h"
 
@@ -103,7 +104,7 @@ __global__ __launch_bounds__(256) void pack_kernel(const _Float16 *__restrict__ 
     } else {
       scale = (double)sc16;
       z = rint(-mn / scale);
-      z16 = (_Float16)z;  // exact: an integer in 0..15
+      z16 = (_Float16)(int)z;  // the integer 0..15; via int so that -0.0 stores as +0
     }
   }
 
@@ -124,9 +125,14 @@ __global__ __launch_bounds__(256) void pack_kernel(const _Float16 *__restrict__ 
     }
   }
   Wq[tile * 64 + lane] = out;
+  const int Gq = meta_groups(G) / kMetaQuad;
   if (c == 0) {
-    scales[(size_t)n * G + g] = sc16;
-    zeros[(size_t)n * G + g] = z16;
+    scales[meta_index(n, g, Gq)] = sc16;
+    zeros[meta_index(n, g, Gq)] = z16;
+  } else if (g == G - 1 && G - 1 + c < meta_groups(G)) {
+    // the last tile of a row also clears the row's padding slots (at most 3)
+    scales[meta_index(n, G - 1 + c, Gq)] = (_Float16)0;
+    zeros[meta_index(n, G - 1 + c, Gq)] = (_Float16)0;
   }
   if (bad) atomicOr(status, bad);
 }

@@ -1,24 +1,31 @@
 // Streaming dequantize-matmul for small M (decode M = 1, speculative verify
-// M = draft length + 1): Y[M][N] = X[M][K] . W_hat^T with M <= 16.
+// M = draft length + 1): Y[M][N] = X[M][K] . W_hat^T with M <= 16, for one or
+// several independent problems in a single launch.
 //
 // Where the time goes: the nano-vllm tutorial (discosf.com), section 1.1 and
 // section 2.2, and "Chapter 22" (aiwing.uk) section 22.2's comparison table
 // describe decode as bandwidth-bound -- every token streams all weights -- so
-// this kernel is built to read each packed byte exactly once at HBM rate and
-// to keep the arithmetic off the critical path.
+// this kernel is built to keep HBM busy: each packed byte is read exactly once
+// and all other work hides behind the weight stream.
 //
-// Work split: one workgroup owns one 16-row block of W (a column of packed
-// tiles along K).  Its waves split K: wave w takes chunks of GW consecutive
-// groups, chunk w, w + WAVES, ...  For each group the wave
-//   * loads the 1 KB tile with one 128-bit load per lane (fully coalesced),
-//   * turns each 32-bit word into the exact fp16 values (q - z) (two ALU ops
-//     per pair of codes) -- that register is the lane's MFMA B operand,
-//   * multiplies by X (rows 0..M-1 of the A operand; X * s rounded to fp16
-//     once when an AWQ scale is given) with four 16x16x32 MFMAs, and
-//   * folds the group's fp32 result into the accumulator times the group
-//     scale, so the scale is applied in fp32, once per group and row.
-// The per-wave partials (16 rows x M) are summed in a fixed order through
-// LDS, so results are bit-reproducible run to run.
+// Work split.  A wave owns one 16-row block of W and a slice of its K groups
+// (S waves share a row block when the launch has too few row blocks to fill
+// the GPU, or when a row is long); it walks its slice in chunks of GW groups,
+// issuing the next chunk's loads before computing the current one, so every
+// wave keeps a steady stream of 128-bit loads in flight.  Several problems
+// share a launch by concatenating their workgroups.  Per group a wave
+//   * loads the 1 KB tile with one 128-bit buffer load per lane (coalesced;
+//     buffer loads are bounds-checked by the hardware); the scales and zero
+//     points of a chunk's 4 groups are one 8-byte load each per lane (the
+//     metadata is stored in 4-group quads, 128 contiguous bytes per row block),
+//   * turns each 32-bit word into the exact fp16 values (q - z) in nine ALU
+//     ops -- that register is the lane's 16x16x32 MFMA B operand,
+//   * multiplies by X * s (staged in LDS once per workgroup, rounded to fp16
+//     once; rows m >= M read an all-zero LDS row) with four MFMAs, and
+//   * folds the group's fp32 dot products into the accumulator times the group
+//     scale, in fp32.
+// When S > 1 the S partial sums of a row block are added in a fixed order
+// through LDS, so results are bit-reproducible run to run.
 #include "w4a16_device.h"
 #include "w4a16_internal.h"
 
@@ -27,102 +34,298 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-template <int WAVES, int GW>
-__global__ __launch_bounds__(WAVES * 64) void skinny_kernel(
-    const _Float16 *__restrict__ X, const u32x4 *__restrict__ Wq,
-    const _Float16 *__restrict__ scales, const _Float16 *__restrict__ zeros,
-    const _Float16 *__restrict__ s, _Float16 *__restrict__ Y, int M, int N, int K) {
-  const int G = K / kGroup;
-  const int NB = N / kTileRows;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+constexpr int kWaves = 8;          // waves per workgroup
+constexpr int kGW = 4;             // groups per chunk
+constexpr int kMaxProblems = 8;
+constexpr int kLdsPad = 8;         // halves of padding per staged X row
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer resource, 32-bit data format
+
+struct Problem {
+  const _Float16 *X;
+  const uint8_t *Wq;
+  const _Float16 *scales, *zeros, *s;
+  _Float16 *Y;
+  int M, N, K;
+  int block0;  // first workgroup of this problem
+  int split;   // waves per row block (1, 2, 4 or 8)
+};
+
+struct ProblemSet {
+  Problem p[kMaxProblems];
+  int count;
+};
+
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t bits) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(mask), "v"(bits));
+  return r;
+}
+
+// Eight codes of one word -> the exact fp16 values (q_j - z), j = 0..7.
+// Masks 0x000F000F and 0x00F000F0 pick the two 4-bit slots of each byte of a
+// half-word directly; OR-ing them into 1024.0 gives 1024 + q and 1024 + 16q,
+// both exact.  The first minus (1024 + z) is exact; the second times 1/16
+// minus (64 + z) is exact as well.  Slots (0,4), (1,5), (2,6), (3,7) hold
+// columns (0,1), (2,3), (4,5), (6,7).
+__device__ __forceinline__ half8 decode_word9(uint32_t w, uint32_t m_lo, uint32_t m_hi,
+                                              uint32_t magic, half2v bias_lo, half2v bias_hi) {
+  const half2v sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+  const uint32_t w8 = w >> 8;
+  const half2v a = as_half2(and_or(w, m_lo, magic)) - bias_lo;
+  const half2v b = as_half2(and_or(w, m_hi, magic)) * sixteenth - bias_hi;
+  const half2v c = as_half2(and_or(w8, m_lo, magic)) - bias_lo;
+  const half2v d = as_half2(and_or(w8, m_hi, magic)) * sixteenth - bias_hi;
+  half8 r = {a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+  return r;
+}
+
+// The problem a workgroup works on is the same for all its lanes; say so, so
+// that its pointers and sizes live in scalar registers.
+template <typename T>
+__device__ __forceinline__ T *uniform_ptr(T *p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<T *>(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ int uniform_int(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+template <bool X_LDS>
+__global__ __launch_bounds__(kWaves * 64) void skinny_kernel(ProblemSet ps) {
+  extern __shared__ __attribute__((aligned(16))) _Float16 xs[];
+  __shared__ float red[kWaves][16][17];
+
+  int pi = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxProblems; ++i)
+    if (i < ps.count && (int)blockIdx.x >= ps.p[i].block0) pi = i;
+  Problem P;
+  P.X = uniform_ptr(ps.p[pi].X);
+  P.Wq = uniform_ptr(ps.p[pi].Wq);
+  P.scales = uniform_ptr(ps.p[pi].scales);
+  P.zeros = uniform_ptr(ps.p[pi].zeros);
+  P.s = uniform_ptr(ps.p[pi].s);
+  P.Y = uniform_ptr(ps.p[pi].Y);
+  P.block0 = uniform_int(ps.p[pi].block0);
+  const int M = uniform_int(ps.p[pi].M), N = uniform_int(ps.p[pi].N);
+  const int K = uniform_int(ps.p[pi].K), S = uniform_int(ps.p[pi].split);
+  const int G = K / kGroup, NB = N / kTileRows;
+  const int lane = threadIdx.x & 63, wave = uniform_int(threadIdx.x >> 6);
   const int c = lane >> 4;   // column octet (A/B operands), row quad (D)
   const int r = lane & 15;   // X row m (A), W row in the tile (B), column n (D)
-  __shared__ float red[WAVES][16][17];
+  const int b = ((int)blockIdx.x - P.block0) * (kWaves / S) + wave / S;  // row block
+  const int ks = wave % S;                                               // K slice
+  const bool has_rows = b < NB;
+  const int bb = has_rows ? b : NB - 1;
+  // this wave's groups: [gb, ge), split on chunk boundaries
+  const int chunks = (G + kGW - 1) / kGW;
+  const int gb = min(G, (chunks * ks / S) * kGW);
+  const int ge = has_rows ? min(G, (chunks * (ks + 1) / S) * kGW) : gb;
 
-  const bool a_live = r < M;
-  const _Float16 *xrow = X + (size_t)(a_live ? r : 0) * K + 8 * c;
-  const _Float16 *srow = s ? s + 8 * c : nullptr;
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)P.Wq, (short)0, (int)min((size_t)0x7fffffff, (size_t)N * K / 2), kRsrcWord3);
+  const int Gq = meta_groups(G) / kMetaQuad;
+  const size_t meta_bytes = (size_t)N * Gq * kMetaQuad * 2;
+  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)P.scales, (short)0, (int)min((size_t)0x7fffffff, meta_bytes), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t zrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)P.zeros, (short)0, (int)min((size_t)0x7fffffff, meta_bytes), kRsrcWord3);
+  const int tile_off = bb * G * kTileBytes + lane * 16;              // + g * 1024
+  const int meta_off = ((bb * Gq) * kTileRows + r) * kMetaQuad * 2;   // + quad * 128
 
-  for (int b = blockIdx.x; b < NB; b += gridDim.x) {
-    const int n = b * kTileRows + r;
-    const u32x4 *tiles = Wq + (size_t)b * G * 64 + lane;
-    const _Float16 *sc_row = scales + (size_t)n * G;
-    const _Float16 *z_row = zeros + (size_t)n * G;
-    float4v acc = {0.f, 0.f, 0.f, 0.f};
-
-    for (int g0 = wave * GW; g0 < G; g0 += WAVES * GW) {
-      u32x4 code[GW];
-      _Float16 sc[GW], zp[GW];
+  // A chunk is one metadata quad: 4 groups' scales (and zero points) of this
+  // lane's row are one 8-byte load.
+  static_assert(kGW == kMetaQuad, "a chunk is one metadata quad");
+  u32x4 code[kGW];
+  uint32_t sq[2], zq[2];  // the quad's 4 scales, 4 zero points (fp16 pairs)
+  auto load_chunk = [&](int g0) {
 #pragma unroll
-      for (int i = 0; i < GW; ++i) {
-        const int g = min(g0 + i, G - 1);
-        code[i] = __builtin_nontemporal_load(tiles + (size_t)g * 64);
-        sc[i] = sc_row[g];
-        zp[i] = z_row[g];
+    for (int i = 0; i < kGW; ++i) {
+      const int g = g0 + i;  // past the slice: valid memory or zeros, never used
+      code[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                               wrs, tile_off, g * kTileBytes, 0));
+    }
+    const int qoff = (g0 / kMetaQuad) * kTileRows * kMetaQuad * 2;
+    const auto sv = __builtin_amdgcn_raw_buffer_load_b64(srs, meta_off, qoff, 0);
+    const auto zv = __builtin_amdgcn_raw_buffer_load_b64(zrs, meta_off, qoff, 0);
+    sq[0] = (uint32_t)sv[0];
+    sq[1] = (uint32_t)sv[1];
+    zq[0] = (uint32_t)zv[0];
+    zq[1] = (uint32_t)zv[1];
+  };
+  if (gb < ge) load_chunk(gb);
+
+  const _Float16 *xrow = nullptr;
+  if (X_LDS) {
+    // stage X * s for rows 0..M-1 and an all-zero row M
+    const int ldx = K + kLdsPad, k8 = K / 8;
+    for (int idx = threadIdx.x; idx < (M + 1) * k8; idx += kWaves * 64) {
+      const int m = idx / k8, kk = (idx - m * k8) * 8;
+      half8 v = zero_half8();
+      if (m < M) {
+        v = load_half8(P.X + (size_t)m * K + kk);
+        if (P.s) v = v * load_half8(P.s + kk);
       }
+      *reinterpret_cast<half8 *>(&xs[m * ldx + kk]) = v;
+    }
+    __syncthreads();
+    xrow = xs + (r < M ? r : M) * ldx + 8 * c;
+  }
+
+  const uint32_t m_lo = 0x000F000Fu, m_hi = 0x00F000F0u, magic = kMagic2;
+  float4v acc = {0.f, 0.f, 0.f, 0.f};
+  for (int g0 = gb; g0 < ge; g0 += kGW) {
+    u32x4 cur[kGW];
 #pragma unroll
-      for (int i = 0; i < GW; ++i) {
-        if (g0 + i < G) {
-          const int g = g0 + i;
-          half8 a[4];
+    for (int i = 0; i < kGW; ++i) cur[i] = code[i];
+    const half2v cs[2] = {as_half2(sq[0]), as_half2(sq[1])};
+    const half2v cz[2] = {as_half2(zq[0]), as_half2(zq[1])};
+    if (g0 + kGW < ge) load_chunk(g0 + kGW);  // next chunk in flight during this one
+
+    half8 a[kGW][4];
+    if (!X_LDS) {
+      // X * s straight from global memory, only in the lanes of live rows
+#pragma unroll
+      for (int i = 0; i < kGW; ++i)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) a[i][t] = zero_half8();
+      if (r < M) {
+        const _Float16 *xg = P.X + (size_t)r * K + 8 * c;
+#pragma unroll
+        for (int i = 0; i < kGW; ++i) {
+          const int g = min(g0 + i, G - 1);
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
             const size_t k = (size_t)g * kGroup + 32 * t;
-            half8 xv = zero_half8();
-            if (a_live) {
-              xv = load_half8(xrow + k);
-              if (srow) xv = xv * load_half8(srow + k);
-            }
-            a[t] = xv;
+            half8 v = load_half8(xg + k);
+            if (P.s) v = v * load_half8(P.s + 8 * c + k);
+            a[i][t] = v;
           }
-          const half2v bias = zero_bias(zp[i]);
-          float4v tmp = {0.f, 0.f, 0.f, 0.f};
-          tmp = mfma16(a[0], decode_word(code[i][0], bias), tmp);
-          tmp = mfma16(a[1], decode_word(code[i][1], bias), tmp);
-          tmp = mfma16(a[2], decode_word(code[i][2], bias), tmp);
-          tmp = mfma16(a[3], decode_word(code[i][3], bias), tmp);
-          const float scf = (float)sc[i];
-          acc += tmp * scf;
         }
       }
     }
+#pragma unroll
+    for (int i = 0; i < kGW; ++i) {
+      const int g = g0 + i;
+      if (g < ge) {
+        if (X_LDS) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            a[i][t] = *reinterpret_cast<const half8 *>(xrow + g * kGroup + 32 * t);
+        }
+        const _Float16 zp = cz[i >> 1][i & 1], sc = cs[i >> 1][i & 1];
+        const _Float16 blo = (_Float16)1024.0f + zp, bhi = (_Float16)64.0f + zp;
+        const half2v bias_lo = {blo, blo}, bias_hi = {bhi, bhi};
+        float4v tmp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          tmp = mfma16(a[i][t], decode_word9(cur[i][t], m_lo, m_hi, magic, bias_lo, bias_hi),
+                       tmp);
+        acc += tmp * (float)sc;
+      }
+    }
+  }
 
-    // lane holds D[m = 4c + v][n = r] summed over this wave's groups
+  // lane holds D[m = 4c + v][n = r] of row block b, summed over this wave's groups
+  if (S == 1) {
+    if (has_rows) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = 4 * c + v;
+        if (m < M) P.Y[(size_t)m * N + (size_t)b * kTileRows + r] = (_Float16)acc[v];
+      }
+    }
+  } else {
 #pragma unroll
     for (int v = 0; v < 4; ++v) red[wave][4 * c + v][r] = acc[v];
     __syncthreads();
-    for (int idx = threadIdx.x; idx < 16 * M; idx += WAVES * 64) {
-      const int m = idx >> 4, nn = idx & 15;
-      float sum = 0.f;
+    if (ks == 0 && has_rows) {
 #pragma unroll
-      for (int w = 0; w < WAVES; ++w) sum += red[w][m][nn];
-      Y[(size_t)m * N + (size_t)b * kTileRows + nn] = (_Float16)sum;
+      for (int v = 0; v < 4; ++v) {
+        const int m = 4 * c + v;
+        if (m < M) {
+          float sum = 0.f;
+          for (int w = 0; w < S; ++w) sum += red[wave + w][m][r];
+          P.Y[(size_t)m * N + (size_t)b * kTileRows + r] = (_Float16)sum;
+        }
+      }
     }
-    __syncthreads();
   }
 }
 
-template <int WAVES>
-hipError_t launch_waves(const void *X, const void *Wq, const void *scales, const void *zeros,
-                        const void *s, void *Y, int M, int N, int K, hipStream_t stream) {
-  constexpr int GW = 4;
-  const int NB = N / kTileRows;
-  hipLaunchKernelGGL((skinny_kernel<WAVES, GW>), dim3(NB), dim3(WAVES * 64), 0, stream,
-                     (const _Float16 *)X, (const u32x4 *)Wq, (const _Float16 *)scales,
-                     (const _Float16 *)zeros, (const _Float16 *)s, (_Float16 *)Y, M, N, K);
-  return hipGetLastError();
+// LDS bytes to stage X * s (plus the zero row) of one problem.
+size_t stage_bytes(int M, int K) { return (size_t)(M + 1) * (K + kLdsPad) * sizeof(_Float16); }
+
+constexpr size_t kMaxStageBytes = 96 * 1024;
+constexpr int kTargetWaves = 2048;     // enough waves in flight to cover HBM latency
+constexpr int kMaxGroupsPerWave = 32;  // longer rows are split across waves
+
+int pow2_at_least(int v) {
+  int p = 1;
+  while (p < v) p *= 2;
+  return p;
 }
 
 }  // namespace
 
+int skinny_max_problems() { return kMaxProblems; }
+
+hipError_t launch_skinny_set(const SkinnyDesc *d, int count, hipStream_t stream) {
+  if (count < 1 || count > kMaxProblems) return hipErrorInvalidValue;
+  // How many waves share a row block: enough waves in the whole launch to keep
+  // HBM busy, and no wave walking more than kMaxGroupsPerWave groups.
+  long long rows = 0;
+  for (int i = 0; i < count; ++i) rows += d[i].N / kTileRows;
+  const int s_fill = (int)min(8LL, (long long)pow2_at_least((int)((kTargetWaves + rows - 1) / rows)));
+  // Problems are laid out longest-rows first so that the waves with the most
+  // work start first.
+  int order[kMaxProblems];
+  for (int i = 0; i < count; ++i) order[i] = i;
+  for (int i = 1; i < count; ++i)
+    for (int j = i; j > 0 && d[order[j]].K > d[order[j - 1]].K; --j) {
+      const int t = order[j];
+      order[j] = order[j - 1];
+      order[j - 1] = t;
+    }
+  ProblemSet ps = {};
+  int blocks = 0;
+  size_t lds = 0;
+  for (int i = 0; i < count; ++i) {
+    const SkinnyDesc &q = d[order[i]];
+    Problem &p = ps.p[i];
+    const int G = q.K / kGroup, NB = q.N / kTileRows;
+    int split = s_fill;
+    while (split < 8 && (G + split - 1) / split > kMaxGroupsPerWave) split *= 2;
+    while (split > 1 && (G + kGW - 1) / kGW < split) split /= 2;  // at least a chunk per wave
+    p.X = static_cast<const _Float16 *>(q.X);
+    p.Wq = static_cast<const uint8_t *>(q.Wq);
+    p.scales = static_cast<const _Float16 *>(q.scales);
+    p.zeros = static_cast<const _Float16 *>(q.zeros);
+    p.s = static_cast<const _Float16 *>(q.s);
+    p.Y = static_cast<_Float16 *>(q.Y);
+    p.M = q.M;
+    p.N = q.N;
+    p.K = q.K;
+    p.split = split;
+    p.block0 = blocks;
+    const int rb_per_wg = kWaves / split;
+    blocks += (NB + rb_per_wg - 1) / rb_per_wg;
+    const size_t need = stage_bytes(q.M, q.K);
+    lds = need > lds ? need : lds;
+  }
+  ps.count = count;
+  if (lds <= kMaxStageBytes)
+    hipLaunchKernelGGL(skinny_kernel<true>, dim3(blocks), dim3(kWaves * 64), lds, stream, ps);
+  else
+    hipLaunchKernelGGL(skinny_kernel<false>, dim3(blocks), dim3(kWaves * 64), 0, stream, ps);
+  return hipGetLastError();
+}
+
 hipError_t launch_skinny(const void *X, const void *Wq, const void *scales, const void *zeros,
                          const void *s, void *Y, int M, int N, int K, hipStream_t stream) {
-  // enough waves that each takes about one chunk of 4 groups, at most 16
-  const int chunks = (K / kGroup + 3) / 4;
-  if (chunks <= 2) return launch_waves<2>(X, Wq, scales, zeros, s, Y, M, N, K, stream);
-  if (chunks <= 4) return launch_waves<4>(X, Wq, scales, zeros, s, Y, M, N, K, stream);
-  if (chunks <= 8) return launch_waves<8>(X, Wq, scales, zeros, s, Y, M, N, K, stream);
-  return launch_waves<16>(X, Wq, scales, zeros, s, Y, M, N, K, stream);
+  const SkinnyDesc d = {X, Wq, scales, zeros, s, Y, M, N, K};
+  return launch_skinny_set(&d, 1, stream);
 }
 
 }  // namespace w4a16

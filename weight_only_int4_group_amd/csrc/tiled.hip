@@ -38,6 +38,7 @@ __global__ __launch_bounds__(THREADS) void tiled_kernel(
   const int c = lane >> 4, r = lane & 15;
   const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
   const int G = K / kGroup;
+  const int Gq = meta_groups(G) / kMetaQuad;
   const int wm = wave >> 1, wn = wave & 1;
 
   // A loader: 128 rows x 16 chunks of 8 halves; thread takes chunk tid + 256i.
@@ -68,8 +69,8 @@ __global__ __launch_bounds__(THREADS) void tiled_kernel(
       const int nrow = n0 + 16 * bb;
       if (nrow < N) {
         breg[i] = Wq[((size_t)(nrow / kTileRows) * G + g) * 64 + lane];
-        bsc[i] = scales[(size_t)(nrow + r) * G + g];
-        bz[i] = zeros[(size_t)(nrow + r) * G + g];
+        bsc[i] = scales[meta_index(nrow + r, g, Gq)];
+        bz[i] = zeros[meta_index(nrow + r, g, Gq)];
       } else {
         const u32x4 z4 = {0, 0, 0, 0};
         breg[i] = z4;

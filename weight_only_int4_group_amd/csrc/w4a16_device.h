@@ -21,6 +21,15 @@ constexpr int kGroup = 128;
 constexpr int kTileRows = 16;
 constexpr int kTileBytes = 1024;
 constexpr int kWave = 64;
+constexpr int kMetaQuad = 4;   // groups per metadata quad
+
+// Metadata (scale / zero point) layout: quads of 4 groups.  Element index of
+// row n, group g, for Gq = ceil(G / 4) quads per row.
+__host__ __device__ constexpr int meta_groups(int G) { return (G + kMetaQuad - 1) / kMetaQuad * kMetaQuad; }
+__host__ __device__ inline size_t meta_index(int n, int g, int Gq) {
+  return (((size_t)(n / kTileRows) * Gq + g / kMetaQuad) * kTileRows + n % kTileRows) * kMetaQuad +
+         g % kMetaQuad;
+}
 
 // fp16 bit pattern 0x6400 is 1024.0; OR-ing a 4-bit code q into its low
 // mantissa bits gives the fp16 value 1024 + q exactly (the ulp at 1024 is 1).
