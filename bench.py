@@ -4,17 +4,19 @@ One step = the seven dequantize-matmuls of a Llama-3-8B-shaped decoder layer at
 decode batch M = 1 (q, k, v, o: 4096 -> 4096/1024; gate, up: 4096 -> 14336;
 down: 14336 -> 4096), group 128, AWQ scale s, each with its own seeded input.
 The seven problems are independent here, so the step is ONE grouped launch
-through the C ABI (w4a16_gemm_grouped) on torch's current stream.  Inputs are
-resident in HBM before timing starts; the packed weights rotate over enough
-layer copies (>= 1 GiB) that each step streams its weights from HBM rather
-than from the 256 MB last-level cache.
+through the C ABI (w4a16_gemm_grouped) on torch's current stream.  (Replaying
+the step from a captured HIP graph was measured slower on this stack than a
+direct launch.)  Inputs are resident in HBM before timing starts; the packed
+weights rotate over enough layer copies (>= 1 GiB) that each step streams its
+weights from HBM rather than from the 256 MB last-level cache.
 
 Printed JSON line:
   value         algorithmic bytes per step (packed codes + fp16 scales/zeros + s
                 + X + Y) / wall time per step, in TB/s;
   roofline      the step's kernel (one launch per step): its algorithmic bytes /
                 its average duration, from HIP events recorded on the launch
-                stream around every launch of the timed region;
+                stream around each block of 10 back-to-back launches of the
+                timed region (so a launch's own event overhead is amortised);
   layer_variants  the same layer as 4 launches in a real layer's dependency
                 order ([q,k,v], [o], [gate,up], [down]) and as 7 separate
                 launches, timed the same way (context for the headline);
@@ -76,32 +78,39 @@ def prepare_layer(cfg, M, torch, w4, workloads, copies_min_bytes=POOL_BYTES):
     return mats, pool, layer_w, copies
 
 
-def make_calls(mats, pool, copies, groups, w4):
-    """For every layer copy, one prepared grouped call per group of matrix indices."""
+def make_calls(mats, pool, copies, groups, w4, torch):
+    """For every layer copy, one prepared grouped call per group of matrix indices,
+    bound to torch's current stream."""
+    st = torch.cuda.current_stream().cuda_stream
     return [[w4.GroupedCall([(mats[j]["X"], pool[j][c], mats[j]["s"], mats[j]["Y"])
-                             for j in grp]) for grp in groups] for c in range(copies)]
+                             for j in grp], stream=st) for grp in groups] for c in range(copies)]
 
 
-def timed(calls, steps, warmup, torch):
-    """Warm up, then run `steps` steps (step i uses copy i % copies); every launch is
-    bracketed by HIP events on the launch stream.  Returns (wall s, launch ms [launch][step])."""
+def timed(calls, steps, warmup, torch, per=10):
+    """Warm up, then run exactly `steps` steps (step i uses copy i % copies).  HIP events
+    on the launch stream bracket every block of up to `per` consecutive launches of each
+    kind.  Returns (wall seconds, per-launch ms [launch kind][block]) where a block's
+    per-launch ms is its duration divided by its number of launches."""
     stream = torch.cuda.current_stream()
     nl = len(calls[0])
     for i in range(warmup):
-        for call in calls[i % len(calls)]:
-            call()
+        for u in calls[i % len(calls)]:
+            u()
+    blocks = [(b0, min(per, steps - b0)) for b0 in range(0, steps, per)]
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(nl)] for _ in range(steps)]
+           for _ in range(nl)] for _ in blocks]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(steps):
-        for j, call in enumerate(calls[(warmup + i) % len(calls)]):
-            ev[i][j][0].record(stream)
-            call()
-            ev[i][j][1].record(stream)
+    for (b0, n), evb in zip(blocks, ev):
+        for j in range(nl):
+            evb[j][0].record(stream)
+            for i in range(n):
+                calls[(warmup + b0 + i) % len(calls)][j]()
+            evb[j][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return wall, [[ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(steps)] for j in range(nl)]
+    return wall, [[evb[j][0].elapsed_time(evb[j][1]) / n for (_, n), evb in zip(blocks, ev)]
+                  for j in range(nl)]
 
 
 def variant(mats, groups, launch_ms, steps, wall, unit_key):
@@ -187,7 +196,8 @@ def main():
     one = [list(range(len(mats)))]
     log(f"{copies} layer copies, {layer_w * copies / 2**30:.2f} GiB of packed weights; "
         f"timing {args.steps} steps")
-    wall, lms = timed(make_calls(mats, pool, copies, one, w4), args.steps, args.warmup, torch)
+    wall, lms = timed(make_calls(mats, pool, copies, one, w4, torch), args.steps, args.warmup,
+                      torch)
     ms_per_step = wall / args.steps * 1e3
     avg_ms = float(np.mean(lms[0]))
     achieved = step_bytes / (avg_ms * 1e-3) / 1e9
@@ -212,7 +222,7 @@ def main():
         sep = [[j] for j in range(len(mats))]
         vs = {}
         for label, groups in (("dependency_order_4_launches", dep), ("separate_7_launches", sep)):
-            w, l = timed(make_calls(mats, pool, copies, groups, w4), 200, 20, torch)
+            w, l = timed(make_calls(mats, pool, copies, groups, w4, torch), 200, 20, torch)
             vs[label] = variant(mats, groups, l, 200, w, "bytes")
         out["layer_variants"] = vs
     del pool, mats
@@ -224,7 +234,8 @@ def main():
         log(f"preparing {pcfg.name} M={PM}")
         pmats, ppool, _, pc = prepare_layer(pcfg, PM, torch, w4, workloads, copies_min_bytes=0)
         groups = [[j] for j in range(len(pmats))]
-        pwall, pms = timed(make_calls(pmats, ppool, pc, groups, w4), args.prefill_steps, 2, torch)
+        pwall, pms = timed(make_calls(pmats, ppool, pc, groups, w4, torch), args.prefill_steps, 2,
+                           torch, per=1)
         flops = sum(m["flops"] for m in pmats)
         tot_ms = sum(float(np.mean(x)) for x in pms)
         out["prefill"] = {

@@ -156,3 +156,37 @@ def test_grouped_matches_single_calls_and_oracle():
         assert_close(Y, Yref, f"grouped {M}x{N}x{K}")
         single = to_host(w4.w4a16_gemm(Xd, pw, sd))
         assert np.array_equal(Y.view(np.uint16), single.view(np.uint16)), f"{M}x{N}x{K}"
+
+
+def test_graph_replay_matches_eager():
+    """A grouped call captured in a HIP graph and replayed several times, with eager
+    work and synchronisations in between, gives the eager result on every replay."""
+    torch = torch_cuda()
+    items = []
+    for i, (M, N, K, awq) in enumerate([(1, 1024, 4096, True), (1, 272, 640, False),
+                                        (5, 528, 1152, True), (40, 272, 640, True)]):
+        pw, s, _ = packed_case(N, K, awq, key=10, mat=i)
+        X = to_dev(activations(10, i, M, K))
+        Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        items.append((X, pw, None if s is None else to_dev(s), Y))
+    call = w4.GroupedCall(items)
+    call()
+    eager = [to_host(it[3]).copy() for it in items]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    note("graph capture of a grouped call")
+    with torch.cuda.graph(g):
+        call()
+    for rep in range(4):
+        for it in items:
+            it[3].fill_(float("nan"))          # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for it, ref in zip(items, eager):
+            assert np.array_equal(to_host(it[3]).view(np.uint16), ref.view(np.uint16)), rep

@@ -182,9 +182,12 @@ class GroupedCall:
     each call is a single C call on the current stream (for captured or repeated
     launches over the same buffers).  Items are (X, PackedWeight, s or None, Y)."""
 
-    def __init__(self, items):
+    def __init__(self, items, stream=None):
         torch = _torch()
         self.items = list(items)  # keep the tensors alive
+        # a fixed HIP stream (e.g. torch.cuda.current_stream().cuda_stream) saves
+        # looking up torch's current stream on every call
+        self.stream = None if stream is None else ctypes.c_void_p(stream)
         self.array = (Problem * len(self.items))()
         for i, (X, pw, s, Y) in enumerate(self.items):
             if X.dim() != 2 or X.shape[1] != pw.K or tuple(Y.shape) != (X.shape[0], pw.N):
@@ -199,7 +202,8 @@ class GroupedCall:
     def __call__(self):
         if not self.items:
             return
-        rc = lib().w4a16_gemm_grouped(self.array, len(self.items), _stream_handle(self.device))
+        st = self.stream if self.stream is not None else _stream_handle(self.device)
+        rc = lib().w4a16_gemm_grouped(self.array, len(self.items), st)
         if rc:
             raise W4A16Error(rc, "w4a16_gemm_grouped")
 

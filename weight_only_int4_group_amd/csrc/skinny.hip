@@ -34,8 +34,6 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 8;          // waves per workgroup
-constexpr int kGW = 4;             // groups per chunk
 constexpr int kMaxProblems = 8;
 constexpr int kLdsPad = 8;         // halves of padding per staged X row
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer resource, 32-bit data format
@@ -47,7 +45,7 @@ struct Problem {
   _Float16 *Y;
   int M, N, K;
   int block0;  // first workgroup of this problem
-  int split;   // waves per row block (1, 2, 4 or 8)
+  int split;   // waves per row block (a power of two, at most the workgroup's waves)
 };
 
 struct ProblemSet {
@@ -91,7 +89,7 @@ __device__ __forceinline__ T *uniform_ptr(T *p) {
 
 __device__ __forceinline__ int uniform_int(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-template <bool X_LDS>
+template <bool X_LDS, int kGW, int kWaves, int kDepth>
 __global__ __launch_bounds__(kWaves * 64) void skinny_kernel(ProblemSet ps) {
   extern __shared__ __attribute__((aligned(16))) _Float16 xs[];
   __shared__ float red[kWaves][16][17];
@@ -134,27 +132,35 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_kernel(ProblemSet ps) {
   const int tile_off = bb * G * kTileBytes + lane * 16;              // + g * 1024
   const int meta_off = ((bb * Gq) * kTileRows + r) * kMetaQuad * 2;   // + quad * 128
 
-  // A chunk is one metadata quad: 4 groups' scales (and zero points) of this
-  // lane's row are one 8-byte load.
-  static_assert(kGW == kMetaQuad, "a chunk is one metadata quad");
-  u32x4 code[kGW];
-  uint32_t sq[2], zq[2];  // the quad's 4 scales, 4 zero points (fp16 pairs)
-  auto load_chunk = [&](int g0) {
+  // A chunk is one or two metadata quads: 4 groups' scales (and zero points)
+  // of this lane's row are one 8-byte load.
+  static_assert(kGW % kMetaQuad == 0, "a chunk is whole metadata quads");
+  constexpr int kQ = kGW / kMetaQuad;
+  // kDepth chunks in flight: slot 0 is the next chunk to compute, slot d the
+  // one after d more chunks.
+  u32x4 code[kDepth][kGW];
+  uint32_t sq[kDepth][2 * kQ], zq[kDepth][2 * kQ];  // scales, zero points (fp16 pairs)
+  auto load_chunk = [&](int slot, int g0) {
 #pragma unroll
     for (int i = 0; i < kGW; ++i) {
       const int g = g0 + i;  // past the slice: valid memory or zeros, never used
-      code[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                               wrs, tile_off, g * kTileBytes, 0));
+      code[slot][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                     wrs, tile_off, g * kTileBytes, 0));
     }
-    const int qoff = (g0 / kMetaQuad) * kTileRows * kMetaQuad * 2;
-    const auto sv = __builtin_amdgcn_raw_buffer_load_b64(srs, meta_off, qoff, 0);
-    const auto zv = __builtin_amdgcn_raw_buffer_load_b64(zrs, meta_off, qoff, 0);
-    sq[0] = (uint32_t)sv[0];
-    sq[1] = (uint32_t)sv[1];
-    zq[0] = (uint32_t)zv[0];
-    zq[1] = (uint32_t)zv[1];
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) {
+      const int qoff = (g0 / kMetaQuad + q) * kTileRows * kMetaQuad * 2;
+      const auto sv = __builtin_amdgcn_raw_buffer_load_b64(srs, meta_off, qoff, 0);
+      const auto zv = __builtin_amdgcn_raw_buffer_load_b64(zrs, meta_off, qoff, 0);
+      sq[slot][2 * q] = (uint32_t)sv[0];
+      sq[slot][2 * q + 1] = (uint32_t)sv[1];
+      zq[slot][2 * q] = (uint32_t)zv[0];
+      zq[slot][2 * q + 1] = (uint32_t)zv[1];
+    }
   };
-  if (gb < ge) load_chunk(gb);
+#pragma unroll
+  for (int d = 0; d < kDepth; ++d)
+    if (gb + d * kGW < ge) load_chunk(d, gb + d * kGW);
 
   const _Float16 *xrow = nullptr;
   if (X_LDS) {
@@ -177,11 +183,26 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_kernel(ProblemSet ps) {
   float4v acc = {0.f, 0.f, 0.f, 0.f};
   for (int g0 = gb; g0 < ge; g0 += kGW) {
     u32x4 cur[kGW];
+    half2v cs[2 * kQ], cz[2 * kQ];
 #pragma unroll
-    for (int i = 0; i < kGW; ++i) cur[i] = code[i];
-    const half2v cs[2] = {as_half2(sq[0]), as_half2(sq[1])};
-    const half2v cz[2] = {as_half2(zq[0]), as_half2(zq[1])};
-    if (g0 + kGW < ge) load_chunk(g0 + kGW);  // next chunk in flight during this one
+    for (int i = 0; i < kGW; ++i) cur[i] = code[0][i];
+#pragma unroll
+    for (int q = 0; q < 2 * kQ; ++q) {
+      cs[q] = as_half2(sq[0][q]);
+      cz[q] = as_half2(zq[0][q]);
+    }
+    // shift the ring and start the chunk kDepth ahead, in flight during this one
+#pragma unroll
+    for (int d = 0; d + 1 < kDepth; ++d) {
+#pragma unroll
+      for (int i = 0; i < kGW; ++i) code[d][i] = code[d + 1][i];
+#pragma unroll
+      for (int q = 0; q < 2 * kQ; ++q) {
+        sq[d][q] = sq[d + 1][q];
+        zq[d][q] = zq[d + 1][q];
+      }
+    }
+    if (g0 + kDepth * kGW < ge) load_chunk(kDepth - 1, g0 + kDepth * kGW);
 
     half8 a[kGW][4];
     if (!X_LDS) {
@@ -258,6 +279,18 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_kernel(ProblemSet ps) {
 size_t stage_bytes(int M, int K) { return (size_t)(M + 1) * (K + kLdsPad) * sizeof(_Float16); }
 
 constexpr size_t kMaxStageBytes = 96 * 1024;
+#ifndef W4A16_SKINNY_CHUNK
+#define W4A16_SKINNY_CHUNK 4
+#endif
+constexpr int kChunk = W4A16_SKINNY_CHUNK;  // groups per chunk (weight loads in flight per wave)
+#ifndef W4A16_SKINNY_WAVES
+#define W4A16_SKINNY_WAVES 8
+#endif
+#ifndef W4A16_SKINNY_DEPTH
+#define W4A16_SKINNY_DEPTH 1
+#endif
+constexpr int kWaves = W4A16_SKINNY_WAVES;  // waves per workgroup
+constexpr int kDepth = W4A16_SKINNY_DEPTH;  // chunks in flight per wave
 constexpr int kTargetWaves = 2048;     // enough waves in flight to cover HBM latency
 constexpr int kMaxGroupsPerWave = 32;  // longer rows are split across waves
 
@@ -277,7 +310,8 @@ hipError_t launch_skinny_set(const SkinnyDesc *d, int count, hipStream_t stream)
   // HBM busy, and no wave walking more than kMaxGroupsPerWave groups.
   long long rows = 0;
   for (int i = 0; i < count; ++i) rows += d[i].N / kTileRows;
-  const int s_fill = (int)min(8LL, (long long)pow2_at_least((int)((kTargetWaves + rows - 1) / rows)));
+  const int s_fill =
+      (int)min((long long)kWaves, (long long)pow2_at_least((int)((kTargetWaves + rows - 1) / rows)));
   // Problems are laid out longest-rows first so that the waves with the most
   // work start first.
   int order[kMaxProblems];
@@ -296,8 +330,8 @@ hipError_t launch_skinny_set(const SkinnyDesc *d, int count, hipStream_t stream)
     Problem &p = ps.p[i];
     const int G = q.K / kGroup, NB = q.N / kTileRows;
     int split = s_fill;
-    while (split < 8 && (G + split - 1) / split > kMaxGroupsPerWave) split *= 2;
-    while (split > 1 && (G + kGW - 1) / kGW < split) split /= 2;  // at least a chunk per wave
+    while (split < kWaves && (G + split - 1) / split > kMaxGroupsPerWave) split *= 2;
+    while (split > 1 && (G + kChunk - 1) / kChunk < split) split /= 2;  // a chunk per wave
     p.X = static_cast<const _Float16 *>(q.X);
     p.Wq = static_cast<const uint8_t *>(q.Wq);
     p.scales = static_cast<const _Float16 *>(q.scales);
@@ -316,9 +350,11 @@ hipError_t launch_skinny_set(const SkinnyDesc *d, int count, hipStream_t stream)
   }
   ps.count = count;
   if (lds <= kMaxStageBytes)
-    hipLaunchKernelGGL(skinny_kernel<true>, dim3(blocks), dim3(kWaves * 64), lds, stream, ps);
+    hipLaunchKernelGGL((skinny_kernel<true, kChunk, kWaves, kDepth>), dim3(blocks),
+                       dim3(kWaves * 64), lds, stream, ps);
   else
-    hipLaunchKernelGGL(skinny_kernel<false>, dim3(blocks), dim3(kWaves * 64), 0, stream, ps);
+    hipLaunchKernelGGL((skinny_kernel<false, kChunk, kWaves, kDepth>), dim3(blocks),
+                       dim3(kWaves * 64), 0, stream, ps);
   return hipGetLastError();
 }
 
