@@ -34,6 +34,7 @@ import time
 
 import numpy as np
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 FP16_PEAK_TFLOPS = 2500.0    # MI355X dense fp16 MFMA, published
 POOL_BYTES = 1 << 30         # rotate weight copies over at least this much memory
@@ -43,6 +44,59 @@ METRIC = "W4A16 dequant-GEMM: HBM TB/s @M=1, TFLOP/s @M=4096, % of roofline"
 def alg_bytes(M, N, K, awq):
     """Bytes the method must move: packed codes, fp16 scale + zero per group, s, X, Y."""
     return N * K // 2 + 4 * N * K // 128 + (2 * K if awq else 0) + 2 * M * K + 2 * M * N
+
+
+def kernel_source_sha(name):
+    """SHA-256 of a kernel source file, to tie a counter profile to the code it measured."""
+    import hashlib
+    path = os.path.join(ROOT, "weight_only_int4_group_amd", "csrc", name)
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def profiled_traffic(summary, source):
+    """HBM bytes per launch from a committed rocprofv3 counter summary (FETCH_SIZE +
+    WRITE_SIZE, calibrated against a plain copy), or None when the kernel source has
+    changed since the counters were taken (or there is no summary)."""
+    path = os.path.join(ROOT, "profiles", summary)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("source_sha256") != kernel_source_sha(source):
+        return None
+    try:
+        return int(float(fields["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def profile_run(torch, w4, workloads):
+    """A short, fixed sequence for counter collection under rocprofv3: one 256 MiB
+    device-to-device copy (the calibration kernel: its bytes are known), then 20
+    grouped decode steps of the 8B layer and one launch per 70B prefill matrix."""
+    a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
+    cfg = workloads.config_by_name("llama3_8b_decode")
+    mats, pool, _, copies = prepare_layer(cfg, 1, torch, w4, workloads)
+    calls = make_calls(mats, pool, copies, [list(range(len(mats)))], w4, torch)
+    for i in range(20):
+        calls[i % copies][0]()
+    torch.cuda.synchronize()
+    del calls, pool, mats
+    pcfg = workloads.config_by_name("llama_70b_prefill")
+    pmats, ppool, _, pc = prepare_layer(pcfg, pcfg.Ms[0], torch, w4, workloads, copies_min_bytes=0)
+    for c in make_calls(pmats, ppool, pc, [[j] for j in range(len(pmats))], w4, torch)[0]:
+        c()
+    torch.cuda.synchronize()
+    print("profile run done", flush=True)
 
 
 def log(msg):
@@ -173,6 +227,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-run", action="store_true",
+                    help="only the short fixed sequence used for counter collection")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -187,6 +243,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     w4.lib()  # fail loudly if the HIP library is missing
+    if args.profile_run:
+        profile_run(torch, w4, workloads)
+        return
     cfg = workloads.config_by_name("llama3_8b_decode")
     M = cfg.Ms[0]
     log(f"preparing {cfg.name} M={M}")
@@ -214,7 +273,9 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "skinny_kernel (grouped, 7 problems)",
                      "avg_launch_us": round(avg_ms * 1e3, 3), "per_launch_bytes": step_bytes,
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": profiled_traffic("skinny_decode_llama3_8b_layer_m1_counters.txt",
+                                                 "skinny.hip")},
     }
     if not args.no_variants:
         idx = {n: i for i, n in enumerate(names)}
@@ -248,7 +309,8 @@ def main():
                          "achieved": round(flops / (tot_ms * 1e-3) / 1e12, 2),
                          "peak": FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(flops / (tot_ms * 1e-3) / 1e12 / FP16_PEAK_TFLOPS, 4),
-                         "traffic": None},
+                         "traffic": profiled_traffic("tiled_prefill_70b_layer_m4096_counters.txt",
+                                                     "tiled.hip")},
             "per_matrix": variant(pmats, groups, pms, args.prefill_steps, pwall, "flops")["launches"],
         }
         del ppool, pmats
