@@ -5,8 +5,8 @@
 // large matmul bounded by arithmetic, so this kernel is organised around the
 // MFMA units.  A workgroup of WM x WN waves owns a BM x BN block of Y; each
 // wave owns TM x TN 16x16 sub-blocks (TM*16 rows of X, TN*16 rows of W) and
-// accumulates them in fp32 with 16x16x32 fp16 MFMAs.  K is walked half a
-// quantization group (64 columns) per stage:
+// accumulates them in fp32 with 16x16x32 fp16 MFMAs.  K is walked in stages
+// of KSTAGE columns (one quantization group, or half of one):
 //   * X * s for the block's rows (rounded to fp16 once) goes through LDS,
 //     double-buffered: the next stage's global loads are issued before the
 //     current stage's MFMAs and written to the other buffer after them, with
@@ -27,8 +27,6 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kStageK = 64;                 // K columns per stage
-constexpr int kLdsStride = kStageK + 8;     // halves; the pad spreads rows over banks
 constexpr int kRsrcWord3 = 0x00020000;      // raw buffer resource, 32-bit data format
 
 __device__ __forceinline__ int uniform_int(int v) { return __builtin_amdgcn_readfirstlane(v); }
@@ -62,14 +60,18 @@ __device__ __forceinline__ half8 dequant_word(uint32_t w, half2v bias_lo, half2v
 
 // Two waves per SIMD: with one, the waits on LDS and the barriers are not
 // hidden and MFMA throughput roughly halves (measured on the 70B shapes).
-template <int WM, int WN, int TM, int TN, bool HAS_S>
+template <int WM, int WN, int TM, int TN, int KSTAGE, bool HAS_S>
 __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void tiled_kernel(
     const _Float16 *__restrict__ X, const uint8_t *__restrict__ Wq,
     const _Float16 *__restrict__ scales, const _Float16 *__restrict__ zeros,
     const _Float16 *__restrict__ s, _Float16 *__restrict__ Y, int M, int N, int K) {
   constexpr int THREADS = WM * WN * 64;
   constexpr int BM = WM * TM * 16, BN = WN * TN * 16;
-  constexpr int ROWS_PER_PASS = THREADS / 8;            // A rows one load pass covers
+  constexpr int kStageK = KSTAGE;                       // K columns per stage (64 or 128)
+  constexpr int kLdsStride = kStageK + 8;               // halves; the pad spreads rows over banks
+  constexpr int kStagesPerGroup = kGroup / kStageK;
+  constexpr int kChunksPerRow = kStageK / 8;            // 16-byte chunks per A row per stage
+  constexpr int ROWS_PER_PASS = THREADS / kChunksPerRow;  // A rows one load pass covers
   constexpr int A_PER_T = BM / ROWS_PER_PASS;           // 16-byte A chunks per thread
   static_assert(BM % ROWS_PER_PASS == 0, "A tile rows must divide evenly");
   __shared__ __attribute__((aligned(16))) _Float16 As[2][BM * kLdsStride];
@@ -80,32 +82,32 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
   const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
   const int G = K / kGroup, NB = N / kTileRows;
   const int Gq = meta_groups(G) / kMetaQuad;
-  const int stages = 2 * G;  // stage st covers columns [64 st, 64 st + 64); buffer st % 2
+  const int stages = kStagesPerGroup * G;  // stage st covers columns [KSTAGE st, +KSTAGE)
 
-  // ---- X * s staging: thread covers column chunk (tid % 8), rows tid/8 + pass*ROWS_PER_PASS
-  const int a_col = (tid & 7) * 8;
-  const int a_row = tid >> 3;
-  half8 areg[A_PER_T];
+  // ---- X * s staging: thread covers one 16-byte column chunk of rows a_row + pass*ROWS_PER_PASS
+  const int a_col = (tid % kChunksPerRow) * 8;
+  const int a_row = tid / kChunksPerRow;
+  // The loads are unconditional (rows past M read row M-1) and nothing uses
+  // their results until store_a, after the stage's MFMAs, so their latency is
+  // hidden; rows past M are zeroed and X * s is formed only then.
+  half8 areg[A_PER_T], sreg;
   auto load_a = [&](int st) {
     const int k0 = st * kStageK + a_col;
-    half8 sv;
-    if (HAS_S) sv = load_half8(s + k0);
+    if (HAS_S) sreg = load_half8(s + k0);
 #pragma unroll
     for (int i = 0; i < A_PER_T; ++i) {
-      const int m = m0 + a_row + i * ROWS_PER_PASS;
-      half8 v = zero_half8();
-      if (m < M) {
-        v = load_half8(X + (size_t)m * K + k0);
-        if (HAS_S) v = v * sv;
-      }
-      areg[i] = v;
+      const int m = min(m0 + a_row + i * ROWS_PER_PASS, M - 1);
+      areg[i] = load_half8(X + (size_t)m * K + k0);
     }
   };
   auto store_a = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < A_PER_T; ++i)
-      *reinterpret_cast<half8 *>(&As[buf][(a_row + i * ROWS_PER_PASS) * kLdsStride + a_col]) =
-          areg[i];
+    for (int i = 0; i < A_PER_T; ++i) {
+      half8 v = areg[i];
+      if (HAS_S) v = v * sreg;
+      if (m0 + a_row + i * ROWS_PER_PASS >= M) v = zero_half8();
+      *reinterpret_cast<half8 *>(&As[buf][(a_row + i * ROWS_PER_PASS) * kLdsStride + a_col]) = v;
+    }
   };
 
   // ---- weights: this wave's TN row blocks, loaded a group ahead
@@ -118,8 +120,9 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
       (void *)zeros, (short)0, (int)min((size_t)0x7fffffff, meta_bytes), kRsrcWord3);
   const int rb0 = n0 / kTileRows + wn * TN;  // first row block of this wave
   u32x4 bcode[TN], bnext[TN];
-  uint32_t bmeta[TN], bmeta_next[TN];        // scale (low half), zero point (high half)
-  auto load_b = [&](int g, u32x4 *code, uint32_t *meta) {
+  // raw fp16 bits of each row block's scale and zero point for the group
+  uint32_t bsc[TN], bzp[TN], bsc_next[TN], bzp_next[TN];
+  auto load_b = [&](int g, u32x4 *code, uint32_t *sc, uint32_t *zp) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       // row blocks past N read zeros (bounds-checked buffer loads) and are never stored
@@ -128,9 +131,8 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
           u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrs, (rb * G * 64 + lane) * 16,
                                                         g * kTileBytes, 0));
       const int mo = ((rb * Gq + g / kMetaQuad) * kTileRows + r) * kMetaQuad * 2;
-      const uint32_t sv = __builtin_amdgcn_raw_buffer_load_b16(srs, mo, (g % kMetaQuad) * 2, 0);
-      const uint32_t zv = __builtin_amdgcn_raw_buffer_load_b16(zrs, mo, (g % kMetaQuad) * 2, 0);
-      meta[j] = (sv & 0xFFFFu) | (zv << 16);
+      sc[j] = __builtin_amdgcn_raw_buffer_load_b16(srs, mo, (g % kMetaQuad) * 2, 0);
+      zp[j] = __builtin_amdgcn_raw_buffer_load_b16(zrs, mo, (g % kMetaQuad) * 2, 0);
     }
   };
 
@@ -140,20 +142,23 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = float4v{0.f, 0.f, 0.f, 0.f};
 
-  // MFMAs of k steps 2h and 2h+1 of a group whose codes / metadata are `code` / `meta`,
-  // reading X from LDS buffer `buf`.
-  auto compute_stage = [&](auto H, const u32x4 *code, const uint32_t *meta, int buf) {
+  // MFMAs of the k steps of stage h of a group (k steps t = h*KS .. h*KS + KS-1,
+  // KS = KSTAGE / 32) with the group's codes / metadata, reading X from LDS buffer `buf`.
+  constexpr int KS = kStageK / 32;
+  auto compute_stage = [&](auto H, const u32x4 *code, const uint32_t *sc, const uint32_t *zp,
+                           int buf) {
     constexpr int h = decltype(H)::value;
     const _Float16 *abuf = As[buf] + (wm * TM * 16 + r) * kLdsStride + 8 * c;
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
+    for (int tt = 0; tt < KS; ++tt) {
       half8 bop[TN];
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const half2v sz = as_half2(meta[j]);
-        const _Float16 blo = (_Float16)1024.0f + sz[1], bhi = (_Float16)64.0f + sz[1];
-        const half2v bias_lo = {blo, blo}, bias_hi = {bhi, bhi}, scale = {sz[0], sz[0]};
-        bop[j] = dequant_word(code[j][2 * h + tt], bias_lo, bias_hi, scale);
+        const _Float16 z = __builtin_bit_cast(_Float16, (uint16_t)zp[j]);
+        const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)sc[j]);
+        const _Float16 blo = (_Float16)1024.0f + z, bhi = (_Float16)64.0f + z;
+        const half2v bias_lo = {blo, blo}, bias_hi = {bhi, bhi}, scale = {sv, sv};
+        bop[j] = dequant_word(code[j][h * KS + tt], bias_lo, bias_hi, scale);
       }
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
@@ -163,27 +168,34 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
       }
     }
   };
+
   load_a(0);
-  load_b(0, bcode, bmeta);
+  load_b(0, bcode, bsc, bzp);
   store_a(0);
   lds_barrier();
-  // One group per iteration, two stages: stage 2g reads LDS buffer 0 and
-  // stage 2g+1 buffer 1.  The next group's codes are loaded during the first
-  // stage and moved into place at the end of the group.
+  // One group per iteration, kStagesPerGroup stages; stage st uses LDS buffer
+  // st % 2.  The next group's codes are loaded during the first stage and moved
+  // into place at the end of the group.
   for (int g = 0; g < G; ++g) {
-    const int st = 2 * g;
-    load_a(st + 1);
-    if (g + 1 < G) load_b(g + 1, bnext, bmeta_next);
-    compute_stage(std::integral_constant<int, 0>(), bcode, bmeta, 0);
-    store_a(1);
-    lds_barrier();
-    if (st + 2 < stages) load_a(st + 2);
-    compute_stage(std::integral_constant<int, 1>(), bcode, bmeta, 1);
-    if (st + 2 < stages) store_a(0);
+    const int st = kStagesPerGroup * g;
+    if (st + 1 < stages) load_a(st + 1);
+    if (g + 1 < G) load_b(g + 1, bnext, bsc_next, bzp_next);
+    if constexpr (kStagesPerGroup == 2) {
+      compute_stage(std::integral_constant<int, 0>(), bcode, bsc, bzp, 0);
+      store_a(1);
+      lds_barrier();
+      if (st + 2 < stages) load_a(st + 2);
+      compute_stage(std::integral_constant<int, 1>(), bcode, bsc, bzp, 1);
+      if (st + 2 < stages) store_a(0);
+    } else {
+      compute_stage(std::integral_constant<int, 0>(), bcode, bsc, bzp, g & 1);
+      if (st + 1 < stages) store_a((g + 1) & 1);
+    }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       bcode[j] = bnext[j];
-      bmeta[j] = bmeta_next[j];
+      bsc[j] = bsc_next[j];
+      bzp[j] = bzp_next[j];
     }
     lds_barrier();
   }
@@ -203,17 +215,17 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
   }
 }
 
-template <int WM, int WN, int TM, int TN>
+template <int WM, int WN, int TM, int TN, int KSTAGE>
 hipError_t launch_cfg(const void *X, const void *Wq, const void *scales, const void *zeros,
                       const void *s, void *Y, int M, int N, int K, hipStream_t stream) {
   constexpr int BM = WM * TM * 16, BN = WN * TN * 16;
   const dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM), block(WM * WN * 64);
   if (s)
-    hipLaunchKernelGGL((tiled_kernel<WM, WN, TM, TN, true>), grid, block, 0, stream,
+    hipLaunchKernelGGL((tiled_kernel<WM, WN, TM, TN, KSTAGE, true>), grid, block, 0, stream,
                        (const _Float16 *)X, (const uint8_t *)Wq, (const _Float16 *)scales,
                        (const _Float16 *)zeros, (const _Float16 *)s, (_Float16 *)Y, M, N, K);
   else
-    hipLaunchKernelGGL((tiled_kernel<WM, WN, TM, TN, false>), grid, block, 0, stream,
+    hipLaunchKernelGGL((tiled_kernel<WM, WN, TM, TN, KSTAGE, false>), grid, block, 0, stream,
                        (const _Float16 *)X, (const uint8_t *)Wq, (const _Float16 *)scales,
                        (const _Float16 *)zeros, (const _Float16 *)s, (_Float16 *)Y, M, N, K);
   return hipGetLastError();
@@ -223,9 +235,10 @@ hipError_t launch_cfg(const void *X, const void *Wq, const void *scales, const v
 
 hipError_t launch_tiled(const void *X, const void *Wq, const void *scales, const void *zeros,
                         const void *s, void *Y, int M, int N, int K, hipStream_t stream) {
-  // 64 x 256 blocks of 4 waves (64 x 64 each), two workgroups per CU: the
-  // fastest of the measured shapes at every M of the workloads.
-  return launch_cfg<1, 4, 4, 4>(X, Wq, scales, zeros, s, Y, M, N, K, stream);
+  // 64 x 256 blocks of 4 waves (64 x 64 each), one group per stage, two
+  // workgroups per CU: the fastest of the measured shapes and stage widths at
+  // every M of the workloads.
+  return launch_cfg<1, 4, 4, 4, 128>(X, Wq, scales, zeros, s, Y, M, N, K, stream);
 }
 
 }  // namespace w4a16
