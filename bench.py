@@ -20,6 +20,9 @@ Printed JSON line:
   layer_variants  the same layer as 4 launches in a real layer's dependency
                 order ([q,k,v], [o], [gate,up], [down]) and as 7 separate
                 launches, timed the same way (context for the headline);
+  batched       the same 8B layer at speculative-verify batches M = 2, 5, 9 and a
+                Qwen2-7B-shaped layer at batched-decode M = 16, 64, 256, one grouped
+                call per step (streaming kernel for M <= 16, else the tiled GEMM);
   prefill       the 70B-shaped layer at M = 4096 (compute-bound): TFLOP/s
                 against the dense fp16 MFMA peak;
   cpu_baseline  the fp64 CPU oracle on a bounded sample of the same workload.
@@ -167,6 +170,36 @@ def timed(calls, steps, warmup, torch, per=10):
                   for j in range(nl)]
 
 
+def with_batch(mats, cfg, M, torch, workloads):
+    """The same packed matrices with new seeded activations of batch M."""
+    out = []
+    for mi, m in enumerate(mats):
+        X = torch.from_numpy(workloads.activations(cfg.weight_key, mi, M, m["K"],
+                                                   outliers=cfg.act_outliers)).to("cuda")
+        Y = torch.empty((M, m["N"]), dtype=torch.float16, device="cuda")
+        out.append(dict(m, X=X, Y=Y, bytes=alg_bytes(M, m["N"], m["K"], m["s"] is not None),
+                        flops=2 * M * m["N"] * m["K"]))
+    return out
+
+
+def batched_line(cfg, M, mats, pool, copies, w4, torch, workloads, steps=200, warmup=20):
+    """One grouped call over the whole layer per step at batch M."""
+    bm = with_batch(mats, cfg, M, torch, workloads)
+    calls = make_calls(bm, pool, copies, [list(range(len(bm)))], w4, torch)
+    split = calls[0][0].ws_bytes > 0  # K split across workgroups: + one reduction launch
+    wall, lms = timed(calls, steps, warmup, torch)
+    byts, fl = sum(m["bytes"] for m in bm), sum(m["flops"] for m in bm)
+    kern = float(np.mean(lms[0])) * 1e-3
+    path = "streaming" if w4.w4a16_select_path(M, mats[0]["N"], mats[0]["K"]) == w4.PATH_SKINNY \
+        else "tiled"
+    return {"workload": cfg.name, "M": M, "kernel": path,
+            "launches_per_step": 1 + int(split), "split_k": split,
+            "us_per_step": round(wall / steps * 1e6, 2), "kernel_us_per_step": round(kern * 1e6, 2),
+            "TB/s": round(byts / (wall / steps) / 1e12, 4),
+            "kernel_TB/s": round(byts / kern / 1e12, 4),
+            "TFLOP/s": round(fl / (wall / steps) / 1e12, 2)}
+
+
 def variant(mats, groups, launch_ms, steps, wall, unit_key):
     step_units = sum(m[unit_key] for m in mats)
     kern = sum(float(np.mean(x)) for x in launch_ms)  # ms of kernel time per step
@@ -226,6 +259,7 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
+    ap.add_argument("--no-batched", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-run", action="store_true",
                     help="only the short fixed sequence used for counter collection")
@@ -286,7 +320,22 @@ def main():
             w, l = timed(make_calls(mats, pool, copies, groups, w4, torch), 200, 20, torch)
             vs[label] = variant(mats, groups, l, 200, w, "bytes")
         out["layer_variants"] = vs
-    del pool, mats
+    if not args.no_batched:
+        vcfg = workloads.config_by_name("llama3_8b_verify")
+        assert vcfg.weight_key == cfg.weight_key  # verify runs the decode layer's weights
+        lines = [batched_line(vcfg, vm, mats, pool, copies, w4, torch, workloads)
+                 for vm in vcfg.Ms]
+        del pool, mats
+        torch.cuda.empty_cache()
+        qcfg = workloads.config_by_name("qwen2_7b_batched_decode")
+        log(f"preparing {qcfg.name}")
+        qmats, qpool, _, qc = prepare_layer(qcfg, qcfg.Ms[0], torch, w4, workloads)
+        lines += [batched_line(qcfg, qm, qmats, qpool, qc, w4, torch, workloads)
+                  for qm in qcfg.Ms]
+        out["batched"] = lines
+        del qpool, qmats
+    else:
+        del pool, mats
     torch.cuda.empty_cache()
 
     if not args.no_prefill:

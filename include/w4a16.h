@@ -87,7 +87,10 @@ enum {
 enum {
   W4A16_PATH_AUTO = 0,     /* pick by M (decode / verify / prefill)               */
   W4A16_PATH_SKINNY = 1,   /* streaming split-K MFMA kernel, M <= 16 per pass     */
-  W4A16_PATH_TILED = 2     /* LDS-tiled MFMA GEMM for large M                     */
+  W4A16_PATH_TILED = 2,    /* LDS-tiled MFMA GEMM for large M                     */
+  W4A16_PATH_SKINNY_WINDOW = 3 /* streaming kernel with X*s staged in K windows;
+                              SKINNY takes it by itself when X*s of the whole
+                              row does not fit in LDS (long K at M > 1)        */
 };
 
 /* Byte sizes of the three packed buffers of an [N][K] weight (host outputs).
@@ -129,15 +132,39 @@ typedef struct w4a16_problem {
   int64_t M, N, K;
 } w4a16_problem;
 
-/* Several independent dequantize-matmuls, each computed exactly as
- * w4a16_gemm computes it, in as few launches as possible: problems that the
- * M-dispatch sends to the streaming kernel (small M) share one launch, up to
- * 8 problems per launch, so a layer's small projections ride along with its
- * large ones; the others get a launch each.  `problems` is a host array of
+/* Several independent dequantize-matmuls, each the operation w4a16_gemm
+ * computes, in as few launches as possible: problems that the M-dispatch
+ * sends to the streaming kernel (small M) share one launch, up to 8 problems
+ * per launch, so a layer's small projections ride along with its large ones;
+ * the others get a launch each.  How a shared launch splits K across waves,
+ * and whether it stages X * s in K windows, depends on all of its problems,
+ * so the fp32 summation order (and the last bit of a result) can differ from
+ * a single w4a16_gemm call; the same call always gives the same bits.  `problems` is a host array of
  * `count` entries (count 0 is a no-op).  Every problem is validated first; on
  * an error nothing is launched.  Outputs must not overlap each other or any
  * input.  Asynchronous on `stream`. */
 int w4a16_gemm_grouped(const w4a16_problem *problems, int count, void *stream);
+
+/* Bytes of device workspace that lets w4a16_gemm_grouped_ws split K across
+ * workgroups for these problems (host only; no GPU call).  0 when no problem
+ * benefits (every streaming-path problem, and tiled-path calls whose output
+ * blocks already fill the GPU).  Validates like w4a16_gemm_grouped; *bytes is
+ * a host pointer. */
+int w4a16_gemm_workspace_size(const w4a16_problem *problems, int count, size_t *bytes);
+
+/* w4a16_gemm_grouped with a caller-owned device workspace.  Step 7 of the
+ * method (the K reduction) may then run across workgroups: for large-M
+ * problems whose output blocks are too few to fill the GPU (batched decode;
+ * small projections), each of S K-ranges writes fp32 partial sums to the
+ * workspace, and a second kernel adds the S partials in a fixed order and
+ * rounds to fp16 once, so results are reproducible run to run (they may
+ * differ in the last bit from an unsplit call).  The workspace needs no
+ * initialisation, must hold w4a16_gemm_workspace_size() bytes for the same
+ * problems (else, or when NULL, K is not split), must be 16-byte aligned
+ * (EALIGN), must not overlap any input or output, and may be reused as soon
+ * as the call's work on `stream` has completed.  Asynchronous on `stream`. */
+int w4a16_gemm_grouped_ws(const w4a16_problem *problems, int count, void *workspace,
+                          size_t workspace_bytes, void *stream);
 
 /* Which path AUTO takes for this shape (host only; no GPU call). */
 int w4a16_select_path(int64_t M, int64_t N, int64_t K);

@@ -123,3 +123,41 @@ def test_grouped_validation():
     assert L.w4a16_gemm_grouped(arr, 3, None) == -1
     arr = (w4.Problem * 2)(bad_al, good)
     assert L.w4a16_gemm_grouped(arr, 2, None) == -2
+
+
+def ws_size(*problems):
+    L = w4.lib()
+    arr = (w4.Problem * len(problems))(*problems)
+    nb = ctypes.c_size_t(12345)
+    rc = L.w4a16_gemm_workspace_size(arr, len(problems), ctypes.byref(nb))
+    return rc, nb.value
+
+
+def test_workspace_size():
+    """Host-only size query: zero where K is not split (streaming-path problems, grids
+    that fill the GPU), S fp32 [M][N] slabs where it is."""
+    P = w4.Problem
+    assert ws_size(P(A16, A16, A16, A16, None, A16, 9, 4096, 14336)) == (0, 0)
+    assert ws_size(P(A16, A16, A16, A16, None, A16, 4096, 8192, 8192)) == (0, 0)
+    # 64 x 272 output: two 64 x 256 blocks x 32 groups, far fewer than the GPU's
+    # block slots, so K is cut into ranges of the minimum 8 groups: 4 splits
+    rc, nb = ws_size(P(A16, A16, A16, A16, None, A16, 64, 272, 4096))
+    assert rc == 0 and nb == 4 * 64 * 272 * 4
+    # a problem with M = 0 and a streaming one add nothing
+    rc2, nb2 = ws_size(P(A16, A16, A16, A16, None, A16, 64, 272, 4096),
+                       P(A16, A16, A16, A16, None, A16, 0, 16, 128),
+                       P(A16, A16, A16, A16, None, A16, 1, 4096, 4096))
+    assert (rc2, nb2) == (0, nb)
+    L = w4.lib()
+    arr = (P * 1)(P(A16, A16, A16, A16, None, A16, 64, 272, 4096))
+    assert L.w4a16_gemm_workspace_size(arr, 1, None) == -1
+    assert ws_size(P(A16, A16, A16, A16, None, A16, 64, 272, 100))[0] == -1
+
+
+def test_grouped_ws_validation():
+    L = w4.lib()
+    good = w4.Problem(A16, A16, A16, A16, None, A16, 0, 16, 128)
+    arr = (w4.Problem * 1)(good)
+    assert L.w4a16_gemm_grouped_ws(arr, 1, None, 0, None) == 0
+    assert L.w4a16_gemm_grouped_ws(arr, 1, ODD, 1 << 20, None) == -2   # misaligned workspace
+    assert L.w4a16_gemm_grouped_ws(None, 1, None, 0, None) == -1

@@ -14,7 +14,8 @@ from workloads import activations, awq_scales, weights
 
 pytestmark = pytest.mark.gpu
 
-PATHS = {"auto": w4.PATH_AUTO, "skinny": w4.PATH_SKINNY, "tiled": w4.PATH_TILED}
+PATHS = {"auto": w4.PATH_AUTO, "skinny": w4.PATH_SKINNY, "tiled": w4.PATH_TILED,
+         "window": w4.PATH_SKINNY_WINDOW}
 
 
 def packed_case(N, K, awq, key=2, mat=0):
@@ -42,7 +43,7 @@ def run(X, pw, s, path):
     return to_host(w4.w4a16_gemm_path(Xd, pw, sd, PATHS[path]))
 
 
-@pytest.mark.parametrize("path", ["skinny", "tiled"])
+@pytest.mark.parametrize("path", ["skinny", "window", "tiled"])
 @pytest.mark.parametrize("awq", [False, True])
 @pytest.mark.parametrize("M", list(range(1, 18)))
 def test_small_M_all_paths(M, awq, path):
@@ -54,7 +55,7 @@ def test_small_M_all_paths(M, awq, path):
     assert_close(Y, oracle.gemm(X, ref.q, ref.scales, ref.zeros, s), f"M={M} {path}")
 
 
-@pytest.mark.parametrize("path", ["auto", "skinny", "tiled"])
+@pytest.mark.parametrize("path", ["auto", "skinny", "window", "tiled"])
 @pytest.mark.parametrize("M", [31, 64, 100, 128, 129, 257])
 def test_larger_M(M, path):
     N, K = 272, 640
@@ -75,7 +76,45 @@ def test_shape_extremes(N, K, M):
     assert_close(Y, oracle.gemm(X, ref.q, ref.scales, ref.zeros, s), f"{M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("path", ["skinny", "tiled"])
+@pytest.mark.parametrize("N,K", [(16, 128), (16, 4096), (1024, 128), (528, 1152), (64, 14336),
+                                 (48, 18944)])
+@pytest.mark.parametrize("M", [2, 9, 16])
+def test_window_shapes(N, K, M):
+    """K windows of every width the launcher picks (1..8 chunks), windows that run
+    past K, and row blocks that do not fill a workgroup."""
+    pw, s, ref = packed_case(N, K, True, key=3, mat=N + K)
+    X = activations(3, 1, M, K, outliers=True)
+    note(f"gemm window M={M} N={N} K={K}")
+    Y = run(X, pw, s, "window")
+    assert_close(Y, oracle.gemm(X, ref.q, ref.scales, ref.zeros, s), f"{M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(40, 272, 4096), (64, 272, 14336), (100, 528, 1152),
+                                   (257, 16, 4096), (64, 48, 18944), (17, 1024, 2048)])
+def test_split_k(M, N, K):
+    """Large-M calls whose output blocks are too few for the GPU split K across
+    workgroups (fp32 partials in the workspace, reduced in a fixed order): the result
+    matches the oracle, is reproducible, and agrees with the unsplit kernel."""
+    torch_cuda()
+    pw, s, ref = packed_case(N, K, True, key=11, mat=N + K)
+    assert w4.w4a16_select_path(M, N, K) == w4.PATH_TILED
+    X = activations(11, M, M, K, outliers=True)
+    Xd, sd = to_dev(X), to_dev(s)
+    call = w4.GroupedCall([(Xd, pw, sd, w4._torch().empty((M, N), dtype=w4._torch().float16,
+                                                         device="cuda"))])
+    assert call.ws_bytes > 0, "this shape is expected to split K"
+    note(f"split-K M={M} N={N} K={K} workspace={call.ws_bytes}")
+    call()
+    a = to_host(call.items[0][3]).copy()
+    call()
+    b = to_host(call.items[0][3])
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+    assert_close(a, oracle.gemm(X, ref.q, ref.scales, ref.zeros, s), f"split {M}x{N}x{K}")
+    unsplit = run(X, pw, s, "tiled")
+    assert_close(a, unsplit, f"split vs unsplit {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("path", ["skinny", "window", "tiled"])
 def test_integer_case_bit_exact(path):
     """Pin P5: s = 1, integer weights with codes 0 and 15 in every group -> scale 1,
     zero point 8; X in {-1, 0, 1}: Y is an integer matmul, exact in fp16."""
@@ -102,7 +141,7 @@ def test_zero_weights_give_zero():
     torch_cuda()
     pw = w4.w4a16_quantize_pack(to_dev(W))
     X = activations(4, 0, M, K)
-    for path in ("skinny", "tiled"):
+    for path in ("skinny", "window", "tiled"):
         note(f"zero weights path={path}")
         assert np.all(run(X, pw, None, path) == 0)
 
@@ -112,7 +151,7 @@ def test_deterministic_and_row_independent():
     computed by the same kernel (pin P6's batch identity, on the GPU)."""
     N, K = 1024, 4096
     pw, s, _ = packed_case(N, K, True, key=5)
-    for path, M in (("skinny", 9), ("tiled", 40)):
+    for path, M in (("skinny", 9), ("window", 9), ("tiled", 40)):
         X = activations(5, 0, M, K)
         note(f"determinism path={path} M={M}")
         a = run(X, pw, s, path)
@@ -134,8 +173,10 @@ def test_empty_batch():
 
 def test_grouped_matches_single_calls_and_oracle():
     """One grouped call over problems of mixed shapes, M (including 0 and a tiled-path M)
-    and AWQ scales: each output equals the single-call output bit for bit and the oracle
-    within tolerance.  Nine streaming problems take two launches of the kernel."""
+    and AWQ scales: each output matches the oracle and the single-call output within
+    tolerance, and the same call again gives the same bits.  Nine streaming problems
+    take two launches of the kernel; one problem (M=16, K=4096) needs K windows, so its
+    launch runs windowed while the other launch stages whole rows."""
     torch_cuda()
     cases = [(1, 272, 640, True), (1, 16, 128, False), (5, 528, 1152, True), (0, 64, 256, False),
              (40, 272, 640, False), (16, 1024, 4096, True), (3, 48, 384, False),
@@ -149,13 +190,15 @@ def test_grouped_matches_single_calls_and_oracle():
         refs.append(oracle.gemm(X, ref.q, ref.scales, ref.zeros, s))
     note(f"grouped call over {len(cases)} problems")
     Ys = [to_host(y) for y in w4.w4a16_gemm_grouped(items)]
-    for (M, N, K, _), (Xd, pw, sd), Y, Yref in zip(cases, items, Ys, refs):
+    again = [to_host(y) for y in w4.w4a16_gemm_grouped(items)]
+    for (M, N, K, _), (Xd, pw, sd), Y, Y2, Yref in zip(cases, items, Ys, again, refs):
         assert Y.shape == (M, N)
         if M == 0:
             continue
         assert_close(Y, Yref, f"grouped {M}x{N}x{K}")
+        assert np.array_equal(Y.view(np.uint16), Y2.view(np.uint16)), f"{M}x{N}x{K}"
         single = to_host(w4.w4a16_gemm(Xd, pw, sd))
-        assert np.array_equal(Y.view(np.uint16), single.view(np.uint16)), f"{M}x{N}x{K}"
+        assert_close(Y, single, f"grouped vs single {M}x{N}x{K}")
 
 
 def test_graph_replay_matches_eager():
@@ -164,12 +207,14 @@ def test_graph_replay_matches_eager():
     torch = torch_cuda()
     items = []
     for i, (M, N, K, awq) in enumerate([(1, 1024, 4096, True), (1, 272, 640, False),
-                                        (5, 528, 1152, True), (40, 272, 640, True)]):
+                                        (5, 528, 1152, True), (40, 272, 640, True),
+                                        (64, 272, 4096, False)]):
         pw, s, _ = packed_case(N, K, awq, key=10, mat=i)
         X = to_dev(activations(10, i, M, K))
         Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
         items.append((X, pw, None if s is None else to_dev(s), Y))
     call = w4.GroupedCall(items)
+    assert call.ws_bytes > 0  # the M = 64 problem splits K: the reduction runs in the graph
     call()
     eager = [to_host(it[3]).copy() for it in items]
     side = torch.cuda.Stream()

@@ -19,19 +19,21 @@ from dataclasses import dataclass
 from .build import LIB_PATH
 
 __all__ = [
-    "W4A16Error", "PackedWeight", "GROUP", "PATH_AUTO", "PATH_SKINNY", "PATH_TILED", "lib",
+    "W4A16Error", "PackedWeight", "GROUP", "PATH_AUTO", "PATH_SKINNY", "PATH_TILED",
+    "PATH_SKINNY_WINDOW", "lib",
     "w4a16_packed_sizes", "w4a16_quantize_pack", "w4a16_gemm", "w4a16_gemm_path",
     "w4a16_select_path", "w4a16_strerror", "w4a16_version", "EXPORTED_SYMBOLS",
     "w4a16_gemm_grouped", "GroupedCall",
 ]
 
 GROUP = 128
-PATH_AUTO, PATH_SKINNY, PATH_TILED = 0, 1, 2
+PATH_AUTO, PATH_SKINNY, PATH_TILED, PATH_SKINNY_WINDOW = 0, 1, 2, 3
 STATUS = {0: "W4A16_OK", -1: "W4A16_EINVAL", -2: "W4A16_EALIGN", -3: "W4A16_EUNSUPPORTED",
           -4: "W4A16_ENONFINITE", -5: "W4A16_ERANGE", -6: "W4A16_EHIP"}
 EXPORTED_SYMBOLS = ("w4a16_packed_sizes", "w4a16_quantize_pack", "w4a16_gemm",
-                    "w4a16_gemm_path", "w4a16_gemm_grouped", "w4a16_select_path",
-                    "w4a16_strerror", "w4a16_version")
+                    "w4a16_gemm_path", "w4a16_gemm_grouped", "w4a16_gemm_grouped_ws",
+                    "w4a16_gemm_workspace_size", "w4a16_select_path", "w4a16_strerror",
+                    "w4a16_version")
 
 
 class Problem(ctypes.Structure):
@@ -65,12 +67,16 @@ def lib() -> ctypes.CDLL:
     L.w4a16_gemm.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, vp]
     L.w4a16_gemm_path.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, vp]
     L.w4a16_gemm_grouped.argtypes = [ctypes.POINTER(Problem), ctypes.c_int, vp]
+    L.w4a16_gemm_grouped_ws.argtypes = [ctypes.POINTER(Problem), ctypes.c_int, vp,
+                                        ctypes.c_size_t, vp]
+    L.w4a16_gemm_workspace_size.argtypes = [ctypes.POINTER(Problem), ctypes.c_int, sz]
     L.w4a16_select_path.argtypes = [i64, i64, i64]
     L.w4a16_strerror.argtypes = [ctypes.c_int]
     L.w4a16_strerror.restype = ctypes.c_char_p
     L.w4a16_version.argtypes = []
     for name in ("w4a16_packed_sizes", "w4a16_quantize_pack", "w4a16_gemm", "w4a16_gemm_path",
-                 "w4a16_gemm_grouped", "w4a16_select_path", "w4a16_version"):
+                 "w4a16_gemm_grouped", "w4a16_gemm_grouped_ws", "w4a16_gemm_workspace_size",
+                 "w4a16_select_path", "w4a16_version"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -174,15 +180,26 @@ def w4a16_gemm_path(X, pw: PackedWeight, s=None, path: int = PATH_AUTO, out=None
 
 
 def w4a16_gemm(X, pw: PackedWeight, s=None, out=None):
-    return w4a16_gemm_path(X, pw, s, PATH_AUTO, out)
+    """Y[M][N] = X[M][K] . dequant(pw)^T (fp16) through the grouped entry point with a
+    workspace, so large-M calls may split K across workgroups."""
+    torch = _torch()
+    if X.dim() != 2 or X.shape[1] != pw.K:
+        raise ValueError("X must be [M][K] with K matching the packed weight")
+    if out is None:
+        out = torch.empty((X.shape[0], pw.N), dtype=torch.float16, device=X.device)
+    GroupedCall([(X, pw, s, out)])()
+    return out
 
 
 class GroupedCall:
-    """A prepared w4a16_gemm_grouped call: the problem array is marshalled once, so
-    each call is a single C call on the current stream (for captured or repeated
-    launches over the same buffers).  Items are (X, PackedWeight, s or None, Y)."""
+    """A prepared w4a16_gemm_grouped_ws call: the problem array is marshalled and the
+    workspace (w4a16_gemm_workspace_size bytes, a torch tensor owned by this object)
+    allocated once, so each call is a single C call on the current stream (for
+    captured or repeated launches over the same buffers).  Items are (X,
+    PackedWeight, s or None, Y).  Calls of one object must not overlap in time on
+    different streams, since they share the workspace."""
 
-    def __init__(self, items, stream=None):
+    def __init__(self, items, stream=None, workspace=True):
         torch = _torch()
         self.items = list(items)  # keep the tensors alive
         # a fixed HIP stream (e.g. torch.cuda.current_stream().cuda_stream) saves
@@ -198,14 +215,24 @@ class GroupedCall:
                 _dev_ptr(pw.zeros, "zeros", torch.float16), _dev_ptr(s, "s", torch.float16, pw.K),
                 _dev_ptr(Y, "Y", torch.float16), X.shape[0], pw.N, pw.K)
         self.device = self.items[0][0].device if self.items else None
+        self.ws, self.ws_ptr, self.ws_bytes = None, None, 0
+        if workspace and self.items:
+            nb = ctypes.c_size_t()
+            rc = lib().w4a16_gemm_workspace_size(self.array, len(self.items), ctypes.byref(nb))
+            if rc:
+                raise W4A16Error(rc, "w4a16_gemm_workspace_size")
+            if nb.value:
+                self.ws = torch.empty(nb.value, dtype=torch.uint8, device=self.device)
+                self.ws_ptr, self.ws_bytes = self.ws.data_ptr(), nb.value
 
     def __call__(self):
         if not self.items:
             return
         st = self.stream if self.stream is not None else _stream_handle(self.device)
-        rc = lib().w4a16_gemm_grouped(self.array, len(self.items), st)
+        rc = lib().w4a16_gemm_grouped_ws(self.array, len(self.items), self.ws_ptr,
+                                         self.ws_bytes, st)
         if rc:
-            raise W4A16Error(rc, "w4a16_gemm_grouped")
+            raise W4A16Error(rc, "w4a16_gemm_grouped_ws")
 
 
 def w4a16_gemm_grouped(items):

@@ -121,7 +121,7 @@ int check_gemm(const void *X, const void *Wq, const void *scales, const void *ze
 }
 
 // Streaming-kernel pieces of one problem: 16 rows of X per piece.
-void skinny_pieces(const w4a16_problem &p, std::vector<w4a16::SkinnyDesc> &out) {
+void skinny_pieces(const w4a16_problem &p, std::vector<w4a16::GemmDesc> &out) {
   for (int64_t m0 = 0; m0 < p.M; m0 += kSkinnyMaxM) {
     const int64_t mb = (p.M - m0) < kSkinnyMaxM ? (p.M - m0) : kSkinnyMaxM;
     out.push_back({static_cast<const _Float16 *>(p.X) + m0 * p.K, p.Wq, p.scales, p.zeros, p.s,
@@ -129,11 +129,12 @@ void skinny_pieces(const w4a16_problem &p, std::vector<w4a16::SkinnyDesc> &out) 
   }
 }
 
-hipError_t launch_pieces(const std::vector<w4a16::SkinnyDesc> &pieces, hipStream_t st) {
+hipError_t launch_pieces(const std::vector<w4a16::GemmDesc> &pieces, hipStream_t st,
+                         bool force_window = false) {
   const int cap = w4a16::skinny_max_problems();
   for (size_t i = 0; i < pieces.size(); i += cap) {
     const int n = (int)((pieces.size() - i) < (size_t)cap ? (pieces.size() - i) : (size_t)cap);
-    const hipError_t err = w4a16::launch_skinny_set(pieces.data() + i, n, st);
+    const hipError_t err = w4a16::launch_skinny_set(pieces.data() + i, n, st, force_window);
     if (err != hipSuccess) return err;
   }
   return hipSuccess;
@@ -146,43 +147,93 @@ extern "C" {
 int w4a16_gemm_path(const void *X, const void *Wq, const void *scales, const void *zeros,
                     const void *s, void *Y, int64_t M, int64_t N, int64_t K, int path,
                     void *stream) {
-  if (path != W4A16_PATH_AUTO && path != W4A16_PATH_SKINNY && path != W4A16_PATH_TILED)
+  if (path != W4A16_PATH_AUTO && path != W4A16_PATH_SKINNY && path != W4A16_PATH_TILED &&
+      path != W4A16_PATH_SKINNY_WINDOW)
     return W4A16_EUNSUPPORTED;
   const int rc = check_gemm(X, Wq, scales, zeros, s, Y, M, N, K);
   if (rc || M == 0) return rc;
   if (path == W4A16_PATH_AUTO) path = w4a16_select_path(M, N, K);
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t err;
-  if (path == W4A16_PATH_SKINNY) {
-    std::vector<w4a16::SkinnyDesc> pieces;
+  if (path == W4A16_PATH_SKINNY || path == W4A16_PATH_SKINNY_WINDOW) {
+    std::vector<w4a16::GemmDesc> pieces;
     skinny_pieces({X, Wq, scales, zeros, s, Y, M, N, K}, pieces);
-    err = launch_pieces(pieces, st);
+    err = launch_pieces(pieces, st, path == W4A16_PATH_SKINNY_WINDOW);
   } else {
     err = w4a16::launch_tiled(X, Wq, scales, zeros, s, Y, (int)M, (int)N, (int)K, st);
   }
   return err == hipSuccess ? W4A16_OK : W4A16_EHIP;
 }
 
-int w4a16_gemm_grouped(const w4a16_problem *problems, int count, void *stream) {
+}  // extern "C"
+
+namespace {
+
+int check_problems(const w4a16_problem *problems, int count) {
   if (count < 0 || (count > 0 && !problems)) return W4A16_EINVAL;
   for (int i = 0; i < count; ++i) {
     const w4a16_problem &p = problems[i];
     const int rc = check_gemm(p.X, p.Wq, p.scales, p.zeros, p.s, p.Y, p.M, p.N, p.K);
     if (rc) return rc;
   }
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  std::vector<w4a16::SkinnyDesc> pieces;
+  return W4A16_OK;
+}
+
+w4a16::GemmDesc desc_of(const w4a16_problem &p) {
+  return {p.X, p.Wq, p.scales, p.zeros, p.s, p.Y, (int)p.M, (int)p.N, (int)p.K};
+}
+
+// The tiled-path problems of a grouped call, in call order, in launches of up
+// to tiled_max_problems(): the same batches for the size query and the call.
+std::vector<std::vector<w4a16::GemmDesc>> tiled_batches(const w4a16_problem *problems, int count) {
+  std::vector<std::vector<w4a16::GemmDesc>> out;
+  const size_t cap = (size_t)w4a16::tiled_max_problems();
   for (int i = 0; i < count; ++i) {
     const w4a16_problem &p = problems[i];
-    if (p.M == 0) continue;
-    if (w4a16_select_path(p.M, p.N, p.K) == W4A16_PATH_SKINNY) {
-      skinny_pieces(p, pieces);
-    } else if (w4a16::launch_tiled(p.X, p.Wq, p.scales, p.zeros, p.s, p.Y, (int)p.M, (int)p.N,
-                                   (int)p.K, st) != hipSuccess) {
-      return W4A16_EHIP;
-    }
+    if (p.M == 0 || w4a16_select_path(p.M, p.N, p.K) != W4A16_PATH_TILED) continue;
+    if (out.empty() || out.back().size() == cap) out.emplace_back();
+    out.back().push_back(desc_of(p));
   }
+  return out;
+}
+
+}  // namespace
+
+extern "C" {
+
+int w4a16_gemm_workspace_size(const w4a16_problem *problems, int count, size_t *bytes) {
+  if (!bytes) return W4A16_EINVAL;
+  const int rc = check_problems(problems, count);
+  if (rc) return rc;
+  size_t need = 0;
+  for (const auto &b : tiled_batches(problems, count)) {
+    const size_t n = w4a16::tiled_workspace_bytes(b.data(), (int)b.size());
+    need = n > need ? n : need;
+  }
+  *bytes = need;
+  return W4A16_OK;
+}
+
+int w4a16_gemm_grouped_ws(const w4a16_problem *problems, int count, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+  const int rc = check_problems(problems, count);
+  if (rc) return rc;
+  if (workspace && !aligned16(workspace)) return W4A16_EALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  std::vector<w4a16::GemmDesc> pieces;
+  for (int i = 0; i < count; ++i) {
+    const w4a16_problem &p = problems[i];
+    if (p.M > 0 && w4a16_select_path(p.M, p.N, p.K) == W4A16_PATH_SKINNY) skinny_pieces(p, pieces);
+  }
+  for (const auto &b : tiled_batches(problems, count))
+    if (w4a16::launch_tiled_set(b.data(), (int)b.size(), workspace, workspace_bytes, st) !=
+        hipSuccess)
+      return W4A16_EHIP;
   return launch_pieces(pieces, st) == hipSuccess ? W4A16_OK : W4A16_EHIP;
+}
+
+int w4a16_gemm_grouped(const w4a16_problem *problems, int count, void *stream) {
+  return w4a16_gemm_grouped_ws(problems, count, nullptr, 0, stream);
 }
 
 int w4a16_gemm(const void *X, const void *Wq, const void *scales, const void *zeros,

@@ -26,6 +26,13 @@
 //     scale, in fp32.
 // When S > 1 the S partial sums of a row block are added in a fixed order
 // through LDS, so results are bit-reproducible run to run.
+//
+// X * s of all K columns fits in LDS for decode and short rows; when it does
+// not (long rows at M > 1: the verify and batched-decode shapes), the
+// workgroup walks K in windows instead.  A window is S chunks: the S waves of
+// a row block take one chunk each, all row blocks of the workgroup share the
+// window, and the next window's X * s is loaded into registers while the
+// current one is multiplied, then written over it between two LDS barriers.
 #include "w4a16_device.h"
 #include "w4a16_internal.h"
 
@@ -89,11 +96,14 @@ __device__ __forceinline__ T *uniform_ptr(T *p) {
 
 __device__ __forceinline__ int uniform_int(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-template <bool X_LDS, int kGW, int kWaves, int kDepth>
-__global__ __launch_bounds__(kWaves * 64) void skinny_kernel(ProblemSet ps) {
-  extern __shared__ __attribute__((aligned(16))) _Float16 xs[];
-  __shared__ float red[kWaves][16][17];
+// Barrier for LDS traffic only: waits for this wave's LDS operations, not for
+// its outstanding global loads (which stay in flight across the barrier).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
+// The problem this workgroup works on, with every field in scalar registers.
+__device__ __forceinline__ Problem find_problem(const ProblemSet &ps) {
   int pi = 0;
 #pragma unroll
   for (int i = 1; i < kMaxProblems; ++i)
@@ -106,8 +116,55 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_kernel(ProblemSet ps) {
   P.s = uniform_ptr(ps.p[pi].s);
   P.Y = uniform_ptr(ps.p[pi].Y);
   P.block0 = uniform_int(ps.p[pi].block0);
-  const int M = uniform_int(ps.p[pi].M), N = uniform_int(ps.p[pi].N);
-  const int K = uniform_int(ps.p[pi].K), S = uniform_int(ps.p[pi].split);
+  P.M = uniform_int(ps.p[pi].M);
+  P.N = uniform_int(ps.p[pi].N);
+  P.K = uniform_int(ps.p[pi].K);
+  P.split = uniform_int(ps.p[pi].split);
+  return P;
+}
+
+// Lane (c, r) holds D[m = 4c + v][n = r] of row block b summed over this
+// wave's groups.  With S waves per row block the partial sums are added in
+// the fixed order ks = 0, 1, ..., S - 1.  Every wave of the workgroup calls
+// this (it may synchronise the workgroup).
+template <int kWaves>
+__device__ __forceinline__ void store_rows(const Problem &P, float4v acc, int b, bool has_rows,
+                                           int wave, int ks, int c, int r,
+                                           float (*red)[16][17]) {
+  const int M = P.M, N = P.N, S = P.split;
+  if (S == 1) {
+    if (has_rows) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = 4 * c + v;
+        if (m < M) P.Y[(size_t)m * N + (size_t)b * kTileRows + r] = (_Float16)acc[v];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) red[wave][4 * c + v][r] = acc[v];
+    __syncthreads();
+    if (ks == 0 && has_rows) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = 4 * c + v;
+        if (m < M) {
+          float sum = 0.f;
+          for (int w = 0; w < S; ++w) sum += red[wave + w][m][r];
+          P.Y[(size_t)m * N + (size_t)b * kTileRows + r] = (_Float16)sum;
+        }
+      }
+    }
+  }
+}
+
+template <bool X_LDS, int kGW, int kWaves, int kDepth>
+__global__ __launch_bounds__(kWaves * 64) void skinny_kernel(ProblemSet ps) {
+  extern __shared__ __attribute__((aligned(16))) _Float16 xs[];
+  __shared__ float red[kWaves][16][17];
+
+  const Problem P = find_problem(ps);
+  const int M = P.M, N = P.N, K = P.K, S = P.split;
   const int G = K / kGroup, NB = N / kTileRows;
   const int lane = threadIdx.x & 63, wave = uniform_int(threadIdx.x >> 6);
   const int c = lane >> 4;   // column octet (A/B operands), row quad (D)
@@ -248,31 +305,163 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_kernel(ProblemSet ps) {
     }
   }
 
-  // lane holds D[m = 4c + v][n = r] of row block b, summed over this wave's groups
-  if (S == 1) {
-    if (has_rows) {
+  store_rows<kWaves>(P, acc, b, has_rows, wave, ks, c, r, red);
+}
+
+// Windowed variant: X * s staged one window of S chunks at a time (see the
+// header).  kSlots bounds the 8-column pieces of a window each thread stages.
+template <int kGW, int kWaves, int kDepth, int kSlots>
+__global__ __launch_bounds__(kWaves * 64) void skinny_window_kernel(ProblemSet ps) {
+  extern __shared__ __attribute__((aligned(16))) _Float16 xs[];
+  __shared__ float red[kWaves][16][17];
+  constexpr int kThreads = kWaves * 64;
+
+  const Problem P = find_problem(ps);
+  const int M = P.M, N = P.N, K = P.K, S = P.split;
+  const int G = K / kGroup, NB = N / kTileRows;
+  const int lane = threadIdx.x & 63, wave = uniform_int(threadIdx.x >> 6);
+  const int c = lane >> 4, r = lane & 15;
+  const int b = ((int)blockIdx.x - P.block0) * (kWaves / S) + wave / S;
+  const int ks = wave % S;
+  const bool has_rows = b < NB;
+  const int bb = has_rows ? b : NB - 1;
+  const int chunks = (G + kGW - 1) / kGW;
+  const int steps = (chunks + S - 1) / S;  // windows
+  const int wcols = S * kGW * kGroup;      // columns per window
+  const int ldx = wcols + kLdsPad;
+
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)P.Wq, (short)0, (int)min((size_t)0x7fffffff, (size_t)N * K / 2), kRsrcWord3);
+  const int Gq = meta_groups(G) / kMetaQuad;
+  const size_t meta_bytes = (size_t)N * Gq * kMetaQuad * 2;
+  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)P.scales, (short)0, (int)min((size_t)0x7fffffff, meta_bytes), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t zrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)P.zeros, (short)0, (int)min((size_t)0x7fffffff, meta_bytes), kRsrcWord3);
+  const int tile_off = bb * G * kTileBytes + lane * 16;
+  const int meta_off = ((bb * Gq) * kTileRows + r) * kMetaQuad * 2;
+
+  static_assert(kGW % kMetaQuad == 0, "a chunk is whole metadata quads");
+  constexpr int kQ = kGW / kMetaQuad;
+  u32x4 code[kDepth][kGW];
+  uint32_t sq[kDepth][2 * kQ], zq[kDepth][2 * kQ];
+  auto load_chunk = [&](int slot, int g0) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int m = 4 * c + v;
-        if (m < M) P.Y[(size_t)m * N + (size_t)b * kTileRows + r] = (_Float16)acc[v];
+    for (int i = 0; i < kGW; ++i)
+      code[slot][i] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrs, tile_off, (g0 + i) * kTileBytes, 0));
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) {
+      const int qoff = (g0 / kMetaQuad + q) * kTileRows * kMetaQuad * 2;
+      const auto sv = __builtin_amdgcn_raw_buffer_load_b64(srs, meta_off, qoff, 0);
+      const auto zv = __builtin_amdgcn_raw_buffer_load_b64(zrs, meta_off, qoff, 0);
+      sq[slot][2 * q] = (uint32_t)sv[0];
+      sq[slot][2 * q + 1] = (uint32_t)sv[1];
+      zq[slot][2 * q] = (uint32_t)zv[0];
+      zq[slot][2 * q + 1] = (uint32_t)zv[1];
+    }
+  };
+  // first group of this wave's chunk in window j (may be >= G: nothing to do)
+  auto chunk_g0 = [&](int j) { return (j * S + ks) * kGW; };
+
+  // Staging map: thread -> one 8-column piece of the window (cs) and rows
+  // r0, r0 + rstep, ...  The window's eighths (S * kGW * 16, a power of two
+  // no larger than kThreads) divide kThreads.  Columns past K read zeros
+  // (buffer loads out of range), and are never multiplied.
+  const int c8 = wcols / 8;
+  const int cs = (int)threadIdx.x & (c8 - 1), r0 = (int)threadIdx.x / c8, rstep = kThreads / c8;
+  const __amdgpu_buffer_rsrc_t xrs =
+      __builtin_amdgcn_make_buffer_rsrc((void *)P.X, (short)0, M * K * 2, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t ssr =
+      __builtin_amdgcn_make_buffer_rsrc((void *)P.s, (short)0, P.s ? K * 2 : 0, kRsrcWord3);
+  half8 xr[kSlots], sv;
+  auto load_window = [&](int w) {
+    const int k = w * wcols + cs * 8;
+    const int koff = k < K ? 2 * k : 2 * M * K;  // past K: out of range, reads zeros
+    if (P.s) {
+      sv = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(ssr, k < K ? 2 * k : 2 * K, 0, 0));
+    } else {
+      const _Float16 one = (_Float16)1.0f;
+      sv = (half8){one, one, one, one, one, one, one, one};
+    }
+#pragma unroll
+    for (int i = 0; i < kSlots; ++i) {
+      // rows past M read zeros too (out of range); they are not written to LDS
+      const int m = r0 + i * rstep;
+      xr[i] = __builtin_bit_cast(
+          half8, __builtin_amdgcn_raw_buffer_load_b128(xrs, m < M ? koff + 2 * m * K : 2 * M * K, 0, 0));
+    }
+  };
+  auto store_window = [&]() {
+#pragma unroll
+    for (int i = 0; i < kSlots; ++i) {
+      const int m = r0 + i * rstep;
+      if (m < M) *reinterpret_cast<half8 *>(&xs[m * ldx + cs * 8]) = xr[i] * sv;
+    }
+  };
+
+  // Every step issues the same loads, also past the last window or chunk
+  // (bounds-checked buffer loads; the data is never used), so that the
+  // compiler's wait counts are the same on every path through the loop.
+  load_window(0);
+#pragma unroll
+  for (int d = 0; d < kDepth; ++d) load_chunk(d, chunk_g0(d));
+  store_window();
+  lds_barrier();
+  load_window(1);
+
+  // rows m >= M of the A operand only feed rows of D that are not stored
+  const _Float16 *xrow = xs + min(r, M - 1) * ldx + ks * kGW * kGroup + 8 * c;
+  const uint32_t m_lo = 0x000F000Fu, m_hi = 0x00F000F0u, magic = kMagic2;
+  float4v acc = {0.f, 0.f, 0.f, 0.f};
+  // Issue order per step: this wave's next chunk, then (after the window
+  // swap) the window after next.  Each wait then leaves only younger loads in
+  // flight: the weights for the window's X, that X for the next weights.
+  for (int j = 0; j < steps; ++j) {
+    u32x4 cur[kGW];
+    half2v cs2[2 * kQ], cz2[2 * kQ];
+#pragma unroll
+    for (int i = 0; i < kGW; ++i) cur[i] = code[0][i];
+#pragma unroll
+    for (int q = 0; q < 2 * kQ; ++q) {
+      cs2[q] = as_half2(sq[0][q]);
+      cz2[q] = as_half2(zq[0][q]);
+    }
+#pragma unroll
+    for (int d = 0; d + 1 < kDepth; ++d) {
+#pragma unroll
+      for (int i = 0; i < kGW; ++i) code[d][i] = code[d + 1][i];
+#pragma unroll
+      for (int q = 0; q < 2 * kQ; ++q) {
+        sq[d][q] = sq[d + 1][q];
+        zq[d][q] = zq[d + 1][q];
       }
     }
-  } else {
+    load_chunk(kDepth - 1, chunk_g0(j + kDepth));
+
+    const int g0 = chunk_g0(j);
+    if (has_rows && g0 < G) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) red[wave][4 * c + v][r] = acc[v];
-    __syncthreads();
-    if (ks == 0 && has_rows) {
+      for (int i = 0; i < kGW; ++i) {
+        if (g0 + i < G) {
+          const _Float16 zp = cz2[i >> 1][i & 1], sc = cs2[i >> 1][i & 1];
+          const _Float16 blo = (_Float16)1024.0f + zp, bhi = (_Float16)64.0f + zp;
+          const half2v bias_lo = {blo, blo}, bias_hi = {bhi, bhi};
+          float4v tmp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int m = 4 * c + v;
-        if (m < M) {
-          float sum = 0.f;
-          for (int w = 0; w < S; ++w) sum += red[wave + w][m][r];
-          P.Y[(size_t)m * N + (size_t)b * kTileRows + r] = (_Float16)sum;
+          for (int t = 0; t < 4; ++t)
+            tmp = mfma16(*reinterpret_cast<const half8 *>(xrow + i * kGroup + 32 * t),
+                         decode_word9(cur[i][t], m_lo, m_hi, magic, bias_lo, bias_hi), tmp);
+          acc += tmp * (float)sc;
         }
       }
     }
+    lds_barrier();  // every wave is done with window j
+    store_window();
+    lds_barrier();
+    load_window(j + 2);
   }
+  store_rows<kWaves>(P, acc, b, has_rows, wave, ks, c, r, red);
 }
 
 // LDS bytes to stage X * s (plus the zero row) of one problem.
@@ -291,8 +480,37 @@ constexpr int kChunk = W4A16_SKINNY_CHUNK;  // groups per chunk (weight loads in
 #endif
 constexpr int kWaves = W4A16_SKINNY_WAVES;  // waves per workgroup
 constexpr int kDepth = W4A16_SKINNY_DEPTH;  // chunks in flight per wave
+#ifndef W4A16_SKINNY_WINDOW
+#define W4A16_SKINNY_WINDOW 3
+#endif
+// 0: never window (global X loads when X * s does not fit), 1: window the
+// problems whose X * s does not fit, 2: always window, 3: window the whole call
+// when one problem does not fit
+constexpr int kWindowMode = W4A16_SKINNY_WINDOW;
+#ifndef W4A16_SKINNY_WINDOW_KB
+#define W4A16_SKINNY_WINDOW_KB 72
+#endif
+#ifndef W4A16_SKINNY_WINDOW_SLOTS
+#define W4A16_SKINNY_WINDOW_SLOTS 8
+#endif
+constexpr size_t kMaxWindowBytes = W4A16_SKINNY_WINDOW_KB * 1024;  // 72 KB: two workgroups per CU
+constexpr int kWindowSlots = W4A16_SKINNY_WINDOW_SLOTS;  // staged 8-column pieces per thread
 constexpr int kTargetWaves = 2048;     // enough waves in flight to cover HBM latency
 constexpr int kMaxGroupsPerWave = 32;  // longer rows are split across waves
+
+// LDS bytes of one window of S chunks, M rows.
+size_t window_bytes(int M, int S) {
+  return (size_t)M * (S * kChunk * kGroup + kLdsPad) * sizeof(_Float16);
+}
+
+// 8-column pieces of a window each thread stages (0: the window is wider than
+// the workgroup has threads).
+int window_slots(int M, int S) {
+  const int c8 = S * kChunk * kGroup / 8, threads = kWaves * 64;
+  if (c8 > threads) return 0;
+  const int rstep = threads / c8;
+  return (M + rstep - 1) / rstep;
+}
 
 int pow2_at_least(int v) {
   int p = 1;
@@ -304,12 +522,15 @@ int pow2_at_least(int v) {
 
 int skinny_max_problems() { return kMaxProblems; }
 
-hipError_t launch_skinny_set(const SkinnyDesc *d, int count, hipStream_t stream) {
-  if (count < 1 || count > kMaxProblems) return hipErrorInvalidValue;
+namespace {
+
+// One launch over the problems d[0..count): whole-row X * s staging or K windows.
+hipError_t launch_group(const GemmDesc *const *d, int count, bool window, hipStream_t stream) {
+  if (count == 0) return hipSuccess;
   // How many waves share a row block: enough waves in the whole launch to keep
   // HBM busy, and no wave walking more than kMaxGroupsPerWave groups.
   long long rows = 0;
-  for (int i = 0; i < count; ++i) rows += d[i].N / kTileRows;
+  for (int i = 0; i < count; ++i) rows += d[i]->N / kTileRows;
   const int s_fill =
       (int)min((long long)kWaves, (long long)pow2_at_least((int)((kTargetWaves + rows - 1) / rows)));
   // Problems are laid out longest-rows first so that the waves with the most
@@ -317,7 +538,7 @@ hipError_t launch_skinny_set(const SkinnyDesc *d, int count, hipStream_t stream)
   int order[kMaxProblems];
   for (int i = 0; i < count; ++i) order[i] = i;
   for (int i = 1; i < count; ++i)
-    for (int j = i; j > 0 && d[order[j]].K > d[order[j - 1]].K; --j) {
+    for (int j = i; j > 0 && d[order[j]]->K > d[order[j - 1]]->K; --j) {
       const int t = order[j];
       order[j] = order[j - 1];
       order[j - 1] = t;
@@ -326,12 +547,16 @@ hipError_t launch_skinny_set(const SkinnyDesc *d, int count, hipStream_t stream)
   int blocks = 0;
   size_t lds = 0;
   for (int i = 0; i < count; ++i) {
-    const SkinnyDesc &q = d[order[i]];
+    const GemmDesc &q = *d[order[i]];
     Problem &p = ps.p[i];
     const int G = q.K / kGroup, NB = q.N / kTileRows;
     int split = s_fill;
     while (split < kWaves && (G + split - 1) / split > kMaxGroupsPerWave) split *= 2;
     while (split > 1 && (G + kChunk - 1) / kChunk < split) split /= 2;  // a chunk per wave
+    if (window)  // a window of split chunks must fit in LDS and in the staging registers
+      while (split > 1 && (window_bytes(q.M, split) > kMaxWindowBytes ||
+                           window_slots(q.M, split) < 1 || window_slots(q.M, split) > kWindowSlots))
+        split /= 2;
     p.X = static_cast<const _Float16 *>(q.X);
     p.Wq = static_cast<const uint8_t *>(q.Wq);
     p.scales = static_cast<const _Float16 *>(q.scales);
@@ -345,11 +570,14 @@ hipError_t launch_skinny_set(const SkinnyDesc *d, int count, hipStream_t stream)
     p.block0 = blocks;
     const int rb_per_wg = kWaves / split;
     blocks += (NB + rb_per_wg - 1) / rb_per_wg;
-    const size_t need = stage_bytes(q.M, q.K);
+    const size_t need = window ? window_bytes(q.M, split) : stage_bytes(q.M, q.K);
     lds = need > lds ? need : lds;
   }
   ps.count = count;
-  if (lds <= kMaxStageBytes)
+  if (window)
+    hipLaunchKernelGGL((skinny_window_kernel<kChunk, kWaves, kDepth, kWindowSlots>), dim3(blocks),
+                       dim3(kWaves * 64), lds, stream, ps);
+  else if (lds <= kMaxStageBytes)
     hipLaunchKernelGGL((skinny_kernel<true, kChunk, kWaves, kDepth>), dim3(blocks),
                        dim3(kWaves * 64), lds, stream, ps);
   else
@@ -358,9 +586,37 @@ hipError_t launch_skinny_set(const SkinnyDesc *d, int count, hipStream_t stream)
   return hipGetLastError();
 }
 
+}  // namespace
+
+hipError_t launch_skinny_set(const GemmDesc *d, int count, hipStream_t stream,
+                             bool force_window) {
+  if (count < 1 || count > kMaxProblems) return hipErrorInvalidValue;
+  // By default the whole launch uses windows as soon as one problem's X * s does
+  // not fit: one launch over all problems beats a second, smaller one.  Like
+  // the split factor, the choice depends on all problems of the call, so a
+  // problem's bits can differ between a grouped and a single call (both stay
+  // within rounding of the exact result; each call is reproducible).
+  const GemmDesc *whole[kMaxProblems], *windowed[kMaxProblems];
+  int nwhole = 0, nwin = 0;
+  bool any = false;
+  for (int i = 0; i < count; ++i) any |= stage_bytes(d[i].M, d[i].K) > kMaxStageBytes;
+  for (int i = 0; i < count; ++i) {
+    const bool fits = stage_bytes(d[i].M, d[i].K) <= kMaxStageBytes;
+    const bool win = force_window || kWindowMode == 2 || (kWindowMode == 1 && !fits) ||
+                     (kWindowMode == 3 && any);
+    if (win)
+      windowed[nwin++] = d + i;
+    else
+      whole[nwhole++] = d + i;
+  }
+  hipError_t err = launch_group(windowed, nwin, true, stream);
+  if (err == hipSuccess) err = launch_group(whole, nwhole, false, stream);
+  return err;
+}
+
 hipError_t launch_skinny(const void *X, const void *Wq, const void *scales, const void *zeros,
                          const void *s, void *Y, int M, int N, int K, hipStream_t stream) {
-  const SkinnyDesc d = {X, Wq, scales, zeros, s, Y, M, N, K};
+  const GemmDesc d = {X, Wq, scales, zeros, s, Y, M, N, K};
   return launch_skinny_set(&d, 1, stream);
 }
 

@@ -17,6 +17,14 @@
 //     to exact (q - z) and multiplies by the group scale in fp16 -- the
 //     weight-only "dequantize to FP16, then multiply" of "Chapter 22"
 //     (aiwing.uk) section 22.3 -- just before use.
+//
+// Several problems share one launch (a layer's projections), and when the
+// blocks of a call would leave CUs idle (few output blocks, long K: batched
+// decode, small projections) K is split across workgroups: each split writes
+// its fp32 partial block to a caller-provided workspace and a second small
+// kernel adds the splits in a fixed order and rounds to fp16 once, so results
+// are reproducible run to run.
+#include <algorithm>
 #include <type_traits>
 
 #include "w4a16_device.h"
@@ -58,13 +66,68 @@ __device__ __forceinline__ half8 dequant_word(uint32_t w, half2v bias_lo, half2v
   return r;
 }
 
+constexpr int kMaxTiled = 8;  // problems per launch
+
+struct TiledProblem {
+  const _Float16 *X;
+  const uint8_t *Wq;
+  const _Float16 *scales, *zeros, *s;
+  _Float16 *Y;
+  float *part;      // split > 1: split fp32 [M][N] partial slabs
+  int M, N, K;
+  int tiles_n;      // output blocks along N
+  int tiles;        // output blocks (tiles_n * blocks along M)
+  int split;        // K ranges per output block
+  int block0;       // first workgroup of this problem in the GEMM launch
+  int rblock0;      // first workgroup of this problem in the reduction launch
+};
+
+struct TiledSet {
+  TiledProblem p[kMaxTiled];
+  int count;
+};
+
+template <typename T>
+__device__ __forceinline__ T *uniform_ptr(T *p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<T *>(((uint64_t)hi << 32) | lo);
+}
+
+// The problem of workgroup `block` (first workgroups given by `first`), every
+// field in scalar registers.
+template <bool REDUCE>
+__device__ __forceinline__ TiledProblem find_tiled(const TiledSet &ts, int block) {
+  int pi = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxTiled; ++i)
+    if (i < ts.count && block >= (REDUCE ? ts.p[i].rblock0 : ts.p[i].block0)) pi = i;
+  const TiledProblem &q = ts.p[pi];
+  TiledProblem P;
+  P.X = uniform_ptr(q.X);
+  P.Wq = uniform_ptr(q.Wq);
+  P.scales = uniform_ptr(q.scales);
+  P.zeros = uniform_ptr(q.zeros);
+  P.s = uniform_ptr(q.s);
+  P.Y = uniform_ptr(q.Y);
+  P.part = uniform_ptr(q.part);
+  P.M = uniform_int(q.M);
+  P.N = uniform_int(q.N);
+  P.K = uniform_int(q.K);
+  P.tiles_n = uniform_int(q.tiles_n);
+  P.tiles = uniform_int(q.tiles);
+  P.split = uniform_int(q.split);
+  P.block0 = uniform_int(q.block0);
+  P.rblock0 = uniform_int(q.rblock0);
+  return P;
+}
+
 // Two waves per SIMD: with one, the waits on LDS and the barriers are not
 // hidden and MFMA throughput roughly halves (measured on the 70B shapes).
-template <int WM, int WN, int TM, int TN, int KSTAGE, bool HAS_S>
+template <int WM, int WN, int TM, int TN, int KSTAGE>
 __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void tiled_kernel(
-    const _Float16 *__restrict__ X, const uint8_t *__restrict__ Wq,
-    const _Float16 *__restrict__ scales, const _Float16 *__restrict__ zeros,
-    const _Float16 *__restrict__ s, _Float16 *__restrict__ Y, int M, int N, int K) {
+    TiledSet ts) {
   constexpr int THREADS = WM * WN * 64;
   constexpr int BM = WM * TM * 16, BN = WN * TN * 16;
   constexpr int kStageK = KSTAGE;                       // K columns per stage (64 or 128)
@@ -76,13 +139,28 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
   static_assert(BM % ROWS_PER_PASS == 0, "A tile rows must divide evenly");
   __shared__ __attribute__((aligned(16))) _Float16 As[2][BM * kLdsStride];
 
+  const TiledProblem P = find_tiled<false>(ts, (int)blockIdx.x);
+  const _Float16 *__restrict__ X = P.X;
+  const uint8_t *__restrict__ Wq = P.Wq;
+  const _Float16 *__restrict__ scales = P.scales;
+  const _Float16 *__restrict__ zeros = P.zeros;
+  const _Float16 *__restrict__ s = P.s;
+  const bool has_s = s != nullptr;
+  const int M = P.M, N = P.N, K = P.K;
+
   const int tid = threadIdx.x, lane = tid & 63, wave = uniform_int(tid >> 6);
   const int c = lane >> 4, r = lane & 15;
   const int wm = wave / WN, wn = wave % WN;
-  const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
+  // block -> (split sp, output block t); consecutive blocks share a K range
+  // and walk N first, so neighbours share their rows of X
+  const int local = (int)blockIdx.x - P.block0;
+  const int sp = local / P.tiles, t = local - sp * P.tiles;
+  const int mt = t / P.tiles_n;
+  const int n0 = (t - mt * P.tiles_n) * BN, m0 = mt * BM;
   const int G = K / kGroup, NB = N / kTileRows;
   const int Gq = meta_groups(G) / kMetaQuad;
-  const int stages = kStagesPerGroup * G;  // stage st covers columns [KSTAGE st, +KSTAGE)
+  // this block's groups [gb, ge): the split-th of G, in whole groups
+  const int gb = (int)((long long)G * sp / P.split), ge = (int)((long long)G * (sp + 1) / P.split);
 
   // ---- X * s staging: thread covers one 16-byte column chunk of rows a_row + pass*ROWS_PER_PASS
   const int a_col = (tid % kChunksPerRow) * 8;
@@ -93,7 +171,7 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
   half8 areg[A_PER_T], sreg;
   auto load_a = [&](int st) {
     const int k0 = st * kStageK + a_col;
-    if (HAS_S) sreg = load_half8(s + k0);
+    if (has_s) sreg = load_half8(s + k0);
 #pragma unroll
     for (int i = 0; i < A_PER_T; ++i) {
       const int m = min(m0 + a_row + i * ROWS_PER_PASS, M - 1);
@@ -104,7 +182,7 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
 #pragma unroll
     for (int i = 0; i < A_PER_T; ++i) {
       half8 v = areg[i];
-      if (HAS_S) v = v * sreg;
+      if (has_s) v = v * sreg;
       if (m0 + a_row + i * ROWS_PER_PASS >= M) v = zero_half8();
       *reinterpret_cast<half8 *>(&As[buf][(a_row + i * ROWS_PER_PASS) * kLdsStride + a_col]) = v;
     }
@@ -169,17 +247,20 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
     }
   };
 
-  load_a(0);
-  load_b(0, bcode, bsc, bzp);
+  // stage st covers columns [KSTAGE st, +KSTAGE); this block's stages end at
+  const int stages = kStagesPerGroup * ge;
+  load_a(kStagesPerGroup * gb);
+  load_b(gb, bcode, bsc, bzp);
   store_a(0);
   lds_barrier();
-  // One group per iteration, kStagesPerGroup stages; stage st uses LDS buffer
-  // st % 2.  The next group's codes are loaded during the first stage and moved
-  // into place at the end of the group.
-  for (int g = 0; g < G; ++g) {
+  // One group per iteration, kStagesPerGroup stages; stage st of the block
+  // uses LDS buffer st % 2 (counted from the block's first stage).  The next
+  // group's codes are loaded during the first stage and moved into place at
+  // the end of the group.
+  for (int g = gb; g < ge; ++g) {
     const int st = kStagesPerGroup * g;
     if (st + 1 < stages) load_a(st + 1);
-    if (g + 1 < G) load_b(g + 1, bnext, bsc_next, bzp_next);
+    if (g + 1 < ge) load_b(g + 1, bnext, bsc_next, bzp_next);
     if constexpr (kStagesPerGroup == 2) {
       compute_stage(std::integral_constant<int, 0>(), bcode, bsc, bzp, 0);
       store_a(1);
@@ -188,8 +269,8 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
       compute_stage(std::integral_constant<int, 1>(), bcode, bsc, bzp, 1);
       if (st + 2 < stages) store_a(0);
     } else {
-      compute_stage(std::integral_constant<int, 0>(), bcode, bsc, bzp, g & 1);
-      if (st + 1 < stages) store_a((g + 1) & 1);
+      compute_stage(std::integral_constant<int, 0>(), bcode, bsc, bzp, (g - gb) & 1);
+      if (st + 1 < stages) store_a((g - gb + 1) & 1);
     }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
@@ -200,7 +281,9 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
     lds_barrier();
   }
 
-  // lane holds D[4c + v][r] of each 16x16 sub-block
+  // lane holds D[4c + v][r] of each 16x16 sub-block: the output, or this
+  // split's fp32 partial
+  float *part = P.split > 1 ? P.part + (size_t)sp * M * N : nullptr;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -209,36 +292,122 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int m = m0 + (wm * TM + i) * 16 + 4 * c + v;
-        if (m < M && n < N) Y[(size_t)m * N + n] = (_Float16)acc[i][j][v];
+        if (m < M && n < N) {
+          if (part)
+            part[(size_t)m * N + n] = acc[i][j][v];
+          else
+            P.Y[(size_t)m * N + n] = (_Float16)acc[i][j][v];
+        }
       }
     }
   }
 }
 
-template <int WM, int WN, int TM, int TN, int KSTAGE>
-hipError_t launch_cfg(const void *X, const void *Wq, const void *scales, const void *zeros,
-                      const void *s, void *Y, int M, int N, int K, hipStream_t stream) {
-  constexpr int BM = WM * TM * 16, BN = WN * TN * 16;
-  const dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM), block(WM * WN * 64);
-  if (s)
-    hipLaunchKernelGGL((tiled_kernel<WM, WN, TM, TN, KSTAGE, true>), grid, block, 0, stream,
-                       (const _Float16 *)X, (const uint8_t *)Wq, (const _Float16 *)scales,
-                       (const _Float16 *)zeros, (const _Float16 *)s, (_Float16 *)Y, M, N, K);
-  else
-    hipLaunchKernelGGL((tiled_kernel<WM, WN, TM, TN, KSTAGE, false>), grid, block, 0, stream,
-                       (const _Float16 *)X, (const uint8_t *)Wq, (const _Float16 *)scales,
-                       (const _Float16 *)zeros, (const _Float16 *)s, (_Float16 *)Y, M, N, K);
-  return hipGetLastError();
+// Y = fp16(sum of the split partials, in split order) for the problems with
+// split > 1; four outputs per thread.
+constexpr int kReduceThreads = 256;
+
+__global__ __launch_bounds__(kReduceThreads) void split_reduce_kernel(TiledSet ts) {
+  const TiledProblem P = find_tiled<true>(ts, (int)blockIdx.x);
+  const long long quads = (long long)P.M * P.N / 4;
+  const long long i = (long long)((int)blockIdx.x - P.rblock0) * kReduceThreads + threadIdx.x;
+  if (i >= quads) return;
+  const float4v *src = reinterpret_cast<const float4v *>(P.part) + i;
+  float4v acc = src[0];
+  for (int k = 1; k < P.split; ++k) acc += src[(size_t)k * quads];
+  typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+  const half4 out = {(_Float16)acc[0], (_Float16)acc[1], (_Float16)acc[2], (_Float16)acc[3]};
+  reinterpret_cast<half4 *>(P.Y)[i] = out;
+}
+
+// 64 x 256 blocks of 4 waves (64 x 64 each), one group per stage, two
+// workgroups per CU: the fastest of the measured shapes and stage widths at
+// every M of the workloads.
+constexpr int kWM = 1, kWN = 4, kTM = 4, kTN = 4, kStage = 128;
+constexpr int kBM = kWM * kTM * 16, kBN = kWN * kTN * 16;
+constexpr long long kBlockSlots = 256 * 2;  // CUs x resident workgroups per CU
+constexpr int kMinSplitGroups = 8;          // no split shorter than this many groups
+constexpr int kMaxSplit = 16;
+
+int tiles_of(const GemmDesc &d) { return ((d.N + kBN - 1) / kBN) * ((d.M + kBM - 1) / kBM); }
+
+size_t part_bytes(const GemmDesc &d, int split) {
+  return split > 1 ? ((size_t)split * d.M * d.N * sizeof(float) + 255) / 256 * 256 : 0;
+}
+
+// K splits of each problem of one launch: enough workgroups to fill every
+// slot, and no workgroup longer than the launch's average share of groups.
+void choose_splits(const GemmDesc *d, int count, int *split) {
+  long long units = 0;
+  for (int i = 0; i < count; ++i) units += (long long)tiles_of(d[i]) * (d[i].K / kGroup);
+  const long long target = std::max<long long>(kMinSplitGroups, (units + kBlockSlots - 1) / kBlockSlots);
+  for (int i = 0; i < count; ++i) {
+    const long long G = d[i].K / kGroup;
+    split[i] = (int)std::min<long long>(std::min<long long>(kMaxSplit, G), (G + target - 1) / target);
+    if (split[i] < 1) split[i] = 1;
+  }
 }
 
 }  // namespace
 
+size_t tiled_workspace_bytes(const GemmDesc *d, int count) {
+  if (count < 1 || count > kMaxTiled) return 0;
+  int split[kMaxTiled];
+  choose_splits(d, count, split);
+  size_t bytes = 0;
+  for (int i = 0; i < count; ++i) bytes += part_bytes(d[i], split[i]);
+  return bytes;
+}
+
+int tiled_max_problems() { return kMaxTiled; }
+
+hipError_t launch_tiled_set(const GemmDesc *d, int count, void *workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+  if (count < 1 || count > kMaxTiled) return hipErrorInvalidValue;
+  int split[kMaxTiled];
+  choose_splits(d, count, split);
+  if (!workspace || workspace_bytes < tiled_workspace_bytes(d, count))
+    for (int i = 0; i < count; ++i) split[i] = 1;  // no room for partials: one K range
+  TiledSet ts = {};
+  int blocks = 0, rblocks = 0;
+  size_t off = 0;
+  for (int i = 0; i < count; ++i) {
+    TiledProblem &p = ts.p[i];
+    p.X = static_cast<const _Float16 *>(d[i].X);
+    p.Wq = static_cast<const uint8_t *>(d[i].Wq);
+    p.scales = static_cast<const _Float16 *>(d[i].scales);
+    p.zeros = static_cast<const _Float16 *>(d[i].zeros);
+    p.s = static_cast<const _Float16 *>(d[i].s);
+    p.Y = static_cast<_Float16 *>(d[i].Y);
+    p.M = d[i].M;
+    p.N = d[i].N;
+    p.K = d[i].K;
+    p.tiles_n = (d[i].N + kBN - 1) / kBN;
+    p.tiles = tiles_of(d[i]);
+    p.split = split[i];
+    p.part = split[i] > 1 ? reinterpret_cast<float *>(static_cast<char *>(workspace) + off) : nullptr;
+    off += part_bytes(d[i], split[i]);
+    p.block0 = blocks;
+    blocks += p.tiles * p.split;
+    p.rblock0 = rblocks;
+    if (split[i] > 1)
+      rblocks += (int)(((long long)d[i].M * d[i].N / 4 + kReduceThreads - 1) / kReduceThreads);
+  }
+  ts.count = count;
+  hipLaunchKernelGGL((tiled_kernel<kWM, kWN, kTM, kTN, kStage>), dim3(blocks), dim3(kWM * kWN * 64),
+                     0, stream, ts);
+  hipError_t err = hipGetLastError();
+  if (err == hipSuccess && rblocks > 0) {
+    hipLaunchKernelGGL(split_reduce_kernel, dim3(rblocks), dim3(kReduceThreads), 0, stream, ts);
+    err = hipGetLastError();
+  }
+  return err;
+}
+
 hipError_t launch_tiled(const void *X, const void *Wq, const void *scales, const void *zeros,
                         const void *s, void *Y, int M, int N, int K, hipStream_t stream) {
-  // 64 x 256 blocks of 4 waves (64 x 64 each), one group per stage, two
-  // workgroups per CU: the fastest of the measured shapes and stage widths at
-  // every M of the workloads.
-  return launch_cfg<1, 4, 4, 4, 128>(X, Wq, scales, zeros, s, Y, M, N, K, stream);
+  const GemmDesc d = {X, Wq, scales, zeros, s, Y, M, N, K};
+  return launch_tiled_set(&d, 1, nullptr, 0, stream);
 }
 
 }  // namespace w4a16

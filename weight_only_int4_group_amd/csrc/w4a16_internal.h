@@ -13,8 +13,8 @@ constexpr unsigned kPackRange = 2u;
 hipError_t launch_pack(const void *W, const void *s, int N, int K, void *Wq, void *scales,
                        void *zeros, unsigned *status, hipStream_t stream);
 
-// One problem of the streaming kernel (validated by the caller).
-struct SkinnyDesc {
+// One dequantize-matmul problem (validated by the caller).
+struct GemmDesc {
   const void *X, *Wq, *scales, *zeros, *s;
   void *Y;
   int M, N, K;
@@ -22,13 +22,24 @@ struct SkinnyDesc {
 
 // Streaming kernel for small M (decode and speculative verify): M <= 16.
 // launch_skinny_set runs up to skinny_max_problems() independent problems in
-// one launch.
+// one launch; X * s is staged in K windows when it does not fit in LDS whole,
+// or always with force_window.
 int skinny_max_problems();
-hipError_t launch_skinny_set(const SkinnyDesc *problems, int count, hipStream_t stream);
+hipError_t launch_skinny_set(const GemmDesc *problems, int count, hipStream_t stream,
+                             bool force_window = false);
 hipError_t launch_skinny(const void *X, const void *Wq, const void *scales, const void *zeros,
                          const void *s, void *Y, int M, int N, int K, hipStream_t stream);
 
 // LDS-tiled MFMA GEMM for large M (batched decode and prefill): any M >= 1.
+// launch_tiled_set runs up to tiled_max_problems() problems in one launch.
+// When the workspace holds tiled_workspace_bytes() for the same problems, K
+// is split across workgroups where that fills the GPU better (fp32 partials
+// in the workspace, then a second launch adds them); otherwise (NULL, or too
+// small) every output block walks all of K.
+int tiled_max_problems();
+size_t tiled_workspace_bytes(const GemmDesc *problems, int count);
+hipError_t launch_tiled_set(const GemmDesc *problems, int count, void *workspace,
+                            size_t workspace_bytes, hipStream_t stream);
 hipError_t launch_tiled(const void *X, const void *Wq, const void *scales, const void *zeros,
                         const void *s, void *Y, int M, int N, int K, hipStream_t stream);
 
