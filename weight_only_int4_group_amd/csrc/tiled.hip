@@ -5,16 +5,18 @@
 // large matmul bounded by arithmetic, so this kernel is organised around the
 // MFMA units.  A workgroup of WM x WN waves owns a BM x BN block of Y; each
 // wave owns TM x TN 16x16 sub-blocks (TM*16 rows of X, TN*16 rows of W) and
-// accumulates them in fp32 with 16x16x32 fp16 MFMAs.  K is walked in stages
-// of KSTAGE columns (one quantization group, or half of one):
+// accumulates them in fp32 with 16x16x32 fp16 MFMAs.  K is walked one
+// quantization group (128 columns) per stage:
 //   * X * s for the block's rows (rounded to fp16 once) goes through LDS,
 //     double-buffered: the next stage's global loads are issued before the
 //     current stage's MFMAs and written to the other buffer after them, with
 //     one LDS barrier per stage;
 //   * the packed weight tile layout makes each lane's 32-bit code word its
-//     MFMA B operand, so W never touches LDS: every wave loads its own tiles
-//     one group ahead (a 128-bit load per lane per 16-row tile), decodes them
-//     to exact (q - z) and multiplies by the group scale in fp16 -- the
+//     MFMA B operand, so W is never rearranged: every wave fetches its own
+//     tiles one group ahead (16 bytes per lane per 16-row tile, copied
+//     unchanged into the wave's LDS slots by DMA loads, which costs no
+//     registers while in flight), takes them into registers, decodes them to
+//     exact (q - z) and multiplies by the group scale in fp16 -- the
 //     weight-only "dequantize to FP16, then multiply" of "Chapter 22"
 //     (aiwing.uk) section 22.3 -- just before use.
 //
@@ -25,7 +27,6 @@
 // kernel adds the splits in a fixed order and rounds to fp16 once, so results
 // are reproducible run to run.
 #include <algorithm>
-#include <type_traits>
 
 #include "w4a16_device.h"
 #include "w4a16_internal.h"
@@ -125,27 +126,26 @@ __device__ __forceinline__ TiledProblem find_tiled(const TiledSet &ts, int block
 
 // Two waves per SIMD: with one, the waits on LDS and the barriers are not
 // hidden and MFMA throughput roughly halves (measured on the 70B shapes).
-template <int WM, int WN, int TM, int TN, int KSTAGE>
+template <int WM, int WN, int TM, int TN>
 __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void tiled_kernel(
     TiledSet ts) {
   constexpr int THREADS = WM * WN * 64;
   constexpr int BM = WM * TM * 16, BN = WN * TN * 16;
-  constexpr int kStageK = KSTAGE;                       // K columns per stage (64 or 128)
-  constexpr int kLdsStride = kStageK + 8;               // halves; the pad spreads rows over banks
-  constexpr int kStagesPerGroup = kGroup / kStageK;
-  constexpr int kChunksPerRow = kStageK / 8;            // 16-byte chunks per A row per stage
+  constexpr int kLdsStride = kGroup + 8;                  // halves; the pad spreads rows over banks
+  constexpr int kChunksPerRow = kGroup / 8;               // 16-byte chunks per A row per stage
   constexpr int ROWS_PER_PASS = THREADS / kChunksPerRow;  // A rows one load pass covers
-  constexpr int A_PER_T = BM / ROWS_PER_PASS;           // 16-byte A chunks per thread
+  constexpr int A_PER_T = BM / ROWS_PER_PASS;             // 16-byte A chunks per thread
   static_assert(BM % ROWS_PER_PASS == 0, "A tile rows must divide evenly");
   __shared__ __attribute__((aligned(16))) _Float16 As[2][BM * kLdsStride];
 
-  const TiledProblem P = find_tiled<false>(ts, (int)blockIdx.x);
+  const int block = (int)blockIdx.x;
+  const TiledProblem P = find_tiled<false>(ts, block);
   const _Float16 *__restrict__ X = P.X;
   const uint8_t *__restrict__ Wq = P.Wq;
   const _Float16 *__restrict__ scales = P.scales;
   const _Float16 *__restrict__ zeros = P.zeros;
   const _Float16 *__restrict__ s = P.s;
-  const bool has_s = s != nullptr;
+  const bool has_s = s != nullptr;  // else s = 1
   const int M = P.M, N = P.N, K = P.K;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = uniform_int(tid >> 6);
@@ -153,7 +153,7 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
   const int wm = wave / WN, wn = wave % WN;
   // block -> (split sp, output block t); consecutive blocks share a K range
   // and walk N first, so neighbours share their rows of X
-  const int local = (int)blockIdx.x - P.block0;
+  const int local = block - P.block0;
   const int sp = local / P.tiles, t = local - sp * P.tiles;
   const int mt = t / P.tiles_n;
   const int n0 = (t - mt * P.tiles_n) * BN, m0 = mt * BM;
@@ -162,16 +162,22 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
   // this block's groups [gb, ge): the split-th of G, in whole groups
   const int gb = (int)((long long)G * sp / P.split), ge = (int)((long long)G * (sp + 1) / P.split);
 
-  // ---- X * s staging: thread covers one 16-byte column chunk of rows a_row + pass*ROWS_PER_PASS
+  // ---- X * s, one group (128 columns) per stage: a thread covers one 16-byte
+  // column chunk of rows a_row + i * ROWS_PER_PASS.  The loads are
+  // unconditional (rows past M read row M - 1: rows of A only reach the same
+  // rows of D, which are not stored) and nothing uses their results until
+  // store_a, after the stage's MFMAs, so their latency is hidden.
   const int a_col = (tid % kChunksPerRow) * 8;
   const int a_row = tid / kChunksPerRow;
-  // The loads are unconditional (rows past M read row M-1) and nothing uses
-  // their results until store_a, after the stage's MFMAs, so their latency is
-  // hidden; rows past M are zeroed and X * s is formed only then.
   half8 areg[A_PER_T], sreg;
-  auto load_a = [&](int st) {
-    const int k0 = st * kStageK + a_col;
-    if (has_s) sreg = load_half8(s + k0);
+  auto load_a = [&](int g) {
+    const int k0 = g * kGroup + a_col;
+    if (has_s) {
+      sreg = load_half8(s + k0);
+    } else {
+      const _Float16 one = (_Float16)1.0f;
+      sreg = (half8){one, one, one, one, one, one, one, one};  // x * 1 is exact
+    }
 #pragma unroll
     for (int i = 0; i < A_PER_T; ++i) {
       const int m = min(m0 + a_row + i * ROWS_PER_PASS, M - 1);
@@ -181,14 +187,16 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
   auto store_a = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < A_PER_T; ++i) {
-      half8 v = areg[i];
-      if (has_s) v = v * sreg;
-      if (m0 + a_row + i * ROWS_PER_PASS >= M) v = zero_half8();
+      const half8 v = areg[i] * sreg;
       *reinterpret_cast<half8 *>(&As[buf][(a_row + i * ROWS_PER_PASS) * kLdsStride + a_col]) = v;
     }
   };
 
-  // ---- weights: this wave's TN row blocks, loaded a group ahead
+  // ---- weights: this wave's TN row blocks.  The next group's code tiles go
+  // straight from HBM to this wave's own LDS slots (one 16-byte DMA load per
+  // lane per tile, bounds-checked: row blocks past N read zeros and are never
+  // stored), so only the current group's codes occupy registers; scales and
+  // zero points come as raw 16-bit words into one of two register sets.
   const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
       (void *)Wq, (short)0, (int)min((size_t)0x7fffffff, (size_t)N * K / 2), kRsrcWord3);
   const size_t meta_bytes = (size_t)N * Gq * kMetaQuad * 2;
@@ -197,20 +205,22 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
   const __amdgpu_buffer_rsrc_t zrs = __builtin_amdgcn_make_buffer_rsrc(
       (void *)zeros, (short)0, (int)min((size_t)0x7fffffff, meta_bytes), kRsrcWord3);
   const int rb0 = n0 / kTileRows + wn * TN;  // first row block of this wave
-  u32x4 bcode[TN], bnext[TN];
-  // raw fp16 bits of each row block's scale and zero point for the group
-  uint32_t bsc[TN], bzp[TN], bsc_next[TN], bzp_next[TN];
-  auto load_b = [&](int g, u32x4 *code, uint32_t *sc, uint32_t *zp) {
+  __shared__ __attribute__((aligned(16))) uint8_t Bs[2][WM * WN * TN * kTileBytes];
+  struct BRegs {
+    u32x4 code[TN];
+    uint32_t sc[TN], zp[TN];  // raw fp16 bits of each row block's scale and zero point
+  };
+  BRegs b0, b1;
+  auto load_b = [&](int g, int buf, BRegs &b) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      // row blocks past N read zeros (bounds-checked buffer loads) and are never stored
       const int rb = min(rb0 + j, NB);
-      code[j] = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrs, (rb * G * 64 + lane) * 16,
-                                                        g * kTileBytes, 0));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          wrs, (__attribute__((address_space(3))) void *)&Bs[buf][(wave * TN + j) * kTileBytes], 16,
+          (rb * G * 64 + lane) * 16, g * kTileBytes, 0, 0);
       const int mo = ((rb * Gq + g / kMetaQuad) * kTileRows + r) * kMetaQuad * 2;
-      sc[j] = __builtin_amdgcn_raw_buffer_load_b16(srs, mo, (g % kMetaQuad) * 2, 0);
-      zp[j] = __builtin_amdgcn_raw_buffer_load_b16(zrs, mo, (g % kMetaQuad) * 2, 0);
+      b.sc[j] = __builtin_amdgcn_raw_buffer_load_b16(srs, mo, (g % kMetaQuad) * 2, 0);
+      b.zp[j] = __builtin_amdgcn_raw_buffer_load_b16(zrs, mo, (g % kMetaQuad) * 2, 0);
     }
   };
 
@@ -220,23 +230,20 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = float4v{0.f, 0.f, 0.f, 0.f};
 
-  // MFMAs of the k steps of stage h of a group (k steps t = h*KS .. h*KS + KS-1,
-  // KS = KSTAGE / 32) with the group's codes / metadata, reading X from LDS buffer `buf`.
-  constexpr int KS = kStageK / 32;
-  auto compute_stage = [&](auto H, const u32x4 *code, const uint32_t *sc, const uint32_t *zp,
-                           int buf) {
-    constexpr int h = decltype(H)::value;
+  // the four k steps of a group: dequantize this wave's B operands, then
+  // TM x TN MFMAs reading A from LDS buffer `buf`
+  auto compute = [&](const BRegs &b, int buf) {
     const _Float16 *abuf = As[buf] + (wm * TM * 16 + r) * kLdsStride + 8 * c;
 #pragma unroll
-    for (int tt = 0; tt < KS; ++tt) {
+    for (int tt = 0; tt < 4; ++tt) {
       half8 bop[TN];
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const _Float16 z = __builtin_bit_cast(_Float16, (uint16_t)zp[j]);
-        const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)sc[j]);
+        const _Float16 z = __builtin_bit_cast(_Float16, (uint16_t)b.zp[j]);
+        const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)b.sc[j]);
         const _Float16 blo = (_Float16)1024.0f + z, bhi = (_Float16)64.0f + z;
         const half2v bias_lo = {blo, blo}, bias_hi = {bhi, bhi}, scale = {sv, sv};
-        bop[j] = dequant_word(code[j][h * KS + tt], bias_lo, bias_hi, scale);
+        bop[j] = dequant_word(b.code[j][tt], bias_lo, bias_hi, scale);
       }
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
@@ -245,40 +252,39 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
         for (int j = 0; j < TN; ++j) acc[i][j] = mfma16(aop, bop[j], acc[i][j]);
       }
     }
+    // let the scheduler interleave the MFMAs with the dequantization and LDS
+    // reads around them (LLVM's single-wave small-GEMM strategy; measured
+    // best of the available strategies and of hand-placed group barriers)
+    __builtin_amdgcn_iglp_opt(1);
   };
 
-  // stage st covers columns [KSTAGE st, +KSTAGE); this block's stages end at
-  const int stages = kStagesPerGroup * ge;
-  load_a(kStagesPerGroup * gb);
-  load_b(gb, bcode, bsc, bzp);
+  // One group per step.  The group's codes and metadata were issued a step
+  // ago: wait for them (the only loads in flight) and take the codes into
+  // registers; then issue the next group's X and weight loads, run this
+  // group's MFMAs, and write the next X * s to the other LDS buffer.  Steps
+  // alternate LDS buffers and metadata register sets, two steps per
+  // iteration, so nothing is copied between them.
+  auto step = [&](int g, BRegs &cur, BRegs &nxt, int buf) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the DMA writes are not seen by the compiler
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+      cur.code[j] = *reinterpret_cast<const u32x4 *>(&Bs[buf][(wave * TN + j) * kTileBytes + lane * 16]);
+    const bool more = g + 1 < ge;
+    if (more) {
+      load_a(g + 1);
+      load_b(g + 1, buf ^ 1, nxt);
+    }
+    compute(cur, buf);
+    if (more) store_a(buf ^ 1);
+    lds_barrier();
+  };
+  load_a(gb);
+  load_b(gb, 0, b0);
   store_a(0);
   lds_barrier();
-  // One group per iteration, kStagesPerGroup stages; stage st of the block
-  // uses LDS buffer st % 2 (counted from the block's first stage).  The next
-  // group's codes are loaded during the first stage and moved into place at
-  // the end of the group.
-  for (int g = gb; g < ge; ++g) {
-    const int st = kStagesPerGroup * g;
-    if (st + 1 < stages) load_a(st + 1);
-    if (g + 1 < ge) load_b(g + 1, bnext, bsc_next, bzp_next);
-    if constexpr (kStagesPerGroup == 2) {
-      compute_stage(std::integral_constant<int, 0>(), bcode, bsc, bzp, 0);
-      store_a(1);
-      lds_barrier();
-      if (st + 2 < stages) load_a(st + 2);
-      compute_stage(std::integral_constant<int, 1>(), bcode, bsc, bzp, 1);
-      if (st + 2 < stages) store_a(0);
-    } else {
-      compute_stage(std::integral_constant<int, 0>(), bcode, bsc, bzp, (g - gb) & 1);
-      if (st + 1 < stages) store_a((g - gb + 1) & 1);
-    }
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      bcode[j] = bnext[j];
-      bsc[j] = bsc_next[j];
-      bzp[j] = bzp_next[j];
-    }
-    lds_barrier();
+  for (int g = gb; g < ge; g += 2) {
+    step(g, b0, b1, 0);
+    if (g + 1 < ge) step(g + 1, b1, b0, 1);
   }
 
   // lane holds D[4c + v][r] of each 16x16 sub-block: the output, or this
@@ -320,12 +326,20 @@ __global__ __launch_bounds__(kReduceThreads) void split_reduce_kernel(TiledSet t
   reinterpret_cast<half4 *>(P.Y)[i] = out;
 }
 
-// 64 x 256 blocks of 4 waves (64 x 64 each), one group per stage, two
-// workgroups per CU: the fastest of the measured shapes and stage widths at
-// every M of the workloads.
-constexpr int kWM = 1, kWN = 4, kTM = 4, kTN = 4, kStage = 128;
+#ifndef W4A16_TILED_SHAPE
+#define W4A16_TILED_SHAPE 1, 4, 4, 4
+#endif
+// 64 x 256 blocks of 4 waves (64 x 64 each), two workgroups per CU: the
+// fastest of the measured shapes at every M of the workloads.
+template <int WM_, int WN_, int TM_, int TN_>
+struct Shape {
+  static constexpr int WM = WM_, WN = WN_, TM = TM_, TN = TN_;
+};
+using TileShape = Shape<W4A16_TILED_SHAPE>;
+constexpr int kWM = TileShape::WM, kWN = TileShape::WN, kTM = TileShape::TM, kTN = TileShape::TN;
 constexpr int kBM = kWM * kTM * 16, kBN = kWN * kTN * 16;
-constexpr long long kBlockSlots = 256 * 2;  // CUs x resident workgroups per CU
+// CUs x resident workgroups per CU (two waves per SIMD, four SIMDs)
+constexpr long long kBlockSlots = 256 * 8 / (kWM * kWN);
 constexpr int kMinSplitGroups = 8;          // no split shorter than this many groups
 constexpr int kMaxSplit = 16;
 
@@ -394,7 +408,7 @@ hipError_t launch_tiled_set(const GemmDesc *d, int count, void *workspace, size_
       rblocks += (int)(((long long)d[i].M * d[i].N / 4 + kReduceThreads - 1) / kReduceThreads);
   }
   ts.count = count;
-  hipLaunchKernelGGL((tiled_kernel<kWM, kWN, kTM, kTN, kStage>), dim3(blocks), dim3(kWM * kWN * 64),
+  hipLaunchKernelGGL((tiled_kernel<kWM, kWN, kTM, kTN>), dim3(blocks), dim3(kWM * kWN * 64),
                      0, stream, ts);
   hipError_t err = hipGetLastError();
   if (err == hipSuccess && rblocks > 0) {
