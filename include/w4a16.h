@@ -36,19 +36,22 @@
  *
  * Packed layout (this library's own; the pages only fix the content):
  *  - Wq: N*K/2 bytes.  Tile (b, g) covers rows 16b..16b+15 and the 128
- *    columns of group g; it is 1024 bytes at byte offset (b*G + g)*1024,
- *    G = K/128.  Inside a tile, lane L = 16c + r (row r, column octet c =
+ *    columns of group g; it is 1024 bytes at byte offset (g*NB + b)*1024,
+ *    NB = N/16 (group-major: the tiles of one group are contiguous, which
+ *    spreads the concurrent streams of neighbouring row blocks over memory
+ *    channels).  Inside a tile, lane L = 16c + r (row r, column octet c =
  *    0..3) owns the 16 bytes at 16L: four little-endian 32-bit words, word t
  *    holding the codes of columns 128g + 32t + 8c + j, j = 0..7, with column
  *    j in the 4-bit slot i (bits 4i..4i+3) where j = 2*(i % 4) + i / 4.
  *    One 64-lane wave therefore reads a whole tile with one 128-bit load per
  *    lane, and word t of a lane is exactly that lane's B operand of a
  *    16x16x32 fp16 MFMA.
- *  - scales, zeros: fp16, in quads of 4 groups.  With Gq = ceil(G / 4), the
- *    value of row n = 16b + r and group g = 4u + i is element
- *    ((b*Gq + u)*16 + r)*4 + i; each buffer holds N*4*Gq elements, and the
- *    slots of groups G..4*Gq-1 are zero.  The metadata of one 16-row block
- *    and 4 consecutive groups is thus one contiguous 128-byte run.
+ *  - scales, zeros: fp16, in quads of 4 groups.  With G = K/128 and
+ *    Gq = ceil(G / 4), the value of row n = 16b + r and group g = 4u + i is
+ *    element ((u*NB + b)*16 + r)*4 + i; each buffer holds N*4*Gq elements,
+ *    and the slots of groups G..4*Gq-1 are zero.  The metadata of one 16-row
+ *    block and 4 consecutive groups is thus one contiguous 128-byte run, and
+ *    the runs of one quad follow each other row block after row block.
  *
  * Ownership and streams: the caller allocates and owns every buffer (device
  * memory unless noted) and passes a hipStream_t as `stream` (NULL = the null

@@ -7,9 +7,11 @@ discosf.com tutorial sec.2.3 and aiwing.uk ch.22 sec.22.3 table).  The oracle
 restates it element by element from the definition below; nothing is shared
 with the HIP packer.
 
-Definition.  W is [N][K]; G = K / 128 groups per row; N is a multiple of 16.
+Definition.  W is [N][K]; G = K / 128 groups per row; N is a multiple of 16;
+NB = N / 16 row blocks.
   * Tile (b, g) covers rows 16b .. 16b+15 and the 128 columns of group g.  It
-    is 1024 bytes at byte offset (b * G + g) * 1024 of the code buffer.
+    is 1024 bytes at byte offset (g * NB + b) * 1024 of the code buffer: the
+    tiles of one group are contiguous, row block after row block.
   * Inside a tile, 64 "lanes" own 16 bytes each: lane L = 16 * c + r (row
     r = 0..15 inside the tile, column octet c = 0..3) at byte 16 * L.
   * The lane's 16 bytes are four little-endian 32-bit words; word t (t = 0..3)
@@ -19,10 +21,11 @@ Definition.  W is [N][K]; G = K / 128 groups per row; N is a multiple of 16.
     half-word, each in increasing order.
   * Scales and zero points (fp16 each) are stored in quads of 4 groups:
     with Gq = ceil(G / 4), the value of row n = 16b + r, group g = 4u + i is
-    element ((b * Gq + u) * 16 + r) * 4 + i of its buffer (N * 4 * Gq
+    element ((u * NB + b) * 16 + r) * 4 + i of its buffer (N * 4 * Gq
     elements; the slots of groups G .. 4*Gq - 1 hold zero).  So the metadata
     of one 16-row block and 4 consecutive groups is one contiguous 128-byte
-    run: a single 8-byte load per row fetches 4 groups.
+    run (a single 8-byte load per row fetches 4 groups), and the runs of one
+    quad follow each other row block after row block.
 TEST INFRASTRUCTURE: see the package docstring for who may import this.
 """
 from __future__ import annotations
@@ -46,12 +49,13 @@ def nibble_address(n, k, N: int, K: int):
     G = _check(N, K)
     n = np.asarray(n, dtype=np.int64)
     k = np.asarray(k, dtype=np.int64)
+    NB = N // TILE_ROWS
     b, r = n // TILE_ROWS, n % TILE_ROWS          # tile row block, row inside the tile
     g, kk = k // _GROUP, k % _GROUP               # group, column inside the group
     t, c, j = kk // 32, (kk % 32) // 8, kk % 8    # word, column octet (lane), column in octet
     slot = (j // 2) + 4 * (j % 2)                 # inverse of j = 2*(slot % 4) + slot // 4
     lane = 16 * c + r
-    byte = (b * G + g) * TILE_BYTES + 16 * lane + 4 * t + slot // 2
+    byte = (g * NB + b) * TILE_BYTES + 16 * lane + 4 * t + slot // 2
     shift = 4 * (slot % 2)
     return byte, shift
 
@@ -94,9 +98,10 @@ def meta_index(n, g, N: int, K: int):
     Gq = meta_groups(K) // META_QUAD
     n = np.asarray(n, dtype=np.int64)
     g = np.asarray(g, dtype=np.int64)
+    NB = N // TILE_ROWS
     b, r = n // TILE_ROWS, n % TILE_ROWS
     u, i = g // META_QUAD, g % META_QUAD
-    return ((b * Gq + u) * TILE_ROWS + r) * META_QUAD + i
+    return ((u * NB + b) * TILE_ROWS + r) * META_QUAD + i
 
 
 def pack_meta(a: np.ndarray) -> np.ndarray:

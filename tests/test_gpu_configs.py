@@ -53,23 +53,25 @@ def test_config_matrix(ci, mi):
     del Wd
     wq, sc, zr = to_host(pw.wq), to_host(pw.scales), to_host(pw.zeros)
 
-    G = K // 128
+    G, NB = K // 128, N // 16
     blocks = sample_blocks(N, rng)
     rows = np.concatenate([np.arange(16 * b, 16 * b + 16) for b in blocks])
     Wr = np.concatenate([weight_rows(cfg.weight_key, mi, N, K, 16 * b, 16 * b + 16)
                          for b in blocks])
     ref = oracle.quantize(Wr, s)
+    # A 16-row block packed on its own is its G tiles back to back; in the whole
+    # buffer (group-major) tile g of row block b sits at (g * NB + b) * 1024.
     for j, b in enumerate(blocks):
         qb = ref.q[16 * j:16 * j + 16]
-        assert np.array_equal(wq[b * G * 1024:(b + 1) * G * 1024], oracle.pack_codes(qb)), \
-            f"packed codes differ in row block {b}"
+        got = np.concatenate([wq[(g * NB + b) * 1024:(g * NB + b + 1) * 1024] for g in range(G)])
+        assert np.array_equal(got, oracle.pack_codes(qb)), f"packed codes differ in row block {b}"
     assert np.array_equal(h16_bits(oracle.unpack_meta(sc, N, K)[rows]), h16_bits(ref.scales))
     assert np.array_equal(h16_bits(oracle.unpack_meta(zr, N, K)[rows]), h16_bits(ref.zeros))
-    Gm = oracle.meta_groups(K)
-    for b in blocks:   # whole metadata blocks of the sampled row blocks, padding included
-        lo, hi = b * 16 * Gm, (b + 1) * 16 * Gm
-        refb = oracle.pack_meta(ref.scales[16 * blocks.index(b):16 * blocks.index(b) + 16])
-        assert np.array_equal(h16_bits(sc[lo:hi]), h16_bits(refb))
+    Gq = oracle.meta_groups(K) // 4
+    for j, b in enumerate(blocks):   # whole metadata runs of the sampled row blocks, padding included
+        got = np.concatenate([sc[(u * NB + b) * 64:(u * NB + b + 1) * 64] for u in range(Gq)])
+        refb = oracle.pack_meta(ref.scales[16 * j:16 * j + 16])
+        assert np.array_equal(h16_bits(got), h16_bits(refb))
 
     for M in cfg.Ms:
         note(f"config {cfg.name} matrix {mat.name} M={M}: gemm "

@@ -53,16 +53,21 @@ def test_meta_layout():
     buf = oracle.pack_meta(a)
     assert buf.size == N * 8 and oracle.meta_groups(K) == 8
     assert np.array_equal(oracle.unpack_meta(buf, N, K), a)
-    # hand-derived: row 17 = block 1, r 1; group 4 = quad 1, slot 0; Gq = 2
-    # index ((1 * 2 + 1) * 16 + 1) * 4 + 0 = 196
-    assert int(oracle.meta_index(17, 4, N, K)) == 196 and buf[196] == a[17, 4]
-    # row 5, group 2: ((0 * 2 + 0) * 16 + 5) * 4 + 2 = 22
+    # hand-derived: NB = 3 row blocks; row 17 = block 1, r 1; group 4 = quad 1, slot 0
+    # index ((1 * 3 + 1) * 16 + 1) * 4 + 0 = 260
+    assert int(oracle.meta_index(17, 4, N, K)) == 260 and buf[260] == a[17, 4]
+    # row 5, group 2: ((0 * 3 + 0) * 16 + 5) * 4 + 2 = 22
     assert int(oracle.meta_index(5, 2, N, K)) == 22
+    # row 47 (block 2, r 15), group 3 (quad 0, slot 3): ((0 * 3 + 2) * 16 + 15) * 4 + 3 = 191
+    assert int(oracle.meta_index(47, 3, N, K)) == 191
     # padding slots (groups 5..7) are zero, and every real value appears once
     assert np.count_nonzero(buf) == N * G
     # one 16-row block x 4 groups is one contiguous run of 64 elements (128 bytes)
     idx = oracle.meta_index(np.repeat(np.arange(16, 32), 4), np.tile(np.arange(4, 8), 16), N, K)
     assert sorted(idx.tolist()) == list(range(idx.min(), idx.min() + 64))
+    # and the runs of one quad (all N rows x groups 4..7) follow each other
+    idx = oracle.meta_index(np.repeat(np.arange(N), 4), np.tile(np.arange(4, 8), N), N, K)
+    assert sorted(idx.tolist()) == list(range(N * 4, 2 * N * 4))
 
 
 def test_layout_rejects_bad_shapes():

@@ -55,13 +55,14 @@ __global__ __launch_bounds__(256) void pack_kernel(const _Float16 *__restrict__ 
                                                    _Float16 *__restrict__ zeros,
                                                    unsigned *__restrict__ status) {
 #pragma clang fp contract(off)
-  const int G = K / kGroup;
-  const long long tiles = (long long)(N / kTileRows) * G;
+  const int G = K / kGroup, NB = N / kTileRows;
+  const long long tiles = (long long)NB * G;
+  // the wave's tile, numbered as stored: group-major
   const long long tile = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (tile >= tiles) return;  // uniform per wave
   const int lane = threadIdx.x & 63;
   const int c = lane >> 4, r = lane & 15;
-  const int b = (int)(tile / G), g = (int)(tile % G);
+  const int g = (int)(tile / NB), b = (int)(tile % NB);
   const int n = b * kTileRows + r;
 
   double wp[32];
@@ -125,14 +126,13 @@ __global__ __launch_bounds__(256) void pack_kernel(const _Float16 *__restrict__ 
     }
   }
   Wq[tile * 64 + lane] = out;
-  const int Gq = meta_groups(G) / kMetaQuad;
   if (c == 0) {
-    scales[meta_index(n, g, Gq)] = sc16;
-    zeros[meta_index(n, g, Gq)] = z16;
+    scales[meta_index(n, g, NB)] = sc16;
+    zeros[meta_index(n, g, NB)] = z16;
   } else if (g == G - 1 && G - 1 + c < meta_groups(G)) {
     // the last tile of a row also clears the row's padding slots (at most 3)
-    scales[meta_index(n, G - 1 + c, Gq)] = (_Float16)0;
-    zeros[meta_index(n, G - 1 + c, Gq)] = (_Float16)0;
+    scales[meta_index(n, G - 1 + c, NB)] = (_Float16)0;
+    zeros[meta_index(n, G - 1 + c, NB)] = (_Float16)0;
   }
   if (bad) atomicOr(status, bad);
 }

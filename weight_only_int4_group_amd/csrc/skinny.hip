@@ -186,8 +186,11 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_kernel(ProblemSet ps) {
       (void *)P.scales, (short)0, (int)min((size_t)0x7fffffff, meta_bytes), kRsrcWord3);
   const __amdgpu_buffer_rsrc_t zrs = __builtin_amdgcn_make_buffer_rsrc(
       (void *)P.zeros, (short)0, (int)min((size_t)0x7fffffff, meta_bytes), kRsrcWord3);
-  const int tile_off = bb * G * kTileBytes + lane * 16;              // + g * 1024
-  const int meta_off = ((bb * Gq) * kTileRows + r) * kMetaQuad * 2;   // + quad * 128
+  // group-major tiles and quad-major metadata: the row block's part of the
+  // offset is per lane, the group's part is uniform
+  const int tile_off = bb * kTileBytes + lane * 16;               // + g * tile_stride
+  const int meta_off = (bb * kTileRows + r) * kMetaQuad * 2;      // + quad * meta_stride
+  const int tile_stride = NB * kTileBytes, meta_stride = NB * kTileRows * kMetaQuad * 2;
 
   // A chunk is one or two metadata quads: 4 groups' scales (and zero points)
   // of this lane's row are one 8-byte load.
@@ -200,13 +203,15 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_kernel(ProblemSet ps) {
   auto load_chunk = [&](int slot, int g0) {
 #pragma unroll
     for (int i = 0; i < kGW; ++i) {
-      const int g = g0 + i;  // past the slice: valid memory or zeros, never used
+      // groups past the row (a partial last chunk) re-read its last tile: every
+      // load stays inside the buffer; their products are never used
+      const int g = min(g0 + i, G - 1);
       code[slot][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                     wrs, tile_off, g * kTileBytes, 0));
+                                                     wrs, tile_off, g * tile_stride, 0));
     }
 #pragma unroll
     for (int q = 0; q < kQ; ++q) {
-      const int qoff = (g0 / kMetaQuad + q) * kTileRows * kMetaQuad * 2;
+      const int qoff = min(g0 / kMetaQuad + q, Gq - 1) * meta_stride;
       const auto sv = __builtin_amdgcn_raw_buffer_load_b64(srs, meta_off, qoff, 0);
       const auto zv = __builtin_amdgcn_raw_buffer_load_b64(zrs, meta_off, qoff, 0);
       sq[slot][2 * q] = (uint32_t)sv[0];
@@ -338,8 +343,9 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_window_kernel(ProblemSet p
       (void *)P.scales, (short)0, (int)min((size_t)0x7fffffff, meta_bytes), kRsrcWord3);
   const __amdgpu_buffer_rsrc_t zrs = __builtin_amdgcn_make_buffer_rsrc(
       (void *)P.zeros, (short)0, (int)min((size_t)0x7fffffff, meta_bytes), kRsrcWord3);
-  const int tile_off = bb * G * kTileBytes + lane * 16;
-  const int meta_off = ((bb * Gq) * kTileRows + r) * kMetaQuad * 2;
+  const int tile_off = bb * kTileBytes + lane * 16;               // + g * tile_stride
+  const int meta_off = (bb * kTileRows + r) * kMetaQuad * 2;      // + quad * meta_stride
+  const int tile_stride = NB * kTileBytes, meta_stride = NB * kTileRows * kMetaQuad * 2;
 
   static_assert(kGW % kMetaQuad == 0, "a chunk is whole metadata quads");
   constexpr int kQ = kGW / kMetaQuad;
@@ -347,12 +353,12 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_window_kernel(ProblemSet p
   uint32_t sq[kDepth][2 * kQ], zq[kDepth][2 * kQ];
   auto load_chunk = [&](int slot, int g0) {
 #pragma unroll
-    for (int i = 0; i < kGW; ++i)
+    for (int i = 0; i < kGW; ++i)  // past the row: re-read its last tile (never used)
       code[slot][i] = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrs, tile_off, (g0 + i) * kTileBytes, 0));
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrs, tile_off, min(g0 + i, G - 1) * tile_stride, 0));
 #pragma unroll
     for (int q = 0; q < kQ; ++q) {
-      const int qoff = (g0 / kMetaQuad + q) * kTileRows * kMetaQuad * 2;
+      const int qoff = min(g0 / kMetaQuad + q, Gq - 1) * meta_stride;
       const auto sv = __builtin_amdgcn_raw_buffer_load_b64(srs, meta_off, qoff, 0);
       const auto zv = __builtin_amdgcn_raw_buffer_load_b64(zrs, meta_off, qoff, 0);
       sq[slot][2 * q] = (uint32_t)sv[0];
@@ -401,8 +407,9 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_window_kernel(ProblemSet p
   };
 
   // Every step issues the same loads, also past the last window or chunk
-  // (bounds-checked buffer loads; the data is never used), so that the
-  // compiler's wait counts are the same on every path through the loop.
+  // (clamped to the row's last group, or out-of-range buffer offsets that read
+  // zeros; the data is never used), so that the compiler's wait counts are the
+  // same on every path through the loop.
   load_window(0);
 #pragma unroll
   for (int d = 0; d < kDepth; ++d) load_chunk(d, chunk_g0(d));

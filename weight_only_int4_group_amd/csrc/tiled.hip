@@ -194,9 +194,9 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
 
   // ---- weights: this wave's TN row blocks.  The next group's code tiles go
   // straight from HBM to this wave's own LDS slots (one 16-byte DMA load per
-  // lane per tile, bounds-checked: row blocks past N read zeros and are never
-  // stored), so only the current group's codes occupy registers; scales and
-  // zero points come as raw 16-bit words into one of two register sets.
+  // lane per tile), so only the current group's codes occupy registers;
+  // scales and zero points come as raw 16-bit words into one of two register
+  // sets.
   const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
       (void *)Wq, (short)0, (int)min((size_t)0x7fffffff, (size_t)N * K / 2), kRsrcWord3);
   const size_t meta_bytes = (size_t)N * Gq * kMetaQuad * 2;
@@ -211,16 +211,21 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
     uint32_t sc[TN], zp[TN];  // raw fp16 bits of each row block's scale and zero point
   };
   BRegs b0, b1;
+  // group-major tiles and quad-major metadata: the row block's part of each
+  // offset is per lane, the group's part uniform
+  const int tile_stride = NB * kTileBytes, meta_stride = NB * kTileRows * kMetaQuad * 2;
   auto load_b = [&](int g, int buf, BRegs &b) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      const int rb = min(rb0 + j, NB);
+      // row blocks past N re-read the last one (in bounds) and are never stored
+      const int rb = min(rb0 + j, NB - 1);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           wrs, (__attribute__((address_space(3))) void *)&Bs[buf][(wave * TN + j) * kTileBytes], 16,
-          (rb * G * 64 + lane) * 16, g * kTileBytes, 0, 0);
-      const int mo = ((rb * Gq + g / kMetaQuad) * kTileRows + r) * kMetaQuad * 2;
-      b.sc[j] = __builtin_amdgcn_raw_buffer_load_b16(srs, mo, (g % kMetaQuad) * 2, 0);
-      b.zp[j] = __builtin_amdgcn_raw_buffer_load_b16(zrs, mo, (g % kMetaQuad) * 2, 0);
+          (rb * 64 + lane) * 16, g * tile_stride, 0, 0);
+      const int mo = (rb * kTileRows + r) * kMetaQuad * 2;
+      const int qo = (g / kMetaQuad) * meta_stride + (g % kMetaQuad) * 2;
+      b.sc[j] = __builtin_amdgcn_raw_buffer_load_b16(srs, mo, qo, 0);
+      b.zp[j] = __builtin_amdgcn_raw_buffer_load_b16(zrs, mo, qo, 0);
     }
   };
 

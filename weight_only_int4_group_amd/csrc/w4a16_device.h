@@ -23,11 +23,15 @@ constexpr int kTileBytes = 1024;
 constexpr int kWave = 64;
 constexpr int kMetaQuad = 4;   // groups per metadata quad
 
-// Metadata (scale / zero point) layout: quads of 4 groups.  Element index of
-// row n, group g, for Gq = ceil(G / 4) quads per row.
+// Code tiles are group-major: tile (row block b, group g) is the 1 KB at
+// (g * NB + b) * 1024, NB = N / 16, so the tiles that concurrently running
+// waves stream (neighbouring row blocks, same group) are neighbours in memory.
+//
+// Metadata (scale / zero point) layout: quads of 4 groups, quad-major in the
+// same way.  Element index of row n, group g, for NB row blocks.
 __host__ __device__ constexpr int meta_groups(int G) { return (G + kMetaQuad - 1) / kMetaQuad * kMetaQuad; }
-__host__ __device__ inline size_t meta_index(int n, int g, int Gq) {
-  return (((size_t)(n / kTileRows) * Gq + g / kMetaQuad) * kTileRows + n % kTileRows) * kMetaQuad +
+__host__ __device__ inline size_t meta_index(int n, int g, int NB) {
+  return (((size_t)(g / kMetaQuad) * NB + n / kTileRows) * kTileRows + n % kTileRows) * kMetaQuad +
          g % kMetaQuad;
 }
 
