@@ -158,10 +158,10 @@ __device__ __forceinline__ void store_rows(const Problem &P, float4v acc, int b,
   }
 }
 
-template <bool X_LDS, int kGW, int kWaves, int kDepth>
+template <int kGW, int kWaves, int kDepth>
 __global__ __launch_bounds__(kWaves * 64) void skinny_kernel(ProblemSet ps) {
+  // X * s, then (after the last use of X) the split-K reduction
   extern __shared__ __attribute__((aligned(16))) _Float16 xs[];
-  __shared__ float red[kWaves][16][17];
 
   const Problem P = find_problem(ps);
   const int M = P.M, N = P.N, K = P.K, S = P.split;
@@ -177,6 +177,8 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_kernel(ProblemSet ps) {
   const int chunks = (G + kGW - 1) / kGW;
   const int gb = min(G, (chunks * ks / S) * kGW);
   const int ge = has_rows ? min(G, (chunks * (ks + 1) / S) * kGW) : gb;
+  const int nch = (ge - gb + kGW - 1) / kGW;  // chunks of this wave
+  const int glast = max(gb, ge - 1);          // loads past the slice re-read this group
 
   const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
       (void *)P.Wq, (short)0, (int)min((size_t)0x7fffffff, (size_t)N * K / 2), kRsrcWord3);
@@ -195,122 +197,98 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_kernel(ProblemSet ps) {
   // A chunk is one or two metadata quads: 4 groups' scales (and zero points)
   // of this lane's row are one 8-byte load.
   static_assert(kGW % kMetaQuad == 0, "a chunk is whole metadata quads");
+  static_assert(kDepth == 1, "one chunk of codes in flight (measured best)");
   constexpr int kQ = kGW / kMetaQuad;
-  // kDepth chunks in flight: slot 0 is the next chunk to compute, slot d the
-  // one after d more chunks.
-  u32x4 code[kDepth][kGW];
-  uint32_t sq[kDepth][2 * kQ], zq[kDepth][2 * kQ];  // scales, zero points (fp16 pairs)
-  auto load_chunk = [&](int slot, int g0) {
+  // Codes are loaded one chunk ahead, metadata two chunks ahead into one of
+  // two register sets (so its loads never hold up a chunk's codes), steps
+  // alternating between the sets so that nothing is copied.  Every step issues
+  // the same loads: past the wave's last group they re-read it (in bounds and
+  // in cache, never used), so the compiler's wait counts are the same on
+  // every path.
+  struct Meta {
+    uint32_t sq[2 * kQ], zq[2 * kQ];  // scales, zero points (fp16 pairs)
+  };
+  u32x4 code[kGW];
+  Meta m0, m1;
+  auto load_codes = [&](int g0) {
 #pragma unroll
-    for (int i = 0; i < kGW; ++i) {
-      // groups past the row (a partial last chunk) re-read its last tile: every
-      // load stays inside the buffer; their products are never used
-      const int g = min(g0 + i, G - 1);
-      code[slot][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                     wrs, tile_off, g * tile_stride, 0));
-    }
+    for (int i = 0; i < kGW; ++i)
+      code[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             wrs, tile_off, min(g0 + i, glast) * tile_stride, 0));
+  };
+  auto load_meta = [&](Meta &mt, int g0) {
 #pragma unroll
     for (int q = 0; q < kQ; ++q) {
-      const int qoff = min(g0 / kMetaQuad + q, Gq - 1) * meta_stride;
+      const int qoff = (min(g0, glast) / kMetaQuad + q) * meta_stride;
       const auto sv = __builtin_amdgcn_raw_buffer_load_b64(srs, meta_off, qoff, 0);
       const auto zv = __builtin_amdgcn_raw_buffer_load_b64(zrs, meta_off, qoff, 0);
-      sq[slot][2 * q] = (uint32_t)sv[0];
-      sq[slot][2 * q + 1] = (uint32_t)sv[1];
-      zq[slot][2 * q] = (uint32_t)zv[0];
-      zq[slot][2 * q + 1] = (uint32_t)zv[1];
+      mt.sq[2 * q] = (uint32_t)sv[0];
+      mt.sq[2 * q + 1] = (uint32_t)sv[1];
+      mt.zq[2 * q] = (uint32_t)zv[0];
+      mt.zq[2 * q + 1] = (uint32_t)zv[1];
     }
   };
-#pragma unroll
-  for (int d = 0; d < kDepth; ++d)
-    if (gb + d * kGW < ge) load_chunk(d, gb + d * kGW);
+  // issue order: meta 0, codes 0, meta 1
+  load_meta(m0, gb);
+  load_codes(gb);
+  load_meta(m1, gb + kGW);
 
-  const _Float16 *xrow = nullptr;
-  if (X_LDS) {
-    // stage X * s for rows 0..M-1 and an all-zero row M
+  // stage X * s for rows 0..M-1; lanes of rows m >= M read row M - 1 (rows of
+  // the A operand only reach the same rows of D, and those are not stored)
+  {
     const int ldx = K + kLdsPad, k8 = K / 8;
-    for (int idx = threadIdx.x; idx < (M + 1) * k8; idx += kWaves * 64) {
+    for (int idx = threadIdx.x; idx < M * k8; idx += kWaves * 64) {
       const int m = idx / k8, kk = (idx - m * k8) * 8;
-      half8 v = zero_half8();
-      if (m < M) {
-        v = load_half8(P.X + (size_t)m * K + kk);
-        if (P.s) v = v * load_half8(P.s + kk);
-      }
+      half8 v = load_half8(P.X + (size_t)m * K + kk);
+      if (P.s) v = v * load_half8(P.s + kk);
       *reinterpret_cast<half8 *>(&xs[m * ldx + kk]) = v;
     }
     __syncthreads();
-    xrow = xs + (r < M ? r : M) * ldx + 8 * c;
   }
+  const _Float16 *xrow = xs + min(r, M - 1) * (K + kLdsPad) + 8 * c;
 
   const uint32_t m_lo = 0x000F000Fu, m_hi = 0x00F000F0u, magic = kMagic2;
   float4v acc = {0.f, 0.f, 0.f, 0.f};
-  for (int g0 = gb; g0 < ge; g0 += kGW) {
+  // chunk j: its codes and metadata (in `mt`) were issued earlier; take them,
+  // issue chunk j+1's codes and chunk j+2's metadata (into `mt`), compute
+  auto step = [&](int j, Meta &mt) {
+    const int g0 = gb + j * kGW;
     u32x4 cur[kGW];
     half2v cs[2 * kQ], cz[2 * kQ];
 #pragma unroll
-    for (int i = 0; i < kGW; ++i) cur[i] = code[0][i];
+    for (int i = 0; i < kGW; ++i) cur[i] = code[i];
 #pragma unroll
     for (int q = 0; q < 2 * kQ; ++q) {
-      cs[q] = as_half2(sq[0][q]);
-      cz[q] = as_half2(zq[0][q]);
+      cs[q] = as_half2(mt.sq[q]);
+      cz[q] = as_half2(mt.zq[q]);
     }
-    // shift the ring and start the chunk kDepth ahead, in flight during this one
-#pragma unroll
-    for (int d = 0; d + 1 < kDepth; ++d) {
-#pragma unroll
-      for (int i = 0; i < kGW; ++i) code[d][i] = code[d + 1][i];
-#pragma unroll
-      for (int q = 0; q < 2 * kQ; ++q) {
-        sq[d][q] = sq[d + 1][q];
-        zq[d][q] = zq[d + 1][q];
-      }
-    }
-    if (g0 + kDepth * kGW < ge) load_chunk(kDepth - 1, g0 + kDepth * kGW);
-
-    half8 a[kGW][4];
-    if (!X_LDS) {
-      // X * s straight from global memory, only in the lanes of live rows
-#pragma unroll
-      for (int i = 0; i < kGW; ++i)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) a[i][t] = zero_half8();
-      if (r < M) {
-        const _Float16 *xg = P.X + (size_t)r * K + 8 * c;
-#pragma unroll
-        for (int i = 0; i < kGW; ++i) {
-          const int g = min(g0 + i, G - 1);
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const size_t k = (size_t)g * kGroup + 32 * t;
-            half8 v = load_half8(xg + k);
-            if (P.s) v = v * load_half8(P.s + 8 * c + k);
-            a[i][t] = v;
-          }
-        }
-      }
-    }
+    load_codes(g0 + kGW);
+    load_meta(mt, g0 + 2 * kGW);
 #pragma unroll
     for (int i = 0; i < kGW; ++i) {
       const int g = g0 + i;
       if (g < ge) {
-        if (X_LDS) {
+        half8 a[4];
 #pragma unroll
-          for (int t = 0; t < 4; ++t)
-            a[i][t] = *reinterpret_cast<const half8 *>(xrow + g * kGroup + 32 * t);
-        }
+        for (int t = 0; t < 4; ++t) a[t] = *reinterpret_cast<const half8 *>(xrow + g * kGroup + 32 * t);
         const _Float16 zp = cz[i >> 1][i & 1], sc = cs[i >> 1][i & 1];
         const _Float16 blo = (_Float16)1024.0f + zp, bhi = (_Float16)64.0f + zp;
         const half2v bias_lo = {blo, blo}, bias_hi = {bhi, bhi};
         float4v tmp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < 4; ++t)
-          tmp = mfma16(a[i][t], decode_word9(cur[i][t], m_lo, m_hi, magic, bias_lo, bias_hi),
-                       tmp);
+          tmp = mfma16(a[t], decode_word9(cur[i][t], m_lo, m_hi, magic, bias_lo, bias_hi), tmp);
         acc += tmp * (float)sc;
       }
     }
+  };
+  for (int j = 0; j < nch; j += 2) {
+    step(j, m0);
+    if (j + 1 < nch) step(j + 1, m1);
   }
 
-  store_rows<kWaves>(P, acc, b, has_rows, wave, ks, c, r, red);
+  if (S > 1) __syncthreads();  // every wave is done with X * s: its LDS takes the partial sums
+  store_rows<kWaves>(P, acc, b, has_rows, wave, ks, c, r, reinterpret_cast<float (*)[16][17]>(xs));
 }
 
 // Windowed variant: X * s staged one window of S chunks at a time (see the
@@ -471,9 +449,6 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_window_kernel(ProblemSet p
   store_rows<kWaves>(P, acc, b, has_rows, wave, ks, c, r, red);
 }
 
-// LDS bytes to stage X * s (plus the zero row) of one problem.
-size_t stage_bytes(int M, int K) { return (size_t)(M + 1) * (K + kLdsPad) * sizeof(_Float16); }
-
 constexpr size_t kMaxStageBytes = 96 * 1024;
 #ifndef W4A16_SKINNY_CHUNK
 #define W4A16_SKINNY_CHUNK 4
@@ -490,10 +465,10 @@ constexpr int kDepth = W4A16_SKINNY_DEPTH;  // chunks in flight per wave
 #ifndef W4A16_SKINNY_WINDOW
 #define W4A16_SKINNY_WINDOW 3
 #endif
-// 0: never window (global X loads when X * s does not fit), 1: window the
-// problems whose X * s does not fit, 2: always window, 3: window the whole call
-// when one problem does not fit
+// 1: window the problems whose X * s does not fit, 2: always window, 3:
+// window the whole call when one problem does not fit
 constexpr int kWindowMode = W4A16_SKINNY_WINDOW;
+static_assert(kWindowMode >= 1 && kWindowMode <= 3, "X * s must fit in LDS or go in windows");
 #ifndef W4A16_SKINNY_WINDOW_KB
 #define W4A16_SKINNY_WINDOW_KB 72
 #endif
@@ -502,6 +477,14 @@ constexpr int kWindowMode = W4A16_SKINNY_WINDOW;
 #endif
 constexpr size_t kMaxWindowBytes = W4A16_SKINNY_WINDOW_KB * 1024;  // 72 KB: two workgroups per CU
 constexpr int kWindowSlots = W4A16_SKINNY_WINDOW_SLOTS;  // staged 8-column pieces per thread
+// LDS bytes of the whole-row kernel: X * s of one problem, at least the
+// reduction's partial sums (which reuse it).
+size_t stage_bytes(int M, int K) {
+  const size_t x = (size_t)M * (K + kLdsPad) * sizeof(_Float16);
+  const size_t red = (size_t)kWaves * 16 * 17 * sizeof(float);
+  return x > red ? x : red;
+}
+
 constexpr int kTargetWaves = 2048;     // enough waves in flight to cover HBM latency
 constexpr int kMaxGroupsPerWave = 32;  // longer rows are split across waves
 
@@ -584,12 +567,9 @@ hipError_t launch_group(const GemmDesc *const *d, int count, bool window, hipStr
   if (window)
     hipLaunchKernelGGL((skinny_window_kernel<kChunk, kWaves, kDepth, kWindowSlots>), dim3(blocks),
                        dim3(kWaves * 64), lds, stream, ps);
-  else if (lds <= kMaxStageBytes)
-    hipLaunchKernelGGL((skinny_kernel<true, kChunk, kWaves, kDepth>), dim3(blocks),
-                       dim3(kWaves * 64), lds, stream, ps);
   else
-    hipLaunchKernelGGL((skinny_kernel<false, kChunk, kWaves, kDepth>), dim3(blocks),
-                       dim3(kWaves * 64), 0, stream, ps);
+    hipLaunchKernelGGL((skinny_kernel<kChunk, kWaves, kDepth>), dim3(blocks), dim3(kWaves * 64),
+                       lds, stream, ps);
   return hipGetLastError();
 }
 
