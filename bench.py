@@ -25,7 +25,10 @@ Printed JSON line:
                 call per step (streaming kernel for M <= 16, else the tiled GEMM);
   prefill       the 70B-shaped layer at M = 4096 (compute-bound): TFLOP/s
                 against the dense fp16 MFMA peak;
-  cpu_baseline  the fp64 CPU oracle on a bounded sample of the same workload.
+  cpu_baseline  the fp64 CPU oracle on a bounded sample of the same workload;
+  ceilings      measured context, not targets: a plain 1 GiB device-to-device
+                copy (read + write GB/s) and torch's dense fp16 GEMM (the
+                vendor library, dense fp16 weights) at the 70B prefill shapes.
 """
 from __future__ import annotations
 
@@ -216,6 +219,46 @@ def variant(mats, groups, launch_ms, steps, wall, unit_key):
     return out
 
 
+def ceilings(torch, reps=10):
+    """Measured ceilings on this GPU, for context: a plain device-to-device copy, and
+    the vendor dense fp16 GEMM (torch.matmul on contiguous fp16 operands) at the 70B
+    prefill shapes, M = 4096."""
+    stream = torch.cuda.current_stream()
+
+    def time_it(fn, n):
+        for _ in range(2):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e-3  # seconds per call
+
+    a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    t = time_it(lambda: b.copy_(a), reps)
+    out = {"device_copy_GBps": round(2 * a.numel() / t / 1e9, 1),
+           "device_copy": "1 GiB device-to-device copy_, read + write bytes / time"}
+    del a, b
+    gemm = {}
+    M = 4096
+    for name, N, K in (("q/o 8192x8192", 8192, 8192), ("gate/up 28672x8192", 28672, 8192),
+                       ("down 8192x28672", 8192, 28672)):
+        X = torch.randn(M, K, dtype=torch.float16, device="cuda")
+        Wt = torch.randn(K, N, dtype=torch.float16, device="cuda")  # W^T, contiguous
+        t = time_it(lambda: torch.matmul(X, Wt), reps)
+        gemm[name] = round(2 * M * N * K / t / 1e12, 1)
+        del X, Wt
+    out["fp16_gemm_TFLOPs"] = gemm
+    out["fp16_gemm"] = ("torch.matmul, fp16 X[4096][K] @ W^T[K][N] with dense fp16 weights "
+                        "(4x the bytes of the packed INT4 weights); context, not a target")
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(cfg, M, workloads, rows=1024, budget_s=10.0):
     """The fp64 oracle (dequantize then matmul), timed on this host on a bounded
     sample of the workload: the first `rows` rows of every matrix, quantized by
@@ -260,6 +303,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--no-batched", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-run", action="store_true",
                     help="only the short fixed sequence used for counter collection")
@@ -365,6 +409,9 @@ def main():
         del ppool, pmats
         torch.cuda.empty_cache()
 
+    if not args.no_ceilings:
+        log("measuring the copy and dense fp16 GEMM ceilings")
+        out["ceilings"] = ceilings(torch)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
         out["cpu_baseline"] = cpu_baseline(cfg, M, workloads)
