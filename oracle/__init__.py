@@ -35,12 +35,16 @@ in the design notes of the repository):
      adding z;  R8 W' = W / s is one correctly rounded fp64 division;
   R9 an all-zero group has scale 0, zero point 0 and codes 0; non-finite W or
      s, or s <= 0, is an error; a scale that overflows fp16 is an error.
+The symmetric variant (``quantize_symmetric``, the signed -7..7 grid of [mhpq]
+sec.2.1) takes R2, R5, R7's ties, R8 and R9's errors as they are, with
+scale = max|W'| / 7 rounded up, signed codes rint(W' / scale) stored + 8 and a
+constant zero point 8 (an all-zero group: scale 0, codes 8).
 Pins: every function here is checked by tests against facts the pages or the
 mathematics fix (bound, grid reconstruction, byte counts, brute force in exact
 rationals, integer special case); see tests/test_oracle_*.py.
 """
-from .quantizer import (GROUP, QMAX, NonFiniteInput, OracleError, QuantResult, ScaleOverflow,
-                       quantize, round_up_fp16)
+from .quantizer import (GROUP, QMAX, SYM_QMAX, SYM_ZERO, NonFiniteInput, OracleError, QuantResult,
+                        ScaleOverflow, quantize, quantize_symmetric, round_up_fp16)
 from .layout import (META_QUAD, TILE_BYTES, TILE_ROWS, meta_groups, meta_index, nibble_address,
                      pack_codes, pack_meta, unpack_codes, unpack_meta)
 from .matmul import dequantize, gemm
@@ -48,7 +52,7 @@ from . import accounting, exact
 
 __all__ = [
     "GROUP", "QMAX", "NonFiniteInput", "OracleError", "QuantResult", "ScaleOverflow",
-    "quantize", "round_up_fp16", "META_QUAD", "TILE_BYTES", "TILE_ROWS", "meta_groups",
+    "quantize", "quantize_symmetric", "SYM_QMAX", "SYM_ZERO", "round_up_fp16", "META_QUAD", "TILE_BYTES", "TILE_ROWS", "meta_groups",
     "meta_index", "nibble_address",
     "pack_codes", "pack_meta", "unpack_codes", "unpack_meta", "dequantize", "gemm",
     "accounting", "exact",

@@ -18,6 +18,8 @@ import numpy as np
 
 GROUP = 128   # elements per quantization group along K (discosf sec.2.1)
 QMAX = 15     # unsigned 4-bit code range 0..15 (reading R1)
+SYM_QMAX = 7  # symmetric signed grid -7..7 (mhpq.cn notes sec.2.1: INT4 max +-7)
+SYM_ZERO = 8  # its fixed zero point: stored code = signed code + 8, in 1..15
 
 
 class OracleError(ValueError):
@@ -98,4 +100,52 @@ def quantize(W: np.ndarray, s: np.ndarray | None = None) -> QuantResult:
         q=q.reshape(N, K).astype(np.uint8),
         scales=np.where(live, scale16, np.float16(0)).astype(np.float16),
         zeros=z.astype(np.int64).astype(np.float16),   # integer -> fp16: never a negative zero
+    )
+
+
+def quantize_symmetric(W: np.ndarray, s: np.ndarray | None = None) -> QuantResult:
+    """Symmetric variant of ``quantize``: signed codes -7..7 around a fixed zero point.
+
+    Steps, in the same order as ``quantize``:
+      * W' = W / s (aiwing sec.22.3's AWQ pre-scale), fp64;
+      * per group of 128 (discosf sec.2.1), the scale maps the largest magnitude
+        onto 7, the top of the signed 4-bit grid of the mhpq.cn notes sec.2.1:
+        scale = max|W'| / 7 rounded UP to fp16 (as R5: so |W' / scale| <= 7 and
+        no code is ever clamped);
+      * signed code c = rint(W' / scale) (ties to even), clamped to -7..7;
+      * stored as the unsigned code c + 8 (1..15) with zero point 8, so that the
+        library's dequantization (q - z) * scale * s applies unchanged.
+    An all-zero group stores scale 0, codes 8 and zero point 8 (so q - z = 0).
+    """
+    W = np.asarray(W)
+    if W.dtype != np.float16 or W.ndim != 2:
+        raise TypeError("W must be a 2-D float16 array")
+    N, K = W.shape
+    if K % GROUP:
+        raise ValueError("K must be a multiple of 128")
+    Wd = W.astype(np.float64)
+    if s is None:
+        sd = np.ones(K, dtype=np.float64)
+    else:
+        s = np.asarray(s)
+        if s.dtype != np.float16 or s.shape != (K,):
+            raise TypeError("s must be a float16 array of length K")
+        sd = s.astype(np.float64)
+    if not np.all(np.isfinite(Wd)) or not np.all(np.isfinite(sd)) or not np.all(sd > 0):
+        raise NonFiniteInput("non-finite W or s, or s <= 0")
+    Wp = Wd / sd[None, :]
+    G = K // GROUP
+    Wg = Wp.reshape(N, G, GROUP)
+    amax = np.abs(Wg).max(axis=2)
+    scale16 = round_up_fp16(amax / SYM_QMAX)
+    if not np.all(np.isfinite(scale16)):
+        raise ScaleOverflow("group scale exceeds the fp16 range")
+    live = amax > 0
+    safe = np.where(live, scale16.astype(np.float64), 1.0)
+    c = np.clip(np.rint(Wg / safe[:, :, None]), -SYM_QMAX, SYM_QMAX)
+    c = np.where(live[:, :, None], c, 0.0)
+    return QuantResult(
+        q=(c + SYM_ZERO).reshape(N, K).astype(np.uint8),
+        scales=np.where(live, scale16, np.float16(0)).astype(np.float16),
+        zeros=np.full((N, G), SYM_ZERO, dtype=np.float16),
     )
