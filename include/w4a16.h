@@ -80,7 +80,7 @@ enum {
   W4A16_OK = 0,
   W4A16_EINVAL = -1,       /* NULL pointer, M/N/K out of range, K % 128, N % 16 */
   W4A16_EALIGN = -2,       /* a pointer is not 16-byte aligned                  */
-  W4A16_EUNSUPPORTED = -3, /* unknown kernel path requested                     */
+  W4A16_EUNSUPPORTED = -3, /* unknown kernel path or quantization mode requested */
   W4A16_ENONFINITE = -4,   /* NaN/Inf in W or s, or some s <= 0 (packer)        */
   W4A16_ERANGE = -5,       /* a group scale rounds up past the fp16 range       */
   W4A16_EHIP = -6          /* a HIP runtime call or kernel launch failed        */
@@ -110,6 +110,23 @@ int w4a16_packed_sizes(int64_t N, int64_t K, size_t *wq_bytes, size_t *scales_by
  * error the outputs hold unspecified values. */
 int w4a16_quantize_pack(const void *W, const void *s, int64_t N, int64_t K, void *Wq,
                         void *scales, void *zeros, void *stream);
+
+/* Quantization grids for w4a16_quantize_pack_mode(). */
+enum {
+  W4A16_QUANT_ASYM = 0, /* the readings above (w4a16_quantize_pack)              */
+  W4A16_QUANT_SYM = 1   /* signed -7..7 around a constant zero point 8           */
+};
+
+/* Quantize and pack on a chosen grid; same arguments, layout, blocking and
+ * errors as w4a16_quantize_pack, plus `mode` (EUNSUPPORTED if unknown).
+ * W4A16_QUANT_SYM is the signed 4-bit grid of the practitioner notes at
+ * mhpq.cn, section 2.1 (INT4 spans -7..7): per group, scale = max|W'| / 7
+ * rounded UP to fp16 (so no code clamps), signed code rint(W' / scale) (ties
+ * to even) stored as code + 8, zero point 8; an all-zero group stores scale 0
+ * and codes 8.  The packed buffers are in the same layout and feed the same
+ * GEMM entry points: (q - z) * scale reproduces the signed value. */
+int w4a16_quantize_pack_mode(const void *W, const void *s, int64_t N, int64_t K, int mode,
+                             void *Wq, void *scales, void *zeros, void *stream);
 
 /* Y[M][N] = X[M][K] . W_hat^T with W_hat[n][k] = (q - z) * scale * s[k].
  * X: fp16 [M][K]; Wq/scales/zeros: packed as above; s: fp16 [K] or NULL;

@@ -115,6 +115,22 @@ def test_split_k(M, N, K):
 
 
 @pytest.mark.parametrize("path", ["skinny", "window", "tiled"])
+@pytest.mark.parametrize("M", [1, 9, 40])
+def test_symmetric_weights(M, path):
+    """Weights packed on the signed -7..7 grid run through the same kernels."""
+    torch_cuda()
+    N, K = 272, 1152
+    W = weights(12, 0, N, K)
+    s = awq_scales(12, 0, K)
+    pw = w4.w4a16_quantize_pack(to_dev(W), to_dev(s), mode=w4.QUANT_SYM)
+    ref = oracle.quantize_symmetric(W, s)
+    X = activations(12, 0, M, K)
+    note(f"symmetric weights path={path} M={M}")
+    Y = run(X, pw, s, path)
+    assert_close(Y, oracle.gemm(X, ref.q, ref.scales, ref.zeros, s), f"sym M={M} {path}")
+
+
+@pytest.mark.parametrize("path", ["skinny", "window", "tiled"])
 def test_integer_case_bit_exact(path):
     """Pin P5: s = 1, integer weights with codes 0 and 15 in every group -> scale 1,
     zero point 8; X in {-1, 0, 1}: Y is an integer matmul, exact in fp16."""

@@ -10,31 +10,37 @@ from workloads import awq_scales, weights
 pytestmark = pytest.mark.gpu
 
 
-def gpu_pack(W, s):
+def gpu_pack(W, s, mode=w4.QUANT_ASYM):
     torch_cuda()
-    pw = w4.w4a16_quantize_pack(to_dev(W), None if s is None else to_dev(s))
+    pw = w4.w4a16_quantize_pack(to_dev(W), None if s is None else to_dev(s), mode=mode)
     return to_host(pw.wq), to_host(pw.scales), to_host(pw.zeros)
 
 
-def check_exact(W, s, tag):
-    note(f"pack {tag} N={W.shape[0]} K={W.shape[1]} awq={s is not None}")
-    wq, sc, z = gpu_pack(W, s)
-    ref = oracle.quantize(W, s)
+def check_exact(W, s, tag, mode=w4.QUANT_ASYM):
+    note(f"pack {tag} N={W.shape[0]} K={W.shape[1]} awq={s is not None} mode={mode}")
+    wq, sc, z = gpu_pack(W, s, mode)
+    ref = oracle.quantize(W, s) if mode == w4.QUANT_ASYM else oracle.quantize_symmetric(W, s)
     assert np.array_equal(h16_bits(sc), h16_bits(oracle.pack_meta(ref.scales))), tag
     assert np.array_equal(h16_bits(z), h16_bits(oracle.pack_meta(ref.zeros))), tag
     assert np.array_equal(wq, oracle.pack_codes(ref.q)), tag
 
 
-def test_pack_gemv_1024():
-    check_exact(weights(0, 0, 1024, 1024), None, "1024x1024")
+MODES = [w4.QUANT_ASYM, w4.QUANT_SYM]
 
 
+@pytest.mark.parametrize("mode", MODES)
+def test_pack_gemv_1024(mode):
+    check_exact(weights(0, 0, 1024, 1024), None, "1024x1024", mode)
+
+
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("N,K", [(16, 128), (48, 384), (272, 640), (1024, 4096)])
-def test_pack_awq_shapes(N, K):
-    check_exact(weights(1, 9, N, K), awq_scales(1, 9, K), f"awq {N}x{K}")
+def test_pack_awq_shapes(N, K, mode):
+    check_exact(weights(1, 9, N, K), awq_scales(1, 9, K), f"awq {N}x{K}", mode)
 
 
-def test_pack_edge_groups():
+@pytest.mark.parametrize("mode", MODES)
+def test_pack_edge_groups(mode):
     rng = np.random.default_rng(11)
     N, K = 64, 1024
     W = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
@@ -47,9 +53,24 @@ def test_pack_edge_groups():
     W[21, 640:768] = np.float16(60000.0)                # near the top of fp16
     W[22, 768:896] *= 500                               # outlier-heavy group
     W[23, 896:1024] = np.linspace(-1, 1, 128).astype(np.float16)  # ties land on .5
-    check_exact(W, None, "edge groups")
+    check_exact(W, None, "edge groups", mode)
     s = np.exp(rng.uniform(-1, 1, K)).astype(np.float16)   # keeps 60000 / s in range
-    check_exact(W, s, "edge groups + awq")
+    check_exact(W, s, "edge groups + awq", mode)
+
+
+def test_pack_symmetric_on_grid_exact():
+    # weights on the signed -7..7 grid (with +-7 in every group) come back exactly
+    rng = np.random.default_rng(6)
+    N, K, G = 32, 256, 2
+    c = rng.integers(-7, 8, size=(N, G, 128))
+    c[:, :, 0], c[:, :, 1] = 7, -7
+    scale = np.ldexp(rng.integers(64, 128, size=(N, G)).astype(np.float64),
+                     rng.integers(-16, -8, size=(N, G)))
+    W = (c * scale[:, :, None]).reshape(N, K).astype(np.float16)
+    wq, sc, zz = gpu_pack(W, None, w4.QUANT_SYM)
+    assert np.array_equal(oracle.unpack_meta(sc, N, K).astype(np.float64), scale)
+    assert np.all(oracle.unpack_meta(zz, N, K) == 8)
+    assert np.array_equal(oracle.unpack_codes(wq, N, K).astype(np.int64) - 8, c.reshape(N, K))
 
 
 def test_pack_on_grid_exact():

@@ -20,7 +20,7 @@ from .build import LIB_PATH
 
 __all__ = [
     "W4A16Error", "PackedWeight", "GROUP", "PATH_AUTO", "PATH_SKINNY", "PATH_TILED",
-    "PATH_SKINNY_WINDOW", "lib",
+    "PATH_SKINNY_WINDOW", "QUANT_ASYM", "QUANT_SYM", "lib",
     "w4a16_packed_sizes", "w4a16_quantize_pack", "w4a16_gemm", "w4a16_gemm_path",
     "w4a16_select_path", "w4a16_strerror", "w4a16_version", "EXPORTED_SYMBOLS",
     "w4a16_gemm_grouped", "GroupedCall",
@@ -28,9 +28,11 @@ __all__ = [
 
 GROUP = 128
 PATH_AUTO, PATH_SKINNY, PATH_TILED, PATH_SKINNY_WINDOW = 0, 1, 2, 3
+QUANT_ASYM, QUANT_SYM = 0, 1
 STATUS = {0: "W4A16_OK", -1: "W4A16_EINVAL", -2: "W4A16_EALIGN", -3: "W4A16_EUNSUPPORTED",
           -4: "W4A16_ENONFINITE", -5: "W4A16_ERANGE", -6: "W4A16_EHIP"}
-EXPORTED_SYMBOLS = ("w4a16_packed_sizes", "w4a16_quantize_pack", "w4a16_gemm",
+EXPORTED_SYMBOLS = ("w4a16_packed_sizes", "w4a16_quantize_pack", "w4a16_quantize_pack_mode",
+                    "w4a16_gemm",
                     "w4a16_gemm_path", "w4a16_gemm_grouped", "w4a16_gemm_grouped_ws",
                     "w4a16_gemm_workspace_size", "w4a16_select_path", "w4a16_strerror",
                     "w4a16_version")
@@ -64,6 +66,7 @@ def lib() -> ctypes.CDLL:
     i64, vp, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t)
     L.w4a16_packed_sizes.argtypes = [i64, i64, sz, sz, sz]
     L.w4a16_quantize_pack.argtypes = [vp, vp, i64, i64, vp, vp, vp, vp]
+    L.w4a16_quantize_pack_mode.argtypes = [vp, vp, i64, i64, ctypes.c_int, vp, vp, vp, vp]
     L.w4a16_gemm.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, vp]
     L.w4a16_gemm_path.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, vp]
     L.w4a16_gemm_grouped.argtypes = [ctypes.POINTER(Problem), ctypes.c_int, vp]
@@ -74,7 +77,8 @@ def lib() -> ctypes.CDLL:
     L.w4a16_strerror.argtypes = [ctypes.c_int]
     L.w4a16_strerror.restype = ctypes.c_char_p
     L.w4a16_version.argtypes = []
-    for name in ("w4a16_packed_sizes", "w4a16_quantize_pack", "w4a16_gemm", "w4a16_gemm_path",
+    for name in ("w4a16_packed_sizes", "w4a16_quantize_pack", "w4a16_quantize_pack_mode",
+                 "w4a16_gemm", "w4a16_gemm_path",
                  "w4a16_gemm_grouped", "w4a16_gemm_grouped_ws", "w4a16_gemm_workspace_size",
                  "w4a16_select_path", "w4a16_version"):
         getattr(L, name).restype = ctypes.c_int
@@ -137,8 +141,10 @@ def _dev_ptr(t, name, dtype=None, numel=None):
     return ctypes.c_void_p(t.data_ptr())
 
 
-def w4a16_quantize_pack(W, s=None, out: PackedWeight | None = None) -> PackedWeight:
-    """Quantize fp16 W[N][K] (AWQ scale s[K] or None) into a PackedWeight (blocks)."""
+def w4a16_quantize_pack(W, s=None, out: PackedWeight | None = None,
+                        mode: int = QUANT_ASYM) -> PackedWeight:
+    """Quantize fp16 W[N][K] (AWQ scale s[K] or None) into a PackedWeight (blocks).
+    mode: QUANT_ASYM (w4a16_quantize_pack) or QUANT_SYM (signed -7..7 grid)."""
     torch = _torch()
     if W.dim() != 2:
         raise ValueError("W must be 2-D [N][K]")
@@ -149,8 +155,8 @@ def w4a16_quantize_pack(W, s=None, out: PackedWeight | None = None) -> PackedWei
                            torch.empty(sc_b // 2, dtype=torch.float16, device=W.device),
                            torch.empty(z_b // 2, dtype=torch.float16, device=W.device),
                            N, K)
-    rc = lib().w4a16_quantize_pack(
-        _dev_ptr(W, "W", torch.float16), _dev_ptr(s, "s", torch.float16, K), N, K,
+    rc = lib().w4a16_quantize_pack_mode(
+        _dev_ptr(W, "W", torch.float16), _dev_ptr(s, "s", torch.float16, K), N, K, mode,
         _dev_ptr(out.wq, "wq", torch.uint8, wq_b),
         _dev_ptr(out.scales, "scales", torch.float16, sc_b // 2),
         _dev_ptr(out.zeros, "zeros", torch.float16, z_b // 2), _stream_handle(W.device))

@@ -55,7 +55,7 @@ const char *w4a16_strerror(int status) {
     case W4A16_OK: return "ok";
     case W4A16_EINVAL: return "invalid argument (NULL pointer, or M/N/K out of range, K % 128 != 0, N % 16 != 0)";
     case W4A16_EALIGN: return "pointer not 16-byte aligned";
-    case W4A16_EUNSUPPORTED: return "unsupported kernel path";
+    case W4A16_EUNSUPPORTED: return "unsupported kernel path or quantization mode";
     case W4A16_ENONFINITE: return "non-finite W or s, or s <= 0";
     case W4A16_ERANGE: return "group scale exceeds the fp16 range";
     case W4A16_EHIP: return "HIP runtime error";
@@ -74,8 +74,9 @@ int w4a16_packed_sizes(int64_t N, int64_t K, size_t *wq_bytes, size_t *scales_by
   return W4A16_OK;
 }
 
-int w4a16_quantize_pack(const void *W, const void *s, int64_t N, int64_t K, void *Wq,
-                        void *scales, void *zeros, void *stream) {
+int w4a16_quantize_pack_mode(const void *W, const void *s, int64_t N, int64_t K, int mode,
+                             void *Wq, void *scales, void *zeros, void *stream) {
+  if (mode != W4A16_QUANT_ASYM && mode != W4A16_QUANT_SYM) return W4A16_EUNSUPPORTED;
   if (!W || !Wq || !scales || !zeros) return W4A16_EINVAL;
   int rc = check_shape(N, K);
   if (rc) return rc;
@@ -86,7 +87,8 @@ int w4a16_quantize_pack(const void *W, const void *s, int64_t N, int64_t K, void
   if ((rc = status_word(&status))) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (hipMemsetAsync(status, 0, sizeof(unsigned), st) != hipSuccess) return W4A16_EHIP;
-  if (w4a16::launch_pack(W, s, (int)N, (int)K, Wq, scales, zeros, status, st) != hipSuccess)
+  if (w4a16::launch_pack(W, s, (int)N, (int)K, Wq, scales, zeros, status,
+                         mode == W4A16_QUANT_SYM, st) != hipSuccess)
     return W4A16_EHIP;
   unsigned host = 0;
   if (hipMemcpyAsync(&host, status, sizeof(unsigned), hipMemcpyDeviceToHost, st) != hipSuccess)
@@ -95,6 +97,11 @@ int w4a16_quantize_pack(const void *W, const void *s, int64_t N, int64_t K, void
   if (host & w4a16::kPackNonFinite) return W4A16_ENONFINITE;
   if (host & w4a16::kPackRange) return W4A16_ERANGE;
   return W4A16_OK;
+}
+
+int w4a16_quantize_pack(const void *W, const void *s, int64_t N, int64_t K, void *Wq,
+                        void *scales, void *zeros, void *stream) {
+  return w4a16_quantize_pack_mode(W, s, N, K, W4A16_QUANT_ASYM, Wq, scales, zeros, stream);
 }
 
 int w4a16_select_path(int64_t M, int64_t N, int64_t K) {

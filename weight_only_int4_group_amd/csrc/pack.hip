@@ -10,6 +10,12 @@
 // scale = range / 15 rounded up to fp16, z = rint(-min / scale),
 // q = clamp(rint(W' / scale) + z, 0, 15), ties to even.
 //
+// The symmetric variant (the signed -7..7 grid of the practitioner notes at
+// mhpq.cn, section 2.1) keeps every step but the grid: scale = max|W'| / 7
+// rounded up to fp16, signed code c = clamp(rint(W' / scale), -7, 7) stored as
+// c + 8 with the constant zero point 8 (so (q - z) * scale is unchanged for
+// the GEMM kernels); an all-zero group stores scale 0 and codes 8.
+//
 // One 64-lane wave handles one packed tile (16 rows x 128 columns = one group
 // of 16 rows).  Lane L = 16c + r reads the 32 values of row r that it will
 // own in the packed tile (columns 32t + 8c + j), so the group's min/max is a
@@ -48,6 +54,7 @@ __device__ __forceinline__ bool finite_h(_Float16 x) {
   return (b & 0x7C00u) != 0x7C00u;
 }
 
+template <bool SYM>
 __global__ __launch_bounds__(256) void pack_kernel(const _Float16 *__restrict__ W,
                                                    const _Float16 *__restrict__ s, int N, int K,
                                                    u32x4 *__restrict__ Wq,
@@ -94,30 +101,41 @@ __global__ __launch_bounds__(256) void pack_kernel(const _Float16 *__restrict__ 
   mx = fmax(mx, __shfl_xor(mx, 16));
   mx = fmax(mx, __shfl_xor(mx, 32));
 
-  const double range = mx - mn;
-  _Float16 sc16 = 0, z16 = 0;
-  double scale = 1.0, z = 0.0;
+  // asymmetric: the range [mn, mx]; symmetric: the largest magnitude
+  const double range = SYM ? (mx > -mn ? mx : -mn) : mx - mn;
+  _Float16 sc16 = 0, z16 = SYM ? (_Float16)8 : (_Float16)0;
+  double scale = 1.0, z = SYM ? 8.0 : 0.0;
   const bool live = range > 0.0;
   if (live) {
-    if (!fp16_ceil(range / 15.0, &sc16)) {
+    if (!fp16_ceil(range / (SYM ? 7.0 : 15.0), &sc16)) {
       bad |= kPackRange;
       sc16 = 0;
     } else {
       scale = (double)sc16;
-      z = rint(-mn / scale);
-      z16 = (_Float16)(int)z;  // the integer 0..15; via int so that -0.0 stores as +0
+      if (!SYM) {
+        z = rint(-mn / scale);
+        z16 = (_Float16)(int)z;  // the integer 0..15; via int so that -0.0 stores as +0
+      }
     }
   }
 
-  u32x4 out = {0, 0, 0, 0};
+  // an all-zero group: codes 0 (asymmetric) or 8 (symmetric, the zero point)
+  const uint32_t fill = SYM ? 0x88888888u : 0u;
+  u32x4 out = {fill, fill, fill, fill};
   if (live) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       uint32_t word = 0;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        double v = rint(wp[8 * t + j] / scale) + z;
-        v = v < 0.0 ? 0.0 : (v > 15.0 ? 15.0 : v);
+        double v;
+        if (SYM) {
+          v = rint(wp[8 * t + j] / scale);
+          v = (v < -7.0 ? -7.0 : (v > 7.0 ? 7.0 : v)) + 8.0;
+        } else {
+          v = rint(wp[8 * t + j] / scale) + z;
+          v = v < 0.0 ? 0.0 : (v > 15.0 ? 15.0 : v);
+        }
         const uint32_t code = (uint32_t)v;
         const int slot = (j >> 1) + 4 * (j & 1);  // column j -> 4-bit slot
         word |= code << (4 * slot);
@@ -140,12 +158,17 @@ __global__ __launch_bounds__(256) void pack_kernel(const _Float16 *__restrict__ 
 }  // namespace
 
 hipError_t launch_pack(const void *W, const void *s, int N, int K, void *Wq, void *scales,
-                       void *zeros, unsigned *status, hipStream_t stream) {
+                       void *zeros, unsigned *status, bool symmetric, hipStream_t stream) {
   const long long tiles = (long long)(N / kTileRows) * (K / kGroup);
   const long long blocks = (tiles + 3) / 4;
-  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
-                     (const _Float16 *)W, (const _Float16 *)s, N, K, (u32x4 *)Wq,
-                     (_Float16 *)scales, (_Float16 *)zeros, status);
+  if (symmetric)
+    hipLaunchKernelGGL(pack_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       (const _Float16 *)W, (const _Float16 *)s, N, K, (u32x4 *)Wq,
+                       (_Float16 *)scales, (_Float16 *)zeros, status);
+  else
+    hipLaunchKernelGGL(pack_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       (const _Float16 *)W, (const _Float16 *)s, N, K, (u32x4 *)Wq,
+                       (_Float16 *)scales, (_Float16 *)zeros, status);
   return hipGetLastError();
 }
 

@@ -11,7 +11,7 @@ constexpr unsigned kPackNonFinite = 1u;
 constexpr unsigned kPackRange = 2u;
 
 hipError_t launch_pack(const void *W, const void *s, int N, int K, void *Wq, void *scales,
-                       void *zeros, unsigned *status, hipStream_t stream);
+                       void *zeros, unsigned *status, bool symmetric, hipStream_t stream);
 
 // One dequantize-matmul problem (validated by the caller).
 struct GemmDesc {
