@@ -48,12 +48,12 @@ from .quantizer import (GROUP, QMAX, SYM_QMAX, SYM_ZERO, NonFiniteInput, OracleE
 from .layout import (META_QUAD, TILE_BYTES, TILE_ROWS, meta_groups, meta_index, nibble_address,
                      pack_codes, pack_meta, unpack_codes, unpack_meta)
 from .matmul import dequantize, gemm
-from . import accounting, exact
+from . import accounting, exact, spec
 
 __all__ = [
     "GROUP", "QMAX", "NonFiniteInput", "OracleError", "QuantResult", "ScaleOverflow",
     "quantize", "quantize_symmetric", "SYM_QMAX", "SYM_ZERO", "round_up_fp16", "META_QUAD", "TILE_BYTES", "TILE_ROWS", "meta_groups",
     "meta_index", "nibble_address",
     "pack_codes", "pack_meta", "unpack_codes", "unpack_meta", "dequantize", "gemm",
-    "accounting", "exact",
+    "accounting", "exact", "spec",
 ]
