@@ -27,7 +27,9 @@ Readings where the page leaves a step open (taken identically by the library):
      distribution by at most V * 2^-40 in total variation;
   S4 if the corrected residual has no mass in fixed point, the draw uses the
      target row of that position instead; if that has none either, the token
-     is -1.
+     is -1;
+  S5 a draft id outside 0 .. V-1 is rejected; u' is clamped to [0, 1) on the
+     2^-32 grid (NaN counts as 0).
 """
 from __future__ import annotations
 
@@ -53,7 +55,9 @@ def draw(w: np.ndarray, u: float) -> int:
     S = sum(wi)
     if S == 0:
         return -1
-    ui = int(np.floor(np.float64(np.float32(u)) * float(2 ** U_BITS)))
+    uf = np.float64(np.float32(u))
+    ui = int(np.floor(uf * float(2 ** U_BITS))) if uf > 0 else 0     # NaN, negatives: 0
+    ui = min(ui, 2 ** U_BITS - 1)                                    # S5: u' < 1
     T = (ui * S) >> U_BITS
     acc = 0
     for x, v in enumerate(wi):
@@ -70,10 +74,11 @@ def verify(p_target: np.ndarray, p_draft: np.ndarray, draft: np.ndarray, u_accep
     pt = _clean(p_target)
     pd = _clean(p_draft)
     K = pd.shape[0]
+    V = pt.shape[1]
     for i in range(K):
         x = int(draft[i])
         u = np.float64(np.float32(u_accept[i]))
-        if not (u * pd[i, x] <= pt[i, x]):       # rejected (S2)
+        if not (0 <= x < V) or not (u * pd[i, x] <= pt[i, x]):   # rejected (S2, S5)
             tok = draw(np.maximum(pt[i] - pd[i], 0.0), u_sample)
             if tok < 0:
                 tok = draw(pt[i], u_sample)      # S4
