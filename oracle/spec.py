@@ -18,13 +18,17 @@ Readings where the page leaves a step open (taken identically by the library):
   S2 the acceptance test is the exact comparison u * p_draft <= p_target in
      fp64 (the product of two fp32 values is exact there), so p_draft = 0
      always accepts;
-  S3 a draw from weights w (the corrected residual, or the target row) is an
-     inverse-CDF draw in fixed point: w_int(x) = floor(w(x) * 2^40), summed
-     exactly in integers; with u' the sampling uniform, T = (floor(u' * 2^32) *
-     S) >> 32 for S = sum w_int, and the token is the smallest x whose
-     inclusive prefix sum exceeds T.  Sums are exact, so the order of
+  S3 a draw is an inverse-CDF draw in fixed point.  Each probability p is
+     taken to fx(p) = floor(p * 2^40); the target row's weights are fx(p_target)
+     and the corrected residual's are max(0, fx(p_target) - fx(p_draft)), the
+     page's max(0, p_target - p_draft) formed on the fixed-point values (within
+     one unit, 2^-40, of the fixed point of the real difference).  Weights are
+     summed exactly in integers; with u' the sampling uniform, T = (floor(u' *
+     2^32) * S) >> 32 for S = sum of the weights, and the token is the smallest
+     x whose inclusive prefix sum exceeds T.  Sums are exact, so the order of
      summation cannot change the token; the fixed point moves the drawn
-     distribution by at most V * 2^-40 in total variation;
+     distribution by at most about V * 2^-40 in total variation.  (Rows are
+     taken to sum to less than 2^12, so every partial sum stays below 2^52.)
   S4 if the corrected residual has no mass in fixed point, the draw uses the
      target row of that position instead; if that has none either, the token
      is -1;
@@ -45,13 +49,13 @@ def _clean(p: np.ndarray) -> np.ndarray:
 
 
 def fixed_weights(w: np.ndarray) -> np.ndarray:
-    """floor(w * 2^40) as Python-exact integers (object array avoids int64 overflow checks)."""
+    """fx(w) = floor(w * 2^40) for w >= 0, as int64 (S3)."""
     return np.floor(np.asarray(w, dtype=np.float64) * float(2 ** FIX_BITS)).astype(np.int64)
 
 
-def draw(w: np.ndarray, u: float) -> int:
-    """Inverse-CDF draw in fixed point (S3); -1 if w has no mass."""
-    wi = [int(v) for v in fixed_weights(w)]
+def draw_fixed(wi, u: float) -> int:
+    """Inverse-CDF draw from non-negative integer weights (S3); -1 if they have no mass."""
+    wi = [int(v) for v in wi]
     S = sum(wi)
     if S == 0:
         return -1
@@ -67,6 +71,16 @@ def draw(w: np.ndarray, u: float) -> int:
     raise AssertionError("T < S always")
 
 
+def draw(w: np.ndarray, u: float) -> int:
+    """Inverse-CDF draw from probabilities w >= 0 in fixed point (S3); -1 if no mass."""
+    return draw_fixed(fixed_weights(w), u)
+
+
+def residual_weights(pt_row: np.ndarray, pd_row: np.ndarray) -> np.ndarray:
+    """The corrected residual max(0, p_target - p_draft) on the fixed-point values (S3)."""
+    return np.maximum(fixed_weights(pt_row) - fixed_weights(pd_row), 0)
+
+
 def verify(p_target: np.ndarray, p_draft: np.ndarray, draft: np.ndarray, u_accept: np.ndarray,
            u_sample: float) -> tuple[int, int]:
     """One sequence.  p_target [K+1][V], p_draft [K][V], draft [K] token ids, u_accept [K],
@@ -79,7 +93,7 @@ def verify(p_target: np.ndarray, p_draft: np.ndarray, draft: np.ndarray, u_accep
         x = int(draft[i])
         u = np.float64(np.float32(u_accept[i]))
         if not (0 <= x < V) or not (u * pd[i, x] <= pt[i, x]):   # rejected (S2, S5)
-            tok = draw(np.maximum(pt[i] - pd[i], 0.0), u_sample)
+            tok = draw_fixed(residual_weights(pt[i], pd[i]), u_sample)
             if tok < 0:
                 tok = draw(pt[i], u_sample)      # S4
             return i, tok

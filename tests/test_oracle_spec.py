@@ -121,6 +121,38 @@ def test_v4_fixed_point_draw_exact_cases():
     assert spec.draw(w, np.float32(1 - 2 ** -24)) == 4      # last token with mass
 
 
+def test_v4_residual_draw_exact_cases():
+    """The token drawn after a rejection, for dyadic p_target / p_draft (exact in fixed
+    point) and u on the 2^-32 grid, against the exact rational inverse CDF of the page's
+    corrected distribution max(0, p_target - p_draft)."""
+    rng = np.random.default_rng(8)
+    checked = 0
+    for _ in range(300):
+        V = int(rng.integers(2, 10))
+        pt = (rng.integers(0, 33, size=V) / 32.0).astype(np.float32)
+        pd = (rng.integers(0, 33, size=V) / 32.0).astype(np.float32)
+        x = int(rng.integers(0, V))
+        if not (pt[x] < pd[x]):
+            continue                                         # need a rejection at u = 1 - 2^-24
+        u = float(rng.integers(0, 2 ** 24)) / 2 ** 24
+        res = [max(Fraction(float(a)) - Fraction(float(b)), Fraction(0)) for a, b in zip(pt, pd)]
+        n, tok = spec.verify(np.stack([pt, pt]), pd[None], np.array([x]),
+                             np.array([1 - 2 ** -24], np.float32), np.float32(u))
+        assert n == 0
+        if sum(res) == 0:                                    # S4: the target row instead
+            assert tok == spec.draw(pt, np.float32(u))
+            continue
+        target = Fraction(u) * sum(res)
+        acc = Fraction(0)
+        for y, v in enumerate(res):
+            acc += v
+            if acc > target:
+                break
+        assert tok == y
+        checked += 1
+    assert checked > 50
+
+
 def test_mutation_swapped_ratio_breaks_v1_and_v2():
     def swapped(pt, pd, draft, u_acc, u_s):
         pt = np.asarray(pt, np.float64)
