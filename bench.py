@@ -23,6 +23,8 @@ Printed JSON line:
   batched       the same 8B layer at speculative-verify batches M = 2, 5, 9 and a
                 Qwen2-7B-shaped layer at batched-decode M = 16, 64, 256, one grouped
                 call per step (streaming kernel for M <= 16, else the tiled GEMM);
+  spec_verify   the accept / reject / draw step after a K = 4 verify pass over the
+                Llama-3 vocabulary (V = 128256), for 1 and 64 sequences per call;
   prefill       the 70B-shaped layer at M = 4096 (compute-bound): TFLOP/s
                 against the dense fp16 MFMA peak;
   cpu_baseline  the fp64 CPU oracle on a bounded sample of the same workload;
@@ -219,6 +221,39 @@ def variant(mats, groups, launch_ms, steps, wall, unit_key):
     return out
 
 
+def spec_verify_line(torch, w4, B, K, V, steps=200, warmup=20, per=10):
+    """Speculative-sampling verification (w4a16_spec_verify) of B sequences with K drafts
+    over a V-token vocabulary.  The inputs are cloned into enough copies that the rows
+    the calls touch exceed 1 GiB, so every call reads them from HBM.  Algorithmic bytes
+    per call: the rows the outcome needs, read once (target and draft rows at a
+    rejection, the target row after K acceptances), plus the K probes and the outputs."""
+    from workloads import verify as wv
+    host = wv.batch(7, B, K, V)
+    base = [torch.from_numpy(a).to("cuda") for a in host]
+    n, _ = w4.w4a16_spec_verify(*base)
+    n = n.cpu().numpy()
+    rows = int(np.sum(np.where(n < K, 2, 1)))
+    call_bytes = rows * V * 4 + B * K * (4 + 4 + 4 + 4) + B * (4 + 8)
+    copies = max(1, -(-(1 << 30) // call_bytes))
+    sets = [base] + [[t.clone() for t in base] for _ in range(copies - 1)]
+    outs = [(torch.empty(B, dtype=torch.int32, device="cuda"),
+             torch.empty(B, dtype=torch.int32, device="cuda")) for _ in range(copies)]
+    ws = torch.empty(max(1, w4.w4a16_spec_verify_workspace_size(B, K, V)), dtype=torch.uint8,
+                     device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    calls = [[w4.SpecVerifyCall(*sets[c], out=outs[c], workspace=ws, stream=st)]
+             for c in range(copies)]
+    wall, lms = timed(calls, steps, warmup, torch, per=per)
+    kern = float(np.mean(lms[0])) * 1e-3
+    return {"workload": f"spec_verify: B={B} sequences, K={K} drafts, V={V}, fp32 "
+                        "probabilities, synthetic target/draft distributions",
+            "B": B, "K": K, "V": V, "accepted_mean": round(float(n.mean()), 3),
+            "copies": copies, "us_per_call": round(wall / steps * 1e6, 2),
+            "kernel_us_per_call": round(kern * 1e6, 2), "call_bytes": call_bytes,
+            "kernel_GB/s": round(call_bytes / kern / 1e9, 1),
+            "frac_of_hbm_peak": round(call_bytes / kern / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def ceilings(torch, reps=10):
     """Measured ceilings on this GPU, for context: a plain device-to-device copy, and
     the vendor dense fp16 GEMM (torch.matmul on contiguous fp16 operands) at the 70B
@@ -304,6 +339,7 @@ def main():
     ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--no-batched", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true")
+    ap.add_argument("--no-spec", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-run", action="store_true",
                     help="only the short fixed sequence used for counter collection")
@@ -381,6 +417,11 @@ def main():
     else:
         del pool, mats
     torch.cuda.empty_cache()
+
+    if not args.no_spec:
+        log("timing speculative verification")
+        out["spec_verify"] = [spec_verify_line(torch, w4, B, 4, 128256) for B in (1, 64)]
+        torch.cuda.empty_cache()
 
     if not args.no_prefill:
         pcfg = workloads.config_by_name("llama_70b_prefill")

@@ -186,6 +186,42 @@ int w4a16_gemm_workspace_size(const w4a16_problem *problems, int count, size_t *
 int w4a16_gemm_grouped_ws(const w4a16_problem *problems, int count, void *workspace,
                           size_t workspace_bytes, void *stream);
 
+/* Speculative-sampling verification: the accept / reject step that consumes a
+ * verify pass ("Chapter 22: Advanced inference optimisation", aiwing.uk,
+ * section 22.1).  For each of B sequences: draft token x_i (i < K) is
+ * accepted if u_i <= p_target(x_i) / p_draft(x_i); at the first rejection
+ * one token is drawn from normalize(max(0, p_target_i - p_draft_i)) and the
+ * later drafts are dropped; after K acceptances one more token is drawn from
+ * the target distribution of position K.
+ *   p_target fp32 [B][K+1][V], p_draft fp32 [B][K][V] (probabilities, not
+ *   necessarily normalised; NaN and negatives count as 0), draft int32 [B][K]
+ *   token ids (an id outside 0..V-1 is rejected), u_accept fp32 [B][K] and
+ *   u_sample fp32 [B] uniforms in [0, 1) supplied by the caller, all
+ *   row-major and contiguous.
+ *   Outputs: n_accepted int32 [B] (0..K) and token int32 [B] (the drawn
+ *   token, or -1 if the row it is drawn from has no mass).
+ * Every decision is exact: the test is u * p_draft <= p_target in fp64; a draw
+ * is an inverse-CDF draw in fixed point, with fx(p) = floor(p * 2^40), weights
+ * fx(p_target) for the target row and max(0, fx(p_target) - fx(p_draft)) for
+ * the corrected residual, exact integer sums, and threshold
+ * (floor(u' * 2^32) * S) >> 32 (u' clamped to [0, 1), NaN as 0), taking the
+ * smallest id whose inclusive prefix sum exceeds it; with no mass in the
+ * residual the target row of that position is used.
+ * Limits (EINVAL beyond them): K <= 1024, V and B <= 2^24, B * (K+1) * V <=
+ * 2^40, B * ceil(V / 4096) < 2^24.  Rows whose entries sum to 2^12 or more
+ * (infinities included) are outside the contract: the call still ends and
+ * writes only its outputs, whose values are then unspecified.
+ * workspace: caller-owned device memory of at least the size
+ * w4a16_spec_verify_workspace_size reports, 256-byte aligned (EALIGN), not
+ * cleared by the caller; calls that share a workspace must not overlap.
+ * Device pointers, 4-byte aligned (EALIGN); p_draft, draft and u_accept may be
+ * NULL when K = 0; B = 0 is a no-op.  Asynchronous on `stream` (two launches). */
+int w4a16_spec_verify_workspace_size(int64_t B, int64_t K, int64_t V, size_t *bytes);
+int w4a16_spec_verify(const void *p_target, const void *p_draft, const void *draft,
+                      const void *u_accept, const void *u_sample, int64_t B, int64_t K, int64_t V,
+                      void *workspace, size_t workspace_bytes, void *n_accepted, void *token,
+                      void *stream);
+
 /* Which path AUTO takes for this shape (host only; no GPU call). */
 int w4a16_select_path(int64_t M, int64_t N, int64_t K);
 

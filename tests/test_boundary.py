@@ -172,3 +172,54 @@ def test_quantize_mode_validation():
     for mode in (w4.QUANT_ASYM, w4.QUANT_SYM):
         assert L.w4a16_quantize_pack_mode(A16, None, 16, 100, mode, A16, A16, A16, None) == -1
         assert L.w4a16_quantize_pack_mode(ODD, None, 16, 128, mode, A16, A16, A16, None) == -2
+
+
+def test_spec_verify_workspace_size():
+    # per sequence: two 8-byte sums per 4096-id chunk and the first rejection (4 bytes),
+    # rounded up to 256 bytes
+    assert w4.w4a16_spec_verify_workspace_size(64, 4, 128256) == -(-(64 * 32 * 16 + 64 * 4) // 256) * 256
+    assert w4.w4a16_spec_verify_workspace_size(1, 0, 1) == 256
+    assert w4.w4a16_spec_verify_workspace_size(0, 4, 32000) == 0
+    for B, K, Vv in ((-1, 4, 10), (1, -1, 10), (1, 4, 0), (1, 1025, 10), (1 << 20, 1024, 1 << 20),
+                     (1 << 22, 0, 1 << 14)):
+        with pytest.raises(w4.W4A16Error):
+            w4.w4a16_spec_verify_workspace_size(B, K, Vv)
+    L = w4.lib()
+    assert L.w4a16_spec_verify_workspace_size(1, 1, 1, None) == -1
+
+
+def test_spec_verify_validation():
+    L = w4.lib()
+    A4 = V((1 << 20) + 4)   # 4-byte aligned
+    ODD1 = V((1 << 20) + 1)
+    WS = V(1 << 24)         # 256-byte aligned
+    big = 1 << 20
+
+    def call(pt=A4, pd=A4, dr=A4, ua=A4, us=A4, B=2, K=4, Vv=32000, ws=WS, wsb=big,
+             na=A4, tk=A4):
+        return L.w4a16_spec_verify(pt, pd, dr, ua, us, B, K, Vv, ws, wsb, na, tk, None)
+
+    # shapes: B, K >= 0, V >= 1, K <= 1024, B and V <= 2^24, B (K+1) V <= 2^40,
+    # B * ceil(V / 4096) < 2^24
+    assert call(B=-1) == -1
+    assert call(K=-1) == -1
+    assert call(Vv=0) == -1
+    assert call(K=1025) == -1
+    assert call(Vv=(1 << 24) + 1) == -1
+    assert call(B=(1 << 24) + 1) == -1
+    assert call(B=1 << 20, K=1024, Vv=1 << 20) == -1
+    assert call(B=1 << 22, K=0, Vv=1 << 14) == -1
+    # an empty batch is a no-op, whatever the pointers
+    assert call(B=0, pt=None, us=None, na=None, tk=None, ws=None, wsb=0) == 0
+    # required pointers
+    for name in ("pt", "us", "na", "tk", "ws", "pd", "dr", "ua"):
+        assert call(**{name: None}) == -1, name
+    # a workspace smaller than w4a16_spec_verify_workspace_size
+    need = w4.w4a16_spec_verify_workspace_size(2, 4, 32000)
+    assert call(wsb=need - 1) == -1
+    # 4-byte alignment of every buffer, 256 of the workspace
+    for name in ("pt", "pd", "dr", "ua", "us", "na", "tk"):
+        assert call(**{name: ODD1}) == -2, name
+    assert call(ws=V((1 << 24) + 128)) == -2
+    # with K = 0 the draft buffers are not read and may be NULL (or misaligned)
+    assert call(K=0, pd=None, dr=None, ua=None, pt=ODD1) == -2

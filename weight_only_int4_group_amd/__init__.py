@@ -23,7 +23,8 @@ __all__ = [
     "PATH_SKINNY_WINDOW", "QUANT_ASYM", "QUANT_SYM", "lib",
     "w4a16_packed_sizes", "w4a16_quantize_pack", "w4a16_gemm", "w4a16_gemm_path",
     "w4a16_select_path", "w4a16_strerror", "w4a16_version", "EXPORTED_SYMBOLS",
-    "w4a16_gemm_grouped", "GroupedCall",
+    "w4a16_gemm_grouped", "GroupedCall", "w4a16_spec_verify",
+    "w4a16_spec_verify_workspace_size", "SpecVerifyCall",
 ]
 
 GROUP = 128
@@ -34,8 +35,9 @@ STATUS = {0: "W4A16_OK", -1: "W4A16_EINVAL", -2: "W4A16_EALIGN", -3: "W4A16_EUNS
 EXPORTED_SYMBOLS = ("w4a16_packed_sizes", "w4a16_quantize_pack", "w4a16_quantize_pack_mode",
                     "w4a16_gemm",
                     "w4a16_gemm_path", "w4a16_gemm_grouped", "w4a16_gemm_grouped_ws",
-                    "w4a16_gemm_workspace_size", "w4a16_select_path", "w4a16_strerror",
-                    "w4a16_version")
+                    "w4a16_gemm_workspace_size", "w4a16_spec_verify",
+                    "w4a16_spec_verify_workspace_size", "w4a16_select_path",
+                    "w4a16_strerror", "w4a16_version")
 
 
 class Problem(ctypes.Structure):
@@ -73,6 +75,9 @@ def lib() -> ctypes.CDLL:
     L.w4a16_gemm_grouped_ws.argtypes = [ctypes.POINTER(Problem), ctypes.c_int, vp,
                                         ctypes.c_size_t, vp]
     L.w4a16_gemm_workspace_size.argtypes = [ctypes.POINTER(Problem), ctypes.c_int, sz]
+    L.w4a16_spec_verify.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp, ctypes.c_size_t, vp,
+                                    vp, vp]
+    L.w4a16_spec_verify_workspace_size.argtypes = [i64, i64, i64, ctypes.POINTER(ctypes.c_size_t)]
     L.w4a16_select_path.argtypes = [i64, i64, i64]
     L.w4a16_strerror.argtypes = [ctypes.c_int]
     L.w4a16_strerror.restype = ctypes.c_char_p
@@ -80,7 +85,8 @@ def lib() -> ctypes.CDLL:
     for name in ("w4a16_packed_sizes", "w4a16_quantize_pack", "w4a16_quantize_pack_mode",
                  "w4a16_gemm", "w4a16_gemm_path",
                  "w4a16_gemm_grouped", "w4a16_gemm_grouped_ws", "w4a16_gemm_workspace_size",
-                 "w4a16_select_path", "w4a16_version"):
+                 "w4a16_spec_verify", "w4a16_spec_verify_workspace_size", "w4a16_select_path",
+                 "w4a16_version"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -249,3 +255,71 @@ def w4a16_gemm_grouped(items):
             for (X, pw, s) in items]
     GroupedCall(full)()
     return [it[3] for it in full]
+
+
+def w4a16_spec_verify_workspace_size(B: int, K: int, V: int) -> int:
+    n = ctypes.c_size_t()
+    rc = lib().w4a16_spec_verify_workspace_size(B, K, V, ctypes.byref(n))
+    if rc:
+        raise W4A16Error(rc, "w4a16_spec_verify_workspace_size")
+    return n.value
+
+
+class SpecVerifyCall:
+    """A prepared w4a16_spec_verify call over fixed buffers: shapes are checked, pointers
+    marshalled and the workspace allocated once, so each call is a single C call (two
+    kernel launches) on the stream.
+
+    p_target fp32 [B][K+1][V], p_draft fp32 [B][K][V], draft int32 [B][K], u_accept fp32
+    [B][K], u_sample fp32 [B] (device tensors).  Each call writes n_accepted and token,
+    int32 [B] each: the number of accepted drafts and the token drawn after them (-1 if
+    the row it is drawn from has no mass).  `workspace` (uint8 device tensor of at least
+    w4a16_spec_verify_workspace_size bytes) is allocated when not given; calls sharing a
+    workspace must not overlap in time on different streams."""
+
+    def __init__(self, p_target, p_draft, draft, u_accept, u_sample, out=None, workspace=None,
+                 stream=None):
+        torch = _torch()
+        if p_target.dim() != 3:
+            raise ValueError("p_target must be [B][K+1][V]")
+        B, K1, V = p_target.shape
+        K = K1 - 1
+        if K < 0:
+            raise ValueError("p_target needs at least one position")
+        if tuple(p_draft.shape) != (B, K, V) or tuple(draft.shape) != (B, K) \
+                or tuple(u_accept.shape) != (B, K) or tuple(u_sample.shape) != (B,):
+            raise ValueError("p_draft [B][K][V], draft [B][K], u_accept [B][K], u_sample [B]")
+        ws_bytes = w4a16_spec_verify_workspace_size(B, K, V)
+        dev = p_target.device
+        if workspace is None:
+            workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+        elif workspace.numel() < ws_bytes:
+            raise ValueError(f"workspace needs {ws_bytes} bytes")
+        if out is None:
+            out = (torch.empty(B, dtype=torch.int32, device=dev),
+                   torch.empty(B, dtype=torch.int32, device=dev))
+        self.out = out
+        self.keep = (p_target, p_draft, draft, u_accept, u_sample, workspace)
+        self.device = dev
+        self.stream = None if stream is None else ctypes.c_void_p(stream)
+        self.args = (
+            _dev_ptr(p_target, "p_target", torch.float32),
+            _dev_ptr(p_draft, "p_draft", torch.float32),
+            _dev_ptr(draft, "draft", torch.int32), _dev_ptr(u_accept, "u_accept", torch.float32),
+            _dev_ptr(u_sample, "u_sample", torch.float32), B, K, V,
+            _dev_ptr(workspace, "workspace", torch.uint8), workspace.numel(),
+            _dev_ptr(out[0], "n_accepted", torch.int32, B),
+            _dev_ptr(out[1], "token", torch.int32, B))
+
+    def __call__(self):
+        st = self.stream if self.stream is not None else _stream_handle(self.device)
+        rc = lib().w4a16_spec_verify(*self.args, st)
+        if rc:
+            raise W4A16Error(rc, "w4a16_spec_verify")
+        return self.out
+
+
+def w4a16_spec_verify(p_target, p_draft, draft, u_accept, u_sample, out=None, workspace=None):
+    """Speculative-sampling verification of B sequences on the current stream; returns
+    (n_accepted, token).  Arguments as for SpecVerifyCall."""
+    return SpecVerifyCall(p_target, p_draft, draft, u_accept, u_sample, out, workspace)()

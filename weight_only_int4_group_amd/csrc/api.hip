@@ -243,6 +243,44 @@ int w4a16_gemm_grouped(const w4a16_problem *problems, int count, void *stream) {
   return w4a16_gemm_grouped_ws(problems, count, nullptr, 0, stream);
 }
 
+static bool spec_shape_ok(int64_t B, int64_t K, int64_t V) {
+  if (B < 0 || K < 0 || V < 1 || B > (int64_t(1) << 24) || K > 1024 || V > (int64_t(1) << 24))
+    return false;
+  if (B * (K + 1) * V > (int64_t(1) << 40)) return false;
+  // the first launch has B * chunks workgroups of 256 threads
+  return B * (int64_t)w4a16::spec_verify_chunks((int)V) < (int64_t(1) << 24);
+}
+
+int w4a16_spec_verify_workspace_size(int64_t B, int64_t K, int64_t V, size_t *bytes) {
+  if (!bytes || !spec_shape_ok(B, K, V)) return W4A16_EINVAL;
+  *bytes = B == 0 ? 0 : w4a16::spec_verify_workspace_bytes((int)B, (int)V);
+  return W4A16_OK;
+}
+
+int w4a16_spec_verify(const void *p_target, const void *p_draft, const void *draft,
+                      const void *u_accept, const void *u_sample, int64_t B, int64_t K, int64_t V,
+                      void *workspace, size_t workspace_bytes, void *n_accepted, void *token,
+                      void *stream) {
+  if (!spec_shape_ok(B, K, V)) return W4A16_EINVAL;
+  if (B == 0) return W4A16_OK;
+  if (!p_target || !u_sample || !n_accepted || !token || !workspace) return W4A16_EINVAL;
+  if (K > 0 && (!p_draft || !draft || !u_accept)) return W4A16_EINVAL;
+  if (workspace_bytes < w4a16::spec_verify_workspace_bytes((int)B, (int)V)) return W4A16_EINVAL;
+  auto al4 = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; };
+  if (!al4(p_target) || !al4(u_sample) || !al4(n_accepted) || !al4(token) ||
+      (K > 0 && (!al4(p_draft) || !al4(draft) || !al4(u_accept))) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return W4A16_EALIGN;
+  return w4a16::launch_spec_verify(
+             static_cast<const float *>(p_target), static_cast<const float *>(p_draft),
+             static_cast<const int32_t *>(draft), static_cast<const float *>(u_accept),
+             static_cast<const float *>(u_sample), (int)B, (int)K, (int)V, workspace,
+             static_cast<int32_t *>(n_accepted), static_cast<int32_t *>(token),
+             static_cast<hipStream_t>(stream)) == hipSuccess
+             ? W4A16_OK
+             : W4A16_EHIP;
+}
+
 int w4a16_gemm(const void *X, const void *Wq, const void *scales, const void *zeros,
                const void *s, void *Y, int64_t M, int64_t N, int64_t K, void *stream) {
   return w4a16_gemm_path(X, Wq, scales, zeros, s, Y, M, N, K, W4A16_PATH_AUTO, stream);

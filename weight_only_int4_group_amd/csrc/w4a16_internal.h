@@ -43,4 +43,15 @@ hipError_t launch_tiled_set(const GemmDesc *problems, int count, void *workspace
 hipError_t launch_tiled(const void *X, const void *Wq, const void *scales, const void *zeros,
                         const void *s, void *Y, int M, int N, int K, hipStream_t stream);
 
+// Speculative-sampling verification of B sequences (validated by the caller):
+// the vocabulary is cut into spec_verify_chunks(V) chunks, and the workspace
+// (spec_verify_workspace_bytes(B, V) bytes, 256-byte aligned) holds the
+// per-chunk sums and the first rejection of every sequence.
+int spec_verify_chunks(int V);
+size_t spec_verify_workspace_bytes(int B, int V);
+hipError_t launch_spec_verify(const float *p_target, const float *p_draft, const int32_t *draft,
+                              const float *u_accept, const float *u_sample, int B, int K, int V,
+                              void *workspace, int32_t *n_accepted, int32_t *token,
+                              hipStream_t stream);
+
 }  // namespace w4a16
