@@ -21,7 +21,9 @@ Sources (web pages; cited by page, section and table/equation):
     kernel; the AWQ equation W_hat = quant(W / s) * s with s the per-channel
     activation magnitude; weights can be quantized offline.
   * [mhpq] mhpq.cn news 1188791, practitioner notes.  Section 2.1: a 1024x1024
-    weight matrix in INT4 takes a quarter of its FP16 size.
+    weight matrix in INT4 takes a quarter of its FP16 size.  Section 2.2: the
+    top 0.1% of the weights by magnitude go to an FP16 sub-tensor, merged with
+    the INT4 rest by a where(mask, ...).
 
 Readings taken where the pages are silent (each one is listed with its reason
 in the design notes of the repository):
@@ -39,6 +41,9 @@ The symmetric variant (``quantize_symmetric``, the signed -7..7 grid of [mhpq]
 sec.2.1) takes R2, R5, R7's ties, R8 and R9's errors as they are, with
 scale = max|W'| / 7 rounded up, signed codes rint(W' / scale) stored + 8 and a
 constant zero point 8 (an all-zero group: scale 0, codes 8).
+The outlier side path (``outliers``, [mhpq] sec.2.2) keeps the largest |W / s|
+in fp16 and quantizes the rest with those positions set to 0; its readings
+O1-O5 are in that module.
 Pins: every function here is checked by tests against facts the pages or the
 mathematics fix (bound, grid reconstruction, byte counts, brute force in exact
 rationals, integer special case); see tests/test_oracle_*.py.
@@ -48,12 +53,12 @@ from .quantizer import (GROUP, QMAX, SYM_QMAX, SYM_ZERO, NonFiniteInput, OracleE
 from .layout import (META_QUAD, TILE_BYTES, TILE_ROWS, meta_groups, meta_index, nibble_address,
                      pack_codes, pack_meta, unpack_codes, unpack_meta)
 from .matmul import dequantize, gemm
-from . import accounting, exact, spec
+from . import accounting, exact, outliers, spec
 
 __all__ = [
     "GROUP", "QMAX", "NonFiniteInput", "OracleError", "QuantResult", "ScaleOverflow",
     "quantize", "quantize_symmetric", "SYM_QMAX", "SYM_ZERO", "round_up_fp16", "META_QUAD", "TILE_BYTES", "TILE_ROWS", "meta_groups",
     "meta_index", "nibble_address",
     "pack_codes", "pack_meta", "unpack_codes", "unpack_meta", "dequantize", "gemm",
-    "accounting", "exact", "spec",
+    "accounting", "exact", "outliers", "spec",
 ]
