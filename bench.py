@@ -23,6 +23,9 @@ Printed JSON line:
   batched       the same 8B layer at speculative-verify batches M = 2, 5, 9 and a
                 Qwen2-7B-shaped layer at batched-decode M = 16, 64, 256, one grouped
                 call per step (streaming kernel for M <= 16, else the tiled GEMM);
+  outliers      the headline layer with each matrix's top 0.1% |W/s| kept in fp16
+                and added by the kernels (one grouped launch per step); the prefill
+                line carries the same variant of the 70B layer;
   spec_verify   the accept / reject / draw step after a K = 4 verify pass over the
                 Llama-3 vocabulary (V = 128256), for 1 and 64 sequences per call;
   prefill       the 70B-shaped layer at M = 4096 (compute-bound): TFLOP/s
@@ -111,9 +114,17 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def prepare_layer(cfg, M, torch, w4, workloads, copies_min_bytes=POOL_BYTES):
-    """Pack every matrix of a configuration once on the GPU, and replicate the packed
-    buffers into enough copies to cover `copies_min_bytes`."""
+def outlier_bytes(pw):
+    """Bytes of a packed weight's fp16 outliers: row pointers, columns and values."""
+    if pw.o_row_ptr is None:
+        return 0
+    return 4 * pw.o_row_ptr.numel() + 6 * pw.o_col.numel()
+
+
+def prepare_layer(cfg, M, torch, w4, workloads, copies_min_bytes=POOL_BYTES, outliers=False):
+    """Pack every matrix of a configuration once on the GPU (with the 0.1% fp16 outliers
+    when asked), and replicate the packed buffers into enough copies to cover
+    `copies_min_bytes`."""
     mats = []
     for mi, mat in enumerate(cfg.matrices):
         W = workloads.weights(cfg.weight_key, mi, mat.N, mat.K, threads=16)
@@ -121,20 +132,25 @@ def prepare_layer(cfg, M, torch, w4, workloads, copies_min_bytes=POOL_BYTES):
         Wd = torch.from_numpy(W).to("cuda")
         sd = None if s is None else torch.from_numpy(s).to("cuda")
         del W
-        pw = w4.w4a16_quantize_pack(Wd, sd)
+        pw = w4.w4a16_quantize_pack_outliers(Wd, sd) if outliers else w4.w4a16_quantize_pack(Wd, sd)
         del Wd
         X = torch.from_numpy(workloads.activations(cfg.weight_key, mi, M, mat.K,
                                                    outliers=cfg.act_outliers)).to("cuda")
         Y = torch.empty((M, mat.N), dtype=torch.float16, device="cuda")
         mats.append(dict(name=mat.name, N=mat.N, K=mat.K, pw=pw, s=sd, X=X, Y=Y,
-                         bytes=alg_bytes(M, mat.N, mat.K, sd is not None),
+                         bytes=alg_bytes(M, mat.N, mat.K, sd is not None) + outlier_bytes(pw),
                          flops=2 * M * mat.N * mat.K))
-    layer_w = sum(m["pw"].wq.numel() + 4 * m["pw"].scales.numel() for m in mats)
+    layer_w = sum(m["pw"].wq.numel() + 4 * m["pw"].scales.numel() + outlier_bytes(m["pw"])
+                  for m in mats)
     copies = max(1, -(-copies_min_bytes // layer_w))
     pool = [[m["pw"]] for m in mats] if copies == 1 else None
     if copies > 1:
+        def clone(t):
+            return None if t is None else t.clone()
         pool = [[w4.PackedWeight(m["pw"].wq.clone(), m["pw"].scales.clone(),
-                                 m["pw"].zeros.clone(), m["N"], m["K"]) for _ in range(copies)]
+                                 m["pw"].zeros.clone(), m["N"], m["K"], clone(m["pw"].o_row_ptr),
+                                 clone(m["pw"].o_col), clone(m["pw"].o_val))
+                 for _ in range(copies)]
                 for m in mats]
     torch.cuda.synchronize()
     return mats, pool, layer_w, copies
@@ -340,6 +356,7 @@ def main():
     ap.add_argument("--no-batched", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true")
     ap.add_argument("--no-spec", action="store_true")
+    ap.add_argument("--no-outliers", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-run", action="store_true",
                     help="only the short fixed sequence used for counter collection")
@@ -418,6 +435,26 @@ def main():
         del pool, mats
     torch.cuda.empty_cache()
 
+    if not args.no_outliers:
+        log(f"preparing {cfg.name} with fp16 outliers")
+        omats, opool, ow, oc = prepare_layer(cfg, M, torch, w4, workloads, outliers=True)
+        ob = sum(m["bytes"] for m in omats)
+        owall, olms = timed(make_calls(omats, opool, oc, one, w4, torch), args.steps // 2,
+                            args.warmup, torch)
+        okern = float(np.mean(olms[0])) * 1e-3
+        out["outliers"] = {
+            "workload": f"{cfg.name} with fp16 outliers: the same 7 matrices, M={M}, each with "
+                        "its top 0.1% |W/s| kept in fp16 (row-compressed) and added in the "
+                        "epilogue, one grouped launch per step",
+            "kept": int(sum(m["pw"].o_col.numel() for m in omats)),
+            "step_bytes": ob, "outlier_bytes": int(sum(outlier_bytes(m["pw"]) for m in omats)),
+            "us_per_step": round(owall / (args.steps // 2) * 1e6, 2),
+            "kernel_us_per_step": round(okern * 1e6, 2),
+            "kernel_TB/s": round(ob / okern / 1e12, 4),
+            "vs_plain_kernel_time": round(okern / (avg_ms * 1e-3), 4)}
+        del opool, omats
+        torch.cuda.empty_cache()
+
     if not args.no_spec:
         log("timing speculative verification")
         out["spec_verify"] = [spec_verify_line(torch, w4, B, 4, 128256) for B in (1, 64)]
@@ -449,6 +486,20 @@ def main():
         }
         del ppool, pmats
         torch.cuda.empty_cache()
+        if not args.no_outliers:
+            log(f"preparing {pcfg.name} M={PM} with fp16 outliers")
+            omats, opool, _, opc = prepare_layer(pcfg, PM, torch, w4, workloads,
+                                                 copies_min_bytes=0, outliers=True)
+            _, oms = timed(make_calls(omats, opool, opc, groups, w4, torch), args.prefill_steps, 2,
+                           torch, per=1)
+            otot = sum(float(np.mean(x)) for x in oms)
+            out["prefill"]["outliers"] = {
+                "workload": "the same layer with each matrix's top 0.1% |W/s| kept in fp16",
+                "kernel_ms_per_step": round(otot, 4),
+                "TFLOP/s": round(flops / (otot * 1e-3) / 1e12, 2),
+                "vs_plain_kernel_time": round(otot / tot_ms, 4)}
+            del opool, omats
+            torch.cuda.empty_cache()
 
     if not args.no_ceilings:
         log("measuring the copy and dense fp16 GEMM ceilings")

@@ -128,6 +128,34 @@ enum {
 int w4a16_quantize_pack_mode(const void *W, const void *s, int64_t N, int64_t K, int mode,
                              void *Wq, void *scales, void *zeros, void *stream);
 
+/* FP16 outlier side path (the practitioner notes at mhpq.cn, section 2.2,
+ * outlier handling: the top 0.1% of the weights by magnitude stay in FP16,
+ * the rest go to INT4, merged as where(mask, fp16, int4)).
+ * Keeps exactly `count` weights of W in fp16 -- the largest |W[n][k] / s[k]|
+ * (|W| when s is NULL; one correctly rounded fp64 division, so the ranking is
+ * exact), ties to the lower flat index n * K + k -- and quantizes and packs
+ * the rest exactly as w4a16_quantize_pack_mode would with the kept weights
+ * replaced by 0: they leave their groups' ranges and their codes decode to
+ * exactly 0.  The kept weights are written row-compressed:
+ *   o_row_ptr int32 [N + 1] (o_row_ptr[0] = 0, o_row_ptr[N] = count),
+ *   o_col int32 [count] and o_val fp16 [count]: the columns (increasing
+ *   within a row) and the original fp16 values of row n at
+ *   o_row_ptr[n] .. o_row_ptr[n + 1] - 1.
+ * The page's share is count = round(0.001 * N * K).  0 <= count <= N * K and
+ * count < 2^31 (EINVAL); o_col and o_val may be NULL when count = 0.
+ * workspace: caller-owned device memory of w4a16_outlier_workspace_size()
+ * bytes (EINVAL if smaller), 256-byte aligned; contents on entry do not
+ * matter.  Alignment (EALIGN): W, Wq, scales, zeros, s 16 bytes, o_row_ptr
+ * and o_col 4, o_val 2.  Blocks until done; errors as w4a16_quantize_pack
+ * (ENONFINITE also for a non-finite kept weight).  The packed buffers feed
+ * the GEMM entry points together with the three outlier arrays
+ * (w4a16_problem's o_row_ptr, o_col, o_val). */
+int w4a16_outlier_workspace_size(int64_t N, int64_t K, size_t *bytes);
+int w4a16_quantize_pack_outliers(const void *W, const void *s, int64_t N, int64_t K, int mode,
+                                 int64_t count, void *Wq, void *scales, void *zeros,
+                                 void *o_row_ptr, void *o_col, void *o_val, void *workspace,
+                                 size_t workspace_bytes, void *stream);
+
 /* Y[M][N] = X[M][K] . W_hat^T with W_hat[n][k] = (q - z) * scale * s[k].
  * X: fp16 [M][K]; Wq/scales/zeros: packed as above; s: fp16 [K] or NULL;
  * Y: fp16 [M][N] row-major, fully overwritten.  fp32 accumulation; X * s is
@@ -150,6 +178,15 @@ typedef struct w4a16_problem {
   const void *s;
   void *Y;
   int64_t M, N, K;
+  /* Optional fp16 outliers (w4a16_quantize_pack_outliers), all NULL or all
+   * set: W_hat[n][k] = o_val[e] where o_col[e] = k for some e in
+   * o_row_ptr[n] .. o_row_ptr[n + 1] - 1 (the codes there decode to 0), so
+   * Y = X . W_hat^T gains X[m][k] * o_val[e] per kept weight, summed in fp32
+   * in stored order into the output before its rounding.  o_row_ptr int32
+   * [N + 1] and o_col int32 4-byte aligned, o_val fp16 2-byte aligned. */
+  const void *o_row_ptr;
+  const void *o_col;
+  const void *o_val;
 } w4a16_problem;
 
 /* Several independent dequantize-matmuls, each the operation w4a16_gemm

@@ -31,14 +31,12 @@ from dataclasses import dataclass
 
 import numpy as np
 
-from .quantizer import QuantResult, quantize, quantize_symmetric
-
-PAGE_SHARE = 0.001   # top 0.1% (mhpq.cn sec.2.2)
+from .quantizer import NonFiniteInput, QuantResult, quantize, quantize_symmetric
 
 
 def page_count(N: int, K: int) -> int:
-    """The page's 0.1% share of an N x K matrix, rounded to the nearest integer (O2)."""
-    return int(np.floor(PAGE_SHARE * N * K + 0.5))
+    """The page's 0.1% share of an N x K matrix, N*K/1000 rounded half up (O2)."""
+    return (N * K + 500) // 1000
 
 
 def ranking_keys(W: np.ndarray, s: np.ndarray | None) -> np.ndarray:
@@ -74,6 +72,8 @@ def quantize_with_outliers(W: np.ndarray, s: np.ndarray | None, count: int,
                            symmetric: bool = False) -> OutlierResult:
     """Split W into `count` fp16 outliers and an INT4 remainder (O1-O5)."""
     W = np.asarray(W)
+    if not np.all(np.isfinite(W.astype(np.float64))):
+        raise NonFiniteInput("non-finite W (kept weights included)")   # R9
     mask = select(W, s, count)
     rest = np.where(mask, np.float16(0), W).astype(np.float16)        # O4
     quant = (quantize_symmetric if symmetric else quantize)(rest, s)

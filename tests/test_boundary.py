@@ -223,3 +223,48 @@ def test_spec_verify_validation():
     assert call(ws=V((1 << 24) + 128)) == -2
     # with K = 0 the draft buffers are not read and may be NULL (or misaligned)
     assert call(K=0, pd=None, dr=None, ua=None, pt=ODD1) == -2
+
+
+def test_outlier_pack_validation():
+    L = w4.lib()
+    A4 = V((1 << 20) + 4)
+    WS = V(1 << 24)
+    need = w4.w4a16_outlier_workspace_size(32, 256)
+    assert need >= 32 * 256 // 8
+
+    def call(W=A16, s=None, N=32, K=256, mode=0, count=8, wq=A16, sc=A16, z=A16, rp=A4, col=A4,
+             val=A4, ws=WS, wsb=need):
+        return L.w4a16_quantize_pack_outliers(W, s, N, K, mode, count, wq, sc, z, rp, col, val,
+                                              ws, wsb, None)
+
+    assert call(mode=5) == -3
+    assert call(N=8) == -1 and call(K=100) == -1          # shapes as the plain packer
+    assert call(count=-1) == -1 and call(count=32 * 256 + 1) == -1
+    assert call(wsb=need - 1) == -1
+    for name in ("W", "wq", "sc", "z", "rp", "ws"):
+        assert call(**{name: None}) == -1, name
+    assert call(col=None) == -1 and call(val=None) == -1
+    assert call(W=ODD) == -2 and call(rp=V((1 << 20) + 2)) == -2
+    assert call(col=V((1 << 20) + 2)) == -2 and call(val=V((1 << 20) + 1)) == -2
+    assert call(ws=V((1 << 24) + 128)) == -2
+    with pytest.raises(w4.W4A16Error):
+        w4.w4a16_outlier_workspace_size(30, 256)
+    assert w4.page_outlier_count(4096, 4096) == 16777
+
+
+def test_grouped_outlier_fields_validation():
+    L = w4.lib()
+    A4 = V((1 << 20) + 4)
+
+    def prob(**kw):
+        p = w4.Problem(A16, A16, A16, A16, None, A16, 1, 32, 256)
+        for k, v in kw.items():
+            setattr(p, k, v.value if isinstance(v, ctypes.c_void_p) else v)
+        return p
+
+    arr = (w4.Problem * 1)(prob(o_row_ptr=A4))            # only one of three set
+    assert L.w4a16_gemm_grouped(arr, 1, None) == -1
+    arr = (w4.Problem * 1)(prob(o_row_ptr=V((1 << 20) + 2), o_col=A4, o_val=A4))
+    assert L.w4a16_gemm_grouped(arr, 1, None) == -2
+    arr = (w4.Problem * 1)(prob(o_row_ptr=A4, o_col=A4, o_val=V((1 << 20) + 1)))
+    assert L.w4a16_gemm_grouped(arr, 1, None) == -2

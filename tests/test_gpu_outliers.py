@@ -1,0 +1,173 @@
+"""FP16 outlier side path on the GPU against the oracle (mhpq.cn notes sec.2.2).
+
+Selection, row-compressed outliers and the packed INT4 rest must be bit-exact;
+products with the merged weight are within the float tolerance of the fp64 oracle
+on every kernel (streaming whole-row, streaming windowed, tiled, tiled split-K).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import weight_only_int4_group_amd as w4
+from oracle import outliers as ol
+from tests.gpu_helpers import assert_close, errors, h16_bits, note, to_dev, to_host, torch_cuda
+from workloads import activations, awq_scales, weights
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_pack(W, s, count, mode=w4.QUANT_ASYM):
+    torch_cuda()
+    return w4.w4a16_quantize_pack_outliers(to_dev(W), None if s is None else to_dev(s), count,
+                                           mode)
+
+
+def check_pack(W, s, count, tag, mode=w4.QUANT_ASYM):
+    note(f"outlier pack {tag} N={W.shape[0]} K={W.shape[1]} count={count} mode={mode}")
+    pw = gpu_pack(W, s, count, mode)
+    ref = ol.quantize_with_outliers(W, s, count, symmetric=mode == w4.QUANT_SYM)
+    assert np.array_equal(to_host(pw.o_row_ptr), ref.row_ptr), tag
+    assert np.array_equal(to_host(pw.o_col), ref.col), tag
+    assert np.array_equal(h16_bits(to_host(pw.o_val)), h16_bits(ref.val)), tag
+    assert np.array_equal(to_host(pw.wq), oracle.pack_codes(ref.quant.q)), tag
+    assert np.array_equal(h16_bits(to_host(pw.scales)), h16_bits(oracle.pack_meta(ref.quant.scales)))
+    assert np.array_equal(h16_bits(to_host(pw.zeros)), h16_bits(oracle.pack_meta(ref.quant.zeros)))
+    return pw, ref
+
+
+@pytest.mark.parametrize("mode", [w4.QUANT_ASYM, w4.QUANT_SYM])
+@pytest.mark.parametrize("N,K,awq", [(16, 128, False), (48, 384, True), (272, 640, True),
+                                     (1024, 1024, False)])
+def test_pack_matches_oracle(N, K, awq, mode):
+    W = weights(3, 1, N, K)
+    s = awq_scales(3, 1, K) if awq else None
+    for count in (0, 1, ol.page_count(N, K), 37 * N):
+        check_pack(W, s, min(count, N * K), f"{N}x{K} count={count}", mode)
+
+
+def test_pack_ties_and_extremes():
+    rng = np.random.default_rng(17)
+    N, K = 64, 512
+    # a handful of distinct magnitudes: the threshold falls inside a long run of ties
+    W = rng.choice(np.array([-0.5, -0.25, -0.125, 0.0, 0.125, 0.25, 0.5], np.float16),
+                   size=(N, K))
+    for count in (1, 100, 4000, 9000, N * K - 1, N * K):
+        check_pack(W, None, count, f"ties count={count}")
+    s = np.full(K, np.float16(2.0))
+    check_pack(W, s, 5000, "ties with a constant s")
+    Z = np.zeros((N, K), np.float16)              # every key ties at 0
+    check_pack(Z, None, 777, "all zero")
+    Wn = W.copy()
+    Wn[3, 5] = np.float16(-0.0)
+    Wn[7, 9] = np.float16(6e-8)                    # subnormal
+    Wn[9, 100] = np.float16(60000.0)
+    check_pack(Wn, None, 3, "extremes")
+
+
+def test_pack_full_size_q_proj():
+    """An 8B q projection (4096 x 4096, AWQ s, planted outliers) with the page's 0.1%."""
+    W = weights(1, 0, 4096, 4096)
+    s = awq_scales(1, 0, 4096)
+    pw, ref = check_pack(W, s, ol.page_count(4096, 4096), "q_proj 4096x4096")
+    # the planted large weights (x10) are what the selection picks, mostly
+    assert ref.mask.sum() == 16777
+
+
+def test_pack_errors_report_like_the_plain_packer():
+    torch = torch_cuda()
+    W = weights(3, 2, 32, 256).copy()
+    W[4, 7] = np.float16(np.inf)                    # kept (largest) but not finite
+    with pytest.raises(w4.W4A16Error) as e:
+        w4.w4a16_quantize_pack_outliers(to_dev(W), None, 10)
+    assert e.value.status == -4
+    assert torch is not None
+
+
+def _case(N, K, awq, key, M, count=None):
+    W = weights(key, 0, N, K)
+    s = awq_scales(key, 0, K) if awq else None
+    X = activations(key, 0, M, K)
+    count = ol.page_count(N, K) if count is None else count
+    return W, s, X, count
+
+
+@pytest.mark.parametrize("M,N,K,awq", [
+    (1, 4096, 4096, True),      # streaming, whole-row X * s
+    (5, 1040, 3584, True),      # streaming, ragged N
+    (16, 2048, 14336, False),   # streaming, K windows (X * s does not fit in LDS)
+    (17, 1024, 2048, True),     # tiled, ragged M
+    (64, 4096, 4096, True),     # tiled, split K
+    (300, 1296, 1536, False),   # tiled, ragged M and N
+])
+def test_gemm_with_outliers_matches_oracle(M, N, K, awq):
+    torch_cuda()
+    W, s, X, count = _case(N, K, awq, 4, M)
+    note(f"outlier gemm M={M} N={N} K={K} awq={awq} count={count}")
+    pw = gpu_pack(W, s, count)
+    Y = to_host(w4.w4a16_gemm(to_dev(X), pw, None if s is None else to_dev(s)))
+    ref = ol.quantize_with_outliers(W, s, count)
+    assert_close(Y, ol.gemm(X, ref, W, s), f"M={M} N={N} K={K}")
+
+
+def test_outliers_reduce_the_error_against_the_fp16_weights():
+    """The point of the side path: with the planted large weights kept in fp16, the
+    product is closer to X . W^T than with every weight in INT4."""
+    torch_cuda()
+    N, K, M = 4096, 4096, 4
+    W, s, X, count = _case(N, K, True, 5, M)
+    exact = X.astype(np.float64) @ W.astype(np.float64).T
+    plain = w4.w4a16_quantize_pack(to_dev(W), to_dev(s))
+    with_o = gpu_pack(W, s, count)
+    e_plain = errors(to_host(w4.w4a16_gemm(to_dev(X), plain, to_dev(s))), exact)[0]
+    e_out = errors(to_host(w4.w4a16_gemm(to_dev(X), with_o, to_dev(s))), exact)[0]
+    note(f"rel-L2 vs X.W^T: plain {e_plain:.4e}, with outliers {e_out:.4e}")
+    assert e_out < e_plain     # measured 0.203 vs 0.232 on this input
+
+
+def test_grouped_mixes_problems_with_and_without_outliers():
+    torch = torch_cuda()
+    shapes = [(1024, 4096, True), (512, 2048, False), (1024, 4096, False)]
+    for M in (1, 9, 40):
+        items, refs = [], []
+        for i, (N, K, awq) in enumerate(shapes):
+            W, s, X, count = _case(N, K, awq, 10 + i, M)
+            pw = gpu_pack(W, s, count) if i != 1 else w4.w4a16_quantize_pack(to_dev(W),
+                                                                             None if s is None else to_dev(s))
+            Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+            items.append((to_dev(X), pw, None if s is None else to_dev(s), Y))
+            if i != 1:
+                refs.append(ol.gemm(X, ol.quantize_with_outliers(W, s, count), W, s))
+            else:
+                q = oracle.quantize(W, s)
+                refs.append(oracle.gemm(X, q.q, q.scales, q.zeros, s))
+        note(f"grouped outliers M={M}")
+        w4.GroupedCall(items)()
+        for (_, _, _, Y), ref in zip(items, refs):
+            assert_close(to_host(Y), ref, f"grouped M={M}")
+
+
+@pytest.mark.parametrize("M", [1, 20, 64, 300])
+def test_many_outliers_in_one_group(M):
+    """Rows with several kept weights inside one 128-column group (first, middle and last
+    group, and at split-K range edges): every one of them is applied exactly once."""
+    torch_cuda()
+    N, K = 512, 4096
+    W = weights(6, 0, N, K).copy()
+    s = awq_scales(6, 0, K)
+    big = np.float16(4.0)
+    W[3, 0:6] = big                       # six in the first group
+    W[17, 130:135] = -big                 # five in group 1
+    W[40, 2048 - 3:2048 + 3] = big        # straddling a group boundary
+    W[200, K - 7:K] = big                 # seven in the last group
+    W[511, 1024:1024 + 128:16] = -big     # eight spread over one group
+    W[256, 128 * 7 - 1] = big             # the last column of group 6
+    for g in range(32):                   # one row with an entry in every group
+        W[300, 128 * g + 5] = big
+    X = activations(6, 0, M, K)
+    count = 200
+    note(f"outliers in one group M={M}")
+    pw = gpu_pack(W, s, count)
+    ref = ol.quantize_with_outliers(W, s, count)
+    assert ref.mask[3, 0:6].all() and ref.mask[200, K - 7:K].all() and ref.mask[300].sum() >= 32
+    Y = to_host(w4.w4a16_gemm(to_dev(X), pw, to_dev(s)))
+    assert_close(Y, ol.gemm(X, ref, W, s), f"M={M}")

@@ -24,7 +24,8 @@ __all__ = [
     "w4a16_packed_sizes", "w4a16_quantize_pack", "w4a16_gemm", "w4a16_gemm_path",
     "w4a16_select_path", "w4a16_strerror", "w4a16_version", "EXPORTED_SYMBOLS",
     "w4a16_gemm_grouped", "GroupedCall", "w4a16_spec_verify",
-    "w4a16_spec_verify_workspace_size", "SpecVerifyCall",
+    "w4a16_spec_verify_workspace_size", "SpecVerifyCall", "w4a16_quantize_pack_outliers",
+    "w4a16_outlier_workspace_size", "page_outlier_count",
 ]
 
 GROUP = 128
@@ -35,7 +36,8 @@ STATUS = {0: "W4A16_OK", -1: "W4A16_EINVAL", -2: "W4A16_EALIGN", -3: "W4A16_EUNS
 EXPORTED_SYMBOLS = ("w4a16_packed_sizes", "w4a16_quantize_pack", "w4a16_quantize_pack_mode",
                     "w4a16_gemm",
                     "w4a16_gemm_path", "w4a16_gemm_grouped", "w4a16_gemm_grouped_ws",
-                    "w4a16_gemm_workspace_size", "w4a16_spec_verify",
+                    "w4a16_gemm_workspace_size", "w4a16_outlier_workspace_size",
+                    "w4a16_quantize_pack_outliers", "w4a16_spec_verify",
                     "w4a16_spec_verify_workspace_size", "w4a16_select_path",
                     "w4a16_strerror", "w4a16_version")
 
@@ -44,7 +46,9 @@ class Problem(ctypes.Structure):
     """Mirror of the C struct w4a16_problem."""
     _fields_ = [("X", ctypes.c_void_p), ("Wq", ctypes.c_void_p), ("scales", ctypes.c_void_p),
                 ("zeros", ctypes.c_void_p), ("s", ctypes.c_void_p), ("Y", ctypes.c_void_p),
-                ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64)]
+                ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("o_row_ptr", ctypes.c_void_p), ("o_col", ctypes.c_void_p),
+                ("o_val", ctypes.c_void_p)]
 
 
 class W4A16Error(RuntimeError):
@@ -78,6 +82,9 @@ def lib() -> ctypes.CDLL:
     L.w4a16_spec_verify.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp, ctypes.c_size_t, vp,
                                     vp, vp]
     L.w4a16_spec_verify_workspace_size.argtypes = [i64, i64, i64, ctypes.POINTER(ctypes.c_size_t)]
+    L.w4a16_outlier_workspace_size.argtypes = [i64, i64, sz]
+    L.w4a16_quantize_pack_outliers.argtypes = [vp, vp, i64, i64, ctypes.c_int, i64, vp, vp, vp,
+                                               vp, vp, vp, vp, ctypes.c_size_t, vp]
     L.w4a16_select_path.argtypes = [i64, i64, i64]
     L.w4a16_strerror.argtypes = [ctypes.c_int]
     L.w4a16_strerror.restype = ctypes.c_char_p
@@ -86,6 +93,7 @@ def lib() -> ctypes.CDLL:
                  "w4a16_gemm", "w4a16_gemm_path",
                  "w4a16_gemm_grouped", "w4a16_gemm_grouped_ws", "w4a16_gemm_workspace_size",
                  "w4a16_spec_verify", "w4a16_spec_verify_workspace_size", "w4a16_select_path",
+                 "w4a16_outlier_workspace_size", "w4a16_quantize_pack_outliers",
                  "w4a16_version"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
@@ -115,12 +123,26 @@ def w4a16_select_path(M: int, N: int, K: int) -> int:
 @dataclass
 class PackedWeight:
     """Packed INT4 weight: codes (uint8, N*K/2 bytes) and the fp16 scale and zero-point
-    buffers (flat, in the 4-group-quad layout of include/w4a16.h)."""
+    buffers (flat, in the 4-group-quad layout of include/w4a16.h); with fp16 outliers
+    (w4a16_quantize_pack_outliers) also their row pointers (int32 [N+1]), columns
+    (int32) and values (fp16)."""
     wq: "object"
     scales: "object"
     zeros: "object"
     N: int
     K: int
+    o_row_ptr: "object" = None
+    o_col: "object" = None
+    o_val: "object" = None
+
+    def outlier_ptrs(self):
+        """(row_ptr, col, val) device pointers, or three None without outliers."""
+        if self.o_row_ptr is None or self.o_col is None or self.o_col.numel() == 0:
+            return None, None, None
+        torch = _torch()
+        return (_dev_ptr(self.o_row_ptr, "o_row_ptr", torch.int32, self.N + 1),
+                _dev_ptr(self.o_col, "o_col", torch.int32),
+                _dev_ptr(self.o_val, "o_val", torch.float16, self.o_col.numel()))
 
 
 def _torch():
@@ -171,9 +193,58 @@ def w4a16_quantize_pack(W, s=None, out: PackedWeight | None = None,
     return out
 
 
-def w4a16_gemm_path(X, pw: PackedWeight, s=None, path: int = PATH_AUTO, out=None):
-    """Y[M][N] = X[M][K] . dequant(pw)^T (fp16), on the current stream, asynchronously."""
+def page_outlier_count(N: int, K: int) -> int:
+    """The 0.1% share of an N x K matrix kept in fp16 by the mhpq.cn notes (sec.2.2),
+    rounded to the nearest integer."""
+    return (N * K + 500) // 1000
+
+
+def w4a16_outlier_workspace_size(N: int, K: int) -> int:
+    n = ctypes.c_size_t()
+    rc = lib().w4a16_outlier_workspace_size(N, K, ctypes.byref(n))
+    if rc:
+        raise W4A16Error(rc, "w4a16_outlier_workspace_size")
+    return n.value
+
+
+def w4a16_quantize_pack_outliers(W, s=None, count: int | None = None,
+                                 mode: int = QUANT_ASYM) -> PackedWeight:
+    """Keep the `count` largest |W / s| of fp16 W[N][K] in fp16 (default: the 0.1% share)
+    and quantize the rest into a PackedWeight that carries the outliers."""
     torch = _torch()
+    if W.dim() != 2:
+        raise ValueError("W must be 2-D [N][K]")
+    N, K = W.shape
+    if count is None:
+        count = page_outlier_count(N, K)
+    wq_b, sc_b, z_b = w4a16_packed_sizes(N, K)
+    dev = W.device
+    pw = PackedWeight(torch.empty(wq_b, dtype=torch.uint8, device=dev),
+                      torch.empty(sc_b // 2, dtype=torch.float16, device=dev),
+                      torch.empty(z_b // 2, dtype=torch.float16, device=dev), N, K,
+                      torch.empty(N + 1, dtype=torch.int32, device=dev),
+                      torch.empty(max(count, 1), dtype=torch.int32, device=dev)[:count],
+                      torch.empty(max(count, 1), dtype=torch.float16, device=dev)[:count])
+    ws = torch.empty(w4a16_outlier_workspace_size(N, K), dtype=torch.uint8, device=dev)
+    rc = lib().w4a16_quantize_pack_outliers(
+        _dev_ptr(W, "W", torch.float16), _dev_ptr(s, "s", torch.float16, K), N, K, mode, count,
+        _dev_ptr(pw.wq, "wq", torch.uint8, wq_b),
+        _dev_ptr(pw.scales, "scales", torch.float16, sc_b // 2),
+        _dev_ptr(pw.zeros, "zeros", torch.float16, z_b // 2),
+        _dev_ptr(pw.o_row_ptr, "o_row_ptr", torch.int32, N + 1),
+        ctypes.c_void_p(pw.o_col.data_ptr()), ctypes.c_void_p(pw.o_val.data_ptr()),
+        _dev_ptr(ws, "workspace", torch.uint8), ws.numel(), _stream_handle(dev))
+    if rc:
+        raise W4A16Error(rc, "w4a16_quantize_pack_outliers")
+    return pw
+
+
+def w4a16_gemm_path(X, pw: PackedWeight, s=None, path: int = PATH_AUTO, out=None):
+    """Y[M][N] = X[M][K] . dequant(pw)^T (fp16), on the current stream, asynchronously.
+    (Without fp16 outliers: the forced-path entry point does not take them.)"""
+    torch = _torch()
+    if pw.outlier_ptrs()[0] is not None:
+        raise ValueError("w4a16_gemm_path takes no fp16 outliers; use w4a16_gemm")
     if X.dim() != 2 or X.shape[1] != pw.K:
         raise ValueError("X must be [M][K] with K matching the packed weight")
     M = X.shape[0]
@@ -225,7 +296,7 @@ class GroupedCall:
                 _dev_ptr(X, "X", torch.float16), _dev_ptr(pw.wq, "wq", torch.uint8),
                 _dev_ptr(pw.scales, "scales", torch.float16),
                 _dev_ptr(pw.zeros, "zeros", torch.float16), _dev_ptr(s, "s", torch.float16, pw.K),
-                _dev_ptr(Y, "Y", torch.float16), X.shape[0], pw.N, pw.K)
+                _dev_ptr(Y, "Y", torch.float16), X.shape[0], pw.N, pw.K, *pw.outlier_ptrs())
         self.device = self.items[0][0].device if self.items else None
         self.ws, self.ws_ptr, self.ws_bytes = None, None, 0
         if workspace and self.items:

@@ -13,7 +13,7 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_NAME = "libw4a16.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = ("api.hip", "pack.hip", "skinny.hip", "tiled.hip", "spec.hip")
+SOURCES = ("api.hip", "pack.hip", "skinny.hip", "tiled.hip", "spec.hip", "outliers.hip")
 ARCH = "gfx950"
 
 

@@ -74,6 +74,22 @@ int w4a16_packed_sizes(int64_t N, int64_t K, size_t *wq_bytes, size_t *scales_by
   return W4A16_OK;
 }
 
+static int pack_and_check(const void *W, const void *s, int64_t N, int64_t K,
+                          const uint8_t *keep, int mode, void *Wq, void *scales, void *zeros,
+                          unsigned *status, hipStream_t st) {
+  if (hipMemsetAsync(status, 0, sizeof(unsigned), st) != hipSuccess) return W4A16_EHIP;
+  if (w4a16::launch_pack(W, s, (int)N, (int)K, keep, Wq, scales, zeros, status,
+                         mode == W4A16_QUANT_SYM, st) != hipSuccess)
+    return W4A16_EHIP;
+  unsigned host = 0;
+  if (hipMemcpyAsync(&host, status, sizeof(unsigned), hipMemcpyDeviceToHost, st) != hipSuccess)
+    return W4A16_EHIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return W4A16_EHIP;
+  if (host & w4a16::kPackNonFinite) return W4A16_ENONFINITE;
+  if (host & w4a16::kPackRange) return W4A16_ERANGE;
+  return W4A16_OK;
+}
+
 int w4a16_quantize_pack_mode(const void *W, const void *s, int64_t N, int64_t K, int mode,
                              void *Wq, void *scales, void *zeros, void *stream) {
   if (mode != W4A16_QUANT_ASYM && mode != W4A16_QUANT_SYM) return W4A16_EUNSUPPORTED;
@@ -86,17 +102,42 @@ int w4a16_quantize_pack_mode(const void *W, const void *s, int64_t N, int64_t K,
   unsigned *status = nullptr;
   if ((rc = status_word(&status))) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (hipMemsetAsync(status, 0, sizeof(unsigned), st) != hipSuccess) return W4A16_EHIP;
-  if (w4a16::launch_pack(W, s, (int)N, (int)K, Wq, scales, zeros, status,
-                         mode == W4A16_QUANT_SYM, st) != hipSuccess)
-    return W4A16_EHIP;
-  unsigned host = 0;
-  if (hipMemcpyAsync(&host, status, sizeof(unsigned), hipMemcpyDeviceToHost, st) != hipSuccess)
-    return W4A16_EHIP;
-  if (hipStreamSynchronize(st) != hipSuccess) return W4A16_EHIP;
-  if (host & w4a16::kPackNonFinite) return W4A16_ENONFINITE;
-  if (host & w4a16::kPackRange) return W4A16_ERANGE;
+  return pack_and_check(W, s, N, K, nullptr, mode, Wq, scales, zeros, status, st);
+}
+
+int w4a16_outlier_workspace_size(int64_t N, int64_t K, size_t *bytes) {
+  if (!bytes) return W4A16_EINVAL;
+  const int rc = check_shape(N, K);
+  if (rc) return rc;
+  *bytes = w4a16::outlier_workspace_bytes((int)N, (int)K);
   return W4A16_OK;
+}
+
+int w4a16_quantize_pack_outliers(const void *W, const void *s, int64_t N, int64_t K, int mode,
+                                 int64_t count, void *Wq, void *scales, void *zeros,
+                                 void *o_row_ptr, void *o_col, void *o_val, void *workspace,
+                                 size_t workspace_bytes, void *stream) {
+  if (mode != W4A16_QUANT_ASYM && mode != W4A16_QUANT_SYM) return W4A16_EUNSUPPORTED;
+  int rc = check_shape(N, K);
+  if (rc) return rc;
+  if (count < 0 || count > N * K || count > INT32_MAX) return W4A16_EINVAL;
+  if (!W || !Wq || !scales || !zeros || !o_row_ptr || !workspace) return W4A16_EINVAL;
+  if (count > 0 && (!o_col || !o_val)) return W4A16_EINVAL;
+  if (workspace_bytes < w4a16::outlier_workspace_bytes((int)N, (int)K)) return W4A16_EINVAL;
+  auto aligned = [](const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; };
+  if (!aligned16(W) || !aligned16(Wq) || !aligned16(scales) || !aligned16(zeros) ||
+      (s && !aligned16(s)) || !aligned(o_row_ptr, 4) || !aligned(o_col, 4) || !aligned(o_val, 2) ||
+      !aligned(workspace, 256))
+    return W4A16_EALIGN;
+  unsigned *status = nullptr;
+  if ((rc = status_word(&status))) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const uint8_t *keep = nullptr;
+  if (w4a16::select_outliers(W, s, (int)N, (int)K, count, static_cast<int32_t *>(o_row_ptr),
+                             static_cast<int32_t *>(o_col), static_cast<_Float16 *>(o_val),
+                             workspace, &keep, st) != 0)
+    return W4A16_EHIP;
+  return pack_and_check(W, s, N, K, keep, mode, Wq, scales, zeros, status, st);
 }
 
 int w4a16_quantize_pack(const void *W, const void *s, int64_t N, int64_t K, void *Wq,
@@ -132,7 +173,8 @@ void skinny_pieces(const w4a16_problem &p, std::vector<w4a16::GemmDesc> &out) {
   for (int64_t m0 = 0; m0 < p.M; m0 += kSkinnyMaxM) {
     const int64_t mb = (p.M - m0) < kSkinnyMaxM ? (p.M - m0) : kSkinnyMaxM;
     out.push_back({static_cast<const _Float16 *>(p.X) + m0 * p.K, p.Wq, p.scales, p.zeros, p.s,
-                   static_cast<_Float16 *>(p.Y) + m0 * p.N, (int)mb, (int)p.N, (int)p.K});
+                   static_cast<_Float16 *>(p.Y) + m0 * p.N, (int)mb, (int)p.N, (int)p.K,
+                   p.o_row_ptr, p.o_col, p.o_val});
   }
 }
 
@@ -182,12 +224,19 @@ int check_problems(const w4a16_problem *problems, int count) {
     const w4a16_problem &p = problems[i];
     const int rc = check_gemm(p.X, p.Wq, p.scales, p.zeros, p.s, p.Y, p.M, p.N, p.K);
     if (rc) return rc;
+    const bool any = p.o_row_ptr || p.o_col || p.o_val;
+    if (any && !(p.o_row_ptr && p.o_col && p.o_val)) return W4A16_EINVAL;  // all or none
+    if (any && ((reinterpret_cast<uintptr_t>(p.o_row_ptr) & 3u) ||
+                (reinterpret_cast<uintptr_t>(p.o_col) & 3u) ||
+                (reinterpret_cast<uintptr_t>(p.o_val) & 1u)))
+      return W4A16_EALIGN;
   }
   return W4A16_OK;
 }
 
 w4a16::GemmDesc desc_of(const w4a16_problem &p) {
-  return {p.X, p.Wq, p.scales, p.zeros, p.s, p.Y, (int)p.M, (int)p.N, (int)p.K};
+  return {p.X,      p.Wq,     p.scales,      p.zeros, p.s,    p.Y, (int)p.M, (int)p.N,
+          (int)p.K, p.o_row_ptr, p.o_col, p.o_val};
 }
 
 // The tiled-path problems of a grouped call, in call order, in launches of up

@@ -54,9 +54,14 @@ __device__ __forceinline__ bool finite_h(_Float16 x) {
   return (b & 0x7C00u) != 0x7C00u;
 }
 
+// keep (optional): one bit per weight, row-major (bit k % 8 of byte
+// (n * K + k) / 8); a set bit marks a weight kept in fp16 elsewhere, which is
+// quantized here as 0 (it leaves the group range, and its code is the zero
+// point, so it decodes to exactly 0).
 template <bool SYM>
 __global__ __launch_bounds__(256) void pack_kernel(const _Float16 *__restrict__ W,
                                                    const _Float16 *__restrict__ s, int N, int K,
+                                                   const uint8_t *__restrict__ keep,
                                                    u32x4 *__restrict__ Wq,
                                                    _Float16 *__restrict__ scales,
                                                    _Float16 *__restrict__ zeros,
@@ -79,6 +84,9 @@ __global__ __launch_bounds__(256) void pack_kernel(const _Float16 *__restrict__ 
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const half8 wv = load_half8(wrow + 32 * t);
+    // the 8 columns g * 128 + 32 t + 8 c .. + 7 are one byte of the mask
+    const unsigned kb =
+        keep ? keep[((size_t)n * K + (size_t)g * kGroup + 32 * t + 8 * c) >> 3] : 0u;
     half8 sv;
     if (s) {
       sv = load_half8(s + (size_t)g * kGroup + 32 * t + 8 * c);
@@ -89,7 +97,7 @@ __global__ __launch_bounds__(256) void pack_kernel(const _Float16 *__restrict__ 
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if (!finite_h(wv[j]) || !finite_h(sv[j]) || !((double)sv[j] > 0.0)) bad |= kPackNonFinite;
-      const double q = (double)wv[j] / (double)sv[j];
+      const double q = (kb >> j) & 1u ? 0.0 : (double)wv[j] / (double)sv[j];
       wp[8 * t + j] = q;
       mn = q < mn ? q : mn;
       mx = q > mx ? q : mx;
@@ -157,17 +165,18 @@ __global__ __launch_bounds__(256) void pack_kernel(const _Float16 *__restrict__ 
 
 }  // namespace
 
-hipError_t launch_pack(const void *W, const void *s, int N, int K, void *Wq, void *scales,
-                       void *zeros, unsigned *status, bool symmetric, hipStream_t stream) {
+hipError_t launch_pack(const void *W, const void *s, int N, int K, const uint8_t *keep, void *Wq,
+                       void *scales, void *zeros, unsigned *status, bool symmetric,
+                       hipStream_t stream) {
   const long long tiles = (long long)(N / kTileRows) * (K / kGroup);
   const long long blocks = (tiles + 3) / 4;
   if (symmetric)
     hipLaunchKernelGGL(pack_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       (const _Float16 *)W, (const _Float16 *)s, N, K, (u32x4 *)Wq,
+                       (const _Float16 *)W, (const _Float16 *)s, N, K, keep, (u32x4 *)Wq,
                        (_Float16 *)scales, (_Float16 *)zeros, status);
   else
     hipLaunchKernelGGL(pack_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       (const _Float16 *)W, (const _Float16 *)s, N, K, (u32x4 *)Wq,
+                       (const _Float16 *)W, (const _Float16 *)s, N, K, keep, (u32x4 *)Wq,
                        (_Float16 *)scales, (_Float16 *)zeros, status);
   return hipGetLastError();
 }

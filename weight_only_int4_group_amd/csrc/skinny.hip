@@ -53,6 +53,8 @@ struct Problem {
   int M, N, K;
   int block0;  // first workgroup of this problem
   int split;   // waves per row block (a power of two, at most the workgroup's waves)
+  const int32_t *orp, *ocol;  // fp16 outliers, row-compressed (null: none)
+  const _Float16 *oval;
 };
 
 struct ProblemSet {
@@ -120,20 +122,69 @@ __device__ __forceinline__ Problem find_problem(const ProblemSet &ps) {
   P.N = uniform_int(ps.p[pi].N);
   P.K = uniform_int(ps.p[pi].K);
   P.split = uniform_int(ps.p[pi].split);
+  P.orp = uniform_ptr(ps.p[pi].orp);
+  P.ocol = uniform_ptr(ps.p[pi].ocol);
+  P.oval = uniform_ptr(ps.p[pi].oval);
   return P;
+}
+
+// The kept fp16 weights e0 .. e1 - 1 of the lane's row (its row-pointer pair,
+// loaded when the kernel starts) for lane (c, r): o[v] = the sum over them, in
+// stored order, of X[4c + v][col_e] * val_e (rows past M read row M - 1 and
+// are not stored).  Two entries' loads are issued at a time (more raise the
+// register count past what six waves per SIMD allow).
+__device__ __forceinline__ float4v outlier_terms(const Problem &P, int e0, int e1, int c) {
+  constexpr int kBatch = 2;
+  float4v o = {0.f, 0.f, 0.f, 0.f};
+  for (int e = e0; e < e1; e += kBatch) {
+    int col[kBatch];
+    float val[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int ee = min(e + u, e1 - 1);
+      col[u] = P.ocol[ee];
+      val[u] = (float)P.oval[ee];
+    }
+    float x[kBatch][4];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        x[u][v] = (float)P.X[(size_t)min(4 * c + v, P.M - 1) * P.K + col[u]];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) o[v] += e + u < e1 ? x[u][v] * val[u] : 0.f;
+  }
+  return o;
+}
+
+// The lane's row-pointer pair when its wave stores outputs with outliers (the
+// first K slice of a row block), else an empty range; issued first thing so
+// that it has arrived by the epilogue.
+__device__ __forceinline__ int2 outlier_range(const Problem &P, int b, bool has_rows, int ks,
+                                              int r) {
+  int2 e = {0, 0};
+  if (P.orp && has_rows && ks == 0) {
+    const int n = b * kTileRows + r;
+    e.x = P.orp[n];
+    e.y = P.orp[n + 1];
+  }
+  return e;
 }
 
 // Lane (c, r) holds D[m = 4c + v][n = r] of row block b summed over this
 // wave's groups.  With S waves per row block the partial sums are added in
 // the fixed order ks = 0, 1, ..., S - 1.  Every wave of the workgroup calls
 // this (it may synchronise the workgroup).
-template <int kWaves>
+template <int kWaves, bool kOut>
 __device__ __forceinline__ void store_rows(const Problem &P, float4v acc, int b, bool has_rows,
                                            int wave, int ks, int c, int r,
-                                           float (*red)[16][17]) {
+                                           float (*red)[16][17], int2 orange) {
   const int M = P.M, N = P.N, S = P.split;
   if (S == 1) {
     if (has_rows) {
+      if (kOut) acc += outlier_terms(P, orange.x, orange.y, c);
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int m = 4 * c + v;
@@ -145,12 +196,15 @@ __device__ __forceinline__ void store_rows(const Problem &P, float4v acc, int b,
     for (int v = 0; v < 4; ++v) red[wave][4 * c + v][r] = acc[v];
     __syncthreads();
     if (ks == 0 && has_rows) {
+      float4v o = {0.f, 0.f, 0.f, 0.f};
+      if (kOut) o = outlier_terms(P, orange.x, orange.y, c);
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int m = 4 * c + v;
         if (m < M) {
           float sum = 0.f;
           for (int w = 0; w < S; ++w) sum += red[wave + w][m][r];
+          if (kOut) sum += o[v];
           P.Y[(size_t)m * N + (size_t)b * kTileRows + r] = (_Float16)sum;
         }
       }
@@ -158,7 +212,7 @@ __device__ __forceinline__ void store_rows(const Problem &P, float4v acc, int b,
   }
 }
 
-template <int kGW, int kWaves, int kDepth>
+template <int kGW, int kWaves, int kDepth, bool kOut>
 __global__ __launch_bounds__(kWaves * 64) void skinny_kernel(ProblemSet ps) {
   // X * s, then (after the last use of X) the split-K reduction
   extern __shared__ __attribute__((aligned(16))) _Float16 xs[];
@@ -228,7 +282,8 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_kernel(ProblemSet ps) {
       mt.zq[2 * q + 1] = (uint32_t)zv[1];
     }
   };
-  // issue order: meta 0, codes 0, meta 1
+  // issue order: outlier row range, meta 0, codes 0, meta 1
+  const int2 orange = kOut ? outlier_range(P, b, has_rows, ks, r) : int2{0, 0};
   load_meta(m0, gb);
   load_codes(gb);
   load_meta(m1, gb + kGW);
@@ -288,12 +343,13 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_kernel(ProblemSet ps) {
   }
 
   if (S > 1) __syncthreads();  // every wave is done with X * s: its LDS takes the partial sums
-  store_rows<kWaves>(P, acc, b, has_rows, wave, ks, c, r, reinterpret_cast<float (*)[16][17]>(xs));
+  store_rows<kWaves, kOut>(P, acc, b, has_rows, wave, ks, c, r,
+                           reinterpret_cast<float (*)[16][17]>(xs), orange);
 }
 
 // Windowed variant: X * s staged one window of S chunks at a time (see the
 // header).  kSlots bounds the 8-column pieces of a window each thread stages.
-template <int kGW, int kWaves, int kDepth, int kSlots>
+template <int kGW, int kWaves, int kDepth, int kSlots, bool kOut>
 __global__ __launch_bounds__(kWaves * 64) void skinny_window_kernel(ProblemSet ps) {
   extern __shared__ __attribute__((aligned(16))) _Float16 xs[];
   __shared__ float red[kWaves][16][17];
@@ -321,6 +377,7 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_window_kernel(ProblemSet p
       (void *)P.scales, (short)0, (int)min((size_t)0x7fffffff, meta_bytes), kRsrcWord3);
   const __amdgpu_buffer_rsrc_t zrs = __builtin_amdgcn_make_buffer_rsrc(
       (void *)P.zeros, (short)0, (int)min((size_t)0x7fffffff, meta_bytes), kRsrcWord3);
+  const int2 orange = kOut ? outlier_range(P, b, has_rows, ks, r) : int2{0, 0};
   const int tile_off = bb * kTileBytes + lane * 16;               // + g * tile_stride
   const int meta_off = (bb * kTileRows + r) * kMetaQuad * 2;      // + quad * meta_stride
   const int tile_stride = NB * kTileBytes, meta_stride = NB * kTileRows * kMetaQuad * 2;
@@ -446,7 +503,7 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_window_kernel(ProblemSet p
     lds_barrier();
     load_window(j + 2);
   }
-  store_rows<kWaves>(P, acc, b, has_rows, wave, ks, c, r, red);
+  store_rows<kWaves, kOut>(P, acc, b, has_rows, wave, ks, c, r, red, orange);
 }
 
 constexpr size_t kMaxStageBytes = 96 * 1024;
@@ -536,6 +593,7 @@ hipError_t launch_group(const GemmDesc *const *d, int count, bool window, hipStr
   ProblemSet ps = {};
   int blocks = 0;
   size_t lds = 0;
+  bool out = false;  // some problem has fp16 outliers
   for (int i = 0; i < count; ++i) {
     const GemmDesc &q = *d[order[i]];
     Problem &p = ps.p[i];
@@ -557,6 +615,10 @@ hipError_t launch_group(const GemmDesc *const *d, int count, bool window, hipStr
     p.N = q.N;
     p.K = q.K;
     p.split = split;
+    p.orp = static_cast<const int32_t *>(q.o_row_ptr);
+    p.ocol = static_cast<const int32_t *>(q.o_col);
+    p.oval = static_cast<const _Float16 *>(q.o_val);
+    out |= q.o_row_ptr != nullptr;
     p.block0 = blocks;
     const int rb_per_wg = kWaves / split;
     blocks += (NB + rb_per_wg - 1) / rb_per_wg;
@@ -564,12 +626,19 @@ hipError_t launch_group(const GemmDesc *const *d, int count, bool window, hipStr
     lds = need > lds ? need : lds;
   }
   ps.count = count;
-  if (window)
-    hipLaunchKernelGGL((skinny_window_kernel<kChunk, kWaves, kDepth, kWindowSlots>), dim3(blocks),
-                       dim3(kWaves * 64), lds, stream, ps);
+  const dim3 grid(blocks), threads(kWaves * 64);
+  if (window && out)
+    hipLaunchKernelGGL((skinny_window_kernel<kChunk, kWaves, kDepth, kWindowSlots, true>), grid,
+                       threads, lds, stream, ps);
+  else if (window)
+    hipLaunchKernelGGL((skinny_window_kernel<kChunk, kWaves, kDepth, kWindowSlots, false>), grid,
+                       threads, lds, stream, ps);
+  else if (out)
+    hipLaunchKernelGGL((skinny_kernel<kChunk, kWaves, kDepth, true>), grid, threads, lds, stream,
+                       ps);
   else
-    hipLaunchKernelGGL((skinny_kernel<kChunk, kWaves, kDepth>), dim3(blocks), dim3(kWaves * 64),
-                       lds, stream, ps);
+    hipLaunchKernelGGL((skinny_kernel<kChunk, kWaves, kDepth, false>), grid, threads, lds, stream,
+                       ps);
   return hipGetLastError();
 }
 

@@ -81,6 +81,8 @@ struct TiledProblem {
   int split;        // K ranges per output block
   int block0;       // first workgroup of this problem in the GEMM launch
   int rblock0;      // first workgroup of this problem in the reduction launch
+  const int32_t *orp, *ocol;  // fp16 outliers, row-compressed (null: none)
+  const _Float16 *oval;
 };
 
 struct TiledSet {
@@ -121,12 +123,15 @@ __device__ __forceinline__ TiledProblem find_tiled(const TiledSet &ts, int block
   P.split = uniform_int(q.split);
   P.block0 = uniform_int(q.block0);
   P.rblock0 = uniform_int(q.rblock0);
+  P.orp = uniform_ptr(q.orp);
+  P.ocol = uniform_ptr(q.ocol);
+  P.oval = uniform_ptr(q.oval);
   return P;
 }
 
 // Two waves per SIMD: with one, the waits on LDS and the barriers are not
 // hidden and MFMA throughput roughly halves (measured on the 70B shapes).
-template <int WM, int WN, int TM, int TN>
+template <int WM, int WN, int TM, int TN, bool OUT>
 __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void tiled_kernel(
     TiledSet ts) {
   constexpr int THREADS = WM * WN * 64;
@@ -184,12 +189,17 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
       areg[i] = load_half8(X + (size_t)m * K + k0);
     }
   };
+  // with fp16 outliers, the group's s goes to LDS too (the outlier terms
+  // divide the staged X * s by it)
+  __shared__ __attribute__((aligned(16))) _Float16 Ss[OUT ? 2 : 1][OUT ? kGroup : 8];
+  const bool has_out = OUT && P.orp != nullptr;
   auto store_a = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < A_PER_T; ++i) {
       const half8 v = areg[i] * sreg;
       *reinterpret_cast<half8 *>(&As[buf][(a_row + i * ROWS_PER_PASS) * kLdsStride + a_col]) = v;
     }
+    if (OUT && has_out && a_row == 0) *reinterpret_cast<half8 *>(&Ss[OUT ? buf : 0][a_col]) = sreg;
   };
 
   // ---- weights: this wave's TN row blocks.  The next group's code tiles go
@@ -263,6 +273,95 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
     __builtin_amdgcn_iglp_opt(1);
   };
 
+  // ---- fp16 outliers.  Lane (c, r) holds outputs of rows n_j = n0 + (wn TN +
+  // j) 16 + r, j = 0..3, and keeps the walk over the kept weights of row n_c
+  // (columns increasing) with the next two of them in registers; each step
+  // the four lanes of a row share their entries by shuffles.  An entry whose
+  // column lies in group g is applied in step g, from the staged X * s of that
+  // group (divided by s, so the term is X[m][col] * val up to the rounding of
+  // X * s), to the 16 rows m the lane holds.  Entries of groups outside this
+  // block's K range belong to another split.  Slots refilled in a step are
+  // first read in the next one (after its wait for all loads), so no step
+  // waits on them; a third entry of one row in one group arrives a step late
+  // and is then applied from global X.
+  static_assert(TN == 4, "one row walk per lane of a row's four lanes");
+  constexpr int kNone = 0x7fffffff;
+  int oe = 0, oend = 0, ocol0 = kNone, ocol1 = kNone;
+  float oval0 = 0.f, oval1 = 0.f;
+  auto refill = [&](int &col, float &val) {
+    col = kNone;
+    if (oe < oend) {
+      col = P.ocol[oe];
+      val = (float)P.oval[oe];
+      ++oe;
+    }
+  };
+  auto outlier_start = [&]() {
+    const int n = n0 + (wn * TN + c) * 16 + r;
+    int lo = n < N ? P.orp[n] : 0, hi = n < N ? P.orp[n + 1] : 0;
+    oend = hi;
+    // first entry at or after this K range (binary search; nothing to skip
+    // for the first range)
+    if (gb > 0) {
+      const int kb = gb * kGroup;
+      while (__any(lo < hi)) {
+        if (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (P.ocol[mid] < kb)
+            lo = mid + 1;
+          else
+            hi = mid;
+        }
+      }
+    }
+    oe = lo;
+    refill(ocol0, oval0);
+    refill(ocol1, oval1);
+  };
+  // entry (col, val) of row j on the lane's 16 rows: from LDS for group g
+  // (buffer buf), or from global X when its group has already passed
+  auto apply_entry = [&](int j, int col, float val, int g, int buf) {
+    const int kk = col - g * kGroup;
+    if (kk >= 0) {
+      const float vs = has_s ? val / (float)Ss[OUT ? buf : 0][kk] : val;
+      const _Float16 *xb = As[buf] + (wm * TM * 16 + 4 * c) * kLdsStride + kk;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          acc[i][j][v] += (float)xb[(i * 16 + v) * kLdsStride] * vs;
+    } else {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int m = min(m0 + (wm * TM + i) * 16 + 4 * c + v, M - 1);
+          acc[i][j][v] += (float)X[(size_t)m * K + col] * val;
+        }
+    }
+  };
+  auto apply_outliers = [&](int g, int buf) {
+    const int khi = (g + 1) * kGroup;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int src = 16 * j + r;  // the lane walking row n_j
+      const int c0 = __shfl(ocol0, src), c1 = __shfl(ocol1, src);
+      const float v0 = __shfl(oval0, src), v1 = __shfl(oval1, src);
+      if (c0 < khi) apply_entry(j, c0, v0, g, buf);
+      if (c0 < khi && c1 < khi) apply_entry(j, c1, v1, g, buf);
+    }
+    // advance this lane's own walk past what was applied
+    const bool take0 = ocol0 < khi, take1 = take0 && ocol1 < khi;
+    if (take1) {
+      refill(ocol0, oval0);
+      refill(ocol1, oval1);
+    } else if (take0) {
+      ocol0 = ocol1;
+      oval0 = oval1;
+      refill(ocol1, oval1);
+    }
+  };
+
   // One group per step.  The group's codes and metadata were issued a step
   // ago: wait for them (the only loads in flight) and take the codes into
   // registers; then issue the next group's X and weight loads, run this
@@ -280,16 +379,36 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
       load_b(g + 1, buf ^ 1, nxt);
     }
     compute(cur, buf);
+    if (has_out) apply_outliers(g, buf);
     if (more) store_a(buf ^ 1);
     lds_barrier();
   };
   load_a(gb);
   load_b(gb, 0, b0);
+  if (has_out) outlier_start();  // its waits overlap the first group's loads
   store_a(0);
   lds_barrier();
   for (int g = gb; g < ge; g += 2) {
     step(g, b0, b1, 0);
     if (g + 1 < ge) step(g + 1, b1, b0, 1);
+  }
+  if (has_out) {
+    // late entries of the last group (a third or later in one row), from global X
+    const int kend = ge * kGroup;
+    while (__any(ocol0 < kend)) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int src = 16 * j + r;
+        const int c0 = __shfl(ocol0, src);
+        const float v0 = __shfl(oval0, src);
+        if (c0 < kend) apply_entry(j, c0, v0, ge, 0);
+      }
+      if (ocol0 < kend) {
+        ocol0 = ocol1;
+        oval0 = oval1;
+        refill(ocol1, oval1);
+      }
+    }
   }
 
   // lane holds D[4c + v][r] of each 16x16 sub-block: the output, or this
@@ -390,6 +509,7 @@ hipError_t launch_tiled_set(const GemmDesc *d, int count, void *workspace, size_
   TiledSet ts = {};
   int blocks = 0, rblocks = 0;
   size_t off = 0;
+  bool out = false;  // some problem has fp16 outliers
   for (int i = 0; i < count; ++i) {
     TiledProblem &p = ts.p[i];
     p.X = static_cast<const _Float16 *>(d[i].X);
@@ -406,6 +526,10 @@ hipError_t launch_tiled_set(const GemmDesc *d, int count, void *workspace, size_
     p.split = split[i];
     p.part = split[i] > 1 ? reinterpret_cast<float *>(static_cast<char *>(workspace) + off) : nullptr;
     off += part_bytes(d[i], split[i]);
+    p.orp = static_cast<const int32_t *>(d[i].o_row_ptr);
+    p.ocol = static_cast<const int32_t *>(d[i].o_col);
+    p.oval = static_cast<const _Float16 *>(d[i].o_val);
+    out |= d[i].o_row_ptr != nullptr;
     p.block0 = blocks;
     blocks += p.tiles * p.split;
     p.rblock0 = rblocks;
@@ -413,8 +537,12 @@ hipError_t launch_tiled_set(const GemmDesc *d, int count, void *workspace, size_
       rblocks += (int)(((long long)d[i].M * d[i].N / 4 + kReduceThreads - 1) / kReduceThreads);
   }
   ts.count = count;
-  hipLaunchKernelGGL((tiled_kernel<kWM, kWN, kTM, kTN>), dim3(blocks), dim3(kWM * kWN * 64),
-                     0, stream, ts);
+  if (out)
+    hipLaunchKernelGGL((tiled_kernel<kWM, kWN, kTM, kTN, true>), dim3(blocks),
+                       dim3(kWM * kWN * 64), 0, stream, ts);
+  else
+    hipLaunchKernelGGL((tiled_kernel<kWM, kWN, kTM, kTN, false>), dim3(blocks),
+                       dim3(kWM * kWN * 64), 0, stream, ts);
   hipError_t err = hipGetLastError();
   if (err == hipSuccess && rblocks > 0) {
     hipLaunchKernelGGL(split_reduce_kernel, dim3(rblocks), dim3(kReduceThreads), 0, stream, ts);

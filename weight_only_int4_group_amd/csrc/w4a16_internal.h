@@ -10,14 +10,25 @@ namespace w4a16 {
 constexpr unsigned kPackNonFinite = 1u;
 constexpr unsigned kPackRange = 2u;
 
-hipError_t launch_pack(const void *W, const void *s, int N, int K, void *Wq, void *scales,
-                       void *zeros, unsigned *status, bool symmetric, hipStream_t stream);
+hipError_t launch_pack(const void *W, const void *s, int N, int K, const uint8_t *keep, void *Wq,
+                       void *scales, void *zeros, unsigned *status, bool symmetric,
+                       hipStream_t stream);
+
+// The weights kept in fp16 (validated by the caller): writes row_ptr [N + 1],
+// col and val [count], and a keep bit mask in the workspace (returned in
+// *mask) for launch_pack.  Blocks until done.  0 on success, -1 on a HIP error.
+size_t outlier_workspace_bytes(int N, int K);
+int select_outliers(const void *W, const void *s, int N, int K, long long count, int32_t *row_ptr,
+                    int32_t *col, _Float16 *val, void *workspace, const uint8_t **mask,
+                    hipStream_t stream);
 
 // One dequantize-matmul problem (validated by the caller).
 struct GemmDesc {
   const void *X, *Wq, *scales, *zeros, *s;
   void *Y;
   int M, N, K;
+  // optional fp16 outliers, row-compressed (all set or all null)
+  const void *o_row_ptr = nullptr, *o_col = nullptr, *o_val = nullptr;
 };
 
 // Streaming kernel for small M (decode and speculative verify): M <= 16.
