@@ -41,6 +41,10 @@ The symmetric variant (``quantize_symmetric``, the signed -7..7 grid of [mhpq]
 sec.2.1) takes R2, R5, R7's ties, R8 and R9's errors as they are, with
 scale = max|W'| / 7 rounded up, signed codes rint(W' / scale) stored + 8 and a
 constant zero point 8 (an all-zero group: scale 0, codes 8).
+``quantize(..., granularity="channel" | "tensor")`` are the coarser granularities of
+[discosf] sec.2.1 (one scale per output channel, or per tensor): the range of
+R3 is taken over the row or the whole tensor, and every group slot of the
+packed metadata repeats that scale and zero point.
 The outlier side path (``outliers``, [mhpq] sec.2.2) keeps the largest |W / s|
 in fp16 and quantizes the rest with those positions set to 0; its readings
 O1-O5 are in that module.
@@ -48,15 +52,15 @@ Pins: every function here is checked by tests against facts the pages or the
 mathematics fix (bound, grid reconstruction, byte counts, brute force in exact
 rationals, integer special case); see tests/test_oracle_*.py.
 """
-from .quantizer import (GROUP, QMAX, SYM_QMAX, SYM_ZERO, NonFiniteInput, OracleError, QuantResult,
-                        ScaleOverflow, quantize, quantize_symmetric, round_up_fp16)
+from .quantizer import (GRANULARITIES, GROUP, QMAX, SYM_QMAX, SYM_ZERO, NonFiniteInput, OracleError,
+                        QuantResult, ScaleOverflow, quantize, quantize_symmetric, round_up_fp16)
 from .layout import (META_QUAD, TILE_BYTES, TILE_ROWS, meta_groups, meta_index, nibble_address,
                      pack_codes, pack_meta, unpack_codes, unpack_meta)
 from .matmul import dequantize, gemm
 from . import accounting, exact, outliers, spec
 
 __all__ = [
-    "GROUP", "QMAX", "NonFiniteInput", "OracleError", "QuantResult", "ScaleOverflow",
+    "GRANULARITIES", "GROUP", "QMAX", "NonFiniteInput", "OracleError", "QuantResult", "ScaleOverflow",
     "quantize", "quantize_symmetric", "SYM_QMAX", "SYM_ZERO", "round_up_fp16", "META_QUAD", "TILE_BYTES", "TILE_ROWS", "meta_groups",
     "meta_index", "nibble_address",
     "pack_codes", "pack_meta", "unpack_codes", "unpack_meta", "dequantize", "gemm",

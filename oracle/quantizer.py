@@ -55,8 +55,18 @@ def round_up_fp16(v: np.ndarray) -> np.ndarray:
     return h
 
 
-def quantize(W: np.ndarray, s: np.ndarray | None = None) -> QuantResult:
-    """Quantize fp16 ``W[N][K]`` (optionally divided by fp16 ``s[K]`` first) to INT4 groups."""
+GRANULARITIES = ("group", "channel", "tensor")
+
+
+def quantize(W: np.ndarray, s: np.ndarray | None = None, granularity: str = "group") -> QuantResult:
+    """Quantize fp16 ``W[N][K]`` (optionally divided by fp16 ``s[K]`` first) to INT4 groups.
+
+    ``granularity`` (discosf sec.2.1: per-tensor, per-channel or per-group scales) picks
+    the range a scale and zero point cover: each group of 128 (reading R2), each row
+    (output channel), or the whole tensor.  The coarser ones keep the per-group storage:
+    every group of a row (or of the tensor) carries the same scale and zero point."""
+    if granularity not in GRANULARITIES:
+        raise ValueError(f"granularity must be one of {GRANULARITIES}")
     W = np.asarray(W)
     if W.dtype != np.float16 or W.ndim != 2:
         raise TypeError("W must be a 2-D float16 array")
@@ -79,9 +89,17 @@ def quantize(W: np.ndarray, s: np.ndarray | None = None) -> QuantResult:
     G = K // GROUP
     Wg = Wp.reshape(N, G, GROUP)
 
-    # Group range, widened to contain 0 (R3); scale = range / 15 rounded up to fp16 (R4, R5).
-    mn = np.minimum(Wg.min(axis=2), 0.0)
-    mx = np.maximum(Wg.max(axis=2), 0.0)
+    # Range of each group (or row, or tensor), widened to contain 0 (R3);
+    # scale = range / 15 rounded up to fp16 (R4, R5).
+    if granularity == "group":
+        lo, hi = Wg.min(axis=2), Wg.max(axis=2)
+    elif granularity == "channel":
+        lo = np.repeat(Wp.min(axis=1, keepdims=True), G, axis=1)
+        hi = np.repeat(Wp.max(axis=1, keepdims=True), G, axis=1)
+    else:
+        lo, hi = np.full((N, G), Wp.min()), np.full((N, G), Wp.max())
+    mn = np.minimum(lo, 0.0)
+    mx = np.maximum(hi, 0.0)
     rng = mx - mn
     scale16 = round_up_fp16(rng / QMAX)
     if not np.all(np.isfinite(scale16)):
