@@ -111,10 +111,12 @@ int w4a16_packed_sizes(int64_t N, int64_t K, size_t *wq_bytes, size_t *scales_by
 int w4a16_quantize_pack(const void *W, const void *s, int64_t N, int64_t K, void *Wq,
                         void *scales, void *zeros, void *stream);
 
-/* Quantization grids for w4a16_quantize_pack_mode(). */
+/* Quantization grids and granularities for w4a16_quantize_pack_mode(). */
 enum {
-  W4A16_QUANT_ASYM = 0, /* the readings above (w4a16_quantize_pack)              */
-  W4A16_QUANT_SYM = 1   /* signed -7..7 around a constant zero point 8           */
+  W4A16_QUANT_ASYM = 0,         /* the readings above (w4a16_quantize_pack)        */
+  W4A16_QUANT_SYM = 1,          /* signed -7..7 around a constant zero point 8     */
+  W4A16_QUANT_ASYM_CHANNEL = 2, /* asymmetric, one scale/zero per row (channel)    */
+  W4A16_QUANT_ASYM_TENSOR = 3   /* asymmetric, one scale/zero for the whole tensor */
 };
 
 /* Quantize and pack on a chosen grid; same arguments, layout, blocking and
@@ -124,7 +126,14 @@ enum {
  * rounded UP to fp16 (so no code clamps), signed code rint(W' / scale) (ties
  * to even) stored as code + 8, zero point 8; an all-zero group stores scale 0
  * and codes 8.  The packed buffers are in the same layout and feed the same
- * GEMM entry points: (q - z) * scale reproduces the signed value. */
+ * GEMM entry points: (q - z) * scale reproduces the signed value.
+ * W4A16_QUANT_ASYM_CHANNEL and W4A16_QUANT_ASYM_TENSOR are the per-channel and
+ * per-tensor granularities of the nano-vllm tutorial (discosf.com, section
+ * 2.1): the range [min(0, min W'), max(0, max W')] is taken over the row or
+ * over the whole tensor instead of the group, and every group slot of the row
+ * repeats the resulting scale and zero point (same layout, same kernels).
+ * These two modes allocate 16 bytes per row of device memory for the
+ * duration of the call. */
 int w4a16_quantize_pack_mode(const void *W, const void *s, int64_t N, int64_t K, int mode,
                              void *Wq, void *scales, void *zeros, void *stream);
 

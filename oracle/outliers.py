@@ -69,14 +69,15 @@ class OutlierResult:
 
 
 def quantize_with_outliers(W: np.ndarray, s: np.ndarray | None, count: int,
-                           symmetric: bool = False) -> OutlierResult:
-    """Split W into `count` fp16 outliers and an INT4 remainder (O1-O5)."""
+                           symmetric: bool = False, granularity: str = "group") -> OutlierResult:
+    """Split W into `count` fp16 outliers and an INT4 remainder (O1-O5), the remainder on
+    the symmetric grid or at an asymmetric granularity (group, channel or tensor)."""
     W = np.asarray(W)
     if not np.all(np.isfinite(W.astype(np.float64))):
         raise NonFiniteInput("non-finite W (kept weights included)")   # R9
     mask = select(W, s, count)
     rest = np.where(mask, np.float16(0), W).astype(np.float16)        # O4
-    quant = (quantize_symmetric if symmetric else quantize)(rest, s)
+    quant = quantize_symmetric(rest, s) if symmetric else quantize(rest, s, granularity)
     rows, cols = np.nonzero(mask)                                      # row-major order (O5)
     row_ptr = np.zeros(W.shape[0] + 1, dtype=np.int64)
     np.add.at(row_ptr, rows + 1, 1)

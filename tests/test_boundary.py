@@ -166,10 +166,10 @@ def test_grouped_ws_validation():
 def test_quantize_mode_validation():
     L = w4.lib()
     # unknown mode: rejected before anything else, without a GPU call
-    assert L.w4a16_quantize_pack_mode(A16, None, 16, 128, 2, A16, A16, A16, None) == -3
+    assert L.w4a16_quantize_pack_mode(A16, None, 16, 128, 4, A16, A16, A16, None) == -3
     assert L.w4a16_quantize_pack_mode(A16, None, 16, 128, -1, A16, A16, A16, None) == -3
     # known modes validate shapes and alignment like w4a16_quantize_pack
-    for mode in (w4.QUANT_ASYM, w4.QUANT_SYM):
+    for mode in (w4.QUANT_ASYM, w4.QUANT_SYM, w4.QUANT_ASYM_CHANNEL, w4.QUANT_ASYM_TENSOR):
         assert L.w4a16_quantize_pack_mode(A16, None, 16, 100, mode, A16, A16, A16, None) == -1
         assert L.w4a16_quantize_pack_mode(ODD, None, 16, 128, mode, A16, A16, A16, None) == -2
 

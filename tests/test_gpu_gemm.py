@@ -130,6 +130,24 @@ def test_symmetric_weights(M, path):
     assert_close(Y, oracle.gemm(X, ref.q, ref.scales, ref.zeros, s), f"sym M={M} {path}")
 
 
+@pytest.mark.parametrize("gran,mode", [("channel", w4.QUANT_ASYM_CHANNEL),
+                                       ("tensor", w4.QUANT_ASYM_TENSOR)])
+@pytest.mark.parametrize("M,path", [(1, "skinny"), (9, "window"), (40, "tiled")])
+def test_coarser_granularity_weights(gran, mode, M, path):
+    """Per-channel and per-tensor packs (their scale repeated in every group) run through
+    the same kernels."""
+    torch_cuda()
+    N, K = 272, 1152
+    W = weights(13, 0, N, K)
+    s = awq_scales(13, 0, K)
+    pw = w4.w4a16_quantize_pack(to_dev(W), to_dev(s), mode=mode)
+    ref = oracle.quantize(W, s, gran)
+    X = activations(13, 0, M, K)
+    note(f"{gran} weights path={path} M={M}")
+    Y = run(X, pw, s, path)
+    assert_close(Y, oracle.gemm(X, ref.q, ref.scales, ref.zeros, s), f"{gran} M={M} {path}")
+
+
 @pytest.mark.parametrize("path", ["skinny", "window", "tiled"])
 def test_integer_case_bit_exact(path):
     """Pin P5: s = 1, integer weights with codes 0 and 15 in every group -> scale 1,

@@ -22,10 +22,15 @@ def gpu_pack(W, s, count, mode=w4.QUANT_ASYM):
                                            mode)
 
 
+GRANULARITY = {w4.QUANT_ASYM: "group", w4.QUANT_SYM: "group", w4.QUANT_ASYM_CHANNEL: "channel",
+               w4.QUANT_ASYM_TENSOR: "tensor"}
+
+
 def check_pack(W, s, count, tag, mode=w4.QUANT_ASYM):
     note(f"outlier pack {tag} N={W.shape[0]} K={W.shape[1]} count={count} mode={mode}")
     pw = gpu_pack(W, s, count, mode)
-    ref = ol.quantize_with_outliers(W, s, count, symmetric=mode == w4.QUANT_SYM)
+    ref = ol.quantize_with_outliers(W, s, count, symmetric=mode == w4.QUANT_SYM,
+                                    granularity=GRANULARITY[mode])
     assert np.array_equal(to_host(pw.o_row_ptr), ref.row_ptr), tag
     assert np.array_equal(to_host(pw.o_col), ref.col), tag
     assert np.array_equal(h16_bits(to_host(pw.o_val)), h16_bits(ref.val)), tag
@@ -35,7 +40,8 @@ def check_pack(W, s, count, tag, mode=w4.QUANT_ASYM):
     return pw, ref
 
 
-@pytest.mark.parametrize("mode", [w4.QUANT_ASYM, w4.QUANT_SYM])
+@pytest.mark.parametrize("mode", [w4.QUANT_ASYM, w4.QUANT_SYM, w4.QUANT_ASYM_CHANNEL,
+                                  w4.QUANT_ASYM_TENSOR])
 @pytest.mark.parametrize("N,K,awq", [(16, 128, False), (48, 384, True), (272, 640, True),
                                      (1024, 1024, False)])
 def test_pack_matches_oracle(N, K, awq, mode):

@@ -16,16 +16,26 @@ def gpu_pack(W, s, mode=w4.QUANT_ASYM):
     return to_host(pw.wq), to_host(pw.scales), to_host(pw.zeros)
 
 
+GRANULARITY = {w4.QUANT_ASYM: "group", w4.QUANT_ASYM_CHANNEL: "channel",
+               w4.QUANT_ASYM_TENSOR: "tensor"}
+
+
+def oracle_quant(W, s, mode):
+    if mode == w4.QUANT_SYM:
+        return oracle.quantize_symmetric(W, s)
+    return oracle.quantize(W, s, GRANULARITY[mode])
+
+
 def check_exact(W, s, tag, mode=w4.QUANT_ASYM):
     note(f"pack {tag} N={W.shape[0]} K={W.shape[1]} awq={s is not None} mode={mode}")
     wq, sc, z = gpu_pack(W, s, mode)
-    ref = oracle.quantize(W, s) if mode == w4.QUANT_ASYM else oracle.quantize_symmetric(W, s)
+    ref = oracle_quant(W, s, mode)
     assert np.array_equal(h16_bits(sc), h16_bits(oracle.pack_meta(ref.scales))), tag
     assert np.array_equal(h16_bits(z), h16_bits(oracle.pack_meta(ref.zeros))), tag
     assert np.array_equal(wq, oracle.pack_codes(ref.q)), tag
 
 
-MODES = [w4.QUANT_ASYM, w4.QUANT_SYM]
+MODES = [w4.QUANT_ASYM, w4.QUANT_SYM, w4.QUANT_ASYM_CHANNEL, w4.QUANT_ASYM_TENSOR]
 
 
 @pytest.mark.parametrize("mode", MODES)

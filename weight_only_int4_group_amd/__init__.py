@@ -20,7 +20,8 @@ from .build import LIB_PATH
 
 __all__ = [
     "W4A16Error", "PackedWeight", "GROUP", "PATH_AUTO", "PATH_SKINNY", "PATH_TILED",
-    "PATH_SKINNY_WINDOW", "QUANT_ASYM", "QUANT_SYM", "lib",
+    "PATH_SKINNY_WINDOW", "QUANT_ASYM", "QUANT_SYM", "QUANT_ASYM_CHANNEL", "QUANT_ASYM_TENSOR",
+    "lib",
     "w4a16_packed_sizes", "w4a16_quantize_pack", "w4a16_gemm", "w4a16_gemm_path",
     "w4a16_select_path", "w4a16_strerror", "w4a16_version", "EXPORTED_SYMBOLS",
     "w4a16_gemm_grouped", "GroupedCall", "w4a16_spec_verify",
@@ -30,7 +31,7 @@ __all__ = [
 
 GROUP = 128
 PATH_AUTO, PATH_SKINNY, PATH_TILED, PATH_SKINNY_WINDOW = 0, 1, 2, 3
-QUANT_ASYM, QUANT_SYM = 0, 1
+QUANT_ASYM, QUANT_SYM, QUANT_ASYM_CHANNEL, QUANT_ASYM_TENSOR = 0, 1, 2, 3
 STATUS = {0: "W4A16_OK", -1: "W4A16_EINVAL", -2: "W4A16_EALIGN", -3: "W4A16_EUNSUPPORTED",
           -4: "W4A16_ENONFINITE", -5: "W4A16_ERANGE", -6: "W4A16_EHIP"}
 EXPORTED_SYMBOLS = ("w4a16_packed_sizes", "w4a16_quantize_pack", "w4a16_quantize_pack_mode",
@@ -172,7 +173,8 @@ def _dev_ptr(t, name, dtype=None, numel=None):
 def w4a16_quantize_pack(W, s=None, out: PackedWeight | None = None,
                         mode: int = QUANT_ASYM) -> PackedWeight:
     """Quantize fp16 W[N][K] (AWQ scale s[K] or None) into a PackedWeight (blocks).
-    mode: QUANT_ASYM (w4a16_quantize_pack) or QUANT_SYM (signed -7..7 grid)."""
+    mode: QUANT_ASYM (w4a16_quantize_pack), QUANT_SYM (signed -7..7 grid),
+    QUANT_ASYM_CHANNEL or QUANT_ASYM_TENSOR (one scale per row or per tensor)."""
     torch = _torch()
     if W.dim() != 2:
         raise ValueError("W must be 2-D [N][K]")

@@ -74,17 +74,37 @@ int w4a16_packed_sizes(int64_t N, int64_t K, size_t *wq_bytes, size_t *scales_by
   return W4A16_OK;
 }
 
+static bool known_mode(int mode) {
+  return mode == W4A16_QUANT_ASYM || mode == W4A16_QUANT_SYM || mode == W4A16_QUANT_ASYM_CHANNEL ||
+         mode == W4A16_QUANT_ASYM_TENSOR;
+}
+
 static int pack_and_check(const void *W, const void *s, int64_t N, int64_t K,
                           const uint8_t *keep, int mode, void *Wq, void *scales, void *zeros,
                           unsigned *status, hipStream_t st) {
-  if (hipMemsetAsync(status, 0, sizeof(unsigned), st) != hipSuccess) return W4A16_EHIP;
-  if (w4a16::launch_pack(W, s, (int)N, (int)K, keep, Wq, scales, zeros, status,
-                         mode == W4A16_QUANT_SYM, st) != hipSuccess)
+  // the coarser granularities need each row's range first: 16 bytes per row
+  // of device memory for the duration of the call
+  double *range = nullptr;
+  const bool coarse = mode == W4A16_QUANT_ASYM_CHANNEL || mode == W4A16_QUANT_ASYM_TENSOR;
+  if (coarse && hipMalloc(&range, (size_t)N * 2 * sizeof(double)) != hipSuccess)
     return W4A16_EHIP;
+  int rc = W4A16_OK;
+  if (hipMemsetAsync(status, 0, sizeof(unsigned), st) != hipSuccess) rc = W4A16_EHIP;
+  if (!rc && coarse &&
+      w4a16::launch_row_range(W, s, (int)N, (int)K, keep, mode == W4A16_QUANT_ASYM_TENSOR, range,
+                              range + N, st) != hipSuccess)
+    rc = W4A16_EHIP;
+  if (!rc && w4a16::launch_pack(W, s, (int)N, (int)K, keep, range, range ? range + N : nullptr,
+                                Wq, scales, zeros, status, mode == W4A16_QUANT_SYM,
+                                st) != hipSuccess)
+    rc = W4A16_EHIP;
   unsigned host = 0;
-  if (hipMemcpyAsync(&host, status, sizeof(unsigned), hipMemcpyDeviceToHost, st) != hipSuccess)
-    return W4A16_EHIP;
-  if (hipStreamSynchronize(st) != hipSuccess) return W4A16_EHIP;
+  if (!rc && hipMemcpyAsync(&host, status, sizeof(unsigned), hipMemcpyDeviceToHost, st) !=
+                 hipSuccess)
+    rc = W4A16_EHIP;
+  if (hipStreamSynchronize(st) != hipSuccess) rc = W4A16_EHIP;  // also before freeing `range`
+  if (range) hipFree(range);
+  if (rc) return rc;
   if (host & w4a16::kPackNonFinite) return W4A16_ENONFINITE;
   if (host & w4a16::kPackRange) return W4A16_ERANGE;
   return W4A16_OK;
@@ -92,7 +112,7 @@ static int pack_and_check(const void *W, const void *s, int64_t N, int64_t K,
 
 int w4a16_quantize_pack_mode(const void *W, const void *s, int64_t N, int64_t K, int mode,
                              void *Wq, void *scales, void *zeros, void *stream) {
-  if (mode != W4A16_QUANT_ASYM && mode != W4A16_QUANT_SYM) return W4A16_EUNSUPPORTED;
+  if (!known_mode(mode)) return W4A16_EUNSUPPORTED;
   if (!W || !Wq || !scales || !zeros) return W4A16_EINVAL;
   int rc = check_shape(N, K);
   if (rc) return rc;
@@ -117,7 +137,7 @@ int w4a16_quantize_pack_outliers(const void *W, const void *s, int64_t N, int64_
                                  int64_t count, void *Wq, void *scales, void *zeros,
                                  void *o_row_ptr, void *o_col, void *o_val, void *workspace,
                                  size_t workspace_bytes, void *stream) {
-  if (mode != W4A16_QUANT_ASYM && mode != W4A16_QUANT_SYM) return W4A16_EUNSUPPORTED;
+  if (!known_mode(mode)) return W4A16_EUNSUPPORTED;
   int rc = check_shape(N, K);
   if (rc) return rc;
   if (count < 0 || count > N * K || count > INT32_MAX) return W4A16_EINVAL;

@@ -10,6 +10,11 @@
 // scale = range / 15 rounded up to fp16, z = rint(-min / scale),
 // q = clamp(rint(W' / scale) + z, 0, 15), ties to even.
 //
+// The per-channel and per-tensor granularities of the same tutorial (section
+// 2.1: one scale per channel, or per tensor) take the range over the row or
+// the whole tensor (row_range_kernel, tensor_range_kernel) and repeat its
+// scale and zero point in every group of the row.
+//
 // The symmetric variant (the signed -7..7 grid of the practitioner notes at
 // mhpq.cn, section 2.1) keeps every step but the grid: scale = max|W'| / 7
 // rounded up to fp16, signed code c = clamp(rint(W' / scale), -7, 7) stored as
@@ -58,10 +63,14 @@ __device__ __forceinline__ bool finite_h(_Float16 x) {
 // (n * K + k) / 8); a set bit marks a weight kept in fp16 elsewhere, which is
 // quantized here as 0 (it leaves the group range, and its code is the zero
 // point, so it decodes to exactly 0).
+// rmin, rmax (optional): the range of each row's W' (per-channel or
+// per-tensor granularity) in place of each group's own.
 template <bool SYM>
 __global__ __launch_bounds__(256) void pack_kernel(const _Float16 *__restrict__ W,
                                                    const _Float16 *__restrict__ s, int N, int K,
                                                    const uint8_t *__restrict__ keep,
+                                                   const double *__restrict__ rmin,
+                                                   const double *__restrict__ rmax,
                                                    u32x4 *__restrict__ Wq,
                                                    _Float16 *__restrict__ scales,
                                                    _Float16 *__restrict__ zeros,
@@ -108,6 +117,10 @@ __global__ __launch_bounds__(256) void pack_kernel(const _Float16 *__restrict__ 
   mn = fmin(mn, __shfl_xor(mn, 32));
   mx = fmax(mx, __shfl_xor(mx, 16));
   mx = fmax(mx, __shfl_xor(mx, 32));
+  if (rmin) {  // a coarser granularity: the row's (or tensor's) range, still containing 0
+    mn = fmin(rmin[n], 0.0);
+    mx = fmax(rmax[n], 0.0);
+  }
 
   // asymmetric: the range [mn, mx]; symmetric: the largest magnitude
   const double range = SYM ? (mx > -mn ? mx : -mn) : mx - mn;
@@ -163,20 +176,105 @@ __global__ __launch_bounds__(256) void pack_kernel(const _Float16 *__restrict__ 
   if (bad) atomicOr(status, bad);
 }
 
+// Per row n: the least and largest W' = W / s over the row (kept weights
+// count as 0), one workgroup per row.  Exact: min and max round nothing.
+__global__ __launch_bounds__(256) void row_range_kernel(const _Float16 *__restrict__ W,
+                                                        const _Float16 *__restrict__ s, int K,
+                                                        const uint8_t *__restrict__ keep,
+                                                        double *__restrict__ rmin,
+                                                        double *__restrict__ rmax) {
+#pragma clang fp contract(off)
+  __shared__ double red[2][4];
+  const int n = blockIdx.x, tid = threadIdx.x;
+  double lo = 0.0, hi = 0.0;  // 0 is in every range anyway
+  for (int k0 = 8 * tid; k0 < K; k0 += 8 * 256) {
+    const half8 wv = load_half8(W + (size_t)n * K + k0);
+    const unsigned kb = keep ? keep[((size_t)n * K + k0) >> 3] : 0u;
+    half8 sv;
+    if (s) {
+      sv = load_half8(s + k0);
+    } else {
+      const half8 one = {1, 1, 1, 1, 1, 1, 1, 1};
+      sv = one;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const double q = (kb >> j) & 1u ? 0.0 : (double)wv[j] / (double)sv[j];
+      lo = q < lo ? q : lo;
+      hi = q > hi ? q : hi;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    lo = fmin(lo, __shfl_xor(lo, o));
+    hi = fmax(hi, __shfl_xor(hi, o));
+  }
+  if ((tid & 63) == 0) {
+    red[0][tid >> 6] = lo;
+    red[1][tid >> 6] = hi;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    rmin[n] = fmin(fmin(red[0][0], red[0][1]), fmin(red[0][2], red[0][3]));
+    rmax[n] = fmax(fmax(red[1][0], red[1][1]), fmax(red[1][2], red[1][3]));
+  }
+}
+
+// The tensor's range: every row gets the least of rmin and the largest of
+// rmax.  One workgroup.
+__global__ __launch_bounds__(256) void tensor_range_kernel(int N, double *__restrict__ rmin,
+                                                           double *__restrict__ rmax) {
+  __shared__ double red[2][4];
+  const int tid = threadIdx.x;
+  double lo = 0.0, hi = 0.0;
+  for (int n = tid; n < N; n += 256) {
+    lo = fmin(lo, rmin[n]);
+    hi = fmax(hi, rmax[n]);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    lo = fmin(lo, __shfl_xor(lo, o));
+    hi = fmax(hi, __shfl_xor(hi, o));
+  }
+  if ((tid & 63) == 0) {
+    red[0][tid >> 6] = lo;
+    red[1][tid >> 6] = hi;
+  }
+  __syncthreads();
+  lo = fmin(fmin(red[0][0], red[0][1]), fmin(red[0][2], red[0][3]));
+  hi = fmax(fmax(red[1][0], red[1][1]), fmax(red[1][2], red[1][3]));
+  for (int n = tid; n < N; n += 256) {
+    rmin[n] = lo;
+    rmax[n] = hi;
+  }
+}
+
 }  // namespace
 
-hipError_t launch_pack(const void *W, const void *s, int N, int K, const uint8_t *keep, void *Wq,
-                       void *scales, void *zeros, unsigned *status, bool symmetric,
-                       hipStream_t stream) {
+hipError_t launch_row_range(const void *W, const void *s, int N, int K, const uint8_t *keep,
+                            bool tensor, double *rmin, double *rmax, hipStream_t stream) {
+  hipLaunchKernelGGL(row_range_kernel, dim3(N), dim3(256), 0, stream, (const _Float16 *)W,
+                     (const _Float16 *)s, K, keep, rmin, rmax);
+  hipError_t err = hipGetLastError();
+  if (err == hipSuccess && tensor) {
+    hipLaunchKernelGGL(tensor_range_kernel, dim3(1), dim3(256), 0, stream, N, rmin, rmax);
+    err = hipGetLastError();
+  }
+  return err;
+}
+
+hipError_t launch_pack(const void *W, const void *s, int N, int K, const uint8_t *keep,
+                       const double *rmin, const double *rmax, void *Wq, void *scales, void *zeros,
+                       unsigned *status, bool symmetric, hipStream_t stream) {
   const long long tiles = (long long)(N / kTileRows) * (K / kGroup);
   const long long blocks = (tiles + 3) / 4;
   if (symmetric)
     hipLaunchKernelGGL(pack_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       (const _Float16 *)W, (const _Float16 *)s, N, K, keep, (u32x4 *)Wq,
+                       (const _Float16 *)W, (const _Float16 *)s, N, K, keep, rmin, rmax, (u32x4 *)Wq,
                        (_Float16 *)scales, (_Float16 *)zeros, status);
   else
     hipLaunchKernelGGL(pack_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       (const _Float16 *)W, (const _Float16 *)s, N, K, keep, (u32x4 *)Wq,
+                       (const _Float16 *)W, (const _Float16 *)s, N, K, keep, rmin, rmax, (u32x4 *)Wq,
                        (_Float16 *)scales, (_Float16 *)zeros, status);
   return hipGetLastError();
 }

@@ -10,9 +10,13 @@ namespace w4a16 {
 constexpr unsigned kPackNonFinite = 1u;
 constexpr unsigned kPackRange = 2u;
 
-hipError_t launch_pack(const void *W, const void *s, int N, int K, const uint8_t *keep, void *Wq,
-                       void *scales, void *zeros, unsigned *status, bool symmetric,
-                       hipStream_t stream);
+hipError_t launch_pack(const void *W, const void *s, int N, int K, const uint8_t *keep,
+                       const double *rmin, const double *rmax, void *Wq, void *scales, void *zeros,
+                       unsigned *status, bool symmetric, hipStream_t stream);
+// Per-row range of W / s (kept weights as 0) into rmin/rmax [N]; with `tensor`
+// every row then holds the whole tensor's range.
+hipError_t launch_row_range(const void *W, const void *s, int N, int K, const uint8_t *keep,
+                            bool tensor, double *rmin, double *rmax, hipStream_t stream);
 
 // The weights kept in fp16 (validated by the caller): writes row_ptr [N + 1],
 // col and val [count], and a keep bit mask in the workspace (returned in
