@@ -26,6 +26,8 @@ Printed JSON line:
   outliers      the headline layer with each matrix's top 0.1% |W/s| kept in fp16
                 and added by the kernels (one grouped launch per step); the prefill
                 line carries the same variant of the 70B layer;
+  bf16          the headline layer (and, in the prefill line, the 70B layer) with bf16
+                activations and outputs on the same packed weights;
   spec_verify   the accept / reject / draw step after a K = 4 verify pass over the
                 Llama-3 vocabulary (V = 128256), for 1 and 64 sequences per call;
   prefill       the 70B-shaped layer at M = 4096 (compute-bound): TFLOP/s
@@ -203,6 +205,18 @@ def with_batch(mats, cfg, M, torch, workloads):
     return out
 
 
+def with_bf16(mats, cfg, M, torch, workloads):
+    """The same packed matrices with bf16 activations and outputs (the same draws as the
+    fp16 activations, rounded to bf16)."""
+    out = []
+    for mi, m in enumerate(mats):
+        bits = workloads.activations_bf16(cfg.weight_key, mi, M, m["K"], outliers=cfg.act_outliers)
+        X = torch.from_numpy(bits.view(np.int16)).to("cuda").view(torch.bfloat16)
+        Y = torch.empty((M, m["N"]), dtype=torch.bfloat16, device="cuda")
+        out.append(dict(m, X=X, Y=Y))
+    return out
+
+
 def batched_line(cfg, M, mats, pool, copies, w4, torch, workloads, steps=200, warmup=20):
     """One grouped call over the whole layer per step at batch M."""
     bm = with_batch(mats, cfg, M, torch, workloads)
@@ -357,6 +371,7 @@ def main():
     ap.add_argument("--no-ceilings", action="store_true")
     ap.add_argument("--no-spec", action="store_true")
     ap.add_argument("--no-outliers", action="store_true")
+    ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-run", action="store_true",
                     help="only the short fixed sequence used for counter collection")
@@ -417,6 +432,18 @@ def main():
             w, l = timed(make_calls(mats, pool, copies, groups, w4, torch), 200, 20, torch)
             vs[label] = variant(mats, groups, l, 200, w, "bytes")
         out["layer_variants"] = vs
+    if not args.no_bf16:
+        bmats = with_bf16(mats, cfg, M, torch, workloads)
+        bwall, blms = timed(make_calls(bmats, pool, copies, one, w4, torch), args.steps // 2,
+                            args.warmup, torch)
+        bkern = float(np.mean(blms[0])) * 1e-3
+        out["bf16"] = {"workload": f"{cfg.name} with bf16 activations and outputs, M={M}, "
+                                   "the same packed weights, one grouped launch per step",
+                       "us_per_step": round(bwall / (args.steps // 2) * 1e6, 2),
+                       "kernel_us_per_step": round(bkern * 1e6, 2),
+                       "kernel_TB/s": round(step_bytes / bkern / 1e12, 4),
+                       "vs_fp16_kernel_time": round(bkern / (avg_ms * 1e-3), 4)}
+        del bmats
     if not args.no_batched:
         vcfg = workloads.config_by_name("llama3_8b_verify")
         assert vcfg.weight_key == cfg.weight_key  # verify runs the decode layer's weights
@@ -484,6 +511,18 @@ def main():
                                                      "tiled.hip")},
             "per_matrix": variant(pmats, groups, pms, args.prefill_steps, pwall, "flops")["launches"],
         }
+        if not args.no_bf16:
+            bpm = with_bf16(pmats, pcfg, PM, torch, workloads)
+            _, bpms = timed(make_calls(bpm, ppool, pc, groups, w4, torch), args.prefill_steps, 2,
+                            torch, per=1)
+            btot = sum(float(np.mean(x)) for x in bpms)
+            out["prefill"]["bf16"] = {
+                "workload": "the same layer with bf16 activations and outputs",
+                "kernel_ms_per_step": round(btot, 4),
+                "TFLOP/s": round(flops / (btot * 1e-3) / 1e12, 2),
+                "frac_of_dense_bf16_peak": round(flops / (btot * 1e-3) / 1e12 / FP16_PEAK_TFLOPS, 4),
+                "vs_fp16_kernel_time": round(btot / tot_ms, 4)}
+            del bpm
         del ppool, pmats
         torch.cuda.empty_cache()
         if not args.no_outliers:

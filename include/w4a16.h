@@ -196,7 +196,17 @@ typedef struct w4a16_problem {
   const void *o_row_ptr;
   const void *o_col;
   const void *o_val;
+  /* Activation type of X and Y: W4A16_DTYPE_F16 (0, the default of a zeroed
+   * struct) or W4A16_DTYPE_BF16 (1); s and the packed weights stay fp16.  With
+   * bf16, X * s is rounded to bf16 once, the streaming kernels multiply the
+   * exact codes and apply scale and zero point in fp32 per group, and the tiled
+   * kernel rounds each dequantized weight to bf16 once (fp32 accumulation
+   * throughout; Y rounded to bf16 once).  Another value is EUNSUPPORTED. */
+  int32_t dtype;
+  int32_t reserved; /* 0 */
 } w4a16_problem;
+
+enum { W4A16_DTYPE_F16 = 0, W4A16_DTYPE_BF16 = 1 };
 
 /* Several independent dequantize-matmuls, each the operation w4a16_gemm
  * computes, in as few launches as possible: problems that the M-dispatch

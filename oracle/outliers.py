@@ -94,4 +94,4 @@ def merged_weight(res: OutlierResult, W: np.ndarray, s: np.ndarray | None) -> np
 
 def gemm(X: np.ndarray, res: OutlierResult, W: np.ndarray, s: np.ndarray | None) -> np.ndarray:
     """Y = X . W_hat^T in fp64 with the merged weight (the page's where-merge, then a matmul)."""
-    return np.asarray(X, dtype=np.float16).astype(np.float64) @ merged_weight(res, W, s).T
+    return np.asarray(X).astype(np.float64) @ merged_weight(res, W, s).T   # X: fp16 or exact fp64

@@ -268,3 +268,24 @@ def test_grouped_outlier_fields_validation():
     assert L.w4a16_gemm_grouped(arr, 1, None) == -2
     arr = (w4.Problem * 1)(prob(o_row_ptr=A4, o_col=A4, o_val=V((1 << 20) + 1)))
     assert L.w4a16_gemm_grouped(arr, 1, None) == -2
+
+
+def test_grouped_dtype_validation():
+    L = w4.lib()
+    p = w4.Problem(A16, A16, A16, A16, None, A16, 1, 32, 256)
+    p.dtype = 2
+    arr = (w4.Problem * 1)(p)
+    assert L.w4a16_gemm_grouped(arr, 1, None) == -3
+    assert ctypes.sizeof(w4.Problem) == 104
+
+
+def test_bf16_bit_helpers_match_torch():
+    import numpy as np
+    import torch
+    from workloads import bf16_bits_to_f64, to_bf16_bits
+    x = np.random.default_rng(3).standard_normal(4096).astype(np.float32) * 50
+    x[:4] = [0.0, -0.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8]      # ties round to even
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(to_bf16_bits(x), want)
+    assert np.array_equal(bf16_bits_to_f64(want),
+                          torch.from_numpy(want.view(np.int16)).view(torch.bfloat16).double().numpy())

@@ -26,12 +26,13 @@ __all__ = [
     "w4a16_select_path", "w4a16_strerror", "w4a16_version", "EXPORTED_SYMBOLS",
     "w4a16_gemm_grouped", "GroupedCall", "w4a16_spec_verify",
     "w4a16_spec_verify_workspace_size", "SpecVerifyCall", "w4a16_quantize_pack_outliers",
-    "w4a16_outlier_workspace_size", "page_outlier_count",
+    "w4a16_outlier_workspace_size", "page_outlier_count", "DTYPE_F16", "DTYPE_BF16",
 ]
 
 GROUP = 128
 PATH_AUTO, PATH_SKINNY, PATH_TILED, PATH_SKINNY_WINDOW = 0, 1, 2, 3
 QUANT_ASYM, QUANT_SYM, QUANT_ASYM_CHANNEL, QUANT_ASYM_TENSOR = 0, 1, 2, 3
+DTYPE_F16, DTYPE_BF16 = 0, 1
 STATUS = {0: "W4A16_OK", -1: "W4A16_EINVAL", -2: "W4A16_EALIGN", -3: "W4A16_EUNSUPPORTED",
           -4: "W4A16_ENONFINITE", -5: "W4A16_ERANGE", -6: "W4A16_EHIP"}
 EXPORTED_SYMBOLS = ("w4a16_packed_sizes", "w4a16_quantize_pack", "w4a16_quantize_pack_mode",
@@ -49,7 +50,7 @@ class Problem(ctypes.Structure):
                 ("zeros", ctypes.c_void_p), ("s", ctypes.c_void_p), ("Y", ctypes.c_void_p),
                 ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
                 ("o_row_ptr", ctypes.c_void_p), ("o_col", ctypes.c_void_p),
-                ("o_val", ctypes.c_void_p)]
+                ("o_val", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class W4A16Error(RuntimeError):
@@ -265,13 +266,13 @@ def w4a16_gemm_path(X, pw: PackedWeight, s=None, path: int = PATH_AUTO, out=None
 
 
 def w4a16_gemm(X, pw: PackedWeight, s=None, out=None):
-    """Y[M][N] = X[M][K] . dequant(pw)^T (fp16) through the grouped entry point with a
-    workspace, so large-M calls may split K across workgroups."""
+    """Y[M][N] = X[M][K] . dequant(pw)^T through the grouped entry point with a workspace,
+    so large-M calls may split K across workgroups.  X (and Y) fp16 or bf16."""
     torch = _torch()
     if X.dim() != 2 or X.shape[1] != pw.K:
         raise ValueError("X must be [M][K] with K matching the packed weight")
     if out is None:
-        out = torch.empty((X.shape[0], pw.N), dtype=torch.float16, device=X.device)
+        out = torch.empty((X.shape[0], pw.N), dtype=X.dtype, device=X.device)
     GroupedCall([(X, pw, s, out)])()
     return out
 
@@ -294,11 +295,14 @@ class GroupedCall:
         for i, (X, pw, s, Y) in enumerate(self.items):
             if X.dim() != 2 or X.shape[1] != pw.K or tuple(Y.shape) != (X.shape[0], pw.N):
                 raise ValueError(f"problem {i}: X must be [M][K] and Y [M][N]")
+            if X.dtype not in (torch.float16, torch.bfloat16):
+                raise TypeError(f"problem {i}: X must be float16 or bfloat16")
             self.array[i] = Problem(
-                _dev_ptr(X, "X", torch.float16), _dev_ptr(pw.wq, "wq", torch.uint8),
+                _dev_ptr(X, "X", X.dtype), _dev_ptr(pw.wq, "wq", torch.uint8),
                 _dev_ptr(pw.scales, "scales", torch.float16),
                 _dev_ptr(pw.zeros, "zeros", torch.float16), _dev_ptr(s, "s", torch.float16, pw.K),
-                _dev_ptr(Y, "Y", torch.float16), X.shape[0], pw.N, pw.K, *pw.outlier_ptrs())
+                _dev_ptr(Y, "Y", X.dtype), X.shape[0], pw.N, pw.K, *pw.outlier_ptrs(),
+                DTYPE_BF16 if X.dtype == torch.bfloat16 else DTYPE_F16, 0)
         self.device = self.items[0][0].device if self.items else None
         self.ws, self.ws_ptr, self.ws_bytes = None, None, 0
         if workspace and self.items:
@@ -324,7 +328,7 @@ def w4a16_gemm_grouped(items):
     """Several independent Y = X . dequant(pw)^T in as few launches as possible.
     items: list of (X, PackedWeight, s or None); returns the list of Y tensors."""
     torch = _torch()
-    full = [(X, pw, s, torch.empty((X.shape[0], pw.N), dtype=torch.float16, device=X.device))
+    full = [(X, pw, s, torch.empty((X.shape[0], pw.N), dtype=X.dtype, device=X.device))
             for (X, pw, s) in items]
     GroupedCall(full)()
     return [it[3] for it in full]

@@ -194,7 +194,7 @@ void skinny_pieces(const w4a16_problem &p, std::vector<w4a16::GemmDesc> &out) {
     const int64_t mb = (p.M - m0) < kSkinnyMaxM ? (p.M - m0) : kSkinnyMaxM;
     out.push_back({static_cast<const _Float16 *>(p.X) + m0 * p.K, p.Wq, p.scales, p.zeros, p.s,
                    static_cast<_Float16 *>(p.Y) + m0 * p.N, (int)mb, (int)p.N, (int)p.K,
-                   p.o_row_ptr, p.o_col, p.o_val});
+                   p.o_row_ptr, p.o_col, p.o_val, p.dtype == W4A16_DTYPE_BF16});
   }
 }
 
@@ -244,6 +244,7 @@ int check_problems(const w4a16_problem *problems, int count) {
     const w4a16_problem &p = problems[i];
     const int rc = check_gemm(p.X, p.Wq, p.scales, p.zeros, p.s, p.Y, p.M, p.N, p.K);
     if (rc) return rc;
+    if (p.dtype != W4A16_DTYPE_F16 && p.dtype != W4A16_DTYPE_BF16) return W4A16_EUNSUPPORTED;
     const bool any = p.o_row_ptr || p.o_col || p.o_val;
     if (any && !(p.o_row_ptr && p.o_col && p.o_val)) return W4A16_EINVAL;  // all or none
     if (any && ((reinterpret_cast<uintptr_t>(p.o_row_ptr) & 3u) ||
@@ -255,8 +256,8 @@ int check_problems(const w4a16_problem *problems, int count) {
 }
 
 w4a16::GemmDesc desc_of(const w4a16_problem &p) {
-  return {p.X,      p.Wq,     p.scales,      p.zeros, p.s,    p.Y, (int)p.M, (int)p.N,
-          (int)p.K, p.o_row_ptr, p.o_col, p.o_val};
+  return {p.X,      p.Wq,        p.scales, p.zeros, p.s,  p.Y, (int)p.M, (int)p.N,
+          (int)p.K, p.o_row_ptr, p.o_col,  p.o_val, p.dtype == W4A16_DTYPE_BF16};
 }
 
 // The tiled-path problems of a grouped call, in call order, in launches of up
@@ -267,8 +268,11 @@ std::vector<std::vector<w4a16::GemmDesc>> tiled_batches(const w4a16_problem *pro
   for (int i = 0; i < count; ++i) {
     const w4a16_problem &p = problems[i];
     if (p.M == 0 || w4a16_select_path(p.M, p.N, p.K) != W4A16_PATH_TILED) continue;
-    if (out.empty() || out.back().size() == cap) out.emplace_back();
-    out.back().push_back(desc_of(p));
+    const w4a16::GemmDesc d = desc_of(p);
+    // a launch is one kernel instance: one activation type
+    if (out.empty() || out.back().size() == cap || out.back().back().bf16 != d.bf16)
+      out.emplace_back();
+    out.back().push_back(d);
   }
   return out;
 }

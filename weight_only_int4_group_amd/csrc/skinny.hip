@@ -86,6 +86,60 @@ __device__ __forceinline__ half8 decode_word9(uint32_t w, uint32_t m_lo, uint32_
   return r;
 }
 
+// bf16 operands: eight codes of one word -> the exact bf16 values 128 + q_j,
+// j = 0..7, in seven ALU ops (the same slot-to-column order as above).  The
+// zero point is taken off after the product: sum_k a_k (q_k - z) =
+// sum_k a_k (128 + q_k) - (128 + z) sum_k a_k, with sum_k a_k staged per group.
+__device__ __forceinline__ u32x4 decode_word_bf16(uint32_t w) {
+  const uint32_t m = 0x000F000Fu;
+  u32x4 r = {and_or(w, m, kMagicBF), and_or(w >> 4, m, kMagicBF), and_or(w >> 8, m, kMagicBF),
+             and_or(w >> 12, m, kMagicBF)};
+  return r;
+}
+
+// X * s of 8 consecutive columns, rounded once to the activation type (the
+// exact product of a bf16 and an fp16 fits an fp32, so bf16 rounds once too),
+// and the fp32 sum of the 8 rounded values (bf16 only).
+template <bool kBF>
+__device__ __forceinline__ u32x4 scale_x8(u32x4 xw, const _Float16 *s8, float &sum) {
+  if (!kBF) {
+    half8 v = __builtin_bit_cast(half8, xw);
+    if (s8) v = v * load_half8(s8);
+    return __builtin_bit_cast(u32x4, v);
+  }
+  half8 sv;
+  if (s8) {
+    sv = load_half8(s8);
+  } else {
+    const _Float16 one = (_Float16)1.0f;
+    sv = (half8){one, one, one, one, one, one, one, one};
+  }
+  u32x4 out;
+  sum = 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float lo = bf16_to_f32((uint16_t)xw[q]) * (float)sv[2 * q];
+    const float hi = bf16_to_f32((uint16_t)(xw[q] >> 16)) * (float)sv[2 * q + 1];
+    const uint16_t l16 = f32_to_bf16(lo), h16 = f32_to_bf16(hi);
+    out[q] = (uint32_t)l16 | ((uint32_t)h16 << 16);
+    sum += bf16_to_f32(l16) + bf16_to_f32(h16);
+  }
+  return out;
+}
+
+// Sum over the 16 lanes of a lane's 16-lane segment (one group of one row when
+// the segment stages its 128 columns), in a fixed order.
+__device__ __forceinline__ float segment_sum16(float v) {
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+__device__ __forceinline__ float x_value(const _Float16 *X, size_t i, bool bf) {
+  const uint16_t h = __builtin_bit_cast(uint16_t, X[i]);
+  return bf ? bf16_to_f32(h) : (float)X[i];
+}
+
 // The problem a workgroup works on is the same for all its lanes; say so, so
 // that its pointers and sizes live in scalar registers.
 template <typename T>
@@ -133,6 +187,7 @@ __device__ __forceinline__ Problem find_problem(const ProblemSet &ps) {
 // stored order, of X[4c + v][col_e] * val_e (rows past M read row M - 1 and
 // are not stored).  Two entries' loads are issued at a time (more raise the
 // register count past what six waves per SIMD allow).
+template <bool kBF>
 __device__ __forceinline__ float4v outlier_terms(const Problem &P, int e0, int e1, int c) {
   constexpr int kBatch = 2;
   float4v o = {0.f, 0.f, 0.f, 0.f};
@@ -150,7 +205,7 @@ __device__ __forceinline__ float4v outlier_terms(const Problem &P, int e0, int e
     for (int u = 0; u < kBatch; ++u)
 #pragma unroll
       for (int v = 0; v < 4; ++v)
-        x[u][v] = (float)P.X[(size_t)min(4 * c + v, P.M - 1) * P.K + col[u]];
+        x[u][v] = x_value(P.X, (size_t)min(4 * c + v, P.M - 1) * P.K + col[u], kBF);
 #pragma unroll
     for (int u = 0; u < kBatch; ++u)
 #pragma unroll
@@ -177,18 +232,27 @@ __device__ __forceinline__ int2 outlier_range(const Problem &P, int b, bool has_
 // wave's groups.  With S waves per row block the partial sums are added in
 // the fixed order ks = 0, 1, ..., S - 1.  Every wave of the workgroup calls
 // this (it may synchronise the workgroup).
-template <int kWaves, bool kOut>
+// One output, rounded once to the activation type.
+template <bool kBF>
+__device__ __forceinline__ void store_y(_Float16 *Y, size_t i, float v) {
+  if (kBF)
+    reinterpret_cast<uint16_t *>(Y)[i] = f32_to_bf16(v);
+  else
+    Y[i] = (_Float16)v;
+}
+
+template <int kWaves, bool kOut, bool kBF>
 __device__ __forceinline__ void store_rows(const Problem &P, float4v acc, int b, bool has_rows,
                                            int wave, int ks, int c, int r,
                                            float (*red)[16][17], int2 orange) {
   const int M = P.M, N = P.N, S = P.split;
   if (S == 1) {
     if (has_rows) {
-      if (kOut) acc += outlier_terms(P, orange.x, orange.y, c);
+      if (kOut) acc += outlier_terms<kBF>(P, orange.x, orange.y, c);
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int m = 4 * c + v;
-        if (m < M) P.Y[(size_t)m * N + (size_t)b * kTileRows + r] = (_Float16)acc[v];
+        if (m < M) store_y<kBF>(P.Y, (size_t)m * N + (size_t)b * kTileRows + r, acc[v]);
       }
     }
   } else {
@@ -197,7 +261,7 @@ __device__ __forceinline__ void store_rows(const Problem &P, float4v acc, int b,
     __syncthreads();
     if (ks == 0 && has_rows) {
       float4v o = {0.f, 0.f, 0.f, 0.f};
-      if (kOut) o = outlier_terms(P, orange.x, orange.y, c);
+      if (kOut) o = outlier_terms<kBF>(P, orange.x, orange.y, c);
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int m = 4 * c + v;
@@ -205,14 +269,14 @@ __device__ __forceinline__ void store_rows(const Problem &P, float4v acc, int b,
           float sum = 0.f;
           for (int w = 0; w < S; ++w) sum += red[wave + w][m][r];
           if (kOut) sum += o[v];
-          P.Y[(size_t)m * N + (size_t)b * kTileRows + r] = (_Float16)sum;
+          store_y<kBF>(P.Y, (size_t)m * N + (size_t)b * kTileRows + r, sum);
         }
       }
     }
   }
 }
 
-template <int kGW, int kWaves, int kDepth, bool kOut>
+template <int kGW, int kWaves, int kDepth, bool kOut, bool kBF>
 __global__ __launch_bounds__(kWaves * 64) void skinny_kernel(ProblemSet ps) {
   // X * s, then (after the last use of X) the split-K reduction
   extern __shared__ __attribute__((aligned(16))) _Float16 xs[];
@@ -290,17 +354,28 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_kernel(ProblemSet ps) {
 
   // stage X * s for rows 0..M-1; lanes of rows m >= M read row M - 1 (rows of
   // the A operand only reach the same rows of D, and those are not stored)
+  // (bf16: also each group's sum of X * s per row, gsum[m][g], after the rows;
+  // a 16-lane segment stages exactly one group of one row)
+  float *gsum = reinterpret_cast<float *>(xs + M * (K + kLdsPad));
   {
     const int ldx = K + kLdsPad, k8 = K / 8;
     for (int idx = threadIdx.x; idx < M * k8; idx += kWaves * 64) {
       const int m = idx / k8, kk = (idx - m * k8) * 8;
-      half8 v = load_half8(P.X + (size_t)m * K + kk);
-      if (P.s) v = v * load_half8(P.s + kk);
-      *reinterpret_cast<half8 *>(&xs[m * ldx + kk]) = v;
+      float part = 0.f;
+      const u32x4 v = scale_x8<kBF>(*reinterpret_cast<const u32x4 *>(P.X + (size_t)m * K + kk),
+                                    P.s ? P.s + kk : nullptr, part);
+      *reinterpret_cast<u32x4 *>(&xs[m * ldx + kk]) = v;
+      if (kBF) {
+        part = segment_sum16(part);
+        if ((idx & 15) == 0) gsum[m * G + kk / kGroup] = part;
+      }
     }
     __syncthreads();
   }
   const _Float16 *xrow = xs + min(r, M - 1) * (K + kLdsPad) + 8 * c;
+  int gs_row[4];  // bf16: rows 4c + v of gsum (rows past M read row M - 1)
+#pragma unroll
+  for (int v = 0; v < 4; ++v) gs_row[v] = min(4 * c + v, M - 1) * G;
 
   const uint32_t m_lo = 0x000F000Fu, m_hi = 0x00F000F0u, magic = kMagic2;
   float4v acc = {0.f, 0.f, 0.f, 0.f};
@@ -323,17 +398,27 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_kernel(ProblemSet ps) {
     for (int i = 0; i < kGW; ++i) {
       const int g = g0 + i;
       if (g < ge) {
-        half8 a[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) a[t] = *reinterpret_cast<const half8 *>(xrow + g * kGroup + 32 * t);
         const _Float16 zp = cz[i >> 1][i & 1], sc = cs[i >> 1][i & 1];
-        const _Float16 blo = (_Float16)1024.0f + zp, bhi = (_Float16)64.0f + zp;
-        const half2v bias_lo = {blo, blo}, bias_hi = {bhi, bhi};
         float4v tmp = {0.f, 0.f, 0.f, 0.f};
+        if (kBF) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-          tmp = mfma16(a[t], decode_word9(cur[i][t], m_lo, m_hi, magic, bias_lo, bias_hi), tmp);
-        acc += tmp * (float)sc;
+          for (int t = 0; t < 4; ++t)
+            tmp = mfma16_bf16(*reinterpret_cast<const u32x4 *>(xrow + g * kGroup + 32 * t),
+                              decode_word_bf16(cur[i][t]), tmp);
+          const float zb = 128.0f + (float)zp;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[v] += (tmp[v] - zb * gsum[gs_row[v] + g]) * (float)sc;
+        } else {
+          half8 a[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) a[t] = *reinterpret_cast<const half8 *>(xrow + g * kGroup + 32 * t);
+          const _Float16 blo = (_Float16)1024.0f + zp, bhi = (_Float16)64.0f + zp;
+          const half2v bias_lo = {blo, blo}, bias_hi = {bhi, bhi};
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            tmp = mfma16(a[t], decode_word9(cur[i][t], m_lo, m_hi, magic, bias_lo, bias_hi), tmp);
+          acc += tmp * (float)sc;
+        }
       }
     }
   };
@@ -343,13 +428,13 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_kernel(ProblemSet ps) {
   }
 
   if (S > 1) __syncthreads();  // every wave is done with X * s: its LDS takes the partial sums
-  store_rows<kWaves, kOut>(P, acc, b, has_rows, wave, ks, c, r,
-                           reinterpret_cast<float (*)[16][17]>(xs), orange);
+  store_rows<kWaves, kOut, kBF>(P, acc, b, has_rows, wave, ks, c, r,
+                                reinterpret_cast<float (*)[16][17]>(xs), orange);
 }
 
 // Windowed variant: X * s staged one window of S chunks at a time (see the
 // header).  kSlots bounds the 8-column pieces of a window each thread stages.
-template <int kGW, int kWaves, int kDepth, int kSlots, bool kOut>
+template <int kGW, int kWaves, int kDepth, int kSlots, bool kOut, bool kBF>
 __global__ __launch_bounds__(kWaves * 64) void skinny_window_kernel(ProblemSet ps) {
   extern __shared__ __attribute__((aligned(16))) _Float16 xs[];
   __shared__ float red[kWaves][16][17];
@@ -433,11 +518,34 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_window_kernel(ProblemSet p
           half8, __builtin_amdgcn_raw_buffer_load_b128(xrs, m < M ? koff + 2 * m * K : 2 * M * K, 0, 0));
     }
   };
+  // bf16: each window group's sum of X * s per row, wsum[m][window group],
+  // after the window's rows (a 16-lane segment stages one group of one row)
+  const int wgroups = S * kGW;
+  float *wsum = reinterpret_cast<float *>(xs + M * ldx);
   auto store_window = [&]() {
 #pragma unroll
     for (int i = 0; i < kSlots; ++i) {
       const int m = r0 + i * rstep;
-      if (m < M) *reinterpret_cast<half8 *>(&xs[m * ldx + cs * 8]) = xr[i] * sv;
+      if (!kBF) {
+        if (m < M) *reinterpret_cast<half8 *>(&xs[m * ldx + cs * 8]) = xr[i] * sv;
+      } else {
+        float part = 0.f;
+        u32x4 out;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t xw = __builtin_bit_cast(u32x4, xr[i])[q];
+          const float lo = bf16_to_f32((uint16_t)xw) * (float)sv[2 * q];
+          const float hi = bf16_to_f32((uint16_t)(xw >> 16)) * (float)sv[2 * q + 1];
+          const uint16_t l16 = f32_to_bf16(lo), h16 = f32_to_bf16(hi);
+          out[q] = (uint32_t)l16 | ((uint32_t)h16 << 16);
+          part += bf16_to_f32(l16) + bf16_to_f32(h16);
+        }
+        part = segment_sum16(part);  // all 16 lanes of the segment share m
+        if (m < M) {
+          *reinterpret_cast<u32x4 *>(&xs[m * ldx + cs * 8]) = out;
+          if ((cs & 15) == 0) wsum[m * wgroups + cs / 16] = part;
+        }
+      }
     }
   };
 
@@ -454,6 +562,9 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_window_kernel(ProblemSet p
 
   // rows m >= M of the A operand only feed rows of D that are not stored
   const _Float16 *xrow = xs + min(r, M - 1) * ldx + ks * kGW * kGroup + 8 * c;
+  int ws_row[4];  // bf16: rows 4c + v of wsum at this wave's chunk
+#pragma unroll
+  for (int v = 0; v < 4; ++v) ws_row[v] = min(4 * c + v, M - 1) * wgroups + ks * kGW;
   const uint32_t m_lo = 0x000F000Fu, m_hi = 0x00F000F0u, magic = kMagic2;
   float4v acc = {0.f, 0.f, 0.f, 0.f};
   // Issue order per step: this wave's next chunk, then (after the window
@@ -487,14 +598,24 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_window_kernel(ProblemSet p
       for (int i = 0; i < kGW; ++i) {
         if (g0 + i < G) {
           const _Float16 zp = cz2[i >> 1][i & 1], sc = cs2[i >> 1][i & 1];
-          const _Float16 blo = (_Float16)1024.0f + zp, bhi = (_Float16)64.0f + zp;
-          const half2v bias_lo = {blo, blo}, bias_hi = {bhi, bhi};
           float4v tmp = {0.f, 0.f, 0.f, 0.f};
+          if (kBF) {
 #pragma unroll
-          for (int t = 0; t < 4; ++t)
-            tmp = mfma16(*reinterpret_cast<const half8 *>(xrow + i * kGroup + 32 * t),
-                         decode_word9(cur[i][t], m_lo, m_hi, magic, bias_lo, bias_hi), tmp);
-          acc += tmp * (float)sc;
+            for (int t = 0; t < 4; ++t)
+              tmp = mfma16_bf16(*reinterpret_cast<const u32x4 *>(xrow + i * kGroup + 32 * t),
+                                decode_word_bf16(cur[i][t]), tmp);
+            const float zb = 128.0f + (float)zp;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[v] += (tmp[v] - zb * wsum[ws_row[v] + i]) * (float)sc;
+          } else {
+            const _Float16 blo = (_Float16)1024.0f + zp, bhi = (_Float16)64.0f + zp;
+            const half2v bias_lo = {blo, blo}, bias_hi = {bhi, bhi};
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+              tmp = mfma16(*reinterpret_cast<const half8 *>(xrow + i * kGroup + 32 * t),
+                           decode_word9(cur[i][t], m_lo, m_hi, magic, bias_lo, bias_hi), tmp);
+            acc += tmp * (float)sc;
+          }
         }
       }
     }
@@ -503,7 +624,7 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_window_kernel(ProblemSet p
     lds_barrier();
     load_window(j + 2);
   }
-  store_rows<kWaves, kOut>(P, acc, b, has_rows, wave, ks, c, r, red, orange);
+  store_rows<kWaves, kOut, kBF>(P, acc, b, has_rows, wave, ks, c, r, red, orange);
 }
 
 constexpr size_t kMaxStageBytes = 96 * 1024;
@@ -536,8 +657,9 @@ constexpr size_t kMaxWindowBytes = W4A16_SKINNY_WINDOW_KB * 1024;  // 72 KB: two
 constexpr int kWindowSlots = W4A16_SKINNY_WINDOW_SLOTS;  // staged 8-column pieces per thread
 // LDS bytes of the whole-row kernel: X * s of one problem, at least the
 // reduction's partial sums (which reuse it).
-size_t stage_bytes(int M, int K) {
-  const size_t x = (size_t)M * (K + kLdsPad) * sizeof(_Float16);
+size_t stage_bytes(int M, int K, bool bf16) {
+  const size_t x = (size_t)M * (K + kLdsPad) * sizeof(_Float16) +
+                   (bf16 ? (size_t)M * (K / kGroup) * sizeof(float) : 0);
   const size_t red = (size_t)kWaves * 16 * 17 * sizeof(float);
   return x > red ? x : red;
 }
@@ -546,8 +668,9 @@ constexpr int kTargetWaves = 2048;     // enough waves in flight to cover HBM la
 constexpr int kMaxGroupsPerWave = 32;  // longer rows are split across waves
 
 // LDS bytes of one window of S chunks, M rows.
-size_t window_bytes(int M, int S) {
-  return (size_t)M * (S * kChunk * kGroup + kLdsPad) * sizeof(_Float16);
+size_t window_bytes(int M, int S, bool bf16) {
+  return (size_t)M * (S * kChunk * kGroup + kLdsPad) * sizeof(_Float16) +
+         (bf16 ? (size_t)M * S * kChunk * sizeof(float) : 0);
 }
 
 // 8-column pieces of a window each thread stages (0: the window is wider than
@@ -602,7 +725,7 @@ hipError_t launch_group(const GemmDesc *const *d, int count, bool window, hipStr
     while (split < kWaves && (G + split - 1) / split > kMaxGroupsPerWave) split *= 2;
     while (split > 1 && (G + kChunk - 1) / kChunk < split) split /= 2;  // a chunk per wave
     if (window)  // a window of split chunks must fit in LDS and in the staging registers
-      while (split > 1 && (window_bytes(q.M, split) > kMaxWindowBytes ||
+      while (split > 1 && (window_bytes(q.M, split, q.bf16) > kMaxWindowBytes ||
                            window_slots(q.M, split) < 1 || window_slots(q.M, split) > kWindowSlots))
         split /= 2;
     p.X = static_cast<const _Float16 *>(q.X);
@@ -622,23 +745,39 @@ hipError_t launch_group(const GemmDesc *const *d, int count, bool window, hipStr
     p.block0 = blocks;
     const int rb_per_wg = kWaves / split;
     blocks += (NB + rb_per_wg - 1) / rb_per_wg;
-    const size_t need = window ? window_bytes(q.M, split) : stage_bytes(q.M, q.K);
+    const size_t need = window ? window_bytes(q.M, split, q.bf16) : stage_bytes(q.M, q.K, q.bf16);
     lds = need > lds ? need : lds;
   }
   ps.count = count;
   const dim3 grid(blocks), threads(kWaves * 64);
-  if (window && out)
-    hipLaunchKernelGGL((skinny_window_kernel<kChunk, kWaves, kDepth, kWindowSlots, true>), grid,
-                       threads, lds, stream, ps);
-  else if (window)
-    hipLaunchKernelGGL((skinny_window_kernel<kChunk, kWaves, kDepth, kWindowSlots, false>), grid,
-                       threads, lds, stream, ps);
-  else if (out)
-    hipLaunchKernelGGL((skinny_kernel<kChunk, kWaves, kDepth, true>), grid, threads, lds, stream,
-                       ps);
-  else
-    hipLaunchKernelGGL((skinny_kernel<kChunk, kWaves, kDepth, false>), grid, threads, lds, stream,
-                       ps);
+  const bool bf = d[0]->bf16;  // one activation type per launch
+  if (window) {
+    if (bf && out)
+      hipLaunchKernelGGL((skinny_window_kernel<kChunk, kWaves, kDepth, kWindowSlots, true, true>),
+                         grid, threads, lds, stream, ps);
+    else if (bf)
+      hipLaunchKernelGGL((skinny_window_kernel<kChunk, kWaves, kDepth, kWindowSlots, false, true>),
+                         grid, threads, lds, stream, ps);
+    else if (out)
+      hipLaunchKernelGGL((skinny_window_kernel<kChunk, kWaves, kDepth, kWindowSlots, true, false>),
+                         grid, threads, lds, stream, ps);
+    else
+      hipLaunchKernelGGL((skinny_window_kernel<kChunk, kWaves, kDepth, kWindowSlots, false, false>),
+                         grid, threads, lds, stream, ps);
+  } else {
+    if (bf && out)
+      hipLaunchKernelGGL((skinny_kernel<kChunk, kWaves, kDepth, true, true>), grid, threads, lds,
+                         stream, ps);
+    else if (bf)
+      hipLaunchKernelGGL((skinny_kernel<kChunk, kWaves, kDepth, false, true>), grid, threads, lds,
+                         stream, ps);
+    else if (out)
+      hipLaunchKernelGGL((skinny_kernel<kChunk, kWaves, kDepth, true, false>), grid, threads, lds,
+                         stream, ps);
+    else
+      hipLaunchKernelGGL((skinny_kernel<kChunk, kWaves, kDepth, false, false>), grid, threads, lds,
+                         stream, ps);
+  }
   return hipGetLastError();
 }
 
@@ -651,22 +790,28 @@ hipError_t launch_skinny_set(const GemmDesc *d, int count, hipStream_t stream,
   // not fit: one launch over all problems beats a second, smaller one.  Like
   // the split factor, the choice depends on all problems of the call, so a
   // problem's bits can differ between a grouped and a single call (both stay
-  // within rounding of the exact result; each call is reproducible).
-  const GemmDesc *whole[kMaxProblems], *windowed[kMaxProblems];
-  int nwhole = 0, nwin = 0;
-  bool any = false;
-  for (int i = 0; i < count; ++i) any |= stage_bytes(d[i].M, d[i].K) > kMaxStageBytes;
-  for (int i = 0; i < count; ++i) {
-    const bool fits = stage_bytes(d[i].M, d[i].K) <= kMaxStageBytes;
-    const bool win = force_window || kWindowMode == 2 || (kWindowMode == 1 && !fits) ||
-                     (kWindowMode == 3 && any);
-    if (win)
-      windowed[nwin++] = d + i;
-    else
-      whole[nwhole++] = d + i;
+  // within rounding of the exact result; each call is reproducible).  fp16 and
+  // bf16 problems go in separate launches (one kernel instance each).
+  hipError_t err = hipSuccess;
+  for (int bf = 0; bf < 2 && err == hipSuccess; ++bf) {
+    const GemmDesc *whole[kMaxProblems], *windowed[kMaxProblems];
+    int nwhole = 0, nwin = 0;
+    bool any = false;
+    for (int i = 0; i < count; ++i)
+      if (d[i].bf16 == (bf == 1)) any |= stage_bytes(d[i].M, d[i].K, d[i].bf16) > kMaxStageBytes;
+    for (int i = 0; i < count; ++i) {
+      if (d[i].bf16 != (bf == 1)) continue;
+      const bool fits = stage_bytes(d[i].M, d[i].K, d[i].bf16) <= kMaxStageBytes;
+      const bool win = force_window || kWindowMode == 2 || (kWindowMode == 1 && !fits) ||
+                       (kWindowMode == 3 && any);
+      if (win)
+        windowed[nwin++] = d + i;
+      else
+        whole[nwhole++] = d + i;
+    }
+    err = launch_group(windowed, nwin, true, stream);
+    if (err == hipSuccess) err = launch_group(whole, nwhole, false, stream);
   }
-  hipError_t err = launch_group(windowed, nwin, true, stream);
-  if (err == hipSuccess) err = launch_group(whole, nwhole, false, stream);
   return err;
 }
 

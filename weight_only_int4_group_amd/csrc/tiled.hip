@@ -67,6 +67,23 @@ __device__ __forceinline__ half8 dequant_word(uint32_t w, half2v bias_lo, half2v
   return r;
 }
 
+// bf16 activations: eight codes -> bf16((q_j - z) * scale), each rounded once.
+// and_or builds the exact bf16 128 + q (see the streaming kernel); as fp32 it
+// is one shift or mask away, and one FMA with the fp32 scale, minus
+// (128 + z) * scale, leaves (q - z) * scale before the bf16 rounding.
+__device__ __forceinline__ u32x4 dequant_word_bf16(uint32_t w, float scale, float zb) {
+  const uint32_t m = 0x000F000Fu;
+  u32x4 r;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t x = and_or(w >> (4 * p), m, kMagicBF);
+    const float lo = __builtin_fmaf(__builtin_bit_cast(float, x << 16), scale, -zb);
+    const float hi = __builtin_fmaf(__builtin_bit_cast(float, x & 0xFFFF0000u), scale, -zb);
+    r[p] = (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+  }
+  return r;
+}
+
 constexpr int kMaxTiled = 8;  // problems per launch
 
 struct TiledProblem {
@@ -83,6 +100,7 @@ struct TiledProblem {
   int rblock0;      // first workgroup of this problem in the reduction launch
   const int32_t *orp, *ocol;  // fp16 outliers, row-compressed (null: none)
   const _Float16 *oval;
+  int bf16;                   // X and Y are bf16 (one value per launch)
 };
 
 struct TiledSet {
@@ -126,12 +144,13 @@ __device__ __forceinline__ TiledProblem find_tiled(const TiledSet &ts, int block
   P.orp = uniform_ptr(q.orp);
   P.ocol = uniform_ptr(q.ocol);
   P.oval = uniform_ptr(q.oval);
+  P.bf16 = uniform_int(q.bf16);
   return P;
 }
 
 // Two waves per SIMD: with one, the waits on LDS and the barriers are not
 // hidden and MFMA throughput roughly halves (measured on the 70B shapes).
-template <int WM, int WN, int TM, int TN, bool OUT>
+template <int WM, int WN, int TM, int TN, bool OUT, bool BF>
 __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void tiled_kernel(
     TiledSet ts) {
   constexpr int THREADS = WM * WN * 64;
@@ -196,8 +215,19 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
   auto store_a = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < A_PER_T; ++i) {
-      const half8 v = areg[i] * sreg;
-      *reinterpret_cast<half8 *>(&As[buf][(a_row + i * ROWS_PER_PASS) * kLdsStride + a_col]) = v;
+      u32x4 v;
+      if (BF) {  // bf16 X times fp16 s: exact in fp32, rounded once to bf16
+        const u32x4 xw = __builtin_bit_cast(u32x4, areg[i]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float lo = bf16_to_f32((uint16_t)xw[q]) * (float)sreg[2 * q];
+          const float hi = bf16_to_f32((uint16_t)(xw[q] >> 16)) * (float)sreg[2 * q + 1];
+          v[q] = (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+        }
+      } else {
+        v = __builtin_bit_cast(u32x4, areg[i] * sreg);
+      }
+      *reinterpret_cast<u32x4 *>(&As[buf][(a_row + i * ROWS_PER_PASS) * kLdsStride + a_col]) = v;
     }
     if (OUT && has_out && a_row == 0) *reinterpret_cast<half8 *>(&Ss[OUT ? buf : 0][a_col]) = sreg;
   };
@@ -251,20 +281,36 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
     const _Float16 *abuf = As[buf] + (wm * TM * 16 + r) * kLdsStride + 8 * c;
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
-      half8 bop[TN];
+      if (BF) {
+        u32x4 bop[TN];
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const _Float16 z = __builtin_bit_cast(_Float16, (uint16_t)b.zp[j]);
-        const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)b.sc[j]);
-        const _Float16 blo = (_Float16)1024.0f + z, bhi = (_Float16)64.0f + z;
-        const half2v bias_lo = {blo, blo}, bias_hi = {bhi, bhi}, scale = {sv, sv};
-        bop[j] = dequant_word(b.code[j][tt], bias_lo, bias_hi, scale);
-      }
+        for (int j = 0; j < TN; ++j) {
+          const float z = (float)__builtin_bit_cast(_Float16, (uint16_t)b.zp[j]);
+          const float sv = (float)__builtin_bit_cast(_Float16, (uint16_t)b.sc[j]);
+          bop[j] = dequant_word_bf16(b.code[j][tt], sv, (128.0f + z) * sv);
+        }
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const half8 aop = *reinterpret_cast<const half8 *>(abuf + i * 16 * kLdsStride + 32 * tt);
+        for (int i = 0; i < TM; ++i) {
+          const u32x4 aop = *reinterpret_cast<const u32x4 *>(abuf + i * 16 * kLdsStride + 32 * tt);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = mfma16(aop, bop[j], acc[i][j]);
+          for (int j = 0; j < TN; ++j) acc[i][j] = mfma16_bf16(aop, bop[j], acc[i][j]);
+        }
+      } else {
+        half8 bop[TN];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const _Float16 z = __builtin_bit_cast(_Float16, (uint16_t)b.zp[j]);
+          const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)b.sc[j]);
+          const _Float16 blo = (_Float16)1024.0f + z, bhi = (_Float16)64.0f + z;
+          const half2v bias_lo = {blo, blo}, bias_hi = {bhi, bhi}, scale = {sv, sv};
+          bop[j] = dequant_word(b.code[j][tt], bias_lo, bias_hi, scale);
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const half8 aop = *reinterpret_cast<const half8 *>(abuf + i * 16 * kLdsStride + 32 * tt);
+#pragma unroll
+          for (int j = 0; j < TN; ++j) acc[i][j] = mfma16(aop, bop[j], acc[i][j]);
+        }
       }
     }
     // let the scheduler interleave the MFMAs with the dequantization and LDS
@@ -328,15 +374,18 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-          acc[i][j][v] += (float)xb[(i * 16 + v) * kLdsStride] * vs;
+        for (int v = 0; v < 4; ++v) {
+          const _Float16 xv = xb[(i * 16 + v) * kLdsStride];
+          acc[i][j][v] += (BF ? bf16_to_f32(__builtin_bit_cast(uint16_t, xv)) : (float)xv) * vs;
+        }
     } else {
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int m = min(m0 + (wm * TM + i) * 16 + 4 * c + v, M - 1);
-          acc[i][j][v] += (float)X[(size_t)m * K + col] * val;
+          const _Float16 xv = X[(size_t)m * K + col];
+          acc[i][j][v] += (BF ? bf16_to_f32(__builtin_bit_cast(uint16_t, xv)) : (float)xv) * val;
         }
     }
   };
@@ -425,6 +474,8 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
         if (m < M && n < N) {
           if (part)
             part[(size_t)m * N + n] = acc[i][j][v];
+          else if (BF)
+            reinterpret_cast<uint16_t *>(P.Y)[(size_t)m * N + n] = f32_to_bf16(acc[i][j][v]);
           else
             P.Y[(size_t)m * N + n] = (_Float16)acc[i][j][v];
         }
@@ -446,8 +497,15 @@ __global__ __launch_bounds__(kReduceThreads) void split_reduce_kernel(TiledSet t
   float4v acc = src[0];
   for (int k = 1; k < P.split; ++k) acc += src[(size_t)k * quads];
   typedef _Float16 half4 __attribute__((ext_vector_type(4)));
-  const half4 out = {(_Float16)acc[0], (_Float16)acc[1], (_Float16)acc[2], (_Float16)acc[3]};
-  reinterpret_cast<half4 *>(P.Y)[i] = out;
+  typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+  if (P.bf16) {
+    const u16x4 out = {f32_to_bf16(acc[0]), f32_to_bf16(acc[1]), f32_to_bf16(acc[2]),
+                       f32_to_bf16(acc[3])};
+    reinterpret_cast<u16x4 *>(P.Y)[i] = out;
+  } else {
+    const half4 out = {(_Float16)acc[0], (_Float16)acc[1], (_Float16)acc[2], (_Float16)acc[3]};
+    reinterpret_cast<half4 *>(P.Y)[i] = out;
+  }
 }
 
 #ifndef W4A16_TILED_SHAPE
@@ -530,6 +588,7 @@ hipError_t launch_tiled_set(const GemmDesc *d, int count, void *workspace, size_
     p.ocol = static_cast<const int32_t *>(d[i].o_col);
     p.oval = static_cast<const _Float16 *>(d[i].o_val);
     out |= d[i].o_row_ptr != nullptr;
+    p.bf16 = d[i].bf16;
     p.block0 = blocks;
     blocks += p.tiles * p.split;
     p.rblock0 = rblocks;
@@ -537,12 +596,18 @@ hipError_t launch_tiled_set(const GemmDesc *d, int count, void *workspace, size_
       rblocks += (int)(((long long)d[i].M * d[i].N / 4 + kReduceThreads - 1) / kReduceThreads);
   }
   ts.count = count;
-  if (out)
-    hipLaunchKernelGGL((tiled_kernel<kWM, kWN, kTM, kTN, true>), dim3(blocks),
-                       dim3(kWM * kWN * 64), 0, stream, ts);
+  const dim3 grid(blocks), threads(kWM * kWN * 64);
+  if (d[0].bf16 && out)  // one activation type per launch
+    hipLaunchKernelGGL((tiled_kernel<kWM, kWN, kTM, kTN, true, true>), grid, threads, 0, stream, ts);
+  else if (d[0].bf16)
+    hipLaunchKernelGGL((tiled_kernel<kWM, kWN, kTM, kTN, false, true>), grid, threads, 0, stream,
+                       ts);
+  else if (out)
+    hipLaunchKernelGGL((tiled_kernel<kWM, kWN, kTM, kTN, true, false>), grid, threads, 0, stream,
+                       ts);
   else
-    hipLaunchKernelGGL((tiled_kernel<kWM, kWN, kTM, kTN, false>), dim3(blocks),
-                       dim3(kWM * kWN * 64), 0, stream, ts);
+    hipLaunchKernelGGL((tiled_kernel<kWM, kWN, kTM, kTN, false, false>), grid, threads, 0, stream,
+                       ts);
   hipError_t err = hipGetLastError();
   if (err == hipSuccess && rblocks > 0) {
     hipLaunchKernelGGL(split_reduce_kernel, dim3(rblocks), dim3(kReduceThreads), 0, stream, ts);

@@ -75,4 +75,24 @@ __device__ __forceinline__ float4v mfma16(half8 a, half8 b, float4v c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// The same MFMA on bf16 operands (the operands' bits as four 32-bit words).
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4v mfma16_bf16(u32x4v a, u32x4v b, float4v c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// bf16 <-> fp32 on raw 16-bit patterns (bf16 is the top half of an fp32)
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __builtin_bit_cast(float, (uint32_t)h << 16);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {  // round to nearest even
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+// bf16 128.0 in both halves: OR-ing a 4-bit code q into the low mantissa bits
+// gives the exact bf16 value 128 + q
+constexpr uint32_t kMagicBF = 0x43004300u;
+
 }  // namespace w4a16

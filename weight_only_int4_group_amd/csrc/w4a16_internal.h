@@ -33,6 +33,7 @@ struct GemmDesc {
   int M, N, K;
   // optional fp16 outliers, row-compressed (all set or all null)
   const void *o_row_ptr = nullptr, *o_col = nullptr, *o_val = nullptr;
+  bool bf16 = false;  // X and Y are bf16 (else fp16)
 };
 
 // Streaming kernel for small M (decode and speculative verify): M <= 16.

@@ -6,7 +6,9 @@ path (``weight_only_int4_group_amd``) can both draw their inputs from it without
 sharing any of the method's code.
 """
 from .configs import CONFIGS, Config, Matrix, config_by_name
-from .synth import activations, awq_scales, weights, weight_rows
+from .synth import (activations, activations_bf16, awq_scales, bf16_bits_to_f64, to_bf16_bits,
+                    weights, weight_rows)
 
-__all__ = ["CONFIGS", "Config", "Matrix", "config_by_name", "activations", "awq_scales",
+__all__ = ["CONFIGS", "Config", "Matrix", "config_by_name", "activations", "activations_bf16",
+           "bf16_bits_to_f64", "to_bf16_bits", "awq_scales",
            "weights", "weight_rows"]

@@ -8,7 +8,7 @@ Recipe (all draws float32, then cast to fp16 once at the end):
     mhpq.cn notes (section 2.2, outlier handling) and the aiwing.uk chapter
     (section 22.3, AWQ: a small share of salient weights) talk about.
   * s[K]: LogNormal(mu=0, sigma=0.5) per input channel (AWQ scale), fp16.
-  * X[M][K]: N(0, 1).  For the prefill workload, round(0.01 * K) columns drawn
+  * X[M][K]: N(0, 1) (fp16, or bf16 bit patterns for the bf16 path).  For the prefill workload, round(0.01 * K) columns drawn
     uniformly without replacement are multiplied by 20 (activation outliers,
     aiwing.uk section 22.3, activation quantization paragraph).
 Every stream is ``default_rng([0, key, matrix_index, tensor_id, ...])`` so any
@@ -78,14 +78,35 @@ def awq_scales(key: int, mat: int, K: int) -> np.ndarray:
     return rng.lognormal(mean=0.0, sigma=0.5, size=K).astype(np.float32).astype(np.float16)
 
 
-def activations(key: int, mat: int, M: int, K: int, outliers: bool = False) -> np.ndarray:
-    """X[M][K] fp16 ~ N(0, 1); with ``outliers`` 1% of the columns are scaled by 20.
-
-    Row i does not depend on M, so the M=1 input is the first row of any larger batch.
-    """
+def _activations_f32(key: int, mat: int, M: int, K: int, outliers: bool) -> np.ndarray:
     # one sequential stream: the first rows are the same whatever M is
     x = _rng(key, mat, _T_X).standard_normal((M, K), dtype=np.float32)
     if outliers:
         cols = _rng(key, mat, _T_XCOLS).choice(K, size=int(round(0.01 * K)), replace=False)
         x[:, cols] *= np.float32(20.0)
-    return x.astype(np.float16)
+    return x
+
+
+def activations(key: int, mat: int, M: int, K: int, outliers: bool = False) -> np.ndarray:
+    """X[M][K] fp16 ~ N(0, 1); with ``outliers`` 1% of the columns are scaled by 20.
+
+    Row i does not depend on M, so the M=1 input is the first row of any larger batch.
+    """
+    return _activations_f32(key, mat, M, K, outliers).astype(np.float16)
+
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns (uint16), rounded to nearest, ties to even."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)
+
+
+def bf16_bits_to_f64(b: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> their exact float64 values."""
+    return (np.asarray(b, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def activations_bf16(key: int, mat: int, M: int, K: int, outliers: bool = False) -> np.ndarray:
+    """The same draws as ``activations``, rounded to bf16 instead: uint16 bit patterns."""
+    return to_bf16_bits(_activations_f32(key, mat, M, K, outliers))
