@@ -45,6 +45,9 @@ constant zero point 8 (an all-zero group: scale 0, codes 8).
 [discosf] sec.2.1 (one scale per output channel, or per tensor): the range of
 R3 is taken over the row or the whole tensor, and every group slot of the
 packed metadata repeats that scale and zero point.
+``gptq.quantize_gptq`` is the GPTQ alternative producer of aiwing.uk sec.22.3 (Hessian
+H = 2 X^T X from calibration activations, error compensation along each row); its
+readings Q1-Q5 are in that module.
 The outlier side path (``outliers``, [mhpq] sec.2.2) keeps the largest |W / s|
 in fp16 and quantizes the rest with those positions set to 0; its readings
 O1-O5 are in that module.
@@ -57,12 +60,12 @@ from .quantizer import (GRANULARITIES, GROUP, QMAX, SYM_QMAX, SYM_ZERO, NonFinit
 from .layout import (META_QUAD, TILE_BYTES, TILE_ROWS, meta_groups, meta_index, nibble_address,
                      pack_codes, pack_meta, unpack_codes, unpack_meta)
 from .matmul import dequantize, gemm
-from . import accounting, exact, outliers, spec
+from . import accounting, exact, gptq, outliers, spec
 
 __all__ = [
     "GRANULARITIES", "GROUP", "QMAX", "NonFiniteInput", "OracleError", "QuantResult", "ScaleOverflow",
     "quantize", "quantize_symmetric", "SYM_QMAX", "SYM_ZERO", "round_up_fp16", "META_QUAD", "TILE_BYTES", "TILE_ROWS", "meta_groups",
     "meta_index", "nibble_address",
     "pack_codes", "pack_meta", "unpack_codes", "unpack_meta", "dequantize", "gemm",
-    "accounting", "exact", "outliers", "spec",
+    "accounting", "exact", "gptq", "outliers", "spec",
 ]
