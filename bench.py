@@ -28,6 +28,7 @@ Printed JSON line:
                 line carries the same variant of the 70B layer;
   bf16          the headline layer (and, in the prefill line, the 70B layer) with bf16
                 activations and outputs on the same packed weights;
+  gptq          the GPTQ packer (offline) on an 8B q projection: seconds and fp64 rate;
   spec_verify   the accept / reject / draw step after a K = 4 verify pass over the
                 Llama-3 vocabulary (V = 128256), for 1 and 64 sequences per call;
   prefill       the 70B-shaped layer at M = 4096 (compute-bound): TFLOP/s
@@ -284,6 +285,27 @@ def spec_verify_line(torch, w4, B, K, V, steps=200, warmup=20, per=10):
             "frac_of_hbm_peak": round(call_bytes / kern / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def gptq_line(torch, w4, N=4096, K=4096, n=4096, reps=3):
+    """GPTQ quantize-and-pack of an 8B q projection (N x K, AWQ s) with n seeded
+    calibration rows: wall seconds per call (blocking, offline) and the fp64 work it
+    amounts to -- H = 2 X^T X (2 n K^2) and the compensation (about 2 N K^2: the
+    in-group sweeps plus the trailing products) -- against the fp64 peak."""
+    rng = np.random.default_rng(0)
+    W = torch.from_numpy((rng.standard_normal((N, K)) * 0.02).astype(np.float16)).to("cuda")
+    s = torch.from_numpy(rng.lognormal(0.0, 0.5, K).astype(np.float16)).to("cuda")
+    X = torch.from_numpy(rng.standard_normal((n, K)).astype(np.float16)).to("cuda")
+    w4.w4a16_quantize_pack_gptq(W, s, X)  # loads the solver libraries
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        w4.w4a16_quantize_pack_gptq(W, s, X)
+    sec = (time.perf_counter() - t0) / reps
+    flops = 2.0 * n * K * K + 2.0 * N * K * K
+    return {"workload": f"GPTQ pack of a {N}x{K} projection (AWQ s), {n} calibration rows",
+            "seconds_per_matrix": round(sec, 4), "fp64_TFLOP/s": round(flops / sec / 1e12, 2),
+            "frac_of_fp64_peak": round(flops / sec / 1e12 / 78.6, 4)}
+
+
 def ceilings(torch, reps=10):
     """Measured ceilings on this GPU, for context: a plain device-to-device copy, and
     the vendor dense fp16 GEMM (torch.matmul on contiguous fp16 operands) at the 70B
@@ -372,6 +394,7 @@ def main():
     ap.add_argument("--no-spec", action="store_true")
     ap.add_argument("--no-outliers", action="store_true")
     ap.add_argument("--no-bf16", action="store_true")
+    ap.add_argument("--no-gptq", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-run", action="store_true",
                     help="only the short fixed sequence used for counter collection")
@@ -539,6 +562,11 @@ def main():
                 "vs_plain_kernel_time": round(otot / tot_ms, 4)}
             del opool, omats
             torch.cuda.empty_cache()
+
+    if not args.no_gptq:
+        log("timing the GPTQ packer")
+        out["gptq"] = gptq_line(torch, w4)
+        torch.cuda.empty_cache()
 
     if not args.no_ceilings:
         log("measuring the copy and dense fp16 GEMM ceilings")

@@ -165,6 +165,29 @@ int w4a16_quantize_pack_outliers(const void *W, const void *s, int64_t N, int64_
                                  void *o_row_ptr, void *o_col, void *o_val, void *workspace,
                                  size_t workspace_bytes, void *stream);
 
+/* GPTQ-style quantize-and-pack ("Chapter 22: Advanced inference
+ * optimisation", aiwing.uk, section 22.3: minimise ||W X - W_hat X||_F^2 for
+ * calibration activations X, with H = 2 X X^T spreading each quantized
+ * weight's error over the rest of its row).  Same packed output as
+ * w4a16_quantize_pack (asymmetric grid, group 128, AWQ s optional).
+ *   X: fp16 [n_samples][K] calibration activations (device, 16-byte aligned);
+ *   the Hessian is H = 2 (X s)^T (X s) in fp64, plus damp * mean(diag H) on its
+ *   diagonal (damp >= 0, typically 0.01); columns are quantized in their
+ *   natural order; error compensation uses the upper Cholesky factor U of H^-1
+ *   (H^-1 = U^T U); each group's scale and zero point come from its current
+ *   (compensated) weights when the group starts, by the packer's rules.
+ * All arithmetic is fp64.  The Cholesky factorisations use rocSOLVER and the
+ * two large products rocBLAS, loaded on the first call: EUNSUPPORTED if they
+ * cannot be loaded.  EINVAL also when the damped Hessian is not positive
+ * definite.  Limits: K <= 65536, 1 <= n_samples <= 2^24, n_samples * K <= 2^32.
+ * workspace: caller-owned device memory of w4a16_gptq_workspace_size() bytes,
+ * 256-byte aligned (about 8 * (n_samples * K + K * K + N * K) bytes).
+ * Blocks until done; other errors as w4a16_quantize_pack. */
+int w4a16_gptq_workspace_size(int64_t N, int64_t K, int64_t n_samples, size_t *bytes);
+int w4a16_quantize_pack_gptq(const void *W, const void *s, int64_t N, int64_t K, const void *X,
+                             int64_t n_samples, double damp, void *Wq, void *scales, void *zeros,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
 /* Y[M][N] = X[M][K] . W_hat^T with W_hat[n][k] = (q - z) * scale * s[k].
  * X: fp16 [M][K]; Wq/scales/zeros: packed as above; s: fp16 [K] or NULL;
  * Y: fp16 [M][N] row-major, fully overwritten.  fp32 accumulation; X * s is

@@ -27,6 +27,7 @@ __all__ = [
     "w4a16_gemm_grouped", "GroupedCall", "w4a16_spec_verify",
     "w4a16_spec_verify_workspace_size", "SpecVerifyCall", "w4a16_quantize_pack_outliers",
     "w4a16_outlier_workspace_size", "page_outlier_count", "DTYPE_F16", "DTYPE_BF16",
+    "w4a16_quantize_pack_gptq",
 ]
 
 GROUP = 128
@@ -39,6 +40,7 @@ EXPORTED_SYMBOLS = ("w4a16_packed_sizes", "w4a16_quantize_pack", "w4a16_quantize
                     "w4a16_gemm",
                     "w4a16_gemm_path", "w4a16_gemm_grouped", "w4a16_gemm_grouped_ws",
                     "w4a16_gemm_workspace_size", "w4a16_outlier_workspace_size",
+                    "w4a16_gptq_workspace_size", "w4a16_quantize_pack_gptq",
                     "w4a16_quantize_pack_outliers", "w4a16_spec_verify",
                     "w4a16_spec_verify_workspace_size", "w4a16_select_path",
                     "w4a16_strerror", "w4a16_version")
@@ -87,6 +89,9 @@ def lib() -> ctypes.CDLL:
     L.w4a16_outlier_workspace_size.argtypes = [i64, i64, sz]
     L.w4a16_quantize_pack_outliers.argtypes = [vp, vp, i64, i64, ctypes.c_int, i64, vp, vp, vp,
                                                vp, vp, vp, vp, ctypes.c_size_t, vp]
+    L.w4a16_gptq_workspace_size.argtypes = [i64, i64, i64, sz]
+    L.w4a16_quantize_pack_gptq.argtypes = [vp, vp, i64, i64, vp, i64, ctypes.c_double, vp, vp, vp,
+                                           vp, ctypes.c_size_t, vp]
     L.w4a16_select_path.argtypes = [i64, i64, i64]
     L.w4a16_strerror.argtypes = [ctypes.c_int]
     L.w4a16_strerror.restype = ctypes.c_char_p
@@ -96,6 +101,7 @@ def lib() -> ctypes.CDLL:
                  "w4a16_gemm_grouped", "w4a16_gemm_grouped_ws", "w4a16_gemm_workspace_size",
                  "w4a16_spec_verify", "w4a16_spec_verify_workspace_size", "w4a16_select_path",
                  "w4a16_outlier_workspace_size", "w4a16_quantize_pack_outliers",
+                 "w4a16_gptq_workspace_size", "w4a16_quantize_pack_gptq",
                  "w4a16_version"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
@@ -239,6 +245,36 @@ def w4a16_quantize_pack_outliers(W, s=None, count: int | None = None,
         _dev_ptr(ws, "workspace", torch.uint8), ws.numel(), _stream_handle(dev))
     if rc:
         raise W4A16Error(rc, "w4a16_quantize_pack_outliers")
+    return pw
+
+
+def w4a16_quantize_pack_gptq(W, s, Xcal, damp: float = 0.01) -> PackedWeight:
+    """GPTQ quantize-and-pack of fp16 W[N][K] (AWQ s[K] or None) with fp16 calibration
+    activations Xcal[n][K]: the packed format of w4a16_quantize_pack."""
+    torch = _torch()
+    if W.dim() != 2 or Xcal.dim() != 2 or Xcal.shape[1] != W.shape[1]:
+        raise ValueError("W must be [N][K] and Xcal [n][K]")
+    N, K = W.shape
+    n = Xcal.shape[0]
+    wq_b, sc_b, z_b = w4a16_packed_sizes(N, K)
+    dev = W.device
+    pw = PackedWeight(torch.empty(wq_b, dtype=torch.uint8, device=dev),
+                      torch.empty(sc_b // 2, dtype=torch.float16, device=dev),
+                      torch.empty(z_b // 2, dtype=torch.float16, device=dev), N, K)
+    nb = ctypes.c_size_t()
+    rc = lib().w4a16_gptq_workspace_size(N, K, n, ctypes.byref(nb))
+    if rc:
+        raise W4A16Error(rc, "w4a16_gptq_workspace_size")
+    ws = torch.empty(nb.value, dtype=torch.uint8, device=dev)
+    rc = lib().w4a16_quantize_pack_gptq(
+        _dev_ptr(W, "W", torch.float16), _dev_ptr(s, "s", torch.float16, K), N, K,
+        _dev_ptr(Xcal, "Xcal", torch.float16), n, float(damp),
+        _dev_ptr(pw.wq, "wq", torch.uint8, wq_b),
+        _dev_ptr(pw.scales, "scales", torch.float16, sc_b // 2),
+        _dev_ptr(pw.zeros, "zeros", torch.float16, z_b // 2),
+        _dev_ptr(ws, "workspace", torch.uint8), ws.numel(), _stream_handle(dev))
+    if rc:
+        raise W4A16Error(rc, "w4a16_quantize_pack_gptq")
     return pw
 
 

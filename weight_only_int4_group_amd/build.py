@@ -13,7 +13,8 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_NAME = "libw4a16.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = ("api.hip", "pack.hip", "skinny.hip", "tiled.hip", "spec.hip", "outliers.hip")
+SOURCES = ("api.hip", "pack.hip", "skinny.hip", "tiled.hip", "spec.hip", "outliers.hip",
+           "gptq.hip")
 ARCH = "gfx950"
 
 
@@ -39,7 +40,7 @@ def build(verbose: bool = False) -> str:
     """Compile every source into LIB_PATH (always recompiles) and return the path."""
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
     tmp = LIB_PATH + f".tmp{os.getpid()}"
-    cmd = [hipcc(), *compile_flags(), *srcs, "-o", tmp]
+    cmd = [hipcc(), *compile_flags(), *srcs, "-ldl", "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

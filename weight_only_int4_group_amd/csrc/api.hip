@@ -125,6 +125,44 @@ int w4a16_quantize_pack_mode(const void *W, const void *s, int64_t N, int64_t K,
   return pack_and_check(W, s, N, K, nullptr, mode, Wq, scales, zeros, status, st);
 }
 
+static bool gptq_shape_ok(int64_t N, int64_t K, int64_t n) {
+  return check_shape(N, K) == W4A16_OK && n >= 1 && n <= (int64_t(1) << 24) &&
+         K <= 65536 && n * K <= (int64_t(1) << 32);
+}
+
+int w4a16_gptq_workspace_size(int64_t N, int64_t K, int64_t n_samples, size_t *bytes) {
+  if (!bytes || !gptq_shape_ok(N, K, n_samples)) return W4A16_EINVAL;
+  *bytes = w4a16::gptq_workspace_bytes((int)N, (int)K, n_samples);
+  return W4A16_OK;
+}
+
+int w4a16_quantize_pack_gptq(const void *W, const void *s, int64_t N, int64_t K, const void *X,
+                             int64_t n_samples, double damp, void *Wq, void *scales, void *zeros,
+                             void *workspace, size_t workspace_bytes, void *stream) {
+  if (!gptq_shape_ok(N, K, n_samples) || !(damp >= 0.0 && damp < 1e30)) return W4A16_EINVAL;
+  if (!W || !X || !Wq || !scales || !zeros || !workspace) return W4A16_EINVAL;
+  if (workspace_bytes < w4a16::gptq_workspace_bytes((int)N, (int)K, n_samples)) return W4A16_EINVAL;
+  if (!aligned16(W) || !aligned16(Wq) || !aligned16(scales) || !aligned16(zeros) ||
+      (s && !aligned16(s)) || !aligned16(X) || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return W4A16_EALIGN;
+  unsigned *status = nullptr;
+  int rc = status_word(&status);
+  if (rc) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (hipMemsetAsync(status, 0, sizeof(unsigned), st) != hipSuccess) return W4A16_EHIP;
+  const int g = w4a16::gptq_pack(W, s, (int)N, (int)K, X, n_samples, damp, Wq, scales, zeros,
+                                 workspace, status, st);
+  if (g == 1) return W4A16_EUNSUPPORTED;
+  if (g == 2) return W4A16_EINVAL;
+  if (g != 0) return W4A16_EHIP;
+  unsigned host = 0;
+  if (hipMemcpy(&host, status, sizeof(unsigned), hipMemcpyDeviceToHost) != hipSuccess)
+    return W4A16_EHIP;
+  if (host & w4a16::kPackNonFinite) return W4A16_ENONFINITE;
+  if (host & w4a16::kPackRange) return W4A16_ERANGE;
+  return W4A16_OK;
+}
+
 int w4a16_outlier_workspace_size(int64_t N, int64_t K, size_t *bytes) {
   if (!bytes) return W4A16_EINVAL;
   const int rc = check_shape(N, K);

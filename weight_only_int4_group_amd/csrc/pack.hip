@@ -35,25 +35,6 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// Smallest fp16 value >= v for finite v > 0, built from the binary16 grid:
-// below 2^-14 the grid step is 2^-24; in [2^e, 2^(e+1)) it is 2^(e-10).
-// Returns false when that value would exceed the largest finite fp16.
-__device__ bool fp16_ceil(double v, _Float16 *out) {
-  if (!(v <= 65504.0)) return false;
-  double step;
-  if (v < 0x1p-14) {
-    step = 0x1p-24;
-  } else {
-    int e;
-    (void)frexp(v, &e);          // v = m * 2^e, m in [0.5, 1): v in [2^(e-1), 2^e)
-    step = ldexp(1.0, e - 11);   // 2^((e-1) - 10)
-  }
-  const double h = ceil(v / step) * step;   // exact: step is a power of two
-  if (h > 65504.0) return false;
-  *out = (_Float16)h;                       // exact: h lies on the fp16 grid
-  return true;
-}
-
 __device__ __forceinline__ bool finite_h(_Float16 x) {
   const uint16_t b = __builtin_bit_cast(uint16_t, x);
   return (b & 0x7C00u) != 0x7C00u;

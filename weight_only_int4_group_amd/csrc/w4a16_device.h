@@ -95,4 +95,23 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {  // round to nearest 
 // gives the exact bf16 value 128 + q
 constexpr uint32_t kMagicBF = 0x43004300u;
 
+// Smallest fp16 value >= v for finite v > 0, built from the binary16 grid:
+// below 2^-14 the grid step is 2^-24; in [2^e, 2^(e+1)) it is 2^(e-10).
+// Returns false when that value would exceed the largest finite fp16.
+__device__ inline bool fp16_ceil(double v, _Float16 *out) {
+  if (!(v <= 65504.0)) return false;
+  double step;
+  if (v < 0x1p-14) {
+    step = 0x1p-24;
+  } else {
+    int e;
+    (void)frexp(v, &e);          // v = m * 2^e, m in [0.5, 1): v in [2^(e-1), 2^e)
+    step = ldexp(1.0, e - 11);   // 2^((e-1) - 10)
+  }
+  const double h = ceil(v / step) * step;   // exact: step is a power of two
+  if (h > 65504.0) return false;
+  *out = (_Float16)h;                       // exact: h lies on the fp16 grid
+  return true;
+}
+
 }  // namespace w4a16

@@ -26,6 +26,15 @@ int select_outliers(const void *W, const void *s, int N, int K, long long count,
                     int32_t *col, _Float16 *val, void *workspace, const uint8_t **mask,
                     hipStream_t stream);
 
+// GPTQ quantize-and-pack (validated by the caller; blocks until done).  0 on
+// success, 1 when rocBLAS / rocSOLVER cannot be loaded, 2 when the damped
+// Hessian is not positive definite, -1 on a HIP or library error; non-finite
+// inputs and scale overflow are flagged in *status as for launch_pack.
+size_t gptq_workspace_bytes(int N, int K, long long n);
+int gptq_pack(const void *W, const void *s, int N, int K, const void *X, long long n, double damp,
+              void *Wq, void *scales, void *zeros, void *workspace, unsigned *status,
+              hipStream_t stream);
+
 // One dequantize-matmul problem (validated by the caller).
 struct GemmDesc {
   const void *X, *Wq, *scales, *zeros, *s;
