@@ -41,6 +41,8 @@ The symmetric variant (``quantize_symmetric``, the signed -7..7 grid of [mhpq]
 sec.2.1) takes R2, R5, R7's ties, R8 and R9's errors as they are, with
 scale = max|W'| / 7 rounded up, signed codes rint(W' / scale) stored + 8 and a
 constant zero point 8 (an all-zero group: scale 0, codes 8).
+``quantize(..., bits=8)`` is the INT8 (W8A16) variant: codes 0..255 under the same
+readings, packed one byte per weight in 2048-byte tiles (``pack_codes8``).
 ``quantize(..., granularity="channel" | "tensor")`` are the coarser granularities of
 [discosf] sec.2.1 (one scale per output channel, or per tensor): the range of
 R3 is taken over the row or the whole tensor, and every group slot of the
@@ -57,8 +59,9 @@ rationals, integer special case); see tests/test_oracle_*.py.
 """
 from .quantizer import (GRANULARITIES, GROUP, QMAX, SYM_QMAX, SYM_ZERO, NonFiniteInput, OracleError,
                         QuantResult, ScaleOverflow, quantize, quantize_symmetric, round_up_fp16)
-from .layout import (META_QUAD, TILE_BYTES, TILE_ROWS, meta_groups, meta_index, nibble_address,
-                     pack_codes, pack_meta, unpack_codes, unpack_meta)
+from .layout import (META_QUAD, TILE_BYTES, TILE_BYTES8, TILE_ROWS, byte_address8, meta_groups,
+                     meta_index, nibble_address, pack_codes, pack_codes8, pack_meta, unpack_codes,
+                     unpack_codes8, unpack_meta)
 from .matmul import dequantize, gemm
 from . import accounting, exact, gptq, outliers, spec
 
@@ -67,5 +70,6 @@ __all__ = [
     "quantize", "quantize_symmetric", "SYM_QMAX", "SYM_ZERO", "round_up_fp16", "META_QUAD", "TILE_BYTES", "TILE_ROWS", "meta_groups",
     "meta_index", "nibble_address",
     "pack_codes", "pack_meta", "unpack_codes", "unpack_meta", "dequantize", "gemm",
+    "TILE_BYTES8", "byte_address8", "pack_codes8", "unpack_codes8",
     "accounting", "exact", "gptq", "outliers", "spec",
 ]

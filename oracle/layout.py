@@ -26,6 +26,12 @@ NB = N / 16 row blocks.
     of one 16-row block and 4 consecutive groups is one contiguous 128-byte
     run (a single 8-byte load per row fetches 4 groups), and the runs of one
     quad follow each other row block after row block.
+INT8 codes (the W8A16 variant, one byte per weight) use the same groups, row
+blocks and metadata, with 2048-byte tiles:
+  * tile (b, g) is at byte offset (g * NB + b) * 2048 of the code buffer;
+  * lane L = 16 * c + r owns the 32 bytes at byte 32 * L;
+  * its byte 8 * t + j holds the code of column 128 g + 32 t + 8 c + j
+    (t = 0..3, j = 0..7): increasing column order.
 TEST INFRASTRUCTURE: see the package docstring for who may import this.
 """
 from __future__ import annotations
@@ -34,6 +40,7 @@ import numpy as np
 
 TILE_ROWS = 16
 TILE_BYTES = 1024
+TILE_BYTES8 = 2048
 META_QUAD = 4
 _GROUP = 128
 
@@ -124,3 +131,38 @@ def unpack_meta(buf: np.ndarray, N: int, K: int) -> np.ndarray:
         raise ValueError("buffer size mismatch")
     nn, gg = np.meshgrid(np.arange(N), np.arange(G), indexing="ij")
     return buf[meta_index(nn.ravel(), gg.ravel(), N, K)].reshape(N, G)
+
+
+def byte_address8(n, k, N: int, K: int):
+    """Byte offset of the INT8 code of W[n][k].  Works on scalars or index arrays."""
+    _check(N, K)
+    n = np.asarray(n, dtype=np.int64)
+    k = np.asarray(k, dtype=np.int64)
+    NB = N // TILE_ROWS
+    b, r = n // TILE_ROWS, n % TILE_ROWS
+    g, kk = k // _GROUP, k % _GROUP
+    t, c, j = kk // 32, (kk % 32) // 8, kk % 8
+    return (g * NB + b) * TILE_BYTES8 + 32 * (16 * c + r) + 8 * t + j
+
+
+def pack_codes8(q: np.ndarray) -> np.ndarray:
+    """uint8 codes q[N][K] (0..255) -> packed buffer of N*K bytes."""
+    q = np.asarray(q)
+    N, K = q.shape
+    _check(N, K)
+    if q.dtype != np.uint8:
+        raise ValueError("codes must be uint8")
+    nn, kk = np.meshgrid(np.arange(N), np.arange(K), indexing="ij")
+    out = np.zeros(N * K, dtype=np.uint8)
+    out[byte_address8(nn.ravel(), kk.ravel(), N, K)] = q.ravel()
+    return out
+
+
+def unpack_codes8(buf: np.ndarray, N: int, K: int) -> np.ndarray:
+    """Packed INT8 buffer -> codes q[N][K]."""
+    _check(N, K)
+    buf = np.asarray(buf, dtype=np.uint8).ravel()
+    if buf.size != N * K:
+        raise ValueError("buffer size mismatch")
+    nn, kk = np.meshgrid(np.arange(N), np.arange(K), indexing="ij")
+    return buf[byte_address8(nn.ravel(), kk.ravel(), N, K)].reshape(N, K)

@@ -58,15 +58,22 @@ def round_up_fp16(v: np.ndarray) -> np.ndarray:
 GRANULARITIES = ("group", "channel", "tensor")
 
 
-def quantize(W: np.ndarray, s: np.ndarray | None = None, granularity: str = "group") -> QuantResult:
+def quantize(W: np.ndarray, s: np.ndarray | None = None, granularity: str = "group",
+             bits: int = 4) -> QuantResult:
     """Quantize fp16 ``W[N][K]`` (optionally divided by fp16 ``s[K]`` first) to INT4 groups.
 
     ``granularity`` (discosf sec.2.1: per-tensor, per-channel or per-group scales) picks
     the range a scale and zero point cover: each group of 128 (reading R2), each row
     (output channel), or the whole tensor.  The coarser ones keep the per-group storage:
-    every group of a row (or of the tensor) carries the same scale and zero point."""
+    every group of a row (or of the tensor) carries the same scale and zero point.
+
+    ``bits`` = 8 is the INT8 (W8A16) variant of the same readings: codes 0..255, so
+    scale = range / 255 (aiwing sec.22.3's table: INT8 at one byte per parameter)."""
     if granularity not in GRANULARITIES:
         raise ValueError(f"granularity must be one of {GRANULARITIES}")
+    if bits not in (4, 8):
+        raise ValueError("bits must be 4 or 8")
+    qmax = (1 << bits) - 1
     W = np.asarray(W)
     if W.dtype != np.float16 or W.ndim != 2:
         raise TypeError("W must be a 2-D float16 array")
@@ -101,18 +108,18 @@ def quantize(W: np.ndarray, s: np.ndarray | None = None, granularity: str = "gro
     mn = np.minimum(lo, 0.0)
     mx = np.maximum(hi, 0.0)
     rng = mx - mn
-    scale16 = round_up_fp16(rng / QMAX)
+    scale16 = round_up_fp16(rng / qmax)
     if not np.all(np.isfinite(scale16)):
         raise ScaleOverflow("group scale exceeds the fp16 range")
     scale = scale16.astype(np.float64)
 
     live = rng > 0   # an all-zero group keeps scale 0, zero point 0, codes 0 (R9)
     safe = np.where(live, scale, 1.0)
-    # Zero point: the integer nearest to -min/scale (R6); lies in 0..15 because scale >= range/15.
+    # Zero point: the integer nearest to -min/scale (R6); lies in 0..qmax because scale >= range/qmax.
     z = np.where(live, np.rint(-mn / safe), 0.0)
-    # Codes: rint (ties to even) of W'/scale, then shifted by z and clamped to 0..15 (R7).
+    # Codes: rint (ties to even) of W'/scale, then shifted by z and clamped to 0..qmax (R7).
     t = np.rint(Wg / safe[:, :, None]) + z[:, :, None]
-    q = np.where(live[:, :, None], np.clip(t, 0, QMAX), 0.0)
+    q = np.where(live[:, :, None], np.clip(t, 0, qmax), 0.0)
 
     return QuantResult(
         q=q.reshape(N, K).astype(np.uint8),
