@@ -55,9 +55,9 @@ POOL_BYTES = 1 << 30         # rotate weight copies over at least this much memo
 METRIC = "W4A16 dequant-GEMM: HBM TB/s @M=1, TFLOP/s @M=4096, % of roofline"
 
 
-def alg_bytes(M, N, K, awq):
+def alg_bytes(M, N, K, awq, bits=4):
     """Bytes the method must move: packed codes, fp16 scale + zero per group, s, X, Y."""
-    return N * K // 2 + 4 * N * K // 128 + (2 * K if awq else 0) + 2 * M * K + 2 * M * N
+    return N * K * bits // 8 + 4 * N * K // 128 + (2 * K if awq else 0) + 2 * M * K + 2 * M * N
 
 
 def kernel_source_sha(name):
@@ -124,10 +124,11 @@ def outlier_bytes(pw):
     return 4 * pw.o_row_ptr.numel() + 6 * pw.o_col.numel()
 
 
-def prepare_layer(cfg, M, torch, w4, workloads, copies_min_bytes=POOL_BYTES, outliers=False):
+def prepare_layer(cfg, M, torch, w4, workloads, copies_min_bytes=POOL_BYTES, outliers=False,
+                  int8=False):
     """Pack every matrix of a configuration once on the GPU (with the 0.1% fp16 outliers
-    when asked), and replicate the packed buffers into enough copies to cover
-    `copies_min_bytes`."""
+    when asked, or as INT8 codes), and replicate the packed buffers into enough copies to
+    cover `copies_min_bytes`."""
     mats = []
     for mi, mat in enumerate(cfg.matrices):
         W = workloads.weights(cfg.weight_key, mi, mat.N, mat.K, threads=16)
@@ -135,13 +136,17 @@ def prepare_layer(cfg, M, torch, w4, workloads, copies_min_bytes=POOL_BYTES, out
         Wd = torch.from_numpy(W).to("cuda")
         sd = None if s is None else torch.from_numpy(s).to("cuda")
         del W
-        pw = w4.w4a16_quantize_pack_outliers(Wd, sd) if outliers else w4.w4a16_quantize_pack(Wd, sd)
+        if outliers:
+            pw = w4.w4a16_quantize_pack_outliers(Wd, sd)
+        else:
+            pw = w4.w4a16_quantize_pack(Wd, sd, mode=w4.QUANT_ASYM8 if int8 else w4.QUANT_ASYM)
         del Wd
         X = torch.from_numpy(workloads.activations(cfg.weight_key, mi, M, mat.K,
                                                    outliers=cfg.act_outliers)).to("cuda")
         Y = torch.empty((M, mat.N), dtype=torch.float16, device="cuda")
         mats.append(dict(name=mat.name, N=mat.N, K=mat.K, pw=pw, s=sd, X=X, Y=Y,
-                         bytes=alg_bytes(M, mat.N, mat.K, sd is not None) + outlier_bytes(pw),
+                         bytes=alg_bytes(M, mat.N, mat.K, sd is not None, pw.wbits)
+                         + outlier_bytes(pw),
                          flops=2 * M * mat.N * mat.K))
     layer_w = sum(m["pw"].wq.numel() + 4 * m["pw"].scales.numel() + outlier_bytes(m["pw"])
                   for m in mats)
@@ -152,7 +157,7 @@ def prepare_layer(cfg, M, torch, w4, workloads, copies_min_bytes=POOL_BYTES, out
             return None if t is None else t.clone()
         pool = [[w4.PackedWeight(m["pw"].wq.clone(), m["pw"].scales.clone(),
                                  m["pw"].zeros.clone(), m["N"], m["K"], clone(m["pw"].o_row_ptr),
-                                 clone(m["pw"].o_col), clone(m["pw"].o_val))
+                                 clone(m["pw"].o_col), clone(m["pw"].o_val), m["pw"].wbits)
                  for _ in range(copies)]
                 for m in mats]
     torch.cuda.synchronize()
@@ -201,7 +206,8 @@ def with_batch(mats, cfg, M, torch, workloads):
         X = torch.from_numpy(workloads.activations(cfg.weight_key, mi, M, m["K"],
                                                    outliers=cfg.act_outliers)).to("cuda")
         Y = torch.empty((M, m["N"]), dtype=torch.float16, device="cuda")
-        out.append(dict(m, X=X, Y=Y, bytes=alg_bytes(M, m["N"], m["K"], m["s"] is not None),
+        out.append(dict(m, X=X, Y=Y, bytes=alg_bytes(M, m["N"], m["K"], m["s"] is not None,
+                                                     m["pw"].wbits),
                         flops=2 * M * m["N"] * m["K"]))
     return out
 
@@ -395,6 +401,7 @@ def main():
     ap.add_argument("--no-outliers", action="store_true")
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--no-gptq", action="store_true")
+    ap.add_argument("--no-int8", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-run", action="store_true",
                     help="only the short fixed sequence used for counter collection")
@@ -505,6 +512,24 @@ def main():
         del opool, omats
         torch.cuda.empty_cache()
 
+    if not args.no_int8:
+        log(f"preparing {cfg.name} with INT8 codes")
+        imats, ipool, _, ic = prepare_layer(cfg, M, torch, w4, workloads, int8=True)
+        ib = sum(m["bytes"] for m in imats)
+        iwall, ilms = timed(make_calls(imats, ipool, ic, one, w4, torch), args.steps // 2,
+                            args.warmup, torch)
+        ikern = float(np.mean(ilms[0])) * 1e-3
+        out["int8"] = {
+            "workload": f"{cfg.name} with INT8 codes (W8A16): the same 7 matrices, M={M}, "
+                        "group 128, asym uint8 + fp16 scale/zero, one grouped launch per step",
+            "step_bytes": ib, "us_per_step": round(iwall / (args.steps // 2) * 1e6, 2),
+            "kernel_us_per_step": round(ikern * 1e6, 2),
+            "kernel_TB/s": round(ib / ikern / 1e12, 4),
+            "frac_of_hbm_peak": round(ib / ikern / 1e9 / HBM_PEAK_GBS, 4),
+            "vs_int4_kernel_time": round(ikern / (avg_ms * 1e-3), 4)}
+        del ipool, imats
+        torch.cuda.empty_cache()
+
     if not args.no_spec:
         log("timing speculative verification")
         out["spec_verify"] = [spec_verify_line(torch, w4, B, 4, 128256) for B in (1, 64)]
@@ -548,6 +573,21 @@ def main():
             del bpm
         del ppool, pmats
         torch.cuda.empty_cache()
+        if not args.no_int8:
+            log(f"preparing {pcfg.name} M={PM} with INT8 codes")
+            imats, ipool, _, ipc = prepare_layer(pcfg, PM, torch, w4, workloads,
+                                                 copies_min_bytes=0, int8=True)
+            _, ims = timed(make_calls(imats, ipool, ipc, groups, w4, torch), args.prefill_steps,
+                           2, torch, per=1)
+            itot = sum(float(np.mean(x)) for x in ims)
+            out["prefill"]["int8"] = {
+                "workload": "the same layer with INT8 codes (W8A16)",
+                "kernel_ms_per_step": round(itot, 4),
+                "TFLOP/s": round(flops / (itot * 1e-3) / 1e12, 2),
+                "frac_of_dense_fp16_peak": round(flops / (itot * 1e-3) / 1e12 / FP16_PEAK_TFLOPS, 4),
+                "vs_int4_kernel_time": round(itot / tot_ms, 4)}
+            del ipool, imats
+            torch.cuda.empty_cache()
         if not args.no_outliers:
             log(f"preparing {pcfg.name} M={PM} with fp16 outliers")
             omats, opool, _, opc = prepare_layer(pcfg, PM, torch, w4, workloads,

@@ -116,7 +116,8 @@ enum {
   W4A16_QUANT_ASYM = 0,         /* the readings above (w4a16_quantize_pack)        */
   W4A16_QUANT_SYM = 1,          /* signed -7..7 around a constant zero point 8     */
   W4A16_QUANT_ASYM_CHANNEL = 2, /* asymmetric, one scale/zero per row (channel)    */
-  W4A16_QUANT_ASYM_TENSOR = 3   /* asymmetric, one scale/zero for the whole tensor */
+  W4A16_QUANT_ASYM_TENSOR = 3,  /* asymmetric, one scale/zero for the whole tensor */
+  W4A16_QUANT_ASYM8 = 4         /* INT8 codes 0..255 (W8A16), group 128            */
 };
 
 /* Quantize and pack on a chosen grid; same arguments, layout, blocking and
@@ -133,7 +134,16 @@ enum {
  * over the whole tensor instead of the group, and every group slot of the row
  * repeats the resulting scale and zero point (same layout, same kernels).
  * These two modes allocate 16 bytes per row of device memory for the
- * duration of the call. */
+ * duration of the call.
+ * W4A16_QUANT_ASYM8 is the INT8 (W8A16) variant ("Chapter 22", aiwing.uk,
+ * section 22.3's table: INT8 at one byte per parameter): the same rules with
+ * codes 0..255 (scale = range / 255 rounded up), one byte per weight in
+ * 2048-byte tiles -- tile (b, g) at (g * NB + b) * 2048, lane L = 16 c + r at
+ * 32 L, its byte 8 t + j holding column 128 g + 32 t + 8 c + j -- and the same
+ * metadata layout.  Wq holds N * K bytes (w4a16_packed_sizes_mode); the GEMM
+ * reads it with w4a16_problem.wbits = 8. */
+int w4a16_packed_sizes_mode(int64_t N, int64_t K, int mode, size_t *wq_bytes, size_t *scales_bytes,
+                            size_t *zeros_bytes);
 int w4a16_quantize_pack_mode(const void *W, const void *s, int64_t N, int64_t K, int mode,
                              void *Wq, void *scales, void *zeros, void *stream);
 
@@ -226,7 +236,11 @@ typedef struct w4a16_problem {
    * kernel rounds each dequantized weight to bf16 once (fp32 accumulation
    * throughout; Y rounded to bf16 once).  Another value is EUNSUPPORTED. */
   int32_t dtype;
-  int32_t reserved; /* 0 */
+  /* Code width: 0 or 4 (INT4, the default) or 8 (INT8 codes packed by
+   * W4A16_QUANT_ASYM8, N * K bytes, the same size limit as the INT4 code
+   * bytes else EINVAL); INT8 with bf16 activations or with fp16 outliers is
+   * EUNSUPPORTED, and so is any other width. */
+  int32_t wbits;
 } w4a16_problem;
 
 enum { W4A16_DTYPE_F16 = 0, W4A16_DTYPE_BF16 = 1 };

@@ -67,6 +67,27 @@ def test_packed_sizes_rejects(N, K):
 
 def test_packed_sizes_null_outputs():
     assert w4.lib().w4a16_packed_sizes(16, 128, None, None, None) == -1
+    assert w4.lib().w4a16_packed_sizes_mode(16, 128, 0, None, None, None) == -1
+
+
+@pytest.mark.parametrize("N,K", [(16, 128), (14336, 4096), (4096, 14336), (18944, 3584)])
+def test_packed_sizes_per_mode(N, K):
+    """INT4 modes share one size; INT8 codes take a byte per weight, same metadata."""
+    wq4, sc, z = oracle_sizes(N, K)
+    for mode in (w4.QUANT_ASYM, w4.QUANT_SYM, w4.QUANT_ASYM_CHANNEL, w4.QUANT_ASYM_TENSOR):
+        assert w4.w4a16_packed_sizes(N, K, mode) == (wq4, sc, z)
+    assert w4.w4a16_packed_sizes(N, K, w4.QUANT_ASYM8) == (N * K, sc, z)
+    with pytest.raises(w4.W4A16Error) as e:
+        w4.w4a16_packed_sizes(N, K, 5)
+    assert e.value.status == -3
+
+
+def test_packed_sizes_int8_limit():
+    # 32768 x 65536 INT4 codes fit the limit (1 GiB); as INT8 bytes (2 GiB) they do not
+    assert w4.w4a16_packed_sizes(32768, 65536)[0] == 1 << 30
+    with pytest.raises(w4.W4A16Error) as e:
+        w4.w4a16_packed_sizes(32768, 65536, w4.QUANT_ASYM8)
+    assert e.value.status == -1
 
 
 def gemm_rc(X=A16, Wq=A16, sc=A16, z=A16, s=None, Y=A16, M=1, N=16, K=128, path=0):
@@ -166,10 +187,11 @@ def test_grouped_ws_validation():
 def test_quantize_mode_validation():
     L = w4.lib()
     # unknown mode: rejected before anything else, without a GPU call
-    assert L.w4a16_quantize_pack_mode(A16, None, 16, 128, 4, A16, A16, A16, None) == -3
+    assert L.w4a16_quantize_pack_mode(A16, None, 16, 128, 5, A16, A16, A16, None) == -3
     assert L.w4a16_quantize_pack_mode(A16, None, 16, 128, -1, A16, A16, A16, None) == -3
     # known modes validate shapes and alignment like w4a16_quantize_pack
-    for mode in (w4.QUANT_ASYM, w4.QUANT_SYM, w4.QUANT_ASYM_CHANNEL, w4.QUANT_ASYM_TENSOR):
+    for mode in (w4.QUANT_ASYM, w4.QUANT_SYM, w4.QUANT_ASYM_CHANNEL, w4.QUANT_ASYM_TENSOR,
+                 w4.QUANT_ASYM8):
         assert L.w4a16_quantize_pack_mode(A16, None, 16, 100, mode, A16, A16, A16, None) == -1
         assert L.w4a16_quantize_pack_mode(ODD, None, 16, 128, mode, A16, A16, A16, None) == -2
 
@@ -277,6 +299,25 @@ def test_grouped_dtype_validation():
     arr = (w4.Problem * 1)(p)
     assert L.w4a16_gemm_grouped(arr, 1, None) == -3
     assert ctypes.sizeof(w4.Problem) == 104
+
+
+def test_grouped_code_width_validation():
+    L = w4.lib()
+    A4 = V((1 << 20) + 4)
+
+    def rc(**kw):
+        p = w4.Problem(A16, A16, A16, A16, None, A16, 1, 32, 256)
+        for k, v in kw.items():
+            setattr(p, k, v.value if isinstance(v, ctypes.c_void_p) else v)
+        return L.w4a16_gemm_grouped((w4.Problem * 1)(p), 1, None)
+
+    for bits in (1, 2, 3, 5, 16, -4):
+        assert rc(wbits=bits) == -3, bits
+    assert rc(wbits=8, dtype=w4.DTYPE_BF16) == -3               # INT8 takes fp16 only
+    assert rc(wbits=8, o_row_ptr=A4, o_col=A4, o_val=A4) == -3  # and no fp16 outliers
+    assert rc(wbits=8, N=32768, K=65536) == -1                  # 2 GiB of INT8 codes
+    assert rc(wbits=8, K=100) == -1
+    assert rc(wbits=8, X=ODD) == -2
 
 
 def test_bf16_bit_helpers_match_torch():

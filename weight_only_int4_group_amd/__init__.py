@@ -21,6 +21,7 @@ from .build import LIB_PATH
 __all__ = [
     "W4A16Error", "PackedWeight", "GROUP", "PATH_AUTO", "PATH_SKINNY", "PATH_TILED",
     "PATH_SKINNY_WINDOW", "QUANT_ASYM", "QUANT_SYM", "QUANT_ASYM_CHANNEL", "QUANT_ASYM_TENSOR",
+    "QUANT_ASYM8",
     "lib",
     "w4a16_packed_sizes", "w4a16_quantize_pack", "w4a16_gemm", "w4a16_gemm_path",
     "w4a16_select_path", "w4a16_strerror", "w4a16_version", "EXPORTED_SYMBOLS",
@@ -32,11 +33,12 @@ __all__ = [
 
 GROUP = 128
 PATH_AUTO, PATH_SKINNY, PATH_TILED, PATH_SKINNY_WINDOW = 0, 1, 2, 3
-QUANT_ASYM, QUANT_SYM, QUANT_ASYM_CHANNEL, QUANT_ASYM_TENSOR = 0, 1, 2, 3
+QUANT_ASYM, QUANT_SYM, QUANT_ASYM_CHANNEL, QUANT_ASYM_TENSOR, QUANT_ASYM8 = 0, 1, 2, 3, 4
 DTYPE_F16, DTYPE_BF16 = 0, 1
 STATUS = {0: "W4A16_OK", -1: "W4A16_EINVAL", -2: "W4A16_EALIGN", -3: "W4A16_EUNSUPPORTED",
           -4: "W4A16_ENONFINITE", -5: "W4A16_ERANGE", -6: "W4A16_EHIP"}
-EXPORTED_SYMBOLS = ("w4a16_packed_sizes", "w4a16_quantize_pack", "w4a16_quantize_pack_mode",
+EXPORTED_SYMBOLS = ("w4a16_packed_sizes", "w4a16_packed_sizes_mode", "w4a16_quantize_pack",
+                    "w4a16_quantize_pack_mode",
                     "w4a16_gemm",
                     "w4a16_gemm_path", "w4a16_gemm_grouped", "w4a16_gemm_grouped_ws",
                     "w4a16_gemm_workspace_size", "w4a16_outlier_workspace_size",
@@ -52,7 +54,7 @@ class Problem(ctypes.Structure):
                 ("zeros", ctypes.c_void_p), ("s", ctypes.c_void_p), ("Y", ctypes.c_void_p),
                 ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
                 ("o_row_ptr", ctypes.c_void_p), ("o_col", ctypes.c_void_p),
-                ("o_val", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("o_val", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("wbits", ctypes.c_int32)]
 
 
 class W4A16Error(RuntimeError):
@@ -75,6 +77,7 @@ def lib() -> ctypes.CDLL:
     L = ctypes.CDLL(LIB_PATH)
     i64, vp, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t)
     L.w4a16_packed_sizes.argtypes = [i64, i64, sz, sz, sz]
+    L.w4a16_packed_sizes_mode.argtypes = [i64, i64, ctypes.c_int, sz, sz, sz]
     L.w4a16_quantize_pack.argtypes = [vp, vp, i64, i64, vp, vp, vp, vp]
     L.w4a16_quantize_pack_mode.argtypes = [vp, vp, i64, i64, ctypes.c_int, vp, vp, vp, vp]
     L.w4a16_gemm.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, vp]
@@ -96,7 +99,8 @@ def lib() -> ctypes.CDLL:
     L.w4a16_strerror.argtypes = [ctypes.c_int]
     L.w4a16_strerror.restype = ctypes.c_char_p
     L.w4a16_version.argtypes = []
-    for name in ("w4a16_packed_sizes", "w4a16_quantize_pack", "w4a16_quantize_pack_mode",
+    for name in ("w4a16_packed_sizes", "w4a16_packed_sizes_mode", "w4a16_quantize_pack",
+                 "w4a16_quantize_pack_mode",
                  "w4a16_gemm", "w4a16_gemm_path",
                  "w4a16_gemm_grouped", "w4a16_gemm_grouped_ws", "w4a16_gemm_workspace_size",
                  "w4a16_spec_verify", "w4a16_spec_verify_workspace_size", "w4a16_select_path",
@@ -116,9 +120,10 @@ def w4a16_version() -> int:
     return lib().w4a16_version()
 
 
-def w4a16_packed_sizes(N: int, K: int) -> tuple:
+def w4a16_packed_sizes(N: int, K: int, mode: int = QUANT_ASYM) -> tuple:
     a, b, c = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
-    rc = lib().w4a16_packed_sizes(N, K, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c))
+    rc = lib().w4a16_packed_sizes_mode(N, K, mode, ctypes.byref(a), ctypes.byref(b),
+                                       ctypes.byref(c))
     if rc:
         raise W4A16Error(rc, "w4a16_packed_sizes")
     return a.value, b.value, c.value
@@ -130,8 +135,9 @@ def w4a16_select_path(M: int, N: int, K: int) -> int:
 
 @dataclass
 class PackedWeight:
-    """Packed INT4 weight: codes (uint8, N*K/2 bytes) and the fp16 scale and zero-point
-    buffers (flat, in the 4-group-quad layout of include/w4a16.h); with fp16 outliers
+    """Packed weight: INT4 codes (uint8, N*K/2 bytes) or, with wbits = 8, INT8 codes (N*K
+    bytes), and the fp16 scale and zero-point buffers (flat, in the 4-group-quad layout
+    of include/w4a16.h); with fp16 outliers
     (w4a16_quantize_pack_outliers) also their row pointers (int32 [N+1]), columns
     (int32) and values (fp16)."""
     wq: "object"
@@ -142,6 +148,7 @@ class PackedWeight:
     o_row_ptr: "object" = None
     o_col: "object" = None
     o_val: "object" = None
+    wbits: int = 4      # 8: INT8 codes (QUANT_ASYM8)
 
     def outlier_ptrs(self):
         """(row_ptr, col, val) device pointers, or three None without outliers."""
@@ -181,17 +188,18 @@ def w4a16_quantize_pack(W, s=None, out: PackedWeight | None = None,
                         mode: int = QUANT_ASYM) -> PackedWeight:
     """Quantize fp16 W[N][K] (AWQ scale s[K] or None) into a PackedWeight (blocks).
     mode: QUANT_ASYM (w4a16_quantize_pack), QUANT_SYM (signed -7..7 grid),
-    QUANT_ASYM_CHANNEL or QUANT_ASYM_TENSOR (one scale per row or per tensor)."""
+    QUANT_ASYM_CHANNEL or QUANT_ASYM_TENSOR (one scale per row or per tensor), or
+    QUANT_ASYM8 (INT8 codes, one byte per weight)."""
     torch = _torch()
     if W.dim() != 2:
         raise ValueError("W must be 2-D [N][K]")
     N, K = W.shape
-    wq_b, sc_b, z_b = w4a16_packed_sizes(N, K)
+    wq_b, sc_b, z_b = w4a16_packed_sizes(N, K, mode)
     if out is None:
         out = PackedWeight(torch.empty(wq_b, dtype=torch.uint8, device=W.device),
                            torch.empty(sc_b // 2, dtype=torch.float16, device=W.device),
                            torch.empty(z_b // 2, dtype=torch.float16, device=W.device),
-                           N, K)
+                           N, K, wbits=8 if mode == QUANT_ASYM8 else 4)
     rc = lib().w4a16_quantize_pack_mode(
         _dev_ptr(W, "W", torch.float16), _dev_ptr(s, "s", torch.float16, K), N, K, mode,
         _dev_ptr(out.wq, "wq", torch.uint8, wq_b),
@@ -199,6 +207,7 @@ def w4a16_quantize_pack(W, s=None, out: PackedWeight | None = None,
         _dev_ptr(out.zeros, "zeros", torch.float16, z_b // 2), _stream_handle(W.device))
     if rc:
         raise W4A16Error(rc, "w4a16_quantize_pack")
+    out.wbits = 8 if mode == QUANT_ASYM8 else 4
     return out
 
 
@@ -284,6 +293,8 @@ def w4a16_gemm_path(X, pw: PackedWeight, s=None, path: int = PATH_AUTO, out=None
     torch = _torch()
     if pw.outlier_ptrs()[0] is not None:
         raise ValueError("w4a16_gemm_path takes no fp16 outliers; use w4a16_gemm")
+    if pw.wbits != 4:
+        raise ValueError("w4a16_gemm_path takes INT4 codes only; use w4a16_gemm")
     if X.dim() != 2 or X.shape[1] != pw.K:
         raise ValueError("X must be [M][K] with K matching the packed weight")
     M = X.shape[0]
@@ -334,11 +345,12 @@ class GroupedCall:
             if X.dtype not in (torch.float16, torch.bfloat16):
                 raise TypeError(f"problem {i}: X must be float16 or bfloat16")
             self.array[i] = Problem(
-                _dev_ptr(X, "X", X.dtype), _dev_ptr(pw.wq, "wq", torch.uint8),
+                _dev_ptr(X, "X", X.dtype),
+                _dev_ptr(pw.wq, "wq", torch.uint8, pw.N * pw.K * pw.wbits // 8),
                 _dev_ptr(pw.scales, "scales", torch.float16),
                 _dev_ptr(pw.zeros, "zeros", torch.float16), _dev_ptr(s, "s", torch.float16, pw.K),
                 _dev_ptr(Y, "Y", X.dtype), X.shape[0], pw.N, pw.K, *pw.outlier_ptrs(),
-                DTYPE_BF16 if X.dtype == torch.bfloat16 else DTYPE_F16, 0)
+                DTYPE_BF16 if X.dtype == torch.bfloat16 else DTYPE_F16, pw.wbits)
         self.device = self.items[0][0].device if self.items else None
         self.ws, self.ws_ptr, self.ws_bytes = None, None, 0
         if workspace and self.items:

@@ -76,7 +76,27 @@ int w4a16_packed_sizes(int64_t N, int64_t K, size_t *wq_bytes, size_t *scales_by
 
 static bool known_mode(int mode) {
   return mode == W4A16_QUANT_ASYM || mode == W4A16_QUANT_SYM || mode == W4A16_QUANT_ASYM_CHANNEL ||
-         mode == W4A16_QUANT_ASYM_TENSOR;
+         mode == W4A16_QUANT_ASYM_TENSOR || mode == W4A16_QUANT_ASYM8;
+}
+
+// INT8 codes take N * K bytes
+static int check_shape_mode(int64_t N, int64_t K, int mode) {
+  const int rc = check_shape(N, K);
+  if (rc) return rc;
+  if (mode == W4A16_QUANT_ASYM8 && N * K > kMaxPackedBytes) return W4A16_EINVAL;
+  return W4A16_OK;
+}
+
+int w4a16_packed_sizes_mode(int64_t N, int64_t K, int mode, size_t *wq_bytes, size_t *scales_bytes,
+                            size_t *zeros_bytes) {
+  if (!known_mode(mode)) return W4A16_EUNSUPPORTED;
+  if (!wq_bytes || !scales_bytes || !zeros_bytes) return W4A16_EINVAL;
+  const int rc = check_shape_mode(N, K, mode);
+  if (rc) return rc;
+  *wq_bytes = (size_t)N * (size_t)K / (mode == W4A16_QUANT_ASYM8 ? 1 : 2);
+  *scales_bytes = (size_t)N * (size_t)w4a16::meta_groups((int)(K / W4A16_GROUP)) * 2;
+  *zeros_bytes = *scales_bytes;
+  return W4A16_OK;
 }
 
 static int pack_and_check(const void *W, const void *s, int64_t N, int64_t K,
@@ -95,15 +115,15 @@ static int pack_and_check(const void *W, const void *s, int64_t N, int64_t K,
                               range + N, st) != hipSuccess)
     rc = W4A16_EHIP;
   if (!rc && w4a16::launch_pack(W, s, (int)N, (int)K, keep, range, range ? range + N : nullptr,
-                                Wq, scales, zeros, status, mode == W4A16_QUANT_SYM,
-                                st) != hipSuccess)
+                                Wq, scales, zeros, status, mode == W4A16_QUANT_SYM, st,
+                                mode == W4A16_QUANT_ASYM8) != hipSuccess)
     rc = W4A16_EHIP;
   unsigned host = 0;
   if (!rc && hipMemcpyAsync(&host, status, sizeof(unsigned), hipMemcpyDeviceToHost, st) !=
                  hipSuccess)
     rc = W4A16_EHIP;
   if (hipStreamSynchronize(st) != hipSuccess) rc = W4A16_EHIP;  // also before freeing `range`
-  if (range) hipFree(range);
+  if (range && hipFree(range) != hipSuccess && !rc) rc = W4A16_EHIP;
   if (rc) return rc;
   if (host & w4a16::kPackNonFinite) return W4A16_ENONFINITE;
   if (host & w4a16::kPackRange) return W4A16_ERANGE;
@@ -114,7 +134,7 @@ int w4a16_quantize_pack_mode(const void *W, const void *s, int64_t N, int64_t K,
                              void *Wq, void *scales, void *zeros, void *stream) {
   if (!known_mode(mode)) return W4A16_EUNSUPPORTED;
   if (!W || !Wq || !scales || !zeros) return W4A16_EINVAL;
-  int rc = check_shape(N, K);
+  int rc = check_shape_mode(N, K, mode);
   if (rc) return rc;
   if (!aligned16(W) || !aligned16(Wq) || !aligned16(scales) || !aligned16(zeros) ||
       (s && !aligned16(s)))
@@ -175,7 +195,7 @@ int w4a16_quantize_pack_outliers(const void *W, const void *s, int64_t N, int64_
                                  int64_t count, void *Wq, void *scales, void *zeros,
                                  void *o_row_ptr, void *o_col, void *o_val, void *workspace,
                                  size_t workspace_bytes, void *stream) {
-  if (!known_mode(mode)) return W4A16_EUNSUPPORTED;
+  if (!known_mode(mode) || mode == W4A16_QUANT_ASYM8) return W4A16_EUNSUPPORTED;
   int rc = check_shape(N, K);
   if (rc) return rc;
   if (count < 0 || count > N * K || count > INT32_MAX) return W4A16_EINVAL;
@@ -232,7 +252,7 @@ void skinny_pieces(const w4a16_problem &p, std::vector<w4a16::GemmDesc> &out) {
     const int64_t mb = (p.M - m0) < kSkinnyMaxM ? (p.M - m0) : kSkinnyMaxM;
     out.push_back({static_cast<const _Float16 *>(p.X) + m0 * p.K, p.Wq, p.scales, p.zeros, p.s,
                    static_cast<_Float16 *>(p.Y) + m0 * p.N, (int)mb, (int)p.N, (int)p.K,
-                   p.o_row_ptr, p.o_col, p.o_val, p.dtype == W4A16_DTYPE_BF16});
+                   p.o_row_ptr, p.o_col, p.o_val, p.dtype == W4A16_DTYPE_BF16, p.wbits == 8});
   }
 }
 
@@ -283,6 +303,10 @@ int check_problems(const w4a16_problem *problems, int count) {
     const int rc = check_gemm(p.X, p.Wq, p.scales, p.zeros, p.s, p.Y, p.M, p.N, p.K);
     if (rc) return rc;
     if (p.dtype != W4A16_DTYPE_F16 && p.dtype != W4A16_DTYPE_BF16) return W4A16_EUNSUPPORTED;
+    if (p.wbits != 0 && p.wbits != 4 && p.wbits != 8) return W4A16_EUNSUPPORTED;
+    if (p.wbits == 8 && p.dtype == W4A16_DTYPE_BF16) return W4A16_EUNSUPPORTED;
+    if (p.wbits == 8 && p.N * p.K > kMaxPackedBytes) return W4A16_EINVAL;
+    if (p.wbits == 8 && (p.o_row_ptr || p.o_col || p.o_val)) return W4A16_EUNSUPPORTED;
     const bool any = p.o_row_ptr || p.o_col || p.o_val;
     if (any && !(p.o_row_ptr && p.o_col && p.o_val)) return W4A16_EINVAL;  // all or none
     if (any && ((reinterpret_cast<uintptr_t>(p.o_row_ptr) & 3u) ||
@@ -295,7 +319,7 @@ int check_problems(const w4a16_problem *problems, int count) {
 
 w4a16::GemmDesc desc_of(const w4a16_problem &p) {
   return {p.X,      p.Wq,        p.scales, p.zeros, p.s,  p.Y, (int)p.M, (int)p.N,
-          (int)p.K, p.o_row_ptr, p.o_col,  p.o_val, p.dtype == W4A16_DTYPE_BF16};
+          (int)p.K, p.o_row_ptr, p.o_col,  p.o_val, p.dtype == W4A16_DTYPE_BF16, p.wbits == 8};
 }
 
 // The tiled-path problems of a grouped call, in call order, in launches of up
@@ -308,7 +332,8 @@ std::vector<std::vector<w4a16::GemmDesc>> tiled_batches(const w4a16_problem *pro
     if (p.M == 0 || w4a16_select_path(p.M, p.N, p.K) != W4A16_PATH_TILED) continue;
     const w4a16::GemmDesc d = desc_of(p);
     // a launch is one kernel instance: one activation type
-    if (out.empty() || out.back().size() == cap || out.back().back().bf16 != d.bf16)
+    if (out.empty() || out.back().size() == cap || out.back().back().bf16 != d.bf16 ||
+        out.back().back().w8 != d.w8)
       out.emplace_back();
     out.back().push_back(d);
   }

@@ -46,7 +46,9 @@ __device__ __forceinline__ bool finite_h(_Float16 x) {
 // point, so it decodes to exactly 0).
 // rmin, rmax (optional): the range of each row's W' (per-channel or
 // per-tensor granularity) in place of each group's own.
-template <bool SYM>
+// W8: INT8 codes (0..255, scale = range / 255), a 2048-byte tile per group of
+// a row block, 32 bytes per lane (byte 8 t + j holds column 32 t + 8 c + j).
+template <bool SYM, bool W8>
 __global__ __launch_bounds__(256) void pack_kernel(const _Float16 *__restrict__ W,
                                                    const _Float16 *__restrict__ s, int N, int K,
                                                    const uint8_t *__restrict__ keep,
@@ -109,7 +111,7 @@ __global__ __launch_bounds__(256) void pack_kernel(const _Float16 *__restrict__ 
   double scale = 1.0, z = SYM ? 8.0 : 0.0;
   const bool live = range > 0.0;
   if (live) {
-    if (!fp16_ceil(range / (SYM ? 7.0 : 15.0), &sc16)) {
+    if (!fp16_ceil(range / (SYM ? 7.0 : (W8 ? 255.0 : 15.0)), &sc16)) {
       bad |= kPackRange;
       sc16 = 0;
     } else {
@@ -121,10 +123,26 @@ __global__ __launch_bounds__(256) void pack_kernel(const _Float16 *__restrict__ 
     }
   }
 
+  if (W8) {  // byte 8 t + j of the lane's 32 bytes: column 32 t + 8 c + j
+    uint32_t words[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (live) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          double v = rint(wp[8 * t + j] / scale) + z;
+          v = v < 0.0 ? 0.0 : (v > 255.0 ? 255.0 : v);
+          words[2 * t + j / 4] |= (uint32_t)v << (8 * (j % 4));
+        }
+    }
+    u32x4 lo = {words[0], words[1], words[2], words[3]}, hi = {words[4], words[5], words[6], words[7]};
+    Wq[tile * 128 + lane * 2] = lo;
+    Wq[tile * 128 + lane * 2 + 1] = hi;
+  }
   // an all-zero group: codes 0 (asymmetric) or 8 (symmetric, the zero point)
   const uint32_t fill = SYM ? 0x88888888u : 0u;
   u32x4 out = {fill, fill, fill, fill};
-  if (live) {
+  if (live && !W8) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       uint32_t word = 0;
@@ -145,7 +163,7 @@ __global__ __launch_bounds__(256) void pack_kernel(const _Float16 *__restrict__ 
       out[t] = word;
     }
   }
-  Wq[tile * 64 + lane] = out;
+  if (!W8) Wq[tile * 64 + lane] = out;
   if (c == 0) {
     scales[meta_index(n, g, NB)] = sc16;
     zeros[meta_index(n, g, NB)] = z16;
@@ -246,15 +264,19 @@ hipError_t launch_row_range(const void *W, const void *s, int N, int K, const ui
 
 hipError_t launch_pack(const void *W, const void *s, int N, int K, const uint8_t *keep,
                        const double *rmin, const double *rmax, void *Wq, void *scales, void *zeros,
-                       unsigned *status, bool symmetric, hipStream_t stream) {
+                       unsigned *status, bool symmetric, hipStream_t stream, bool w8) {
   const long long tiles = (long long)(N / kTileRows) * (K / kGroup);
   const long long blocks = (tiles + 3) / 4;
-  if (symmetric)
-    hipLaunchKernelGGL(pack_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream,
+  if (w8)
+    hipLaunchKernelGGL((pack_kernel<false, true>), dim3((unsigned)blocks), dim3(256), 0, stream,
+                       (const _Float16 *)W, (const _Float16 *)s, N, K, keep, rmin, rmax, (u32x4 *)Wq,
+                       (_Float16 *)scales, (_Float16 *)zeros, status);
+  else if (symmetric)
+    hipLaunchKernelGGL((pack_kernel<true, false>), dim3((unsigned)blocks), dim3(256), 0, stream,
                        (const _Float16 *)W, (const _Float16 *)s, N, K, keep, rmin, rmax, (u32x4 *)Wq,
                        (_Float16 *)scales, (_Float16 *)zeros, status);
   else
-    hipLaunchKernelGGL(pack_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream,
+    hipLaunchKernelGGL((pack_kernel<false, false>), dim3((unsigned)blocks), dim3(256), 0, stream,
                        (const _Float16 *)W, (const _Float16 *)s, N, K, keep, rmin, rmax, (u32x4 *)Wq,
                        (_Float16 *)scales, (_Float16 *)zeros, status);
   return hipGetLastError();

@@ -86,6 +86,20 @@ __device__ __forceinline__ half8 decode_word9(uint32_t w, uint32_t m_lo, uint32_
   return r;
 }
 
+// INT8 codes: two words (columns j = 0..3 and 4..7, one byte each, in order)
+// -> the exact fp16 values (q_j - z): v_perm_b32 pairs each code byte with the
+// 0x64 high byte of 1024.0 (1024 + q, exact: fp16 spacing is 1 there), then
+// minus (1024 + z).  Eight ops for eight codes.
+__device__ __forceinline__ half8 decode_words8(uint32_t wa, uint32_t wb, half2v bias) {
+  const uint32_t magic = 0x64646464u;
+  const half2v a = as_half2(__builtin_amdgcn_perm(magic, wa, 0x05010400u)) - bias;
+  const half2v b = as_half2(__builtin_amdgcn_perm(magic, wa, 0x05030402u)) - bias;
+  const half2v c = as_half2(__builtin_amdgcn_perm(magic, wb, 0x05010400u)) - bias;
+  const half2v d = as_half2(__builtin_amdgcn_perm(magic, wb, 0x05030402u)) - bias;
+  half8 r = {a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+  return r;
+}
+
 // bf16 operands: eight codes of one word -> the exact bf16 values 128 + q_j,
 // j = 0..7, in seven ALU ops (the same slot-to-column order as above).  The
 // zero point is taken off after the product: sum_k a_k (q_k - z) =
@@ -276,8 +290,9 @@ __device__ __forceinline__ void store_rows(const Problem &P, float4v acc, int b,
   }
 }
 
-template <int kGW, int kWaves, int kDepth, bool kOut, bool kBF>
+template <int kGW, int kWaves, int kDepth, bool kOut, bool kBF, bool kW8 = false>
 __global__ __launch_bounds__(kWaves * 64) void skinny_kernel(ProblemSet ps) {
+  constexpr int kCW = kW8 ? 2 : 1;  // 16-byte code loads per lane per tile
   // X * s, then (after the last use of X) the split-K reduction
   extern __shared__ __attribute__((aligned(16))) _Float16 xs[];
 
@@ -299,7 +314,7 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_kernel(ProblemSet ps) {
   const int glast = max(gb, ge - 1);          // loads past the slice re-read this group
 
   const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)P.Wq, (short)0, (int)min((size_t)0x7fffffff, (size_t)N * K / 2), kRsrcWord3);
+      (void *)P.Wq, (short)0, (int)min((size_t)0x7fffffff, (size_t)N * K * kCW / 2), kRsrcWord3);
   const int Gq = meta_groups(G) / kMetaQuad;
   const size_t meta_bytes = (size_t)N * Gq * kMetaQuad * 2;
   const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
@@ -308,9 +323,9 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_kernel(ProblemSet ps) {
       (void *)P.zeros, (short)0, (int)min((size_t)0x7fffffff, meta_bytes), kRsrcWord3);
   // group-major tiles and quad-major metadata: the row block's part of the
   // offset is per lane, the group's part is uniform
-  const int tile_off = bb * kTileBytes + lane * 16;               // + g * tile_stride
+  const int tile_off = bb * kTileBytes * kCW + lane * 16 * kCW;    // + g * tile_stride
   const int meta_off = (bb * kTileRows + r) * kMetaQuad * 2;      // + quad * meta_stride
-  const int tile_stride = NB * kTileBytes, meta_stride = NB * kTileRows * kMetaQuad * 2;
+  const int tile_stride = NB * kTileBytes * kCW, meta_stride = NB * kTileRows * kMetaQuad * 2;
 
   // A chunk is one or two metadata quads: 4 groups' scales (and zero points)
   // of this lane's row are one 8-byte load.
@@ -326,13 +341,16 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_kernel(ProblemSet ps) {
   struct Meta {
     uint32_t sq[2 * kQ], zq[2 * kQ];  // scales, zero points (fp16 pairs)
   };
-  u32x4 code[kGW];
+  u32x4 code[kGW][kCW];
   Meta m0, m1;
   auto load_codes = [&](int g0) {
 #pragma unroll
     for (int i = 0; i < kGW; ++i)
-      code[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                             wrs, tile_off, min(g0 + i, glast) * tile_stride, 0));
+#pragma unroll
+      for (int h = 0; h < kCW; ++h)
+        code[i][h] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrs, tile_off + 16 * h,
+                                                         min(g0 + i, glast) * tile_stride, 0));
   };
   auto load_meta = [&](Meta &mt, int g0) {
 #pragma unroll
@@ -383,10 +401,12 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_kernel(ProblemSet ps) {
   // issue chunk j+1's codes and chunk j+2's metadata (into `mt`), compute
   auto step = [&](int j, Meta &mt) {
     const int g0 = gb + j * kGW;
-    u32x4 cur[kGW];
+    u32x4 cur[kGW][kCW];
     half2v cs[2 * kQ], cz[2 * kQ];
 #pragma unroll
-    for (int i = 0; i < kGW; ++i) cur[i] = code[i];
+    for (int i = 0; i < kGW; ++i)
+#pragma unroll
+      for (int h = 0; h < kCW; ++h) cur[i][h] = code[i][h];
 #pragma unroll
     for (int q = 0; q < 2 * kQ; ++q) {
       cs[q] = as_half2(mt.sq[q]);
@@ -404,7 +424,7 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_kernel(ProblemSet ps) {
 #pragma unroll
           for (int t = 0; t < 4; ++t)
             tmp = mfma16_bf16(*reinterpret_cast<const u32x4 *>(xrow + g * kGroup + 32 * t),
-                              decode_word_bf16(cur[i][t]), tmp);
+                              decode_word_bf16(cur[i][0][t]), tmp);
           const float zb = 128.0f + (float)zp;
 #pragma unroll
           for (int v = 0; v < 4; ++v) acc[v] += (tmp[v] - zb * gsum[gs_row[v] + g]) * (float)sc;
@@ -415,8 +435,12 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_kernel(ProblemSet ps) {
           const _Float16 blo = (_Float16)1024.0f + zp, bhi = (_Float16)64.0f + zp;
           const half2v bias_lo = {blo, blo}, bias_hi = {bhi, bhi};
 #pragma unroll
-          for (int t = 0; t < 4; ++t)
-            tmp = mfma16(a[t], decode_word9(cur[i][t], m_lo, m_hi, magic, bias_lo, bias_hi), tmp);
+          for (int t = 0; t < 4; ++t) {
+            const half8 bop = kW8 ? decode_words8(cur[i][t >> 1 & (kCW - 1)][2 * (t & 1)],
+                                                  cur[i][t >> 1 & (kCW - 1)][2 * (t & 1) + 1], bias_lo)
+                                  : decode_word9(cur[i][0][t], m_lo, m_hi, magic, bias_lo, bias_hi);
+            tmp = mfma16(a[t], bop, tmp);
+          }
           acc += tmp * (float)sc;
         }
       }
@@ -434,8 +458,9 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_kernel(ProblemSet ps) {
 
 // Windowed variant: X * s staged one window of S chunks at a time (see the
 // header).  kSlots bounds the 8-column pieces of a window each thread stages.
-template <int kGW, int kWaves, int kDepth, int kSlots, bool kOut, bool kBF>
+template <int kGW, int kWaves, int kDepth, int kSlots, bool kOut, bool kBF, bool kW8 = false>
 __global__ __launch_bounds__(kWaves * 64) void skinny_window_kernel(ProblemSet ps) {
+  constexpr int kCW = kW8 ? 2 : 1;  // 16-byte code loads per lane per tile
   extern __shared__ __attribute__((aligned(16))) _Float16 xs[];
   __shared__ float red[kWaves][16][17];
   constexpr int kThreads = kWaves * 64;
@@ -455,7 +480,7 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_window_kernel(ProblemSet p
   const int ldx = wcols + kLdsPad;
 
   const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)P.Wq, (short)0, (int)min((size_t)0x7fffffff, (size_t)N * K / 2), kRsrcWord3);
+      (void *)P.Wq, (short)0, (int)min((size_t)0x7fffffff, (size_t)N * K * kCW / 2), kRsrcWord3);
   const int Gq = meta_groups(G) / kMetaQuad;
   const size_t meta_bytes = (size_t)N * Gq * kMetaQuad * 2;
   const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
@@ -463,19 +488,22 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_window_kernel(ProblemSet p
   const __amdgpu_buffer_rsrc_t zrs = __builtin_amdgcn_make_buffer_rsrc(
       (void *)P.zeros, (short)0, (int)min((size_t)0x7fffffff, meta_bytes), kRsrcWord3);
   const int2 orange = kOut ? outlier_range(P, b, has_rows, ks, r) : int2{0, 0};
-  const int tile_off = bb * kTileBytes + lane * 16;               // + g * tile_stride
+  const int tile_off = bb * kTileBytes * kCW + lane * 16 * kCW;    // + g * tile_stride
   const int meta_off = (bb * kTileRows + r) * kMetaQuad * 2;      // + quad * meta_stride
-  const int tile_stride = NB * kTileBytes, meta_stride = NB * kTileRows * kMetaQuad * 2;
+  const int tile_stride = NB * kTileBytes * kCW, meta_stride = NB * kTileRows * kMetaQuad * 2;
 
   static_assert(kGW % kMetaQuad == 0, "a chunk is whole metadata quads");
   constexpr int kQ = kGW / kMetaQuad;
-  u32x4 code[kDepth][kGW];
+  u32x4 code[kDepth][kGW][kCW];
   uint32_t sq[kDepth][2 * kQ], zq[kDepth][2 * kQ];
   auto load_chunk = [&](int slot, int g0) {
 #pragma unroll
     for (int i = 0; i < kGW; ++i)  // past the row: re-read its last tile (never used)
-      code[slot][i] = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrs, tile_off, min(g0 + i, G - 1) * tile_stride, 0));
+#pragma unroll
+      for (int h = 0; h < kCW; ++h)
+        code[slot][i][h] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrs, tile_off + 16 * h,
+                                                         min(g0 + i, G - 1) * tile_stride, 0));
 #pragma unroll
     for (int q = 0; q < kQ; ++q) {
       const int qoff = min(g0 / kMetaQuad + q, Gq - 1) * meta_stride;
@@ -571,10 +599,12 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_window_kernel(ProblemSet p
   // swap) the window after next.  Each wait then leaves only younger loads in
   // flight: the weights for the window's X, that X for the next weights.
   for (int j = 0; j < steps; ++j) {
-    u32x4 cur[kGW];
+    u32x4 cur[kGW][kCW];
     half2v cs2[2 * kQ], cz2[2 * kQ];
 #pragma unroll
-    for (int i = 0; i < kGW; ++i) cur[i] = code[0][i];
+    for (int i = 0; i < kGW; ++i)
+#pragma unroll
+      for (int h = 0; h < kCW; ++h) cur[i][h] = code[0][i][h];
 #pragma unroll
     for (int q = 0; q < 2 * kQ; ++q) {
       cs2[q] = as_half2(sq[0][q]);
@@ -583,7 +613,9 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_window_kernel(ProblemSet p
 #pragma unroll
     for (int d = 0; d + 1 < kDepth; ++d) {
 #pragma unroll
-      for (int i = 0; i < kGW; ++i) code[d][i] = code[d + 1][i];
+      for (int i = 0; i < kGW; ++i)
+#pragma unroll
+        for (int h = 0; h < kCW; ++h) code[d][i][h] = code[d + 1][i][h];
 #pragma unroll
       for (int q = 0; q < 2 * kQ; ++q) {
         sq[d][q] = sq[d + 1][q];
@@ -603,7 +635,7 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_window_kernel(ProblemSet p
 #pragma unroll
             for (int t = 0; t < 4; ++t)
               tmp = mfma16_bf16(*reinterpret_cast<const u32x4 *>(xrow + i * kGroup + 32 * t),
-                                decode_word_bf16(cur[i][t]), tmp);
+                                decode_word_bf16(cur[i][0][t]), tmp);
             const float zb = 128.0f + (float)zp;
 #pragma unroll
             for (int v = 0; v < 4; ++v) acc[v] += (tmp[v] - zb * wsum[ws_row[v] + i]) * (float)sc;
@@ -611,9 +643,13 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_window_kernel(ProblemSet p
             const _Float16 blo = (_Float16)1024.0f + zp, bhi = (_Float16)64.0f + zp;
             const half2v bias_lo = {blo, blo}, bias_hi = {bhi, bhi};
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
-              tmp = mfma16(*reinterpret_cast<const half8 *>(xrow + i * kGroup + 32 * t),
-                           decode_word9(cur[i][t], m_lo, m_hi, magic, bias_lo, bias_hi), tmp);
+            for (int t = 0; t < 4; ++t) {
+              const half8 bop =
+                  kW8 ? decode_words8(cur[i][t >> 1 & (kCW - 1)][2 * (t & 1)],
+                                      cur[i][t >> 1 & (kCW - 1)][2 * (t & 1) + 1], bias_lo)
+                      : decode_word9(cur[i][0][t], m_lo, m_hi, magic, bias_lo, bias_hi);
+              tmp = mfma16(*reinterpret_cast<const half8 *>(xrow + i * kGroup + 32 * t), bop, tmp);
+            }
             acc += tmp * (float)sc;
           }
         }
@@ -750,8 +786,16 @@ hipError_t launch_group(const GemmDesc *const *d, int count, bool window, hipStr
   }
   ps.count = count;
   const dim3 grid(blocks), threads(kWaves * 64);
-  const bool bf = d[0]->bf16;  // one activation type per launch
-  if (window) {
+  const bool bf = d[0]->bf16;  // one activation type (and code width) per launch
+  if (d[0]->w8) {  // INT8 codes: fp16 activations, no outliers
+    if (window)
+      hipLaunchKernelGGL(
+          (skinny_window_kernel<kChunk, kWaves, kDepth, kWindowSlots, false, false, true>), grid,
+          threads, lds, stream, ps);
+    else
+      hipLaunchKernelGGL((skinny_kernel<kChunk, kWaves, kDepth, false, false, true>), grid, threads,
+                         lds, stream, ps);
+  } else if (window) {
     if (bf && out)
       hipLaunchKernelGGL((skinny_window_kernel<kChunk, kWaves, kDepth, kWindowSlots, true, true>),
                          grid, threads, lds, stream, ps);
@@ -793,14 +837,17 @@ hipError_t launch_skinny_set(const GemmDesc *d, int count, hipStream_t stream,
   // within rounding of the exact result; each call is reproducible).  fp16 and
   // bf16 problems go in separate launches (one kernel instance each).
   hipError_t err = hipSuccess;
-  for (int bf = 0; bf < 2 && err == hipSuccess; ++bf) {
+  for (int cls = 0; cls < 3 && err == hipSuccess; ++cls) {
+    // classes: fp16 INT4, bf16 INT4, fp16 INT8
+    const bool want_bf = cls == 1, want_w8 = cls == 2;
+    auto in_class = [&](const GemmDesc &q) { return q.bf16 == want_bf && q.w8 == want_w8; };
     const GemmDesc *whole[kMaxProblems], *windowed[kMaxProblems];
     int nwhole = 0, nwin = 0;
     bool any = false;
     for (int i = 0; i < count; ++i)
-      if (d[i].bf16 == (bf == 1)) any |= stage_bytes(d[i].M, d[i].K, d[i].bf16) > kMaxStageBytes;
+      if (in_class(d[i])) any |= stage_bytes(d[i].M, d[i].K, d[i].bf16) > kMaxStageBytes;
     for (int i = 0; i < count; ++i) {
-      if (d[i].bf16 != (bf == 1)) continue;
+      if (!in_class(d[i])) continue;
       const bool fits = stage_bytes(d[i].M, d[i].K, d[i].bf16) <= kMaxStageBytes;
       const bool win = force_window || kWindowMode == 2 || (kWindowMode == 1 && !fits) ||
                        (kWindowMode == 3 && any);

@@ -84,6 +84,19 @@ __device__ __forceinline__ u32x4 dequant_word_bf16(uint32_t w, float scale, floa
   return r;
 }
 
+// INT8 codes: two words (columns j = 0..3 and 4..7, one byte each) ->
+// (q_j - z) * scale in fp16: v_perm_b32 builds the exact 1024 + q (see the
+// streaming kernel), minus (1024 + z) is exact, one rounding by the scale.
+__device__ __forceinline__ half8 dequant_words8(uint32_t wa, uint32_t wb, half2v bias, half2v scale) {
+  const uint32_t magic = 0x64646464u;
+  const half2v a = (as_half2(__builtin_amdgcn_perm(magic, wa, 0x05010400u)) - bias) * scale;
+  const half2v b = (as_half2(__builtin_amdgcn_perm(magic, wa, 0x05030402u)) - bias) * scale;
+  const half2v c = (as_half2(__builtin_amdgcn_perm(magic, wb, 0x05010400u)) - bias) * scale;
+  const half2v d = (as_half2(__builtin_amdgcn_perm(magic, wb, 0x05030402u)) - bias) * scale;
+  half8 r = {a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+  return r;
+}
+
 constexpr int kMaxTiled = 8;  // problems per launch
 
 struct TiledProblem {
@@ -150,10 +163,11 @@ __device__ __forceinline__ TiledProblem find_tiled(const TiledSet &ts, int block
 
 // Two waves per SIMD: with one, the waits on LDS and the barriers are not
 // hidden and MFMA throughput roughly halves (measured on the 70B shapes).
-template <int WM, int WN, int TM, int TN, bool OUT, bool BF>
+template <int WM, int WN, int TM, int TN, bool OUT, bool BF, bool W8 = false>
 __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void tiled_kernel(
     TiledSet ts) {
   constexpr int THREADS = WM * WN * 64;
+  constexpr int kCW = W8 ? 2 : 1;  // 16-byte code pieces per lane per tile
   constexpr int BM = WM * TM * 16, BN = WN * TN * 16;
   constexpr int kLdsStride = kGroup + 8;                  // halves; the pad spreads rows over banks
   constexpr int kChunksPerRow = kGroup / 8;               // 16-byte chunks per A row per stage
@@ -238,30 +252,35 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
   // scales and zero points come as raw 16-bit words into one of two register
   // sets.
   const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)Wq, (short)0, (int)min((size_t)0x7fffffff, (size_t)N * K / 2), kRsrcWord3);
+      (void *)Wq, (short)0, (int)min((size_t)0x7fffffff, (size_t)N * K * kCW / 2), kRsrcWord3);
   const size_t meta_bytes = (size_t)N * Gq * kMetaQuad * 2;
   const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
       (void *)scales, (short)0, (int)min((size_t)0x7fffffff, meta_bytes), kRsrcWord3);
   const __amdgpu_buffer_rsrc_t zrs = __builtin_amdgcn_make_buffer_rsrc(
       (void *)zeros, (short)0, (int)min((size_t)0x7fffffff, meta_bytes), kRsrcWord3);
   const int rb0 = n0 / kTileRows + wn * TN;  // first row block of this wave
-  __shared__ __attribute__((aligned(16))) uint8_t Bs[2][WM * WN * TN * kTileBytes];
+  // INT8 tiles are twice as large: two 16-byte pieces per lane, the second
+  // 1 KB after the first in LDS
+  __shared__ __attribute__((aligned(16))) uint8_t Bs[2][WM * WN * TN * kTileBytes * kCW];
   struct BRegs {
-    u32x4 code[TN];
+    u32x4 code[TN][kCW];
     uint32_t sc[TN], zp[TN];  // raw fp16 bits of each row block's scale and zero point
   };
   BRegs b0, b1;
   // group-major tiles and quad-major metadata: the row block's part of each
   // offset is per lane, the group's part uniform
-  const int tile_stride = NB * kTileBytes, meta_stride = NB * kTileRows * kMetaQuad * 2;
+  const int tile_stride = NB * kTileBytes * kCW, meta_stride = NB * kTileRows * kMetaQuad * 2;
   auto load_b = [&](int g, int buf, BRegs &b) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       // row blocks past N re-read the last one (in bounds) and are never stored
       const int rb = min(rb0 + j, NB - 1);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          wrs, (__attribute__((address_space(3))) void *)&Bs[buf][(wave * TN + j) * kTileBytes], 16,
-          (rb * 64 + lane) * 16, g * tile_stride, 0, 0);
+#pragma unroll
+      for (int h = 0; h < kCW; ++h)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            wrs,
+            (__attribute__((address_space(3))) void *)&Bs[buf][((wave * TN + j) * kCW + h) * kTileBytes],
+            16, (rb * 64 + lane) * 16 * kCW + 16 * h, g * tile_stride, 0, 0);
       const int mo = (rb * kTileRows + r) * kMetaQuad * 2;
       const int qo = (g / kMetaQuad) * meta_stride + (g % kMetaQuad) * 2;
       b.sc[j] = __builtin_amdgcn_raw_buffer_load_b16(srs, mo, qo, 0);
@@ -287,7 +306,7 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
         for (int j = 0; j < TN; ++j) {
           const float z = (float)__builtin_bit_cast(_Float16, (uint16_t)b.zp[j]);
           const float sv = (float)__builtin_bit_cast(_Float16, (uint16_t)b.sc[j]);
-          bop[j] = dequant_word_bf16(b.code[j][tt], sv, (128.0f + z) * sv);
+          bop[j] = dequant_word_bf16(b.code[j][0][tt], sv, (128.0f + z) * sv);
         }
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
@@ -303,7 +322,9 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
           const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)b.sc[j]);
           const _Float16 blo = (_Float16)1024.0f + z, bhi = (_Float16)64.0f + z;
           const half2v bias_lo = {blo, blo}, bias_hi = {bhi, bhi}, scale = {sv, sv};
-          bop[j] = dequant_word(b.code[j][tt], bias_lo, bias_hi, scale);
+          bop[j] = W8 ? dequant_words8(b.code[j][tt >> 1 & (kCW - 1)][2 * (tt & 1)],
+                                       b.code[j][tt >> 1 & (kCW - 1)][2 * (tt & 1) + 1], bias_lo, scale)
+                      : dequant_word(b.code[j][0][tt], bias_lo, bias_hi, scale);
         }
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
@@ -421,7 +442,10 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the DMA writes are not seen by the compiler
 #pragma unroll
     for (int j = 0; j < TN; ++j)
-      cur.code[j] = *reinterpret_cast<const u32x4 *>(&Bs[buf][(wave * TN + j) * kTileBytes + lane * 16]);
+#pragma unroll
+      for (int h = 0; h < kCW; ++h)
+        cur.code[j][h] = *reinterpret_cast<const u32x4 *>(
+            &Bs[buf][((wave * TN + j) * kCW + h) * kTileBytes + lane * 16]);
     const bool more = g + 1 < ge;
     if (more) {
       load_a(g + 1);
@@ -597,7 +621,10 @@ hipError_t launch_tiled_set(const GemmDesc *d, int count, void *workspace, size_
   }
   ts.count = count;
   const dim3 grid(blocks), threads(kWM * kWN * 64);
-  if (d[0].bf16 && out)  // one activation type per launch
+  if (d[0].w8)  // INT8 codes: fp16 activations, no outliers
+    hipLaunchKernelGGL((tiled_kernel<kWM, kWN, kTM, kTN, false, false, true>), grid, threads, 0,
+                       stream, ts);
+  else if (d[0].bf16 && out)  // one activation type (and code width) per launch
     hipLaunchKernelGGL((tiled_kernel<kWM, kWN, kTM, kTN, true, true>), grid, threads, 0, stream, ts);
   else if (d[0].bf16)
     hipLaunchKernelGGL((tiled_kernel<kWM, kWN, kTM, kTN, false, true>), grid, threads, 0, stream,

@@ -12,7 +12,7 @@ constexpr unsigned kPackRange = 2u;
 
 hipError_t launch_pack(const void *W, const void *s, int N, int K, const uint8_t *keep,
                        const double *rmin, const double *rmax, void *Wq, void *scales, void *zeros,
-                       unsigned *status, bool symmetric, hipStream_t stream);
+                       unsigned *status, bool symmetric, hipStream_t stream, bool w8 = false);
 // Per-row range of W / s (kept weights as 0) into rmin/rmax [N]; with `tensor`
 // every row then holds the whole tensor's range.
 hipError_t launch_row_range(const void *W, const void *s, int N, int K, const uint8_t *keep,
@@ -43,6 +43,7 @@ struct GemmDesc {
   // optional fp16 outliers, row-compressed (all set or all null)
   const void *o_row_ptr = nullptr, *o_col = nullptr, *o_val = nullptr;
   bool bf16 = false;  // X and Y are bf16 (else fp16)
+  bool w8 = false;    // INT8 codes (2048-byte tiles), else INT4
 };
 
 // Streaming kernel for small M (decode and speculative verify): M <= 16.
