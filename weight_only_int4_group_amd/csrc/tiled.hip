@@ -260,8 +260,12 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
       (void *)zeros, (short)0, (int)min((size_t)0x7fffffff, meta_bytes), kRsrcWord3);
   const int rb0 = n0 / kTileRows + wn * TN;  // first row block of this wave
   // INT8 tiles are twice as large: two 16-byte pieces per lane, the second
-  // 1 KB after the first in LDS
-  __shared__ __attribute__((aligned(16))) uint8_t Bs[2][WM * WN * TN * kTileBytes * kCW];
+  // 1 KB after the first in LDS.  They use one LDS buffer, not two, so that
+  // two workgroups still fit in a CU's LDS: each wave DMAs into and reads only
+  // its own slots, so it can take the group's codes into registers, wait for
+  // those reads, and then let the next group's DMA overwrite the slots.
+  constexpr int kBBufs = W8 ? 1 : 2;
+  __shared__ __attribute__((aligned(16))) uint8_t Bs[kBBufs][WM * WN * TN * kTileBytes * kCW];
   struct BRegs {
     u32x4 code[TN][kCW];
     uint32_t sc[TN], zp[TN];  // raw fp16 bits of each row block's scale and zero point
@@ -279,7 +283,7 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
       for (int h = 0; h < kCW; ++h)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             wrs,
-            (__attribute__((address_space(3))) void *)&Bs[buf][((wave * TN + j) * kCW + h) * kTileBytes],
+            (__attribute__((address_space(3))) void *)&Bs[buf % kBBufs][((wave * TN + j) * kCW + h) * kTileBytes],
             16, (rb * 64 + lane) * 16 * kCW + 16 * h, g * tile_stride, 0, 0);
       const int mo = (rb * kTileRows + r) * kMetaQuad * 2;
       const int qo = (g / kMetaQuad) * meta_stride + (g % kMetaQuad) * 2;
@@ -323,7 +327,8 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
           const _Float16 blo = (_Float16)1024.0f + z, bhi = (_Float16)64.0f + z;
           const half2v bias_lo = {blo, blo}, bias_hi = {bhi, bhi}, scale = {sv, sv};
           bop[j] = W8 ? dequant_words8(b.code[j][tt >> 1 & (kCW - 1)][2 * (tt & 1)],
-                                       b.code[j][tt >> 1 & (kCW - 1)][2 * (tt & 1) + 1], bias_lo, scale)
+                                       b.code[j][tt >> 1 & (kCW - 1)][2 * (tt & 1) + 1], bias_lo,
+                                       scale)
                       : dequant_word(b.code[j][0][tt], bias_lo, bias_hi, scale);
         }
 #pragma unroll
@@ -445,7 +450,9 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
 #pragma unroll
       for (int h = 0; h < kCW; ++h)
         cur.code[j][h] = *reinterpret_cast<const u32x4 *>(
-            &Bs[buf][((wave * TN + j) * kCW + h) * kTileBytes + lane * 16]);
+            &Bs[buf % kBBufs][((wave * TN + j) * kCW + h) * kTileBytes + lane * 16]);
+    // one INT8 buffer: the reads must land before the next DMA overwrites it
+    if (W8) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     const bool more = g + 1 < ge;
     if (more) {
       load_a(g + 1);
