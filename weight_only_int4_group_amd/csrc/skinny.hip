@@ -196,34 +196,93 @@ __device__ __forceinline__ Problem find_problem(const ProblemSet &ps) {
   return P;
 }
 
-// The kept fp16 weights e0 .. e1 - 1 of the lane's row (its row-pointer pair,
-// loaded when the kernel starts) for lane (c, r): o[v] = the sum over them, in
-// stored order, of X[4c + v][col_e] * val_e (rows past M read row M - 1 and
-// are not stored).  Two entries' loads are issued at a time (more raise the
-// register count past what six waves per SIMD allow).
+// fp16 outliers of a row block, added by the wave that stores it, all 64
+// lanes at once.  The kept weights of the block's 16 rows are one range
+// e0 .. e1 - 1 of the row-compressed arrays; round u hands entry e0 + 64 u +
+// lane to each lane.  The columns and values of the first kOutRounds rounds
+// are loaded early (once X is staged, when the row pointers have arrived), so
+// that only the X values they select are loaded in the epilogue.
+constexpr int kOutRounds = 4;
+struct OutPrefetch {
+  int e0, e1;
+  int col[kOutRounds];
+  uint32_t val[kOutRounds];  // fp16 bits
+};
+
+// The loads go through buffer resources that cover only e0 .. e1 - 1:
+// entries past e1 read 0 and are masked by index (e < e1) where used, so the
+// loads are unconditional and nothing waits for them before the epilogue.
+__device__ __forceinline__ OutPrefetch outlier_prefetch(const Problem &P, int2 orange, int lane) {
+  OutPrefetch f;
+  // lanes 0..15 (c = 0) hold the pairs of rows 0..15
+  f.e0 = __builtin_amdgcn_readfirstlane(__shfl(orange.x, 0));
+  f.e1 = __builtin_amdgcn_readfirstlane(__shfl(orange.y, 15));
+  const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(P.ocol + f.e0), (short)0, (f.e1 - f.e0) * 4, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(P.oval + f.e0), (short)0, (f.e1 - f.e0) * 2, kRsrcWord3);
+#pragma unroll
+  for (int u = 0; u < kOutRounds; ++u) {
+    const int i = 64 * u + lane;
+    f.col[u] = (int)__builtin_amdgcn_raw_buffer_load_b32(crs, 4 * i, 0, 0);
+    f.val[u] = __builtin_amdgcn_raw_buffer_load_b16(vrs, 2 * i, 0, 0);
+  }
+  return f;
+}
+
+__device__ __forceinline__ float wave_prefix_sum(float x, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float t = __shfl_up(x, o);
+    x += lane >= o ? t : 0.f;
+  }
+  return x;
+}
+
+// o[v] for lane (c, r) of the storing wave: the sum over row r's kept weights
+// of X[4c + v][col] * val (rows past M give 0 and are not stored).  In each
+// round the lanes holding row r's entries are one run lo .. hi - 1 (entries
+// are in row order); a wave-wide prefix sum of the terms gives the run's sum
+// as a difference of two prefix values.  The order of the additions depends
+// only on the row pointers, so results are reproducible.
 template <bool kBF>
-__device__ __forceinline__ float4v outlier_terms(const Problem &P, int e0, int e1, int c) {
-  constexpr int kBatch = 2;
+__device__ float4v outlier_terms(const Problem &P, const OutPrefetch &f, int2 orange, int lane,
+                                 int c) {
   float4v o = {0.f, 0.f, 0.f, 0.f};
-  for (int e = e0; e < e1; e += kBatch) {
-    int col[kBatch];
-    float val[kBatch];
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int ee = min(e + u, e1 - 1);
-      col[u] = P.ocol[ee];
-      val[u] = (float)P.oval[ee];
-    }
-    float x[kBatch][4];
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u)
+  const int M = P.M, K = P.K;
+  auto round = [&](int base, int col, float val) {
+    const int lo = min(max(orange.x - base, 0), 64), hi = min(max(orange.y - base, 0), 64);
+    for (int m0 = 0; m0 < M; m0 += 4) {  // uniform
+      float t[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int v = 0; v < 4; ++v)
-        x[u][v] = x_value(P.X, (size_t)min(4 * c + v, P.M - 1) * P.K + col[u], kBF);
+        if (col >= 0 && m0 + v < M) t[v] = x_value(P.X, (size_t)(m0 + v) * K + col, kBF) * val;
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u)
+      for (int v = 0; v < 4; ++v) {
+        if (m0 + v >= M) break;  // uniform
+        const float pre = wave_prefix_sum(t[v], lane);
+        const float ph = __shfl(pre, max(hi - 1, 0)), pl = __shfl(pre, max(lo - 1, 0));
+        if (c == (m0 >> 2) && hi > lo) o[v] += ph - (lo > 0 ? pl : 0.f);
+      }
+    }
+  };
+  const int rounds = (f.e1 - f.e0 + 63) / 64;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) o[v] += e + u < e1 ? x[u][v] * val[u] : 0.f;
+  for (int u = 0; u < kOutRounds; ++u) {
+    if (u >= rounds) break;  // uniform
+    const bool in = f.e0 + 64 * u + lane < f.e1;
+    round(f.e0 + 64 * u, in ? f.col[u] : -1,
+          (float)__builtin_bit_cast(_Float16, (uint16_t)f.val[u]));
+  }
+  for (int u = kOutRounds; u < rounds; ++u) {  // rows with many kept weights
+    const int e = f.e0 + 64 * u + lane;
+    int col = -1;
+    float val = 0.f;
+    if (e < f.e1) {
+      col = P.ocol[e];
+      val = (float)P.oval[e];
+    }
+    round(f.e0 + 64 * u, col, val);
   }
   return o;
 }
@@ -258,11 +317,13 @@ __device__ __forceinline__ void store_y(_Float16 *Y, size_t i, float v) {
 template <int kWaves, bool kOut, bool kBF>
 __device__ __forceinline__ void store_rows(const Problem &P, float4v acc, int b, bool has_rows,
                                            int wave, int ks, int c, int r,
-                                           float (*red)[16][17], int2 orange) {
+                                           float (*red)[16][17], int2 orange,
+                                           const OutPrefetch &of) {
+  const int lane = 16 * c + r;
   const int M = P.M, N = P.N, S = P.split;
   if (S == 1) {
     if (has_rows) {
-      if (kOut) acc += outlier_terms<kBF>(P, orange.x, orange.y, c);
+      if (kOut) acc += outlier_terms<kBF>(P, of, orange, lane, c);
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int m = 4 * c + v;
@@ -275,7 +336,7 @@ __device__ __forceinline__ void store_rows(const Problem &P, float4v acc, int b,
     __syncthreads();
     if (ks == 0 && has_rows) {
       float4v o = {0.f, 0.f, 0.f, 0.f};
-      if (kOut) o = outlier_terms<kBF>(P, orange.x, orange.y, c);
+      if (kOut) o = outlier_terms<kBF>(P, of, orange, lane, c);
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int m = 4 * c + v;
@@ -390,6 +451,8 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_kernel(ProblemSet ps) {
     }
     __syncthreads();
   }
+  OutPrefetch of = {};
+  if (kOut) of = outlier_prefetch(P, orange, lane);
   const _Float16 *xrow = xs + min(r, M - 1) * (K + kLdsPad) + 8 * c;
   int gs_row[4];  // bf16: rows 4c + v of gsum (rows past M read row M - 1)
 #pragma unroll
@@ -453,7 +516,7 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_kernel(ProblemSet ps) {
 
   if (S > 1) __syncthreads();  // every wave is done with X * s: its LDS takes the partial sums
   store_rows<kWaves, kOut, kBF>(P, acc, b, has_rows, wave, ks, c, r,
-                                reinterpret_cast<float (*)[16][17]>(xs), orange);
+                                reinterpret_cast<float (*)[16][17]>(xs), orange, of);
 }
 
 // Windowed variant: X * s staged one window of S chunks at a time (see the
@@ -586,6 +649,8 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_window_kernel(ProblemSet p
   for (int d = 0; d < kDepth; ++d) load_chunk(d, chunk_g0(d));
   store_window();
   lds_barrier();
+  OutPrefetch of = {};
+  if (kOut) of = outlier_prefetch(P, orange, lane);
   load_window(1);
 
   // rows m >= M of the A operand only feed rows of D that are not stored
@@ -660,7 +725,7 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_window_kernel(ProblemSet p
     lds_barrier();
     load_window(j + 2);
   }
-  store_rows<kWaves, kOut, kBF>(P, acc, b, has_rows, wave, ks, c, r, red, orange);
+  store_rows<kWaves, kOut, kBF>(P, acc, b, has_rows, wave, ks, c, r, red, orange, of);
 }
 
 constexpr size_t kMaxStageBytes = 96 * 1024;
