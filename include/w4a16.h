@@ -259,10 +259,10 @@ enum { W4A16_DTYPE_F16 = 0, W4A16_DTYPE_BF16 = 1 };
 int w4a16_gemm_grouped(const w4a16_problem *problems, int count, void *stream);
 
 /* Bytes of device workspace that lets w4a16_gemm_grouped_ws split K across
- * workgroups for these problems (host only; no GPU call).  0 when no problem
- * benefits (every streaming-path problem, and tiled-path calls whose output
- * blocks already fill the GPU).  Validates like w4a16_gemm_grouped; *bytes is
- * a host pointer. */
+ * workgroups and prescale bf16 activations for these problems (host only; no
+ * GPU call).  0 when no problem benefits (fp16 streaming-path problems, and
+ * tiled-path calls whose output blocks already fill the GPU).  Validates like
+ * w4a16_gemm_grouped; *bytes is a host pointer. */
 int w4a16_gemm_workspace_size(const w4a16_problem *problems, int count, size_t *bytes);
 
 /* w4a16_gemm_grouped with a caller-owned device workspace.  Step 7 of the
@@ -271,7 +271,11 @@ int w4a16_gemm_workspace_size(const w4a16_problem *problems, int count, size_t *
  * small projections), each of S K-ranges writes fp32 partial sums to the
  * workspace, and a second kernel adds the S partials in a fixed order and
  * rounds to fp16 once, so results are reproducible run to run (they may
- * differ in the last bit from an unsplit call).  The workspace needs no
+ * differ in the last bit from an unsplit call).  For bf16 streaming-path
+ * problems whose X * s is staged in K windows, a small first kernel computes
+ * bf16(X * s) and its group sums once into the workspace, and the GEMM kernel
+ * copies them instead of recomputing them in every workgroup (the same
+ * values, so the results are identical).  The workspace needs no
  * initialisation, must hold w4a16_gemm_workspace_size() bytes for the same
  * problems (else, or when NULL, K is not split), must be 16-byte aligned
  * (EALIGN), must not overlap any input or output, and may be reused as soon

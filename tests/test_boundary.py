@@ -169,6 +169,14 @@ def test_workspace_size():
                        P(A16, A16, A16, A16, None, A16, 0, 16, 128),
                        P(A16, A16, A16, A16, None, A16, 1, 4096, 4096))
     assert (rc2, nb2) == (0, nb)
+    # bf16 streaming problems: room for bf16(X * s) [M][K] and fp32 group sums [M][G]
+    pb = P(A16, A16, A16, A16, None, A16, 9, 4096, 14336)
+    pb.dtype = w4.DTYPE_BF16
+    a256 = lambda n: -(-n // 256) * 256
+    assert ws_size(pb) == (0, a256(9 * 14336 * 2) + a256(9 * 112 * 4))
+    # launches share the workspace in stream order: the larger need counts
+    rc3, nb3 = ws_size(pb, P(A16, A16, A16, A16, None, A16, 64, 272, 4096))
+    assert rc3 == 0 and nb3 == max(nb, a256(9 * 14336 * 2) + a256(9 * 112 * 4))
     L = w4.lib()
     arr = (P * 1)(P(A16, A16, A16, A16, None, A16, 64, 272, 4096))
     assert L.w4a16_gemm_workspace_size(arr, 1, None) == -1

@@ -119,3 +119,36 @@ def test_bf16_integer_case():
         ref = np.resize(exact, (path_M, N))
         want = bf16_bits_to_f64(to_bf16_bits(np.asarray(ref, dtype=np.float32)))  # exact -> RNE
         assert np.array_equal(Y, want), path_M
+
+
+@pytest.mark.parametrize("M,N,K,awq,outl", [
+    (9, 1024, 14336, True, False),
+    (16, 2048, 4096, True, False),
+    (5, 528, 18944, False, False),
+    (8, 272, 14336, True, True),
+    (16, 1024, 4096, True, True),
+])
+def test_bf16_prescaled_windows_are_identical(M, N, K, awq, outl):
+    """With a workspace, bf16 problems that stage X * s in K windows get it from a
+    small first kernel (once per call) instead of computing it in every workgroup:
+    the same values, so the outputs are bit-identical to the call without one."""
+    torch = torch_cuda()
+    W = weights(22, M, N, K)
+    s = awq_scales(22, M, K) if awq else None
+    sd = None if s is None else to_dev(s)
+    pw = (w4.w4a16_quantize_pack_outliers(to_dev(W), sd, count=ol.page_count(N, K)) if outl
+          else w4.w4a16_quantize_pack(to_dev(W), sd))
+    X = bf16_dev(activations_bf16(22, M, M, K))
+    outs = []
+    for ws in (True, False):
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        call = w4.GroupedCall([(X, pw, sd, Y)], workspace=ws)
+        assert (call.ws_bytes > 0) == ws
+        note(f"bf16 windows M={M} N={N} K={K} outliers={outl} workspace={call.ws_bytes}")
+        call()
+        outs.append(bf16_host(Y))
+    assert np.array_equal(outs[0], outs[1])
+    if not outl:
+        q = oracle.quantize(W, s)
+        check(outs[0], oracle.gemm(bf16_bits_to_f64(activations_bf16(22, M, M, K)), q.q,
+                                   q.scales, q.zeros, s), f"prescaled M={M} N={N} K={K}")

@@ -256,15 +256,30 @@ void skinny_pieces(const w4a16_problem &p, std::vector<w4a16::GemmDesc> &out) {
   }
 }
 
+// The streaming-path launches of a call, up to skinny_max_problems() pieces
+// each, in order on one stream: each may reuse the whole workspace.
 hipError_t launch_pieces(const std::vector<w4a16::GemmDesc> &pieces, hipStream_t st,
-                         bool force_window = false) {
+                         bool force_window = false, void *workspace = nullptr,
+                         size_t workspace_bytes = 0) {
   const int cap = w4a16::skinny_max_problems();
   for (size_t i = 0; i < pieces.size(); i += cap) {
     const int n = (int)((pieces.size() - i) < (size_t)cap ? (pieces.size() - i) : (size_t)cap);
-    const hipError_t err = w4a16::launch_skinny_set(pieces.data() + i, n, st, force_window);
+    const hipError_t err = w4a16::launch_skinny_set(pieces.data() + i, n, st, force_window,
+                                                    workspace, workspace_bytes);
     if (err != hipSuccess) return err;
   }
   return hipSuccess;
+}
+
+size_t pieces_workspace_bytes(const std::vector<w4a16::GemmDesc> &pieces) {
+  const int cap = w4a16::skinny_max_problems();
+  size_t need = 0;
+  for (size_t i = 0; i < pieces.size(); i += cap) {
+    const int n = (int)((pieces.size() - i) < (size_t)cap ? (pieces.size() - i) : (size_t)cap);
+    const size_t b = w4a16::skinny_workspace_bytes(pieces.data() + i, n);
+    need = b > need ? b : need;
+  }
+  return need;
 }
 
 }  // namespace
@@ -348,12 +363,19 @@ int w4a16_gemm_workspace_size(const w4a16_problem *problems, int count, size_t *
   if (!bytes) return W4A16_EINVAL;
   const int rc = check_problems(problems, count);
   if (rc) return rc;
+  // launches run in order on one stream, so they share the workspace
   size_t need = 0;
   for (const auto &b : tiled_batches(problems, count)) {
     const size_t n = w4a16::tiled_workspace_bytes(b.data(), (int)b.size());
     need = n > need ? n : need;
   }
-  *bytes = need;
+  std::vector<w4a16::GemmDesc> pieces;
+  for (int i = 0; i < count; ++i) {
+    const w4a16_problem &p = problems[i];
+    if (p.M > 0 && w4a16_select_path(p.M, p.N, p.K) == W4A16_PATH_SKINNY) skinny_pieces(p, pieces);
+  }
+  const size_t sk = pieces_workspace_bytes(pieces);
+  *bytes = sk > need ? sk : need;
   return W4A16_OK;
 }
 
@@ -372,7 +394,8 @@ int w4a16_gemm_grouped_ws(const w4a16_problem *problems, int count, void *worksp
     if (w4a16::launch_tiled_set(b.data(), (int)b.size(), workspace, workspace_bytes, st) !=
         hipSuccess)
       return W4A16_EHIP;
-  return launch_pieces(pieces, st) == hipSuccess ? W4A16_OK : W4A16_EHIP;
+  return launch_pieces(pieces, st, false, workspace, workspace_bytes) == hipSuccess ? W4A16_OK
+                                                                                   : W4A16_EHIP;
 }
 
 int w4a16_gemm_grouped(const w4a16_problem *problems, int count, void *stream) {

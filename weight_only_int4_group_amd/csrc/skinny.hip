@@ -55,6 +55,10 @@ struct Problem {
   int split;   // waves per row block (a power of two, at most the workgroup's waves)
   const int32_t *orp, *ocol;  // fp16 outliers, row-compressed (null: none)
   const _Float16 *oval;
+  // bf16 only (else null): X * s [M][K] as bf16 bits and its per-group sums
+  // [M][G], written by prescale_kernel earlier in the call
+  uint16_t *xpre;
+  float *gpre;
 };
 
 struct ProblemSet {
@@ -193,6 +197,8 @@ __device__ __forceinline__ Problem find_problem(const ProblemSet &ps) {
   P.orp = uniform_ptr(ps.p[pi].orp);
   P.ocol = uniform_ptr(ps.p[pi].ocol);
   P.oval = uniform_ptr(ps.p[pi].oval);
+  P.xpre = uniform_ptr(ps.p[pi].xpre);
+  P.gpre = uniform_ptr(ps.p[pi].gpre);
   return P;
 }
 
@@ -519,9 +525,29 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_kernel(ProblemSet ps) {
                                 reinterpret_cast<float (*)[16][17]>(xs), orange, of);
 }
 
+// bf16 X * s and its per-group sums, once per call, for the windowed kernel
+// (which otherwise recomputes them in every workgroup, for every window).
+// One 16-lane segment per (row m, group g), the same arithmetic and
+// summation order as the staging in the kernels, so the values are identical.
+__global__ __launch_bounds__(256) void prescale_kernel(ProblemSet ps) {
+  const Problem P = find_problem(ps);
+  const int K = P.K, G = K / kGroup;
+  const int seg = ((int)blockIdx.x - P.block0) * 16 + (int)(threadIdx.x >> 4);
+  if (seg >= P.M * G) return;  // whole segments
+  const int m = seg / G, g = seg - m * G;
+  const size_t k = (size_t)m * K + (size_t)g * kGroup + (threadIdx.x & 15) * 8;
+  float part = 0.f;
+  const u32x4 v = scale_x8<true>(*reinterpret_cast<const u32x4 *>(P.X + k),
+                                 P.s ? P.s + g * kGroup + (threadIdx.x & 15) * 8 : nullptr, part);
+  part = segment_sum16(part);
+  *reinterpret_cast<u32x4 *>(P.xpre + k) = v;
+  if ((threadIdx.x & 15) == 0) P.gpre[m * G + g] = part;
+}
+
 // Windowed variant: X * s staged one window of S chunks at a time (see the
 // header).  kSlots bounds the 8-column pieces of a window each thread stages.
-template <int kGW, int kWaves, int kDepth, int kSlots, bool kOut, bool kBF, bool kW8 = false>
+template <int kGW, int kWaves, int kDepth, int kSlots, bool kOut, bool kBF, bool kW8 = false,
+          bool kPre = false>
 __global__ __launch_bounds__(kWaves * 64) void skinny_window_kernel(ProblemSet ps) {
   constexpr int kCW = kW8 ? 2 : 1;  // 16-byte code loads per lane per tile
   extern __shared__ __attribute__((aligned(16))) _Float16 xs[];
@@ -552,6 +578,7 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_window_kernel(ProblemSet p
       (void *)P.zeros, (short)0, (int)min((size_t)0x7fffffff, meta_bytes), kRsrcWord3);
   const int2 orange = kOut ? outlier_range(P, b, has_rows, ks, r) : int2{0, 0};
   const int tile_off = bb * kTileBytes * kCW + lane * 16 * kCW;    // + g * tile_stride
+  static_assert(!kPre || kBF, "prescaled X * s is a bf16 path");
   const int meta_off = (bb * kTileRows + r) * kMetaQuad * 2;      // + quad * meta_stride
   const int tile_stride = NB * kTileBytes * kCW, meta_stride = NB * kTileRows * kMetaQuad * 2;
 
@@ -587,15 +614,31 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_window_kernel(ProblemSet p
   // (buffer loads out of range), and are never multiplied.
   const int c8 = wcols / 8;
   const int cs = (int)threadIdx.x & (c8 - 1), r0 = (int)threadIdx.x / c8, rstep = kThreads / c8;
-  const __amdgpu_buffer_rsrc_t xrs =
-      __builtin_amdgcn_make_buffer_rsrc((void *)P.X, (short)0, M * K * 2, kRsrcWord3);
+  // bf16 with a prescaled X * s (prescale_kernel): the window is a plain copy
+  // of it and of its group sums
+  constexpr bool pre = kBF && kPre;
+  const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+      pre ? (void *)P.xpre : (void *)P.X, (short)0, M * K * 2, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t ssr =
       __builtin_amdgcn_make_buffer_rsrc((void *)P.s, (short)0, P.s ? K * 2 : 0, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t grs =
+      __builtin_amdgcn_make_buffer_rsrc((void *)P.gpre, (short)0, pre ? M * G * 4 : 0, kRsrcWord3);
   half8 xr[kSlots], sv;
+  float gp[kBF ? kSlots : 1];
   auto load_window = [&](int w) {
     const int k = w * wcols + cs * 8;
     const int koff = k < K ? 2 * k : 2 * M * K;  // past K: out of range, reads zeros
-    if (P.s) {
+    if (pre) {
+      // the group sum of this lane's segment (groups past G read zeros)
+      const int gw = k / kGroup;
+#pragma unroll
+      for (int i = 0; i < kSlots; ++i) {
+        const int m = r0 + i * rstep;
+        gp[kBF ? i : 0] = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(
+                       grs, m < M && gw < G ? 4 * (m * G + gw) : 4 * M * G, 0, 0));
+      }
+    } else if (P.s) {
       sv = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(ssr, k < K ? 2 * k : 2 * K, 0, 0));
     } else {
       const _Float16 one = (_Float16)1.0f;
@@ -619,6 +662,11 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_window_kernel(ProblemSet p
       const int m = r0 + i * rstep;
       if (!kBF) {
         if (m < M) *reinterpret_cast<half8 *>(&xs[m * ldx + cs * 8]) = xr[i] * sv;
+      } else if (pre) {
+        if (m < M) {
+          *reinterpret_cast<half8 *>(&xs[m * ldx + cs * 8]) = xr[i];
+          if ((cs & 15) == 0) wsum[m * wgroups + cs / 16] = gp[kBF ? i : 0];
+        }
       } else {
         float part = 0.f;
         u32x4 out;
@@ -789,6 +837,14 @@ int pow2_at_least(int v) {
   return p;
 }
 
+size_t align256(size_t n) { return (n + 255) / 256 * 256; }
+
+// Workspace of one bf16 problem's prescaled X * s: bf16 [M][K], then fp32
+// group sums [M][G].
+size_t prescale_bytes(int M, int K) {
+  return align256((size_t)M * K * 2) + align256((size_t)M * (K / kGroup) * 4);
+}
+
 }  // namespace
 
 int skinny_max_problems() { return kMaxProblems; }
@@ -842,6 +898,10 @@ hipError_t launch_group(const GemmDesc *const *d, int count, bool window, hipStr
     p.orp = static_cast<const int32_t *>(q.o_row_ptr);
     p.ocol = static_cast<const int32_t *>(q.o_col);
     p.oval = static_cast<const _Float16 *>(q.o_val);
+    p.xpre = static_cast<uint16_t *>(q.xpre);
+    p.gpre = q.xpre ? reinterpret_cast<float *>(static_cast<char *>(q.xpre) +
+                                                align256((size_t)q.M * q.K * 2))
+                    : nullptr;
     out |= q.o_row_ptr != nullptr;
     p.block0 = blocks;
     const int rb_per_wg = kWaves / split;
@@ -861,7 +921,16 @@ hipError_t launch_group(const GemmDesc *const *d, int count, bool window, hipStr
       hipLaunchKernelGGL((skinny_kernel<kChunk, kWaves, kDepth, false, false, true>), grid, threads,
                          lds, stream, ps);
   } else if (window) {
-    if (bf && out)
+    const bool pre = d[0]->xpre != nullptr;  // all or none of a launch (launch_skinny_set)
+    if (bf && out && pre)
+      hipLaunchKernelGGL(
+          (skinny_window_kernel<kChunk, kWaves, kDepth, kWindowSlots, true, true, false, true>),
+          grid, threads, lds, stream, ps);
+    else if (bf && pre)
+      hipLaunchKernelGGL(
+          (skinny_window_kernel<kChunk, kWaves, kDepth, kWindowSlots, false, true, false, true>),
+          grid, threads, lds, stream, ps);
+    else if (bf && out)
       hipLaunchKernelGGL((skinny_window_kernel<kChunk, kWaves, kDepth, kWindowSlots, true, true>),
                          grid, threads, lds, stream, ps);
     else if (bf)
@@ -890,10 +959,39 @@ hipError_t launch_group(const GemmDesc *const *d, int count, bool window, hipStr
   return hipGetLastError();
 }
 
+// bf16 X * s and group sums of the problems d[0..count) into their xpre.
+hipError_t launch_prescale(const GemmDesc *const *d, int count, hipStream_t stream) {
+  ProblemSet ps = {};
+  int blocks = 0;
+  for (int i = 0; i < count; ++i) {
+    const GemmDesc &q = *d[i];
+    Problem &p = ps.p[i];
+    p.X = static_cast<const _Float16 *>(q.X);
+    p.s = static_cast<const _Float16 *>(q.s);
+    p.M = q.M;
+    p.N = q.N;
+    p.K = q.K;
+    p.xpre = static_cast<uint16_t *>(q.xpre);
+    p.gpre = reinterpret_cast<float *>(static_cast<char *>(q.xpre) + align256((size_t)q.M * q.K * 2));
+    p.block0 = blocks;
+    blocks += (q.M * (q.K / kGroup) + 15) / 16;  // 16 segments of 16 lanes per workgroup
+  }
+  ps.count = count;
+  hipLaunchKernelGGL(prescale_kernel, dim3(blocks), dim3(256), 0, stream, ps);
+  return hipGetLastError();
+}
+
 }  // namespace
 
-hipError_t launch_skinny_set(const GemmDesc *d, int count, hipStream_t stream,
-                             bool force_window) {
+size_t skinny_workspace_bytes(const GemmDesc *d, int count) {
+  size_t n = 0;
+  for (int i = 0; i < count; ++i)
+    if (d[i].bf16 && !d[i].w8) n += prescale_bytes(d[i].M, d[i].K);
+  return n;
+}
+
+hipError_t launch_skinny_set(const GemmDesc *d, int count, hipStream_t stream, bool force_window,
+                             void *workspace, size_t workspace_bytes) {
   if (count < 1 || count > kMaxProblems) return hipErrorInvalidValue;
   // By default the whole launch uses windows as soon as one problem's X * s does
   // not fit: one launch over all problems beats a second, smaller one.  Like
@@ -921,7 +1019,23 @@ hipError_t launch_skinny_set(const GemmDesc *d, int count, hipStream_t stream,
       else
         whole[nwhole++] = d + i;
     }
-    err = launch_group(windowed, nwin, true, stream);
+    // bf16 windows: X * s once per call when the workspace has room for it
+    GemmDesc pre[kMaxProblems];
+    size_t need = 0;
+    if (want_bf && nwin > 0 && workspace) {
+      for (int i = 0; i < nwin; ++i) need += prescale_bytes(windowed[i]->M, windowed[i]->K);
+      if (need <= workspace_bytes) {
+        char *ws = static_cast<char *>(workspace);
+        for (int i = 0; i < nwin; ++i) {
+          pre[i] = *windowed[i];
+          pre[i].xpre = ws;
+          ws += prescale_bytes(pre[i].M, pre[i].K);
+          windowed[i] = pre + i;
+        }
+        err = launch_prescale(windowed, nwin, stream);
+      }
+    }
+    if (err == hipSuccess) err = launch_group(windowed, nwin, true, stream);
     if (err == hipSuccess) err = launch_group(whole, nwhole, false, stream);
   }
   return err;

@@ -44,15 +44,23 @@ struct GemmDesc {
   const void *o_row_ptr = nullptr, *o_col = nullptr, *o_val = nullptr;
   bool bf16 = false;  // X and Y are bf16 (else fp16)
   bool w8 = false;    // INT8 codes (2048-byte tiles), else INT4
+  // streaming path, bf16: workspace for X * s prescaled once per call
+  // (skinny_prescale_bytes(M, K) bytes), set by launch_skinny_set
+  void *xpre = nullptr;
 };
 
 // Streaming kernel for small M (decode and speculative verify): M <= 16.
 // launch_skinny_set runs up to skinny_max_problems() independent problems in
 // one launch; X * s is staged in K windows when it does not fit in LDS whole,
-// or always with force_window.
+// or always with force_window.  When the workspace holds
+// skinny_workspace_bytes() for the same problems, bf16 problems that run in
+// windows get X * s computed once by a small kernel first (else every
+// workgroup computes its windows' share itself).
 int skinny_max_problems();
+size_t skinny_workspace_bytes(const GemmDesc *problems, int count);
 hipError_t launch_skinny_set(const GemmDesc *problems, int count, hipStream_t stream,
-                             bool force_window = false);
+                             bool force_window = false, void *workspace = nullptr,
+                             size_t workspace_bytes = 0);
 hipError_t launch_skinny(const void *X, const void *Wq, const void *scales, const void *zeros,
                          const void *s, void *Y, int M, int N, int K, hipStream_t stream);
 
