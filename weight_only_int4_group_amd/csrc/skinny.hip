@@ -804,6 +804,11 @@ static_assert(kWindowMode >= 1 && kWindowMode <= 3, "X * s must fit in LDS or go
 #endif
 constexpr size_t kMaxWindowBytes = W4A16_SKINNY_WINDOW_KB * 1024;  // 72 KB: two workgroups per CU
 constexpr int kWindowSlots = W4A16_SKINNY_WINDOW_SLOTS;  // staged 8-column pieces per thread
+// bf16: fewer pieces keep the prescaled instance within 128 VGPRs, two 8-wave
+// workgroups per CU (with eight it takes 146); the instance that scales X
+// itself uses the same count, so both choose the same splits and give the
+// same bits
+constexpr int kWindowSlotsBF = 4;
 // LDS bytes of the whole-row kernel: X * s of one problem, at least the
 // reduction's partial sums (which reuse it).
 size_t stage_bytes(int M, int K, bool bf16) {
@@ -874,6 +879,9 @@ hipError_t launch_group(const GemmDesc *const *d, int count, bool window, hipStr
   int blocks = 0;
   size_t lds = 0;
   bool out = false;  // some problem has fp16 outliers
+  // bf16 with prescaled X * s: all or none of a launch (launch_skinny_set)
+  const bool pre = window && d[0]->bf16 && d[0]->xpre != nullptr;
+  const int slot_cap = d[0]->bf16 ? kWindowSlotsBF : kWindowSlots;
   for (int i = 0; i < count; ++i) {
     const GemmDesc &q = *d[order[i]];
     Problem &p = ps.p[i];
@@ -883,7 +891,7 @@ hipError_t launch_group(const GemmDesc *const *d, int count, bool window, hipStr
     while (split > 1 && (G + kChunk - 1) / kChunk < split) split /= 2;  // a chunk per wave
     if (window)  // a window of split chunks must fit in LDS and in the staging registers
       while (split > 1 && (window_bytes(q.M, split, q.bf16) > kMaxWindowBytes ||
-                           window_slots(q.M, split) < 1 || window_slots(q.M, split) > kWindowSlots))
+                           window_slots(q.M, split) < 1 || window_slots(q.M, split) > slot_cap))
         split /= 2;
     p.X = static_cast<const _Float16 *>(q.X);
     p.Wq = static_cast<const uint8_t *>(q.Wq);
@@ -921,20 +929,19 @@ hipError_t launch_group(const GemmDesc *const *d, int count, bool window, hipStr
       hipLaunchKernelGGL((skinny_kernel<kChunk, kWaves, kDepth, false, false, true>), grid, threads,
                          lds, stream, ps);
   } else if (window) {
-    const bool pre = d[0]->xpre != nullptr;  // all or none of a launch (launch_skinny_set)
     if (bf && out && pre)
       hipLaunchKernelGGL(
-          (skinny_window_kernel<kChunk, kWaves, kDepth, kWindowSlots, true, true, false, true>),
+          (skinny_window_kernel<kChunk, kWaves, kDepth, kWindowSlotsBF, true, true, false, true>),
           grid, threads, lds, stream, ps);
     else if (bf && pre)
       hipLaunchKernelGGL(
-          (skinny_window_kernel<kChunk, kWaves, kDepth, kWindowSlots, false, true, false, true>),
+          (skinny_window_kernel<kChunk, kWaves, kDepth, kWindowSlotsBF, false, true, false, true>),
           grid, threads, lds, stream, ps);
     else if (bf && out)
-      hipLaunchKernelGGL((skinny_window_kernel<kChunk, kWaves, kDepth, kWindowSlots, true, true>),
+      hipLaunchKernelGGL((skinny_window_kernel<kChunk, kWaves, kDepth, kWindowSlotsBF, true, true>),
                          grid, threads, lds, stream, ps);
     else if (bf)
-      hipLaunchKernelGGL((skinny_window_kernel<kChunk, kWaves, kDepth, kWindowSlots, false, true>),
+      hipLaunchKernelGGL((skinny_window_kernel<kChunk, kWaves, kDepth, kWindowSlotsBF, false, true>),
                          grid, threads, lds, stream, ps);
     else if (out)
       hipLaunchKernelGGL((skinny_window_kernel<kChunk, kWaves, kDepth, kWindowSlots, true, false>),
