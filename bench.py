@@ -527,6 +527,16 @@ def main():
             "kernel_TB/s": round(ib / ikern / 1e12, 4),
             "frac_of_hbm_peak": round(ib / ikern / 1e9 / HBM_PEAK_GBS, 4),
             "vs_int4_kernel_time": round(ikern / (avg_ms * 1e-3), 4)}
+        if not args.no_bf16:
+            ibm = with_bf16(imats, cfg, M, torch, workloads)
+            _, iblms = timed(make_calls(ibm, ipool, ic, one, w4, torch), args.steps // 2,
+                             args.warmup, torch)
+            ibkern = float(np.mean(iblms[0])) * 1e-3
+            out["int8"]["bf16"] = {"workload": "the same INT8 layer with bf16 activations and outputs",
+                                   "kernel_us_per_step": round(ibkern * 1e6, 2),
+                                   "kernel_TB/s": round(ib / ibkern / 1e12, 4),
+                                   "vs_fp16_kernel_time": round(ibkern / ikern, 4)}
+            del ibm
         del ipool, imats
         torch.cuda.empty_cache()
 

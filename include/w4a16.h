@@ -238,8 +238,8 @@ typedef struct w4a16_problem {
   int32_t dtype;
   /* Code width: 0 or 4 (INT4, the default) or 8 (INT8 codes packed by
    * W4A16_QUANT_ASYM8, N * K bytes, the same size limit as the INT4 code
-   * bytes else EINVAL); INT8 with bf16 activations or with fp16 outliers is
-   * EUNSUPPORTED, and so is any other width. */
+   * bytes else EINVAL), with fp16 or bf16 activations; INT8 with fp16
+   * outliers is EUNSUPPORTED, and so is any other width. */
   int32_t wbits;
 } w4a16_problem;
 

@@ -1,5 +1,6 @@
 """INT8 codes (W8A16): the GPU packer against the oracle's INT8 variant, bit for bit, and
-the dequantize-matmul on INT8 codes against the fp64 oracle on every kernel path.
+the dequantize-matmul on INT8 codes against the fp64 oracle on every kernel path, with fp16
+and with bf16 activations.
 
 The streaming kernel takes M <= 16 (whole-row X * s staging when it fits in LDS, K
 windows otherwise), the tiled
@@ -12,8 +13,10 @@ import pytest
 
 import oracle
 import weight_only_int4_group_amd as w4
-from tests.gpu_helpers import assert_close, h16_bits, note, to_dev, to_host, torch_cuda
-from workloads import activations, awq_scales, weights
+from tests.gpu_helpers import (MAX_REL_BF16, REL_L2_BF16, assert_close, h16_bits, note, to_dev,
+                               to_host, torch_cuda)
+from workloads import (activations, activations_bf16, awq_scales, bf16_bits_to_f64, to_bf16_bits,
+                       weights)
 
 pytestmark = pytest.mark.gpu
 
@@ -205,3 +208,67 @@ def test_int8_full_size_decode_sampled():
         Y = to_host(w4.w4a16_gemm(to_dev(X), pw, to_dev(s)))
         Yref = oracle.gemm(X, ref.q, ref.scales, ref.zeros, s)
         assert_close(Y[:, rows], Yref, f"full-size M={M}")
+
+
+def bf16_dev(bits):
+    torch = torch_cuda()
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to("cuda").view(
+        torch.bfloat16)
+
+
+def bf16_host(t):
+    torch = torch_cuda()
+    torch.cuda.synchronize()
+    return bf16_bits_to_f64(t.view(torch.int16).cpu().numpy().view(np.uint16))
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 272, 640), (5, 528, 1152), (1, 64, 14336),
+                                   (9, 48, 18944), (16, 64, 14336), (16, 16, 4096),
+                                   (17, 1024, 2048), (64, 272, 4096), (300, 272, 640)])
+def test_gemm_int8_bf16_matches_oracle(M, N, K):
+    """INT8 codes with bf16 activations and outputs on every path (whole-row and
+    windowed streaming, tiled with and without split K), at the bf16 tolerance."""
+    torch_cuda()
+    pw, s, ref = case(N, K, key=31)
+    xb = activations_bf16(31, M, M, K, outliers=True)
+    note(f"int8 bf16 gemm M={M} N={N} K={K} path={w4.w4a16_select_path(M, N, K)}")
+    Y = w4.w4a16_gemm(bf16_dev(xb), pw, to_dev(s))
+    assert str(Y.dtype) == "torch.bfloat16"
+    assert_close(bf16_host(Y), oracle.gemm(bf16_bits_to_f64(xb), ref.q, ref.scales, ref.zeros, s),
+                 f"int8 bf16 {M}x{N}x{K}", REL_L2_BF16, MAX_REL_BF16)
+
+
+@pytest.mark.parametrize("M", [1, 9, 40])
+def test_gemm_int8_bf16_integer_case(M):
+    """The integer case with bf16 activations: Y is the exact integer result (within
+    2048, so exact in fp32 partial sums), rounded once to bf16."""
+    rng = np.random.default_rng(32)
+    N, K = 64, 256
+    W = rng.integers(-128, 128, size=(N, K))
+    W[:, 0::128], W[:, 1::128] = -128, 127
+    W = W.astype(np.float16)
+    X = (rng.integers(-1, 2, size=(M, K)) * (rng.random((M, K)) < 0.06)).astype(np.float32)
+    X[:, 0:2] = 0
+    Yref = X.astype(np.float64) @ W.astype(np.float64).T
+    assert np.abs(Yref).max() <= 2048
+    note(f"int8 bf16 integer case M={M}")
+    Y = bf16_host(w4.w4a16_gemm(bf16_dev(to_bf16_bits(X)), pack8(W, None)))
+    assert np.array_equal(Y, bf16_bits_to_f64(to_bf16_bits(Yref.astype(np.float32))))
+
+
+@pytest.mark.parametrize("M,N,K", [(9, 1024, 14336), (16, 272, 4096)])
+def test_int8_bf16_prescaled_windows_are_identical(M, N, K):
+    """bf16 windows over INT8 codes: prescaled X * s (with a workspace) gives the same
+    bits as the in-kernel scaling (without one)."""
+    torch = torch_cuda()
+    pw, s, _ = case(N, K, key=33)
+    X = bf16_dev(activations_bf16(33, M, M, K))
+    outs = []
+    for ws in (True, False):
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        call = w4.GroupedCall([(X, pw, to_dev(s), Y)], workspace=ws)
+        assert (call.ws_bytes > 0) == ws
+        note(f"int8 bf16 windows M={M} N={N} K={K} workspace={call.ws_bytes}")
+        call()
+        outs.append(bf16_host(Y))
+    assert np.array_equal(outs[0], outs[1])

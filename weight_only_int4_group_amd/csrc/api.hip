@@ -319,7 +319,6 @@ int check_problems(const w4a16_problem *problems, int count) {
     if (rc) return rc;
     if (p.dtype != W4A16_DTYPE_F16 && p.dtype != W4A16_DTYPE_BF16) return W4A16_EUNSUPPORTED;
     if (p.wbits != 0 && p.wbits != 4 && p.wbits != 8) return W4A16_EUNSUPPORTED;
-    if (p.wbits == 8 && p.dtype == W4A16_DTYPE_BF16) return W4A16_EUNSUPPORTED;
     if (p.wbits == 8 && p.N * p.K > kMaxPackedBytes) return W4A16_EINVAL;
     if (p.wbits == 8 && (p.o_row_ptr || p.o_col || p.o_val)) return W4A16_EUNSUPPORTED;
     const bool any = p.o_row_ptr || p.o_col || p.o_val;

@@ -115,6 +115,22 @@ __device__ __forceinline__ u32x4 decode_word_bf16(uint32_t w) {
   return r;
 }
 
+// INT8 codes for bf16 operands: two words (columns j = 0..3 and 4..7, one
+// byte each) -> the exact bf16 values q_j (a code 0..255 has at most 8
+// significant bits, as many as bf16 holds): each byte converts to fp32
+// exactly, and the fp32's upper half is the bf16.  The zero point comes off
+// after the product, as for INT4 codes.
+__device__ __forceinline__ uint32_t bytes_to_bf16x2(uint32_t w, int sh) {
+  const float a = (float)((w >> sh) & 0xFFu), b = (float)((w >> (sh + 8)) & 0xFFu);
+  return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, a),
+                               0x07060302u);
+}
+__device__ __forceinline__ u32x4 decode_words8_bf16(uint32_t wa, uint32_t wb) {
+  u32x4 r = {bytes_to_bf16x2(wa, 0), bytes_to_bf16x2(wa, 16), bytes_to_bf16x2(wb, 0),
+             bytes_to_bf16x2(wb, 16)};
+  return r;
+}
+
 // X * s of 8 consecutive columns, rounded once to the activation type (the
 // exact product of a bf16 and an fp16 fits an fp32, so bf16 rounds once too),
 // and the fp32 sum of the 8 rounded values (bf16 only).
@@ -493,8 +509,11 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_kernel(ProblemSet ps) {
 #pragma unroll
           for (int t = 0; t < 4; ++t)
             tmp = mfma16_bf16(*reinterpret_cast<const u32x4 *>(xrow + g * kGroup + 32 * t),
-                              decode_word_bf16(cur[i][0][t]), tmp);
-          const float zb = 128.0f + (float)zp;
+                              kW8 ? decode_words8_bf16(cur[i][t >> 1 & (kCW - 1)][2 * (t & 1)],
+                                                       cur[i][t >> 1 & (kCW - 1)][2 * (t & 1) + 1])
+                                  : decode_word_bf16(cur[i][0][t]),
+                              tmp);
+          const float zb = (kW8 ? 0.0f : 128.0f) + (float)zp;
 #pragma unroll
           for (int v = 0; v < 4; ++v) acc[v] += (tmp[v] - zb * gsum[gs_row[v] + g]) * (float)sc;
         } else {
@@ -747,9 +766,13 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_window_kernel(ProblemSet p
           if (kBF) {
 #pragma unroll
             for (int t = 0; t < 4; ++t)
-              tmp = mfma16_bf16(*reinterpret_cast<const u32x4 *>(xrow + i * kGroup + 32 * t),
-                                decode_word_bf16(cur[i][0][t]), tmp);
-            const float zb = 128.0f + (float)zp;
+              tmp = mfma16_bf16(
+                  *reinterpret_cast<const u32x4 *>(xrow + i * kGroup + 32 * t),
+                  kW8 ? decode_words8_bf16(cur[i][t >> 1 & (kCW - 1)][2 * (t & 1)],
+                                           cur[i][t >> 1 & (kCW - 1)][2 * (t & 1) + 1])
+                      : decode_word_bf16(cur[i][0][t]),
+                  tmp);
+            const float zb = (kW8 ? 0.0f : 128.0f) + (float)zp;
 #pragma unroll
             for (int v = 0; v < 4; ++v) acc[v] += (tmp[v] - zb * wsum[ws_row[v] + i]) * (float)sc;
           } else {
@@ -804,10 +827,10 @@ static_assert(kWindowMode >= 1 && kWindowMode <= 3, "X * s must fit in LDS or go
 #endif
 constexpr size_t kMaxWindowBytes = W4A16_SKINNY_WINDOW_KB * 1024;  // 72 KB: two workgroups per CU
 constexpr int kWindowSlots = W4A16_SKINNY_WINDOW_SLOTS;  // staged 8-column pieces per thread
-// bf16: fewer pieces keep the prescaled instance within 128 VGPRs, two 8-wave
-// workgroups per CU (with eight it takes 146); the instance that scales X
-// itself uses the same count, so both choose the same splits and give the
-// same bits
+// bf16 and INT8 codes: fewer pieces cut the registers (the prescaled bf16
+// instance needs 110 instead of 146: two 8-wave workgroups per CU instead of
+// one); the bf16 instance that scales X itself uses the same count, so both
+// choose the same splits and give the same bits
 constexpr int kWindowSlotsBF = 4;
 // LDS bytes of the whole-row kernel: X * s of one problem, at least the
 // reduction's partial sums (which reuse it).
@@ -881,7 +904,7 @@ hipError_t launch_group(const GemmDesc *const *d, int count, bool window, hipStr
   bool out = false;  // some problem has fp16 outliers
   // bf16 with prescaled X * s: all or none of a launch (launch_skinny_set)
   const bool pre = window && d[0]->bf16 && d[0]->xpre != nullptr;
-  const int slot_cap = d[0]->bf16 ? kWindowSlotsBF : kWindowSlots;
+  const int slot_cap = d[0]->bf16 || d[0]->w8 ? kWindowSlotsBF : kWindowSlots;
   for (int i = 0; i < count; ++i) {
     const GemmDesc &q = *d[order[i]];
     Problem &p = ps.p[i];
@@ -920,11 +943,22 @@ hipError_t launch_group(const GemmDesc *const *d, int count, bool window, hipStr
   ps.count = count;
   const dim3 grid(blocks), threads(kWaves * 64);
   const bool bf = d[0]->bf16;  // one activation type (and code width) per launch
-  if (d[0]->w8) {  // INT8 codes: fp16 activations, no outliers
-    if (window)
+  if (d[0]->w8) {  // INT8 codes: no outliers
+    if (window && bf && pre)
       hipLaunchKernelGGL(
-          (skinny_window_kernel<kChunk, kWaves, kDepth, kWindowSlots, false, false, true>), grid,
+          (skinny_window_kernel<kChunk, kWaves, kDepth, kWindowSlotsBF, false, true, true, true>),
+          grid, threads, lds, stream, ps);
+    else if (window && bf)
+      hipLaunchKernelGGL(
+          (skinny_window_kernel<kChunk, kWaves, kDepth, kWindowSlotsBF, false, true, true>), grid,
           threads, lds, stream, ps);
+    else if (window)
+      hipLaunchKernelGGL(
+          (skinny_window_kernel<kChunk, kWaves, kDepth, kWindowSlotsBF, false, false, true>), grid,
+          threads, lds, stream, ps);
+    else if (bf)
+      hipLaunchKernelGGL((skinny_kernel<kChunk, kWaves, kDepth, false, true, true>), grid, threads,
+                         lds, stream, ps);
     else
       hipLaunchKernelGGL((skinny_kernel<kChunk, kWaves, kDepth, false, false, true>), grid, threads,
                          lds, stream, ps);
@@ -993,7 +1027,7 @@ hipError_t launch_prescale(const GemmDesc *const *d, int count, hipStream_t stre
 size_t skinny_workspace_bytes(const GemmDesc *d, int count) {
   size_t n = 0;
   for (int i = 0; i < count; ++i)
-    if (d[i].bf16 && !d[i].w8) n += prescale_bytes(d[i].M, d[i].K);
+    if (d[i].bf16) n += prescale_bytes(d[i].M, d[i].K);
   return n;
 }
 
@@ -1007,9 +1041,9 @@ hipError_t launch_skinny_set(const GemmDesc *d, int count, hipStream_t stream, b
   // within rounding of the exact result; each call is reproducible).  fp16 and
   // bf16 problems go in separate launches (one kernel instance each).
   hipError_t err = hipSuccess;
-  for (int cls = 0; cls < 3 && err == hipSuccess; ++cls) {
-    // classes: fp16 INT4, bf16 INT4, fp16 INT8
-    const bool want_bf = cls == 1, want_w8 = cls == 2;
+  for (int cls = 0; cls < 4 && err == hipSuccess; ++cls) {
+    // classes: fp16 INT4, bf16 INT4, fp16 INT8, bf16 INT8
+    const bool want_bf = (cls & 1) != 0, want_w8 = cls >= 2;
     auto in_class = [&](const GemmDesc &q) { return q.bf16 == want_bf && q.w8 == want_w8; };
     const GemmDesc *whole[kMaxProblems], *windowed[kMaxProblems];
     int nwhole = 0, nwin = 0;

@@ -97,6 +97,23 @@ __device__ __forceinline__ half8 dequant_words8(uint32_t wa, uint32_t wb, half2v
   return r;
 }
 
+// INT8 codes, bf16 activations: eight codes (columns j = 0..3 in wa, 4..7 in
+// wb) -> bf16((q_j - z) * scale), each rounded once: a byte converts to fp32
+// exactly, one FMA with the fp32 scale minus z * scale.
+__device__ __forceinline__ u32x4 dequant_words8_bf16(uint32_t wa, uint32_t wb, float scale,
+                                                     float zs) {
+  u32x4 r;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t w = p < 2 ? wa : wb;
+    const int sh = (p & 1) * 16;
+    const float lo = __builtin_fmaf((float)((w >> sh) & 0xFFu), scale, -zs);
+    const float hi = __builtin_fmaf((float)((w >> (sh + 8)) & 0xFFu), scale, -zs);
+    r[p] = (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+  }
+  return r;
+}
+
 constexpr int kMaxTiled = 8;  // problems per launch
 
 struct TiledProblem {
@@ -310,7 +327,10 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
         for (int j = 0; j < TN; ++j) {
           const float z = (float)__builtin_bit_cast(_Float16, (uint16_t)b.zp[j]);
           const float sv = (float)__builtin_bit_cast(_Float16, (uint16_t)b.sc[j]);
-          bop[j] = dequant_word_bf16(b.code[j][0][tt], sv, (128.0f + z) * sv);
+          bop[j] = W8 ? dequant_words8_bf16(b.code[j][tt >> 1 & (kCW - 1)][2 * (tt & 1)],
+                                            b.code[j][tt >> 1 & (kCW - 1)][2 * (tt & 1) + 1], sv,
+                                            z * sv)
+                      : dequant_word_bf16(b.code[j][0][tt], sv, (128.0f + z) * sv);
         }
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
@@ -628,7 +648,10 @@ hipError_t launch_tiled_set(const GemmDesc *d, int count, void *workspace, size_
   }
   ts.count = count;
   const dim3 grid(blocks), threads(kWM * kWN * 64);
-  if (d[0].w8)  // INT8 codes: fp16 activations, no outliers
+  if (d[0].w8 && d[0].bf16)  // INT8 codes (no outliers)
+    hipLaunchKernelGGL((tiled_kernel<kWM, kWN, kTM, kTN, false, true, true>), grid, threads, 0,
+                       stream, ts);
+  else if (d[0].w8)
     hipLaunchKernelGGL((tiled_kernel<kWM, kWN, kTM, kTN, false, false, true>), grid, threads, 0,
                        stream, ts);
   else if (d[0].bf16 && out)  // one activation type (and code width) per launch
