@@ -69,15 +69,19 @@ class OutlierResult:
 
 
 def quantize_with_outliers(W: np.ndarray, s: np.ndarray | None, count: int,
-                           symmetric: bool = False, granularity: str = "group") -> OutlierResult:
+                           symmetric: bool = False, granularity: str = "group",
+                           bits: int = 4) -> OutlierResult:
     """Split W into `count` fp16 outliers and an INT4 remainder (O1-O5), the remainder on
-    the symmetric grid or at an asymmetric granularity (group, channel or tensor)."""
+    the symmetric grid or at an asymmetric granularity (group, channel or tensor); with
+    bits = 8 the remainder takes INT8 codes instead (the same O1-O5 on the 0..255 grid)."""
+    if symmetric and bits != 4:
+        raise ValueError("the symmetric grid is INT4 only")
     W = np.asarray(W)
     if not np.all(np.isfinite(W.astype(np.float64))):
         raise NonFiniteInput("non-finite W (kept weights included)")   # R9
     mask = select(W, s, count)
     rest = np.where(mask, np.float16(0), W).astype(np.float16)        # O4
-    quant = quantize_symmetric(rest, s) if symmetric else quantize(rest, s, granularity)
+    quant = quantize_symmetric(rest, s) if symmetric else quantize(rest, s, granularity, bits)
     rows, cols = np.nonzero(mask)                                      # row-major order (O5)
     row_ptr = np.zeros(W.shape[0] + 1, dtype=np.int64)
     np.add.at(row_ptr, rows + 1, 1)

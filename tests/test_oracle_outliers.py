@@ -147,3 +147,35 @@ def test_mutations_are_caught():
     unforced = oracle.quantize(W, s)
     z = unforced.zeros.astype(np.float64)[:, np.arange(K) // 128]
     assert not np.all(unforced.q[res.mask] == z[res.mask])
+
+
+def test_o_int8_remainder():
+    """The same split with INT8 codes for the remainder: count 0 is the plain INT8
+    quantizer byte for byte; kept positions decode to exactly 0 (code == zero point)
+    and merge back to W exactly; groups only shrink; the round-trip bound holds on
+    the 0..255 grid; selection and CSR do not depend on the code width."""
+    rng = np.random.default_rng(46)
+    N, K = 48, 512
+    W, s = _data(rng, N, K, planted=25)
+    plain8 = oracle.quantize(W, s, bits=8)
+    r0 = ol.quantize_with_outliers(W, s, 0, bits=8)
+    assert np.array_equal(r0.quant.q, plain8.q)
+    assert np.array_equal(r0.quant.scales.view(np.uint16), plain8.scales.view(np.uint16))
+    count = ol.page_count(N, K) + 5
+    r8 = ol.quantize_with_outliers(W, s, count, bits=8)
+    r4 = ol.quantize_with_outliers(W, s, count)
+    assert np.array_equal(r8.mask, r4.mask) and np.array_equal(r8.col, r4.col)
+    assert np.array_equal(r8.row_ptr, r4.row_ptr) and np.array_equal(r8.val.view(np.uint16),
+                                                                    r4.val.view(np.uint16))
+    g = np.arange(K) // 128
+    z = r8.quant.zeros.astype(np.float64)[:, g]
+    assert np.all(r8.quant.q[r8.mask] == z[r8.mask])
+    assert np.array_equal(ol.merged_weight(r8, W, s)[r8.mask], W[r8.mask].astype(np.float64))
+    sc = r8.quant.scales.astype(np.float64)
+    assert np.all(sc <= plain8.scales.astype(np.float64))
+    Wp = W.astype(np.float64) / s.astype(np.float64)[None, :]
+    recon = (r8.quant.q.astype(np.float64) - z) * sc[:, g]
+    assert np.all(np.abs(np.where(r8.mask, 0.0, Wp) - recon) <= sc[:, g] / 2 + 1e-300)
+    assert r8.quant.q.max() > 15                      # the codes really use the byte
+    with pytest.raises(ValueError):
+        ol.quantize_with_outliers(W, s, count, symmetric=True, bits=8)
