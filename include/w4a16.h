@@ -153,9 +153,10 @@ int w4a16_quantize_pack_mode(const void *W, const void *s, int64_t N, int64_t K,
  * Keeps exactly `count` weights of W in fp16 -- the largest |W[n][k] / s[k]|
  * (|W| when s is NULL; one correctly rounded fp64 division, so the ranking is
  * exact), ties to the lower flat index n * K + k -- and quantizes and packs
- * the rest exactly as w4a16_quantize_pack_mode would with the kept weights
- * replaced by 0: they leave their groups' ranges and their codes decode to
- * exactly 0.  The kept weights are written row-compressed:
+ * the rest exactly as w4a16_quantize_pack_mode would (any mode, INT8 codes
+ * included) with the kept weights replaced by 0: they leave their groups'
+ * ranges and their codes decode to exactly 0.  The kept weights are written
+ * row-compressed:
  *   o_row_ptr int32 [N + 1] (o_row_ptr[0] = 0, o_row_ptr[N] = count),
  *   o_col int32 [count] and o_val fp16 [count]: the columns (increasing
  *   within a row) and the original fp16 values of row n at
@@ -238,8 +239,8 @@ typedef struct w4a16_problem {
   int32_t dtype;
   /* Code width: 0 or 4 (INT4, the default) or 8 (INT8 codes packed by
    * W4A16_QUANT_ASYM8, N * K bytes, the same size limit as the INT4 code
-   * bytes else EINVAL), with fp16 or bf16 activations; INT8 with fp16
-   * outliers is EUNSUPPORTED, and so is any other width. */
+   * bytes else EINVAL), with fp16 or bf16 activations and with or without
+   * fp16 outliers; any other width is EUNSUPPORTED. */
   int32_t wbits;
 } w4a16_problem;
 

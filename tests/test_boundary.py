@@ -321,7 +321,7 @@ def test_grouped_code_width_validation():
 
     for bits in (1, 2, 3, 5, 16, -4):
         assert rc(wbits=bits) == -3, bits
-    assert rc(wbits=8, o_row_ptr=A4, o_col=A4, o_val=A4) == -3  # INT8 takes no fp16 outliers
+    assert rc(wbits=8, o_row_ptr=A4, o_col=A4) == -1            # outliers: all three or none
     assert rc(wbits=8, dtype=w4.DTYPE_BF16, X=ODD) == -2        # bf16 with INT8 is validated
     assert rc(wbits=8, N=32768, K=65536) == -1                  # 2 GiB of INT8 codes
     assert rc(wbits=8, K=100) == -1

@@ -272,3 +272,54 @@ def test_int8_bf16_prescaled_windows_are_identical(M, N, K):
         call()
         outs.append(bf16_host(Y))
     assert np.array_equal(outs[0], outs[1])
+
+
+@pytest.mark.parametrize("N,K,awq", [(16, 128, False), (272, 640, True), (1024, 1024, True)])
+def test_int8_outlier_pack_matches_oracle(N, K, awq):
+    """fp16 outliers over INT8 codes: the row-compressed outliers and the packed INT8
+    rest bit-exact with the oracle's split (count 0, one, the page's share, many)."""
+    from oracle import outliers as ol
+    W = weights(34, 1, N, K)
+    s = awq_scales(34, 1, K) if awq else None
+    for count in (0, 1, ol.page_count(N, K), 37 * N):
+        note(f"int8 outlier pack N={N} K={K} count={count}")
+        pw = w4.w4a16_quantize_pack_outliers(to_dev(W), None if s is None else to_dev(s), count,
+                                             w4.QUANT_ASYM8)
+        assert pw.wbits == 8
+        ref = ol.quantize_with_outliers(W, s, count, bits=8)
+        assert np.array_equal(to_host(pw.o_row_ptr), ref.row_ptr)
+        assert np.array_equal(to_host(pw.o_col), ref.col)
+        assert np.array_equal(h16_bits(to_host(pw.o_val)), h16_bits(ref.val))
+        assert np.array_equal(to_host(pw.wq), oracle.pack_codes8(ref.quant.q))
+        assert np.array_equal(h16_bits(to_host(pw.scales)),
+                              h16_bits(oracle.pack_meta(ref.quant.scales)))
+        assert np.array_equal(h16_bits(to_host(pw.zeros)),
+                              h16_bits(oracle.pack_meta(ref.quant.zeros)))
+
+
+@pytest.mark.parametrize("bf", [False, True])
+@pytest.mark.parametrize("M,N,K", [(1, 272, 640), (5, 528, 1152), (9, 48, 18944),
+                                   (16, 64, 14336), (40, 272, 4096), (300, 272, 640)])
+def test_gemm_int8_with_outliers(M, N, K, bf):
+    """INT8 codes plus fp16 outliers (the page's share, and extra ones planted in one
+    group) on every path, fp16 and bf16 activations, against the oracle's merged
+    weight."""
+    from oracle import outliers as ol
+    torch_cuda()
+    W = weights(35, N + K, N, K)
+    s = awq_scales(35, N + K, K)
+    W[3, 130:134] = np.float16(0.9)             # several kept weights in one group
+    count = ol.page_count(N, K) + 4
+    pw = w4.w4a16_quantize_pack_outliers(to_dev(W), to_dev(s), count, w4.QUANT_ASYM8)
+    res = ol.quantize_with_outliers(W, s, count, bits=8)
+    assert res.mask[3, 130:134].all()
+    note(f"int8 outliers gemm M={M} N={N} K={K} bf16={bf}")
+    if bf:
+        xb = activations_bf16(35, M, M, K, outliers=True)
+        Y = bf16_host(w4.w4a16_gemm(bf16_dev(xb), pw, to_dev(s)))
+        assert_close(Y, ol.gemm(bf16_bits_to_f64(xb), res, W, s), f"int8+out bf16 {M}x{N}x{K}",
+                     REL_L2_BF16, MAX_REL_BF16)
+    else:
+        X = activations(35, M, M, K, outliers=True)
+        Y = to_host(w4.w4a16_gemm(to_dev(X), pw, to_dev(s)))
+        assert_close(Y, ol.gemm(X, res, W, s), f"int8+out {M}x{N}x{K}")

@@ -235,14 +235,15 @@ def w4a16_quantize_pack_outliers(W, s=None, count: int | None = None,
     N, K = W.shape
     if count is None:
         count = page_outlier_count(N, K)
-    wq_b, sc_b, z_b = w4a16_packed_sizes(N, K)
+    wq_b, sc_b, z_b = w4a16_packed_sizes(N, K, mode)
     dev = W.device
     pw = PackedWeight(torch.empty(wq_b, dtype=torch.uint8, device=dev),
                       torch.empty(sc_b // 2, dtype=torch.float16, device=dev),
                       torch.empty(z_b // 2, dtype=torch.float16, device=dev), N, K,
                       torch.empty(N + 1, dtype=torch.int32, device=dev),
                       torch.empty(max(count, 1), dtype=torch.int32, device=dev)[:count],
-                      torch.empty(max(count, 1), dtype=torch.float16, device=dev)[:count])
+                      torch.empty(max(count, 1), dtype=torch.float16, device=dev)[:count],
+                      8 if mode == QUANT_ASYM8 else 4)
     ws = torch.empty(w4a16_outlier_workspace_size(N, K), dtype=torch.uint8, device=dev)
     rc = lib().w4a16_quantize_pack_outliers(
         _dev_ptr(W, "W", torch.float16), _dev_ptr(s, "s", torch.float16, K), N, K, mode, count,

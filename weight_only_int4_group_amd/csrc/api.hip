@@ -195,8 +195,8 @@ int w4a16_quantize_pack_outliers(const void *W, const void *s, int64_t N, int64_
                                  int64_t count, void *Wq, void *scales, void *zeros,
                                  void *o_row_ptr, void *o_col, void *o_val, void *workspace,
                                  size_t workspace_bytes, void *stream) {
-  if (!known_mode(mode) || mode == W4A16_QUANT_ASYM8) return W4A16_EUNSUPPORTED;
-  int rc = check_shape(N, K);
+  if (!known_mode(mode)) return W4A16_EUNSUPPORTED;
+  int rc = check_shape_mode(N, K, mode);
   if (rc) return rc;
   if (count < 0 || count > N * K || count > INT32_MAX) return W4A16_EINVAL;
   if (!W || !Wq || !scales || !zeros || !o_row_ptr || !workspace) return W4A16_EINVAL;
@@ -320,7 +320,6 @@ int check_problems(const w4a16_problem *problems, int count) {
     if (p.dtype != W4A16_DTYPE_F16 && p.dtype != W4A16_DTYPE_BF16) return W4A16_EUNSUPPORTED;
     if (p.wbits != 0 && p.wbits != 4 && p.wbits != 8) return W4A16_EUNSUPPORTED;
     if (p.wbits == 8 && p.N * p.K > kMaxPackedBytes) return W4A16_EINVAL;
-    if (p.wbits == 8 && (p.o_row_ptr || p.o_col || p.o_val)) return W4A16_EUNSUPPORTED;
     const bool any = p.o_row_ptr || p.o_col || p.o_val;
     if (any && !(p.o_row_ptr && p.o_col && p.o_val)) return W4A16_EINVAL;  // all or none
     if (any && ((reinterpret_cast<uintptr_t>(p.o_row_ptr) & 3u) ||

@@ -879,6 +879,30 @@ int skinny_max_problems() { return kMaxProblems; }
 
 namespace {
 
+// The windowed instances over INT8 codes.
+void launch_window8(bool bf, bool out, bool pre, dim3 grid, dim3 threads, size_t lds,
+                    hipStream_t stream, const ProblemSet &ps) {
+  constexpr int S = kWindowSlotsBF;
+  if (bf && out && pre)
+    hipLaunchKernelGGL((skinny_window_kernel<kChunk, kWaves, kDepth, S, true, true, true, true>),
+                       grid, threads, lds, stream, ps);
+  else if (bf && pre)
+    hipLaunchKernelGGL((skinny_window_kernel<kChunk, kWaves, kDepth, S, false, true, true, true>),
+                       grid, threads, lds, stream, ps);
+  else if (bf && out)
+    hipLaunchKernelGGL((skinny_window_kernel<kChunk, kWaves, kDepth, S, true, true, true>), grid,
+                       threads, lds, stream, ps);
+  else if (bf)
+    hipLaunchKernelGGL((skinny_window_kernel<kChunk, kWaves, kDepth, S, false, true, true>), grid,
+                       threads, lds, stream, ps);
+  else if (out)
+    hipLaunchKernelGGL((skinny_window_kernel<kChunk, kWaves, kDepth, S, true, false, true>), grid,
+                       threads, lds, stream, ps);
+  else
+    hipLaunchKernelGGL((skinny_window_kernel<kChunk, kWaves, kDepth, S, false, false, true>), grid,
+                       threads, lds, stream, ps);
+}
+
 // One launch over the problems d[0..count): whole-row X * s staging or K windows.
 hipError_t launch_group(const GemmDesc *const *d, int count, bool window, hipStream_t stream) {
   if (count == 0) return hipSuccess;
@@ -943,21 +967,17 @@ hipError_t launch_group(const GemmDesc *const *d, int count, bool window, hipStr
   ps.count = count;
   const dim3 grid(blocks), threads(kWaves * 64);
   const bool bf = d[0]->bf16;  // one activation type (and code width) per launch
-  if (d[0]->w8) {  // INT8 codes: no outliers
-    if (window && bf && pre)
-      hipLaunchKernelGGL(
-          (skinny_window_kernel<kChunk, kWaves, kDepth, kWindowSlotsBF, false, true, true, true>),
-          grid, threads, lds, stream, ps);
-    else if (window && bf)
-      hipLaunchKernelGGL(
-          (skinny_window_kernel<kChunk, kWaves, kDepth, kWindowSlotsBF, false, true, true>), grid,
-          threads, lds, stream, ps);
-    else if (window)
-      hipLaunchKernelGGL(
-          (skinny_window_kernel<kChunk, kWaves, kDepth, kWindowSlotsBF, false, false, true>), grid,
-          threads, lds, stream, ps);
+  if (d[0]->w8) {  // INT8 codes
+    if (window)
+      launch_window8(bf, out, pre, grid, threads, lds, stream, ps);
+    else if (bf && out)
+      hipLaunchKernelGGL((skinny_kernel<kChunk, kWaves, kDepth, true, true, true>), grid, threads,
+                         lds, stream, ps);
     else if (bf)
       hipLaunchKernelGGL((skinny_kernel<kChunk, kWaves, kDepth, false, true, true>), grid, threads,
+                         lds, stream, ps);
+    else if (out)
+      hipLaunchKernelGGL((skinny_kernel<kChunk, kWaves, kDepth, true, false, true>), grid, threads,
                          lds, stream, ps);
     else
       hipLaunchKernelGGL((skinny_kernel<kChunk, kWaves, kDepth, false, false, true>), grid, threads,

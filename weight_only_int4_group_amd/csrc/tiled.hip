@@ -648,8 +648,14 @@ hipError_t launch_tiled_set(const GemmDesc *d, int count, void *workspace, size_
   }
   ts.count = count;
   const dim3 grid(blocks), threads(kWM * kWN * 64);
-  if (d[0].w8 && d[0].bf16)  // INT8 codes (no outliers)
+  if (d[0].w8 && d[0].bf16 && out)  // INT8 codes
+    hipLaunchKernelGGL((tiled_kernel<kWM, kWN, kTM, kTN, true, true, true>), grid, threads, 0,
+                       stream, ts);
+  else if (d[0].w8 && d[0].bf16)
     hipLaunchKernelGGL((tiled_kernel<kWM, kWN, kTM, kTN, false, true, true>), grid, threads, 0,
+                       stream, ts);
+  else if (d[0].w8 && out)
+    hipLaunchKernelGGL((tiled_kernel<kWM, kWN, kTM, kTN, true, false, true>), grid, threads, 0,
                        stream, ts);
   else if (d[0].w8)
     hipLaunchKernelGGL((tiled_kernel<kWM, kWN, kTM, kTN, false, false, true>), grid, threads, 0,
