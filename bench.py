@@ -242,6 +242,22 @@ def batched_line(cfg, M, mats, pool, copies, w4, torch, workloads, steps=200, wa
             "TFLOP/s": round(fl / (wall / steps) / 1e12, 2)}
 
 
+def gemv_line(torch, w4, workloads, steps=400, warmup=40):
+    """The single 1024 x 1024 matrix at M = 1: 0.56 MB per call, far below what
+    keeps HBM busy, so the time is launch latency, not bandwidth."""
+    cfg = workloads.config_by_name("gemv_1024")
+    mats, pool, _, copies = prepare_layer(cfg, 1, torch, w4, workloads)
+    byts = sum(m["bytes"] for m in mats)
+    wall, lms = timed(make_calls(mats, pool, copies, [[0]], w4, torch), steps, warmup, torch)
+    kern = float(np.mean(lms[0])) * 1e-3
+    return {"workload": f"{cfg.name}: one 1024x1024 matrix, M=1, no AWQ s, {copies} rotating "
+                        "copies", "bytes": byts,
+            "us_per_call": round(wall / steps * 1e6, 2), "kernel_us": round(kern * 1e6, 2),
+            "kernel_TB/s": round(byts / kern / 1e12, 4),
+            "frac_of_hbm_peak": round(byts / kern / 1e9 / HBM_PEAK_GBS, 4),
+            "note": "launch-latency bound: the roofline time at 8 TB/s is 0.07 us"}
+
+
 def variant(mats, groups, launch_ms, steps, wall, unit_key):
     step_units = sum(m[unit_key] for m in mats)
     kern = sum(float(np.mean(x)) for x in launch_ms)  # ms of kernel time per step
@@ -253,7 +269,9 @@ def variant(mats, groups, launch_ms, steps, wall, unit_key):
     else:
         out["TFLOP/s"] = round(step_units / (wall / steps) / 1e12, 2)
     out["launches"] = [{"matrices": [mats[j]["name"] for j in grp],
-                        "us": round(float(np.median(launch_ms[i])) * 1e3, 2)}
+                        "us": round(float(np.median(launch_ms[i])) * 1e3, 2),
+                        "us_p10": round(float(np.percentile(launch_ms[i], 10)) * 1e3, 2),
+                        "us_p90": round(float(np.percentile(launch_ms[i], 90)) * 1e3, 2)}
                        for i, grp in enumerate(groups)]
     return out
 
@@ -451,9 +469,21 @@ def main():
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": profiled_traffic("skinny_decode_llama3_8b_layer_m1_counters.txt",
-                                                 "skinny.hip")},
+                                                 "skinny.hip"),
+                     # spread of the per-launch durations (blocks of 10 launches)
+                     "launch_us_p10_median_p90": [round(float(np.percentile(lms[0], q)) * 1e3, 3)
+                                                  for q in (10, 50, 90)]},
     }
     if not args.no_variants:
+        # the same launches over one buffer copy: the 116 MB layer then largely
+        # stays in the 256 MB last-level cache, so this is not an HBM figure
+        wwall, wl = timed(make_calls(mats, [[p[0]] for p in pool], 1, one, w4, torch), 200, 20,
+                          torch)
+        wms = float(np.mean(wl[0]))
+        out["warm_same_buffer"] = {"workload": f"{cfg.name}, one weight copy reused every step",
+                                   "kernel_us_per_step": round(wms * 1e3, 2),
+                                   "kernel_TB/s": round(step_bytes / (wms * 1e-3) / 1e12, 4)}
+        out["gemv_1024"] = gemv_line(torch, w4, workloads)
         idx = {n: i for i, n in enumerate(names)}
         dep = [[idx["q"], idx["k"], idx["v"]], [idx["o"]], [idx["gate"], idx["up"]], [idx["down"]]]
         sep = [[j] for j in range(len(mats))]
