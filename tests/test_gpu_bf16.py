@@ -152,3 +152,41 @@ def test_bf16_prescaled_windows_are_identical(M, N, K, awq, outl):
         q = oracle.quantize(W, s)
         check(outs[0], oracle.gemm(bf16_bits_to_f64(activations_bf16(22, M, M, K)), q.q,
                                    q.scales, q.zeros, s), f"prescaled M={M} N={N} K={K}")
+
+
+def test_bf16_graph_replay_with_prescale():
+    """A grouped bf16 call whose windowed problems use the prescale kernel (two launches
+    per call, plus a tiled split-K problem and its reduction), captured in a HIP graph
+    and replayed with eager work in between: every replay gives the eager bits."""
+    torch = torch_cuda()
+    items = []
+    for i, (M, N, K) in enumerate([(9, 1024, 14336), (16, 272, 4096), (1, 272, 640),
+                                   (64, 272, 4096)]):
+        W = weights(23, i, N, K)
+        s = awq_scales(23, i, K)
+        pw = w4.w4a16_quantize_pack(to_dev(W), to_dev(s))
+        X = bf16_dev(activations_bf16(23, i, M, K))
+        items.append((X, pw, to_dev(s), torch.empty((M, N), dtype=torch.bfloat16, device="cuda")))
+    call = w4.GroupedCall(items)
+    assert call.ws_bytes > 0
+    call()
+    eager = [bf16_host(it[3]).copy() for it in items]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    note("graph capture of a bf16 grouped call with prescaled windows")
+    with torch.cuda.graph(g):
+        call()
+    for rep in range(4):
+        for it in items:
+            it[3].fill_(float("nan"))
+        call.ws.fill_(255)                     # the workspace holds nothing between calls
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for it, ref in zip(items, eager):
+            assert np.array_equal(bf16_host(it[3]), ref), rep
