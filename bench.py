@@ -398,11 +398,40 @@ def cpu_baseline(cfg, M, workloads, rows=1024, budget_s=10.0):
         dt = time.perf_counter() - t0
         if dt >= budget_s:
             break
-    return {"value": float(f"{byts / dt / 1e12:.6g}"), "unit": "TB/s", "cores": int(threads),
-            "kind": "oracle", "seconds": round(dt, 2),
-            "sample": f"first {rows} rows of each of the {len(cfg.matrices)} matrices of "
-                      f"{cfg.name} at M={M}, oracle.gemm (fp64 dequantize + matmul) "
-                      f"repeated {reps}x"}
+    out = {"value": float(f"{byts / dt / 1e12:.6g}"), "unit": "TB/s", "cores": int(threads),
+           "kind": "oracle", "seconds": round(dt, 2),
+           "sample": f"first {rows} rows of each of the {len(cfg.matrices)} matrices of "
+                     f"{cfg.name} at M={M}, oracle.gemm (fp64 dequantize + matmul) "
+                     f"repeated {reps}x"}
+    # the offline step on the same sample, and the single 1024 x 1024 matrix with one
+    # BLAS thread (the oracle's quantize and pack are single-threaded NumPy)
+    t0 = time.perf_counter()
+    wbytes = 0
+    for mi, mat in enumerate(cfg.matrices):
+        n = min(rows, mat.N)
+        Wr = workloads.weight_rows(cfg.weight_key, mi, mat.N, mat.K, 0, n)
+        s = workloads.awq_scales(cfg.weight_key, mi, mat.K) if cfg.awq else None
+        ref = oracle.quantize(Wr, s)
+        oracle.pack_codes(ref.q)
+        oracle.pack_meta(ref.scales)
+        oracle.pack_meta(ref.zeros)
+        wbytes += 2 * n * mat.K
+    out["quantize_pack"] = {"MB_of_fp16_weights_per_s": round(wbytes / (time.perf_counter() - t0)
+                                                              / 1e6, 2),
+                            "sample": f"the same {rows}-row slices: oracle.quantize + pack_codes "
+                                      "+ pack_meta"}
+    g1 = workloads.config_by_name("gemv_1024")
+    W1 = workloads.weights(g1.weight_key, 0, 1024, 1024)
+    X1 = workloads.activations(g1.weight_key, 0, 1, 1024)
+    r1 = oracle.quantize(W1, None)
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1):
+        t0, n1 = time.perf_counter(), 0
+        while time.perf_counter() - t0 < 1.0:
+            oracle.gemm(X1, r1.q, r1.scales, r1.zeros, None)
+            n1 += 1
+        out["gemv_1024_one_thread_ms"] = round((time.perf_counter() - t0) / n1 * 1e3, 3)
+    return out
 
 
 def main():
