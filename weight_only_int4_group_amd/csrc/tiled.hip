@@ -573,8 +573,16 @@ constexpr int kWM = TileShape::WM, kWN = TileShape::WN, kTM = TileShape::TM, kTN
 constexpr int kBM = kWM * kTM * 16, kBN = kWN * kTN * 16;
 // CUs x resident workgroups per CU (two waves per SIMD, four SIMDs)
 constexpr long long kBlockSlots = 256 * 8 / (kWM * kWN);
-constexpr int kMinSplitGroups = 8;          // no split shorter than this many groups
+constexpr int kMinSplitGroups = 8;          // splits about this many groups long at the shortest
 constexpr int kMaxSplit = 16;
+// Cost model of one launch (measured on the 70B prefill and Qwen2-7B batched
+// shapes): with every slot busy, a workgroup takes about kStageUs per group
+// plus kBlockStages groups' worth of prologue, epilogue and tail; workgroups
+// run in rounds of kBlockSlots; split partials cost their fp32 writes and the
+// reduction's reads at about kReduceBytesPerUs.
+constexpr double kStageUs = 2.3;
+constexpr double kBlockStages = 2.0;
+constexpr double kReduceBytesPerUs = 4.0e6;
 
 int tiles_of(const GemmDesc &d) { return ((d.N + kBN - 1) / kBN) * ((d.M + kBM - 1) / kBM); }
 
@@ -582,16 +590,35 @@ size_t part_bytes(const GemmDesc &d, int split) {
   return split > 1 ? ((size_t)split * d.M * d.N * sizeof(float) + 255) / 256 * 256 : 0;
 }
 
-// K splits of each problem of one launch: enough workgroups to fill every
-// slot, and no workgroup longer than the launch's average share of groups.
+// K splits of each problem of one launch.  Every problem's groups are cut
+// into ranges of at most T groups; T is the one whose modelled launch time is
+// least: ceil(workgroups / slots) rounds, each as long as the longest range,
+// plus the reduction of the partials.  Counting whole rounds matters: a launch
+// a few workgroups past a multiple of the slots takes a whole extra round.
+// Ties keep the longer ranges (fewer partials).
 void choose_splits(const GemmDesc *d, int count, int *split) {
-  long long units = 0;
-  for (int i = 0; i < count; ++i) units += (long long)tiles_of(d[i]) * (d[i].K / kGroup);
-  const long long target = std::max<long long>(kMinSplitGroups, (units + kBlockSlots - 1) / kBlockSlots);
-  for (int i = 0; i < count; ++i) {
-    const long long G = d[i].K / kGroup;
-    split[i] = (int)std::min<long long>(std::min<long long>(kMaxSplit, G), (G + target - 1) / target);
-    if (split[i] < 1) split[i] = 1;
+  int gmax = 1;
+  for (int i = 0; i < count; ++i) gmax = std::max(gmax, d[i].K / kGroup);
+  double best = 0.0;
+  for (int T = gmax; T >= 1; --T) {
+    int s[kMaxTiled];
+    long long blocks = 0;
+    int longest = 0;
+    double reduce_bytes = 0.0;
+    for (int i = 0; i < count; ++i) {
+      const int G = d[i].K / kGroup;
+      const int cap = std::min(std::min(kMaxSplit, G), (G + kMinSplitGroups - 1) / kMinSplitGroups);
+      s[i] = std::max(1, std::min(cap, (G + T - 1) / T));
+      blocks += (long long)tiles_of(d[i]) * s[i];
+      longest = std::max(longest, (G + s[i] - 1) / s[i]);
+      if (s[i] > 1) reduce_bytes += (double)(4 * s[i] + 2) * d[i].M * d[i].N;
+    }
+    const long long rounds = (blocks + kBlockSlots - 1) / kBlockSlots;
+    const double t = (double)rounds * (longest + kBlockStages) * kStageUs + reduce_bytes / kReduceBytesPerUs;
+    if (T == gmax || t < best) {
+      best = t;
+      for (int i = 0; i < count; ++i) split[i] = s[i];
+    }
   }
 }
 
