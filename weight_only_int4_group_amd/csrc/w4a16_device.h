@@ -59,8 +59,12 @@ __device__ __forceinline__ half8 decode_word(uint32_t w, half2v bias) {
   return r;
 }
 
+// 16 bytes from device memory as a global (not flat) load: flat loads count
+// against both the vector-memory and the LDS wait counters and may complete
+// out of order, so a pending one makes every later wait a full drain.
 __device__ __forceinline__ half8 load_half8(const _Float16 *p) {
-  return *reinterpret_cast<const half8 *>(p);
+  typedef const __attribute__((address_space(1))) half8 *global_half8;
+  return *(global_half8)(p);
 }
 
 __device__ __forceinline__ half8 zero_half8() {
