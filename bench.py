@@ -60,12 +60,18 @@ def alg_bytes(M, N, K, awq, bits=4):
     return N * K * bits // 8 + 4 * N * K // 128 + (2 * K if awq else 0) + 2 * M * K + 2 * M * N
 
 
+KERNEL_HEADERS = ("w4a16_device.h", "w4a16_internal.h")
+
+
 def kernel_source_sha(name):
-    """SHA-256 of a kernel source file, to tie a counter profile to the code it measured."""
+    """SHA-256 of a kernel source file followed by the device headers it includes, to
+    tie a counter profile to the code it measured."""
     import hashlib
-    path = os.path.join(ROOT, "weight_only_int4_group_amd", "csrc", name)
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for part in (name,) + KERNEL_HEADERS:
+        with open(os.path.join(ROOT, "weight_only_int4_group_amd", "csrc", part), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def profiled_traffic(summary, source):
