@@ -597,10 +597,19 @@ size_t part_bytes(const GemmDesc &d, int split) {
 // a few workgroups past a multiple of the slots takes a whole extra round.
 // Ties keep the longer ranges (fewer partials).
 void choose_splits(const GemmDesc *d, int count, int *split) {
-  int gmax = 1;
-  for (int i = 0; i < count; ++i) gmax = std::max(gmax, d[i].K / kGroup);
+  // Only range lengths ceil(G / n) for some problem's G and n <= kMaxSplit give
+  // distinct split vectors; try those, longest first.
+  int cand[kMaxTiled * kMaxSplit];
+  int nc = 0;
+  for (int i = 0; i < count; ++i) {
+    const int G = d[i].K / kGroup;
+    for (int n = 1; n <= kMaxSplit && n <= G; ++n) cand[nc++] = (G + n - 1) / n;
+  }
+  std::sort(cand, cand + nc, [](int a, int b) { return a > b; });
+  nc = (int)(std::unique(cand, cand + nc) - cand);
   double best = 0.0;
-  for (int T = gmax; T >= 1; --T) {
+  for (int ci = 0; ci < nc; ++ci) {
+    const int T = cand[ci];
     int s[kMaxTiled];
     long long blocks = 0;
     int longest = 0;
@@ -615,7 +624,7 @@ void choose_splits(const GemmDesc *d, int count, int *split) {
     }
     const long long rounds = (blocks + kBlockSlots - 1) / kBlockSlots;
     const double t = (double)rounds * (longest + kBlockStages) * kStageUs + reduce_bytes / kReduceBytesPerUs;
-    if (T == gmax || t < best) {
+    if (ci == 0 || t < best) {
       best = t;
       for (int i = 0; i < count; ++i) split[i] = s[i];
     }
