@@ -282,7 +282,8 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
   // its own slots, so it can take the group's codes into registers, wait for
   // those reads, and then let the next group's DMA overwrite the slots.
   constexpr int kBBufs = W8 ? 1 : 2;
-  __shared__ __attribute__((aligned(16))) uint8_t Bs[kBBufs][WM * WN * TN * kTileBytes * kCW];
+  __shared__ __attribute__((aligned(16))) uint8_t Bs0[WM * WN * TN * kTileBytes * kCW];
+  __shared__ __attribute__((aligned(16))) uint8_t Bs1[kBBufs > 1 ? WM * WN * TN * kTileBytes * kCW : 16];
   struct BRegs {
     u32x4 code[TN][kCW];
     uint32_t sc[TN], zp[TN];  // raw fp16 bits of each row block's scale and zero point
@@ -291,17 +292,28 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
   // group-major tiles and quad-major metadata: the row block's part of each
   // offset is per lane, the group's part uniform
   const int tile_stride = NB * kTileBytes * kCW, meta_stride = NB * kTileRows * kMetaQuad * 2;
-  auto load_b = [&](int g, int buf, BRegs &b) {
+  // code buffer `buf` of this wave: two separate LDS arrays (not one array
+  // of two), so the compiler can tell a read of one from a DMA into the other
+  auto bslot = [&](int buf) -> uint8_t * {
+    return (kBBufs == 1 || buf % kBBufs == 0) ? Bs0 : Bs1;
+  };
+  // row blocks past N re-read the last one (in bounds) and are never stored
+  auto load_codes = [&](int g, int buf) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      // row blocks past N re-read the last one (in bounds) and are never stored
       const int rb = min(rb0 + j, NB - 1);
 #pragma unroll
       for (int h = 0; h < kCW; ++h)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             wrs,
-            (__attribute__((address_space(3))) void *)&Bs[buf % kBBufs][((wave * TN + j) * kCW + h) * kTileBytes],
+            (__attribute__((address_space(3))) void *)(bslot(buf) + ((wave * TN + j) * kCW + h) * kTileBytes),
             16, (rb * 64 + lane) * 16 * kCW + 16 * h, g * tile_stride, 0, 0);
+    }
+  };
+  auto load_meta = [&](int g, BRegs &b) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int rb = min(rb0 + j, NB - 1);
       const int mo = (rb * kTileRows + r) * kMetaQuad * 2;
       const int qo = (g / kMetaQuad) * meta_stride + (g % kMetaQuad) * 2;
       b.sc[j] = __builtin_amdgcn_raw_buffer_load_b16(srs, mo, qo, 0);
@@ -463,34 +475,89 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
   // group's MFMAs, and write the next X * s to the other LDS buffer.  Steps
   // alternate LDS buffers and metadata register sets, two steps per
   // iteration, so nothing is copied between them.
-  auto step = [&](int g, BRegs &cur, BRegs &nxt, int buf) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the DMA writes are not seen by the compiler
+  auto take_codes = [&](BRegs &b, int buf) {
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int h = 0; h < kCW; ++h)
-        cur.code[j][h] = *reinterpret_cast<const u32x4 *>(
-            &Bs[buf % kBBufs][((wave * TN + j) * kCW + h) * kTileBytes + lane * 16]);
+        b.code[j][h] = *reinterpret_cast<const u32x4 *>(
+            bslot(buf) + ((wave * TN + j) * kCW + h) * kTileBytes + lane * 16);
+  };
+  auto step = [&](int g, BRegs &cur, BRegs &nxt, int buf) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the DMA writes are not seen by the compiler
+    take_codes(cur, buf);
     // one INT8 buffer: the reads must land before the next DMA overwrites it
     if (W8) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     const bool more = g + 1 < ge;
     if (more) {
       load_a(g + 1);
-      load_b(g + 1, buf ^ 1, nxt);
+      load_codes(g + 1, buf ^ 1);
+      load_meta(g + 1, nxt);
     }
     compute(cur, buf);
     if (has_out) apply_outliers(g, buf);
     if (more) store_a(buf ^ 1);
     lds_barrier();
   };
+  // Two groups of codes in flight (INT4 codes, no outliers), with the same
+  // two code buffers.  A step's codes are taken into registers at the end of
+  // the step before; once they have landed the buffer is free, and the step
+  // refills it with group g + 2's codes, issued last, after group g + 1's X
+  // and metadata.  All three, and the store of the next X * s, happen
+  // unconditionally (past the range they re-read the last group into
+  // registers and buffers nobody reads again), so a step has no branches (at
+  // a join the compiler forgets which buffer a DMA in flight writes), every
+  // step issues the same loads, and the wait before taking the next group's
+  // codes is always "all but the newest kCodeLoads loads" (this step's DMA).
+  constexpr bool kDepth2 = !OUT && !W8;
+  constexpr int kCodeLoads = TN * kCW;  // vector memory loads of one load_codes
+  static_assert(!kDepth2 || kCodeLoads == 4, "the two-deep wait below counts 4 loads");
+  auto step2 = [&](int g, BRegs &cur, BRegs &nxt, int buf) {
+    const int gn = min(g + 1, ge - 1);
+    load_a(gn);
+    load_meta(gn, nxt);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this buffer's code reads have landed
+    load_codes(min(g + 2, ge - 1), buf);
+    // keep the DMA here, ahead of the MFMAs (the scheduler would sink it)
+    __builtin_amdgcn_sched_barrier(0);
+    compute(cur, buf);
+    store_a(buf ^ 1);  // (past the range: the last group again, never read)
+    // group g + 1's codes (DMA'd a step earlier): s_waitcnt vmcnt(4), expcnt
+    // and lgkmcnt at their maxima (7, 15), through the builtin so that the
+    // compiler's own wait counting knows it
+    __builtin_amdgcn_s_waitcnt(4 | (7 << 4) | (15 << 8));
+    take_codes(nxt, buf ^ 1);
+    lds_barrier();
+  };
   load_a(gb);
-  load_b(gb, 0, b0);
+  load_meta(gb, b0);
+  load_codes(gb, 0);
+  if (kDepth2) load_codes(min(gb + 1, ge - 1), 1);  // issued last: the first wait leaves it in flight
   if (has_out) outlier_start();  // its waits overlap the first group's loads
   store_a(0);
+  if (kDepth2) {
+    __builtin_amdgcn_s_waitcnt(4 | (7 << 4) | (15 << 8));
+    take_codes(b0, 0);
+  }
   lds_barrier();
-  for (int g = gb; g < ge; g += 2) {
-    step(g, b0, b1, 0);
-    if (g + 1 < ge) step(g + 1, b1, b0, 1);
+  if (kDepth2) {
+    // both steps unconditional, so the register sets keep their roles across
+    // the back edge (nothing is copied, so nothing waits for loads in flight)
+    int g = gb;
+    for (; g + 1 < ge; g += 2) {
+      step2(g, b0, b1, 0);
+      step2(g + 1, b1, b0, 1);
+    }
+    if (g < ge) step2(g, b0, b1, 0);
+    // the last steps' loads re-read the range's last group into registers
+    // and LDS nothing reads; they must land before the workgroup's LDS is
+    // released
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  } else {
+    for (int g = gb; g < ge; g += 2) {
+      step(g, b0, b1, 0);
+      if (g + 1 < ge) step(g + 1, b1, b0, 1);
+    }
   }
   if (has_out) {
     // late entries of the last group (a third or later in one row), from global X
