@@ -183,6 +183,31 @@ def test_workspace_size():
     assert ws_size(P(A16, A16, A16, A16, None, A16, 64, 272, 100))[0] == -1
 
 
+def test_split_counts_whole_rounds():
+    """K splits of a grouped tiled call are chosen by whole rounds of resident
+    workgroups (host-only, through the workspace size).  Qwen2-7B-shaped layer,
+    64 x 256 output blocks, 512 slots: at M = 64 the 14-group ranges of the plain
+    fill-the-slots rule give 514 workgroups (two rounds); 15-group ranges give 500
+    (down in 10 splits, the six 28-group rows in 2).  At M = 256 one round cannot
+    hold the layer; two rounds of 30-group ranges split only down (5 ways)."""
+    P = w4.Problem
+    shapes = [(3584, 3584), (512, 3584), (512, 3584), (3584, 3584), (18944, 3584),
+              (18944, 3584), (3584, 18944)]
+
+    def layer(M):
+        return [P(A16, A16, A16, A16, None, A16, M, N, K) for N, K in shapes]
+
+    splits64 = [2, 2, 2, 2, 2, 2, 10]
+    rc, nb = ws_size(*layer(64))
+    assert rc == 0 and nb == sum(s * 64 * N * 4 for s, (N, _) in zip(splits64, shapes))
+    blocks = sum(s * -(-N // 256) for s, (N, _) in zip(splits64, shapes))
+    assert blocks == 500
+    rc, nb = ws_size(*layer(256))
+    assert rc == 0 and nb == 5 * 256 * 3584 * 4
+    # prefill-sized calls fill the GPU without splitting
+    assert ws_size(P(A16, A16, A16, A16, None, A16, 4096, 28672, 8192)) == (0, 0)
+
+
 def test_grouped_ws_validation():
     L = w4.lib()
     good = w4.Problem(A16, A16, A16, A16, None, A16, 0, 16, 128)
