@@ -209,8 +209,8 @@ def test_grouped_matches_single_calls_and_oracle():
     """One grouped call over problems of mixed shapes, M (including 0 and a tiled-path M)
     and AWQ scales: each output matches the oracle and the single-call output within
     tolerance, and the same call again gives the same bits.  Nine streaming problems
-    take two launches of the kernel; one problem (M=16, K=4096) needs K windows, so its
-    launch runs windowed while the other launch stages whole rows."""
+    take two launches; one problem (M=16, K=4096) needs K windows, so its launch is a
+    mixed one: that problem's workgroups walk windows, the others stage whole rows."""
     torch_cuda()
     cases = [(1, 272, 640, True), (1, 16, 128, False), (5, 528, 1152, True), (0, 64, 256, False),
              (40, 272, 640, False), (16, 1024, 4096, True), (3, 48, 384, False),
@@ -233,6 +233,30 @@ def test_grouped_matches_single_calls_and_oracle():
         assert np.array_equal(Y.view(np.uint16), Y2.view(np.uint16)), f"{M}x{N}x{K}"
         single = to_host(w4.w4a16_gemm(Xd, pw, sd))
         assert_close(Y, single, f"grouped vs single {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M", [5, 9])
+def test_mixed_launch_verify_layer(M):
+    """The 8B layer's seven shapes at a verify batch (fewer rows of W each): down's
+    X * s (K = 14336) does not fit in LDS while the others' does, so one launch mixes
+    whole-row staging and K windows.  Each output matches the oracle and the single
+    call (whole rows for K = 4096, windows for K = 14336), and repeats bit for bit."""
+    torch_cuda()
+    shapes = [(256, 4096), (64, 4096), (64, 4096), (256, 4096), (512, 4096), (512, 4096),
+              (256, 14336)]
+    items, refs = [], []
+    for i, (N, K) in enumerate(shapes):
+        pw, s, ref = packed_case(N, K, True, key=11, mat=i)
+        X = activations(11, 10 * M + i, M, K)
+        items.append((to_dev(X), pw, to_dev(s)))
+        refs.append(oracle.gemm(X, ref.q, ref.scales, ref.zeros, s))
+    note(f"mixed streaming launch, 8B layer shapes, M={M}")
+    Ys = [to_host(y) for y in w4.w4a16_gemm_grouped(items)]
+    again = [to_host(y) for y in w4.w4a16_gemm_grouped(items)]
+    for (N, K), (Xd, pw, sd), Y, Y2, Yref in zip(shapes, items, Ys, again, refs):
+        assert_close(Y, Yref, f"mixed {M}x{N}x{K}")
+        assert np.array_equal(Y.view(np.uint16), Y2.view(np.uint16)), f"{M}x{N}x{K}"
+        assert_close(Y, to_host(w4.w4a16_gemm(Xd, pw, sd)), f"mixed vs single {M}x{N}x{K}")
 
 
 def test_graph_replay_matches_eager():

@@ -33,6 +33,9 @@
 // a row block take one chunk each, all row blocks of the workgroup share the
 // window, and the next window's X * s is loaded into registers while the
 // current one is multiplied, then written over it between two LDS barriers.
+// A call whose fp16 problems are of both kinds (speculative verify: the down
+// projection's long rows do not fit, the others do) runs as one launch in
+// which each workgroup stages its problem's X * s the way it fits.
 #include "w4a16_device.h"
 #include "w4a16_internal.h"
 
@@ -75,6 +78,7 @@ struct Problem {
   // [M][G], written by prescale_kernel earlier in the call
   uint16_t *xpre;
   float *gpre;
+  int window;  // hybrid launches: this problem walks K in windows
 };
 
 struct ProblemSet {
@@ -389,11 +393,11 @@ __device__ __forceinline__ void store_rows(const Problem &P, float4v acc, int b,
   }
 }
 
+// Whole-row body: xs (dynamic LDS) holds X * s, then (after the last use of
+// X) the split-K reduction.
 template <int kGW, int kWaves, int kDepth, bool kOut, bool kBF, bool kW8 = false>
-__global__ __launch_bounds__(kWaves * 64) void skinny_kernel(ProblemSet ps) {
+__device__ __forceinline__ void skinny_body(const ProblemSet &ps, _Float16 *xs) {
   constexpr int kCW = kW8 ? 2 : 1;  // 16-byte code loads per lane per tile
-  // X * s, then (after the last use of X) the split-K reduction
-  extern __shared__ __attribute__((aligned(16))) _Float16 xs[];
 
   const Problem P = find_problem(ps);
   const int M = P.M, N = P.N, K = P.K, S = P.split;
@@ -561,6 +565,12 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_kernel(ProblemSet ps) {
                                 reinterpret_cast<float (*)[16][17]>(xs), orange, of);
 }
 
+template <int kGW, int kWaves, int kDepth, bool kOut, bool kBF, bool kW8 = false>
+__global__ __launch_bounds__(kWaves * 64) void skinny_kernel(ProblemSet ps) {
+  extern __shared__ __attribute__((aligned(16))) _Float16 xs[];
+  skinny_body<kGW, kWaves, kDepth, kOut, kBF, kW8>(ps, xs);
+}
+
 // bf16 X * s and its per-group sums, once per call, for the windowed kernel
 // (which otherwise recomputes them in every workgroup, for every window).
 // One 16-lane segment per (row m, group g), the same arithmetic and
@@ -582,12 +592,12 @@ __global__ __launch_bounds__(256) void prescale_kernel(ProblemSet ps) {
 
 // Windowed variant: X * s staged one window of S chunks at a time (see the
 // header).  kSlots bounds the 8-column pieces of a window each thread stages.
+// xs (dynamic LDS) holds the window, then (after the last window) the split-K
+// reduction.
 template <int kGW, int kWaves, int kDepth, int kSlots, bool kOut, bool kBF, bool kW8 = false,
           bool kPre = false>
-__global__ __launch_bounds__(kWaves * 64) void skinny_window_kernel(ProblemSet ps) {
+__device__ __forceinline__ void skinny_window_body(const ProblemSet &ps, _Float16 *xs) {
   constexpr int kCW = kW8 ? 2 : 1;  // 16-byte code loads per lane per tile
-  extern __shared__ __attribute__((aligned(16))) _Float16 xs[];
-  __shared__ float red[kWaves][16][17];
   constexpr int kThreads = kWaves * 64;
 
   const Problem P = find_problem(ps);
@@ -814,7 +824,32 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_window_kernel(ProblemSet p
     lds_barrier();
     load_window(j + 2);
   }
-  store_rows<kWaves, kOut, kBF>(P, acc, b, has_rows, wave, ks, c, r, red, orange, of);
+  // every wave is past the last barrier: the window's LDS takes the partial sums
+  store_rows<kWaves, kOut, kBF>(P, acc, b, has_rows, wave, ks, c, r,
+                                reinterpret_cast<float (*)[16][17]>(xs), orange, of);
+}
+
+template <int kGW, int kWaves, int kDepth, int kSlots, bool kOut, bool kBF, bool kW8 = false,
+          bool kPre = false>
+__global__ __launch_bounds__(kWaves * 64) void skinny_window_kernel(ProblemSet ps) {
+  extern __shared__ __attribute__((aligned(16))) _Float16 xs[];
+  skinny_window_body<kGW, kWaves, kDepth, kSlots, kOut, kBF, kW8, kPre>(ps, xs);
+}
+
+// Both kinds in one launch (fp16 INT4 codes without outliers): a workgroup
+// stages the whole rows of its problem's X * s when they fit in LDS, and
+// walks K in windows otherwise (the problem's `window` flag).
+template <int kGW, int kWaves, int kDepth, int kSlots>
+__global__ __launch_bounds__(kWaves * 64) void skinny_hybrid_kernel(ProblemSet ps) {
+  extern __shared__ __attribute__((aligned(16))) _Float16 xs[];
+  int pi = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxProblems; ++i)
+    if (i < ps.count && (int)blockIdx.x >= ps.p[i].block0) pi = i;
+  if (uniform_int(ps.p[pi].window))
+    skinny_window_body<kGW, kWaves, kDepth, kSlots, false, false>(ps, xs);
+  else
+    skinny_body<kGW, kWaves, kDepth, false, false>(ps, xs);
 }
 
 constexpr size_t kMaxStageBytes = 96 * 1024;
@@ -836,6 +871,12 @@ constexpr int kDepth = W4A16_SKINNY_DEPTH;  // chunks in flight per wave
 // 1: window the problems whose X * s does not fit, 2: always window, 3:
 // window the whole call when one problem does not fit
 constexpr int kWindowMode = W4A16_SKINNY_WINDOW;
+#ifndef W4A16_SKINNY_HYBRID
+#define W4A16_SKINNY_HYBRID 1
+#endif
+// fp16 INT4 calls with problems of both kinds: one launch in which each
+// problem stages its X * s the way it fits (skinny_hybrid_kernel)
+constexpr bool kHybridLaunch = W4A16_SKINNY_HYBRID != 0;
 static_assert(kWindowMode >= 1 && kWindowMode <= 3, "X * s must fit in LDS or go in windows");
 #ifndef W4A16_SKINNY_WINDOW_KB
 #define W4A16_SKINNY_WINDOW_KB 72
@@ -921,8 +962,15 @@ void launch_window8(bool bf, bool out, bool pre, dim3 grid, dim3 threads, size_t
                        threads, lds, stream, ps);
 }
 
-// One launch over the problems d[0..count): whole-row X * s staging or K windows.
-hipError_t launch_group(const GemmDesc *const *d, int count, bool window, hipStream_t stream) {
+// LDS bytes of the split-K partial sums (the kernels reuse the X * s space).
+constexpr size_t kRedBytes = (size_t)kWaves * 16 * 17 * sizeof(float);
+
+enum LaunchKind { kWhole = 0, kWindowed = 1, kHybrid = 2 };
+
+// One launch over the problems d[0..count): whole-row X * s staging, K
+// windows, or (kHybrid: fp16 INT4 codes without outliers) each problem the
+// way its X * s fits.
+hipError_t launch_group(const GemmDesc *const *d, int count, LaunchKind kind, hipStream_t stream) {
   if (count == 0) return hipSuccess;
   // How many waves share a row block: enough waves in the whole launch to keep
   // HBM busy, and no wave walking more than kMaxGroupsPerWave groups.
@@ -944,6 +992,7 @@ hipError_t launch_group(const GemmDesc *const *d, int count, bool window, hipStr
   int blocks = 0;
   size_t lds = 0;
   bool out = false;  // some problem has fp16 outliers
+  const bool window = kind == kWindowed;
   // bf16 with prescaled X * s: all or none of a launch (launch_skinny_set)
   const bool pre = window && d[0]->bf16 && d[0]->xpre != nullptr;
   const int slot_cap = d[0]->bf16 || d[0]->w8 ? kWindowSlotsBF : kWindowSlots;
@@ -951,10 +1000,12 @@ hipError_t launch_group(const GemmDesc *const *d, int count, bool window, hipStr
     const GemmDesc &q = *d[order[i]];
     Problem &p = ps.p[i];
     const int G = q.K / kGroup, NB = q.N / kTileRows;
+    const bool win = kind == kWindowed ||
+                     (kind == kHybrid && stage_bytes(q.M, q.K, q.bf16) > kMaxStageBytes);
     int split = s_fill;
     while (split < kWaves && (G + split - 1) / split > kMaxGroupsPerWave) split *= 2;
     while (split > 1 && (G + kChunk - 1) / kChunk < split) split /= 2;  // a chunk per wave
-    if (window)  // a window of split chunks must fit in LDS and in the staging registers
+    if (win)  // a window of split chunks must fit in LDS and in the staging registers
       while (split > 1 && (window_bytes(q.M, split, q.bf16) > kMaxWindowBytes ||
                            window_slots(q.M, split) < 1 || window_slots(q.M, split) > slot_cap))
         split /= 2;
@@ -976,16 +1027,22 @@ hipError_t launch_group(const GemmDesc *const *d, int count, bool window, hipStr
                                                 align256((size_t)q.M * q.K * 2))
                     : nullptr;
     out |= q.o_row_ptr != nullptr;
+    p.window = win;
     p.block0 = blocks;
     const int rb_per_wg = kWaves / split;
     blocks += (NB + rb_per_wg - 1) / rb_per_wg;
-    const size_t need = window ? window_bytes(q.M, split, q.bf16) : stage_bytes(q.M, q.K, q.bf16);
+    const size_t wb = window_bytes(q.M, split, q.bf16);
+    const size_t need = win ? (wb > kRedBytes ? wb : kRedBytes) : stage_bytes(q.M, q.K, q.bf16);
     lds = need > lds ? need : lds;
   }
   ps.count = count;
   const dim3 grid(blocks), threads(kWaves * 64);
   const bool bf = d[0]->bf16;  // one activation type (and code width) per launch
-  if (d[0]->w8) {  // INT8 codes
+  if (kind == kHybrid) {
+    if (bf || out || d[0]->w8) return hipErrorInvalidValue;  // not instantiated
+    hipLaunchKernelGGL((skinny_hybrid_kernel<kChunk, kWaves, kDepth, kWindowSlots>), grid, threads,
+                       lds, stream, ps);
+  } else if (d[0]->w8) {  // INT8 codes
     if (window)
       launch_window8(bf, out, pre, grid, threads, lds, stream, ps);
     else if (bf && out)
@@ -1085,9 +1142,23 @@ hipError_t launch_skinny_set(const GemmDesc *d, int count, hipStream_t stream, b
     auto in_class = [&](const GemmDesc &q) { return q.bf16 == want_bf && q.w8 == want_w8; };
     const GemmDesc *whole[kMaxProblems], *windowed[kMaxProblems];
     int nwhole = 0, nwin = 0;
-    bool any = false;
+    bool any = false, all = true, outl = false;
+    const GemmDesc *members[kMaxProblems];
+    int nm = 0;
     for (int i = 0; i < count; ++i)
-      if (in_class(d[i])) any |= stage_bytes(d[i].M, d[i].K, d[i].bf16) > kMaxStageBytes;
+      if (in_class(d[i])) {
+        const bool big = stage_bytes(d[i].M, d[i].K, d[i].bf16) > kMaxStageBytes;
+        any |= big;
+        all &= big;
+        outl |= d[i].o_row_ptr != nullptr;
+        members[nm++] = d + i;
+      }
+    // fp16 INT4 without outliers: problems that fit stage whole rows and the
+    // others walk windows, in the same launch
+    if (kHybridLaunch && cls == 0 && any && !all && !outl && !force_window && kWindowMode == 3) {
+      err = launch_group(members, nm, kHybrid, stream);
+      continue;
+    }
     for (int i = 0; i < count; ++i) {
       if (!in_class(d[i])) continue;
       const bool fits = stage_bytes(d[i].M, d[i].K, d[i].bf16) <= kMaxStageBytes;
@@ -1114,8 +1185,8 @@ hipError_t launch_skinny_set(const GemmDesc *d, int count, hipStream_t stream, b
         err = launch_prescale(windowed, nwin, stream);
       }
     }
-    if (err == hipSuccess) err = launch_group(windowed, nwin, true, stream);
-    if (err == hipSuccess) err = launch_group(whole, nwhole, false, stream);
+    if (err == hipSuccess) err = launch_group(windowed, nwin, kWindowed, stream);
+    if (err == hipSuccess) err = launch_group(whole, nwhole, kWhole, stream);
   }
   return err;
 }
