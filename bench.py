@@ -119,6 +119,21 @@ def profile_run(torch, w4, workloads):
     print("profile run done", flush=True)
 
 
+def profile_run_batches(torch, w4, workloads, name, Ms):
+    """A short sequence for wave-level counters: ten grouped calls of one layer
+    configuration at each batch size in Ms (one launch per call, plus the split-K
+    reduction where the tiled kernel splits K)."""
+    cfg = workloads.config_by_name(name)
+    for M in Ms:
+        mats, pool, _, copies = prepare_layer(cfg, M, torch, w4, workloads, copies_min_bytes=0)
+        calls = make_calls(mats, pool, copies, [list(range(len(mats)))], w4, torch)
+        for i in range(10):
+            calls[i % copies][0]()
+        torch.cuda.synchronize()
+        del calls, pool, mats
+        print(f"profile run: {name} M={M} done", flush=True)
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -456,8 +471,11 @@ def main():
     ap.add_argument("--no-gptq", action="store_true")
     ap.add_argument("--no-int8", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--profile-run", action="store_true",
-                    help="only the short fixed sequence used for counter collection")
+    ap.add_argument("--profile-run", nargs="?", const="layer", choices=["layer", "verify", "batched"],
+                    help="only a short fixed sequence for counter collection: 'layer' (the "
+                         "default: a calibration copy, 20 decode steps, the 70B prefill "
+                         "matrices), 'verify' (8B layer at M=2, 5, 9) or 'batched' (Qwen2-7B "
+                         "layer at M=64, 256)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path "
@@ -472,6 +490,12 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     w4.lib()  # fail loudly if the HIP library is missing
+    if args.profile_run == "verify":
+        profile_run_batches(torch, w4, workloads, "llama3_8b_verify", (2, 5, 9))
+        return
+    if args.profile_run == "batched":
+        profile_run_batches(torch, w4, workloads, "qwen2_7b_batched_decode", (64, 256))
+        return
     if args.profile_run:
         profile_run(torch, w4, workloads)
         return
