@@ -58,6 +58,20 @@ def round_up_fp16(v: np.ndarray) -> np.ndarray:
 GRANULARITIES = ("group", "channel", "tensor")
 
 
+def _extremes(Wp: np.ndarray, granularity: str):
+    """min and max of W' over what one scale covers, per (row, group slot) [N][G]: the
+    group itself, its whole row (channel), or the whole tensor (discosf sec.2.1)."""
+    N, K = Wp.shape
+    G = K // GROUP
+    if granularity == "group":
+        Wg = Wp.reshape(N, G, GROUP)
+        return Wg.min(axis=2), Wg.max(axis=2)
+    if granularity == "channel":
+        return (np.repeat(Wp.min(axis=1, keepdims=True), G, axis=1),
+                np.repeat(Wp.max(axis=1, keepdims=True), G, axis=1))
+    return np.full((N, G), Wp.min()), np.full((N, G), Wp.max())
+
+
 def quantize(W: np.ndarray, s: np.ndarray | None = None, granularity: str = "group",
              bits: int = 4) -> QuantResult:
     """Quantize fp16 ``W[N][K]`` (optionally divided by fp16 ``s[K]`` first) to INT4 groups.
@@ -98,13 +112,7 @@ def quantize(W: np.ndarray, s: np.ndarray | None = None, granularity: str = "gro
 
     # Range of each group (or row, or tensor), widened to contain 0 (R3);
     # scale = range / 15 rounded up to fp16 (R4, R5).
-    if granularity == "group":
-        lo, hi = Wg.min(axis=2), Wg.max(axis=2)
-    elif granularity == "channel":
-        lo = np.repeat(Wp.min(axis=1, keepdims=True), G, axis=1)
-        hi = np.repeat(Wp.max(axis=1, keepdims=True), G, axis=1)
-    else:
-        lo, hi = np.full((N, G), Wp.min()), np.full((N, G), Wp.max())
+    lo, hi = _extremes(Wp, granularity)
     mn = np.minimum(lo, 0.0)
     mx = np.maximum(hi, 0.0)
     rng = mx - mn

@@ -18,11 +18,11 @@ Readings where the page leaves a step open (taken identically by the library):
   S2 the acceptance test is the exact comparison u * p_draft <= p_target in
      fp64 (the product of two fp32 values is exact there), so p_draft = 0
      always accepts;
-  S3 a draw is an inverse-CDF draw in fixed point.  Each probability p is
-     taken to fx(p) = floor(p * 2^40); the target row's weights are fx(p_target)
-     and the corrected residual's are max(0, fx(p_target) - fx(p_draft)), the
-     page's max(0, p_target - p_draft) formed on the fixed-point values (within
-     one unit, 2^-40, of the fixed point of the real difference).  Weights are
+  S3 a draw is an inverse-CDF draw in fixed point, fx(p) = floor(p * 2^40).  The
+     target row's weights are fx(p_target); the corrected residual's are
+     fx(max(0, p_target - p_draft)): the page's difference, formed in fp64 from the
+     two fp32 values (exact whenever their exponents are at most 29 apart, else
+     rounded once to nearest), then taken to fixed point.  Weights are
      summed exactly in integers; with u' the sampling uniform, T = (floor(u' *
      2^32) * S) >> 32 for S = sum of the weights, and the token is the smallest
      x whose inclusive prefix sum exceeds T.  Sums are exact, so the order of
@@ -77,8 +77,9 @@ def draw(w: np.ndarray, u: float) -> int:
 
 
 def residual_weights(pt_row: np.ndarray, pd_row: np.ndarray) -> np.ndarray:
-    """The corrected residual max(0, p_target - p_draft) on the fixed-point values (S3)."""
-    return np.maximum(fixed_weights(pt_row) - fixed_weights(pd_row), 0)
+    """The page's corrected residual max(0, p_target - p_draft), in fixed point (S3)."""
+    d = np.asarray(pt_row, dtype=np.float64) - np.asarray(pd_row, dtype=np.float64)
+    return fixed_weights(np.maximum(d, 0.0))
 
 
 def verify(p_target: np.ndarray, p_draft: np.ndarray, draft: np.ndarray, u_accept: np.ndarray,

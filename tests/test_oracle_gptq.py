@@ -6,13 +6,22 @@ Q-2  the page's objective: on correlated calibration data ||W X - W_hat X||_F^2 
      below that of round-to-nearest on the same X (with and without AWQ s);
 Q-3  the objective is invariant to scaling X by a power of two, bit for bit;
 Q-4  U is upper triangular with U^T U = (H + damping)^-1;
-and a mutation (error propagated with the wrong sign) that fails Q-2.
+Q-5  the compensated weights in closed form: when column k is reached, the row's
+     remaining weights are those that minimise the page's objective (with the damped
+     H) given the codes already chosen for columns 0..k-1, i.e. the least-squares
+     continuation v = w[k:] + (w[:k] - w_hat[:k]) H[:k, k:] H[k:, k:]^-1.  Every group's
+     scale and zero point are the R3-R5 values of v over the group at its first
+     column (checked in exact rationals), and every code is the nearest code to v_k;
+and mutations (error propagated with the wrong sign; group parameters formed from
+the uncompensated W') that fail Q-2 and Q-5.
 """
+from fractions import Fraction
 import numpy as np
 import pytest
 
 import oracle
 from oracle import gptq
+from oracle.exact import nearest_code, smallest_fp16_at_least
 
 
 def _data(seed, N, K, n, awq):
@@ -72,3 +81,71 @@ def test_mutation_wrong_sign_fails_q2(monkeypatch):
                         lambda H, damp=gptq.DAMP: -real(H, damp) + 2 * np.diag(np.diag(real(H, damp))))
     lm = gptq.layer_loss(W, s, gptq.quantize_gptq(W, s, X), X)
     assert not lm < 0.9 * lr
+
+
+def _near_boundary(x: float, tol: float = 1e-9) -> bool:
+    """True when x lies within tol (relative) of a rounding boundary of rint."""
+    f = x - np.floor(x)
+    return abs(f - 0.5) < tol * max(1.0, abs(x))
+
+
+def _check_q5(W, s, X, damp=gptq.DAMP):
+    """Q-5 on the oracle's result: group parameters and codes against the least-squares
+    continuation of the already-quantized columns.  Returns how many (row, group) pairs
+    were skipped because v sits within rounding noise of a boundary (the closed form
+    and the sequential updates agree to ~1e-12, not bit for bit)."""
+    N, K = W.shape
+    res = gptq.quantize_gptq(W, s, X, damp)
+    Wp = W.astype(np.float64)
+    Xs = X.astype(np.float64)
+    if s is not None:
+        Wp = Wp / s.astype(np.float64)[None, :]
+        Xs = Xs * s.astype(np.float64)[None, :]
+    H = 2.0 * Xs.T @ Xs
+    Hd = H + damp * np.mean(np.diag(H)) * np.eye(K)
+    g_of = np.arange(K) // 128
+    sc = res.scales.astype(np.float64)[:, g_of]
+    zp = res.zeros.astype(np.float64)[:, g_of]
+    What = (res.q.astype(np.float64) - zp) * sc            # dequantized, in W' units
+    skipped = 0
+    for k in range(K):
+        a = Wp[:, :k] - What[:, :k]
+        v = Wp[:, k:] + (a @ Hd[:k, k:]) @ np.linalg.inv(Hd[k:, k:]) if k else Wp.copy()
+        g = k // 128
+        for n in range(N):
+            if k % 128 == 0:                                 # the group's parameters
+                grp = v[n, :128]
+                mn, mx = min(grp.min(), 0.0), max(grp.max(), 0.0)
+                want, _ = smallest_fp16_at_least(Fraction(mx - mn) / 15)
+                lo, _ = smallest_fp16_at_least(Fraction(mx - mn) * (1 - 1e-9) / 15)
+                hi, _ = smallest_fp16_at_least(Fraction(mx - mn) * (1 + 1e-9) / 15)
+                if lo != hi or _near_boundary(-mn / float(want)):
+                    skipped += 1
+                    continue
+                assert Fraction(float(res.scales[n, g])) == want, (n, g)
+                assert float(res.zeros[n, g]) == np.rint(-mn / float(want)), (n, g)
+            t = v[n, 0] / float(res.scales[n, g])
+            if _near_boundary(t):
+                continue
+            assert res.q[n, k] == nearest_code(Fraction(t), int(res.zeros[n, g])), (n, k)
+    return skipped
+
+
+def test_q5_least_squares_continuation():
+    W, s, X = _data(66, 6, 384, 768, True)
+    assert _check_q5(W, s, X) <= 1
+
+
+def test_mutation_uncompensated_group_parameters_fails_q5(monkeypatch):
+    W, s, X = _data(66, 6, 384, 768, True)
+    orig = W.astype(np.float64) / s.astype(np.float64)[None, :]
+    real = gptq.group_params
+    calls = []
+
+    def planted(wg):                     # the g-th call sees the original W' of group g
+        g = len(calls)
+        calls.append(g)
+        return real(orig[:, 128 * g:128 * g + 128])
+    monkeypatch.setattr(gptq, "group_params", planted)
+    with pytest.raises(AssertionError):
+        _check_q5(W, s, X)

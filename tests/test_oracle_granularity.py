@@ -9,7 +9,8 @@ G2  every group of a row (channel) or of the tensor (tensor) carries the same sc
 G3  the round-trip bound |W' - (q - z) scale| <= scale / 2 holds at every granularity;
 G4  the page's ordering: coarser granularity never shrinks a group's scale, and on
     real-shaped weights the reconstruction error grows from group to channel to tensor;
-and a mutation that forgets to widen the range to the row fails G2.
+and a mutation that leaves the range at the group's (never widened to the row or the
+tensor) fails G2.
 """
 from fractions import Fraction
 
@@ -41,9 +42,8 @@ def test_g1_special_cases():
     assert _same(oracle.quantize(W, None, "tensor"), oracle.quantize(W, None, "channel"))
 
 
-@pytest.mark.parametrize("gran", ["channel", "tensor"])
-def test_g2_shared_metadata_and_exact_scale(gran):
-    rng = np.random.default_rng(51)
+def _check_g2(gran, seed=51):
+    rng = np.random.default_rng(seed)
     N, K = 16, 384
     W, s = _w(rng, N, K)
     r = oracle.quantize(W, s, gran)
@@ -58,6 +58,11 @@ def test_g2_shared_metadata_and_exact_scale(gran):
         assert len(set(r.zeros[n].tolist())) == 1
     if gran == "tensor":
         assert len(set(r.scales.ravel().tolist())) == 1
+
+
+@pytest.mark.parametrize("gran", ["channel", "tensor"])
+def test_g2_shared_metadata_and_exact_scale(gran):
+    _check_g2(gran)
 
 
 @pytest.mark.parametrize("gran", oracle.GRANULARITIES)
@@ -87,8 +92,12 @@ def test_g4_coarser_is_worse():
     assert err["group"] < err["channel"] < err["tensor"]
 
 
-def test_mutation_unwidened_row_range_fails_g2():
-    rng = np.random.default_rng(54)
-    W, s = _w(rng, 16, 512)
-    wrong = oracle.quantize(W, s, "group")   # as if the channel range were never formed
-    assert any(len(set(wrong.scales[n].tolist())) > 1 for n in range(16))
+@pytest.mark.parametrize("gran", ["channel", "tensor"])
+def test_mutation_unwidened_range_fails_g2(gran, monkeypatch):
+    """Planted: the range is left at each group's own extremes (never widened to the row
+    or the tensor); G2 must fail."""
+    from oracle import quantizer
+    real = quantizer._extremes
+    monkeypatch.setattr(quantizer, "_extremes", lambda Wp, g: real(Wp, "group"))
+    with pytest.raises(AssertionError):
+        _check_g2(gran)

@@ -7,8 +7,14 @@ V2  the page's losslessness statement: the first token emitted follows p_target
 V3  special cases: p_draft = p_target accepts every draft; p_draft(x) = 0 accepts;
     p_target(x) = 0 < p_draft(x) rejects for every u > 0;
 V4  the fixed-point draw against an exact rational inverse CDF where the fixed point
-    is exact (dyadic weights, u on the 2^-32 grid), and its end points.
-A mutation test swaps the acceptance ratio and checks V1 and V2 catch it.
+    is exact (dyadic weights, u on the 2^-32 grid), and its end points;
+V5  the corrected residual on non-dyadic fp32 rows: its weights are exactly
+    floor(2^40 * max(0, p_target - p_draft)) in rationals (the page's difference in
+    fixed point), and the token drawn after a rejection, over a grid of 2^16 uniforms,
+    follows normalize(max(0, p_target - p_draft)) within the grid's and the fixed
+    point's total-variation bound.
+Mutation tests swap the acceptance ratio (V1 and V2 catch it) and take the residual
+on the fixed-point values, max(0, fx(p_target) - fx(p_draft)) (V5 catches it).
 """
 from fractions import Fraction
 
@@ -168,3 +174,68 @@ def test_mutation_swapped_ratio_breaks_v1_and_v2():
     res = _run(p, q, 3, 20000, seed=2, verify=swapped)
     first = np.bincount([f for _, _, f, _ in res], minlength=6)
     assert _chi2(first, p.astype(np.float64)) > 25.7
+
+
+def _nondyadic_rows(rng, V):
+    """fp32 rows of tail probabilities, log-uniform in 2^-36 .. 2^-12 (the small entries
+    of a large vocabulary), where floor(p * 2^40) drops fractional bits.  Exponents are
+    at most 24 apart, so the fp64 difference of two entries is exact."""
+    pt = np.exp2(rng.uniform(-36, -12, V)).astype(np.float32)
+    pd = np.exp2(rng.uniform(-36, -12, V)).astype(np.float32)
+    return pt, pd
+
+
+def _check_v5_weights(seed=9, rows=400):
+    """V5, first half: the residual weights in exact rationals.  Returns how many entries
+    differ from the fixed-point difference max(0, fx(p_target) - fx(p_draft))."""
+    rng = np.random.default_rng(seed)
+    differ = 0
+    for _ in range(rows):
+        V = int(rng.integers(2, 9))
+        pt, pd = _nondyadic_rows(rng, V)
+        got = spec.residual_weights(pt.astype(np.float64), pd.astype(np.float64))
+        for x in range(V):
+            d = max(Fraction(float(pt[x])) - Fraction(float(pd[x])), Fraction(0))
+            want = (d * 2 ** 40).__floor__()
+            assert int(got[x]) == want, (pt[x], pd[x], int(got[x]), want)
+            fx_t = (Fraction(float(pt[x])) * 2 ** 40).__floor__()
+            fx_d = (Fraction(float(pd[x])) * 2 ** 40).__floor__()
+            differ += want != max(fx_t - fx_d, 0)
+    return differ
+
+
+def test_v5_residual_weights_exact():
+    # the pin tells the page's form apart from the fixed-point difference
+    assert _check_v5_weights() > 50
+
+
+def test_mutation_fixed_point_difference_fails_v5(monkeypatch):
+    monkeypatch.setattr(spec, "residual_weights", lambda a, b: np.maximum(
+        spec.fixed_weights(a) - spec.fixed_weights(b), 0))
+    with pytest.raises(AssertionError):
+        _check_v5_weights()
+
+
+def test_v5_residual_draw_follows_corrected_distribution():
+    """Token after a rejection at position 0, for u = j / 2^16 (j = 0 .. 2^16 - 1): its
+    histogram against the exact normalize(max(0, p_target - p_draft)).  Each grid point
+    stands for 2^16 points of the 2^-32 grid, so the histogram is within V * 2^-16 of the
+    draw's own distribution in total variation; the fixed point adds at most V * 2^-40
+    over the residual's mass."""
+    rng = np.random.default_rng(10)
+    for _ in range(3):
+        V = int(rng.integers(3, 8))
+        pt, pd = _nondyadic_rows(rng, V)
+        x = int(np.argmax(pd.astype(np.float64) - pt.astype(np.float64)))   # pt[x] < pd[x]
+        res = [max(Fraction(float(a)) - Fraction(float(b)), Fraction(0)) for a, b in zip(pt, pd)]
+        mass = sum(res)
+        exact = [float(r / mass) for r in res]
+        counts = np.zeros(V)
+        n_grid = 2 ** 16
+        for j in range(n_grid):
+            n, tok = spec.verify(np.stack([pt, pt]), pd[None], np.array([x]),
+                                 np.array([1 - 2 ** -24], np.float32), np.float32(j / n_grid))
+            assert n == 0
+            counts[tok] += 1
+        tv = 0.5 * np.abs(counts / n_grid - np.array(exact)).sum()
+        assert tv <= V * 2.0 ** -16 + V * 2.0 ** -40 / float(mass), tv
