@@ -55,9 +55,12 @@
  *
  * Ownership and streams: the caller allocates and owns every buffer (device
  * memory unless noted) and passes a hipStream_t as `stream` (NULL = the null
- * stream).  All pointers must be 16-byte aligned.  The library keeps a small
- * per-device status word (allocated on first use, never freed) for the
- * packer's error report; it allocates nothing else.
+ * stream).  All pointers must be 16-byte aligned.  The packers' status word
+ * and row-range scratch (about 512 KB) are a device array of the library's own
+ * code object, one copy per GPU, held until the process ends; the packers
+ * (w4a16_quantize_pack*) share it and run one at a time within a process
+ * (each call blocks anyway).  The library allocates nothing, except that the
+ * GPTQ packer's rocBLAS and rocSOLVER calls manage memory of their own.
  *
  * Errors: every argument is validated on the host before any HIP call, so an
  * invalid call returns its status without touching the GPU.  Status codes are
@@ -133,8 +136,6 @@ enum {
  * 2.1): the range [min(0, min W'), max(0, max W')] is taken over the row or
  * over the whole tensor instead of the group, and every group slot of the row
  * repeats the resulting scale and zero point (same layout, same kernels).
- * These two modes allocate 16 bytes per row of device memory for the
- * duration of the call.
  * W4A16_QUANT_ASYM8 is the INT8 (W8A16) variant ("Chapter 22", aiwing.uk,
  * section 22.3's table: INT8 at one byte per parameter): the same rules with
  * codes 0..255 (scale = range / 255 rounded up), one byte per weight in
@@ -300,8 +301,9 @@ int w4a16_gemm_grouped_ws(const w4a16_problem *problems, int count, void *worksp
  *   token, or -1 if the row it is drawn from has no mass).
  * Every decision is exact: the test is u * p_draft <= p_target in fp64; a draw
  * is an inverse-CDF draw in fixed point, with fx(p) = floor(p * 2^40), weights
- * fx(p_target) for the target row and max(0, fx(p_target) - fx(p_draft)) for
- * the corrected residual, exact integer sums, and threshold
+ * fx(p_target) for the target row and fx(max(0, p_target - p_draft)) for the
+ * corrected residual (the difference formed in fp64 from the two fp32 values),
+ * exact integer sums, and threshold
  * (floor(u' * 2^32) * S) >> 32 (u' clamped to [0, 1), NaN as 0), taking the
  * smallest id whose inclusive prefix sum exceeds it; with no mass in the
  * residual the target row of that position is used.

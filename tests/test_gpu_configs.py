@@ -1,6 +1,9 @@
 """Full-size workloads: every matrix of the five problem configurations, packed on the
-GPU and multiplied at each configuration's batch sizes with the kernel the library's
-dispatch picks (the launch configuration the benchmark times).
+GPU and multiplied at each configuration's batch sizes, one matrix per call, with the
+kernel the library's dispatch picks.  (The benchmark runs each decode, verify and
+batched layer as one grouped call of all seven matrices; those exact calls are checked
+in test_gpu_grouped_layers.py.  The 70B prefill matrices are timed one call each, as
+here.)
 
 The oracle cannot run a whole 70B-shaped layer in seconds, so it checks samples
 it computes on its own: whole 16-row blocks of the packed buffers (first, last

@@ -60,7 +60,9 @@ def test_matches_oracle_objective(N, K, n, awq):
     note(f"loss gpu {lg:.6e} oracle {lo:.6e} rtn {lr:.6e}; identical codes {same:.5f}")
     assert abs(lg - lo) <= 1e-3 * lo
     assert lg < 0.9 * lr
-    assert same >= 0.99
+    # observed: every code identical at these sizes; a row may still diverge after a
+    # code lands on the other side of a rounding boundary (see the module docstring)
+    assert same >= 0.999
     # every code valid, and the metadata follows the packer's rules for its own range
     assert q.max() <= 15 and np.all(z.astype(np.float64) == np.rint(z.astype(np.float64)))
 
@@ -85,6 +87,29 @@ def test_full_size_q_proj_objective():
     lg, lr = loss(g), loss(r)
     note(f"full-size loss gptq {lg:.5e} rtn {lr:.5e} ratio {lg / lr:.3f}")
     assert lg < 0.5 * lr
+
+
+def test_full_size_sampled_rows_match_oracle():
+    """The same 4096 x 4096 GPTQ pack against oracle.gptq on sampled rows: rows are
+    independent given H, so the oracle quantizes just the first, the last and a random
+    16-row block with the same calibration rows and s."""
+    torch_cuda()
+    W, s, X = _data(75, 4096, 4096, 4096, True)
+    note("gptq full size 4096x4096 vs oracle on sampled rows")
+    pw = gpu_gptq(W, s, X)
+    q, sc, z = unpack(pw, 4096, 4096)
+    rows = np.concatenate([np.arange(0, 16), np.arange(2048, 2064), np.arange(4080, 4096)])
+    ref = gptq.quantize_gptq(W[rows], s, X)
+    got = oracle.QuantResult(q=q[rows], scales=sc[rows], zeros=z[rows])
+    same = float((got.q == ref.q).mean())
+    same_meta = float(np.mean((h16_bits(got.scales) == h16_bits(ref.scales))
+                              & (h16_bits(got.zeros) == h16_bits(ref.zeros))))
+    lg = gptq.layer_loss(W[rows], s, got, X)
+    lo = gptq.layer_loss(W[rows], s, ref, X)
+    note(f"sampled rows: identical codes {same:.6f}, identical scale/zero {same_meta:.6f}, "
+         f"loss gpu {lg:.6e} oracle {lo:.6e}")
+    assert same >= 0.999 and same_meta >= 0.999
+    assert abs(lg - lo) <= 1e-3 * lo
 
 
 def test_validation():

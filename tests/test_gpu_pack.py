@@ -49,6 +49,22 @@ def test_pack_awq_shapes(N, K, mode):
     check_exact(weights(1, 9, N, K), awq_scales(1, 9, K), f"awq {N}x{K}", mode)
 
 
+@pytest.mark.parametrize("mode", [w4.QUANT_ASYM_CHANNEL, w4.QUANT_ASYM_TENSOR])
+def test_pack_coarse_granularity_across_range_passes(mode):
+    """More rows than one pass of the packer's row-range scratch (32768 rows): the
+    channel and tensor ranges are formed pass by pass, and the row holding the tensor's
+    extreme value sits in the second pass."""
+    rng = np.random.default_rng(12)
+    N, K = 32768 + 4096 + 48, 256
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
+    W[N - 5, 200] = np.float16(0.75)                    # the tensor's largest weight
+    W[33000, 17] = np.float16(-0.5)                     # and its least
+    s = awq_scales(1, 9, K)
+    check_exact(W, s, "two range passes", mode)
+    # the same packer call again on a different (smaller) matrix: nothing carries over
+    check_exact(W[:4096 + 32], s, "after two range passes", mode)
+
+
 @pytest.mark.parametrize("mode", MODES)
 def test_pack_edge_groups(mode):
     rng = np.random.default_rng(11)

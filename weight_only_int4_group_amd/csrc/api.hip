@@ -26,21 +26,32 @@ int check_shape(int64_t N, int64_t K) {
   return W4A16_OK;
 }
 
-// Per-device status word of the packer, allocated on first use.
-std::mutex g_status_mu;
-std::vector<unsigned *> g_status;
+// The packers' scratch: a status word (offset 0), the running tensor range
+// (two doubles at 256) and the ranges of one chunk of kRangeRows rows (rmin
+// then rmax from 512).  It is device memory of this library's own code object,
+// one copy per GPU, held until the process ends: the packers allocate nothing.
+// Host code never passes the array's name (a host-side stand-in) to the GPU,
+// only the address hipGetSymbolAddress gives on each device.  Pack calls hold
+// g_pack_mu from start to end (they block on their stream anyway), so calls
+// from several host threads take turns instead of sharing the scratch.
+constexpr int kRangeRows = 32768;  // rows per range pass of the coarser granularities
+constexpr size_t kPackScratchBytes = 512 + (size_t)kRangeRows * 2 * sizeof(double);
+static __device__ __align__(256) unsigned char pack_scratch[kPackScratchBytes];
 
-int status_word(unsigned **out) {
+std::mutex g_pack_mu;
+std::vector<unsigned char *> g_pack_ptr;  // per device, set on the first pack call there
+
+// The scratch address on the current device (g_pack_mu held).
+int pack_scratch_ptr(unsigned char **out) {
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return W4A16_EHIP;
-  std::lock_guard<std::mutex> lock(g_status_mu);
-  if ((int)g_status.size() <= dev) g_status.resize(dev + 1, nullptr);
-  if (!g_status[dev]) {
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return W4A16_EHIP;
+  if ((int)g_pack_ptr.size() <= dev) g_pack_ptr.resize(dev + 1, nullptr);
+  if (!g_pack_ptr[dev]) {
     void *p = nullptr;
-    if (hipMalloc(&p, 256) != hipSuccess) return W4A16_EHIP;
-    g_status[dev] = static_cast<unsigned *>(p);
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(pack_scratch)) != hipSuccess || !p) return W4A16_EHIP;
+    g_pack_ptr[dev] = static_cast<unsigned char *>(p);
   }
-  *out = g_status[dev];
+  *out = g_pack_ptr[dev];
   return W4A16_OK;
 }
 
@@ -99,32 +110,45 @@ int w4a16_packed_sizes_mode(int64_t N, int64_t K, int mode, size_t *wq_bytes, si
   return W4A16_OK;
 }
 
+// Quantize and pack with the scratch `scr` (g_pack_mu held); blocks.  The
+// coarser granularities take the row (or tensor) ranges first, kRangeRows rows
+// per pass: per channel, each pass's rows are packed right after their ranges;
+// per tensor, every pass folds its rows into one running range, then one pack
+// launch reads it for every row.
 static int pack_and_check(const void *W, const void *s, int64_t N, int64_t K,
                           const uint8_t *keep, int mode, void *Wq, void *scales, void *zeros,
-                          unsigned *status, hipStream_t st) {
-  // the coarser granularities need each row's range first: 16 bytes per row
-  // of device memory for the duration of the call
-  double *range = nullptr;
-  const bool coarse = mode == W4A16_QUANT_ASYM_CHANNEL || mode == W4A16_QUANT_ASYM_TENSOR;
-  if (coarse && hipMalloc(&range, (size_t)N * 2 * sizeof(double)) != hipSuccess)
-    return W4A16_EHIP;
-  int rc = W4A16_OK;
-  if (hipMemsetAsync(status, 0, sizeof(unsigned), st) != hipSuccess) rc = W4A16_EHIP;
-  if (!rc && coarse &&
-      w4a16::launch_row_range(W, s, (int)N, (int)K, keep, mode == W4A16_QUANT_ASYM_TENSOR, range,
-                              range + N, st) != hipSuccess)
-    rc = W4A16_EHIP;
-  if (!rc && w4a16::launch_pack(W, s, (int)N, (int)K, keep, range, range ? range + N : nullptr,
-                                Wq, scales, zeros, status, mode == W4A16_QUANT_SYM, st,
-                                mode == W4A16_QUANT_ASYM8) != hipSuccess)
-    rc = W4A16_EHIP;
+                          unsigned char *scr, hipStream_t st) {
+  unsigned *status = reinterpret_cast<unsigned *>(scr);
+  double *acc = reinterpret_cast<double *>(scr + 256);
+  double *rmin = reinterpret_cast<double *>(scr + 512), *rmax = rmin + kRangeRows;
+  const bool sym = mode == W4A16_QUANT_SYM, w8 = mode == W4A16_QUANT_ASYM8;
+  const int n = (int)N, k = (int)K, NB = n / W4A16_TILE_ROWS;
+  hipError_t e = hipMemsetAsync(status, 0, sizeof(unsigned), st);
+  if (e == hipSuccess && mode == W4A16_QUANT_ASYM_TENSOR) {
+    for (int n0 = 0; e == hipSuccess && n0 < n; n0 += kRangeRows) {
+      const int rows = n - n0 < kRangeRows ? n - n0 : kRangeRows;
+      e = w4a16::launch_row_range(W, s, n0, rows, k, keep, rmin, rmax, st);
+      if (e == hipSuccess) e = w4a16::launch_tensor_range(rows, rmin, rmax, acc, n0 == 0, st);
+    }
+    if (e == hipSuccess)
+      e = w4a16::launch_pack(W, s, n, k, 0, NB, keep, acc, acc + 1, 0, Wq, scales, zeros, status,
+                             sym, st, w8);
+  } else if (e == hipSuccess && mode == W4A16_QUANT_ASYM_CHANNEL) {
+    for (int n0 = 0; e == hipSuccess && n0 < n; n0 += kRangeRows) {
+      const int rows = n - n0 < kRangeRows ? n - n0 : kRangeRows;  // a multiple of 16
+      e = w4a16::launch_row_range(W, s, n0, rows, k, keep, rmin, rmax, st);
+      if (e == hipSuccess)
+        e = w4a16::launch_pack(W, s, n, k, n0 / W4A16_TILE_ROWS, rows / W4A16_TILE_ROWS, keep,
+                               rmin, rmax, 1, Wq, scales, zeros, status, sym, st, w8);
+    }
+  } else if (e == hipSuccess) {
+    e = w4a16::launch_pack(W, s, n, k, 0, NB, keep, nullptr, nullptr, 0, Wq, scales, zeros,
+                           status, sym, st, w8);
+  }
   unsigned host = 0;
-  if (!rc && hipMemcpyAsync(&host, status, sizeof(unsigned), hipMemcpyDeviceToHost, st) !=
-                 hipSuccess)
-    rc = W4A16_EHIP;
-  if (hipStreamSynchronize(st) != hipSuccess) rc = W4A16_EHIP;  // also before freeing `range`
-  if (range && hipFree(range) != hipSuccess && !rc) rc = W4A16_EHIP;
-  if (rc) return rc;
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(&host, status, sizeof(unsigned), hipMemcpyDeviceToHost, st);
+  if (hipStreamSynchronize(st) != hipSuccess || e != hipSuccess) return W4A16_EHIP;
   if (host & w4a16::kPackNonFinite) return W4A16_ENONFINITE;
   if (host & w4a16::kPackRange) return W4A16_ERANGE;
   return W4A16_OK;
@@ -139,10 +163,11 @@ int w4a16_quantize_pack_mode(const void *W, const void *s, int64_t N, int64_t K,
   if (!aligned16(W) || !aligned16(Wq) || !aligned16(scales) || !aligned16(zeros) ||
       (s && !aligned16(s)))
     return W4A16_EALIGN;
-  unsigned *status = nullptr;
-  if ((rc = status_word(&status))) return rc;
+  std::lock_guard<std::mutex> lock(g_pack_mu);
+  unsigned char *scr = nullptr;
+  if ((rc = pack_scratch_ptr(&scr))) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  return pack_and_check(W, s, N, K, nullptr, mode, Wq, scales, zeros, status, st);
+  return pack_and_check(W, s, N, K, nullptr, mode, Wq, scales, zeros, scr, st);
 }
 
 static bool gptq_shape_ok(int64_t N, int64_t K, int64_t n) {
@@ -165,9 +190,11 @@ int w4a16_quantize_pack_gptq(const void *W, const void *s, int64_t N, int64_t K,
   if (!aligned16(W) || !aligned16(Wq) || !aligned16(scales) || !aligned16(zeros) ||
       (s && !aligned16(s)) || !aligned16(X) || (reinterpret_cast<uintptr_t>(workspace) & 255u))
     return W4A16_EALIGN;
-  unsigned *status = nullptr;
-  int rc = status_word(&status);
+  std::lock_guard<std::mutex> lock(g_pack_mu);
+  unsigned char *scr = nullptr;
+  int rc = pack_scratch_ptr(&scr);
   if (rc) return rc;
+  unsigned *status = reinterpret_cast<unsigned *>(scr);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (hipMemsetAsync(status, 0, sizeof(unsigned), st) != hipSuccess) return W4A16_EHIP;
   const int g = w4a16::gptq_pack(W, s, (int)N, (int)K, X, n_samples, damp, Wq, scales, zeros,
@@ -207,15 +234,16 @@ int w4a16_quantize_pack_outliers(const void *W, const void *s, int64_t N, int64_
       (s && !aligned16(s)) || !aligned(o_row_ptr, 4) || !aligned(o_col, 4) || !aligned(o_val, 2) ||
       !aligned(workspace, 256))
     return W4A16_EALIGN;
-  unsigned *status = nullptr;
-  if ((rc = status_word(&status))) return rc;
+  std::lock_guard<std::mutex> lock(g_pack_mu);
+  unsigned char *scr = nullptr;
+  if ((rc = pack_scratch_ptr(&scr))) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const uint8_t *keep = nullptr;
   if (w4a16::select_outliers(W, s, (int)N, (int)K, count, static_cast<int32_t *>(o_row_ptr),
                              static_cast<int32_t *>(o_col), static_cast<_Float16 *>(o_val),
                              workspace, &keep, st) != 0)
     return W4A16_EHIP;
-  return pack_and_check(W, s, N, K, keep, mode, Wq, scales, zeros, status, st);
+  return pack_and_check(W, s, N, K, keep, mode, Wq, scales, zeros, scr, st);
 }
 
 int w4a16_quantize_pack(const void *W, const void *s, int64_t N, int64_t K, void *Wq,
@@ -399,6 +427,7 @@ int w4a16_gemm_grouped_ws(const w4a16_problem *problems, int count, void *worksp
 int w4a16_gemm_grouped(const w4a16_problem *problems, int count, void *stream) {
   return w4a16_gemm_grouped_ws(problems, count, nullptr, 0, stream);
 }
+
 
 static bool spec_shape_ok(int64_t B, int64_t K, int64_t V) {
   if (B < 0 || K < 0 || V < 1 || B > (int64_t(1) << 24) || K > 1024 || V > (int64_t(1) << 24))

@@ -48,25 +48,30 @@ __device__ __forceinline__ bool finite_h(_Float16 x) {
 // per-tensor granularity) in place of each group's own.
 // W8: INT8 codes (0..255, scale = range / 255), a 2048-byte tile per group of
 // a row block, 32 bytes per lane (byte 8 t + j holds column 32 t + 8 c + j).
+// Row blocks b0 .. b0 + nbw - 1 only (the whole matrix in one launch, or one
+// chunk of rows whose ranges rmin/rmax hold: row n reads entry (n - 16 b0) *
+// rstride, so rstride 0 gives every row the tensor's range).
 template <bool SYM, bool W8>
 __global__ __launch_bounds__(256) void pack_kernel(const _Float16 *__restrict__ W,
                                                    const _Float16 *__restrict__ s, int N, int K,
+                                                   int b0, int nbw,
                                                    const uint8_t *__restrict__ keep,
                                                    const double *__restrict__ rmin,
-                                                   const double *__restrict__ rmax,
+                                                   const double *__restrict__ rmax, int rstride,
                                                    u32x4 *__restrict__ Wq,
                                                    _Float16 *__restrict__ scales,
                                                    _Float16 *__restrict__ zeros,
                                                    unsigned *__restrict__ status) {
 #pragma clang fp contract(off)
   const int G = K / kGroup, NB = N / kTileRows;
-  const long long tiles = (long long)NB * G;
-  // the wave's tile, numbered as stored: group-major
-  const long long tile = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (tile >= tiles) return;  // uniform per wave
+  const long long tiles = (long long)nbw * G;
+  // the wave's tile among the window's: group-major like the stored order
+  const long long local = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (local >= tiles) return;  // uniform per wave
   const int lane = threadIdx.x & 63;
   const int c = lane >> 4, r = lane & 15;
-  const int g = (int)(tile / NB), b = (int)(tile % NB);
+  const int g = (int)(local / nbw), b = b0 + (int)(local % nbw);
+  const long long tile = (long long)g * NB + b;  // stored position
   const int n = b * kTileRows + r;
 
   double wp[32];
@@ -101,8 +106,9 @@ __global__ __launch_bounds__(256) void pack_kernel(const _Float16 *__restrict__ 
   mx = fmax(mx, __shfl_xor(mx, 16));
   mx = fmax(mx, __shfl_xor(mx, 32));
   if (rmin) {  // a coarser granularity: the row's (or tensor's) range, still containing 0
-    mn = fmin(rmin[n], 0.0);
-    mx = fmax(rmax[n], 0.0);
+    const int ri = (n - b0 * kTileRows) * rstride;
+    mn = fmin(rmin[ri], 0.0);
+    mx = fmax(rmax[ri], 0.0);
   }
 
   // asymmetric: the range [mn, mx]; symmetric: the largest magnitude
@@ -175,16 +181,17 @@ __global__ __launch_bounds__(256) void pack_kernel(const _Float16 *__restrict__ 
   if (bad) atomicOr(status, bad);
 }
 
-// Per row n: the least and largest W' = W / s over the row (kept weights
-// count as 0), one workgroup per row.  Exact: min and max round nothing.
+// Per row n = n0 + i: the least and largest W' = W / s over the row (kept
+// weights count as 0) into rmin[i], rmax[i], one workgroup per row.  Exact:
+// min and max round nothing.
 __global__ __launch_bounds__(256) void row_range_kernel(const _Float16 *__restrict__ W,
                                                         const _Float16 *__restrict__ s, int K,
-                                                        const uint8_t *__restrict__ keep,
+                                                        int n0, const uint8_t *__restrict__ keep,
                                                         double *__restrict__ rmin,
                                                         double *__restrict__ rmax) {
 #pragma clang fp contract(off)
   __shared__ double red[2][4];
-  const int n = blockIdx.x, tid = threadIdx.x;
+  const int i = blockIdx.x, n = n0 + i, tid = threadIdx.x;
   double lo = 0.0, hi = 0.0;  // 0 is in every range anyway
   for (int k0 = 8 * tid; k0 < K; k0 += 8 * 256) {
     const half8 wv = load_half8(W + (size_t)n * K + k0);
@@ -214,19 +221,21 @@ __global__ __launch_bounds__(256) void row_range_kernel(const _Float16 *__restri
   }
   __syncthreads();
   if (tid == 0) {
-    rmin[n] = fmin(fmin(red[0][0], red[0][1]), fmin(red[0][2], red[0][3]));
-    rmax[n] = fmax(fmax(red[1][0], red[1][1]), fmax(red[1][2], red[1][3]));
+    rmin[i] = fmin(fmin(red[0][0], red[0][1]), fmin(red[0][2], red[0][3]));
+    rmax[i] = fmax(fmax(red[1][0], red[1][1]), fmax(red[1][2], red[1][3]));
   }
 }
 
-// The tensor's range: every row gets the least of rmin and the largest of
-// rmax.  One workgroup.
-__global__ __launch_bounds__(256) void tensor_range_kernel(int N, double *__restrict__ rmin,
-                                                           double *__restrict__ rmax) {
+// The tensor's range, one chunk of rows at a time: acc[0] = the least of the
+// chunk's rmin[0 .. rows) and of acc[0] (of 0 for the first chunk), acc[1] the
+// largest of rmax and acc[1].  One workgroup.
+__global__ __launch_bounds__(256) void tensor_range_kernel(int rows, const double *__restrict__ rmin,
+                                                           const double *__restrict__ rmax,
+                                                           double *__restrict__ acc, int first) {
   __shared__ double red[2][4];
   const int tid = threadIdx.x;
-  double lo = 0.0, hi = 0.0;
-  for (int n = tid; n < N; n += 256) {
+  double lo = first ? 0.0 : acc[0], hi = first ? 0.0 : acc[1];
+  for (int n = tid; n < rows; n += 256) {
     lo = fmin(lo, rmin[n]);
     hi = fmax(hi, rmax[n]);
   }
@@ -240,45 +249,46 @@ __global__ __launch_bounds__(256) void tensor_range_kernel(int N, double *__rest
     red[1][tid >> 6] = hi;
   }
   __syncthreads();
-  lo = fmin(fmin(red[0][0], red[0][1]), fmin(red[0][2], red[0][3]));
-  hi = fmax(fmax(red[1][0], red[1][1]), fmax(red[1][2], red[1][3]));
-  for (int n = tid; n < N; n += 256) {
-    rmin[n] = lo;
-    rmax[n] = hi;
+  if (tid == 0) {
+    acc[0] = fmin(fmin(red[0][0], red[0][1]), fmin(red[0][2], red[0][3]));
+    acc[1] = fmax(fmax(red[1][0], red[1][1]), fmax(red[1][2], red[1][3]));
   }
 }
 
 }  // namespace
 
-hipError_t launch_row_range(const void *W, const void *s, int N, int K, const uint8_t *keep,
-                            bool tensor, double *rmin, double *rmax, hipStream_t stream) {
-  hipLaunchKernelGGL(row_range_kernel, dim3(N), dim3(256), 0, stream, (const _Float16 *)W,
-                     (const _Float16 *)s, K, keep, rmin, rmax);
-  hipError_t err = hipGetLastError();
-  if (err == hipSuccess && tensor) {
-    hipLaunchKernelGGL(tensor_range_kernel, dim3(1), dim3(256), 0, stream, N, rmin, rmax);
-    err = hipGetLastError();
-  }
-  return err;
+hipError_t launch_row_range(const void *W, const void *s, int n0, int rows, int K,
+                            const uint8_t *keep, double *rmin, double *rmax, hipStream_t stream) {
+  hipLaunchKernelGGL(row_range_kernel, dim3(rows), dim3(256), 0, stream, (const _Float16 *)W,
+                     (const _Float16 *)s, K, n0, keep, rmin, rmax);
+  return hipGetLastError();
 }
 
-hipError_t launch_pack(const void *W, const void *s, int N, int K, const uint8_t *keep,
-                       const double *rmin, const double *rmax, void *Wq, void *scales, void *zeros,
-                       unsigned *status, bool symmetric, hipStream_t stream, bool w8) {
-  const long long tiles = (long long)(N / kTileRows) * (K / kGroup);
+hipError_t launch_tensor_range(int rows, const double *rmin, const double *rmax, double *acc,
+                               bool first, hipStream_t stream) {
+  hipLaunchKernelGGL(tensor_range_kernel, dim3(1), dim3(256), 0, stream, rows, rmin, rmax, acc,
+                     first ? 1 : 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack(const void *W, const void *s, int N, int K, int b0, int nbw,
+                       const uint8_t *keep, const double *rmin, const double *rmax, int rstride,
+                       void *Wq, void *scales, void *zeros, unsigned *status, bool symmetric,
+                       hipStream_t stream, bool w8) {
+  const long long tiles = (long long)nbw * (K / kGroup);
   const long long blocks = (tiles + 3) / 4;
   if (w8)
     hipLaunchKernelGGL((pack_kernel<false, true>), dim3((unsigned)blocks), dim3(256), 0, stream,
-                       (const _Float16 *)W, (const _Float16 *)s, N, K, keep, rmin, rmax, (u32x4 *)Wq,
-                       (_Float16 *)scales, (_Float16 *)zeros, status);
+                       (const _Float16 *)W, (const _Float16 *)s, N, K, b0, nbw, keep, rmin, rmax,
+                       rstride, (u32x4 *)Wq, (_Float16 *)scales, (_Float16 *)zeros, status);
   else if (symmetric)
     hipLaunchKernelGGL((pack_kernel<true, false>), dim3((unsigned)blocks), dim3(256), 0, stream,
-                       (const _Float16 *)W, (const _Float16 *)s, N, K, keep, rmin, rmax, (u32x4 *)Wq,
-                       (_Float16 *)scales, (_Float16 *)zeros, status);
+                       (const _Float16 *)W, (const _Float16 *)s, N, K, b0, nbw, keep, rmin, rmax,
+                       rstride, (u32x4 *)Wq, (_Float16 *)scales, (_Float16 *)zeros, status);
   else
     hipLaunchKernelGGL((pack_kernel<false, false>), dim3((unsigned)blocks), dim3(256), 0, stream,
-                       (const _Float16 *)W, (const _Float16 *)s, N, K, keep, rmin, rmax, (u32x4 *)Wq,
-                       (_Float16 *)scales, (_Float16 *)zeros, status);
+                       (const _Float16 *)W, (const _Float16 *)s, N, K, b0, nbw, keep, rmin, rmax,
+                       rstride, (u32x4 *)Wq, (_Float16 *)scales, (_Float16 *)zeros, status);
   return hipGetLastError();
 }
 

@@ -14,7 +14,8 @@
 //     rejects; NaN and negative probabilities count as 0;
 //   * a draw is an inverse-CDF draw in fixed point: with fx(p) = floor(p *
 //     2^40), the target row's weights are fx(p_target) and the corrected
-//     residual's max(0, fx(p_target) - fx(p_draft)); sums are exact (order-
+//     residual's fx(max(0, p_target - p_draft)), the difference formed in fp64
+//     from the two fp32 values; sums are exact (order-
 //     free), T = (floor(u' * 2^32) * S) >> 32, and the token is the smallest x
 //     whose inclusive prefix sum exceeds T; with no mass in the residual the
 //     target row is used, and with none there either the token is -1.
@@ -51,8 +52,12 @@ __device__ __forceinline__ double clean(float p) { return p > 0.f ? (double)p : 
 // fp64 adds of them are exact.
 __device__ __forceinline__ double fx(float p) { return floor(fmax((double)p, 0.0) * kFix); }
 
-// the corrected residual weight max(0, fx(p_target) - fx(p_draft)) (exact)
-__device__ __forceinline__ double residual(double ft, float pd) { return fmax(ft - fx(pd), 0.0); }
+// the corrected residual weight fx(max(0, p_target - p_draft)): the difference
+// of the two cleaned values in fp64 (exact unless their exponents are more
+// than 29 apart, then rounded once to nearest), in fixed point
+__device__ __forceinline__ double residual(float pt, float pd) {
+  return floor(fmax(fmax((double)pt, 0.0) - fmax((double)pd, 0.0), 0.0) * kFix);
+}
 
 // an exact integer-valued double below 2^52 to an integer (clamped far above
 // anything inside the contract)
@@ -152,7 +157,7 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
           const float4 d = *reinterpret_cast<const float4 *>(rd + x);
           const double f0 = fx(t.x), f1 = fx(t.y), f2 = fx(t.z), f3 = fx(t.w);
           st += (f0 + f1) + (f2 + f3);
-          sr += (residual(f0, d.x) + residual(f1, d.y)) + (residual(f2, d.z) + residual(f3, d.w));
+          sr += (residual(t.x, d.x) + residual(t.y, d.y)) + (residual(t.z, d.z) + residual(t.w, d.w));
         }
       }
     } else {
@@ -168,9 +173,9 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
   } else if (rd) {
 #pragma unroll 8
     for (int x = x0 + tid; x < x1; x += kThreads) {
-      const double f = fx(rt[x]);
-      st += f;
-      sr += residual(f, rd[x]);
+      const float t = rt[x];
+      st += fx(t);
+      sr += residual(t, rd[x]);
     }
   } else {
 #pragma unroll 8
@@ -278,7 +283,7 @@ __global__ __launch_bounds__(kThreads) void draw_kernel(
   double w[kPerThread], wsum = 0;
 #pragma unroll
   for (int j = 0; j < kPerThread; ++j) {
-    w[j] = use_residual ? residual(fx(pt[j]), pd[j]) : fx(pt[j]);
+    w[j] = use_residual ? residual(pt[j], pd[j]) : fx(pt[j]);
     wsum += w[j];
   }
   const uint64_t sum = to_int(wsum);

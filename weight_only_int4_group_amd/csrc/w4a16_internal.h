@@ -10,13 +10,20 @@ namespace w4a16 {
 constexpr unsigned kPackNonFinite = 1u;
 constexpr unsigned kPackRange = 2u;
 
-hipError_t launch_pack(const void *W, const void *s, int N, int K, const uint8_t *keep,
-                       const double *rmin, const double *rmax, void *Wq, void *scales, void *zeros,
-                       unsigned *status, bool symmetric, hipStream_t stream, bool w8 = false);
-// Per-row range of W / s (kept weights as 0) into rmin/rmax [N]; with `tensor`
-// every row then holds the whole tensor's range.
-hipError_t launch_row_range(const void *W, const void *s, int N, int K, const uint8_t *keep,
-                            bool tensor, double *rmin, double *rmax, hipStream_t stream);
+// Packs row blocks b0 .. b0 + nbw - 1 of the N x K matrix.  rmin/rmax (or
+// null for per-group ranges): row n takes entry (n - 16 b0) * rstride.
+hipError_t launch_pack(const void *W, const void *s, int N, int K, int b0, int nbw,
+                       const uint8_t *keep, const double *rmin, const double *rmax, int rstride,
+                       void *Wq, void *scales, void *zeros, unsigned *status, bool symmetric,
+                       hipStream_t stream, bool w8 = false);
+// Range of W / s (kept weights as 0) of rows n0 .. n0 + rows - 1 into
+// rmin/rmax [rows].
+hipError_t launch_row_range(const void *W, const void *s, int n0, int rows, int K,
+                            const uint8_t *keep, double *rmin, double *rmax, hipStream_t stream);
+// acc[0..1] = the least of rmin[0 .. rows) and the largest of rmax, combined
+// with acc's earlier value unless `first` (and with 0 always).
+hipError_t launch_tensor_range(int rows, const double *rmin, const double *rmax, double *acc,
+                               bool first, hipStream_t stream);
 
 // The weights kept in fp16 (validated by the caller): writes row_ptr [N + 1],
 // col and val [count], and a keep bit mask in the workspace (returned in
