@@ -86,7 +86,9 @@ enum {
   W4A16_EUNSUPPORTED = -3, /* unknown kernel path or quantization mode requested */
   W4A16_ENONFINITE = -4,   /* NaN/Inf in W or s, or some s <= 0 (packer)        */
   W4A16_ERANGE = -5,       /* a group scale rounds up past the fp16 range       */
-  W4A16_EHIP = -6          /* a HIP runtime call or kernel launch failed        */
+  W4A16_EHIP = -6,         /* a HIP runtime call or kernel launch failed        */
+  W4A16_ESCRATCH = -7      /* w4a16_gemm_grouped_static: the call needs more
+                              workspace than W4A16_STATIC_SCRATCH_BYTES         */
 };
 
 /* Kernel choice for w4a16_gemm_path(); w4a16_gemm() always uses AUTO. */
@@ -284,6 +286,24 @@ int w4a16_gemm_workspace_size(const w4a16_problem *problems, int count, size_t *
  * as the call's work on `stream` has completed.  Asynchronous on `stream`. */
 int w4a16_gemm_grouped_ws(const w4a16_problem *problems, int count, void *workspace,
                           size_t workspace_bytes, void *stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * w4a16_gemm_grouped_ws with its workspace taken from a device array inside
+ * the library instead of a caller argument.  The array holds
+ * W4A16_STATIC_SCRATCH_BYTES (64 MiB) on each GPU the library runs on, from
+ * the first call there until the process ends; a call calls no hipMalloc,
+ * hipFree or allocating library routine.  A call whose
+ * w4a16_gemm_workspace_size() exceeds the array returns W4A16_ESCRATCH
+ * without launching anything (checked on the host); other arguments and
+ * errors as w4a16_gemm_grouped_ws, and the results are the bits that call
+ * gives with a workspace of the queried size.  Every call on a GPU shares
+ * that GPU's array (nothing in it needs to start at zero): calls on one GPU
+ * whose work overlaps in time -- on different streams, or from different host
+ * threads without ordering -- race, and their results are undefined.
+ * Asynchronous on `stream`. */
+#define W4A16_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+int w4a16_gemm_grouped_static(const w4a16_problem *problems, int count, void *stream);
 
 /* Speculative-sampling verification: the accept / reject step that consumes a
  * verify pass ("Chapter 22: Advanced inference optimisation", aiwing.uk,

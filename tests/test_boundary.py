@@ -217,6 +217,27 @@ def test_grouped_ws_validation():
     assert L.w4a16_gemm_grouped_ws(None, 1, None, 0, None) == -1
 
 
+def test_grouped_static_rejects_calls_beyond_its_scratch():
+    """w4a16_gemm_grouped_static checks the workspace a call needs against its static
+    scratch on the host, before any HIP call: the 70B prefill layer as one grouped call
+    needs far more than 64 MiB (k and v split, with fp32 partials of 4096 x 1024)."""
+    L = w4.lib()
+    P = w4.Problem
+    shapes = [(8192, 8192), (1024, 8192), (1024, 8192), (8192, 8192), (28672, 8192),
+              (28672, 8192), (8192, 28672)]
+    arr = (P * 7)(*[P(A16, A16, A16, A16, A16, A16, 4096, N, K) for N, K in shapes])
+    rc, need = ws_size(*arr)
+    assert rc == 0 and need > w4.STATIC_SCRATCH_BYTES
+    assert L.w4a16_gemm_grouped_static(arr, 7, None) == -7
+    assert w4.w4a16_strerror(-7) != "unknown status"
+    # validation comes first, as for the other grouped entry points
+    assert L.w4a16_gemm_grouped_static(None, 2, None) == -1
+    bad = (P * 1)(P(ODD, A16, A16, A16, None, A16, 1, 16, 128))
+    assert L.w4a16_gemm_grouped_static(bad, 1, None) == -2
+    empty = (P * 1)(P(A16, A16, A16, A16, None, A16, 0, 16, 128))
+    assert L.w4a16_gemm_grouped_static(empty, 1, None) == 0   # M = 0: nothing to do
+
+
 def test_quantize_mode_validation():
     L = w4.lib()
     # unknown mode: rejected before anything else, without a GPU call

@@ -28,7 +28,7 @@ __all__ = [
     "w4a16_gemm_grouped", "GroupedCall", "w4a16_spec_verify",
     "w4a16_spec_verify_workspace_size", "SpecVerifyCall", "w4a16_quantize_pack_outliers",
     "w4a16_outlier_workspace_size", "page_outlier_count", "DTYPE_F16", "DTYPE_BF16",
-    "w4a16_quantize_pack_gptq",
+    "w4a16_quantize_pack_gptq", "w4a16_gemm_grouped_static", "STATIC_SCRATCH_BYTES",
 ]
 
 GROUP = 128
@@ -36,11 +36,13 @@ PATH_AUTO, PATH_SKINNY, PATH_TILED, PATH_SKINNY_WINDOW = 0, 1, 2, 3
 QUANT_ASYM, QUANT_SYM, QUANT_ASYM_CHANNEL, QUANT_ASYM_TENSOR, QUANT_ASYM8 = 0, 1, 2, 3, 4
 DTYPE_F16, DTYPE_BF16 = 0, 1
 STATUS = {0: "W4A16_OK", -1: "W4A16_EINVAL", -2: "W4A16_EALIGN", -3: "W4A16_EUNSUPPORTED",
-          -4: "W4A16_ENONFINITE", -5: "W4A16_ERANGE", -6: "W4A16_EHIP"}
+          -4: "W4A16_ENONFINITE", -5: "W4A16_ERANGE", -6: "W4A16_EHIP", -7: "W4A16_ESCRATCH"}
+STATIC_SCRATCH_BYTES = 64 << 20   # W4A16_STATIC_SCRATCH_BYTES
 EXPORTED_SYMBOLS = ("w4a16_packed_sizes", "w4a16_packed_sizes_mode", "w4a16_quantize_pack",
                     "w4a16_quantize_pack_mode",
                     "w4a16_gemm",
                     "w4a16_gemm_path", "w4a16_gemm_grouped", "w4a16_gemm_grouped_ws",
+                    "w4a16_gemm_grouped_static",
                     "w4a16_gemm_workspace_size", "w4a16_outlier_workspace_size",
                     "w4a16_gptq_workspace_size", "w4a16_quantize_pack_gptq",
                     "w4a16_quantize_pack_outliers", "w4a16_spec_verify",
@@ -86,6 +88,7 @@ def lib() -> ctypes.CDLL:
     L.w4a16_gemm_grouped_ws.argtypes = [ctypes.POINTER(Problem), ctypes.c_int, vp,
                                         ctypes.c_size_t, vp]
     L.w4a16_gemm_workspace_size.argtypes = [ctypes.POINTER(Problem), ctypes.c_int, sz]
+    L.w4a16_gemm_grouped_static.argtypes = [ctypes.POINTER(Problem), ctypes.c_int, vp]
     L.w4a16_spec_verify.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp, ctypes.c_size_t, vp,
                                     vp, vp]
     L.w4a16_spec_verify_workspace_size.argtypes = [i64, i64, i64, ctypes.POINTER(ctypes.c_size_t)]
@@ -103,6 +106,7 @@ def lib() -> ctypes.CDLL:
                  "w4a16_quantize_pack_mode",
                  "w4a16_gemm", "w4a16_gemm_path",
                  "w4a16_gemm_grouped", "w4a16_gemm_grouped_ws", "w4a16_gemm_workspace_size",
+                 "w4a16_gemm_grouped_static",
                  "w4a16_spec_verify", "w4a16_spec_verify_workspace_size", "w4a16_select_path",
                  "w4a16_outlier_workspace_size", "w4a16_quantize_pack_outliers",
                  "w4a16_gptq_workspace_size", "w4a16_quantize_pack_gptq",
@@ -331,9 +335,11 @@ class GroupedCall:
     allocated once, so each call is a single C call on the current stream (for
     captured or repeated launches over the same buffers).  Items are (X,
     PackedWeight, s or None, Y).  Calls of one object must not overlap in time on
-    different streams, since they share the workspace."""
+    different streams, since they share the workspace.  With ``static=True`` the call
+    goes to w4a16_gemm_grouped_static instead: no workspace is allocated here, the
+    library's own static scratch serves (all such calls on a GPU share it)."""
 
-    def __init__(self, items, stream=None, workspace=True):
+    def __init__(self, items, stream=None, workspace=True, static=False):
         torch = _torch()
         self.items = list(items)  # keep the tensors alive
         # a fixed HIP stream (e.g. torch.cuda.current_stream().cuda_stream) saves
@@ -354,7 +360,8 @@ class GroupedCall:
                 DTYPE_BF16 if X.dtype == torch.bfloat16 else DTYPE_F16, pw.wbits)
         self.device = self.items[0][0].device if self.items else None
         self.ws, self.ws_ptr, self.ws_bytes = None, None, 0
-        if workspace and self.items:
+        self.static = static
+        if workspace and self.items and not static:
             nb = ctypes.c_size_t()
             rc = lib().w4a16_gemm_workspace_size(self.array, len(self.items), ctypes.byref(nb))
             if rc:
@@ -367,6 +374,11 @@ class GroupedCall:
         if not self.items:
             return
         st = self.stream if self.stream is not None else _stream_handle(self.device)
+        if self.static:
+            rc = lib().w4a16_gemm_grouped_static(self.array, len(self.items), st)
+            if rc:
+                raise W4A16Error(rc, "w4a16_gemm_grouped_static")
+            return
         rc = lib().w4a16_gemm_grouped_ws(self.array, len(self.items), self.ws_ptr,
                                          self.ws_bytes, st)
         if rc:
@@ -380,6 +392,17 @@ def w4a16_gemm_grouped(items):
     full = [(X, pw, s, torch.empty((X.shape[0], pw.N), dtype=X.dtype, device=X.device))
             for (X, pw, s) in items]
     GroupedCall(full)()
+    return [it[3] for it in full]
+
+
+def w4a16_gemm_grouped_static(items):
+    """w4a16_gemm_grouped with the library's static scratch as the workspace (no device
+    allocation by the library; outputs are allocated here).  items: list of (X,
+    PackedWeight, s or None); returns the list of Y tensors."""
+    torch = _torch()
+    full = [(X, pw, s, torch.empty((X.shape[0], pw.N), dtype=X.dtype, device=X.device))
+            for (X, pw, s) in items]
+    GroupedCall(full, static=True)()
     return [it[3] for it in full]
 
 

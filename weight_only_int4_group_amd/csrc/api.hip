@@ -70,6 +70,7 @@ const char *w4a16_strerror(int status) {
     case W4A16_ENONFINITE: return "non-finite W or s, or s <= 0";
     case W4A16_ERANGE: return "group scale exceeds the fp16 range";
     case W4A16_EHIP: return "HIP runtime error";
+    case W4A16_ESCRATCH: return "the call needs more workspace than the library's static scratch holds";
     default: return "unknown status";
   }
 }
@@ -428,6 +429,52 @@ int w4a16_gemm_grouped(const w4a16_problem *problems, int count, void *stream) {
   return w4a16_gemm_grouped_ws(problems, count, nullptr, 0, stream);
 }
 
+}  // extern "C"
+
+namespace {
+
+// The workspace of w4a16_gemm_grouped_static: W4A16_STATIC_SCRATCH_BYTES of
+// device memory in this library's code object, one copy per GPU, held until
+// the process ends.  Its name is a host-side stand-in in host code: kernels
+// get the address hipGetSymbolAddress returns on each device (taken once per
+// device, with that device current, on the entry point's first call there).
+static __device__ __align__(256) unsigned char scratch[W4A16_STATIC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+std::vector<void *> g_scratch_ptr;  // per device
+
+int scratch_ptr(void **out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return W4A16_EHIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if ((int)g_scratch_ptr.size() <= dev) g_scratch_ptr.resize(dev + 1, nullptr);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return W4A16_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return W4A16_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int w4a16_gemm_grouped_static(const w4a16_problem *problems, int count, void *stream) {
+  size_t need = 0;
+  const int rc = w4a16_gemm_workspace_size(problems, count, &need);  // validates too
+  if (rc) return rc;
+  if (need > W4A16_STATIC_SCRATCH_BYTES) return W4A16_ESCRATCH;
+  void *ws = nullptr;
+  if (need > 0) {
+    const int r = scratch_ptr(&ws);
+    if (r) return r;
+  }
+  // the partial sums and prescaled activations are written before they are
+  // read within the call, so nothing in the scratch needs clearing
+  return w4a16_gemm_grouped_ws(problems, count, ws, need, stream);
+}
 
 static bool spec_shape_ok(int64_t B, int64_t K, int64_t V) {
   if (B < 0 || K < 0 || V < 1 || B > (int64_t(1) << 24) || K > 1024 || V > (int64_t(1) << 24))
