@@ -351,6 +351,70 @@ def gptq_line(torch, w4, N=4096, K=4096, n=4096, reps=3):
             "frac_of_fp64_peak": round(flops / sec / 1e12 / 78.6, 4)}
 
 
+def read_ceiling(torch, nbytes, launches=100, per=10):
+    """The measured read-bandwidth ceiling for `nbytes` per launch: a plain HIP
+    streaming-read kernel (libw4a16_ceiling.so, built with the library) reading one
+    buffer of nbytes per launch, rotating over enough copies (>= 1 GiB) that every
+    launch reads HBM, timed like the decode kernel (HIP events around blocks of `per`
+    back-to-back launches on the launch stream).  Its variants (16-byte loads, 4, 8 or
+    16 in flight per thread, 256 or 512 threads, with or without the non-temporal bit)
+    and grid sizes are swept and the fastest is the ceiling.  Also the same kernel over
+    one buffer (which then largely stays in the 256 MB last-level cache), for context."""
+    import ctypes
+    from weight_only_int4_group_amd.build import CEILING_LIB_PATH
+    if not os.path.exists(CEILING_LIB_PATH):
+        raise RuntimeError(f"{CEILING_LIB_PATH} is missing: build the library first")
+    L = ctypes.CDLL(CEILING_LIB_PATH)
+    L.stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
+                              ctypes.c_void_p, ctypes.c_void_p]
+    L.stream_read.restype = ctypes.c_int
+    nbytes = -(-nbytes // 16) * 16
+    copies = max(1, -(-POOL_BYTES // nbytes))
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda").random_(0, 256)
+            for _ in range(copies)]
+    grids = (512, 1024, 2048, 4096)
+    sink = torch.empty(max(grids) * 512, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    st = stream.cuda_stream
+
+    def run(variant, blocks, pool):
+        def go(i):
+            rc = L.stream_read(pool[i % len(pool)].data_ptr(), nbytes, variant, blocks,
+                               sink.data_ptr(), st)
+            if rc:
+                raise RuntimeError(f"stream_read failed: {rc}")
+        for i in range(10):
+            go(i)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(0, launches, per)]
+        torch.cuda.synchronize()
+        for b, (e0, e1) in enumerate(evs):
+            e0.record(stream)
+            for i in range(per):
+                go(10 + b * per + i)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([e0.elapsed_time(e1) / per for e0, e1 in evs]))  # ms per launch
+
+    table = []
+    for variant in (0, 1, 2, 3, 4, 5, 8, 9, 10, 11, 12, 13):
+        for blocks in grids:
+            ms = run(variant, blocks, bufs)
+            table.append({"variant": variant, "nt": bool(variant & 1),
+                          "loads_in_flight": 4 << ((variant >> 1) & 3),
+                          "threads": 512 if variant & 8 else 256, "workgroups": blocks,
+                          "us": round(ms * 1e3, 3), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1)})
+    best = min(table, key=lambda r: r["us"])
+    warm_ms = run(best["variant"], best["workgroups"], bufs[:1])
+    del bufs, sink
+    torch.cuda.empty_cache()
+    return {"kernel": "stream_read_kernel (plain 16-byte streaming reads, libw4a16_ceiling.so)",
+            "bytes_per_launch": nbytes, "copies": copies, "best": best,
+            "same_buffer_GB/s": round(nbytes / (warm_ms * 1e-3) / 1e9, 1),
+            "swept": len(table),
+            "top5": sorted(table, key=lambda r: r["us"])[:5]}
+
+
 def ceilings(torch, reps=10):
     """Measured ceilings on this GPU, for context: a plain device-to-device copy, and
     the vendor dense fp16 GEMM (torch.matmul on contiguous fp16 operands) at the 70B
@@ -533,6 +597,13 @@ def main():
                      "launch_us_p10_median_p90": [round(float(np.percentile(lms[0], q)) * 1e3, 3)
                                                   for q in (10, 50, 90)]},
     }
+    if not args.no_ceilings:
+        # the plain streaming-read ceiling on the same bytes, same rotation
+        log("measuring the streaming-read ceiling")
+        rc_ = read_ceiling(torch, step_bytes)
+        out["roofline"]["read_ceiling"] = rc_
+        out["roofline"]["frac_of_read_ceiling"] = round(
+            achieved / rc_["best"]["GB/s"], 4)
     if not args.no_variants:
         # the same launches over one buffer copy: the 116 MB layer then largely
         # stays in the 256 MB last-level cache, so this is not an HBM figure

@@ -131,6 +131,7 @@ struct TiledProblem {
   const int32_t *orp, *ocol;  // fp16 outliers, row-compressed (null: none)
   const _Float16 *oval;
   int bf16;                   // X and Y are bf16 (one value per launch)
+  const _Float16 *xs;         // tiled_dma_kernel: X * s (prescaled), or X when s is null
 };
 
 struct TiledSet {
@@ -175,6 +176,7 @@ __device__ __forceinline__ TiledProblem find_tiled(const TiledSet &ts, int block
   P.ocol = uniform_ptr(q.ocol);
   P.oval = uniform_ptr(q.oval);
   P.bf16 = uniform_int(q.bf16);
+  P.xs = uniform_ptr(q.xs);
   return P;
 }
 
@@ -602,6 +604,194 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
   }
 }
 
+// The tiled GEMM for fp16 activations and INT4 codes without outliers, with
+// TM = 8 (128 rows of X per wave) for large M.  The dequantization of a weight
+// costs the same VALU work whatever the rows it feeds, so a wave tile of 128
+// rows halves it per MFMA against 64 rows; the registers for that come from
+// moving X * s off the register path:
+//   * X * s (rounded to fp16 once: prescaled into the workspace by
+//     prescale_f16_kernel when s is given, else X itself) goes straight from
+//     memory into LDS with DMA loads (buffer_load ... lds), one group (128
+//     columns) per stage, double-buffered, one barrier per stage.  A row's 16
+//     chunks of 16 bytes are stored XOR-swizzled (chunk c of row m at c ^ (m %
+//     16)), so the MFMA A-operand reads of 16 rows hit distinct banks without
+//     padding; each DMA lane fetches the chunk that belongs in its slot;
+//   * the wave's code tiles (16 bytes per lane per tile, its MFMA B operands)
+//     and their scales and zero points are loaded into registers one group
+//     ahead, in two register sets that alternate.
+// Blocks are BM x 256 (BM = 16 TM), four waves of BM x 64; K is split across
+// workgroups the same way as in tiled_kernel.
+template <int TM>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void tiled_dma_kernel(
+    TiledSet ts) {
+  constexpr int TN = 4, WN = 4;
+  constexpr int BM = TM * 16, BN = WN * TN * 16;
+  constexpr int kRowChunks = kGroup / 8;            // 16-byte chunks per row per group
+  constexpr int kDma = BM * kRowChunks / (4 * 64);  // DMA loads per wave per group
+  static_assert(kDma * 4 * 64 == BM * kRowChunks, "a stage is whole DMA loads");
+  __shared__ __attribute__((aligned(16))) _Float16 As[2][BM * kGroup];
+
+  const int block = (int)blockIdx.x;
+  const TiledProblem P = find_tiled<false>(ts, block);
+  const int M = P.M, N = P.N, K = P.K;
+  const int tid = threadIdx.x, lane = tid & 63, wave = uniform_int(tid >> 6);
+  const int c = lane >> 4, r = lane & 15;
+  const int local = block - P.block0;
+  const int sp = local / P.tiles, t = local - sp * P.tiles;
+  const int mt = t / P.tiles_n;
+  const int n0 = (t - mt * P.tiles_n) * BN, m0 = mt * BM;
+  const int G = K / kGroup, NB = N / kTileRows;
+  const int gb = (int)((long long)G * sp / P.split), ge = (int)((long long)G * (sp + 1) / P.split);
+
+  // X * s: wave load u fills LDS chunks p = (wave * kDma + u) * 64 + lane of a
+  // stage; chunk p is row p / 16, physical chunk p % 16, holding logical chunk
+  // (p % 16) ^ (row % 16) of that row.  Rows past M read row M - 1 (rows of A
+  // only reach the same rows of D, which are not stored).  M * K * 2 < 2^31
+  // (checked by the launcher), so offsets fit the buffer resource.
+  const __amdgpu_buffer_rsrc_t xrs =
+      __builtin_amdgcn_make_buffer_rsrc((void *)P.xs, (short)0, M * K * 2, kRsrcWord3);
+  int xoff[kDma];
+#pragma unroll
+  for (int u = 0; u < kDma; ++u) {
+    const int p = (wave * kDma + u) * 64 + lane;
+    const int row = p / kRowChunks, lc = (p % kRowChunks) ^ (row % 16);
+    xoff[u] = (min(m0 + row, M - 1) * K + 8 * lc) * 2;
+  }
+  auto load_x = [&](int g, int buf) {
+#pragma unroll
+    for (int u = 0; u < kDma; ++u)
+    {
+      // (an array element passed straight to the builtin keeps the kernel from
+      // being instantiated in the host compilation)
+      const int vo = xoff[u];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          xrs, (__attribute__((address_space(3))) void *)(&As[buf][(wave * kDma + u) * 64 * 8]), 16,
+          vo, g * kGroup * 2, 0, 0);
+    }
+  };
+
+  // the wave's TN row blocks; blocks past N re-read the last one (never stored)
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)P.Wq, (short)0, (int)min((size_t)0x7fffffff, (size_t)N * K / 2), kRsrcWord3);
+  const int Gq = meta_groups(G) / kMetaQuad;
+  const size_t meta_bytes = (size_t)N * Gq * kMetaQuad * 2;
+  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)P.scales, (short)0, (int)min((size_t)0x7fffffff, meta_bytes), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t zrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)P.zeros, (short)0, (int)min((size_t)0x7fffffff, meta_bytes), kRsrcWord3);
+  const int rb0 = n0 / kTileRows + wave * TN;
+  const int tile_stride = NB * kTileBytes, meta_stride = NB * kTileRows * kMetaQuad * 2;
+  struct BStage {
+    u32x4 code[TN];
+    uint32_t sc[TN], zp[TN];  // raw fp16 bits of each row block's scale and zero point
+  };
+  auto load_b = [&](int g, BStage &b) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int rb = min(rb0 + j, NB - 1);
+      b.code[j] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrs, (rb * 64 + lane) * 16, g * tile_stride, 0));
+      const int mo = (rb * kTileRows + r) * kMetaQuad * 2;
+      const int qo = (g / kMetaQuad) * meta_stride + (g % kMetaQuad) * 2;
+      b.sc[j] = __builtin_amdgcn_raw_buffer_load_b16(srs, mo, qo, 0);
+      b.zp[j] = __builtin_amdgcn_raw_buffer_load_b16(zrs, mo, qo, 0);
+    }
+  };
+
+  float4v acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = float4v{0.f, 0.f, 0.f, 0.f};
+
+  // the four k steps of a group: this wave's B operands dequantized once per
+  // k step, then TM x TN MFMAs with A read from LDS buffer `buf`
+  auto compute = [&](const BStage &b, int buf) {
+    half2v bias_lo[TN], bias_hi[TN], scale[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const _Float16 z = __builtin_bit_cast(_Float16, (uint16_t)b.zp[j]);
+      const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)b.sc[j]);
+      const _Float16 blo = (_Float16)1024.0f + z, bhi = (_Float16)64.0f + z;
+      const half2v bl = {blo, blo}, bh = {bhi, bhi}, sc = {sv, sv};
+      bias_lo[j] = bl;
+      bias_hi[j] = bh;
+      scale[j] = sc;
+    }
+    const _Float16 *abuf = As[buf];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      half8 bop[TN];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bop[j] = dequant_word(b.code[j][tt], bias_lo[j], bias_hi[j], scale[j]);
+      // lane (c, r) reads logical chunk 4 tt + c of row 16 i + r
+      const int pc = (4 * tt + c) ^ r;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const half8 aop = *reinterpret_cast<const half8 *>(abuf + (16 * i + r) * kGroup + 8 * pc);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma16(aop, bop[j], acc[i][j]);
+      }
+    }
+  };
+
+  // One group per step: wait until this group's DMA and code loads (issued a
+  // step ago) have landed and every wave is past the previous step (so the
+  // other buffer is free), then issue the next group's loads, which land
+  // while this group's MFMAs run.  Past the range they re-read the last group
+  // (into a buffer and registers nobody reads).
+  auto step = [&](int g, BStage &cur, BStage &nxt, int buf) {
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    const int gn = min(g + 1, ge - 1);
+    load_x(gn, buf ^ 1);
+    load_b(gn, nxt);
+    compute(cur, buf);
+  };
+  BStage b0, b1;
+  load_x(gb, 0);
+  load_b(gb, b0);
+  for (int g = gb; g < ge; g += 2) {
+    step(g, b0, b1, 0);
+    if (g + 1 < ge) step(g + 1, b1, b0, 1);
+  }
+  // the last step's DMA must land before the workgroup's LDS is released
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // lane holds D[4c + v][r] of each 16x16 sub-block: the output, or this
+  // split's fp32 partial
+  float *part = P.split > 1 ? P.part + (size_t)sp * M * N : nullptr;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int n = n0 + (wave * TN + j) * 16 + r;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = m0 + i * 16 + 4 * c + v;
+        if (m < M && n < N) {
+          if (part)
+            part[(size_t)m * N + n] = acc[i][j][v];
+          else
+            P.Y[(size_t)m * N + n] = (_Float16)acc[i][j][v];
+        }
+      }
+    }
+  }
+}
+
+// fp16(X * s) of one problem, rounded once like the kernels' own staging: one
+// thread per 8 columns.
+__global__ __launch_bounds__(256) void prescale_f16_kernel(const _Float16 *__restrict__ X,
+                                                           const _Float16 *__restrict__ s,
+                                                           _Float16 *__restrict__ out, int K,
+                                                           long long n8) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const long long e = i * 8;
+  const int k = (int)(e % K);
+  *reinterpret_cast<half8 *>(out + e) = load_half8(X + e) * load_half8(s + k);
+}
+
 // Y = fp16(sum of the split partials, in split order) for the problems with
 // split > 1; four outputs per thread.
 constexpr int kReduceThreads = 256;
@@ -651,7 +841,37 @@ constexpr double kStageUs = 2.3;
 constexpr double kBlockStages = 2.0;
 constexpr double kReduceBytesPerUs = 4.0e6;
 
-int tiles_of(const GemmDesc &d) { return ((d.N + kBN - 1) / kBN) * ((d.M + kBM - 1) / kBM); }
+int tiles_of(const GemmDesc &d, int bm = kBM) {
+  return ((d.N + kBN - 1) / kBN) * ((d.M + bm - 1) / bm);
+}
+
+// tiled_dma_kernel takes fp16 activations and INT4 codes without outliers
+// whose X (M x K fp16) a buffer resource can cover; it runs 128-row wave
+// tiles, so it serves launches whose largest M exceeds 64.
+bool dma_capable(const GemmDesc &d) {
+  return !d.bf16 && !d.w8 && !d.o_row_ptr && (size_t)d.M * d.K * 2 < ((size_t)1 << 31);
+}
+constexpr int kDmaTM = 8, kDmaBM = kDmaTM * 16;
+constexpr int kDmaMinM = 65;
+
+bool dma_launch(const GemmDesc *d, int count) {
+  int mmax = 0;
+  for (int i = 0; i < count; ++i) {
+    if (!dma_capable(d[i])) return false;
+    mmax = std::max(mmax, d[i].M);
+  }
+  return mmax >= kDmaMinM;
+}
+
+size_t align256(size_t n) { return (n + 255) / 256 * 256; }
+
+// workspace bytes of the prescaled X * s of the problems that have an s
+size_t prescale_need(const GemmDesc *d, int count) {
+  size_t n = 0;
+  for (int i = 0; i < count; ++i)
+    if (d[i].s) n += align256((size_t)d[i].M * d[i].K * 2);
+  return n;
+}
 
 size_t part_bytes(const GemmDesc &d, int split) {
   return split > 1 ? ((size_t)split * d.M * d.N * sizeof(float) + 255) / 256 * 256 : 0;
@@ -663,7 +883,7 @@ size_t part_bytes(const GemmDesc &d, int split) {
 // plus the reduction of the partials.  Counting whole rounds matters: a launch
 // a few workgroups past a multiple of the slots takes a whole extra round.
 // Ties keep the longer ranges (fewer partials).
-void choose_splits(const GemmDesc *d, int count, int *split) {
+void choose_splits(const GemmDesc *d, int count, int *split, int bm = kBM) {
   // Only range lengths ceil(G / n) for some problem's G and n <= kMaxSplit give
   // distinct split vectors; try those, longest first.
   int cand[kMaxTiled * kMaxSplit];
@@ -685,7 +905,7 @@ void choose_splits(const GemmDesc *d, int count, int *split) {
       const int G = d[i].K / kGroup;
       const int cap = std::min(std::min(kMaxSplit, G), (G + kMinSplitGroups - 1) / kMinSplitGroups);
       s[i] = std::max(1, std::min(cap, (G + T - 1) / T));
-      blocks += (long long)tiles_of(d[i]) * s[i];
+      blocks += (long long)tiles_of(d[i], bm) * s[i];
       longest = std::max(longest, (G + s[i] - 1) / s[i]);
       if (s[i] > 1) reduce_bytes += (double)(4 * s[i] + 2) * d[i].M * d[i].N;
     }
@@ -702,9 +922,10 @@ void choose_splits(const GemmDesc *d, int count, int *split) {
 
 size_t tiled_workspace_bytes(const GemmDesc *d, int count) {
   if (count < 1 || count > kMaxTiled) return 0;
+  const bool dma = dma_launch(d, count);
   int split[kMaxTiled];
-  choose_splits(d, count, split);
-  size_t bytes = 0;
+  choose_splits(d, count, split, dma ? kDmaBM : kBM);
+  size_t bytes = dma ? prescale_need(d, count) : 0;
   for (int i = 0; i < count; ++i) bytes += part_bytes(d[i], split[i]);
   return bytes;
 }
@@ -714,13 +935,25 @@ int tiled_max_problems() { return kMaxTiled; }
 hipError_t launch_tiled_set(const GemmDesc *d, int count, void *workspace, size_t workspace_bytes,
                             hipStream_t stream) {
   if (count < 1 || count > kMaxTiled) return hipErrorInvalidValue;
+  // The DMA kernel needs the prescaled X * s of problems with an s in the
+  // workspace; without room for it the launch takes tiled_kernel.  Without
+  // room for the split partials as well, K is not split.
+  const size_t have = workspace ? workspace_bytes : 0;
+  const size_t pre = prescale_need(d, count);
+  const bool dma = dma_launch(d, count) && pre <= have;
+  const int bm = dma ? kDmaBM : kBM;
   int split[kMaxTiled];
-  choose_splits(d, count, split);
-  if (!workspace || workspace_bytes < tiled_workspace_bytes(d, count))
+  choose_splits(d, count, split, bm);
+  size_t parts = 0;
+  for (int i = 0; i < count; ++i) parts += part_bytes(d[i], split[i]);
+  if ((dma ? pre : 0) + parts > have)
     for (int i = 0; i < count; ++i) split[i] = 1;  // no room for partials: one K range
   TiledSet ts = {};
   int blocks = 0, rblocks = 0;
   size_t off = 0;
+  // prescaled X * s after the partials
+  size_t pre_off = 0;
+  for (int i = 0; i < count; ++i) pre_off += part_bytes(d[i], split[i]);
   bool out = false;  // some problem has fp16 outliers
   for (int i = 0; i < count; ++i) {
     TiledProblem &p = ts.p[i];
@@ -734,7 +967,7 @@ hipError_t launch_tiled_set(const GemmDesc *d, int count, void *workspace, size_
     p.N = d[i].N;
     p.K = d[i].K;
     p.tiles_n = (d[i].N + kBN - 1) / kBN;
-    p.tiles = tiles_of(d[i]);
+    p.tiles = tiles_of(d[i], bm);
     p.split = split[i];
     p.part = split[i] > 1 ? reinterpret_cast<float *>(static_cast<char *>(workspace) + off) : nullptr;
     off += part_bytes(d[i], split[i]);
@@ -743,6 +976,18 @@ hipError_t launch_tiled_set(const GemmDesc *d, int count, void *workspace, size_
     p.oval = static_cast<const _Float16 *>(d[i].o_val);
     out |= d[i].o_row_ptr != nullptr;
     p.bf16 = d[i].bf16;
+    p.xs = static_cast<const _Float16 *>(d[i].X);
+    if (dma && d[i].s) {
+      _Float16 *xs = reinterpret_cast<_Float16 *>(static_cast<char *>(workspace) + pre_off);
+      pre_off += align256((size_t)d[i].M * d[i].K * 2);
+      const long long n8 = (long long)d[i].M * d[i].K / 8;
+      hipLaunchKernelGGL(prescale_f16_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0,
+                         stream, static_cast<const _Float16 *>(d[i].X),
+                         static_cast<const _Float16 *>(d[i].s), xs, d[i].K, n8);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      p.xs = xs;
+    }
     p.block0 = blocks;
     blocks += p.tiles * p.split;
     p.rblock0 = rblocks;
@@ -751,7 +996,9 @@ hipError_t launch_tiled_set(const GemmDesc *d, int count, void *workspace, size_
   }
   ts.count = count;
   const dim3 grid(blocks), threads(kWM * kWN * 64);
-  if (d[0].w8 && d[0].bf16 && out)  // INT8 codes
+  if (dma)
+    hipLaunchKernelGGL((tiled_dma_kernel<kDmaTM>), grid, dim3(256), 0, stream, ts);
+  else if (d[0].w8 && d[0].bf16 && out)  // INT8 codes
     hipLaunchKernelGGL((tiled_kernel<kWM, kWN, kTM, kTN, true, true, true>), grid, threads, 0,
                        stream, ts);
   else if (d[0].w8 && d[0].bf16)
