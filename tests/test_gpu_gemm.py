@@ -296,15 +296,17 @@ def test_graph_replay_matches_eager():
 
 
 @pytest.mark.parametrize("awq", [False, True])
-@pytest.mark.parametrize("M,N,K", [(65, 272, 640), (100, 528, 1152), (128, 256, 4096),
+@pytest.mark.parametrize("M,N,K", [(17, 272, 640), (40, 528, 1152), (64, 48, 18944),
+                                   (65, 272, 640), (100, 528, 1152), (128, 256, 4096),
                                    (129, 272, 640), (257, 16, 4096), (300, 1024, 2048),
                                    (520, 784, 1408)])
 def test_dma_tiled_kernel(M, N, K, awq):
-    """The tiled kernel with 128-row wave tiles and X * s brought into LDS by DMA (fp16
-    activations, INT4 codes, M > 64): through w4a16_gemm, which passes a workspace (X * s
+    """The tiled kernel with X * s brought into LDS by DMA (fp16 activations, INT4 codes;
+    64-row wave tiles up to M = 64, 128-row ones above): through w4a16_gemm, which passes
+    a workspace (X * s
     prescaled there when s is given; K split where the blocks are few), and through the
     forced tiled path without a workspace (X straight from its buffer when s is null,
-    else the 64-row kernel).  Ragged M (rows past M re-read row M - 1 and are not
+    else the register-staged kernel).  Ragged M (rows past M re-read row M - 1 and are not
     stored), N not a multiple of 256, K a multiple of 128 but not of 512."""
     pw, s, ref = packed_case(N, K, awq, key=12, mat=N + K)
     X = activations(12, M, M, K, outliers=True)

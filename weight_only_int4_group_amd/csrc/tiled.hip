@@ -719,18 +719,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       scale[j] = sc;
     }
     const _Float16 *abuf = As[buf];
+    // software pipeline: k step tt + 1's B operands are dequantized while k
+    // step tt's MFMAs run, interleaved by the scheduler (one LDS read, four
+    // MFMAs and about seven VALU ops at a time)
+    half8 bop[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) bop[j] = dequant_word(b.code[j][0], bias_lo[j], bias_hi[j], scale[j]);
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
-      half8 bop[TN];
+      half8 bnx[TN];
+      if (tt < 3) {
 #pragma unroll
-      for (int j = 0; j < TN; ++j) bop[j] = dequant_word(b.code[j][tt], bias_lo[j], bias_hi[j], scale[j]);
-      // lane (c, r) reads logical chunk 4 tt + c of row 16 i + r
+        for (int j = 0; j < TN; ++j)
+          bnx[j] = dequant_word(b.code[j][tt + 1], bias_lo[j], bias_hi[j], scale[j]);
+      }
       const int pc = (4 * tt + c) ^ r;
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         const half8 aop = *reinterpret_cast<const half8 *>(abuf + (16 * i + r) * kGroup + 8 * pc);
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = mfma16(aop, bop[j], acc[i][j]);
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, TN, 0);  // TN MFMAs
+        if (tt < 3) __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);  // VALU
+      }
+      if (tt < 3) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) bop[j] = bnx[j];
       }
     }
   };
@@ -739,7 +757,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // step ago) have landed and every wave is past the previous step (so the
   // other buffer is free), then issue the next group's loads, which land
   // while this group's MFMAs run.  Past the range they re-read the last group
-  // (into a buffer and registers nobody reads).
+  // (into a buffer and registers nobody reads).  Buffers and register sets
+  // alternate with the loop unrolled by two, so nothing is copied.
   auto step = [&](int g, BStage &cur, BStage &nxt, int buf) {
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     const int gn = min(g + 1, ge - 1);
@@ -851,17 +870,19 @@ int tiles_of(const GemmDesc &d, int bm = kBM) {
 bool dma_capable(const GemmDesc &d) {
   return !d.bf16 && !d.w8 && !d.o_row_ptr && (size_t)d.M * d.K * 2 < ((size_t)1 << 31);
 }
-constexpr int kDmaTM = 8, kDmaBM = kDmaTM * 16;
-constexpr int kDmaMinM = 65;
+constexpr int kDmaMinM = 17;
 
-bool dma_launch(const GemmDesc *d, int count) {
+// 0 when the launch cannot take tiled_dma_kernel, else its TM: 8 (128-row
+// wave tiles) when the largest M exceeds 64, else 4
+int dma_tm(const GemmDesc *d, int count) {
   int mmax = 0;
   for (int i = 0; i < count; ++i) {
-    if (!dma_capable(d[i])) return false;
+    if (!dma_capable(d[i])) return 0;
     mmax = std::max(mmax, d[i].M);
   }
-  return mmax >= kDmaMinM;
+  return mmax < kDmaMinM ? 0 : (mmax > 64 ? 8 : 4);
 }
+bool dma_launch(const GemmDesc *d, int count) { return dma_tm(d, count) != 0; }
 
 size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 
@@ -922,9 +943,10 @@ void choose_splits(const GemmDesc *d, int count, int *split, int bm = kBM) {
 
 size_t tiled_workspace_bytes(const GemmDesc *d, int count) {
   if (count < 1 || count > kMaxTiled) return 0;
-  const bool dma = dma_launch(d, count);
+  const int tm = dma_tm(d, count);
+  const bool dma = tm != 0;
   int split[kMaxTiled];
-  choose_splits(d, count, split, dma ? kDmaBM : kBM);
+  choose_splits(d, count, split, dma ? 16 * tm : kBM);
   size_t bytes = dma ? prescale_need(d, count) : 0;
   for (int i = 0; i < count; ++i) bytes += part_bytes(d[i], split[i]);
   return bytes;
@@ -940,8 +962,9 @@ hipError_t launch_tiled_set(const GemmDesc *d, int count, void *workspace, size_
   // room for the split partials as well, K is not split.
   const size_t have = workspace ? workspace_bytes : 0;
   const size_t pre = prescale_need(d, count);
-  const bool dma = dma_launch(d, count) && pre <= have;
-  const int bm = dma ? kDmaBM : kBM;
+  const int tm = dma_tm(d, count);
+  const bool dma = tm != 0 && pre <= have;
+  const int bm = dma ? 16 * tm : kBM;
   int split[kMaxTiled];
   choose_splits(d, count, split, bm);
   size_t parts = 0;
@@ -996,8 +1019,10 @@ hipError_t launch_tiled_set(const GemmDesc *d, int count, void *workspace, size_
   }
   ts.count = count;
   const dim3 grid(blocks), threads(kWM * kWN * 64);
-  if (dma)
-    hipLaunchKernelGGL((tiled_dma_kernel<kDmaTM>), grid, dim3(256), 0, stream, ts);
+  if (dma && tm == 8)
+    hipLaunchKernelGGL((tiled_dma_kernel<8>), grid, dim3(256), 0, stream, ts);
+  else if (dma)
+    hipLaunchKernelGGL((tiled_dma_kernel<4>), grid, dim3(256), 0, stream, ts);
   else if (d[0].w8 && d[0].bf16 && out)  // INT8 codes
     hipLaunchKernelGGL((tiled_kernel<kWM, kWN, kTM, kTN, true, true, true>), grid, threads, 0,
                        stream, ts);
