@@ -160,8 +160,9 @@ def test_workspace_size():
     P = w4.Problem
     assert ws_size(P(A16, A16, A16, A16, None, A16, 9, 4096, 14336)) == (0, 0)
     assert ws_size(P(A16, A16, A16, A16, None, A16, 4096, 8192, 8192)) == (0, 0)
-    # 64 x 272 output: two 64 x 256 blocks x 32 groups, far fewer than the GPU's
-    # block slots, so K is cut into ranges of the minimum 8 groups: 4 splits
+    # 64 x 272 output: three 64 x 128 blocks (the DMA-staged kernel's M <= 64 shape)
+    # x 32 groups, far fewer than the GPU's block slots, so K is cut into ranges of
+    # the minimum 8 groups: 4 splits
     rc, nb = ws_size(P(A16, A16, A16, A16, None, A16, 64, 272, 4096))
     assert rc == 0 and nb == 4 * 64 * 272 * 4
     # a problem with M = 0 and a streaming one add nothing
@@ -185,11 +186,12 @@ def test_workspace_size():
 
 def test_split_counts_whole_rounds():
     """K splits of a grouped tiled call are chosen by whole rounds of resident
-    workgroups (host-only, through the workspace size).  Qwen2-7B-shaped layer,
-    64 x 256 output blocks, 512 slots: at M = 64 the 14-group ranges of the plain
-    fill-the-slots rule give 514 workgroups (two rounds); 15-group ranges give 500
-    (down in 10 splits, the six 28-group rows in 2).  At M = 256 one round cannot
-    hold the layer; two rounds of 30-group ranges split only down (5 ways)."""
+    workgroups (host-only, through the workspace size).  Qwen2-7B-shaped layer, fp16
+    activations and INT4 codes, so the launches take the DMA-staged tiled kernel:
+    at M = 64 its 64 x 128 blocks (388 of them) with four workgroups per CU (1024
+    slots): 15-group ranges give 1000 workgroups in one round (down in 10 splits, the
+    six 28-group rows in 2).  At M = 256 its 128 x 256 blocks (388) with two per CU
+    (512 slots): 30-group ranges split only down (5 ways), 500 workgroups."""
     P = w4.Problem
     shapes = [(3584, 3584), (512, 3584), (512, 3584), (3584, 3584), (18944, 3584),
               (18944, 3584), (3584, 18944)]
@@ -200,12 +202,16 @@ def test_split_counts_whole_rounds():
     splits64 = [2, 2, 2, 2, 2, 2, 10]
     rc, nb = ws_size(*layer(64))
     assert rc == 0 and nb == sum(s * 64 * N * 4 for s, (N, _) in zip(splits64, shapes))
-    blocks = sum(s * -(-N // 256) for s, (N, _) in zip(splits64, shapes))
-    assert blocks == 500
+    assert sum(s * -(-N // 128) for s, (N, _) in zip(splits64, shapes)) == 1000
+    splits256 = [1, 1, 1, 1, 1, 1, 5]
     rc, nb = ws_size(*layer(256))
     assert rc == 0 and nb == 5 * 256 * 3584 * 4
+    assert sum(s * 2 * -(-N // 256) for s, (N, _) in zip(splits256, shapes)) == 500
     # prefill-sized calls fill the GPU without splitting
     assert ws_size(P(A16, A16, A16, A16, None, A16, 4096, 28672, 8192)) == (0, 0)
+    # with an AWQ s the DMA kernel's workspace also holds the prescaled X * s
+    a256 = lambda n: -(-n // 256) * 256
+    assert ws_size(P(A16, A16, A16, A16, A16, A16, 4096, 28672, 8192)) == (0, a256(4096 * 8192 * 2))
 
 
 def test_grouped_ws_validation():

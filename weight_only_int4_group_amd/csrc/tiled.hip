@@ -619,12 +619,15 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
 //   * the wave's code tiles (16 bytes per lane per tile, its MFMA B operands)
 //     and their scales and zero points are loaded into registers one group
 //     ahead, in two register sets that alternate.
-// Blocks are BM x 256 (BM = 16 TM), four waves of BM x 64; K is split across
-// workgroups the same way as in tiled_kernel.
-template <int TM>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void tiled_dma_kernel(
+// Blocks are BM x BN (BM = 16 TM, BN = 64 TN), four waves of BM x 16 TN; K is
+// split across workgroups the same way as in tiled_kernel.  Batched decode (M
+// up to 64) takes TN = 2: twice the blocks of TN = 4, so fewer K splits (whose
+// fp32 partials cost HBM traffic) are needed to fill the GPU, and half the
+// accumulators, so four workgroups fit on a CU.
+template <int TM, int TN>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TN == 2 ? 4 : 2, TN == 2 ? 4 : 2))) void tiled_dma_kernel(
     TiledSet ts) {
-  constexpr int TN = 4, WN = 4;
+  constexpr int WN = 4;
   constexpr int BM = TM * 16, BN = WN * TN * 16;
   constexpr int kRowChunks = kGroup / 8;            // 16-byte chunks per row per group
   constexpr int kDma = BM * kRowChunks / (4 * 64);  // DMA loads per wave per group
@@ -860,8 +863,8 @@ constexpr double kStageUs = 2.3;
 constexpr double kBlockStages = 2.0;
 constexpr double kReduceBytesPerUs = 4.0e6;
 
-int tiles_of(const GemmDesc &d, int bm = kBM) {
-  return ((d.N + kBN - 1) / kBN) * ((d.M + bm - 1) / bm);
+int tiles_of(const GemmDesc &d, int bm = kBM, int bn = kBN) {
+  return ((d.N + bn - 1) / bn) * ((d.M + bm - 1) / bm);
 }
 
 // tiled_dma_kernel takes fp16 activations and INT4 codes without outliers
@@ -871,6 +874,17 @@ bool dma_capable(const GemmDesc &d) {
   return !d.bf16 && !d.w8 && !d.o_row_ptr && (size_t)d.M * d.K * 2 < ((size_t)1 << 31);
 }
 constexpr int kDmaMinM = 17;
+
+// Geometry of the tiled_dma_kernel instances: TM = 8, TN = 4 (128 x 256
+// blocks, two workgroups per CU) when the launch's largest M exceeds 64, else
+// TM = 4, TN = 2 (64 x 128 blocks, four workgroups per CU).
+struct DmaShape {
+  int tm, tn;
+  int bm() const { return 16 * tm; }
+  int bn() const { return 64 * tn; }
+  long long slots() const { return tn == 2 ? 1024 : 512; }
+};
+DmaShape dma_shape(int tm) { return tm == 8 ? DmaShape{8, 4} : DmaShape{4, 2}; }
 
 // 0 when the launch cannot take tiled_dma_kernel, else its TM: 8 (128-row
 // wave tiles) when the largest M exceeds 64, else 4
@@ -904,7 +918,8 @@ size_t part_bytes(const GemmDesc &d, int split) {
 // plus the reduction of the partials.  Counting whole rounds matters: a launch
 // a few workgroups past a multiple of the slots takes a whole extra round.
 // Ties keep the longer ranges (fewer partials).
-void choose_splits(const GemmDesc *d, int count, int *split, int bm = kBM) {
+void choose_splits(const GemmDesc *d, int count, int *split, int bm = kBM, int bn = kBN,
+                   long long slots = kBlockSlots) {
   // Only range lengths ceil(G / n) for some problem's G and n <= kMaxSplit give
   // distinct split vectors; try those, longest first.
   int cand[kMaxTiled * kMaxSplit];
@@ -926,11 +941,11 @@ void choose_splits(const GemmDesc *d, int count, int *split, int bm = kBM) {
       const int G = d[i].K / kGroup;
       const int cap = std::min(std::min(kMaxSplit, G), (G + kMinSplitGroups - 1) / kMinSplitGroups);
       s[i] = std::max(1, std::min(cap, (G + T - 1) / T));
-      blocks += (long long)tiles_of(d[i], bm) * s[i];
+      blocks += (long long)tiles_of(d[i], bm, bn) * s[i];
       longest = std::max(longest, (G + s[i] - 1) / s[i]);
       if (s[i] > 1) reduce_bytes += (double)(4 * s[i] + 2) * d[i].M * d[i].N;
     }
-    const long long rounds = (blocks + kBlockSlots - 1) / kBlockSlots;
+    const long long rounds = (blocks + slots - 1) / slots;
     const double t = (double)rounds * (longest + kBlockStages) * kStageUs + reduce_bytes / kReduceBytesPerUs;
     if (ci == 0 || t < best) {
       best = t;
@@ -946,7 +961,10 @@ size_t tiled_workspace_bytes(const GemmDesc *d, int count) {
   const int tm = dma_tm(d, count);
   const bool dma = tm != 0;
   int split[kMaxTiled];
-  choose_splits(d, count, split, dma ? 16 * tm : kBM);
+  if (dma)
+    choose_splits(d, count, split, dma_shape(tm).bm(), dma_shape(tm).bn(), dma_shape(tm).slots());
+  else
+    choose_splits(d, count, split);
   size_t bytes = dma ? prescale_need(d, count) : 0;
   for (int i = 0; i < count; ++i) bytes += part_bytes(d[i], split[i]);
   return bytes;
@@ -964,9 +982,13 @@ hipError_t launch_tiled_set(const GemmDesc *d, int count, void *workspace, size_
   const size_t pre = prescale_need(d, count);
   const int tm = dma_tm(d, count);
   const bool dma = tm != 0 && pre <= have;
-  const int bm = dma ? 16 * tm : kBM;
+  const DmaShape ds = dma_shape(tm);
+  const int bm = dma ? ds.bm() : kBM, bn = dma ? ds.bn() : kBN;
   int split[kMaxTiled];
-  choose_splits(d, count, split, bm);
+  if (dma)
+    choose_splits(d, count, split, bm, bn, ds.slots());
+  else
+    choose_splits(d, count, split);
   size_t parts = 0;
   for (int i = 0; i < count; ++i) parts += part_bytes(d[i], split[i]);
   if ((dma ? pre : 0) + parts > have)
@@ -989,8 +1011,8 @@ hipError_t launch_tiled_set(const GemmDesc *d, int count, void *workspace, size_
     p.M = d[i].M;
     p.N = d[i].N;
     p.K = d[i].K;
-    p.tiles_n = (d[i].N + kBN - 1) / kBN;
-    p.tiles = tiles_of(d[i], bm);
+    p.tiles_n = (d[i].N + bn - 1) / bn;
+    p.tiles = tiles_of(d[i], bm, bn);
     p.split = split[i];
     p.part = split[i] > 1 ? reinterpret_cast<float *>(static_cast<char *>(workspace) + off) : nullptr;
     off += part_bytes(d[i], split[i]);
@@ -1020,9 +1042,9 @@ hipError_t launch_tiled_set(const GemmDesc *d, int count, void *workspace, size_
   ts.count = count;
   const dim3 grid(blocks), threads(kWM * kWN * 64);
   if (dma && tm == 8)
-    hipLaunchKernelGGL((tiled_dma_kernel<8>), grid, dim3(256), 0, stream, ts);
+    hipLaunchKernelGGL((tiled_dma_kernel<8, 4>), grid, dim3(256), 0, stream, ts);
   else if (dma)
-    hipLaunchKernelGGL((tiled_dma_kernel<4>), grid, dim3(256), 0, stream, ts);
+    hipLaunchKernelGGL((tiled_dma_kernel<4, 2>), grid, dim3(256), 0, stream, ts);
   else if (d[0].w8 && d[0].bf16 && out)  // INT8 codes
     hipLaunchKernelGGL((tiled_kernel<kWM, kWN, kTM, kTN, true, true, true>), grid, threads, 0,
                        stream, ts);
