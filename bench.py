@@ -720,12 +720,14 @@ def main():
                         "1% activation channels x20, one launch per matrix",
             "TFLOP/s": round(flops / (pwall / args.prefill_steps) / 1e12, 2),
             "ms_per_step": round(pwall / args.prefill_steps * 1e3, 4),
-            "roofline": {"bound": "mfma", "kernel": "tiled_kernel",
+            "roofline": {"bound": "mfma",
+                         "kernel": "tiled_dma_kernel<8, 4> per matrix call (with prescale_f16_kernel "
+                                   "for X * s, and split_reduce_kernel for k and v)",
                          "avg_launch_us": round(tot_ms / len(pmats) * 1e3, 2),
                          "achieved": round(flops / (tot_ms * 1e-3) / 1e12, 2),
                          "peak": FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(flops / (tot_ms * 1e-3) / 1e12 / FP16_PEAK_TFLOPS, 4),
-                         "traffic": profiled_traffic("tiled_prefill_70b_layer_m4096_counters.txt",
+                         "traffic": profiled_traffic("tiled_dma_prefill_70b_layer_m4096_counters.txt",
                                                      "tiled.hip")},
             "per_matrix": variant(pmats, groups, pms, args.prefill_steps, pwall, "flops")["launches"],
         }
