@@ -415,6 +415,55 @@ def read_ceiling(torch, nbytes, launches=100, per=10):
             "top5": sorted(table, key=lambda r: r["us"])[:5]}
 
 
+def mfma_ceiling(torch, launches=20):
+    """The measured dense fp16 matrix-core ceiling: a HIP kernel (libw4a16_ceiling.so)
+    whose waves only issue independent 16x16x32 fp16 MFMAs from registers, about 2e12
+    flops per launch, timed with HIP events around `launches` back-to-back launches
+    after two untimed ones.  Chains per wave (8, 16, 32) and workgroups (one to four
+    waves per SIMD) are swept; the fastest is the ceiling.  It shows the rate the
+    matrix cores sustain at the clock they run at under full load, beside the
+    nominal 2.5 PFLOP/s."""
+    import ctypes
+    from weight_only_int4_group_amd.build import CEILING_LIB_PATH
+    if not os.path.exists(CEILING_LIB_PATH):
+        raise RuntimeError(f"{CEILING_LIB_PATH} is missing: build the library first")
+    L = ctypes.CDLL(CEILING_LIB_PATH)
+    L.mfma_peak.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                            ctypes.c_void_p]
+    L.mfma_peak.restype = ctypes.c_int
+    grids = (256, 512, 1024)
+    sink = torch.empty(max(grids) * 256, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    table = []
+    for chains in (8, 16, 32):
+        for blocks in grids:
+            iters = max(1, int(2e12 / (blocks * 4 * chains * 16384)))
+            flops = blocks * 4 * chains * iters * 16384
+
+            def go():
+                rc = L.mfma_peak(chains, blocks, iters, sink.data_ptr(), stream.cuda_stream)
+                if rc:
+                    raise RuntimeError(f"mfma_peak failed: {rc}")
+            go()
+            go()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(launches):
+                go()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            sec = e0.elapsed_time(e1) / launches * 1e-3
+            table.append({"chains": chains, "workgroups": blocks, "us": round(sec * 1e6, 1),
+                          "TFLOP/s": round(flops / sec / 1e12, 1)})
+    del sink
+    best = max(table, key=lambda r: r["TFLOP/s"])
+    return {"kernel": "mfma_peak_kernel (independent 16x16x32 fp16 MFMAs from registers, "
+                      "libw4a16_ceiling.so)",
+            "TFLOP/s": best["TFLOP/s"], "best": best,
+            "frac_of_nominal": round(best["TFLOP/s"] / FP16_PEAK_TFLOPS, 4), "table": table}
+
+
 def ceilings(torch, reps=10):
     """Measured ceilings on this GPU, for context: a plain device-to-device copy, and
     the vendor dense fp16 GEMM (torch.matmul on contiguous fp16 operands) at the 70B
@@ -455,67 +504,93 @@ def ceilings(torch, reps=10):
     return out
 
 
-def cpu_baseline(cfg, M, workloads, rows=1024, budget_s=10.0):
-    """The fp64 oracle (dequantize then matmul), timed on this host on a bounded
-    sample of the workload: the first `rows` rows of every matrix, quantized by
-    the oracle beforehand (untimed), then oracle.gemm repeated over the sample
-    until about `budget_s` have passed.  Reported as TB/s of algorithmic bytes."""
+CPU_SAMPLE_ROWS = {"gemv_1024": 1024, "llama3_8b_decode": 512, "llama3_8b_verify": 512,
+                   "qwen2_7b_batched_decode": 256, "llama_70b_prefill": 64}
+
+
+def cpu_baseline(cfg, M, workloads, budget_s=10.0, item_s=1.0):
+    """The fp64 CPU oracle as it stands (oracle.quantize / pack_codes / pack_meta and
+    oracle.gemm = dequantize then one BLAS matmul), timed on this host.  Cores are the
+    CPUs this process may run on (len(os.sched_getaffinity(0))); the BLAS thread count
+    is set to that number.  Every timing runs on a bounded row sample, stated with it:
+      * value: oracle.gemm over the first CPU_SAMPLE_ROWS rows of each matrix of the
+        benchmark's own workload (the M = 1 decode layer), repeated for about
+        `budget_s`, in TB/s of algorithmic bytes like the GPU figure;
+      * per_config: for each of the five configurations, oracle.quantize + pack over
+        that config's row sample (MB of fp16 weights per s), and for each of its M,
+        oracle.gemm over the same sample (TB/s of algorithmic bytes, and TFLOP/s),
+        each repeated for about `item_s`."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover - threadpoolctl missing
-        threads = 1
-    parts = []
-    for mi, mat in enumerate(cfg.matrices):
-        n = min(rows, mat.N)
-        Wr = workloads.weight_rows(cfg.weight_key, mi, mat.N, mat.K, 0, n)
-        s = workloads.awq_scales(cfg.weight_key, mi, mat.K) if cfg.awq else None
-        X = workloads.activations(cfg.weight_key, mi, M, mat.K, outliers=cfg.act_outliers)
-        parts.append((X, oracle.quantize(Wr, s), s, n, mat.K))
-    byts, reps = 0, 0
-    t0 = time.perf_counter()
-    while True:
-        for X, ref, s, n, K in parts:
-            oracle.gemm(X, ref.q, ref.scales, ref.zeros, s)
-            byts += alg_bytes(M, n, K, s is not None)
-        reps += 1
-        dt = time.perf_counter() - t0
-        if dt >= budget_s:
-            break
-    out = {"value": float(f"{byts / dt / 1e12:.6g}"), "unit": "TB/s", "cores": int(threads),
-           "kind": "oracle", "seconds": round(dt, 2),
-           "sample": f"first {rows} rows of each of the {len(cfg.matrices)} matrices of "
-                     f"{cfg.name} at M={M}, oracle.gemm (fp64 dequantize + matmul) "
-                     f"repeated {reps}x"}
-    # the offline step on the same sample, and the single 1024 x 1024 matrix with one
-    # BLAS thread (the oracle's quantize and pack are single-threaded NumPy)
-    t0 = time.perf_counter()
-    wbytes = 0
-    for mi, mat in enumerate(cfg.matrices):
-        n = min(rows, mat.N)
-        Wr = workloads.weight_rows(cfg.weight_key, mi, mat.N, mat.K, 0, n)
-        s = workloads.awq_scales(cfg.weight_key, mi, mat.K) if cfg.awq else None
-        ref = oracle.quantize(Wr, s)
-        oracle.pack_codes(ref.q)
-        oracle.pack_meta(ref.scales)
-        oracle.pack_meta(ref.zeros)
-        wbytes += 2 * n * mat.K
-    out["quantize_pack"] = {"MB_of_fp16_weights_per_s": round(wbytes / (time.perf_counter() - t0)
-                                                              / 1e6, 2),
-                            "sample": f"the same {rows}-row slices: oracle.quantize + pack_codes "
-                                      "+ pack_meta"}
-    g1 = workloads.config_by_name("gemv_1024")
-    W1 = workloads.weights(g1.weight_key, 0, 1024, 1024)
-    X1 = workloads.activations(g1.weight_key, 0, 1, 1024)
-    r1 = oracle.quantize(W1, None)
-    from threadpoolctl import threadpool_limits
-    with threadpool_limits(limits=1):
-        t0, n1 = time.perf_counter(), 0
-        while time.perf_counter() - t0 < 1.0:
-            oracle.gemm(X1, r1.q, r1.scales, r1.zeros, None)
-            n1 += 1
-        out["gemv_1024_one_thread_ms"] = round((time.perf_counter() - t0) / n1 * 1e3, 3)
+    from threadpoolctl import threadpool_info, threadpool_limits
+    cores = len(os.sched_getaffinity(0))
+
+    def sample(c, M_):
+        n_rows = CPU_SAMPLE_ROWS[c.name]
+        parts = []
+        for mi, mat in enumerate(c.matrices):
+            n = min(n_rows, mat.N)
+            Wr = workloads.weight_rows(c.weight_key, mi, mat.N, mat.K, 0, n)
+            sv = workloads.awq_scales(c.weight_key, mi, mat.K) if c.awq else None
+            parts.append((mi, mat, n, Wr, sv))
+        return parts
+
+    def time_gemm(c, M_, parts, quants, budget):
+        xs = [workloads.activations(c.weight_key, mi, M_, mat.K, outliers=c.act_outliers)
+              for mi, mat, n, Wr, sv in parts]
+        byts = flops = reps = 0
+        t0 = time.perf_counter()
+        while True:
+            for X, (mi, mat, n, Wr, sv), ref in zip(xs, parts, quants):
+                oracle.gemm(X, ref.q, ref.scales, ref.zeros, sv)
+                byts += alg_bytes(M_, n, mat.K, sv is not None)
+                flops += 2 * M_ * n * mat.K
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt >= budget:
+                return byts / dt, flops / dt, reps, dt
+
+    with threadpool_limits(limits=cores, user_api="blas"):
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                            if i.get("user_api") == "blas"] + [1])
+        parts = sample(cfg, M)
+        quants = [oracle.quantize(Wr, sv) for mi, mat, n, Wr, sv in parts]
+        bps, fps, reps, dt = time_gemm(cfg, M, parts, quants, budget_s)
+        out = {"value": float(f"{bps / 1e12:.6g}"), "unit": "TB/s", "cores": cores,
+               "blas_threads": blas_threads, "kind": "oracle", "seconds": round(dt, 2),
+               "sample": f"first {CPU_SAMPLE_ROWS[cfg.name]} rows of each of the "
+                         f"{len(cfg.matrices)} matrices of {cfg.name} at M={M}: oracle.gemm "
+                         f"(fp64 dequantize + matmul) repeated {reps}x"}
+        per = []
+        for c in workloads.CONFIGS:
+            parts = sample(c, c.Ms[0])
+            t0, wbytes, qreps = time.perf_counter(), 0, 0
+            while True:
+                quants = []
+                for mi, mat, n, Wr, sv in parts:
+                    ref = oracle.quantize(Wr, sv)
+                    oracle.pack_codes(ref.q)
+                    oracle.pack_meta(ref.scales)
+                    oracle.pack_meta(ref.zeros)
+                    quants.append(ref)
+                    wbytes += 2 * n * mat.K
+                qreps += 1
+                if time.perf_counter() - t0 >= item_s:
+                    break
+            qdt = time.perf_counter() - t0
+            entry = {"config": c.name, "sample_rows": CPU_SAMPLE_ROWS[c.name],
+                     "quantize_pack": {"MB_of_fp16_weights_per_s": round(wbytes / qdt / 1e6, 3),
+                                       "reps": qreps},
+                     "gemm": []}
+            for M_ in c.Ms:
+                bps, fps, reps, dt = time_gemm(c, M_, parts, quants, item_s)
+                entry["gemm"].append({"M": M_, "TB/s": float(f"{bps / 1e12:.4g}"),
+                                      "TFLOP/s": float(f"{fps / 1e12:.4g}"), "reps": reps})
+            per.append(entry)
+        out["per_config"] = per
+        out["per_config_note"] = (
+            f"each config: its matrices' first sample_rows rows; quantize_pack = oracle.quantize "
+            f"+ pack_codes + pack_meta (scales, zeros); gemm = oracle.gemm at each M, about "
+            f"{item_s:g} s each")
     return out
 
 
@@ -731,6 +806,13 @@ def main():
                                                      "tiled.hip")},
             "per_matrix": variant(pmats, groups, pms, args.prefill_steps, pwall, "flops")["launches"],
         }
+        if not args.no_ceilings:
+            # the matrix cores' own sustained rate on this GPU, for context
+            log("measuring the MFMA-only ceiling")
+            mc = mfma_ceiling(torch)
+            out["prefill"]["roofline"]["mfma_ceiling"] = mc
+            out["prefill"]["roofline"]["frac_of_mfma_ceiling"] = round(
+                out["prefill"]["roofline"]["achieved"] / mc["TFLOP/s"], 4)
         if not args.no_bf16:
             bpm = with_bf16(pmats, pcfg, PM, torch, workloads)
             _, bpms = timed(make_calls(bpm, ppool, pc, groups, w4, torch), args.prefill_steps, 2,

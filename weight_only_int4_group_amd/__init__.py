@@ -16,7 +16,11 @@ import ctypes
 import os
 from dataclasses import dataclass
 
-from .build import LIB_PATH
+from .build import LIB_PATH as _BUILT_LIB
+
+# the in-tree build; W4A16_LIB names another build of the same sources (the
+# host-sanitized one, for CPU runs of the validation tests)
+LIB_PATH = os.environ.get("W4A16_LIB") or _BUILT_LIB
 
 __all__ = [
     "W4A16Error", "PackedWeight", "GROUP", "PATH_AUTO", "PATH_SKINNY", "PATH_TILED",

@@ -15,10 +15,16 @@ LIB_NAME = "libw4a16.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 SOURCES = ("api.hip", "pack.hip", "skinny.hip", "tiled.hip", "spec.hip", "outliers.hip",
            "gptq.hip")
-# the plain streaming-read kernel the benchmark times as its bandwidth ceiling:
+# the plain streaming-read and MFMA-only kernels the benchmark times as its
+# bandwidth and matrix-core ceilings:
 # its own small library, not part of the W4A16 ABI
-CEILING_SOURCES = ("stream_read.hip",)
+CEILING_SOURCES = ("stream_read.hip", "mfma_peak.hip")
 CEILING_LIB_PATH = os.path.join(PKG_DIR, "libw4a16_ceiling.so")
+# host-side AddressSanitizer + UndefinedBehaviorSanitizer build of the library
+# (device code unchanged), for running the argument-validation tests on a CPU
+HOSTSAN_LIB_PATH = os.path.join(PKG_DIR, "libw4a16_hostsan.so")
+HOST_SANITIZE_FLAGS = ("-Xarch_host -fsanitize=address -Xarch_host -fsanitize=undefined "
+                       "-Xarch_host -fno-omit-frame-pointer -g").split()
 ARCH = "gfx950"
 
 
@@ -64,5 +70,17 @@ def build(verbose: bool = False) -> str:
     return LIB_PATH
 
 
+def build_host_sanitized(verbose: bool = False) -> str:
+    """Compile the library with ASan and UBSan on its host code into HOSTSAN_LIB_PATH.
+    Load it with the sanitizer runtime preloaded (the Python interpreter itself is
+    not instrumented) and W4A16_LIB pointing at it; its device code is the
+    ordinary build's."""
+    _compile(SOURCES, HOSTSAN_LIB_PATH, ["-ldl", *HOST_SANITIZE_FLAGS], verbose)
+    return HOSTSAN_LIB_PATH
+
+
 if __name__ == "__main__":
-    print(build(verbose=True))
+    if "--host-sanitize" in sys.argv[1:]:
+        print(build_host_sanitized(verbose=True))
+    else:
+        print(build(verbose=True))
