@@ -263,6 +263,42 @@ def batched_line(cfg, M, mats, pool, copies, w4, torch, workloads, steps=200, wa
             "TFLOP/s": round(fl / (wall / steps) / 1e12, 2)}
 
 
+SWEEP_MS = (17, 24, 32, 48, 64, 96, 128, 256)
+
+
+def dispatch_sweep(torch, w4, workloads, steps=50, warmup=5):
+    """The M-dispatch crossover, measured: for the 8B, Qwen2-7B and 70B layers and every
+    M in SWEEP_MS, one layer step through the tiled GEMM (the grouped call with its
+    workspace: what the dispatch picks above 16 rows) against the streaming kernel fed
+    16-row pieces (each piece of every matrix one problem of the grouped call, so the
+    weights are streamed once per 16 rows).  HIP events per layer step, weights rotated
+    over copies like the decode benchmark."""
+    rows = []
+    for name in ("llama3_8b_decode", "qwen2_7b_batched_decode", "llama_70b_prefill"):
+        cfg = workloads.config_by_name(name)
+        log(f"dispatch sweep: preparing {cfg.name}")
+        mats, pool, _, copies = prepare_layer(cfg, 1, torch, w4, workloads,
+                                              copies_min_bytes=POOL_BYTES // 2)
+        st = torch.cuda.current_stream().cuda_stream
+        for M in SWEEP_MS:
+            bm = with_batch(mats, cfg, M, torch, workloads)
+            tiled = make_calls(bm, pool, copies, [list(range(len(bm)))], w4, torch)
+            pieces = [[w4.GroupedCall([(m["X"][m0:m0 + 16], pool[j][c], m["s"], m["Y"][m0:m0 + 16])
+                                       for j, m in enumerate(bm) for m0 in range(0, M, 16)],
+                                      stream=st)] for c in range(copies)]
+            _, tms = timed(tiled, steps, warmup, torch)
+            _, sms = timed(pieces, steps, warmup, torch)
+            t_us, s_us = float(np.mean(tms[0])) * 1e3, float(np.mean(sms[0])) * 1e3
+            rows.append({"layer": cfg.name, "M": M, "tiled_us": round(t_us, 2),
+                         "streaming_pieces_us": round(s_us, 2),
+                         "faster": "tiled" if t_us <= s_us else "streaming"})
+            log(f"  M={M}: tiled {t_us:.1f} us, streaming pieces {s_us:.1f} us")
+            del bm, tiled, pieces
+        del mats, pool
+        torch.cuda.empty_cache()
+    return rows
+
+
 def gemv_line(torch, w4, workloads, steps=400, warmup=40):
     """The single 1024 x 1024 matrix at M = 1: 0.56 MB per call, far below what
     keeps HBM busy, so the time is launch latency, not bandwidth."""
@@ -615,6 +651,10 @@ def main():
                          "default: a calibration copy, 20 decode steps, the 70B prefill "
                          "matrices), 'verify' (8B layer at M=2, 5, 9) or 'batched' (Qwen2-7B "
                          "layer at M=64, 256)")
+    ap.add_argument("--dispatch-sweep", action="store_true",
+                    help="only the M-dispatch crossover sweep (tiled vs 16-row streaming "
+                         "pieces, M = 17..256 on the 8B, Qwen2-7B and 70B layers), as one "
+                         "JSON line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path "
@@ -637,6 +677,9 @@ def main():
         return
     if args.profile_run:
         profile_run(torch, w4, workloads)
+        return
+    if args.dispatch_sweep:
+        print(json.dumps({"dispatch_sweep": dispatch_sweep(torch, w4, workloads)}), flush=True)
         return
     cfg = workloads.config_by_name("llama3_8b_decode")
     M = cfg.Ms[0]

@@ -316,3 +316,30 @@ def test_dma_tiled_kernel(M, N, K, awq):
     assert_close(Y, want, f"dma {M}x{N}x{K} awq={awq}")
     note(f"dma tiled forced path M={M} N={N} K={K} awq={awq}")
     assert_close(run(X, pw, s, "tiled"), want, f"tiled path {M}x{N}x{K} awq={awq}")
+
+
+@pytest.mark.parametrize("M", [40, 130])
+def test_dma_shared_activation_prescale(M):
+    """A grouped call whose problems share X and s (the q, k and v projections of one
+    layer input) prescales X * s once and all of them read it; a fourth problem with its
+    own s in the same call gets its own copy.  Each output matches the oracle."""
+    torch_cuda()
+    K = 1152
+    s = awq_scales(21, 0, K)
+    s2 = awq_scales(21, 1, K)
+    X = activations(21, 0, M, K, outliers=True)
+    Xd, sd, s2d = to_dev(X), to_dev(s), to_dev(s2)
+    cases = []
+    for j, (N, sv, svd) in enumerate([(272, s, sd), (48, s, sd), (48, s, sd), (528, s2, s2d)]):
+        W = weights(21, 10 + j, N, K)
+        pw = w4.w4a16_quantize_pack(to_dev(W), svd)
+        cases.append((pw, sv, svd, oracle.quantize(W, sv), N))
+    T = w4._torch()
+    items = [(Xd, pw, svd, T.empty((M, N), dtype=T.float16, device="cuda"))
+             for pw, sv, svd, ref, N in cases]
+    note(f"shared-activation prescale M={M}")
+    call = w4.GroupedCall(items)
+    call()
+    for (pw, sv, svd, ref, N), it in zip(cases, items):
+        assert_close(to_host(it[3]), oracle.gemm(X, ref.q, ref.scales, ref.zeros, sv),
+                     f"shared X*s M={M} N={N}")

@@ -811,17 +811,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TN == 2 ? 4
   }
 }
 
-// fp16(X * s) of one problem, rounded once like the kernels' own staging: one
-// thread per 8 columns.
-__global__ __launch_bounds__(256) void prescale_f16_kernel(const _Float16 *__restrict__ X,
-                                                           const _Float16 *__restrict__ s,
-                                                           _Float16 *__restrict__ out, int K,
-                                                           long long n8) {
-  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n8) return;
+// fp16(X * s) of the problems of a launch that have an s, rounded once like
+// the kernels' own staging, in one launch: one thread per 8 columns, the
+// problems' workgroups concatenated.
+struct PrescaleItem {
+  const _Float16 *X, *s;
+  _Float16 *out;
+  int K;
+  int block0;  // first workgroup of this problem
+  long long n8;
+};
+struct PrescaleSet {
+  PrescaleItem p[kMaxTiled];
+  int count;
+};
+
+__global__ __launch_bounds__(256) void prescale_f16_kernel(PrescaleSet ps) {
+  int pi = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxTiled; ++i)
+    if (i < ps.count && (int)blockIdx.x >= ps.p[i].block0) pi = i;
+  const _Float16 *X = uniform_ptr(ps.p[pi].X), *sv = uniform_ptr(ps.p[pi].s);
+  _Float16 *out = uniform_ptr(ps.p[pi].out);
+  const int K = uniform_int(ps.p[pi].K), block0 = uniform_int(ps.p[pi].block0);
+  const long long i = (long long)((int)blockIdx.x - block0) * 256 + threadIdx.x;
+  if (i >= ps.p[pi].n8) return;
   const long long e = i * 8;
   const int k = (int)(e % K);
-  *reinterpret_cast<half8 *>(out + e) = load_half8(X + e) * load_half8(s + k);
+  *reinterpret_cast<half8 *>(out + e) = load_half8(X + e) * load_half8(sv + k);
 }
 
 // Y = fp16(sum of the split partials, in split order) for the problems with
@@ -1010,6 +1027,8 @@ hipError_t launch_tiled_set(const GemmDesc *d, int count, void *workspace, size_
   size_t pre_off = 0;
   for (int i = 0; i < count; ++i) pre_off += part_bytes(d[i], split[i]);
   bool out = false;  // some problem has fp16 outliers
+  PrescaleSet pset = {};
+  int pblocks = 0;
   for (int i = 0; i < count; ++i) {
     TiledProblem &p = ts.p[i];
     p.X = static_cast<const _Float16 *>(d[i].X);
@@ -1033,15 +1052,26 @@ hipError_t launch_tiled_set(const GemmDesc *d, int count, void *workspace, size_
     p.bf16 = d[i].bf16;
     p.xs = static_cast<const _Float16 *>(d[i].X);
     if (dma && d[i].s) {
-      _Float16 *xs = reinterpret_cast<_Float16 *>(static_cast<char *>(workspace) + pre_off);
-      pre_off += align256((size_t)d[i].M * d[i].K * 2);
-      const long long n8 = (long long)d[i].M * d[i].K / 8;
-      hipLaunchKernelGGL(prescale_f16_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0,
-                         stream, static_cast<const _Float16 *>(d[i].X),
-                         static_cast<const _Float16 *>(d[i].s), xs, d[i].K, n8);
-      const hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
-      p.xs = xs;
+      // problems with the same X, s and shape (q, k and v of one layer, say)
+      // share one prescaled copy
+      int twin = -1;
+      for (int j = 0; j < i && twin < 0; ++j)
+        if (d[j].s == d[i].s && d[j].X == d[i].X && d[j].M == d[i].M && d[j].K == d[i].K) twin = j;
+      if (twin >= 0) {
+        p.xs = ts.p[twin].xs;
+      } else {
+        _Float16 *xs = reinterpret_cast<_Float16 *>(static_cast<char *>(workspace) + pre_off);
+        pre_off += align256((size_t)d[i].M * d[i].K * 2);
+        PrescaleItem &q = pset.p[pset.count++];
+        q.X = static_cast<const _Float16 *>(d[i].X);
+        q.s = static_cast<const _Float16 *>(d[i].s);
+        q.out = xs;
+        q.K = d[i].K;
+        q.n8 = (long long)d[i].M * d[i].K / 8;
+        q.block0 = pblocks;
+        pblocks += (int)((q.n8 + 255) / 256);
+        p.xs = xs;
+      }
     }
     p.block0 = blocks;
     blocks += p.tiles * p.split;
@@ -1050,6 +1080,11 @@ hipError_t launch_tiled_set(const GemmDesc *d, int count, void *workspace, size_
       rblocks += (int)(((long long)d[i].M * d[i].N / 4 + kReduceThreads - 1) / kReduceThreads);
   }
   ts.count = count;
+  if (pset.count > 0) {
+    hipLaunchKernelGGL(prescale_f16_kernel, dim3(pblocks), dim3(256), 0, stream, pset);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const dim3 grid(blocks), threads(kWM * kWN * 64);
   if (dma && tm == 8)
     hipLaunchKernelGGL((tiled_dma_kernel<8, 4>), grid, dim3(256), 0, stream, ts);
