@@ -188,10 +188,10 @@ def test_split_counts_whole_rounds():
     """K splits of a grouped tiled call are chosen by whole rounds of resident
     workgroups (host-only, through the workspace size).  Qwen2-7B-shaped layer, fp16
     activations and INT4 codes, so the launches take the DMA-staged tiled kernel:
-    at M = 64 its 64 x 128 blocks (388 of them) with four workgroups per CU (1024
-    slots): 15-group ranges give 1000 workgroups in one round (down in 10 splits, the
-    six 28-group rows in 2).  At M = 256 its 128 x 256 blocks (388) with two per CU
-    (512 slots): 30-group ranges split only down (5 ways), 500 workgroups."""
+    at M = 64 its 64 x 128 blocks (388 of them) of two K slices, two workgroups per
+    CU (512 slots): 30-group ranges split only down (5 ways), 500 workgroups in one
+    round.  At M = 256 its 128 x 256 blocks with two per CU (512 slots): 30-group
+    ranges split only down (5 ways), 500 workgroups."""
     P = w4.Problem
     shapes = [(3584, 3584), (512, 3584), (512, 3584), (3584, 3584), (18944, 3584),
               (18944, 3584), (3584, 18944)]
@@ -199,10 +199,10 @@ def test_split_counts_whole_rounds():
     def layer(M):
         return [P(A16, A16, A16, A16, None, A16, M, N, K) for N, K in shapes]
 
-    splits64 = [2, 2, 2, 2, 2, 2, 10]
+    splits64 = [1, 1, 1, 1, 1, 1, 5]
     rc, nb = ws_size(*layer(64))
-    assert rc == 0 and nb == sum(s * 64 * N * 4 for s, (N, _) in zip(splits64, shapes))
-    assert sum(s * -(-N // 128) for s, (N, _) in zip(splits64, shapes)) == 1000
+    assert rc == 0 and nb == 5 * 64 * 3584 * 4
+    assert sum(s * -(-N // 128) for s, (N, _) in zip(splits64, shapes)) == 500
     splits256 = [1, 1, 1, 1, 1, 1, 5]
     rc, nb = ws_size(*layer(256))
     assert rc == 0 and nb == 5 * 256 * 3584 * 4

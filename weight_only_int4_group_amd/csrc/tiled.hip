@@ -619,25 +619,34 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
 //   * the wave's code tiles (16 bytes per lane per tile, its MFMA B operands)
 //     and their scales and zero points are loaded into registers one group
 //     ahead, in two register sets that alternate.
-// Blocks are BM x BN (BM = 16 TM, BN = 64 TN), four waves of BM x 16 TN; K is
-// split across workgroups the same way as in tiled_kernel.  Batched decode (M
-// up to 64) takes TN = 2: twice the blocks of TN = 4, so fewer K splits (whose
-// fp32 partials cost HBM traffic) are needed to fill the GPU, and half the
-// accumulators, so four workgroups fit on a CU.
-template <int TM, int TN>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TN == 2 ? 4 : 2, TN == 2 ? 4 : 2))) void tiled_dma_kernel(
+// Blocks are BM x BN (BM = 16 TM, BN = 64 TN), four waves of BM x 16 TN per
+// K slice; K is split across workgroups the same way as in tiled_kernel.
+// Batched decode (M up to 64) takes TN = 2: twice the blocks of TN = 4, so
+// fewer K splits (whose fp32 partials cost HBM traffic) are needed to fill the
+// GPU, and half the accumulators.  Its blocks have one K slice of four waves
+// or KS = 2: each slice walks every other group of the workgroup's K range
+// into its own X * s stages, and the two sums are added through LDS at the end
+// (slice 0's plus slice 1's, a fixed order).  Two slices double the waves per
+// block without fp32 partials in memory: the Qwen2-7B M = 64 layer then splits
+// only down across workgroups and took 52-56 us against 61, while layers with
+// more blocks than slots (70B at M = 64) keep one slice.  (KS = 2 at TM = 8
+// needs more than 256 VGPRs.)
+template <int TM, int TN, int KS>
+__global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(TN == 2 ? 4 : 2, TN == 2 ? 4 : 2))) void tiled_dma_kernel(
     TiledSet ts) {
   constexpr int WN = 4;
   constexpr int BM = TM * 16, BN = WN * TN * 16;
   constexpr int kRowChunks = kGroup / 8;            // 16-byte chunks per row per group
   constexpr int kDma = BM * kRowChunks / (4 * 64);  // DMA loads per wave per group
   static_assert(kDma * 4 * 64 == BM * kRowChunks, "a stage is whole DMA loads");
-  __shared__ __attribute__((aligned(16))) _Float16 As[2][BM * kGroup];
+  static_assert(KS == 1 || BM * BN * 4 <= KS * 2 * BM * kGroup * 2, "the slices' sums fit the X stages");
+  __shared__ __attribute__((aligned(16))) _Float16 As[KS][2][BM * kGroup];
 
   const int block = (int)blockIdx.x;
   const TiledProblem P = find_tiled<false>(ts, block);
   const int M = P.M, N = P.N, K = P.K;
-  const int tid = threadIdx.x, lane = tid & 63, wave = uniform_int(tid >> 6);
+  const int tid = threadIdx.x, lane = tid & 63, wv = uniform_int(tid >> 6);
+  const int ks = KS == 1 ? 0 : wv >> 2, wave = KS == 1 ? wv : wv & 3;  // K slice; the wave's column
   const int c = lane >> 4, r = lane & 15;
   // Workgroups go to the eight XCDs (each with its own L2) round robin,
   // workgroup i to XCD i mod 8.  A split launch is renumbered so that each XCD
@@ -655,6 +664,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TN == 2 ? 4
   const int n0 = (t - mt * P.tiles_n) * BN, m0 = mt * BM;
   const int G = K / kGroup, NB = N / kTileRows;
   const int gb = (int)((long long)G * sp / P.split), ge = (int)((long long)G * (sp + 1) / P.split);
+  // K slice ks of the workgroup takes groups gb + ks, gb + ks + KS, ...: every
+  // slice runs the same number of steps (and barriers); past ge a step loads
+  // the range's last group again and skips its MFMAs
+  const int nsteps = (ge - gb + KS - 1) / KS;
+  auto group_at = [&](int i) { return min(gb + ks + i * KS, ge - 1); };
 
   // X * s: wave load u fills LDS chunks p = (wave * kDma + u) * 64 + lane of a
   // stage; chunk p is row p / 16, physical chunk p % 16, holding logical chunk
@@ -678,7 +692,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TN == 2 ? 4
       // being instantiated in the host compilation)
       const int vo = xoff[u];
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          xrs, (__attribute__((address_space(3))) void *)(&As[buf][(wave * kDma + u) * 64 * 8]), 16,
+          xrs, (__attribute__((address_space(3))) void *)(&As[ks][buf][(wave * kDma + u) * 64 * 8]), 16,
           vo, g * kGroup * 2, 0, 0);
     }
   };
@@ -731,7 +745,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TN == 2 ? 4
       bias_hi[j] = bh;
       scale[j] = sc;
     }
-    const _Float16 *abuf = As[buf];
+    const _Float16 *abuf = As[ks][buf];
     // software pipeline: k step tt + 1's B operands are dequantized while k
     // step tt's MFMAs run, interleaved by the scheduler (one LDS read, four
     // MFMAs and about seven VALU ops at a time)
@@ -772,22 +786,58 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TN == 2 ? 4
   // while this group's MFMAs run.  Past the range they re-read the last group
   // (into a buffer and registers nobody reads).  Buffers and register sets
   // alternate with the loop unrolled by two, so nothing is copied.
-  auto step = [&](int g, BStage &cur, BStage &nxt, int buf) {
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-    const int gn = min(g + 1, ge - 1);
-    load_x(gn, buf ^ 1);
-    load_b(gn, nxt);
-    compute(cur, buf);
-  };
   BStage b0, b1;
-  load_x(gb, 0);
-  load_b(gb, b0);
-  for (int g = gb; g < ge; g += 2) {
-    step(g, b0, b1, 0);
-    if (g + 1 < ge) step(g + 1, b1, b0, 1);
+  if constexpr (KS == 1) {
+    auto step = [&](int g, BStage &cur, BStage &nxt, int buf) {
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+      const int gn = min(g + 1, ge - 1);
+      load_x(gn, buf ^ 1);
+      load_b(gn, nxt);
+      compute(cur, buf);
+    };
+    load_x(gb, 0);
+    load_b(gb, b0);
+    for (int g = gb; g < ge; g += 2) {
+      step(g, b0, b1, 0);
+      if (g + 1 < ge) step(g + 1, b1, b0, 1);
+    }
+  } else {
+    auto step = [&](int i, BStage &cur, BStage &nxt, int buf) {
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+      const int gn = group_at(min(i + 1, nsteps - 1));
+      load_x(gn, buf ^ 1);
+      load_b(gn, nxt);
+      if (gb + ks + i * KS < ge) compute(cur, buf);
+    };
+    load_x(group_at(0), 0);
+    load_b(group_at(0), b0);
+    for (int i = 0; i < nsteps; i += 2) {
+      step(i, b0, b1, 0);
+      if (i + 1 < nsteps) step(i + 1, b1, b0, 1);
+    }
   }
   // the last step's DMA must land before the workgroup's LDS is released
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (KS == 2) {
+    // slice 1 hands its sums to slice 0 through the X stages' LDS, and slice 0
+    // adds them to its own (a fixed order)
+    float *red = reinterpret_cast<float *>(&As[0][0][0]);
+    __syncthreads();  // every wave is done with the X stages
+    if (ks == 1) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          *reinterpret_cast<float4v *>(&red[((i * TN + j) * 4 + wave) * 256 + lane * 4]) = acc[i][j];
+    }
+    __syncthreads();
+    if (ks == 1) return;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] += *reinterpret_cast<const float4v *>(&red[((i * TN + j) * 4 + wave) * 256 + lane * 4]);
+  }
 
   // lane holds D[4c + v][r] of each 16x16 sub-block: the output, or this
   // split's fp32 partial
@@ -903,15 +953,17 @@ bool dma_capable(const GemmDesc &d) {
 constexpr int kDmaMinM = 17;
 
 // Geometry of the tiled_dma_kernel instances: TM = 8, TN = 4 (128 x 256
-// blocks, two workgroups per CU) when the launch's largest M exceeds 64, else
-// TM = 4, TN = 2 (64 x 128 blocks, four workgroups per CU).
+// blocks of four waves, two workgroups per CU) when the launch's largest M
+// exceeds 64, else TM = 4, TN = 2 (64 x 128 blocks) with one K slice (four
+// waves, four workgroups per CU) or two (eight waves, two per CU), whichever
+// the launch model below prefers.
 struct DmaShape {
   int tm, tn;
   int bm() const { return 16 * tm; }
   int bn() const { return 64 * tn; }
-  long long slots() const { return tn == 2 ? 1024 : 512; }
 };
 DmaShape dma_shape(int tm) { return tm == 8 ? DmaShape{8, 4} : DmaShape{4, 2}; }
+long long dma_slots(int tm, int ks) { return tm == 8 || ks == 2 ? 512 : 1024; }
 
 // 0 when the launch cannot take tiled_dma_kernel, else its TM: 8 (128-row
 // wave tiles) when the largest M exceeds 64, else 4
@@ -939,14 +991,32 @@ size_t part_bytes(const GemmDesc &d, int split) {
   return split > 1 ? ((size_t)split * d.M * d.N * sizeof(float) + 255) / 256 * 256 : 0;
 }
 
+// Modelled time of one launch with the given splits: ceil(workgroups /
+// slots) rounds, each as long as the longest range (in steps: a workgroup of
+// ks K slices takes ceil(range / ks) of them) plus a fixed cost, plus the
+// reduction of the partials.
+double launch_model(const GemmDesc *d, int count, const int *s, int bm, int bn, long long slots,
+                    int ks) {
+  long long blocks = 0;
+  int longest = 0;
+  double reduce_bytes = 0.0;
+  for (int i = 0; i < count; ++i) {
+    const int G = d[i].K / kGroup;
+    blocks += (long long)tiles_of(d[i], bm, bn) * s[i];
+    longest = std::max(longest, ((G + s[i] - 1) / s[i] + ks - 1) / ks);
+    if (s[i] > 1) reduce_bytes += (double)(4 * s[i] + 2) * d[i].M * d[i].N;
+  }
+  const long long rounds = (blocks + slots - 1) / slots;
+  return (double)rounds * (longest + kBlockStages) * kStageUs + reduce_bytes / kReduceBytesPerUs;
+}
+
 // K splits of each problem of one launch.  Every problem's groups are cut
 // into ranges of at most T groups; T is the one whose modelled launch time is
-// least: ceil(workgroups / slots) rounds, each as long as the longest range,
-// plus the reduction of the partials.  Counting whole rounds matters: a launch
-// a few workgroups past a multiple of the slots takes a whole extra round.
-// Ties keep the longer ranges (fewer partials).
-void choose_splits(const GemmDesc *d, int count, int *split, int bm = kBM, int bn = kBN,
-                   long long slots = kBlockSlots) {
+// least.  Counting whole rounds matters: a launch a few workgroups past a
+// multiple of the slots takes a whole extra round.  Ties keep the longer
+// ranges (fewer partials).  Returns the modelled time.
+double choose_splits(const GemmDesc *d, int count, int *split, int bm = kBM, int bn = kBN,
+                     long long slots = kBlockSlots, int ks = 1) {
   // Only range lengths ceil(G / n) for some problem's G and n <= kMaxSplit give
   // distinct split vectors; try those, longest first.
   int cand[kMaxTiled * kMaxSplit];
@@ -961,24 +1031,46 @@ void choose_splits(const GemmDesc *d, int count, int *split, int bm = kBM, int b
   for (int ci = 0; ci < nc; ++ci) {
     const int T = cand[ci];
     int s[kMaxTiled];
-    long long blocks = 0;
-    int longest = 0;
-    double reduce_bytes = 0.0;
     for (int i = 0; i < count; ++i) {
       const int G = d[i].K / kGroup;
       const int cap = std::min(std::min(kMaxSplit, G), (G + kMinSplitGroups - 1) / kMinSplitGroups);
       s[i] = std::max(1, std::min(cap, (G + T - 1) / T));
-      blocks += (long long)tiles_of(d[i], bm, bn) * s[i];
-      longest = std::max(longest, (G + s[i] - 1) / s[i]);
-      if (s[i] > 1) reduce_bytes += (double)(4 * s[i] + 2) * d[i].M * d[i].N;
     }
-    const long long rounds = (blocks + slots - 1) / slots;
-    const double t = (double)rounds * (longest + kBlockStages) * kStageUs + reduce_bytes / kReduceBytesPerUs;
+    const double t = launch_model(d, count, s, bm, bn, slots, ks);
     if (ci == 0 || t < best) {
       best = t;
       for (int i = 0; i < count; ++i) split[i] = s[i];
     }
   }
+  return best;
+}
+
+// The DMA kernel's plan for a launch of TM = tm: splits per problem (all 1
+// when `unsplit`: no room for partials) and K slices per block; returns the
+// slices.  With TM = 4 both slice counts are modelled and the faster kept
+// (ties: two slices, no more partials than one).
+int dma_plan(const GemmDesc *d, int count, int tm, bool unsplit, int *split) {
+  const DmaShape ds = dma_shape(tm);
+  const int kss[2] = {2, 1};
+  int best_ks = 1;
+  double best = 0.0;
+  for (int v = 0; v < (tm == 8 ? 1 : 2); ++v) {
+    const int ks = tm == 8 ? 1 : kss[v];
+    int s[kMaxTiled];
+    double t;
+    if (unsplit) {
+      for (int i = 0; i < count; ++i) s[i] = 1;
+      t = launch_model(d, count, s, ds.bm(), ds.bn(), dma_slots(tm, ks), ks);
+    } else {
+      t = choose_splits(d, count, s, ds.bm(), ds.bn(), dma_slots(tm, ks), ks);
+    }
+    if (v == 0 || t < best) {
+      best = t;
+      best_ks = ks;
+      for (int i = 0; i < count; ++i) split[i] = s[i];
+    }
+  }
+  return best_ks;
 }
 
 }  // namespace
@@ -989,7 +1081,7 @@ size_t tiled_workspace_bytes(const GemmDesc *d, int count) {
   const bool dma = tm != 0;
   int split[kMaxTiled];
   if (dma)
-    choose_splits(d, count, split, dma_shape(tm).bm(), dma_shape(tm).bn(), dma_shape(tm).slots());
+    dma_plan(d, count, tm, false, split);
   else
     choose_splits(d, count, split);
   size_t bytes = dma ? prescale_need(d, count) : 0;
@@ -1012,14 +1104,17 @@ hipError_t launch_tiled_set(const GemmDesc *d, int count, void *workspace, size_
   const DmaShape ds = dma_shape(tm);
   const int bm = dma ? ds.bm() : kBM, bn = dma ? ds.bn() : kBN;
   int split[kMaxTiled];
+  int ks = 1;
   if (dma)
-    choose_splits(d, count, split, bm, bn, ds.slots());
+    ks = dma_plan(d, count, tm, false, split);
   else
     choose_splits(d, count, split);
   size_t parts = 0;
   for (int i = 0; i < count; ++i) parts += part_bytes(d[i], split[i]);
-  if ((dma ? pre : 0) + parts > have)
-    for (int i = 0; i < count; ++i) split[i] = 1;  // no room for partials: one K range
+  if ((dma ? pre : 0) + parts > have) {  // no room for partials: one K range
+    for (int i = 0; i < count; ++i) split[i] = 1;
+    if (dma) ks = dma_plan(d, count, tm, true, split);
+  }
   TiledSet ts = {};
   int blocks = 0, rblocks = 0;
   size_t off = 0;
@@ -1087,9 +1182,11 @@ hipError_t launch_tiled_set(const GemmDesc *d, int count, void *workspace, size_
   }
   const dim3 grid(blocks), threads(kWM * kWN * 64);
   if (dma && tm == 8)
-    hipLaunchKernelGGL((tiled_dma_kernel<8, 4>), grid, dim3(256), 0, stream, ts);
+    hipLaunchKernelGGL((tiled_dma_kernel<8, 4, 1>), grid, dim3(256), 0, stream, ts);
+  else if (dma && ks == 2)
+    hipLaunchKernelGGL((tiled_dma_kernel<4, 2, 2>), grid, dim3(512), 0, stream, ts);
   else if (dma)
-    hipLaunchKernelGGL((tiled_dma_kernel<4, 2>), grid, dim3(256), 0, stream, ts);
+    hipLaunchKernelGGL((tiled_dma_kernel<4, 2, 1>), grid, dim3(256), 0, stream, ts);
   else if (d[0].w8 && d[0].bf16 && out)  // INT8 codes
     hipLaunchKernelGGL((tiled_kernel<kWM, kWN, kTM, kTN, true, true, true>), grid, threads, 0,
                        stream, ts);
