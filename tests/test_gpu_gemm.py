@@ -343,3 +343,24 @@ def test_dma_shared_activation_prescale(M):
     for (pw, sv, svd, ref, N), it in zip(cases, items):
         assert_close(to_host(it[3]), oracle.gemm(X, ref.q, ref.scales, ref.zeros, sv),
                      f"shared X*s M={M} N={N}")
+
+
+def test_dma_one_slice_blocks_at_small_m():
+    """At M <= 64 a launch with more 64 x 128 blocks than two-slice slots takes blocks of
+    one K slice (the launch model prefers four-wave blocks, four per CU, there): a
+    131072 x 256 matrix at M = 40 has 1024 blocks.  Whole-matrix packing on the GPU; the
+    oracle checks 3 sampled 16-row blocks (first, last, one inside) of the output."""
+    torch_cuda()
+    N, K, M = 131072, 256, 40
+    W = weights(23, 0, N, K)
+    s = awq_scales(23, 0, K)
+    X = activations(23, 0, M, K)
+    pw = w4.w4a16_quantize_pack(to_dev(W), to_dev(s))
+    note(f"dma one-slice M={M} N={N} K={K}")
+    Y = to_host(w4.w4a16_gemm(to_dev(X), pw, to_dev(s)))
+    assert np.isfinite(Y.astype(np.float32)).all()
+    for b in (0, N // 16 // 2 + 3, N // 16 - 1):
+        rows = slice(16 * b, 16 * b + 16)
+        ref = oracle.quantize(W[rows], s)
+        assert_close(Y[:, rows], oracle.gemm(X, ref.q, ref.scales, ref.zeros, s),
+                     f"one-slice block {b}")

@@ -53,14 +53,8 @@ constexpr int kMaxProblems = 8;
 // each cache line is touched by two instructions, and with NT the INT8 decode
 // layer measured 19% slower.  Metadata loads, shared by four lanes each, keep
 // the default too (NT measured no better).
-#ifndef W4A16_CODE_CPOL
-#define W4A16_CODE_CPOL 2
-#endif
-#ifndef W4A16_META_CPOL
-#define W4A16_META_CPOL 0
-#endif
-constexpr int kCodeCachePolicy = W4A16_CODE_CPOL;
-constexpr int kMetaCachePolicy = W4A16_META_CPOL;
+constexpr int kCodeCachePolicy = 2;  // NT
+constexpr int kMetaCachePolicy = 0;
 constexpr int kLdsPad = 8;         // halves of padding per staged X row
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer resource, 32-bit data format
 
@@ -853,39 +847,19 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_hybrid_kernel(ProblemSet p
 }
 
 constexpr size_t kMaxStageBytes = 96 * 1024;
-#ifndef W4A16_SKINNY_CHUNK
-#define W4A16_SKINNY_CHUNK 4
-#endif
-constexpr int kChunk = W4A16_SKINNY_CHUNK;  // groups per chunk (weight loads in flight per wave)
-#ifndef W4A16_SKINNY_WAVES
-#define W4A16_SKINNY_WAVES 8
-#endif
-#ifndef W4A16_SKINNY_DEPTH
-#define W4A16_SKINNY_DEPTH 1
-#endif
-constexpr int kWaves = W4A16_SKINNY_WAVES;  // waves per workgroup
-constexpr int kDepth = W4A16_SKINNY_DEPTH;  // chunks in flight per wave
-#ifndef W4A16_SKINNY_WINDOW
-#define W4A16_SKINNY_WINDOW 3
-#endif
+constexpr int kChunk = 4;  // groups per chunk (weight loads in flight per wave)
+constexpr int kWaves = 8;  // waves per workgroup
+constexpr int kDepth = 1;  // chunks in flight per wave
 // 1: window the problems whose X * s does not fit, 2: always window, 3:
-// window the whole call when one problem does not fit
-constexpr int kWindowMode = W4A16_SKINNY_WINDOW;
-#ifndef W4A16_SKINNY_HYBRID
-#define W4A16_SKINNY_HYBRID 1
-#endif
+// window the whole call when one problem does not fit (measured best; 1 and 2
+// are kept as the documented alternatives)
+constexpr int kWindowMode = 3;
 // fp16 INT4 calls with problems of both kinds: one launch in which each
 // problem stages its X * s the way it fits (skinny_hybrid_kernel)
-constexpr bool kHybridLaunch = W4A16_SKINNY_HYBRID != 0;
+constexpr bool kHybridLaunch = true;
 static_assert(kWindowMode >= 1 && kWindowMode <= 3, "X * s must fit in LDS or go in windows");
-#ifndef W4A16_SKINNY_WINDOW_KB
-#define W4A16_SKINNY_WINDOW_KB 72
-#endif
-#ifndef W4A16_SKINNY_WINDOW_SLOTS
-#define W4A16_SKINNY_WINDOW_SLOTS 8
-#endif
-constexpr size_t kMaxWindowBytes = W4A16_SKINNY_WINDOW_KB * 1024;  // 72 KB: two workgroups per CU
-constexpr int kWindowSlots = W4A16_SKINNY_WINDOW_SLOTS;  // staged 8-column pieces per thread
+constexpr size_t kMaxWindowBytes = 72 * 1024;  // two workgroups per CU
+constexpr int kWindowSlots = 8;  // staged 8-column pieces per thread
 // bf16 and INT8 codes: fewer pieces cut the registers (the prescaled bf16
 // instance needs 110 instead of 146: two 8-wave workgroups per CU instead of
 // one); the bf16 instance that scales X itself uses the same count, so both

@@ -915,16 +915,13 @@ __global__ __launch_bounds__(kReduceThreads) void split_reduce_kernel(TiledSet t
   }
 }
 
-#ifndef W4A16_TILED_SHAPE
-#define W4A16_TILED_SHAPE 1, 4, 4, 4
-#endif
 // 64 x 256 blocks of 4 waves (64 x 64 each), two workgroups per CU: the
 // fastest of the measured shapes at every M of the workloads.
 template <int WM_, int WN_, int TM_, int TN_>
 struct Shape {
   static constexpr int WM = WM_, WN = WN_, TM = TM_, TN = TN_;
 };
-using TileShape = Shape<W4A16_TILED_SHAPE>;
+using TileShape = Shape<1, 4, 4, 4>;
 constexpr int kWM = TileShape::WM, kWN = TileShape::WN, kTM = TileShape::TM, kTN = TileShape::TN;
 constexpr int kBM = kWM * kTM * 16, kBN = kWN * kTN * 16;
 // CUs x resident workgroups per CU (two waves per SIMD, four SIMDs)
