@@ -555,7 +555,8 @@ def cpu_baseline(cfg, M, workloads, budget_s=10.0, item_s=1.0):
       * per_config: for each of the five configurations, oracle.quantize + pack over
         that config's row sample (MB of fp16 weights per s), and for each of its M,
         oracle.gemm over the same sample (TB/s of algorithmic bytes, and TFLOP/s),
-        each repeated for about `item_s`."""
+        each repeated for about `item_s`;
+      * gemv_1024_one_thread_ms: oracle.gemm on config 1 with one BLAS thread."""
     import oracle
     from threadpoolctl import threadpool_info, threadpool_limits
     cores = len(os.sched_getaffinity(0))
@@ -623,10 +624,22 @@ def cpu_baseline(cfg, M, workloads, budget_s=10.0, item_s=1.0):
                                       "TFLOP/s": float(f"{fps / 1e12:.4g}"), "reps": reps})
             per.append(entry)
         out["per_config"] = per
-        out["per_config_note"] = (
-            f"each config: its matrices' first sample_rows rows; quantize_pack = oracle.quantize "
-            f"+ pack_codes + pack_meta (scales, zeros); gemm = oracle.gemm at each M, about "
-            f"{item_s:g} s each")
+    # config 1 once more with one BLAS thread (the oracle's quantize and pack are
+    # single-threaded NumPy anyway)
+    g1 = workloads.config_by_name("gemv_1024")
+    W1 = workloads.weights(g1.weight_key, 0, 1024, 1024)
+    X1 = workloads.activations(g1.weight_key, 0, 1, 1024)
+    r1 = oracle.quantize(W1, None)
+    with threadpool_limits(limits=1, user_api="blas"):
+        t0, n1 = time.perf_counter(), 0
+        while time.perf_counter() - t0 < item_s:
+            oracle.gemm(X1, r1.q, r1.scales, r1.zeros, None)
+            n1 += 1
+        out["gemv_1024_one_thread_ms"] = round((time.perf_counter() - t0) / n1 * 1e3, 3)
+    out["per_config_note"] = (
+        f"each config: its matrices' first sample_rows rows; quantize_pack = oracle.quantize "
+        f"+ pack_codes + pack_meta (scales, zeros); gemm = oracle.gemm at each M, about "
+        f"{item_s:g} s each")
     return out
 
 
