@@ -364,3 +364,21 @@ def test_dma_one_slice_blocks_at_small_m():
         ref = oracle.quantize(W[rows], s)
         assert_close(Y[:, rows], oracle.gemm(X, ref.q, ref.scales, ref.zeros, s),
                      f"one-slice block {b}")
+
+
+def test_activations_past_the_dma_buffer_range():
+    """M * K * 2 >= 2^31 bytes of X: the DMA-staged kernel's buffer resource cannot
+    cover X, so the call takes the register-staged tiled kernel (64-bit row offsets).
+    M = 65600, K = 16384 (2.15 GB of X), N = 272 (not a multiple of the block width),
+    AWQ s; the oracle checks sampled rows of Y, first and last included."""
+    torch_cuda()
+    M, N, K = 65600, 272, 16384
+    assert M * K * 2 >= 1 << 31
+    pw, s, ref = packed_case(N, K, True, key=24, mat=0)
+    X = activations(24, 1, M, K)
+    note(f"large X M={M} N={N} K={K}")
+    Y = to_host(w4.w4a16_gemm(to_dev(X), pw, to_dev(s)))
+    rng = np.random.default_rng(24)
+    rows = np.unique(np.concatenate([[0, 1, M - 1], rng.choice(M, 40, replace=False)]))
+    assert_close(Y[rows], oracle.gemm(X[rows], ref.q, ref.scales, ref.zeros, s), "large X rows")
+    assert np.isfinite(Y.astype(np.float32)).all()
