@@ -255,12 +255,24 @@ def batched_line(cfg, M, mats, pool, copies, w4, torch, workloads, steps=200, wa
     kern = float(np.mean(lms[0])) * 1e-3
     path = "streaming" if w4.w4a16_select_path(M, mats[0]["N"], mats[0]["K"]) == w4.PATH_SKINNY \
         else "tiled"
-    return {"workload": cfg.name, "M": M, "kernel": path,
+    line = {"workload": cfg.name, "M": M, "kernel": path,
             "launches_per_step": 1 + int(split), "split_k": split,
             "us_per_step": round(wall / steps * 1e6, 2), "kernel_us_per_step": round(kern * 1e6, 2),
             "TB/s": round(byts / (wall / steps) / 1e12, 4),
             "kernel_TB/s": round(byts / kern / 1e12, 4),
             "TFLOP/s": round(fl / (wall / steps) / 1e12, 2)}
+    if split:
+        # the same layer through w4a16_gemm_grouped, the entry point without a workspace
+        # argument (the library's shared scratch takes the split-K partials)
+        st = torch.cuda.current_stream().cuda_stream
+        ncalls = [[w4.GroupedCall([(m["X"], pool[j][c], m["s"], m["Y"]) for j, m in enumerate(bm)],
+                                  stream=st, workspace=False)] for c in range(copies)]
+        _, nms = timed(ncalls, steps, warmup, torch)
+        nk = float(np.mean(nms[0])) * 1e-3
+        line["no_workspace_arg"] = {"entry": "w4a16_gemm_grouped (library's shared scratch)",
+                                    "kernel_us_per_step": round(nk * 1e6, 2),
+                                    "vs_workspace_call": round(nk / kern, 4)}
+    return line
 
 
 SWEEP_MS = (17, 24, 32, 48, 64, 96, 128, 256)

@@ -205,11 +205,30 @@ int w4a16_quantize_pack_gptq(const void *W, const void *s, int64_t N, int64_t K,
 /* Y[M][N] = X[M][K] . W_hat^T with W_hat[n][k] = (q - z) * scale * s[k].
  * X: fp16 [M][K]; Wq/scales/zeros: packed as above; s: fp16 [K] or NULL;
  * Y: fp16 [M][N] row-major, fully overwritten.  fp32 accumulation; X * s is
- * rounded to fp16 once.  Asynchronous on `stream`.  M >= 1. */
+ * rounded to fp16 once.  Asynchronous on `stream`.  M >= 0 (0: nothing).
+ * The same operation and bits as w4a16_gemm_grouped_ws on this one problem
+ * with its queried workspace, which this call takes from the library's
+ * shared scratch (below) when it fits; otherwise (or under stream capture)
+ * K is not split across workgroups and the bits are those of
+ * w4a16_gemm_path(..., W4A16_PATH_AUTO, ...). */
 int w4a16_gemm(const void *X, const void *Wq, const void *scales, const void *zeros,
                const void *s, void *Y, int64_t M, int64_t N, int64_t K, void *stream);
 
-/* Same as w4a16_gemm with an explicit kernel path (tests and benchmarks). */
+/* The shared scratch of the entry points without a workspace argument
+ * (w4a16_gemm, w4a16_gemm_grouped): W4A16_SHARED_SCRATCH_BYTES of device
+ * memory inside the library on each GPU it runs on (held from the first such
+ * call there until the process ends), for split-K partial sums and prescaled
+ * activations of calls that need at most that much workspace (batched
+ * decode; a 70B prefill matrix with an AWQ s needs more and runs without).
+ * Such calls on one GPU are ordered through an event the library keeps per
+ * GPU: each waits on its stream for the previous one's work, whatever stream
+ * that ran on, so they never race; their work does not overlap in time.  A
+ * call on a stream that is being captured does not use the scratch. */
+#define W4A16_SHARED_SCRATCH_BYTES ((size_t)32 << 20)
+
+/* Same as w4a16_gemm with an explicit kernel path (tests and benchmarks); it
+ * never uses a workspace, so large-M problems are not split across
+ * workgroups. */
 int w4a16_gemm_path(const void *X, const void *Wq, const void *scales, const void *zeros,
                     const void *s, void *Y, int64_t M, int64_t N, int64_t K, int path,
                     void *stream);
@@ -250,7 +269,8 @@ typedef struct w4a16_problem {
 enum { W4A16_DTYPE_F16 = 0, W4A16_DTYPE_BF16 = 1 };
 
 /* Several independent dequantize-matmuls, each the operation w4a16_gemm
- * computes, in as few launches as possible: problems that the M-dispatch
+ * computes, in as few launches as possible (with the shared scratch, above,
+ * as the workspace of w4a16_gemm_grouped_ws when it fits, else none): problems that the M-dispatch
  * sends to the streaming kernel (small M) share one launch, up to 8 problems
  * per launch, so a layer's small projections ride along with its large ones;
  * the others get a launch each.  How a shared launch splits K across waves,

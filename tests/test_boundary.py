@@ -390,3 +390,26 @@ def test_bf16_bit_helpers_match_torch():
     assert np.array_equal(to_bf16_bits(x), want)
     assert np.array_equal(bf16_bits_to_f64(want),
                           torch.from_numpy(want.view(np.int16)).view(torch.bfloat16).double().numpy())
+
+
+def test_scratch_sizes_match_header():
+    """The binding's copies of the header's scratch sizes."""
+    import os
+    import re
+    hdr = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                            "include", "w4a16.h")).read()
+    for name, val in (("W4A16_STATIC_SCRATCH_BYTES", w4.STATIC_SCRATCH_BYTES),
+                      ("W4A16_SHARED_SCRATCH_BYTES", w4.SHARED_SCRATCH_BYTES)):
+        m = re.search(r"#define " + name + r" \(\(size_t\)(\d+) << (\d+)\)", hdr)
+        assert m and int(m.group(1)) << int(m.group(2)) == val
+
+
+def test_gemm_without_workspace_validates_first():
+    """w4a16_gemm and w4a16_gemm_grouped take the shared scratch only after the same
+    host-side validation: bad arguments return before any HIP call (no GPU here)."""
+    L = w4.lib()
+    assert L.w4a16_gemm(A16, A16, A16, A16, None, A16, 64, 272, 100, None) == -1   # K % 128
+    assert L.w4a16_gemm(ODD, A16, A16, A16, None, A16, 64, 272, 128, None) == -2   # alignment
+    assert L.w4a16_gemm(A16, A16, A16, A16, None, A16, 0, 272, 128, None) == 0     # empty batch
+    bad = (w4.Problem * 1)(w4.Problem(A16, A16, A16, A16, None, A16, 64, 270, 128))
+    assert L.w4a16_gemm_grouped(bad, 1, None) == -1

@@ -33,6 +33,7 @@ __all__ = [
     "w4a16_spec_verify_workspace_size", "SpecVerifyCall", "w4a16_quantize_pack_outliers",
     "w4a16_outlier_workspace_size", "page_outlier_count", "DTYPE_F16", "DTYPE_BF16",
     "w4a16_quantize_pack_gptq", "w4a16_gemm_grouped_static", "STATIC_SCRATCH_BYTES",
+    "SHARED_SCRATCH_BYTES",
 ]
 
 GROUP = 128
@@ -42,6 +43,7 @@ DTYPE_F16, DTYPE_BF16 = 0, 1
 STATUS = {0: "W4A16_OK", -1: "W4A16_EINVAL", -2: "W4A16_EALIGN", -3: "W4A16_EUNSUPPORTED",
           -4: "W4A16_ENONFINITE", -5: "W4A16_ERANGE", -6: "W4A16_EHIP", -7: "W4A16_ESCRATCH"}
 STATIC_SCRATCH_BYTES = 64 << 20   # W4A16_STATIC_SCRATCH_BYTES
+SHARED_SCRATCH_BYTES = 32 << 20   # W4A16_SHARED_SCRATCH_BYTES
 EXPORTED_SYMBOLS = ("w4a16_packed_sizes", "w4a16_packed_sizes_mode", "w4a16_quantize_pack",
                     "w4a16_quantize_pack_mode",
                     "w4a16_gemm",
@@ -341,7 +343,9 @@ class GroupedCall:
     PackedWeight, s or None, Y).  Calls of one object must not overlap in time on
     different streams, since they share the workspace.  With ``static=True`` the call
     goes to w4a16_gemm_grouped_static instead: no workspace is allocated here, the
-    library's own static scratch serves (all such calls on a GPU share it)."""
+    library's own static scratch serves (all such calls on a GPU share it).  With
+    ``workspace=False`` it goes to w4a16_gemm_grouped, which takes no workspace
+    argument (the library's event-ordered shared scratch serves when it fits)."""
 
     def __init__(self, items, stream=None, workspace=True, static=False):
         torch = _torch()
@@ -365,6 +369,7 @@ class GroupedCall:
         self.device = self.items[0][0].device if self.items else None
         self.ws, self.ws_ptr, self.ws_bytes = None, None, 0
         self.static = static
+        self.use_ws = workspace
         if workspace and self.items and not static:
             nb = ctypes.c_size_t()
             rc = lib().w4a16_gemm_workspace_size(self.array, len(self.items), ctypes.byref(nb))
@@ -382,6 +387,11 @@ class GroupedCall:
             rc = lib().w4a16_gemm_grouped_static(self.array, len(self.items), st)
             if rc:
                 raise W4A16Error(rc, "w4a16_gemm_grouped_static")
+            return
+        if not self.use_ws:
+            rc = lib().w4a16_gemm_grouped(self.array, len(self.items), st)
+            if rc:
+                raise W4A16Error(rc, "w4a16_gemm_grouped")
             return
         rc = lib().w4a16_gemm_grouped_ws(self.array, len(self.items), self.ws_ptr,
                                          self.ws_bytes, st)

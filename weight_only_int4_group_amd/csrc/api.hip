@@ -425,8 +425,65 @@ int w4a16_gemm_grouped_ws(const w4a16_problem *problems, int count, void *worksp
                                                                                    : W4A16_EHIP;
 }
 
+}  // extern "C"
+
+namespace {
+
+// The scratch of the entry points that take no workspace (w4a16_gemm,
+// w4a16_gemm_grouped): W4A16_SHARED_SCRATCH_BYTES of device memory in this
+// library's code object, one copy per GPU, held until the process ends, with
+// one event per GPU that marks the end of the last call's work in it.  A call
+// whose workspace fits makes its stream wait for that event, launches with
+// the scratch as its workspace and records the event again, under one mutex:
+// the work of such calls runs one after the other on the GPU, whatever their
+// streams, so they never race.  The device address comes from
+// hipGetSymbolAddress (the name is a host-side stand-in in host code).
+static __device__ __align__(256) unsigned char shared_scratch[W4A16_SHARED_SCRATCH_BYTES];
+
+struct SharedScratch {
+  void *ptr = nullptr;
+  hipEvent_t done = nullptr;
+};
+std::mutex g_shared_mu;
+std::vector<SharedScratch> g_shared;  // per device
+
+int grouped_shared(const w4a16_problem *problems, int count, void *stream) {
+  size_t need = 0;
+  const int rc = w4a16_gemm_workspace_size(problems, count, &need);  // validates too
+  if (rc) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  // under capture the event could not order work outside the graph: no split
+  if (need == 0 || need > W4A16_SHARED_SCRATCH_BYTES ||
+      hipStreamIsCapturing(st, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone)
+    return w4a16_gemm_grouped_ws(problems, count, nullptr, 0, stream);
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return W4A16_EHIP;
+  std::lock_guard<std::mutex> lock(g_shared_mu);
+  if ((int)g_shared.size() <= dev) g_shared.resize(dev + 1);
+  SharedScratch &sh = g_shared[dev];
+  if (!sh.ptr) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(shared_scratch)) != hipSuccess || !ptr)
+      return W4A16_EHIP;
+    hipEvent_t ev = nullptr;
+    if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess) return W4A16_EHIP;
+    sh.ptr = ptr;
+    sh.done = ev;
+  }
+  if (hipStreamWaitEvent(st, sh.done, 0) != hipSuccess) return W4A16_EHIP;
+  const int r = w4a16_gemm_grouped_ws(problems, count, sh.ptr, need, stream);
+  // recorded whatever the outcome: later calls must wait for any launched work
+  const bool recorded = hipEventRecord(sh.done, st) == hipSuccess;
+  return r ? r : (recorded ? W4A16_OK : W4A16_EHIP);
+}
+
+}  // namespace
+
+extern "C" {
+
 int w4a16_gemm_grouped(const w4a16_problem *problems, int count, void *stream) {
-  return w4a16_gemm_grouped_ws(problems, count, nullptr, 0, stream);
+  return grouped_shared(problems, count, stream);
 }
 
 }  // extern "C"
@@ -516,7 +573,19 @@ int w4a16_spec_verify(const void *p_target, const void *p_draft, const void *dra
 
 int w4a16_gemm(const void *X, const void *Wq, const void *scales, const void *zeros,
                const void *s, void *Y, int64_t M, int64_t N, int64_t K, void *stream) {
-  return w4a16_gemm_path(X, Wq, scales, zeros, s, Y, M, N, K, W4A16_PATH_AUTO, stream);
+  const int rc = check_gemm(X, Wq, scales, zeros, s, Y, M, N, K);
+  if (rc || M == 0) return rc;
+  w4a16_problem p = {};
+  p.X = X;
+  p.Wq = Wq;
+  p.scales = scales;
+  p.zeros = zeros;
+  p.s = s;
+  p.Y = Y;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  return grouped_shared(&p, 1, stream);
 }
 
 }  // extern "C"
