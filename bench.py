@@ -187,22 +187,38 @@ def prepare_layer(cfg, M, torch, w4, workloads, copies_min_bytes=POOL_BYTES, out
 
 def make_calls(mats, pool, copies, groups, w4, torch):
     """For every layer copy, one prepared grouped call per group of matrix indices,
-    bound to torch's current stream."""
+    bound to torch's current stream.  The copies of a group share one workspace (the
+    calls run one after the other on that stream), as a serving loop would reuse it."""
     st = torch.cuda.current_stream().cuda_stream
-    return [[w4.GroupedCall([(mats[j]["X"], pool[j][c], mats[j]["s"], mats[j]["Y"])
-                             for j in grp], stream=st) for grp in groups] for c in range(copies)]
+    first = [w4.GroupedCall([(mats[j]["X"], pool[j][0], mats[j]["s"], mats[j]["Y"]) for j in grp],
+                            stream=st) for grp in groups]
+    return [first] + [[w4.GroupedCall([(mats[j]["X"], pool[j][c], mats[j]["s"], mats[j]["Y"])
+                                       for j in grp], stream=st,
+                                      workspace=f.ws if f.ws is not None else True)
+                       for grp, f in zip(groups, first)] for c in range(1, copies)]
 
 
-def timed(calls, steps, warmup, torch, per=10):
-    """Warm up, then run exactly `steps` steps (step i uses copy i % copies).  HIP events
-    on the launch stream bracket every block of up to `per` consecutive launches of each
-    kind.  Returns (wall seconds, per-launch ms [launch kind][block]) where a block's
-    per-launch ms is its duration divided by its number of launches."""
+def timed(calls, steps, warmup, torch, per=10, min_warm_s=0.2):
+    """Warm up (`warmup` steps, and on until the GPU has run them for at least
+    `min_warm_s` seconds: after the host-side preparation of a workload the clocks
+    need that long to settle), then run exactly `steps` steps (step i uses copy
+    i % copies).  HIP events on the launch stream bracket every block of up to `per`
+    consecutive launches of each kind.  Returns (wall seconds, per-launch ms [launch
+    kind][block]) where a block's per-launch ms is its duration divided by its number
+    of launches."""
     stream = torch.cuda.current_stream()
     nl = len(calls[0])
-    for i in range(warmup):
-        for u in calls[i % len(calls)]:
+    t_w = time.perf_counter()
+    done = 0
+    while True:
+        if done >= warmup and done % 64 == 0:
+            torch.cuda.synchronize()
+            if time.perf_counter() - t_w >= min_warm_s:
+                break
+        for u in calls[done % len(calls)]:
             u()
+        done += 1
+    warmup = done
     blocks = [(b0, min(per, steps - b0)) for b0 in range(0, steps, per)]
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(nl)] for _ in blocks]
@@ -659,7 +675,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=4000,
+                    help="untimed steps before the timed ones (4000 decode steps: about 0.1 s, "
+                         "enough for the clocks to settle)")
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
@@ -716,7 +734,7 @@ def main():
     log(f"{copies} layer copies, {layer_w * copies / 2**30:.2f} GiB of packed weights; "
         f"timing {args.steps} steps")
     wall, lms = timed(make_calls(mats, pool, copies, one, w4, torch), args.steps, args.warmup,
-                      torch)
+                      torch, min_warm_s=0)
     ms_per_step = wall / args.steps * 1e3
     avg_ms = float(np.mean(lms[0]))
     achieved = step_bytes / (avg_ms * 1e-3) / 1e9

@@ -345,7 +345,9 @@ class GroupedCall:
     goes to w4a16_gemm_grouped_static instead: no workspace is allocated here, the
     library's own static scratch serves (all such calls on a GPU share it).  With
     ``workspace=False`` it goes to w4a16_gemm_grouped, which takes no workspace
-    argument (the library's event-ordered shared scratch serves when it fits)."""
+    argument (the library's event-ordered shared scratch serves when it fits).  A
+    uint8 device tensor as ``workspace`` is used instead of a new one (calls that
+    share it must not overlap in time)."""
 
     def __init__(self, items, stream=None, workspace=True, static=False):
         torch = _torch()
@@ -369,14 +371,21 @@ class GroupedCall:
         self.device = self.items[0][0].device if self.items else None
         self.ws, self.ws_ptr, self.ws_bytes = None, None, 0
         self.static = static
-        self.use_ws = workspace
-        if workspace and self.items and not static:
+        self.use_ws = workspace is not False
+        if self.use_ws and self.items and not static:
             nb = ctypes.c_size_t()
             rc = lib().w4a16_gemm_workspace_size(self.array, len(self.items), ctypes.byref(nb))
             if rc:
                 raise W4A16Error(rc, "w4a16_gemm_workspace_size")
             if nb.value:
-                self.ws = torch.empty(nb.value, dtype=torch.uint8, device=self.device)
+                if isinstance(workspace, torch.Tensor):  # a caller's buffer, shared by calls
+                    if (not workspace.is_cuda or workspace.dtype != torch.uint8
+                            or not workspace.is_contiguous() or workspace.numel() < nb.value):
+                        raise ValueError(f"workspace must be a contiguous uint8 device tensor "
+                                         f"of at least {nb.value} bytes")
+                    self.ws = workspace
+                else:
+                    self.ws = torch.empty(nb.value, dtype=torch.uint8, device=self.device)
                 self.ws_ptr, self.ws_bytes = self.ws.data_ptr(), nb.value
 
     def __call__(self):
