@@ -73,6 +73,9 @@ struct Problem {
   uint16_t *xpre;
   float *gpre;
   int window;  // hybrid launches: this problem walks K in windows
+  // windowed: halves from the first window buffer to the second (0: a single
+  // buffer, restaged between two barriers)
+  int wpair;
 };
 
 struct ProblemSet {
@@ -229,6 +232,8 @@ __device__ __forceinline__ Problem find_problem(const ProblemSet &ps) {
   P.oval = uniform_ptr(ps.p[pi].oval);
   P.xpre = uniform_ptr(ps.p[pi].xpre);
   P.gpre = uniform_ptr(ps.p[pi].gpre);
+  P.window = uniform_int(ps.p[pi].window);
+  P.wpair = uniform_int(ps.p[pi].wpair);
   return P;
 }
 
@@ -586,7 +591,8 @@ __global__ __launch_bounds__(256) void prescale_kernel(ProblemSet ps) {
 
 // Windowed variant: X * s staged one window of S chunks at a time (see the
 // header).  kSlots bounds the 8-column pieces of a window each thread stages.
-// xs (dynamic LDS) holds the window, then (after the last window) the split-K
+// xs (dynamic LDS) holds the window (two windows, alternating, when the
+// launch has room for both), then (after the last window) the split-K
 // reduction.
 template <int kGW, int kWaves, int kDepth, int kSlots, bool kOut, bool kBF, bool kW8 = false,
           bool kPre = false>
@@ -696,16 +702,20 @@ __device__ __forceinline__ void skinny_window_body(const ProblemSet &ps, _Float1
   // bf16: each window group's sum of X * s per row, wsum[m][window group],
   // after the window's rows (a 16-lane segment stages one group of one row)
   const int wgroups = S * kGW;
-  float *wsum = reinterpret_cast<float *>(xs + M * ldx);
-  auto store_window = [&]() {
+  // Window j is in buffer j % 2 when the launch has room for two (wpair > 0):
+  // a window is staged while the one before is read, one barrier per window.
+  // With one buffer, restaging waits for every wave to be done with it.
+  const int wpair = uniform_int(P.wpair);
+  auto store_window = [&](_Float16 *wx) {
+    float *wsum = reinterpret_cast<float *>(wx + M * ldx);
 #pragma unroll
     for (int i = 0; i < kSlots; ++i) {
       const int m = r0 + i * rstep;
       if (!kBF) {
-        if (m < M) *reinterpret_cast<half8 *>(&xs[m * ldx + cs * 8]) = xr[i] * sv;
+        if (m < M) *reinterpret_cast<half8 *>(&wx[m * ldx + cs * 8]) = xr[i] * sv;
       } else if (pre) {
         if (m < M) {
-          *reinterpret_cast<half8 *>(&xs[m * ldx + cs * 8]) = xr[i];
+          *reinterpret_cast<half8 *>(&wx[m * ldx + cs * 8]) = xr[i];
           if ((cs & 15) == 0) wsum[m * wgroups + cs / 16] = gp[kBF ? i : 0];
         }
       } else {
@@ -722,7 +732,7 @@ __device__ __forceinline__ void skinny_window_body(const ProblemSet &ps, _Float1
         }
         part = segment_sum16(part);  // all 16 lanes of the segment share m
         if (m < M) {
-          *reinterpret_cast<u32x4 *>(&xs[m * ldx + cs * 8]) = out;
+          *reinterpret_cast<u32x4 *>(&wx[m * ldx + cs * 8]) = out;
           if ((cs & 15) == 0) wsum[m * wgroups + cs / 16] = part;
         }
       }
@@ -736,17 +746,17 @@ __device__ __forceinline__ void skinny_window_body(const ProblemSet &ps, _Float1
   load_window(0);
 #pragma unroll
   for (int d = 0; d < kDepth; ++d) load_chunk(d, chunk_g0(d));
-  store_window();
+  store_window(xs);
   lds_barrier();
   OutPrefetch of = {};
   if (kOut) of = outlier_prefetch(P, orange, lane);
   load_window(1);
 
   // rows m >= M of the A operand only feed rows of D that are not stored
-  const _Float16 *xrow = xs + min(r, M - 1) * ldx + ks * kGW * kGroup + 8 * c;
-  int ws_row[4];  // bf16: rows 4c + v of wsum at this wave's chunk
+  const _Float16 *xrow0 = xs + min(r, M - 1) * ldx + ks * kGW * kGroup + 8 * c;
+  int ws_row[4];  // bf16: rows 4c + v of wsum (after the window's rows) at this wave's chunk
 #pragma unroll
-  for (int v = 0; v < 4; ++v) ws_row[v] = min(4 * c + v, M - 1) * wgroups + ks * kGW;
+  for (int v = 0; v < 4; ++v) ws_row[v] = M * ldx / 2 + min(4 * c + v, M - 1) * wgroups + ks * kGW;
   const uint32_t m_lo = 0x000F000Fu, m_hi = 0x00F000F0u, magic = kMagic2;
   float4v acc = {0.f, 0.f, 0.f, 0.f};
   // Issue order per step: this wave's next chunk, then (after the window
@@ -779,6 +789,8 @@ __device__ __forceinline__ void skinny_window_body(const ProblemSet &ps, _Float1
     load_chunk(kDepth - 1, chunk_g0(j + kDepth));
 
     const int g0 = chunk_g0(j);
+    const _Float16 *xrow = xrow0 + (j & 1) * wpair;
+    const float *wsum = reinterpret_cast<const float *>(xs + (j & 1) * wpair);
     if (has_rows && g0 < G) {
 #pragma unroll
       for (int i = 0; i < kGW; ++i) {
@@ -813,10 +825,13 @@ __device__ __forceinline__ void skinny_window_body(const ProblemSet &ps, _Float1
         }
       }
     }
-    lds_barrier();  // every wave is done with window j
-    store_window();
-    lds_barrier();
+    // window j + 1: into the other buffer (every wave was done with window j
+    // - 1 there at the last barrier), or into the one buffer once every wave
+    // is done with window j
+    if (!wpair) lds_barrier();
+    store_window(xs + ((j + 1) & 1) * wpair);
     load_window(j + 2);
+    lds_barrier();
   }
   // every wave is past the last barrier: the window's LDS takes the partial sums
   store_rows<kWaves, kOut, kBF>(P, acc, b, has_rows, wave, ks, c, r,
@@ -859,6 +874,8 @@ constexpr int kWindowMode = 3;
 constexpr bool kHybridLaunch = true;
 static_assert(kWindowMode >= 1 && kWindowMode <= 3, "X * s must fit in LDS or go in windows");
 constexpr size_t kMaxWindowBytes = 72 * 1024;  // two workgroups per CU
+// Two window buffers when both fit in this (still two workgroups per CU)
+constexpr size_t kMaxWindowPairBytes = 80 * 1024;
 constexpr int kWindowSlots = 8;  // staged 8-column pieces per thread
 // bf16 and INT8 codes: fewer pieces cut the registers (the prescaled bf16
 // instance needs 110 instead of 146: two 8-wave workgroups per CU instead of
@@ -1005,8 +1022,11 @@ hipError_t launch_group(const GemmDesc *const *d, int count, LaunchKind kind, hi
     p.block0 = blocks;
     const int rb_per_wg = kWaves / split;
     blocks += (NB + rb_per_wg - 1) / rb_per_wg;
-    const size_t wb = window_bytes(q.M, split, q.bf16);
-    const size_t need = win ? (wb > kRedBytes ? wb : kRedBytes) : stage_bytes(q.M, q.K, q.bf16);
+    const size_t wb = window_bytes(q.M, split, q.bf16), wb16 = (wb + 15) / 16 * 16;
+    const bool pair = win && 2 * wb16 <= kMaxWindowPairBytes;
+    p.wpair = pair ? (int)(wb16 / 2) : 0;
+    const size_t wlds = pair ? 2 * wb16 : wb;
+    const size_t need = win ? (wlds > kRedBytes ? wlds : kRedBytes) : stage_bytes(q.M, q.K, q.bf16);
     lds = need > lds ? need : lds;
   }
   ps.count = count;
