@@ -235,12 +235,14 @@ def test_grouped_matches_single_calls_and_oracle():
         assert_close(Y, single, f"grouped vs single {M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("M", [5, 9])
+@pytest.mark.parametrize("M", [4, 5, 9])
 def test_mixed_launch_verify_layer(M):
-    """The 8B layer's seven shapes at a verify batch (fewer rows of W each): down's
-    X * s (K = 14336) does not fit in LDS while the others' does, so one launch mixes
-    whole-row staging and K windows.  Each output matches the oracle and the single
-    call (whole rows for K = 4096, windows for K = 14336), and repeats bit for bit."""
+    """The 8B layer's seven shapes at a verify batch (fewer rows of W each).  At M = 4
+    and 5 down's X * s (K = 14336, 115 and 143 KB) exceeds the 8-wave workgroups' stage
+    but fits the 16-wave ones', so the launch stages whole rows in 16-wave workgroups;
+    at M = 9 it does not fit at all, and one launch mixes whole-row staging and K
+    windows.  Each output matches the oracle and the single call, and repeats bit for
+    bit."""
     torch_cuda()
     shapes = [(256, 4096), (64, 4096), (64, 4096), (256, 4096), (512, 4096), (512, 4096),
               (256, 14336)]
@@ -257,6 +259,26 @@ def test_mixed_launch_verify_layer(M):
         assert_close(Y, Yref, f"mixed {M}x{N}x{K}")
         assert np.array_equal(Y.view(np.uint16), Y2.view(np.uint16)), f"{M}x{N}x{K}"
         assert_close(Y, to_host(w4.w4a16_gemm(Xd, pw, sd)), f"mixed vs single {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("K,wide", [(15232, True), (15360, False)])
+def test_wide_stage_boundary(K, wide):
+    """M = 5 rows of X * s at the edge of the 16-wave whole-row stage (150 KB):
+    K = 15232 fits (152,400 bytes with the row padding) and the call stages whole
+    rows; K = 15360 does not (153,680 bytes) and walks K windows.  Either way, with a
+    second problem that fits the 8-wave stage, the outputs match the oracle."""
+    torch_cuda()
+    M = 5
+    items, refs = [], []
+    for i, (N, KK) in enumerate([(64, K), (48, 4096)]):
+        pw, s, ref = packed_case(N, KK, True, key=13, mat=i)
+        X = activations(13, 20 + i, M, KK)
+        items.append((to_dev(X), pw, to_dev(s)))
+        refs.append(oracle.gemm(X, ref.q, ref.scales, ref.zeros, s))
+    note(f"wide stage boundary M={M} K={K} (whole rows: {wide})")
+    for Y, Yref, (Xd, pw, sd) in zip(w4.w4a16_gemm_grouped(items), refs, items):
+        assert_close(to_host(Y), Yref, f"wide boundary K={K} N={pw.N}")
+        assert_close(to_host(w4.w4a16_gemm(Xd, pw, sd)), Yref, f"single K={K} N={pw.N}")
 
 
 def test_graph_replay_matches_eager():

@@ -864,6 +864,14 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_hybrid_kernel(ProblemSet p
 constexpr size_t kMaxStageBytes = 96 * 1024;
 constexpr int kChunk = 4;  // groups per chunk (weight loads in flight per wave)
 constexpr int kWaves = 8;  // waves per workgroup
+// fp16 INT4 calls whose X * s all fit in kWideStageBytes but not all in
+// kMaxStageBytes (the Llama-3-8B layer at M = 4, 5: 143 KB for down) stage
+// whole rows in 16-wave workgroups, one per CU: the same waves per CU as two
+// 8-wave workgroups, and no windows (measured 26.1 -> 24.9 us at M = 5).
+// Launches with windows keep 8 waves: 16-wave hybrid launches were slower
+// (M = 9: 26.9 -> 31.5 us; Qwen2-7B M = 16: 32.1 -> 37.3 us).
+constexpr int kWideWaves = 16;
+constexpr size_t kWideStageBytes = 150 * 1024;
 constexpr int kDepth = 1;  // chunks in flight per wave
 // 1: window the problems whose X * s does not fit, 2: always window, 3:
 // window the whole call when one problem does not fit (measured best; 1 and 2
@@ -953,22 +961,21 @@ void launch_window8(bool bf, bool out, bool pre, dim3 grid, dim3 threads, size_t
                        threads, lds, stream, ps);
 }
 
-// LDS bytes of the split-K partial sums (the kernels reuse the X * s space).
-constexpr size_t kRedBytes = (size_t)kWaves * 16 * 17 * sizeof(float);
 
 enum LaunchKind { kWhole = 0, kWindowed = 1, kHybrid = 2 };
 
 // One launch over the problems d[0..count): whole-row X * s staging, K
 // windows, or (kHybrid: fp16 INT4 codes without outliers) each problem the
 // way its X * s fits.
-hipError_t launch_group(const GemmDesc *const *d, int count, LaunchKind kind, hipStream_t stream) {
+hipError_t launch_group(const GemmDesc *const *d, int count, LaunchKind kind, hipStream_t stream,
+                        int waves = kWaves) {
   if (count == 0) return hipSuccess;
   // How many waves share a row block: enough waves in the whole launch to keep
   // HBM busy, and no wave walking more than kMaxGroupsPerWave groups.
   long long rows = 0;
   for (int i = 0; i < count; ++i) rows += d[i]->N / kTileRows;
   const int s_fill =
-      (int)min((long long)kWaves, (long long)pow2_at_least((int)((kTargetWaves + rows - 1) / rows)));
+      (int)min((long long)waves, (long long)pow2_at_least((int)((kTargetWaves + rows - 1) / rows)));
   // Problems are laid out longest-rows first so that the waves with the most
   // work start first.
   int order[kMaxProblems];
@@ -994,7 +1001,7 @@ hipError_t launch_group(const GemmDesc *const *d, int count, LaunchKind kind, hi
     const bool win = kind == kWindowed ||
                      (kind == kHybrid && stage_bytes(q.M, q.K, q.bf16) > kMaxStageBytes);
     int split = s_fill;
-    while (split < kWaves && (G + split - 1) / split > kMaxGroupsPerWave) split *= 2;
+    while (split < waves && (G + split - 1) / split > kMaxGroupsPerWave) split *= 2;
     while (split > 1 && (G + kChunk - 1) / kChunk < split) split /= 2;  // a chunk per wave
     if (win)  // a window of split chunks must fit in LDS and in the staging registers
       while (split > 1 && (window_bytes(q.M, split, q.bf16) > kMaxWindowBytes ||
@@ -1020,19 +1027,25 @@ hipError_t launch_group(const GemmDesc *const *d, int count, LaunchKind kind, hi
     out |= q.o_row_ptr != nullptr;
     p.window = win;
     p.block0 = blocks;
-    const int rb_per_wg = kWaves / split;
+    const int rb_per_wg = waves / split;
     blocks += (NB + rb_per_wg - 1) / rb_per_wg;
     const size_t wb = window_bytes(q.M, split, q.bf16), wb16 = (wb + 15) / 16 * 16;
     const bool pair = win && 2 * wb16 <= kMaxWindowPairBytes;
     p.wpair = pair ? (int)(wb16 / 2) : 0;
     const size_t wlds = pair ? 2 * wb16 : wb;
-    const size_t need = win ? (wlds > kRedBytes ? wlds : kRedBytes) : stage_bytes(q.M, q.K, q.bf16);
+    // the split-K partial sums reuse the X * s space
+    const size_t red = (size_t)waves * 16 * 17 * sizeof(float), sb = stage_bytes(q.M, q.K, q.bf16);
+    const size_t need = win ? (wlds > red ? wlds : red) : (sb > red ? sb : red);
     lds = need > lds ? need : lds;
   }
   ps.count = count;
-  const dim3 grid(blocks), threads(kWaves * 64);
+  const dim3 grid(blocks), threads(waves * 64);
   const bool bf = d[0]->bf16;  // one activation type (and code width) per launch
-  if (kind == kHybrid) {
+  if (waves == kWideWaves) {
+    if (kind != kWhole || bf || out || d[0]->w8) return hipErrorInvalidValue;  // not instantiated
+    hipLaunchKernelGGL((skinny_kernel<kChunk, kWideWaves, kDepth, false, false>), grid, threads,
+                       lds, stream, ps);
+  } else if (kind == kHybrid) {
     if (bf || out || d[0]->w8) return hipErrorInvalidValue;  // not instantiated
     hipLaunchKernelGGL((skinny_hybrid_kernel<kChunk, kWaves, kDepth, kWindowSlots>), grid, threads,
                        lds, stream, ps);
@@ -1136,7 +1149,7 @@ hipError_t launch_skinny_set(const GemmDesc *d, int count, hipStream_t stream, b
     auto in_class = [&](const GemmDesc &q) { return q.bf16 == want_bf && q.w8 == want_w8; };
     const GemmDesc *whole[kMaxProblems], *windowed[kMaxProblems];
     int nwhole = 0, nwin = 0;
-    bool any = false, all = true, outl = false;
+    bool any = false, all = true, outl = false, wide = true;
     const GemmDesc *members[kMaxProblems];
     int nm = 0;
     for (int i = 0; i < count; ++i)
@@ -1144,9 +1157,16 @@ hipError_t launch_skinny_set(const GemmDesc *d, int count, hipStream_t stream, b
         const bool big = stage_bytes(d[i].M, d[i].K, d[i].bf16) > kMaxStageBytes;
         any |= big;
         all &= big;
+        wide &= stage_bytes(d[i].M, d[i].K, d[i].bf16) <= kWideStageBytes;
         outl |= d[i].o_row_ptr != nullptr;
         members[nm++] = d + i;
       }
+    // fp16 INT4 without outliers, all X * s within kWideStageBytes: whole rows
+    // in 16-wave workgroups
+    if (cls == 0 && any && wide && !outl && !force_window) {
+      err = launch_group(members, nm, kWhole, stream, kWideWaves);
+      continue;
+    }
     // fp16 INT4 without outliers: problems that fit stage whole rows and the
     // others walk windows, in the same launch
     if (kHybridLaunch && cls == 0 && any && !all && !outl && !force_window && kWindowMode == 3) {
