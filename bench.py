@@ -692,8 +692,9 @@ def main():
     ap.add_argument("--profile-run", nargs="?", const="layer", choices=["layer", "verify", "batched"],
                     help="only a short fixed sequence for counter collection: 'layer' (the "
                          "default: a calibration copy, 20 decode steps, the 70B prefill "
-                         "matrices), 'verify' (8B layer at M=2, 5, 9) or 'batched' (Qwen2-7B "
-                         "layer at M=64, 256)")
+                         "matrices), 'verify' (8B layer at M=2, 5, 9 and Qwen2-7B layer at "
+                         "M=16: the streaming kernel's whole-row, 16-wave, hybrid and windowed "
+                         "launches) or 'batched' (Qwen2-7B layer at M=64, 256)")
     ap.add_argument("--dispatch-sweep", action="store_true",
                     help="only the M-dispatch crossover sweep (tiled vs 16-row streaming "
                          "pieces, M = 17..256 on the 8B, Qwen2-7B and 70B layers), as one "
@@ -714,6 +715,7 @@ def main():
     w4.lib()  # fail loudly if the HIP library is missing
     if args.profile_run == "verify":
         profile_run_batches(torch, w4, workloads, "llama3_8b_verify", (2, 5, 9))
+        profile_run_batches(torch, w4, workloads, "qwen2_7b_batched_decode", (16,))
         return
     if args.profile_run == "batched":
         profile_run_batches(torch, w4, workloads, "qwen2_7b_batched_decode", (64, 256))
