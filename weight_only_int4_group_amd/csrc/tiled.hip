@@ -621,7 +621,8 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
 //     ahead, in two register sets that alternate.
 // Blocks are BM x BN (BM = 16 TM, BN = 64 TN), four waves of BM x 16 TN per
 // K slice; K is split across workgroups the same way as in tiled_kernel.
-// Batched decode (M up to 64) takes TN = 2: twice the blocks of TN = 4, so
+// Batched decode (M up to 64) takes TN = 2 (and TM = 2, 3 or 4, as few rows
+// as cover M): twice the blocks of TN = 4, so
 // fewer K splits (whose fp32 partials cost HBM traffic) are needed to fill the
 // GPU, and half the accumulators.  Its blocks have one K slice of four waves
 // or KS = 2: each slice walks every other group of the workgroup's K range
@@ -951,26 +952,31 @@ constexpr int kDmaMinM = 17;
 
 // Geometry of the tiled_dma_kernel instances: TM = 8, TN = 4 (128 x 256
 // blocks of four waves, two workgroups per CU) when the launch's largest M
-// exceeds 64, else TM = 4, TN = 2 (64 x 128 blocks) with one K slice (four
-// waves, four workgroups per CU) or two (eight waves, two per CU), whichever
-// the launch model below prefers.
+// exceeds 64, else TN = 2 and the fewest 16-row tiles that cover M (TM = 2,
+// 3 or 4: blocks of 32, 48 or 64 x 128) with one K slice (four waves) or two
+// (eight waves), whichever the launch model below prefers.  Below 64 rows the
+// padded rows' MFMAs and A reads are not free: the Qwen2-7B layer at M = 17
+// took 43 us with 64-row tiles and 34 us with 32-row ones, at M = 33 45 and
+// 42 us with 64- and 48-row ones.  Covering 64 rows with two 32-row tiles
+// instead (each weight read twice) was slower: 62 against 50 us.
 struct DmaShape {
   int tm, tn;
   int bm() const { return 16 * tm; }
   int bn() const { return 64 * tn; }
 };
-DmaShape dma_shape(int tm) { return tm == 8 ? DmaShape{8, 4} : DmaShape{4, 2}; }
+DmaShape dma_shape(int tm) { return tm == 8 ? DmaShape{8, 4} : DmaShape{tm, 2}; }
 long long dma_slots(int tm, int ks) { return tm == 8 || ks == 2 ? 512 : 1024; }
 
 // 0 when the launch cannot take tiled_dma_kernel, else its TM: 8 (128-row
-// wave tiles) when the largest M exceeds 64, else 4
+// wave tiles) when the largest M exceeds 64, else 2, 3 or 4 (32, 48 or 64
+// rows)
 int dma_tm(const GemmDesc *d, int count) {
   int mmax = 0;
   for (int i = 0; i < count; ++i) {
     if (!dma_capable(d[i])) return 0;
     mmax = std::max(mmax, d[i].M);
   }
-  return mmax < kDmaMinM ? 0 : (mmax > 64 ? 8 : 4);
+  return mmax < kDmaMinM ? 0 : (mmax > 64 ? 8 : (mmax > 48 ? 4 : (mmax > 32 ? 3 : 2)));
 }
 bool dma_launch(const GemmDesc *d, int count) { return dma_tm(d, count) != 0; }
 
@@ -1180,6 +1186,14 @@ hipError_t launch_tiled_set(const GemmDesc *d, int count, void *workspace, size_
   const dim3 grid(blocks), threads(kWM * kWN * 64);
   if (dma && tm == 8)
     hipLaunchKernelGGL((tiled_dma_kernel<8, 4, 1>), grid, dim3(256), 0, stream, ts);
+  else if (dma && tm == 2 && ks == 2)
+    hipLaunchKernelGGL((tiled_dma_kernel<2, 2, 2>), grid, dim3(512), 0, stream, ts);
+  else if (dma && tm == 2)
+    hipLaunchKernelGGL((tiled_dma_kernel<2, 2, 1>), grid, dim3(256), 0, stream, ts);
+  else if (dma && tm == 3 && ks == 2)
+    hipLaunchKernelGGL((tiled_dma_kernel<3, 2, 2>), grid, dim3(512), 0, stream, ts);
+  else if (dma && tm == 3)
+    hipLaunchKernelGGL((tiled_dma_kernel<3, 2, 1>), grid, dim3(256), 0, stream, ts);
   else if (dma && ks == 2)
     hipLaunchKernelGGL((tiled_dma_kernel<4, 2, 2>), grid, dim3(512), 0, stream, ts);
   else if (dma)
