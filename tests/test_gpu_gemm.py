@@ -321,13 +321,14 @@ def test_graph_replay_matches_eager():
 @pytest.mark.parametrize("M,N,K", [(17, 272, 640), (31, 272, 4096), (32, 48, 18944),
                                    (33, 272, 640), (40, 528, 1152), (48, 528, 1152),
                                    (49, 272, 4096), (64, 48, 18944),
-                                   (65, 272, 640), (100, 528, 1152), (128, 256, 4096),
+                                   (65, 272, 640), (96, 272, 4096), (97, 48, 18944),
+                                   (100, 528, 1152), (128, 256, 4096),
                                    (129, 272, 640), (257, 16, 4096), (300, 1024, 2048),
                                    (520, 784, 1408)])
 def test_dma_tiled_kernel(M, N, K, awq):
     """The tiled kernel with X * s brought into LDS by DMA (fp16 activations, INT4 codes;
-    32-, 48- or 64-row wave tiles up to M = 64, the fewest that cover M, 128-row ones
-    above; each size at and past its edge): through w4a16_gemm, which passes
+    32-, 48-, 64-, 96- or 128-row wave tiles, the fewest that cover M; each size at and
+    past its edge): through w4a16_gemm, which passes
     a workspace (X * s
     prescaled there when s is given; K split where the blocks are few), and through the
     forced tiled path without a workspace (X straight from its buffer when s is null,

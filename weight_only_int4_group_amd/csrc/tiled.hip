@@ -952,23 +952,25 @@ constexpr int kDmaMinM = 17;
 
 // Geometry of the tiled_dma_kernel instances: TM = 8, TN = 4 (128 x 256
 // blocks of four waves, two workgroups per CU) when the launch's largest M
-// exceeds 64, else TN = 2 and the fewest 16-row tiles that cover M (TM = 2,
-// 3 or 4: blocks of 32, 48 or 64 x 128) with one K slice (four waves) or two
-// (eight waves), whichever the launch model below prefers.  Below 64 rows the
+// exceeds 96, TM = 6, TN = 4 (96 x 256) from 65 to 96 rows, else TN = 2 and
+// the fewest 16-row tiles that cover M (TM = 2, 3 or 4: blocks of 32, 48 or
+// 64 x 128) with one K slice (four waves) or two (eight waves), whichever the
+// launch model below prefers.  Below 64 rows the
 // padded rows' MFMAs and A reads are not free: the Qwen2-7B layer at M = 17
 // took 43 us with 64-row tiles and 34 us with 32-row ones, at M = 33 45 and
 // 42 us with 64- and 48-row ones.  Covering 64 rows with two 32-row tiles
-// instead (each weight read twice) was slower: 62 against 50 us.
+// instead (each weight read twice) was slower: 62 against 50 us.  At M = 65
+// 96-row tiles took 62 against 69 us with 128-row ones.
 struct DmaShape {
   int tm, tn;
   int bm() const { return 16 * tm; }
   int bn() const { return 64 * tn; }
 };
-DmaShape dma_shape(int tm) { return tm == 8 ? DmaShape{8, 4} : DmaShape{tm, 2}; }
-long long dma_slots(int tm, int ks) { return tm == 8 || ks == 2 ? 512 : 1024; }
+DmaShape dma_shape(int tm) { return tm >= 6 ? DmaShape{tm, 4} : DmaShape{tm, 2}; }
+long long dma_slots(int tm, int ks) { return tm >= 6 || ks == 2 ? 512 : 1024; }
 
-// 0 when the launch cannot take tiled_dma_kernel, else its TM: 8 (128-row
-// wave tiles) when the largest M exceeds 64, else 2, 3 or 4 (32, 48 or 64
+// 0 when the launch cannot take tiled_dma_kernel, else its TM: the fewest
+// 16-row tiles that cover the largest M among 2, 3, 4, 6 and 8 (32 to 128
 // rows)
 int dma_tm(const GemmDesc *d, int count) {
   int mmax = 0;
@@ -976,7 +978,8 @@ int dma_tm(const GemmDesc *d, int count) {
     if (!dma_capable(d[i])) return 0;
     mmax = std::max(mmax, d[i].M);
   }
-  return mmax < kDmaMinM ? 0 : (mmax > 64 ? 8 : (mmax > 48 ? 4 : (mmax > 32 ? 3 : 2)));
+  return mmax < kDmaMinM ? 0
+                         : (mmax > 96 ? 8 : mmax > 64 ? 6 : mmax > 48 ? 4 : mmax > 32 ? 3 : 2);
 }
 bool dma_launch(const GemmDesc *d, int count) { return dma_tm(d, count) != 0; }
 
@@ -1057,8 +1060,8 @@ int dma_plan(const GemmDesc *d, int count, int tm, bool unsplit, int *split) {
   const int kss[2] = {2, 1};
   int best_ks = 1;
   double best = 0.0;
-  for (int v = 0; v < (tm == 8 ? 1 : 2); ++v) {
-    const int ks = tm == 8 ? 1 : kss[v];
+  for (int v = 0; v < (tm >= 6 ? 1 : 2); ++v) {
+    const int ks = tm >= 6 ? 1 : kss[v];
     int s[kMaxTiled];
     double t;
     if (unsplit) {
@@ -1186,6 +1189,8 @@ hipError_t launch_tiled_set(const GemmDesc *d, int count, void *workspace, size_
   const dim3 grid(blocks), threads(kWM * kWN * 64);
   if (dma && tm == 8)
     hipLaunchKernelGGL((tiled_dma_kernel<8, 4, 1>), grid, dim3(256), 0, stream, ts);
+  else if (dma && tm == 6)
+    hipLaunchKernelGGL((tiled_dma_kernel<6, 4, 1>), grid, dim3(256), 0, stream, ts);
   else if (dma && tm == 2 && ks == 2)
     hipLaunchKernelGGL((tiled_dma_kernel<2, 2, 2>), grid, dim3(512), 0, stream, ts);
   else if (dma && tm == 2)
