@@ -3,7 +3,8 @@
 The benchmark runs a whole layer as one grouped call (``GroupedCall``: all seven
 full-size matrices, with the workspace the library asks for) at each batch size:
 the Llama-3-8B-shaped layer at M = 1 (decode) and M = 2, 5, 9 (speculative verify),
-and the Qwen2-7B-shaped layer at M = 16, 64, 256 (batched decode).  A grouped launch
+and the Qwen2-7B-shaped layer at M = 16, 64, 256 (batched decode); the same layer at
+M = 24, 40 and 80 covers the tiled kernel's 32-, 48- and 96-row tiles.  A grouped launch
 chooses its K split, its X * s staging (whole rows, K windows, or both in one launch)
 and its split-K partials from the whole set of problems, so its summation order can
 differ from a one-problem call of the same matrix; this file checks the grouped call
@@ -23,7 +24,9 @@ pytestmark = pytest.mark.gpu
 
 CASES = [("llama3_8b_decode", 1), ("llama3_8b_verify", 2), ("llama3_8b_verify", 5),
          ("llama3_8b_verify", 9), ("qwen2_7b_batched_decode", 16),
-         ("qwen2_7b_batched_decode", 64), ("qwen2_7b_batched_decode", 256)]
+         ("qwen2_7b_batched_decode", 64), ("qwen2_7b_batched_decode", 256),
+         ("qwen2_7b_batched_decode", 24), ("qwen2_7b_batched_decode", 40),
+         ("qwen2_7b_batched_decode", 80)]
 
 _PACKED = {}
 
