@@ -632,7 +632,7 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
 // only down across workgroups and took 52-56 us against 61, while layers with
 // more blocks than slots (70B at M = 64) keep one slice.  (KS = 2 at TM = 8
 // needs more than 256 VGPRs.)
-template <int TM, int TN, int KS>
+template <int TM, int TN, int KS, bool BF = false>
 __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(TN == 2 ? 4 : 2, TN == 2 ? 4 : 2))) void tiled_dma_kernel(
     TiledSet ts) {
   constexpr int WN = 4;
@@ -736,43 +736,59 @@ __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(TN == 
   // k step, then TM x TN MFMAs with A read from LDS buffer `buf`
   auto compute = [&](const BStage &b, int buf) {
     half2v bias_lo[TN], bias_hi[TN], scale[TN];
+    float fsc[TN], fzb[TN];  // bf16: the fp32 scale and (128 + z) * scale
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const _Float16 z = __builtin_bit_cast(_Float16, (uint16_t)b.zp[j]);
       const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)b.sc[j]);
-      const _Float16 blo = (_Float16)1024.0f + z, bhi = (_Float16)64.0f + z;
-      const half2v bl = {blo, blo}, bh = {bhi, bhi}, sc = {sv, sv};
-      bias_lo[j] = bl;
-      bias_hi[j] = bh;
-      scale[j] = sc;
+      if (BF) {
+        fsc[j] = (float)sv;
+        fzb[j] = (128.0f + (float)z) * fsc[j];
+      } else {
+        const _Float16 blo = (_Float16)1024.0f + z, bhi = (_Float16)64.0f + z;
+        const half2v bl = {blo, blo}, bh = {bhi, bhi}, sc = {sv, sv};
+        bias_lo[j] = bl;
+        bias_hi[j] = bh;
+        scale[j] = sc;
+      }
     }
+    // a B operand: eight dequantized weights, fp16 or bf16 bits
+    auto dequant = [&](int j, int t) -> u32x4 {
+      if constexpr (BF)
+        return dequant_word_bf16(b.code[j][t], fsc[j], fzb[j]);
+      else
+        return __builtin_bit_cast(u32x4, dequant_word(b.code[j][t], bias_lo[j], bias_hi[j], scale[j]));
+    };
     const _Float16 *abuf = As[ks][buf];
     // software pipeline: k step tt + 1's B operands are dequantized while k
-    // step tt's MFMAs run, interleaved by the scheduler (one LDS read, four
-    // MFMAs and about seven VALU ops at a time)
-    half8 bop[TN];
+    // step tt's MFMAs run, interleaved by the scheduler (one LDS read, TN
+    // MFMAs and about seven VALU ops at a time; twice that for bf16, whose
+    // dequantization costs twice the ops)
+    u32x4 bop[TN];
 #pragma unroll
-    for (int j = 0; j < TN; ++j) bop[j] = dequant_word(b.code[j][0], bias_lo[j], bias_hi[j], scale[j]);
+    for (int j = 0; j < TN; ++j) bop[j] = dequant(j, 0);
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
-      half8 bnx[TN];
+      u32x4 bnx[TN];
       if (tt < 3) {
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-          bnx[j] = dequant_word(b.code[j][tt + 1], bias_lo[j], bias_hi[j], scale[j]);
+        for (int j = 0; j < TN; ++j) bnx[j] = dequant(j, tt + 1);
       }
       const int pc = (4 * tt + c) ^ r;
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
-        const half8 aop = *reinterpret_cast<const half8 *>(abuf + (16 * i + r) * kGroup + 8 * pc);
+        const u32x4 aop = *reinterpret_cast<const u32x4 *>(abuf + (16 * i + r) * kGroup + 8 * pc);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = mfma16(aop, bop[j], acc[i][j]);
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = BF ? mfma16_bf16(aop, bop[j], acc[i][j])
+                         : mfma16(__builtin_bit_cast(half8, aop), __builtin_bit_cast(half8, bop[j]),
+                                  acc[i][j]);
       }
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
         __builtin_amdgcn_sched_group_barrier(0x008, TN, 0);  // TN MFMAs
-        if (tt < 3) __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);  // VALU
+        if (tt < 3) __builtin_amdgcn_sched_group_barrier(0x002, BF ? 14 : 7, 0);  // VALU
       }
       if (tt < 3) {
 #pragma unroll
@@ -854,6 +870,8 @@ __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(TN == 
         if (m < M && n < N) {
           if (part)
             part[(size_t)m * N + n] = acc[i][j][v];
+          else if (BF)
+            reinterpret_cast<uint16_t *>(P.Y)[(size_t)m * N + n] = f32_to_bf16(acc[i][j][v]);
           else
             P.Y[(size_t)m * N + n] = (_Float16)acc[i][j][v];
         }
@@ -870,6 +888,7 @@ struct PrescaleItem {
   _Float16 *out;
   int K;
   int block0;  // first workgroup of this problem
+  int bf16;    // X and out are bf16: bf16(X * s), the product exact in fp32
   long long n8;
 };
 struct PrescaleSet {
@@ -889,7 +908,20 @@ __global__ __launch_bounds__(256) void prescale_f16_kernel(PrescaleSet ps) {
   if (i >= ps.p[pi].n8) return;
   const long long e = i * 8;
   const int k = (int)(e % K);
-  *reinterpret_cast<half8 *>(out + e) = load_half8(X + e) * load_half8(sv + k);
+  if (uniform_int(ps.p[pi].bf16)) {
+    const u32x4 xw = *reinterpret_cast<const u32x4 *>(X + e);
+    const half8 s8 = load_half8(sv + k);
+    u32x4 v;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float lo = bf16_to_f32((uint16_t)xw[q]) * (float)s8[2 * q];
+      const float hi = bf16_to_f32((uint16_t)(xw[q] >> 16)) * (float)s8[2 * q + 1];
+      v[q] = (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+    }
+    *reinterpret_cast<u32x4 *>(out + e) = v;
+  } else {
+    *reinterpret_cast<half8 *>(out + e) = load_half8(X + e) * load_half8(sv + k);
+  }
 }
 
 // Y = fp16(sum of the split partials, in split order) for the problems with
@@ -942,11 +974,11 @@ int tiles_of(const GemmDesc &d, int bm = kBM, int bn = kBN) {
   return ((d.N + bn - 1) / bn) * ((d.M + bm - 1) / bm);
 }
 
-// tiled_dma_kernel takes fp16 activations and INT4 codes without outliers
-// whose X (M x K fp16) a buffer resource can cover; it runs 128-row wave
-// tiles, so it serves launches whose largest M exceeds 64.
+// tiled_dma_kernel takes fp16 or bf16 activations and INT4 codes without
+// outliers whose X (M x K, 2 bytes each) a buffer resource can cover; it
+// serves launches whose largest M exceeds 16.
 bool dma_capable(const GemmDesc &d) {
-  return !d.bf16 && !d.w8 && !d.o_row_ptr && (size_t)d.M * d.K * 2 < ((size_t)1 << 31);
+  return !d.w8 && !d.o_row_ptr && (size_t)d.M * d.K * 2 < ((size_t)1 << 31);
 }
 constexpr int kDmaMinM = 17;
 
@@ -978,8 +1010,9 @@ int dma_tm(const GemmDesc *d, int count) {
     if (!dma_capable(d[i])) return 0;
     mmax = std::max(mmax, d[i].M);
   }
-  return mmax < kDmaMinM ? 0
-                         : (mmax > 96 ? 8 : mmax > 64 ? 6 : mmax > 48 ? 4 : mmax > 32 ? 3 : 2);
+  if (mmax < kDmaMinM) return 0;
+  if (d[0].bf16) return mmax > 64 ? 6 : 4;  // bf16: the 64- and 96-row instances
+  return mmax > 96 ? 8 : mmax > 64 ? 6 : mmax > 48 ? 4 : mmax > 32 ? 3 : 2;
 }
 bool dma_launch(const GemmDesc *d, int count) { return dma_tm(d, count) != 0; }
 
@@ -1168,6 +1201,7 @@ hipError_t launch_tiled_set(const GemmDesc *d, int count, void *workspace, size_
         q.s = static_cast<const _Float16 *>(d[i].s);
         q.out = xs;
         q.K = d[i].K;
+        q.bf16 = d[i].bf16;
         q.n8 = (long long)d[i].M * d[i].K / 8;
         q.block0 = pblocks;
         pblocks += (int)((q.n8 + 255) / 256);
@@ -1187,7 +1221,13 @@ hipError_t launch_tiled_set(const GemmDesc *d, int count, void *workspace, size_
     if (e != hipSuccess) return e;
   }
   const dim3 grid(blocks), threads(kWM * kWN * 64);
-  if (dma && tm == 8)
+  if (dma && d[0].bf16 && tm == 6)
+    hipLaunchKernelGGL((tiled_dma_kernel<6, 4, 1, true>), grid, dim3(256), 0, stream, ts);
+  else if (dma && d[0].bf16 && ks == 2)
+    hipLaunchKernelGGL((tiled_dma_kernel<4, 2, 2, true>), grid, dim3(512), 0, stream, ts);
+  else if (dma && d[0].bf16)
+    hipLaunchKernelGGL((tiled_dma_kernel<4, 2, 1, true>), grid, dim3(256), 0, stream, ts);
+  else if (dma && tm == 8)
     hipLaunchKernelGGL((tiled_dma_kernel<8, 4, 1>), grid, dim3(256), 0, stream, ts);
   else if (dma && tm == 6)
     hipLaunchKernelGGL((tiled_dma_kernel<6, 4, 1>), grid, dim3(256), 0, stream, ts);
