@@ -36,6 +36,8 @@ def check(Y, ref, tag):
     (16, 2048, 4096, True),      # streaming, K windows
     (17, 1024, 2048, True),      # tiled, ragged M
     (64, 4096, 4096, True),      # tiled, split K
+    (65, 272, 640, True),        # tiled, 96-row tiles at their lower edge
+    (97, 528, 18944, True),      # tiled, 96-row tiles, ragged M, split K
     (300, 1296, 1536, False),    # tiled, ragged M and N
 ])
 def test_bf16_matches_oracle(M, N, K, awq):
