@@ -632,10 +632,12 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
 // only down across workgroups and took 52-56 us against 61, while layers with
 // more blocks than slots (70B at M = 64) keep one slice.  (KS = 2 at TM = 8
 // needs more than 256 VGPRs.)
-template <int TM, int TN, int KS, bool BF = false>
+template <int TM, int TN, int KS, bool BF = false, bool W8 = false>
 __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(TN == 2 ? 4 : 2, TN == 2 ? 4 : 2))) void tiled_dma_kernel(
     TiledSet ts) {
   constexpr int WN = 4;
+  constexpr int kCW = W8 ? 2 : 1;  // 16-byte code pieces per lane per tile
+  static_assert(!(BF && W8), "INT8 codes: fp16 activations");
   constexpr int BM = TM * 16, BN = WN * TN * 16;
   constexpr int kRowChunks = kGroup / 8;            // 16-byte chunks per row per group
   constexpr int kDma = BM * kRowChunks / (4 * 64);  // DMA loads per wave per group
@@ -700,7 +702,7 @@ __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(TN == 
 
   // the wave's TN row blocks; blocks past N re-read the last one (never stored)
   const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)P.Wq, (short)0, (int)min((size_t)0x7fffffff, (size_t)N * K / 2), kRsrcWord3);
+      (void *)P.Wq, (short)0, (int)min((size_t)0x7fffffff, (size_t)N * K / 2 * kCW), kRsrcWord3);
   const int Gq = meta_groups(G) / kMetaQuad;
   const size_t meta_bytes = (size_t)N * Gq * kMetaQuad * 2;
   const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
@@ -708,17 +710,20 @@ __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(TN == 
   const __amdgpu_buffer_rsrc_t zrs = __builtin_amdgcn_make_buffer_rsrc(
       (void *)P.zeros, (short)0, (int)min((size_t)0x7fffffff, meta_bytes), kRsrcWord3);
   const int rb0 = n0 / kTileRows + wave * TN;
-  const int tile_stride = NB * kTileBytes, meta_stride = NB * kTileRows * kMetaQuad * 2;
+  const int tile_stride = NB * kTileBytes * kCW, meta_stride = NB * kTileRows * kMetaQuad * 2;
   struct BStage {
-    u32x4 code[TN];
+    u32x4 code[TN][kCW];
     uint32_t sc[TN], zp[TN];  // raw fp16 bits of each row block's scale and zero point
   };
   auto load_b = [&](int g, BStage &b) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int rb = min(rb0 + j, NB - 1);
-      b.code[j] = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrs, (rb * 64 + lane) * 16, g * tile_stride, 0));
+#pragma unroll
+      for (int h = 0; h < kCW; ++h)
+        b.code[j][h] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrs, (rb * 64 + lane) * 16 * kCW + 16 * h,
+                                                         g * tile_stride, 0));
       const int mo = (rb * kTileRows + r) * kMetaQuad * 2;
       const int qo = (g / kMetaQuad) * meta_stride + (g % kMetaQuad) * 2;
       b.sc[j] = __builtin_amdgcn_raw_buffer_load_b16(srs, mo, qo, 0);
@@ -755,9 +760,13 @@ __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(TN == 
     // a B operand: eight dequantized weights, fp16 or bf16 bits
     auto dequant = [&](int j, int t) -> u32x4 {
       if constexpr (BF)
-        return dequant_word_bf16(b.code[j][t], fsc[j], fzb[j]);
+        return dequant_word_bf16(b.code[j][0][t], fsc[j], fzb[j]);
+      else if constexpr (W8)  // k step t: the lane's code words 2t and 2t + 1
+        return __builtin_bit_cast(u32x4, dequant_words8(b.code[j][t >> 1][2 * (t & 1)],
+                                                        b.code[j][t >> 1][2 * (t & 1) + 1],
+                                                        bias_lo[j], scale[j]));
       else
-        return __builtin_bit_cast(u32x4, dequant_word(b.code[j][t], bias_lo[j], bias_hi[j], scale[j]));
+        return __builtin_bit_cast(u32x4, dequant_word(b.code[j][0][t], bias_lo[j], bias_hi[j], scale[j]));
     };
     const _Float16 *abuf = As[ks][buf];
     // software pipeline: k step tt + 1's B operands are dequantized while k
@@ -974,11 +983,12 @@ int tiles_of(const GemmDesc &d, int bm = kBM, int bn = kBN) {
   return ((d.N + bn - 1) / bn) * ((d.M + bm - 1) / bm);
 }
 
-// tiled_dma_kernel takes fp16 or bf16 activations and INT4 codes without
-// outliers whose X (M x K, 2 bytes each) a buffer resource can cover; it
-// serves launches whose largest M exceeds 16.
+// tiled_dma_kernel takes fp16 or bf16 activations with INT4 codes, or fp16
+// activations with INT8 codes, without outliers, whose X (M x K, 2 bytes
+// each) a buffer resource can cover; it serves launches whose largest M
+// exceeds 16.
 bool dma_capable(const GemmDesc &d) {
-  return !d.w8 && !d.o_row_ptr && (size_t)d.M * d.K * 2 < ((size_t)1 << 31);
+  return !(d.w8 && d.bf16) && !d.o_row_ptr && (size_t)d.M * d.K * 2 < ((size_t)1 << 31);
 }
 constexpr int kDmaMinM = 17;
 
@@ -1011,7 +1021,7 @@ int dma_tm(const GemmDesc *d, int count) {
     mmax = std::max(mmax, d[i].M);
   }
   if (mmax < kDmaMinM) return 0;
-  if (d[0].bf16) return mmax > 64 ? 6 : 4;  // bf16: the 64- and 96-row instances
+  if (d[0].bf16 || d[0].w8) return mmax > 64 ? 6 : 4;  // bf16, INT8: 64- and 96-row instances
   return mmax > 96 ? 8 : mmax > 64 ? 6 : mmax > 48 ? 4 : mmax > 32 ? 3 : 2;
 }
 bool dma_launch(const GemmDesc *d, int count) { return dma_tm(d, count) != 0; }
@@ -1221,7 +1231,13 @@ hipError_t launch_tiled_set(const GemmDesc *d, int count, void *workspace, size_
     if (e != hipSuccess) return e;
   }
   const dim3 grid(blocks), threads(kWM * kWN * 64);
-  if (dma && d[0].bf16 && tm == 6)
+  if (dma && d[0].w8 && tm == 6)
+    hipLaunchKernelGGL((tiled_dma_kernel<6, 4, 1, false, true>), grid, dim3(256), 0, stream, ts);
+  else if (dma && d[0].w8 && ks == 2)
+    hipLaunchKernelGGL((tiled_dma_kernel<4, 2, 2, false, true>), grid, dim3(512), 0, stream, ts);
+  else if (dma && d[0].w8)
+    hipLaunchKernelGGL((tiled_dma_kernel<4, 2, 1, false, true>), grid, dim3(256), 0, stream, ts);
+  else if (dma && d[0].bf16 && tm == 6)
     hipLaunchKernelGGL((tiled_dma_kernel<6, 4, 1, true>), grid, dim3(256), 0, stream, ts);
   else if (dma && d[0].bf16 && ks == 2)
     hipLaunchKernelGGL((tiled_dma_kernel<4, 2, 2, true>), grid, dim3(512), 0, stream, ts);
