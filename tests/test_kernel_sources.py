@@ -66,3 +66,41 @@ def test_descriptor_copy_is_complete(source, struct, func):
 def test_field_parser_sees_comma_lists():
     fields = struct_fields("struct T { const int *a, *b; int M, N;  float x; };", "T")
     assert fields == ["a", "b", "M", "N", "x"]
+
+
+def _device_asm(source, tmp_path):
+    """Device-only assembly of one library source, built with the library's flags."""
+    import subprocess
+    from weight_only_int4_group_amd import build
+    flags = [f for f in build.compile_flags() if f not in ("-fPIC", "-shared")]
+    out = str(tmp_path / (source + ".s"))
+    res = subprocess.run([build.hipcc(), *flags, "--cuda-device-only", "-S",
+                          os.path.join(CSRC, source), "-o", out], capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-2000:]
+    return open(out).read()
+
+
+def _kernel_metadata(asm):
+    """(name, private segment bytes, VGPR spills, SGPR spills) of every kernel in the
+    assembly's metadata block."""
+    kernels = []
+    for block in asm.split("  - .agpr_count:")[1:]:
+        name = re.search(r"\.name:\s+(\S+)", block).group(1)
+        field = lambda key: int(re.search(r"\." + key + r":\s+(\d+)", block).group(1))
+        kernels.append((name, field("private_segment_fixed_size"), field("vgpr_spill_count"),
+                        field("sgpr_spill_count")))
+    return kernels
+
+
+@pytest.mark.parametrize("source", ["skinny.hip", "tiled.hip", "pack.hip", "outliers.hip",
+                                    "gptq.hip", "spec.hip"])
+def test_kernels_keep_everything_in_registers(source, tmp_path):
+    """Every kernel compiles without register spills and without a private
+    (per-lane scratch) segment.  A kernel whose accumulators land in scratch
+    memory still computes the right values, so the GPU tests do not see it; it
+    only runs several times slower (an instance whose helper lambdas were not
+    inlined kept its accumulators there and took 19x the time)."""
+    kernels = _kernel_metadata(_device_asm(source, tmp_path))
+    assert kernels, f"{source}: no kernels found"
+    bad = [k for k in kernels if k[1] or k[2] or k[3]]
+    assert not bad, f"{source}: (kernel, private bytes, VGPR spills, SGPR spills): {bad}"
