@@ -899,7 +899,7 @@ def main():
             "TFLOP/s": round(flops / (pwall / args.prefill_steps) / 1e12, 2),
             "ms_per_step": round(pwall / args.prefill_steps * 1e3, 4),
             "roofline": {"bound": "mfma",
-                         "kernel": "tiled_dma_kernel<8, 4, 1>, one launch per matrix (k and v: plus "
+                         "kernel": "tiled_dma_kernel<8, 4, 1, false, false>, one launch per matrix (k and v: plus "
                                    "split_reduce_kernel); timed on calls whose X * s was formed "
                                    "beforehand, which launch exactly this kernel",
                          "outputs_identical_to_calls_with_s": same,
