@@ -9,7 +9,8 @@ import pytest
 
 import oracle
 import weight_only_int4_group_amd as w4
-from tests.gpu_helpers import assert_close, note, to_dev, to_host, torch_cuda
+from tests.gpu_helpers import (MAX_REL_BF16, REL_L2_BF16, assert_close, note, to_dev, to_host,
+                               torch_cuda)
 from workloads import activations, awq_scales, weights
 
 pytestmark = pytest.mark.gpu
@@ -129,3 +130,38 @@ def test_capture_takes_the_unsplit_path():
         g.replay()
         torch.cuda.synchronize()
         assert np.array_equal(to_host(out).view(np.uint16), want.view(np.uint16)), rep
+
+
+def test_bf16_and_int8_without_workspace_match_workspace_call():
+    """bf16 activations (INT4 codes) and INT8 codes (fp16 activations): the DMA-staged
+    tiled kernels take X * s from the shared scratch when the call has no workspace,
+    with the same bits as the call with one; the outputs match the oracle."""
+    torch = torch_cuda()
+    items, refs = [], []
+    for i, (M, N, K, awq, bf, bits) in enumerate([(64, 528, 4096, True, True, 4),
+                                                  (100, 256, 4096, True, True, 4),
+                                                  (64, 528, 4096, True, False, 8),
+                                                  (100, 48, 18944, False, False, 8)]):
+        W = weights(33, i, N, K)
+        s = awq_scales(33, i, K) if awq else None
+        sd = None if s is None else to_dev(s)
+        pw = w4.w4a16_quantize_pack(to_dev(W), sd, mode=w4.QUANT_ASYM8 if bits == 8 else w4.QUANT_ASYM)
+        Xd = to_dev(activations(33, i, M, K))
+        dt = torch.bfloat16 if bf else torch.float16
+        Xd = Xd.to(dt)
+        items.append((Xd, pw, sd, torch.empty((M, N), dtype=dt, device="cuda")))
+        refs.append((W, s, bits, Xd.float().cpu().numpy().astype(np.float64)))
+    note("shared scratch: bf16 and INT8 grouped call")
+    call = w4.GroupedCall(items)
+    assert call.ws_bytes > 0
+    call()
+    want = [it[3].float().cpu().numpy().copy() for it in items]
+    for it in items:
+        it[3].fill_(float("nan"))
+    w4.GroupedCall(items, workspace=False)()
+    for it, w, (W, s, bits, X) in zip(items, want, refs):
+        got = it[3].float().cpu().numpy()
+        assert np.array_equal(got, w), (it[0].shape, bits)
+        ref = oracle.quantize(W, s, bits=bits)
+        tol = (REL_L2_BF16, MAX_REL_BF16) if it[0].dtype == torch.bfloat16 else ()
+        assert_close(got, oracle.gemm(X, ref.q, ref.scales, ref.zeros, s), f"bits={bits}", *tol)
