@@ -865,7 +865,8 @@ constexpr size_t kMaxStageBytes = 96 * 1024;
 constexpr int kChunk = 4;  // groups per chunk (weight loads in flight per wave)
 constexpr int kWaves = 8;  // waves per workgroup
 // fp16 INT4 calls whose X * s all fit in kWideStageBytes but not all in
-// kMaxStageBytes (the Llama-3-8B layer at M = 4, 5: 143 KB for down) stage
+// kMaxStageBytes (the Llama-3-8B layer at M = 4 and 5: down's rows take 115
+// and 143 KB) stage
 // whole rows in 16-wave workgroups, one per CU: the same waves per CU as two
 // 8-wave workgroups, and no windows (measured 26.1 -> 24.9 us at M = 5).
 // Launches with windows keep 8 waves: 16-wave hybrid launches were slower

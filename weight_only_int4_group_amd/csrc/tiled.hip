@@ -604,27 +604,30 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
   }
 }
 
-// The tiled GEMM for fp16 activations and INT4 codes without outliers, with
-// TM = 8 (128 rows of X per wave) for large M.  The dequantization of a weight
+// The tiled GEMM for INT4 codes without outliers (fp16 or bf16 activations,
+// BF) and for INT8 codes with fp16 activations (W8), with TM = 8 (128 rows of
+// X per wave) for large M.  The dequantization of a weight
 // costs the same VALU work whatever the rows it feeds, so a wave tile of 128
 // rows halves it per MFMA against 64 rows; the registers for that come from
 // moving X * s off the register path:
-//   * X * s (rounded to fp16 once: prescaled into the workspace by
+//   * X * s (rounded to fp16, or bf16, once: prescaled into the workspace by
 //     prescale_f16_kernel when s is given, else X itself) goes straight from
 //     memory into LDS with DMA loads (buffer_load ... lds), one group (128
 //     columns) per stage, double-buffered, one barrier per stage.  A row's 16
 //     chunks of 16 bytes are stored XOR-swizzled (chunk c of row m at c ^ (m %
 //     16)), so the MFMA A-operand reads of 16 rows hit distinct banks without
 //     padding; each DMA lane fetches the chunk that belongs in its slot;
-//   * the wave's code tiles (16 bytes per lane per tile, its MFMA B operands)
-//     and their scales and zero points are loaded into registers one group
-//     ahead, in two register sets that alternate.
+//   * the wave's code tiles (16 bytes per lane per tile, 32 for INT8 codes:
+//     its MFMA B operands) and their scales and zero points are loaded into
+//     registers one group ahead, in two register sets that alternate.
+// The bf16 and INT8 instances cost more registers: they run 64-row tiles up
+// to M = 64 and 96-row tiles above.
 // Blocks are BM x BN (BM = 16 TM, BN = 64 TN), four waves of BM x 16 TN per
 // K slice; K is split across workgroups the same way as in tiled_kernel.
 // Batched decode (M up to 64) takes TN = 2 (and TM = 2, 3 or 4, as few rows
-// as cover M): twice the blocks of TN = 4, so
-// fewer K splits (whose fp32 partials cost HBM traffic) are needed to fill the
-// GPU, and half the accumulators.  Its blocks have one K slice of four waves
+// as cover M): twice the blocks of TN = 4, so fewer K splits (whose fp32
+// partials cost HBM traffic) are needed to fill the GPU, and half the
+// accumulators.  Its blocks have one K slice of four waves
 // or KS = 2: each slice walks every other group of the workgroup's K range
 // into its own X * s stages, and the two sums are added through LDS at the end
 // (slice 0's plus slice 1's, a fixed order).  Two slices double the waves per
@@ -997,8 +1000,9 @@ constexpr int kDmaMinM = 17;
 // exceeds 96, TM = 6, TN = 4 (96 x 256) from 65 to 96 rows, else TN = 2 and
 // the fewest 16-row tiles that cover M (TM = 2, 3 or 4: blocks of 32, 48 or
 // 64 x 128) with one K slice (four waves) or two (eight waves), whichever the
-// launch model below prefers.  Below 64 rows the
-// padded rows' MFMAs and A reads are not free: the Qwen2-7B layer at M = 17
+// launch model below prefers; bf16 activations and INT8 codes take TM = 4 up
+// to 64 rows and TM = 6 above.  Below 64 rows the padded rows' MFMAs and A
+// reads are not free: the Qwen2-7B layer at M = 17
 // took 43 us with 64-row tiles and 34 us with 32-row ones, at M = 33 45 and
 // 42 us with 64- and 48-row ones.  Covering 64 rows with two 32-row tiles
 // instead (each weight read twice) was slower: 62 against 50 us.  At M = 65
@@ -1013,7 +1017,7 @@ long long dma_slots(int tm, int ks) { return tm >= 6 || ks == 2 ? 512 : 1024; }
 
 // 0 when the launch cannot take tiled_dma_kernel, else its TM: the fewest
 // 16-row tiles that cover the largest M among 2, 3, 4, 6 and 8 (32 to 128
-// rows)
+// rows); among 4 and 6 for bf16 activations and INT8 codes
 int dma_tm(const GemmDesc *d, int count) {
   int mmax = 0;
   for (int i = 0; i < count; ++i) {
