@@ -394,7 +394,7 @@ __device__ __forceinline__ void store_rows(const Problem &P, float4v acc, int b,
 
 // Whole-row body: xs (dynamic LDS) holds X * s, then (after the last use of
 // X) the split-K reduction.
-template <int kGW, int kWaves, int kDepth, bool kOut, bool kBF, bool kW8 = false>
+template <int kGW, int kWaves, int kDepth, bool kOut, bool kBF, bool kW8 = false, bool kML = false>
 __device__ __forceinline__ void skinny_body(const ProblemSet &ps, _Float16 *xs) {
   constexpr int kCW = kW8 ? 2 : 1;  // 16-byte code loads per lane per tile
 
@@ -455,23 +455,54 @@ __device__ __forceinline__ void skinny_body(const ProblemSet &ps, _Float16 *xs) 
                                                          min(g0 + i, glast) * tile_stride,
                                                          kW8 ? 0 : kCodeCachePolicy));
   };
+  // kML: the wave's scales and zero points (its range is at most 8 quads, 32
+  // groups, as the launcher checks) come into a 2 KB LDS slab of the wave
+  // with two DMA loads at the start, and each chunk reads its quad there
+  // instead of issuing two loads (the launcher takes this instance when the
+  // slabs cost no workgroup per CU).
+  static_assert(!kML || (kQ == 1 && !kOut && !kBF && !kW8), "LDS metadata: fp16 INT4, one quad per chunk");
+  unsigned char *mlds = nullptr;
+  if constexpr (kML) {
+    const size_t xbytes = (size_t)M * (K + kLdsPad) * sizeof(_Float16);
+    const size_t rbytes = (size_t)kWaves * 16 * 17 * sizeof(float);
+    mlds = reinterpret_cast<unsigned char *>(xs) + ((xbytes > rbytes ? xbytes : rbytes) + 15) / 16 * 16 +
+           wave * 2048;
+    // lane l: quad l / 8 of the range (clamped to the last), 16-byte piece l % 8
+    const int u = min(gb / kMetaQuad + (lane >> 3), Gq - 1);
+    const int off = (u * NB + bb) * 128 + (lane & 7) * 16;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, (__attribute__((address_space(3))) void *)mlds, 16,
+                                             off, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        zrs, (__attribute__((address_space(3))) void *)(mlds + 1024), 16, off, 0, 0, 0);
+  }
   auto load_meta = [&](Meta &mt, int g0) {
+    if constexpr (kML) {
+      const int ql = (min(g0, glast) - gb) / kMetaQuad;
+      const uint2 sv = *reinterpret_cast<const uint2 *>(mlds + ql * 128 + r * 8);
+      const uint2 zv = *reinterpret_cast<const uint2 *>(mlds + 1024 + ql * 128 + r * 8);
+      mt.sq[0] = sv.x;
+      mt.sq[1] = sv.y;
+      mt.zq[0] = zv.x;
+      mt.zq[1] = zv.y;
+    } else {
 #pragma unroll
-    for (int q = 0; q < kQ; ++q) {
-      const int qoff = (min(g0, glast) / kMetaQuad + q) * meta_stride;
-      const auto sv = __builtin_amdgcn_raw_buffer_load_b64(srs, meta_off, qoff, kMetaCachePolicy);
-      const auto zv = __builtin_amdgcn_raw_buffer_load_b64(zrs, meta_off, qoff, kMetaCachePolicy);
-      mt.sq[2 * q] = (uint32_t)sv[0];
-      mt.sq[2 * q + 1] = (uint32_t)sv[1];
-      mt.zq[2 * q] = (uint32_t)zv[0];
-      mt.zq[2 * q + 1] = (uint32_t)zv[1];
+      for (int q = 0; q < kQ; ++q) {
+        const int qoff = (min(g0, glast) / kMetaQuad + q) * meta_stride;
+        const auto sv = __builtin_amdgcn_raw_buffer_load_b64(srs, meta_off, qoff, kMetaCachePolicy);
+        const auto zv = __builtin_amdgcn_raw_buffer_load_b64(zrs, meta_off, qoff, kMetaCachePolicy);
+        mt.sq[2 * q] = (uint32_t)sv[0];
+        mt.sq[2 * q + 1] = (uint32_t)sv[1];
+        mt.zq[2 * q] = (uint32_t)zv[0];
+        mt.zq[2 * q + 1] = (uint32_t)zv[1];
+      }
     }
   };
-  // issue order: outlier row range, meta 0, codes 0, meta 1
+  // issue order: outlier row range, meta 0, codes 0, meta 1 (kML: the
+  // metadata DMA, codes 0)
   const int2 orange = kOut ? outlier_range(P, b, has_rows, ks, r) : int2{0, 0};
-  load_meta(m0, gb);
+  if (!kML) load_meta(m0, gb);
   load_codes(gb);
-  load_meta(m1, gb + kGW);
+  if (!kML) load_meta(m1, gb + kGW);
 
   // stage X * s for rows 0..M-1; lanes of rows m >= M read row M - 1 (rows of
   // the A operand only reach the same rows of D, and those are not stored)
@@ -492,6 +523,11 @@ __device__ __forceinline__ void skinny_body(const ProblemSet &ps, _Float16 *xs) 
       }
     }
     __syncthreads();
+  }
+  if constexpr (kML) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the metadata DMA has landed
+    load_meta(m0, gb);
+    load_meta(m1, gb + kGW);
   }
   OutPrefetch of = {};
   if (kOut) of = outlier_prefetch(P, orange, lane);
@@ -564,10 +600,10 @@ __device__ __forceinline__ void skinny_body(const ProblemSet &ps, _Float16 *xs) 
                                 reinterpret_cast<float (*)[16][17]>(xs), orange, of);
 }
 
-template <int kGW, int kWaves, int kDepth, bool kOut, bool kBF, bool kW8 = false>
+template <int kGW, int kWaves, int kDepth, bool kOut, bool kBF, bool kW8 = false, bool kML = false>
 __global__ __launch_bounds__(kWaves * 64) void skinny_kernel(ProblemSet ps) {
   extern __shared__ __attribute__((aligned(16))) _Float16 xs[];
-  skinny_body<kGW, kWaves, kDepth, kOut, kBF, kW8>(ps, xs);
+  skinny_body<kGW, kWaves, kDepth, kOut, kBF, kW8, kML>(ps, xs);
 }
 
 // bf16 X * s and its per-group sums, once per call, for the windowed kernel
@@ -872,6 +908,17 @@ constexpr int kWaves = 8;  // waves per workgroup
 // Launches with windows keep 8 waves: 16-wave hybrid launches were slower
 // (M = 9: 26.9 -> 31.5 us; Qwen2-7B M = 16: 32.1 -> 37.3 us).
 constexpr int kWideWaves = 16;
+// LDS metadata slabs of the whole-row kernel: 2 KB per wave (8 quads of
+// scales and zero points, 32 groups), taken when they cost no workgroup per
+// CU: the kernel's registers allow three 8-wave workgroups, LDS 160 KB
+constexpr int kMetaSlabChunks = 8;
+constexpr size_t kMetaSlabBytes = (size_t)kWaves * 2048;
+constexpr size_t kCuLdsBytes = 160 * 1024;
+constexpr size_t kWholeWgsPerCu = 3;
+size_t wgs_per_cu(size_t lds) {
+  const size_t by_lds = lds ? kCuLdsBytes / lds : kWholeWgsPerCu;
+  return by_lds < kWholeWgsPerCu ? by_lds : kWholeWgsPerCu;
+}
 constexpr size_t kWideStageBytes = 150 * 1024;
 constexpr int kDepth = 1;  // chunks in flight per wave
 // 1: window the problems whose X * s does not fit, 2: always window, 3:
@@ -991,6 +1038,7 @@ hipError_t launch_group(const GemmDesc *const *d, int count, LaunchKind kind, hi
   int blocks = 0;
   size_t lds = 0;
   bool out = false;  // some problem has fp16 outliers
+  bool meta_fits = true;  // every wave's groups fit an LDS metadata slab
   const bool window = kind == kWindowed;
   // bf16 with prescaled X * s: all or none of a launch (launch_skinny_set)
   const bool pre = window && d[0]->bf16 && d[0]->xpre != nullptr;
@@ -1038,8 +1086,18 @@ hipError_t launch_group(const GemmDesc *const *d, int count, LaunchKind kind, hi
     const size_t red = (size_t)waves * 16 * 17 * sizeof(float), sb = stage_bytes(q.M, q.K, q.bf16);
     const size_t need = win ? (wlds > red ? wlds : red) : (sb > red ? sb : red);
     lds = need > lds ? need : lds;
+    meta_fits &= ((G + kChunk - 1) / kChunk + split - 1) / split <= kMetaSlabChunks;
   }
   ps.count = count;
+  // whole rows, fp16 INT4 codes without outliers: each wave's scales and zero
+  // points in an LDS slab when every wave's range fits one and the slabs cost
+  // no workgroup per CU (measured 22.72 -> 22.52 us on the 8B layer at M = 1
+  // and 23.0 -> 22.7 us at M = 2; slabs that cost a workgroup per CU made the
+  // M = 9 verify launch slower, 28.1 -> 31.8 us)
+  const size_t lds_ml = (lds + 15) / 16 * 16 + kMetaSlabBytes;
+  const bool ml = kind == kWhole && waves == kWaves && !d[0]->bf16 && !d[0]->w8 && !out &&
+                  meta_fits && wgs_per_cu(lds_ml) == wgs_per_cu(lds);
+  if (ml) lds = lds_ml;
   const dim3 grid(blocks), threads(waves * 64);
   const bool bf = d[0]->bf16;  // one activation type (and code width) per launch
   if (waves == kWideWaves) {
@@ -1096,6 +1154,9 @@ hipError_t launch_group(const GemmDesc *const *d, int count, LaunchKind kind, hi
     else if (out)
       hipLaunchKernelGGL((skinny_kernel<kChunk, kWaves, kDepth, true, false>), grid, threads, lds,
                          stream, ps);
+    else if (ml)
+      hipLaunchKernelGGL((skinny_kernel<kChunk, kWaves, kDepth, false, false, false, true>), grid,
+                         threads, lds, stream, ps);
     else
       hipLaunchKernelGGL((skinny_kernel<kChunk, kWaves, kDepth, false, false>), grid, threads, lds,
                          stream, ps);
