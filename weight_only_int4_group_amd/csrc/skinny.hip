@@ -21,7 +21,8 @@
 //   * turns each 32-bit word into the exact fp16 values (q - z) in nine ALU
 //     ops -- that register is the lane's 16x16x32 MFMA B operand,
 //   * multiplies by X * s (staged in LDS once per workgroup, rounded to fp16
-//     once; rows m >= M read an all-zero LDS row) with four MFMAs, and
+//     once; lanes of rows m >= M read row M - 1, whose products only reach
+//     rows of Y that are not stored) with four MFMAs, and
 //   * folds the group's fp32 dot products into the accumulator times the group
 //     scale, in fp32.
 // When S > 1 the S partial sums of a row block are added in a fixed order
@@ -32,10 +33,16 @@
 // workgroup walks K in windows instead.  A window is S chunks: the S waves of
 // a row block take one chunk each, all row blocks of the workgroup share the
 // window, and the next window's X * s is loaded into registers while the
-// current one is multiplied, then written over it between two LDS barriers.
-// A call whose fp16 problems are of both kinds (speculative verify: the down
-// projection's long rows do not fit, the others do) runs as one launch in
-// which each workgroup stages its problem's X * s the way it fits.
+// current one is multiplied.  When two windows fit, they alternate between two
+// LDS buffers (one barrier per window); otherwise the next one is written over
+// the current one between two barriers.  A call whose fp16 problems are of
+// both kinds (speculative verify: the down projection's long rows do not fit,
+// the others do) runs as one launch in which each workgroup stages its
+// problem's X * s the way it fits.  Calls whose rows all fit a larger stage
+// than two workgroups per CU allow run whole rows in 16-wave workgroups, one
+// per CU, instead of windows.  Whole-row launches without outliers keep each
+// wave's scales and zero points in an LDS slab when that costs no workgroup
+// per CU.
 #include "w4a16_device.h"
 #include "w4a16_internal.h"
 

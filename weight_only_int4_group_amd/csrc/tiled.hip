@@ -1004,9 +1004,10 @@ constexpr int kDmaMinM = 17;
 // tiles up to 64 rows and TM = 6 above.  Below 64 rows the padded rows'
 // MFMAs and A reads are not free: the Qwen2-7B layer at M = 17 took 43 us
 // with 64-row tiles and 34 us with 32-row ones (bf16: 54 and 47 us; INT8
-// codes: 52 and 49 us), at M = 33 45 and 42 us with 64- and 48-row ones.  Covering 64 rows with two 32-row tiles
-// instead (each weight read twice) was slower: 62 against 50 us.  At M = 65
-// 96-row tiles took 62 against 69 us with 128-row ones.
+// codes: 52 and 49 us), at M = 33 45 and 42 us with 64- and 48-row ones.
+// Covering 64 rows with two 32-row tiles instead (each weight read twice) was
+// slower: 62 against 50 us.  At M = 65 96-row tiles took 62 against 69 us
+// with 128-row ones.
 struct DmaShape {
   int tm, tn;
   int bm() const { return 16 * tm; }
