@@ -178,9 +178,8 @@ __device__ __forceinline__ u32x4 scale_x8(u32x4 xw, const _Float16 *s8, float &s
   for (int q = 0; q < 4; ++q) {
     const float lo = bf16_to_f32((uint16_t)xw[q]) * (float)sv[2 * q];
     const float hi = bf16_to_f32((uint16_t)(xw[q] >> 16)) * (float)sv[2 * q + 1];
-    const uint16_t l16 = f32_to_bf16(lo), h16 = f32_to_bf16(hi);
-    out[q] = (uint32_t)l16 | ((uint32_t)h16 << 16);
-    sum += bf16_to_f32(l16) + bf16_to_f32(h16);
+    out[q] = pack_bf16x2(lo, hi);
+    sum += bf16_to_f32((uint16_t)out[q]) + bf16_to_f32((uint16_t)(out[q] >> 16));
   }
   return out;
 }
@@ -769,9 +768,8 @@ __device__ __forceinline__ void skinny_window_body(const ProblemSet &ps, _Float1
           const uint32_t xw = __builtin_bit_cast(u32x4, xr[i])[q];
           const float lo = bf16_to_f32((uint16_t)xw) * (float)sv[2 * q];
           const float hi = bf16_to_f32((uint16_t)(xw >> 16)) * (float)sv[2 * q + 1];
-          const uint16_t l16 = f32_to_bf16(lo), h16 = f32_to_bf16(hi);
-          out[q] = (uint32_t)l16 | ((uint32_t)h16 << 16);
-          part += bf16_to_f32(l16) + bf16_to_f32(h16);
+          out[q] = pack_bf16x2(lo, hi);
+          part += bf16_to_f32((uint16_t)out[q]) + bf16_to_f32((uint16_t)(out[q] >> 16));
         }
         part = segment_sum16(part);  // all 16 lanes of the segment share m
         if (m < M) {

@@ -79,7 +79,7 @@ __device__ __forceinline__ u32x4 dequant_word_bf16(uint32_t w, float scale, floa
     const uint32_t x = and_or(w >> (4 * p), m, kMagicBF);
     const float lo = __builtin_fmaf(__builtin_bit_cast(float, x << 16), scale, -zb);
     const float hi = __builtin_fmaf(__builtin_bit_cast(float, x & 0xFFFF0000u), scale, -zb);
-    r[p] = (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+    r[p] = pack_bf16x2(lo, hi);
   }
   return r;
 }
@@ -109,7 +109,7 @@ __device__ __forceinline__ u32x4 dequant_words8_bf16(uint32_t wa, uint32_t wb, f
     const int sh = (p & 1) * 16;
     const float lo = __builtin_fmaf((float)((w >> sh) & 0xFFu), scale, -zs);
     const float hi = __builtin_fmaf((float)((w >> (sh + 8)) & 0xFFu), scale, -zs);
-    r[p] = (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+    r[p] = pack_bf16x2(lo, hi);
   }
   return r;
 }
@@ -255,7 +255,7 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
         for (int q = 0; q < 4; ++q) {
           const float lo = bf16_to_f32((uint16_t)xw[q]) * (float)sreg[2 * q];
           const float hi = bf16_to_f32((uint16_t)(xw[q] >> 16)) * (float)sreg[2 * q + 1];
-          v[q] = (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+          v[q] = pack_bf16x2(lo, hi);
         }
       } else {
         v = __builtin_bit_cast(u32x4, areg[i] * sreg);
@@ -928,7 +928,7 @@ __global__ __launch_bounds__(256) void prescale_f16_kernel(PrescaleSet ps) {
     for (int q = 0; q < 4; ++q) {
       const float lo = bf16_to_f32((uint16_t)xw[q]) * (float)s8[2 * q];
       const float hi = bf16_to_f32((uint16_t)(xw[q] >> 16)) * (float)s8[2 * q + 1];
-      v[q] = (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+      v[q] = pack_bf16x2(lo, hi);
     }
     *reinterpret_cast<u32x4 *>(out + e) = v;
   } else {

@@ -94,6 +94,14 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {  // round to nearest even
   return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
+// Two floats to a bf16 pair (lo in the low half), each rounded to nearest
+// even: one v_cvt_pk_bf16_f32, where two scalar conversions and a merge would
+// take three instructions.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float float2x __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((float2x){lo, hi}, bf16x2));
+}
 
 // bf16 128.0 in both halves: OR-ing a 4-bit code q into the low mantissa bits
 // gives the exact bf16 value 128 + q
