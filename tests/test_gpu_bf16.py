@@ -37,7 +37,9 @@ def check(Y, ref, tag):
     (17, 1024, 2048, True),      # tiled, ragged M
     (64, 4096, 4096, True),      # tiled, split K
     (65, 272, 640, True),        # tiled, 96-row tiles at their lower edge
-    (97, 528, 18944, True),      # tiled, 96-row tiles, ragged M, split K
+    (97, 528, 18944, True),      # tiled, 128-row tiles at their lower edge, split K
+    (130, 528, 4096, True),      # tiled, 128-row tiles, ragged M across two tiles
+    (257, 272, 2048, False),     # tiled, 128-row tiles, three M blocks, ragged
     (300, 1296, 1536, False),    # tiled, ragged M and N
 ])
 def test_bf16_matches_oracle(M, N, K, awq):

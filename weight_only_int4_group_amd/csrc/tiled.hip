@@ -620,8 +620,10 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
 //   * the wave's code tiles (16 bytes per lane per tile, 32 for INT8 codes:
 //     its MFMA B operands) and their scales and zero points are loaded into
 //     registers one group ahead, in two register sets that alternate.
-// The bf16 and INT8 instances cost more registers: above M = 64 they run
-// 96-row tiles.
+// The INT8 instances cost more registers: above M = 64 they run 96-row
+// tiles.  The 128-row bf16 instance fits in 256 VGPRs because each pair of
+// bf16 weights comes from one packed conversion (pack_bf16x2); with two
+// scalar conversions and a merge it spilled.
 // Blocks are BM x BN (BM = 16 TM, BN = 64 TN), four waves of BM x 16 TN per
 // K slice; K is split across workgroups the same way as in tiled_kernel.
 // Batched decode (M up to 64) takes TN = 2 (and TM = 2, 3 or 4, as few rows
@@ -1000,8 +1002,10 @@ constexpr int kDmaMinM = 17;
 // exceeds 96, TM = 6, TN = 4 (96 x 256) from 65 to 96 rows, else TN = 2 and
 // the fewest 16-row tiles that cover M (TM = 2, 3 or 4: blocks of 32, 48 or
 // 64 x 128) with one K slice (four waves) or two (eight waves), whichever the
-// launch model below prefers; bf16 activations and INT8 codes take the same
-// tiles up to 64 rows and TM = 6 above.  Below 64 rows the padded rows'
+// launch model below prefers; INT8 codes take the same tiles up to 64 rows
+// and TM = 6 above, bf16 activations all of them (the 70B prefill layer ran
+// at 898-918 TFLOP/s with 96-row bf16 tiles and 1090-1102 with 128-row ones).
+// Below 64 rows the padded rows'
 // MFMAs and A reads are not free: the Qwen2-7B layer at M = 17 took 43 us
 // with 64-row tiles and 34 us with 32-row ones (bf16: 54 and 47 us; INT8
 // codes: 52 and 49 us), at M = 33 45 and 42 us with 64- and 48-row ones.
@@ -1018,7 +1022,7 @@ long long dma_slots(int tm, int ks) { return tm >= 6 || ks == 2 ? 512 : 1024; }
 
 // 0 when the launch cannot take tiled_dma_kernel, else its TM: the fewest
 // 16-row tiles that cover the largest M among 2, 3, 4, 6 and 8 (32 to 128
-// rows); bf16 activations and INT8 codes take TM = 6 above 64 rows
+// rows); INT8 codes take TM = 6 above 64 rows
 int dma_tm(const GemmDesc *d, int count) {
   int mmax = 0;
   for (int i = 0; i < count; ++i) {
@@ -1026,7 +1030,8 @@ int dma_tm(const GemmDesc *d, int count) {
     mmax = std::max(mmax, d[i].M);
   }
   if (mmax < kDmaMinM) return 0;
-  if (d[0].bf16 || d[0].w8) return mmax > 64 ? 6 : mmax > 48 ? 4 : mmax > 32 ? 3 : 2;
+  if (d[0].w8) return mmax > 64 ? 6 : mmax > 48 ? 4 : mmax > 32 ? 3 : 2;
+  if (d[0].bf16) return mmax > 96 ? 8 : mmax > 64 ? 6 : mmax > 48 ? 4 : mmax > 32 ? 3 : 2;
   return mmax > 96 ? 8 : mmax > 64 ? 6 : mmax > 48 ? 4 : mmax > 32 ? 3 : 2;
 }
 bool dma_launch(const GemmDesc *d, int count) { return dma_tm(d, count) != 0; }
@@ -1250,6 +1255,8 @@ hipError_t launch_tiled_set(const GemmDesc *d, int count, void *workspace, size_
     hipLaunchKernelGGL((tiled_dma_kernel<4, 2, 2, false, true>), grid, dim3(512), 0, stream, ts);
   else if (dma && d[0].w8)
     hipLaunchKernelGGL((tiled_dma_kernel<4, 2, 1, false, true>), grid, dim3(256), 0, stream, ts);
+  else if (dma && d[0].bf16 && tm == 8)
+    hipLaunchKernelGGL((tiled_dma_kernel<8, 4, 1, true>), grid, dim3(256), 0, stream, ts);
   else if (dma && d[0].bf16 && tm == 6)
     hipLaunchKernelGGL((tiled_dma_kernel<6, 4, 1, true>), grid, dim3(256), 0, stream, ts);
   else if (dma && d[0].bf16 && tm == 2 && ks == 2)
