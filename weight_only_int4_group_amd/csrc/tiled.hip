@@ -27,6 +27,7 @@
 // kernel adds the splits in a fixed order and rounds to fp16 once, so results
 // are reproducible run to run.
 #include <algorithm>
+#include <type_traits>
 
 #include "w4a16_device.h"
 #include "w4a16_internal.h"
@@ -35,6 +36,7 @@ namespace w4a16 {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kRsrcWord3 = 0x00020000;      // raw buffer resource, 32-bit data format
 
@@ -620,10 +622,10 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
 //   * the wave's code tiles (16 bytes per lane per tile, 32 for INT8 codes:
 //     its MFMA B operands) and their scales and zero points are loaded into
 //     registers one group ahead, in two register sets that alternate.
-// The INT8 instances cost more registers: above M = 64 they run 96-row
-// tiles.  The 128-row bf16 instance fits in 256 VGPRs because each pair of
-// bf16 weights comes from one packed conversion (pack_bf16x2); with two
-// scalar conversions and a merge it spilled.
+// The bf16 and INT8 instances cost more registers; their 128-row tiles fit
+// in 256 VGPRs because each pair of bf16 weights comes from one packed
+// conversion (pack_bf16x2) and INT8 codes keep a row block's scale and zero
+// point in one register (otherwise both spilled).
 // Blocks are BM x BN (BM = 16 TM, BN = 64 TN), four waves of BM x 16 TN per
 // K slice; K is split across workgroups the same way as in tiled_kernel.
 // Batched decode (M up to 64) takes TN = 2 (and TM = 2, 3 or 4, as few rows
@@ -716,10 +718,18 @@ __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(TN == 
       (void *)P.zeros, (short)0, (int)min((size_t)0x7fffffff, meta_bytes), kRsrcWord3);
   const int rb0 = n0 / kTileRows + wave * TN;
   const int tile_stride = NB * kTileBytes * kCW, meta_stride = NB * kTileRows * kMetaQuad * 2;
-  struct BStage {
+  // raw fp16 bits of each row block's scale and zero point: INT8 codes keep
+  // both in one register (x: scale, y: zero point), which leaves the 128-row
+  // instance within 256 VGPRs
+  struct BStagePair {
     u32x4 code[TN][kCW];
-    uint32_t sc[TN], zp[TN];  // raw fp16 bits of each row block's scale and zero point
+    uint32_t sc[TN], zp[TN];
   };
+  struct BStagePacked {
+    u32x4 code[TN][kCW];
+    u16x2 sz[TN];
+  };
+  using BStage = std::conditional_t<W8, BStagePacked, BStagePair>;
   auto load_b = [&](int g, BStage &b) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
@@ -731,8 +741,13 @@ __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(TN == 
                                                          g * tile_stride, 0));
       const int mo = (rb * kTileRows + r) * kMetaQuad * 2;
       const int qo = (g / kMetaQuad) * meta_stride + (g % kMetaQuad) * 2;
-      b.sc[j] = __builtin_amdgcn_raw_buffer_load_b16(srs, mo, qo, 0);
-      b.zp[j] = __builtin_amdgcn_raw_buffer_load_b16(zrs, mo, qo, 0);
+      if constexpr (W8) {
+        b.sz[j][0] = __builtin_amdgcn_raw_buffer_load_b16(srs, mo, qo, 0);
+        b.sz[j][1] = __builtin_amdgcn_raw_buffer_load_b16(zrs, mo, qo, 0);
+      } else {
+        b.sc[j] = __builtin_amdgcn_raw_buffer_load_b16(srs, mo, qo, 0);
+        b.zp[j] = __builtin_amdgcn_raw_buffer_load_b16(zrs, mo, qo, 0);
+      }
     }
   };
 
@@ -749,8 +764,16 @@ __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(TN == 
     float fsc[TN], fzb[TN];  // bf16: the fp32 scale and (128 + z) * scale
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      const _Float16 z = __builtin_bit_cast(_Float16, (uint16_t)b.zp[j]);
-      const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)b.sc[j]);
+      uint16_t zr, sr;
+      if constexpr (W8) {
+        sr = b.sz[j][0];
+        zr = b.sz[j][1];
+      } else {
+        sr = (uint16_t)b.sc[j];
+        zr = (uint16_t)b.zp[j];
+      }
+      const _Float16 z = __builtin_bit_cast(_Float16, zr);
+      const _Float16 sv = __builtin_bit_cast(_Float16, sr);
       if (BF) {
         fsc[j] = (float)sv;
         fzb[j] = (128.0f + (float)z) * fsc[j];
@@ -1002,10 +1025,10 @@ constexpr int kDmaMinM = 17;
 // exceeds 96, TM = 6, TN = 4 (96 x 256) from 65 to 96 rows, else TN = 2 and
 // the fewest 16-row tiles that cover M (TM = 2, 3 or 4: blocks of 32, 48 or
 // 64 x 128) with one K slice (four waves) or two (eight waves), whichever the
-// launch model below prefers; INT8 codes take the same tiles up to 64 rows
-// and TM = 6 above, bf16 activations all of them (the 70B prefill layer ran
-// at 898-918 TFLOP/s with 96-row bf16 tiles and 1090-1102 with 128-row ones).
-// Below 64 rows the padded rows'
+// launch model below prefers; bf16 activations and INT8 codes take the same
+// tiles (the 70B prefill layer with bf16 activations ran at 898-918 TFLOP/s
+// with 96-row tiles and 1090-1102 with 128-row ones; with INT8 codes at
+// 941-944 and 1073-1076).  Below 64 rows the padded rows'
 // MFMAs and A reads are not free: the Qwen2-7B layer at M = 17 took 43 us
 // with 64-row tiles and 34 us with 32-row ones (bf16: 54 and 47 us; INT8
 // codes: 52 and 49 us), at M = 33 45 and 42 us with 64- and 48-row ones.
@@ -1022,7 +1045,7 @@ long long dma_slots(int tm, int ks) { return tm >= 6 || ks == 2 ? 512 : 1024; }
 
 // 0 when the launch cannot take tiled_dma_kernel, else its TM: the fewest
 // 16-row tiles that cover the largest M among 2, 3, 4, 6 and 8 (32 to 128
-// rows); INT8 codes take TM = 6 above 64 rows
+// rows)
 int dma_tm(const GemmDesc *d, int count) {
   int mmax = 0;
   for (int i = 0; i < count; ++i) {
@@ -1030,8 +1053,6 @@ int dma_tm(const GemmDesc *d, int count) {
     mmax = std::max(mmax, d[i].M);
   }
   if (mmax < kDmaMinM) return 0;
-  if (d[0].w8) return mmax > 64 ? 6 : mmax > 48 ? 4 : mmax > 32 ? 3 : 2;
-  if (d[0].bf16) return mmax > 96 ? 8 : mmax > 64 ? 6 : mmax > 48 ? 4 : mmax > 32 ? 3 : 2;
   return mmax > 96 ? 8 : mmax > 64 ? 6 : mmax > 48 ? 4 : mmax > 32 ? 3 : 2;
 }
 bool dma_launch(const GemmDesc *d, int count) { return dma_tm(d, count) != 0; }
@@ -1130,6 +1151,32 @@ int dma_plan(const GemmDesc *d, int count, int tm, bool unsplit, int *split) {
     }
   }
   return best_ks;
+}
+
+// The tiled_dma_kernel instance of a DMA plan (dma_tm's TM, dma_plan's K
+// slices) for one activation type and code width; any other shape is an
+// error, never a launch with a grid planned for another tile.
+template <bool BF, bool W8>
+hipError_t launch_dma(int tm, int ks, dim3 grid, hipStream_t stream, const TiledSet &ts) {
+  if (tm == 8 && ks == 1)
+    hipLaunchKernelGGL((tiled_dma_kernel<8, 4, 1, BF, W8>), grid, dim3(256), 0, stream, ts);
+  else if (tm == 6 && ks == 1)
+    hipLaunchKernelGGL((tiled_dma_kernel<6, 4, 1, BF, W8>), grid, dim3(256), 0, stream, ts);
+  else if (tm == 4 && ks == 2)
+    hipLaunchKernelGGL((tiled_dma_kernel<4, 2, 2, BF, W8>), grid, dim3(512), 0, stream, ts);
+  else if (tm == 4 && ks == 1)
+    hipLaunchKernelGGL((tiled_dma_kernel<4, 2, 1, BF, W8>), grid, dim3(256), 0, stream, ts);
+  else if (tm == 3 && ks == 2)
+    hipLaunchKernelGGL((tiled_dma_kernel<3, 2, 2, BF, W8>), grid, dim3(512), 0, stream, ts);
+  else if (tm == 3 && ks == 1)
+    hipLaunchKernelGGL((tiled_dma_kernel<3, 2, 1, BF, W8>), grid, dim3(256), 0, stream, ts);
+  else if (tm == 2 && ks == 2)
+    hipLaunchKernelGGL((tiled_dma_kernel<2, 2, 2, BF, W8>), grid, dim3(512), 0, stream, ts);
+  else if (tm == 2 && ks == 1)
+    hipLaunchKernelGGL((tiled_dma_kernel<2, 2, 1, BF, W8>), grid, dim3(256), 0, stream, ts);
+  else
+    return hipErrorInvalidValue;
+  return hipSuccess;
 }
 
 }  // namespace
@@ -1241,53 +1288,12 @@ hipError_t launch_tiled_set(const GemmDesc *d, int count, void *workspace, size_
     if (e != hipSuccess) return e;
   }
   const dim3 grid(blocks), threads(kWM * kWN * 64);
-  if (dma && d[0].w8 && tm == 6)
-    hipLaunchKernelGGL((tiled_dma_kernel<6, 4, 1, false, true>), grid, dim3(256), 0, stream, ts);
-  else if (dma && d[0].w8 && tm == 2 && ks == 2)
-    hipLaunchKernelGGL((tiled_dma_kernel<2, 2, 2, false, true>), grid, dim3(512), 0, stream, ts);
-  else if (dma && d[0].w8 && tm == 2)
-    hipLaunchKernelGGL((tiled_dma_kernel<2, 2, 1, false, true>), grid, dim3(256), 0, stream, ts);
-  else if (dma && d[0].w8 && tm == 3 && ks == 2)
-    hipLaunchKernelGGL((tiled_dma_kernel<3, 2, 2, false, true>), grid, dim3(512), 0, stream, ts);
-  else if (dma && d[0].w8 && tm == 3)
-    hipLaunchKernelGGL((tiled_dma_kernel<3, 2, 1, false, true>), grid, dim3(256), 0, stream, ts);
-  else if (dma && d[0].w8 && ks == 2)
-    hipLaunchKernelGGL((tiled_dma_kernel<4, 2, 2, false, true>), grid, dim3(512), 0, stream, ts);
-  else if (dma && d[0].w8)
-    hipLaunchKernelGGL((tiled_dma_kernel<4, 2, 1, false, true>), grid, dim3(256), 0, stream, ts);
-  else if (dma && d[0].bf16 && tm == 8)
-    hipLaunchKernelGGL((tiled_dma_kernel<8, 4, 1, true>), grid, dim3(256), 0, stream, ts);
-  else if (dma && d[0].bf16 && tm == 6)
-    hipLaunchKernelGGL((tiled_dma_kernel<6, 4, 1, true>), grid, dim3(256), 0, stream, ts);
-  else if (dma && d[0].bf16 && tm == 2 && ks == 2)
-    hipLaunchKernelGGL((tiled_dma_kernel<2, 2, 2, true>), grid, dim3(512), 0, stream, ts);
-  else if (dma && d[0].bf16 && tm == 2)
-    hipLaunchKernelGGL((tiled_dma_kernel<2, 2, 1, true>), grid, dim3(256), 0, stream, ts);
-  else if (dma && d[0].bf16 && tm == 3 && ks == 2)
-    hipLaunchKernelGGL((tiled_dma_kernel<3, 2, 2, true>), grid, dim3(512), 0, stream, ts);
-  else if (dma && d[0].bf16 && tm == 3)
-    hipLaunchKernelGGL((tiled_dma_kernel<3, 2, 1, true>), grid, dim3(256), 0, stream, ts);
-  else if (dma && d[0].bf16 && ks == 2)
-    hipLaunchKernelGGL((tiled_dma_kernel<4, 2, 2, true>), grid, dim3(512), 0, stream, ts);
-  else if (dma && d[0].bf16)
-    hipLaunchKernelGGL((tiled_dma_kernel<4, 2, 1, true>), grid, dim3(256), 0, stream, ts);
-  else if (dma && tm == 8)
-    hipLaunchKernelGGL((tiled_dma_kernel<8, 4, 1>), grid, dim3(256), 0, stream, ts);
-  else if (dma && tm == 6)
-    hipLaunchKernelGGL((tiled_dma_kernel<6, 4, 1>), grid, dim3(256), 0, stream, ts);
-  else if (dma && tm == 2 && ks == 2)
-    hipLaunchKernelGGL((tiled_dma_kernel<2, 2, 2>), grid, dim3(512), 0, stream, ts);
-  else if (dma && tm == 2)
-    hipLaunchKernelGGL((tiled_dma_kernel<2, 2, 1>), grid, dim3(256), 0, stream, ts);
-  else if (dma && tm == 3 && ks == 2)
-    hipLaunchKernelGGL((tiled_dma_kernel<3, 2, 2>), grid, dim3(512), 0, stream, ts);
-  else if (dma && tm == 3)
-    hipLaunchKernelGGL((tiled_dma_kernel<3, 2, 1>), grid, dim3(256), 0, stream, ts);
-  else if (dma && ks == 2)
-    hipLaunchKernelGGL((tiled_dma_kernel<4, 2, 2>), grid, dim3(512), 0, stream, ts);
-  else if (dma)
-    hipLaunchKernelGGL((tiled_dma_kernel<4, 2, 1>), grid, dim3(256), 0, stream, ts);
-  else if (d[0].w8 && d[0].bf16 && out)  // INT8 codes
+  if (dma) {
+    const hipError_t e = d[0].w8     ? launch_dma<false, true>(tm, ks, grid, stream, ts)
+                         : d[0].bf16 ? launch_dma<true, false>(tm, ks, grid, stream, ts)
+                                     : launch_dma<false, false>(tm, ks, grid, stream, ts);
+    if (e != hipSuccess) return e;
+  } else if (d[0].w8 && d[0].bf16 && out)  // INT8 codes
     hipLaunchKernelGGL((tiled_kernel<kWM, kWN, kTM, kTN, true, true, true>), grid, threads, 0,
                        stream, ts);
   else if (d[0].w8 && d[0].bf16)
