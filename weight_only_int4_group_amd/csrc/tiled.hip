@@ -895,6 +895,41 @@ __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(TN == 
 
   // lane holds D[4c + v][r] of each 16x16 sub-block: the output, or this
   // split's fp32 partial
+  if constexpr (TM <= 4) {
+    // Small tiles (the epilogue is a larger share of the work): buffer
+    // stores through a resource that starts at the block's first row and ends
+    // at row M, so rows past M are dropped by the hardware's range check and
+    // no element needs a branch or a 64-bit address (offsets within a block
+    // stay below 2^31); a 16-column block lies inside N or outside it as a
+    // whole (N is a multiple of 16), a uniform test.
+    const bool split = P.split > 1;
+    const int esize = split ? 4 : 2;
+    char *out = split ? reinterpret_cast<char *>(P.part + (size_t)sp * M * N + (size_t)m0 * N)
+                      : reinterpret_cast<char *>(P.Y) + (size_t)m0 * N * 2;
+    const __amdgpu_buffer_rsrc_t yrs = __builtin_amdgcn_make_buffer_rsrc(
+        out, (short)0, (int)min((size_t)(M - m0) * N * esize, (size_t)0x7fffffff), kRsrcWord3);
+    auto store_all = [&](auto &&store) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int nb = n0 + (wave * TN + j) * 16;
+        if (nb >= N) continue;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) store((i * 16 + 4 * c + v) * N + nb + r, acc[i][j][v]);
+      }
+    };
+    if (split)
+      store_all([&](int e, float a) {
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, a), yrs, e * 4, 0, 0);
+      });
+    else
+      store_all([&](int e, float a) {
+        __builtin_amdgcn_raw_buffer_store_b16(
+            BF ? f32_to_bf16(a) : __builtin_bit_cast(uint16_t, (_Float16)a), yrs, e * 2, 0, 0);
+      });
+    return;
+  }
   float *part = P.split > 1 ? P.part + (size_t)sp * M * N : nullptr;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
