@@ -35,6 +35,7 @@ def check(Y, ref, tag):
     (9, 1024, 14336, True),      # streaming, K windows
     (16, 2048, 4096, True),      # streaming, K windows
     (17, 1024, 2048, True),      # tiled, ragged M
+    (40, 528, 2048, True),       # tiled, 48-row tiles
     (64, 4096, 4096, True),      # tiled, split K
     (65, 272, 640, True),        # tiled, 96-row tiles at their lower edge
     (97, 528, 18944, True),      # tiled, 128-row tiles at their lower edge, split K

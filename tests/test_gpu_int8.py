@@ -89,7 +89,7 @@ def gemm8(X, pw, s):
 
 
 @pytest.mark.parametrize("awq", [False, True])
-@pytest.mark.parametrize("M", [1, 2, 5, 9, 16, 17, 40, 64, 129, 300])
+@pytest.mark.parametrize("M", [1, 2, 5, 9, 16, 17, 40, 64, 80, 129, 300])
 def test_gemm_int8_matches_oracle(M, awq):
     N, K = 272, 640
     pw, s, ref = case(N, K, awq)
