@@ -431,7 +431,9 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2,
   auto apply_entry = [&](int j, int col, float val, int g, int buf) {
     const int kk = col - g * kGroup;
     if (kk >= 0) {
-      const float vs = has_s ? val / (float)Ss[OUT ? buf : 0][kk] : val;
+      // the staged X * s times val / s: the hardware reciprocal (about 1 ulp of
+      // fp32, far below the fp16 rounding of X * s) instead of a full division
+      const float vs = has_s ? val * __builtin_amdgcn_rcpf((float)Ss[OUT ? buf : 0][kk]) : val;
       const _Float16 *xb = As[buf] + (wm * TM * 16 + 4 * c) * kLdsStride + kk;
 #pragma unroll
       for (int i = 0; i < TM; ++i)
