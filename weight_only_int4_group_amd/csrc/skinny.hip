@@ -466,10 +466,11 @@ __device__ __forceinline__ void skinny_body(const ProblemSet &ps, _Float16 *xs) 
   // with two DMA loads at the start, and each chunk reads its quad there
   // instead of issuing two loads (the launcher takes this instance when the
   // slabs cost no workgroup per CU).
-  static_assert(!kML || (kQ == 1 && !kOut && !kBF && !kW8), "LDS metadata: fp16 INT4, one quad per chunk");
+  static_assert(!kML || (kQ == 1 && !kOut && !kW8), "LDS metadata: INT4 codes, one quad per chunk");
   unsigned char *mlds = nullptr;
   if constexpr (kML) {
-    const size_t xbytes = (size_t)M * (K + kLdsPad) * sizeof(_Float16);
+    // after X * s (and, bf16, its group sums) or the reduction's partial sums
+    const size_t xbytes = (size_t)M * (K + kLdsPad) * sizeof(_Float16) + (kBF ? (size_t)M * G * 4 : 0);
     const size_t rbytes = (size_t)kWaves * 16 * 17 * sizeof(float);
     mlds = reinterpret_cast<unsigned char *>(xs) + ((xbytes > rbytes ? xbytes : rbytes) + 15) / 16 * 16 +
            wave * 2048;
@@ -1094,13 +1095,13 @@ hipError_t launch_group(const GemmDesc *const *d, int count, LaunchKind kind, hi
     meta_fits &= ((G + kChunk - 1) / kChunk + split - 1) / split <= kMetaSlabChunks;
   }
   ps.count = count;
-  // whole rows, fp16 INT4 codes without outliers: each wave's scales and zero
+  // whole rows, INT4 codes without outliers: each wave's scales and zero
   // points in an LDS slab when every wave's range fits one and the slabs cost
   // no workgroup per CU (measured 22.72 -> 22.52 us on the 8B layer at M = 1
   // and 23.0 -> 22.7 us at M = 2; slabs that cost a workgroup per CU made the
   // M = 9 verify launch slower, 28.1 -> 31.8 us)
   const size_t lds_ml = (lds + 15) / 16 * 16 + kMetaSlabBytes;
-  const bool ml = kind == kWhole && waves == kWaves && !d[0]->bf16 && !d[0]->w8 && !out &&
+  const bool ml = kind == kWhole && waves == kWaves && !d[0]->w8 && !out &&
                   meta_fits && wgs_per_cu(lds_ml) == wgs_per_cu(lds);
   if (ml) lds = lds_ml;
   const dim3 grid(blocks), threads(waves * 64);
@@ -1153,6 +1154,9 @@ hipError_t launch_group(const GemmDesc *const *d, int count, LaunchKind kind, hi
     if (bf && out)
       hipLaunchKernelGGL((skinny_kernel<kChunk, kWaves, kDepth, true, true>), grid, threads, lds,
                          stream, ps);
+    else if (bf && ml)
+      hipLaunchKernelGGL((skinny_kernel<kChunk, kWaves, kDepth, false, true, false, true>), grid,
+                         threads, lds, stream, ps);
     else if (bf)
       hipLaunchKernelGGL((skinny_kernel<kChunk, kWaves, kDepth, false, true>), grid, threads, lds,
                          stream, ps);
